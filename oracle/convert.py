@@ -1,0 +1,125 @@
+"""MHA -> MLA conversion of one attention layer (oracle; test infrastructure only).
+
+Follows the Paper-Notes ACL2025 page on MHA2MLA, section 关键设计 ("key designs"):
+
+1. Contribution-aware partial-RoPE.  RoPE splits q and k of a head into d_h/2
+   two-dimensional subspaces [2k, 2k+1], each rotated at its own frequency.  The
+   contribution of subspace k to the attention score is bounded (Cauchy-Schwarz)
+   by ||q^[2k,2k+1]|| * ||k^[2k,2k+1]||; each head keeps RoPE on its top-r
+   subspaces and the rest become NoPE dimensions.
+2. Joint SVD.  The NoPE key projections of all heads and the value projections
+   are concatenated, [W_k,nope ; W_v], and given a truncated SVD U S V^T.
+   W_dkv = U_trunc is the down-projection to the latent c_kv, and S V^T is split
+   per head into the up-projections W_uk and W_uv.
+
+Readings where the page leaves a step open (each also listed in the design notes):
+* scores aggregate over calibration tokens as the product of the mean pair norms,
+  which is exactly the mean of the bound over every (query token, key token) pair;
+* ties in the score go to the lower pair index; kept pairs are stored ascending;
+* the concatenation is by columns: all heads' K_nope blocks, then all heads' V blocks;
+* Sigma goes to the up-projections, so W_dkv has orthonormal columns.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def calibration_qk(x_cal, w_q, w_k, n_heads, d_head):
+    """Per-head queries and keys of the calibration tokens, [T, n_heads, d_head], without RoPE.
+
+    RoPE rotates each 2-D subspace, which leaves its 2-norm unchanged, so the pair norms
+    (and hence the scores) are the same with or without it."""
+    t = x_cal.shape[0]
+    q = (x_cal @ w_q).reshape(t, n_heads, d_head)
+    k = (x_cal @ w_k).reshape(t, n_heads, d_head)
+    return q, k
+
+
+def pair_scores(q, k):
+    """2-norm contribution score s[h, p] of subspace p = dims (2p, 2p+1) of head h.
+
+    s[h,p] = mean_t ||q_t^[2p,2p+1]|| * mean_t ||k_t^[2p,2p+1]||, the mean over all token pairs
+    (m, n) of the Cauchy-Schwarz bound ||q_m^p|| * ||k_n^p||."""
+    t, n_heads, d_head = q.shape
+    n_pairs = d_head // 2
+    s = np.zeros((n_heads, n_pairs))
+    for h in range(n_heads):
+        for p in range(n_pairs):
+            qn = np.sqrt(q[:, h, 2 * p] ** 2 + q[:, h, 2 * p + 1] ** 2)
+            kn = np.sqrt(k[:, h, 2 * p] ** 2 + k[:, h, 2 * p + 1] ** 2)
+            s[h, p] = qn.mean() * kn.mean()
+    return s
+
+
+def select_pairs(scores, r):
+    """Head-wise top-r subspaces by score (ties: lower index first), stored ascending, int32 [n_heads, r]."""
+    n_heads, n_pairs = scores.shape
+    out = np.zeros((n_heads, r), dtype=np.int32)
+    for h in range(n_heads):
+        order = sorted(range(n_pairs), key=lambda p: (-scores[h, p], p))
+        out[h] = sorted(order[:r])
+    return out
+
+
+def split_dims(pair_idx, d_head):
+    """Per head: (rope dims, nope dims), both in ascending original order.
+
+    rope(h) lists dims 2p, 2p+1 for p in pair_idx[h] (in slot order j = 0..r-1), nope(h) the rest."""
+    rope, nope = [], []
+    for h in range(pair_idx.shape[0]):
+        rd = []
+        for p in pair_idx[h]:
+            rd += [2 * int(p), 2 * int(p) + 1]
+        rope.append(rd)
+        nope.append([i for i in range(d_head) if i not in set(rd)])
+    return rope, nope
+
+
+def _nope_and_rope_columns(w_k, pair_idx, n_heads, d_head):
+    rope, nope = split_dims(pair_idx, d_head)
+    w_knope = np.concatenate([w_k[:, [h * d_head + i for i in nope[h]]] for h in range(n_heads)], axis=1)
+    w_krope = np.concatenate([w_k[:, [h * d_head + i for i in rope[h]]] for h in range(n_heads)], axis=1)
+    return w_knope, w_krope
+
+
+def joint_svd(w_k, w_v, pair_idx, n_heads, d_head, d_kv):
+    """Truncated joint SVD of M = [W_k,nope | W_v] (columns: K_nope blocks of all heads, then V blocks).
+
+    Returns W_dkv [d, d_kv], W_uk [n_heads, d_kv, d_head-2r], W_uv [n_heads, d_kv, d_head],
+    W_krope [d, n_heads*2r] (kept RoPE columns of W_k packed (head, slot, 2)) and all singular values."""
+    r = pair_idx.shape[1]
+    dn = d_head - 2 * r
+    w_knope, w_krope = _nope_and_rope_columns(w_k, pair_idx, n_heads, d_head)
+    m = np.concatenate([w_knope, w_v], axis=1)
+    u, sig, vt = np.linalg.svd(m, full_matrices=False)
+    w_dkv = u[:, :d_kv]
+    z = sig[:d_kv, None] * vt[:d_kv]
+    w_uk = np.stack([z[:, h * dn:(h + 1) * dn] for h in range(n_heads)])
+    off = n_heads * dn
+    w_uv = np.stack([z[:, off + h * d_head: off + (h + 1) * d_head] for h in range(n_heads)])
+    return dict(w_dkv=w_dkv, w_uk=w_uk, w_uv=w_uv, w_krope=w_krope, sigma=sig, m=m)
+
+
+def split_svd(w_k, w_v, pair_idx, n_heads, d_head, rank_k, rank_v):
+    """SVD_split baseline: separate truncated SVDs of W_k,nope (rank_k) and W_v (rank_v).
+
+    Returns the two rank-truncated approximations (used to check that the joint SVD at the same
+    total latent width is never worse)."""
+    w_knope, _ = _nope_and_rope_columns(w_k, pair_idx, n_heads, d_head)
+
+    def trunc(a, rank):
+        u, s, vt = np.linalg.svd(a, full_matrices=False)
+        return (u[:, :rank] * s[:rank]) @ vt[:rank]
+
+    return trunc(w_knope, rank_k), trunc(w_v, rank_v), w_knope
+
+
+def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv):
+    """Full conversion: calibration -> scores -> head-wise top-r -> joint SVD."""
+    q, k = calibration_qk(x_cal, w_q, w_k, n_heads, d_head)
+    scores = pair_scores(q, k)
+    pair_idx = select_pairs(scores, r)
+    out = joint_svd(w_k, w_v, pair_idx, n_heads, d_head, d_kv)
+    out.update(pair_idx=pair_idx, scores=scores)
+    return out
