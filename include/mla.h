@@ -1,0 +1,154 @@
+/*
+ * mla.h -- C ABI of the MHA2MLA latent-cache attention library (gfx950 / MI355X).
+ *
+ * The method (Paper-Notes ACL2025 page "MHA2MLA: Towards Economical Inference by Enabling
+ * DeepSeek's Multi-Head Latent Attention in Any Transformer-based LLMs", section 关键设计,
+ * "key designs"): an MHA layer is converted so that its KV cache holds, per token,
+ *   - the latent c_kv = x . W_dkv (d_kv values shared by all heads; W_dkv = U_trunc of the
+ *     joint SVD of [W_k,nope ; W_v]), and
+ *   - per head, the keys of the r RoPE subspaces [2p, 2p+1] that head keeps (chosen offline by
+ *     the 2-norm contribution score), already rotated at the token's position.
+ * K_nope and V of head h are recovered from c_kv through that head's up-projections W_uk,h and
+ * W_uv,h (the split of Sigma V^T); the RoPE part is computed separately because it cannot be
+ * merged into the matrices.  The optional 4-bit latent follows the page's remark that the
+ * latent composes with KV-cache quantisation.
+ *
+ * Conventions for every entry point
+ *   - All pointers to tensors are DEVICE pointers to caller-owned memory unless marked [host].
+ *     The library never allocates, frees or synchronises device memory; scratch space comes from
+ *     the caller's workspace, sized by the matching *_workspace_bytes call.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream).  The calls keep no
+ *     mutable global state and may be made from several host threads; calls that share output
+ *     buffers or a workspace must be ordered by the caller (same stream or events).
+ *   - Return value: MLA_OK (0) or a negative mla_status.  Every argument check runs on the host
+ *     before anything is enqueued, so a call that returns an error has written nothing.
+ *     MLA_ERR_HIP reports a failed launch (hipGetLastError after enqueueing); work enqueued
+ *     before the failing launch may have run.
+ *   - Dense row-major layouts; all tensor pointers must be 16-byte aligned (MLA_ERR_ALIGNMENT).
+ *   - Weights use the [out_features, in_features] layout (each output's weights contiguous).
+ *   - dtype MLA_F32: activations, weights, cache and outputs are fp32.  MLA_BF16: bf16 storage
+ *     with fp32 accumulation and fp32 softmax.  RoPE tables are always fp32.
+ *   - Device-resident per-sequence integers (start_pos, seq_lens) are trusted to lie within the
+ *     host-side bound passed next to them; the kernels clamp to that bound, so a larger device
+ *     value cannot make them access memory outside the buffers described here.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, inconsistent shape            */
+  MLA_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype/format/shape combination)     */
+  MLA_ERR_ALIGNMENT = -3,   /* a tensor pointer is not 16-byte aligned                        */
+  MLA_ERR_WORKSPACE = -4,   /* workspace null or smaller than *_workspace_bytes               */
+  MLA_ERR_CAPACITY = -5,    /* positions would exceed the cache's t_max or the RoPE table     */
+  MLA_ERR_HIP = -6          /* a kernel launch failed                                          */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+typedef enum {
+  MLA_CACHE_DENSE = 0,   /* c_kv stored in the config dtype                                    */
+  MLA_CACHE_INT4_G32 = 1 /* c_kv as int4 codes, groups of 32 latent dims, fp16 absmax scale;
+                            k_rope stays in the config dtype (BF16 only)                        */
+} mla_cache_fmt;
+
+/* Layer shape.  d_head even; 0 <= r_pairs <= d_head/2; d_kv >= 1 (multiple of 32 for INT4_G32). */
+typedef struct {
+  int32_t d_model;   /* model width d                                            */
+  int32_t n_heads;   /* attention heads n_h                                      */
+  int32_t d_head;    /* head dim d_h                                             */
+  int32_t r_pairs;   /* RoPE subspaces kept per head, r (2r key dims per head)   */
+  int32_t d_kv;      /* latent width (rank of the joint SVD), shared by all heads */
+  int32_t dtype;     /* mla_dtype                                                 */
+  int32_t cache_fmt; /* mla_cache_fmt                                             */
+} mla_config;
+
+/* Converted weights (read-only, device).  nope(h) = the d_h - 2r dims of head h whose subspace is
+ * not kept, ascending; rope(h) = dims 2p, 2p+1 for p = pair_idx[h][j], j = 0..r-1.              */
+typedef struct {
+  const void *w_dkv;        /* [d_kv, d_model]           W_dkv^T (down-projection, U_trunc)      */
+  const void *w_krope;      /* [n_h*2r, d_model]         rows (h, j, c) = column 2p+c of head h
+                                                          of W_k, p = pair_idx[h][j]               */
+  const void *w_uk;         /* [n_h, d_h-2r, d_kv]       W_uk,h^T: row i rebuilds K dim nope(h)[i] */
+  const void *w_uv;         /* [n_h, d_h, d_kv]          W_uv,h^T: row e rebuilds V dim e          */
+  const int32_t *pair_idx;  /* [n_h, r] int32, ascending per head, each in [0, d_h/2)           */
+  const float *rope_cos;    /* [rope_len, d_h/2] fp32: cos(pos * theta^(-2p/d_h))               */
+  const float *rope_sin;    /* [rope_len, d_h/2] fp32: sin(...)                                 */
+  int32_t rope_len;         /* rows of the RoPE tables (positions 0..rope_len-1)                */
+} mla_weights;
+
+/* Latent cache for `batch` sequences of up to t_max tokens each.
+ *   DENSE:    ckv   [batch, t_max, d_kv]      config dtype
+ *   INT4_G32: ckv   [batch, t_max, d_kv/2]    uint8, byte i = (code[2i] & 15) | (code[2i+1] & 15) << 4,
+ *                                             codes two's-complement in [-7, 7]
+ *             ckv_scale [batch, t_max, d_kv/32] fp16 (ignored / may be NULL for DENSE)
+ *   both:     krope [batch, t_max, n_h, 2r]   config dtype, pair (j, c) of head h at index h*2r + 2j + c */
+typedef struct {
+  void *ckv;
+  void *ckv_scale;
+  void *krope;
+  int32_t batch;
+  int32_t t_max;
+} mla_cache;
+
+/* ---------------------------------------------------------------- append
+ * Writes t_new tokens per sequence into the cache (down-projection and partial RoPE; the
+ * key-designs section's latent c_kv = x . W_dkv and the per-head retained RoPE keys).
+ *   x          [cache->batch, t_new, d_model] activations (config dtype)
+ *   start_pos  [cache->batch] int32 (device): token i of sequence b goes to position start_pos[b]+i
+ *   max_start_pos  host bound on start_pos[]: requires max_start_pos + t_new <= t_max and
+ *                  <= rope_len (else MLA_ERR_CAPACITY)
+ * Per token:  c_kv = x . W_dkv (fp32 accumulate, then rounded to the dtype, or quantised:
+ *             s = fp16(absmax/7), code = clamp(rint(c/s), -7, 7), IEEE fp32 divisions);
+ *             k_rope[h, j] = rotate((x . W_krope)[h, j, 0:2], pos * theta^(-2p/d_h)).
+ * t_new == 0 or batch == 0 is a no-op returning MLA_OK.                                        */
+int mla_cache_append(const mla_config *cfg, const mla_weights *w, mla_cache *cache, const void *x,
+                     const int32_t *start_pos, int32_t t_new, int32_t max_start_pos, hipStream_t stream);
+
+/* ---------------------------------------------------------------- decode
+ * One query token per sequence attends to its cached tokens (the absorbed form of the
+ * key-designs section: W_uk,h folded into the query, W_uv,h applied after the weighted latent sum).
+ *   q          [batch, n_h, d_h] raw query (x . W_q, before RoPE, original head-dim order)
+ *   seq_lens   [batch] int32 (device): L_b cached tokens, the query sits at position L_b - 1
+ *              (append it first); L_b == 0 gives a zero output row
+ *   max_seq_len  host bound on seq_lens[], 0 <= max_seq_len <= t_max and <= rope_len
+ *   out        [batch, n_h, d_h] per-head attention outputs (before the output projection)
+ * Scores are (q_hat . k_hat) / sqrt(d_h) with softmax over positions 0..L_b-1.
+ * Workspace: mla_decode_workspace_bytes(cfg, batch, max_seq_len) bytes.                        */
+size_t mla_decode_workspace_bytes(const mla_config *cfg, int32_t batch, int32_t max_seq_len);
+int mla_decode(const mla_config *cfg, const mla_weights *w, const mla_cache *cache, const void *q,
+               const int32_t *seq_lens, int32_t max_seq_len, void *out, void *workspace, size_t ws_bytes,
+               hipStream_t stream);
+
+/* ---------------------------------------------------------------- prefill
+ * Causal attention of seq_len query tokens per sequence, at positions 0..seq_len-1, over the
+ * cache rows 0..seq_len-1 (append them first).  Unabsorbed form: K_nope and V of every head are
+ * rebuilt from c_kv (c_kv . W_uk,h and c_kv . W_uv,h), the kept RoPE keys are read from the cache.
+ *   q    [batch, seq_len, n_h, d_h] raw queries;   out [batch, seq_len, n_h, d_h]
+ * BF16 dense caches only (MLA_ERR_UNSUPPORTED otherwise).
+ * Workspace: mla_prefill_workspace_bytes(cfg, batch, seq_len) bytes.                           */
+size_t mla_prefill_workspace_bytes(const mla_config *cfg, int32_t batch, int32_t seq_len);
+int mla_prefill(const mla_config *cfg, const mla_weights *w, const mla_cache *cache, const void *q,
+                int32_t seq_len, void *out, void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- int4 codec
+ * The latent quantiser of the INT4_G32 cache on its own, for bit-exact checks of the codes.
+ *   in [n_groups*32] fp32 -> codes [n_groups*16] uint8 (packed as above), scales [n_groups] fp16 bits. */
+int mla_quantize_int4(const float *in, int64_t n_groups, uint8_t *codes, uint16_t *scales, hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char *mla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H_ */

@@ -1,0 +1,20 @@
+"""MHA2MLA latent-cache attention for MI355X (gfx950): a C-ABI HIP library plus this thin binding.
+
+    from mla_latent_kv_cache_amd import LayerShape, pack_weights, LatentCache, append, decode, prefill
+"""
+
+from .api import (  # noqa: F401
+    LatentCache,
+    LayerShape,
+    LayerWeights,
+    MlaError,
+    append,
+    decode,
+    decode_workspace_bytes,
+    pack_weights,
+    prefill,
+    prefill_workspace_bytes,
+    quantize_int4,
+    rope_tables,
+)
+from .convert import convert_layer  # noqa: F401

@@ -1,0 +1,225 @@
+"""Python binding of the latent-cache library: argument marshalling only.
+
+Every step of append / decode / prefill runs in the library's gfx950 kernels; this module builds the
+C structs from torch device tensors, passes the current HIP stream, and raises on a non-zero status.
+There is no fallback: without the built library or a GPU the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import MLA_BF16, MLA_CACHE_DENSE, MLA_CACHE_INT4_G32, MLA_F32, MlaCache, MlaConfig, MlaWeights
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.load().mla_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg} ({status})")
+        self.status = status
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise MlaError(fn, rc)
+
+
+@dataclass(frozen=True)
+class LayerShape:
+    """Shape of one converted layer and its cache format (mirrors mla_config)."""
+
+    d_model: int
+    n_heads: int
+    d_head: int
+    r_pairs: int
+    d_kv: int
+    dtype: str = "bf16"  # "bf16" or "f32"
+    cache_fmt: str = "dense"  # "dense" or "int4_g32"
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def c(self) -> MlaConfig:
+        return MlaConfig(
+            self.d_model,
+            self.n_heads,
+            self.d_head,
+            self.r_pairs,
+            self.d_kv,
+            MLA_BF16 if self.dtype == "bf16" else MLA_F32,
+            MLA_CACHE_INT4_G32 if self.cache_fmt == "int4_g32" else MLA_CACHE_DENSE,
+        )
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def rope_tables(rope_len: int, d_head: int, theta: float = 1e4):
+    """cos / sin tables [rope_len, d_head/2] (fp32) of the angle pos * theta^(-2p/d_head), built in fp64."""
+    pos = np.arange(rope_len, dtype=np.float64)[:, None]
+    freq = theta ** (-2.0 * np.arange(d_head // 2, dtype=np.float64) / d_head)
+    ang = pos * freq[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+@dataclass
+class LayerWeights:
+    """Converted weights on the device, in the ABI's [out_features, in_features] layouts."""
+
+    shape: LayerShape
+    w_dkv: torch.Tensor  # [d_kv, d_model]
+    w_krope: torch.Tensor  # [n_h*2r, d_model]
+    w_uk: torch.Tensor  # [n_h, d_h-2r, d_kv]
+    w_uv: torch.Tensor  # [n_h, d_h, d_kv]
+    pair_idx: torch.Tensor  # [n_h, r] int32
+    rope_cos: torch.Tensor  # [rope_len, d_h/2] fp32
+    rope_sin: torch.Tensor
+
+    def c(self) -> MlaWeights:
+        return MlaWeights(
+            _ptr(self.w_dkv),
+            _ptr(self.w_krope),
+            _ptr(self.w_uk),
+            _ptr(self.w_uv),
+            _ptr(self.pair_idx),
+            _ptr(self.rope_cos),
+            _ptr(self.rope_sin),
+            self.rope_cos.shape[0],
+        )
+
+
+def pack_weights(shape: LayerShape, conv: dict, rope_len: int, theta: float = 1e4, device="cuda") -> LayerWeights:
+    """Move converted weights (math layouts: w_dkv [d, d_kv], w_krope [d, n_h*2r], w_uk [n_h, d_kv, d_h-2r],
+    w_uv [n_h, d_kv, d_h], pair_idx [n_h, r]) to the device in the ABI layouts and dtype."""
+    dt = shape.torch_dtype
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(device=device, dtype=dt).contiguous()
+
+    n_h, dn, dh, D, d = shape.n_heads, shape.d_head - 2 * shape.r_pairs, shape.d_head, shape.d_kv, shape.d_model
+    w_dkv = dev(np.asarray(conv["w_dkv"]).T)
+    w_krope = dev(np.asarray(conv["w_krope"]).reshape(d, -1).T)
+    w_uk = dev(np.asarray(conv["w_uk"]).reshape(n_h, D, dn).transpose(0, 2, 1))
+    w_uv = dev(np.asarray(conv["w_uv"]).reshape(n_h, D, dh).transpose(0, 2, 1))
+    pidx = torch.from_numpy(np.ascontiguousarray(conv["pair_idx"], dtype=np.int32)).to(device)
+    cos, sin = rope_tables(rope_len, dh, theta)
+    return LayerWeights(shape, w_dkv, w_krope, w_uk, w_uv, pidx, torch.from_numpy(cos).to(device),
+                        torch.from_numpy(sin).to(device))
+
+
+@dataclass
+class LatentCache:
+    """Latent cache for `batch` sequences of up to t_max tokens (layouts of mla_cache)."""
+
+    shape: LayerShape
+    ckv: torch.Tensor
+    ckv_scale: Optional[torch.Tensor]
+    krope: torch.Tensor
+    batch: int
+    t_max: int
+
+    @staticmethod
+    def allocate(shape: LayerShape, batch: int, t_max: int, device="cuda", fill: Optional[float] = None):
+        nr = shape.n_heads * 2 * shape.r_pairs
+        if shape.cache_fmt == "int4_g32":
+            ckv = torch.zeros((batch, t_max, shape.d_kv // 2), dtype=torch.uint8, device=device)
+            scale = torch.zeros((batch, t_max, shape.d_kv // 32), dtype=torch.float16, device=device)
+        else:
+            ckv = torch.empty((batch, t_max, shape.d_kv), dtype=shape.torch_dtype, device=device)
+            scale = None
+        krope = torch.empty((batch, t_max, max(nr, 1)), dtype=shape.torch_dtype, device=device)
+        if fill is not None:
+            if scale is None:
+                ckv.fill_(fill)
+            krope.fill_(fill)
+        return LatentCache(shape, ckv, scale, krope, batch, t_max)
+
+    def c(self) -> MlaCache:
+        return MlaCache(_ptr(self.ckv), _ptr(self.ckv_scale), _ptr(self.krope), self.batch, self.t_max)
+
+    def nbytes_per_token(self) -> int:
+        n = self.ckv[0, 0].numel() * self.ckv.element_size() + self.krope[0, 0].numel() * self.krope.element_size()
+        if self.ckv_scale is not None:
+            n += self.ckv_scale[0, 0].numel() * 2
+        return n
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def append(w: LayerWeights, cache: LatentCache, x: torch.Tensor, start_pos: torch.Tensor, max_start_pos: int,
+           stream=None) -> None:
+    """mla_cache_append: x [batch, t_new, d_model] at positions start_pos[b] + i."""
+    lib = _lib.load()
+    cfg, cw, cc = w.shape.c(), w.c(), cache.c()
+    t_new = x.shape[1]
+    _check("mla_cache_append", lib.mla_cache_append(ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc), _ptr(x),
+                                                    _ptr(start_pos), t_new, int(max_start_pos), _stream(stream)))
+
+
+def decode_workspace_bytes(shape: LayerShape, batch: int, max_seq_len: int) -> int:
+    cfg = shape.c()
+    return _lib.load().mla_decode_workspace_bytes(ctypes.byref(cfg), batch, max_seq_len)
+
+
+def decode(w: LayerWeights, cache: LatentCache, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """mla_decode: q [batch, n_h, d_h] -> out [batch, n_h, d_h]."""
+    lib = _lib.load()
+    cfg, cw, cc = w.shape.c(), w.c(), cache.c()
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = lib.mla_decode_workspace_bytes(ctypes.byref(cfg), cache.batch, int(max_seq_len))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check("mla_decode", lib.mla_decode(ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc), _ptr(q),
+                                        _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(workspace),
+                                        workspace.numel(), _stream(stream)))
+    return out
+
+
+def prefill_workspace_bytes(shape: LayerShape, batch: int, seq_len: int) -> int:
+    cfg = shape.c()
+    return _lib.load().mla_prefill_workspace_bytes(ctypes.byref(cfg), batch, seq_len)
+
+
+def prefill(w: LayerWeights, cache: LatentCache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """mla_prefill: q [batch, S, n_h, d_h] at positions 0..S-1 -> out [batch, S, n_h, d_h]."""
+    lib = _lib.load()
+    cfg, cw, cc = w.shape.c(), w.c(), cache.c()
+    seq_len = q.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = lib.mla_prefill_workspace_bytes(ctypes.byref(cfg), cache.batch, seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check("mla_prefill", lib.mla_prefill(ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc), _ptr(q), seq_len,
+                                          _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def quantize_int4(x: torch.Tensor, stream=None):
+    """mla_quantize_int4 on fp32 x [..., 32*g] -> (codes uint8 [..., 16*g], scales float16 [..., g])."""
+    lib = _lib.load()
+    if x.dtype != torch.float32:
+        raise ValueError("quantize_int4 takes fp32 input")
+    n_groups = x.numel() // 32
+    codes = torch.empty(x.shape[:-1] + (x.shape[-1] // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (x.shape[-1] // 32,), dtype=torch.float16, device=x.device)
+    _check("mla_quantize_int4", lib.mla_quantize_int4(_ptr(x), n_groups, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales

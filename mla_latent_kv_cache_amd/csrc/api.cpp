@@ -1,0 +1,174 @@
+// C ABI of the latent-cache library: host-side argument checks, workspace sizing and dispatch.
+// Every check runs before anything is enqueued, so a rejected call has no side effects.
+#include "../../include/mla.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+using mla::Shape;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape-only checks shared by every entry point.
+int check_config(const mla_config* c) {
+  if (!c) return MLA_ERR_INVALID_ARG;
+  if (c->d_model <= 0 || c->n_heads <= 0 || c->d_head <= 0 || c->d_kv <= 0) return MLA_ERR_INVALID_ARG;
+  if (c->d_head % 2 != 0 || c->r_pairs < 0 || 2 * c->r_pairs > c->d_head) return MLA_ERR_INVALID_ARG;
+  if (c->dtype != MLA_F32 && c->dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
+  if (c->cache_fmt != MLA_CACHE_DENSE && c->cache_fmt != MLA_CACHE_INT4_G32) return MLA_ERR_INVALID_ARG;
+  if (c->d_head > 256) return MLA_ERR_UNSUPPORTED;
+  if (c->cache_fmt == MLA_CACHE_INT4_G32 && (c->dtype != MLA_BF16 || c->d_kv % 32 != 0)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+Shape shape_of(const mla_config* c) {
+  return Shape{c->d_model, c->n_heads, c->d_head, c->r_pairs, c->d_kv, c->dtype, c->cache_fmt};
+}
+
+// A pointer that must be present (non-null, 16-byte aligned) when `needed`.
+int check_ptr(const void* p, bool needed) {
+  if (!needed) return MLA_OK;
+  if (!p) return MLA_ERR_INVALID_ARG;
+  return aligned16(p) ? MLA_OK : MLA_ERR_ALIGNMENT;
+}
+
+#define MLA_TRY(expr)          \
+  do {                         \
+    int rc_ = (expr);          \
+    if (rc_ != MLA_OK) return rc_; \
+  } while (0)
+
+int check_weights(const mla_config* c, const mla_weights* w, bool need_dkv, bool need_up) {
+  if (!w) return MLA_ERR_INVALID_ARG;
+  const bool has_rope = c->r_pairs > 0;
+  const bool has_nope = c->d_head - 2 * c->r_pairs > 0;
+  MLA_TRY(check_ptr(w->w_dkv, need_dkv));
+  MLA_TRY(check_ptr(w->w_krope, need_dkv && has_rope));
+  MLA_TRY(check_ptr(w->w_uk, need_up && has_nope));
+  MLA_TRY(check_ptr(w->w_uv, need_up));
+  MLA_TRY(check_ptr(w->pair_idx, has_rope));
+  MLA_TRY(check_ptr(w->rope_cos, has_rope));
+  MLA_TRY(check_ptr(w->rope_sin, has_rope));
+  if (has_rope && w->rope_len <= 0) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+int check_cache(const mla_config* c, const mla_cache* k) {
+  if (!k) return MLA_ERR_INVALID_ARG;
+  if (k->batch < 0 || k->t_max <= 0) return MLA_ERR_INVALID_ARG;
+  MLA_TRY(check_ptr(k->ckv, true));
+  MLA_TRY(check_ptr(k->krope, c->r_pairs > 0));
+  MLA_TRY(check_ptr(k->ckv_scale, c->cache_fmt == MLA_CACHE_INT4_G32));
+  return MLA_OK;
+}
+
+// Positions [0, limit) must fit in the cache and, when RoPE is used, in the RoPE tables.
+int check_positions(const mla_config* c, const mla_weights* w, const mla_cache* k, long long limit) {
+  if (limit > k->t_max) return MLA_ERR_CAPACITY;
+  if (c->r_pairs > 0 && limit > w->rope_len) return MLA_ERR_CAPACITY;
+  return MLA_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLA_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_CAPACITY: return "positions exceed cache or RoPE table capacity";
+    case MLA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int mla_cache_append(const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
+                     const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, hipStream_t stream) {
+  MLA_TRY(check_config(cfg));
+  MLA_TRY(check_weights(cfg, w, true, false));
+  MLA_TRY(check_cache(cfg, cache));
+  if (t_new < 0 || max_start_pos < 0) return MLA_ERR_INVALID_ARG;
+  if (t_new == 0 || cache->batch == 0) return MLA_OK;
+  MLA_TRY(check_ptr(x, true));
+  MLA_TRY(check_ptr(start_pos, true));
+  MLA_TRY(check_positions(cfg, w, cache, (long long)max_start_pos + t_new));
+  if ((long long)cache->batch * t_new > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if (!mla::append_fits(shape_of(cfg))) return MLA_ERR_UNSUPPORTED;
+  mla::AppendArgs a{shape_of(cfg), x, w->w_dkv, w->w_krope, w->pair_idx, w->rope_cos, w->rope_sin,
+                    start_pos, cache->batch, t_new, max_start_pos, cache->t_max,
+                    cache->ckv, cache->ckv_scale, cache->krope};
+  return from_hip(mla::launch_append(a, stream));
+}
+
+size_t mla_decode_workspace_bytes(const mla_config* cfg, int32_t batch, int32_t max_seq_len) {
+  if (check_config(cfg) != MLA_OK || batch < 0 || max_seq_len < 0) return 0;
+  return mla::plan_decode(shape_of(cfg), batch, max_seq_len).total;
+}
+
+int mla_decode(const mla_config* cfg, const mla_weights* w, const mla_cache* cache, const void* q,
+               const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace, size_t ws_bytes,
+               hipStream_t stream) {
+  MLA_TRY(check_config(cfg));
+  MLA_TRY(check_weights(cfg, w, false, true));
+  MLA_TRY(check_cache(cfg, cache));
+  if (max_seq_len < 0) return MLA_ERR_INVALID_ARG;
+  if (cache->batch == 0) return MLA_OK;
+  MLA_TRY(check_ptr(q, true));
+  MLA_TRY(check_ptr(seq_lens, true));
+  MLA_TRY(check_ptr(out, true));
+  MLA_TRY(check_positions(cfg, w, cache, max_seq_len));
+  const Shape s = shape_of(cfg);
+  const mla::DecodePlan plan = mla::plan_decode(s, cache->batch, max_seq_len);
+  if (!mla::decode_fits(s, plan)) return MLA_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < plan.total) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
+  mla::DecodeArgs a{s, q, w->w_uk, w->w_uv, w->pair_idx, w->rope_cos, w->rope_sin,
+                    cache->ckv, cache->ckv_scale, cache->krope, cache->batch, cache->t_max, max_seq_len,
+                    seq_lens, out, (char*)workspace, plan};
+  return from_hip(mla::launch_decode(a, stream));
+}
+
+size_t mla_prefill_workspace_bytes(const mla_config* cfg, int32_t batch, int32_t seq_len) {
+  if (check_config(cfg) != MLA_OK || batch < 0 || seq_len < 0) return 0;
+  return mla::plan_prefill(shape_of(cfg), batch, seq_len).total;
+}
+
+int mla_prefill(const mla_config* cfg, const mla_weights* w, const mla_cache* cache, const void* q,
+                int32_t seq_len, void* out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  MLA_TRY(check_config(cfg));
+  MLA_TRY(check_weights(cfg, w, false, true));
+  MLA_TRY(check_cache(cfg, cache));
+  if (seq_len < 0) return MLA_ERR_INVALID_ARG;
+  const Shape s = shape_of(cfg);
+  if (!mla::prefill_supported(s)) return MLA_ERR_UNSUPPORTED;
+  if (seq_len == 0 || cache->batch == 0) return MLA_OK;
+  MLA_TRY(check_ptr(q, true));
+  MLA_TRY(check_ptr(out, true));
+  MLA_TRY(check_positions(cfg, w, cache, seq_len));
+  const mla::PrefillPlan plan = mla::plan_prefill(s, cache->batch, seq_len);
+  if (!workspace || ws_bytes < plan.total) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
+  mla::PrefillArgs a{s, q, w->w_uk, w->w_uv, w->pair_idx, w->rope_cos, w->rope_sin, cache->ckv, cache->krope,
+                     cache->batch, cache->t_max, seq_len, out, (char*)workspace, plan};
+  return from_hip(mla::launch_prefill(a, stream));
+}
+
+int mla_quantize_int4(const float* in, int64_t n_groups, uint8_t* codes, uint16_t* scales, hipStream_t stream) {
+  if (n_groups < 0) return MLA_ERR_INVALID_ARG;
+  if (n_groups == 0) return MLA_OK;
+  if (!in || !codes || !scales) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(in) || !aligned16(codes) || !aligned16(scales)) return MLA_ERR_ALIGNMENT;
+  if (n_groups > ((int64_t)1 << 36)) return MLA_ERR_UNSUPPORTED;
+  return from_hip(mla::launch_quantize_int4(in, n_groups, codes, scales, stream));
+}
+
+}  // extern "C"

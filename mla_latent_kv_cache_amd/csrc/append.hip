@@ -1,0 +1,274 @@
+// Latent-cache append on gfx950: c_kv = x . W_dkv and the per-head retained RoPE keys.
+//
+// The down-projection of the MHA2MLA key-designs section (Paper-Notes ACL2025 page, 关键设计):
+// each token's latent row c_kv = x . W_dkv is shared by all heads, and each head keeps the keys of
+// its r retained RoPE subspaces [2p, 2p+1], rotated at the token's position (the RoPE part cannot
+// be merged into the matrices, so it is cached separately).  Both projections run as ONE GEMM over
+// the row-concatenation [W_dkv^T ; W_krope] (N = d_kv + n_h*2r outputs per token); the epilogue
+// rotates adjacent output-column pairs and stores c_kv either in the cache dtype or as int4 codes.
+#include <hip/hip_fp16.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace {
+
+__device__ __forceinline__ int cache_row(const AppendArgs& a, int m, int* pos_out) {
+  int b = m / a.t_new;
+  int i = m - b * a.t_new;
+  int sp = a.start_pos[b];
+  sp = sp < 0 ? 0 : (sp > a.max_start ? a.max_start : sp);
+  int pos = sp + i;
+  *pos_out = pos;
+  return b * a.t_max + pos;
+}
+
+// ------------------------------------------------------------------ generic path (any dtype / format)
+// One workgroup per token: x row staged in LDS, one thread per output column, then the epilogue.
+template <typename T>
+__global__ __launch_bounds__(256) void append_generic(AppendArgs a) {
+  extern __shared__ float sh[];
+  const int d = a.s.d_model, D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR;
+  float* xs = sh;
+  float* outs = sh + d;
+  const int m = blockIdx.x;
+  const T* x = (const T*)a.x + (size_t)m * d;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) xs[k] = to_f32(x[k]);
+  __syncthreads();
+  for (int n = threadIdx.x; n < N; n += blockDim.x) {
+    const T* w = n < D ? (const T*)a.w_dkv + (size_t)n * d : (const T*)a.w_krope + (size_t)(n - D) * d;
+    float acc = 0.f;
+    for (int k = 0; k < d; ++k) acc = fmaf(xs[k], to_f32(w[k]), acc);
+    outs[n] = acc;
+  }
+  __syncthreads();
+  int pos;
+  const size_t row = (size_t)cache_row(a, m, &pos);
+  if (a.s.fmt == 0) {
+    T* ckv = (T*)a.ckv + row * D;
+    for (int n = threadIdx.x; n < D; n += blockDim.x) ckv[n] = from_f32<T>(outs[n]);
+  } else {
+    uint8_t* codes = (uint8_t*)a.ckv + row * (D / 2);
+    __half* scales = (__half*)a.ckv_scale + row * (D / 32);
+    for (int g = threadIdx.x; g < D / 32; g += blockDim.x) {
+      float am = 0.f;
+      for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(outs[32 * g + i]));
+      __half s = int4_scale(am);
+      float sf = __half2float(s);
+      for (int i = 0; i < 16; ++i) {
+        int c0 = int4_code(outs[32 * g + 2 * i], sf), c1 = int4_code(outs[32 * g + 2 * i + 1], sf);
+        codes[16 * g + i] = (uint8_t)((c0 & 15) | ((c1 & 15) << 4));
+      }
+      scales[g] = s;
+    }
+  }
+  const int r = a.s.r_pairs, R2 = a.s.r2(), half = a.s.d_head / 2;
+  T* kr = (T*)a.krope + row * NR;
+  for (int q = threadIdx.x; q < a.s.n_heads * r; q += blockDim.x) {
+    int h = q / r, j = q - h * r;
+    int p = load_pair(a.pair_idx, h * r + j, half);
+    float c = a.rope_cos[(size_t)pos * half + p], s = a.rope_sin[(size_t)pos * half + p];
+    float x0 = outs[D + h * R2 + 2 * j], x1 = outs[D + h * R2 + 2 * j + 1];
+    kr[h * R2 + 2 * j] = from_f32<T>(x0 * c - x1 * s);
+    kr[h * R2 + 2 * j + 1] = from_f32<T>(x0 * s + x1 * c);
+  }
+}
+
+// ------------------------------------------------------------------ MFMA path (bf16)
+// Workgroup tile 128 tokens x 128 output columns, K step 64, 4 waves of 64x64 (2x2 MFMA 32x32x16
+// blocks), LDS double buffer with padded rows.  Workgroups are renumbered so that the
+// column tiles of one token block run on the same XCD (its L2 then serves the shared x rows).
+constexpr int TM = 128, TN = 128, TK = 64, PITCH = TK + 8;
+
+__global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 sA[2][TM * PITCH];
+  __shared__ __attribute__((aligned(16))) bf16 sB[2][TN * PITCH];
+  const int K = a.s.d_model, D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR;
+  const int M = a.batch * a.t_new;
+  const int n_tiles = (N + TN - 1) / TN;
+  const int total = gridDim.x;
+  int bid = blockIdx.x;
+  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  const int m0 = (bid / n_tiles) * TM, n0 = (bid % n_tiles) * TN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const bf16* x = (const bf16*)a.x;
+  const bf16* wd = (const bf16*)a.w_dkv;
+  const bf16* wr = (const bf16*)a.w_krope;
+
+  bf16x8 ra[4], rb[4];
+  const bf16x8 zero8 = {};
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      int c = it * 256 + tid, row = c >> 3, kc = (c & 7) * 8;
+      int gm = m0 + row, gn = n0 + row;
+      ra[it] = gm < M ? *(const bf16x8*)(x + (size_t)gm * K + kt * TK + kc) : zero8;
+      const bf16* wrow = gn < D ? wd + (size_t)gn * K : wr + (size_t)(gn - D) * K;
+      rb[it] = gn < N ? *(const bf16x8*)(wrow + kt * TK + kc) : zero8;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      int c = it * 256 + tid, row = c >> 3, kc = (c & 7) * 8;
+      *(bf16x8*)&sA[buf][row * PITCH + kc] = ra[it];
+      *(bf16x8*)&sB[buf][row * PITCH + kc] = rb[it];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  const int KT = K / TK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < TK / 16; ++ks) {
+      bf16x8 av[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        av[i] = *(const bf16x8*)&sA[buf][(wm * 64 + i * 32 + (lane & 31)) * PITCH + ks * 16 + (lane >> 5) * 8];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bv[j] = *(const bf16x8*)&sB[buf][(wn * 64 + j * 32 + (lane & 31)) * PITCH + ks * 16 + (lane >> 5) * 8];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(av[i], bv[j], acc[i][j]);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  const int r = a.s.r_pairs, R2 = a.s.r2(), half = a.s.d_head / 2;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c0 = n0 + wn * 64 + j * 32;
+      const int n = c0 + (lane & 31);
+      if (c0 >= N) continue;  // uniform across the wave
+      if (c0 < D) {
+        if (a.s.fmt == 0) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            if (m < M) {
+              int pos;
+              size_t row = (size_t)cache_row(a, m, &pos);
+              ((bf16*)a.ckv)[row * D + n] = (bf16)acc[i][j][e];
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float v = acc[i][j][e];
+            float am = fabsf(v);
+#pragma unroll
+            for (int msk = 1; msk < 32; msk <<= 1) am = fmaxf(am, shfl_xor(am, msk));
+            __half s = int4_scale(am);
+            int code = int4_code(v, __half2float(s));
+            int partner = __shfl_xor(code, 1, 64);
+            int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            if (m < M) {
+              int pos;
+              size_t row = (size_t)cache_row(a, m, &pos);
+              if ((lane & 1) == 0)
+                ((uint8_t*)a.ckv)[row * (D / 2) + (n >> 1)] = (uint8_t)((code & 15) | ((partner & 15) << 4));
+              if ((lane & 31) == 0) ((__half*)a.ckv_scale)[row * (D / 32) + (n >> 5)] = s;
+            }
+          }
+        }
+      } else {
+        const int rel = n - D;
+        const int h = rel / (R2 > 0 ? R2 : 1);
+        const int jj = (rel - h * R2) >> 1, comp = rel & 1;
+        const bool colok = rel < NR;
+        const int p = colok ? load_pair(a.pair_idx, h * r + jj, half) : 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float v = acc[i][j][e];
+          float partner = shfl_xor(v, 1);
+          int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          if (m < M && colok) {
+            int pos;
+            size_t row = (size_t)cache_row(a, m, &pos);
+            float cs = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
+            float x0 = comp ? partner : v, x1 = comp ? v : partner;
+            float o = comp ? (x0 * sn + x1 * cs) : (x0 * cs - x1 * sn);
+            ((bf16*)a.krope)[row * NR + rel] = (bf16)o;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ standalone int4 quantiser
+__global__ __launch_bounds__(256) void quantize_int4_kernel(const float* in, int64_t n_groups, uint8_t* codes,
+                                                            uint16_t* scales) {
+  int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= n_groups) return;
+  const float* x = in + g * 32;
+  float v[32];
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] = x[i];
+    am = fmaxf(am, fabsf(v[i]));
+  }
+  __half s = int4_scale(am);
+  float sf = __half2float(s);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    int c0 = int4_code(v[2 * i], sf), c1 = int4_code(v[2 * i + 1], sf);
+    codes[g * 16 + i] = (uint8_t)((c0 & 15) | ((c1 & 15) << 4));
+  }
+  scales[g] = __half_as_ushort(s);
+}
+
+}  // namespace
+
+bool append_uses_mfma(const Shape& s) {
+  return s.dtype == 1 && s.d_model % TK == 0 && s.d_kv % 32 == 0;
+}
+
+bool append_fits(const Shape& s) {
+  return append_uses_mfma(s) || (size_t)(s.d_model + s.d_kv + s.n_rope_cols()) * sizeof(float) <= 65536;
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
+  const int M = a.batch * a.t_new;
+  const int N = a.s.d_kv + a.s.n_rope_cols();
+  if (append_uses_mfma(a.s)) {
+    int grid = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
+    hipLaunchKernelGGL(append_mfma_bf16, dim3(grid), dim3(256), 0, st, a);
+  } else {
+    size_t shmem = (size_t)(a.s.d_model + N) * sizeof(float);
+    if (a.s.dtype == 0)
+      hipLaunchKernelGGL(append_generic<float>, dim3(M), dim3(256), shmem, st, a);
+    else
+      hipLaunchKernelGGL(append_generic<bf16>, dim3(M), dim3(256), shmem, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_int4(const float* in, int64_t n_groups, uint8_t* codes, uint16_t* scales, hipStream_t st) {
+  int64_t blocks = (n_groups + 255) / 256;
+  hipLaunchKernelGGL(quantize_int4_kernel, dim3((unsigned)blocks), dim3(256), 0, st, in, n_groups, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,81 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the gfx950 kernels.
+// Everything here is validated by the caller; launchers only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct Shape {
+  int d_model, n_heads, d_head, r_pairs, d_kv;
+  int dtype;  // 0 f32, 1 bf16
+  int fmt;    // 0 dense, 1 int4 g32
+  __host__ __device__ int r2() const { return 2 * r_pairs; }
+  __host__ __device__ int d_nope() const { return d_head - 2 * r_pairs; }
+  __host__ __device__ int n_rope_cols() const { return n_heads * 2 * r_pairs; }
+};
+
+struct AppendArgs {
+  Shape s;
+  const void *x, *w_dkv, *w_krope;
+  const int32_t* pair_idx;
+  const float *rope_cos, *rope_sin;
+  const int32_t* start_pos;
+  int batch, t_new, max_start, t_max;
+  void *ckv, *ckv_scale, *krope;
+};
+
+// Decode split plan: every sequence's positions [0, max_seq_len) are cut into n_splits chunks.
+struct DecodePlan {
+  int chunk;     // tokens per split (multiple of 64)
+  int n_splits;  // ceil(max_seq_len / chunk), >= 1
+  size_t off_qt, off_qr, off_ml, off_o, total;
+};
+DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len);
+
+struct DecodeArgs {
+  Shape s;
+  const void *q, *w_uk, *w_uv;
+  const int32_t* pair_idx;
+  const float *rope_cos, *rope_sin;
+  const void *ckv, *ckv_scale, *krope;
+  int batch, t_max, max_seq_len;
+  const int32_t* seq_lens;
+  void* out;
+  char* ws;
+  DecodePlan plan;
+};
+
+struct PrefillPlan {
+  size_t off_k, off_vt, off_q, total;
+};
+PrefillPlan plan_prefill(const Shape& s, int batch, int seq_len);
+
+struct PrefillArgs {
+  Shape s;
+  const void *q, *w_uk, *w_uv;
+  const int32_t* pair_idx;
+  const float *rope_cos, *rope_sin;
+  const void *ckv, *krope;
+  int batch, t_max, seq_len;
+  void* out;
+  char* ws;
+  PrefillPlan plan;
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_quantize_int4(const float* in, int64_t n_groups, uint8_t* codes, uint16_t* scales, hipStream_t st);
+
+// Shape predicates for the specialised paths (host side, used for dispatch and tests).
+bool append_uses_mfma(const Shape& s);
+bool decode_uses_mfma(const Shape& s);
+bool prefill_supported(const Shape& s);
+// Dynamic LDS of the generic kernels fits the 64 KiB a launch may request.
+bool append_fits(const Shape& s);
+bool decode_fits(const Shape& s, const DecodePlan& p);
+
+}  // namespace mla

@@ -1,0 +1,107 @@
+"""Shared setup for the GPU parity tests: seeded inputs (synth), the oracle's conversion and reference
+results (oracle), and the library calls (mla_latent_kv_cache_amd) on identical rounded values."""
+
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+
+import oracle
+import synth
+from synth import FAMILIES
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_l2(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def max_abs(got, ref) -> float:
+    return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - np.asarray(ref, dtype=np.float64)))) if np.size(ref) else 0.0
+
+
+# Tolerances fixed by the benchmark spec for this path.
+BF16_REL, BF16_ABS = 5e-3, 2e-2
+F32_REL = 1e-5
+
+
+def assert_close(got, ref, dtype, what=""):
+    r, a = rel_l2(got, ref), max_abs(got, ref)
+    if dtype == "f32":
+        assert r <= F32_REL, f"{what}: rel-L2 {r:.3e} > {F32_REL}"
+    else:
+        assert r <= BF16_REL and a <= BF16_ABS, f"{what}: rel-L2 {r:.3e} (<= {BF16_REL}), max-abs {a:.3e} (<= {BF16_ABS})"
+    return r, a
+
+
+@functools.lru_cache(maxsize=4)
+def converted_layer(family: str, r: int, d_kv: int, dtype: str):
+    """The oracle's conversion of the family's seeded layer, with every weight rounded to the device dtype
+    (the GPU gets exactly these values; the oracle consumes them upcast to fp64)."""
+    d, n_h, d_h, _ = FAMILIES[family]
+    wq, wk, wv, xc = synth.layer_weights(family)
+    conv = oracle.convert_layer(wq, wk, wv, xc, n_h, d_h, r, d_kv)
+    out = {k: synth.round_to_device(conv[k], dtype) for k in ("w_dkv", "w_krope", "w_uk", "w_uv")}
+    out["pair_idx"] = conv["pair_idx"]
+    out["w_q"] = wq
+    out["sigma"] = conv["sigma"]
+    return out
+
+
+def shape_of(cfg):
+    from mla_latent_kv_cache_amd import LayerShape
+
+    return LayerShape(cfg.d_model, cfg.n_heads, cfg.d_head, cfg.r_pairs, cfg.d_kv, cfg.dtype, cfg.cache_fmt)
+
+
+def torch_dtype(cfg):
+    import torch
+
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def fill_cache_per_sequence(cfg, layer, w, cache, lens, keep_x=()):
+    """Append every sequence's seeded activations (positions 0..L_b-1) one sequence at a time through
+    mla_cache_append on a one-sequence view of the cache.  Returns ({b: x_b} for b in keep_x,
+    {b: last activation row} for every non-empty sequence)."""
+    import torch
+
+    from mla_latent_kv_cache_amd import LatentCache, append
+
+    kept, last = {}, {}
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for b, L in enumerate(lens):
+        L = int(L)
+        if L == 0:
+            continue
+        x = synth.context_x(cfg, b, L)
+        last[b] = x[-1].copy()
+        if b in keep_x:
+            kept[b] = x
+        xt = torch.from_numpy(x.astype(np.float32)).to("cuda").to(torch_dtype(cfg)).reshape(1, L, cfg.d_model)
+        view = LatentCache(cache.shape, cache.ckv[b:b + 1], None if cache.ckv_scale is None else cache.ckv_scale[b:b + 1],
+                           cache.krope[b:b + 1], 1, cache.t_max)
+        append(w, view, xt, zero, 0)
+        del xt
+    torch.cuda.synchronize()
+    return kept, last
+
+
+def oracle_cache(cfg, layer, x):
+    """Oracle cache rows (c_kv fp64, k_rope fp64) of one sequence's activations at positions 0..L-1."""
+    return oracle.append_ref(x, layer["w_dkv"], layer["w_krope"], layer["pair_idx"], np.arange(x.shape[0]),
+                             cfg.d_head, cfg.theta)
+
+
+def decode_query(cfg, layer, x_last):
+    """Raw query of the decode token (the sequence's last token), rounded to the device dtype."""
+    return synth.query_rows(x_last[None, :], layer["w_q"], cfg.dtype).reshape(cfg.n_heads, cfg.d_head)

@@ -1,0 +1,164 @@
+"""Host-only checks of the C ABI: the library loads, exports every function include/mla.h declares, sizes
+workspaces, and rejects bad arguments before enqueueing anything (no GPU needed: every call here fails
+validation, so no kernel is ever launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_latent_kv_cache_amd import _lib
+from mla_latent_kv_cache_amd._lib import MlaCache, MlaConfig, MlaWeights
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, CAPACITY = 0, -1, -2, -3, -4, -5
+FAKE = 0x10000  # a 16-byte aligned, non-null address that is never dereferenced (calls fail first)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*)\s*\*?\s*(mla_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    assert set(names) == set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def cfg(**kw):
+    base = dict(d_model=4096, n_heads=32, d_head=128, r_pairs=4, d_kv=512, dtype=1, cache_fmt=0)
+    base.update(kw)
+    return MlaConfig(**base)
+
+
+def weights(**kw):
+    base = dict(w_dkv=FAKE, w_krope=FAKE, w_uk=FAKE, w_uv=FAKE, pair_idx=FAKE, rope_cos=FAKE, rope_sin=FAKE,
+                rope_len=4096)
+    base.update(kw)
+    return MlaWeights(**base)
+
+
+def cache(**kw):
+    base = dict(ckv=FAKE, ckv_scale=FAKE, krope=FAKE, batch=32, t_max=4096)
+    base.update(kw)
+    return MlaCache(**base)
+
+
+def decode_call(lib, c=None, w=None, k=None, q=FAKE, lens=FAKE, max_len=4096, out=FAKE, ws=FAKE, ws_bytes=None):
+    c = c or cfg()
+    w = w or weights()
+    k = k or cache()
+    if ws_bytes is None:
+        ws_bytes = lib.mla_decode_workspace_bytes(ctypes.byref(c), k.batch, max_len)
+    return lib.mla_decode(ctypes.byref(c), ctypes.byref(w), ctypes.byref(k), q, lens, max_len, out, ws, ws_bytes, None)
+
+
+def test_workspace_sizes(lib):
+    c = cfg()
+    n = lib.mla_decode_workspace_bytes(ctypes.byref(c), 32, 4096)
+    # latent queries + rotated pairs + per-split (m, l) + per-split latent outputs
+    assert n >= 32 * 32 * 512 * 2 + 32 * 32 * 512 * 4
+    assert lib.mla_decode_workspace_bytes(ctypes.byref(c), 64, 4096) > n
+    assert lib.mla_decode_workspace_bytes(ctypes.byref(c), 1, 1 << 20) > lib.mla_decode_workspace_bytes(ctypes.byref(c), 1, 4096)
+    bad = cfg(d_head=7)
+    assert lib.mla_decode_workspace_bytes(ctypes.byref(bad), 32, 4096) == 0
+    assert lib.mla_decode_workspace_bytes(ctypes.byref(c), -1, 4096) == 0
+
+
+@pytest.mark.parametrize(
+    "kw,expected",
+    [
+        (dict(d_head=127), INVALID),
+        (dict(r_pairs=65), INVALID),
+        (dict(r_pairs=-1), INVALID),
+        (dict(d_kv=0), INVALID),
+        (dict(dtype=7), INVALID),
+        (dict(cache_fmt=9), INVALID),
+        (dict(d_head=512, r_pairs=4), UNSUPPORTED),
+        (dict(cache_fmt=1, dtype=0), UNSUPPORTED),
+        (dict(cache_fmt=1, d_kv=48), UNSUPPORTED),
+    ],
+)
+def test_decode_rejects_bad_config(lib, kw, expected):
+    c = cfg(**kw)
+    assert decode_call(lib, c=c, ws_bytes=1 << 40) == expected
+
+
+def test_decode_rejects_bad_pointers_and_sizes(lib):
+    assert decode_call(lib, q=None) == INVALID
+    assert decode_call(lib, lens=None) == INVALID
+    assert decode_call(lib, out=None) == INVALID
+    assert decode_call(lib, q=FAKE + 4) == ALIGN
+    assert decode_call(lib, w=weights(w_uv=None)) == INVALID
+    assert decode_call(lib, w=weights(w_uk=FAKE + 2)) == ALIGN
+    assert decode_call(lib, w=weights(rope_len=0)) == INVALID
+    assert decode_call(lib, k=cache(ckv=None)) == INVALID
+    assert decode_call(lib, k=cache(t_max=0)) == INVALID
+    assert decode_call(lib, max_len=-1) == INVALID
+    assert decode_call(lib, max_len=4097) == CAPACITY  # beyond t_max
+    assert decode_call(lib, k=cache(t_max=8192), w=weights(rope_len=100), max_len=200) == CAPACITY
+    assert decode_call(lib, ws=None) == WORKSPACE
+    c = cfg()
+    need = lib.mla_decode_workspace_bytes(ctypes.byref(c), 32, 4096)
+    assert decode_call(lib, ws_bytes=need - 1) == WORKSPACE
+    assert decode_call(lib, ws=FAKE + 8, ws_bytes=need) == ALIGN
+    # int4 cache needs its scale buffer
+    c4 = cfg(cache_fmt=1)
+    assert decode_call(lib, c=c4, k=cache(ckv_scale=None), ws_bytes=1 << 40) == INVALID
+    # zero batch is a no-op
+    assert decode_call(lib, k=cache(batch=0), q=None, lens=None, out=None) == OK
+
+
+def test_append_checks(lib):
+    c, w, k = cfg(), weights(), cache()
+
+    def call(x=FAKE, sp=FAKE, t_new=1, max_start=4095, c=c, w=w, k=k):
+        return lib.mla_cache_append(ctypes.byref(c), ctypes.byref(w), ctypes.byref(k), x, sp, t_new, max_start, None)
+
+    assert call(t_new=2, max_start=4095) == CAPACITY
+    assert call(x=None) == INVALID
+    assert call(sp=FAKE + 1) == ALIGN
+    assert call(t_new=-1) == INVALID
+    assert call(max_start=-5) == INVALID
+    assert call(w=weights(w_dkv=None)) == INVALID
+    assert call(w=weights(w_krope=None)) == INVALID
+    assert call(t_new=0, x=None, sp=None) == OK
+    # no RoPE pairs: RoPE pointers may be absent
+    c0 = cfg(r_pairs=0)
+    w0 = weights(w_krope=None, pair_idx=None, rope_cos=None, rope_sin=None, rope_len=0)
+    assert call(c=c0, w=w0, x=None) == INVALID  # fails on x, not on the absent RoPE pointers
+
+
+def test_prefill_checks(lib):
+    c, w, k = cfg(), weights(), cache()
+
+    def call(q=FAKE, s=4096, out=FAKE, ws=FAKE, nbytes=1 << 40, c=c, k=k):
+        return lib.mla_prefill(ctypes.byref(c), ctypes.byref(w), ctypes.byref(k), q, s, out, ws, nbytes, None)
+
+    assert call(c=cfg(dtype=0)) == UNSUPPORTED
+    assert call(c=cfg(cache_fmt=1)) == UNSUPPORTED
+    assert call(s=-1) == INVALID
+
+
+def test_quantize_checks(lib):
+    assert lib.mla_quantize_int4(FAKE, -1, FAKE, FAKE, None) == INVALID
+    assert lib.mla_quantize_int4(None, 4, FAKE, FAKE, None) == INVALID
+    assert lib.mla_quantize_int4(FAKE, 4, FAKE + 1, FAKE, None) == ALIGN
+    assert lib.mla_quantize_int4(None, 0, None, None, None) == OK
+
+
+def test_status_strings(lib):
+    for s in range(-6, 1):
+        assert lib.mla_status_string(s)
+    assert lib.mla_status_string(-99) == b"unknown status"

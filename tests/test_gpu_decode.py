@@ -1,0 +1,181 @@
+"""GPU parity of mla_cache_append + mla_decode against the oracle, through the C ABI.
+
+Small cases (seconds of oracle work) span several 32-token tiles, several splits, ragged tails, a
+one-token and an empty sequence, and NaN-filled cache rows past every sequence's length (a kernel that
+read them would return NaN).  Full-size cases check sampled sequences at the task's shapes."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import CONFIGS, scaled
+
+from parity_lib import (assert_close, converted_layer, decode_query, fill_cache_per_sequence, log, max_abs,
+                        oracle_cache, rel_l2, shape_of, torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+
+def _to_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def run_decode_case(cfg, lens, t_max, sample=None, check_cache=True, repeat_bitwise=True):
+    from mla_latent_kv_cache_amd import LatentCache, decode, pack_weights
+
+    log(f"[decode] {cfg.name} family={cfg.family} d_kv={cfg.d_kv} r={cfg.r_pairs} fmt={cfg.cache_fmt} "
+        f"B={len(lens)} lens={list(lens)[:8]} t_max={t_max}")
+    B = len(lens)
+    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    shape = shape_of(cfg)
+    w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
+    cache = LatentCache.allocate(shape, B, t_max, fill=float("nan"))
+    if cache.ckv_scale is not None:
+        cache.ckv_scale.fill_(float("nan"))
+    sample = list(range(B)) if sample is None else list(sample)
+    xs, last = fill_cache_per_sequence(cfg, layer, w, cache, lens, keep_x=sample)
+
+    rng = np.random.default_rng(7)
+    q = np.zeros((B, cfg.n_heads, cfg.d_head))
+    for b in range(B):
+        if b in last:
+            q[b] = decode_query(cfg, layer, last[b])
+        else:
+            q[b] = synth.round_to_device(rng.standard_normal((cfg.n_heads, cfg.d_head)), cfg.dtype)
+    qt = torch.from_numpy(q.astype(np.float32)).to("cuda").to(torch_dtype(cfg))
+    lens_t = torch.tensor(np.asarray(lens, dtype=np.int32), device="cuda")
+    max_len = int(max(lens)) if len(lens) else 0
+    out = decode(w, cache, qt, lens_t, max_len)
+    torch.cuda.synchronize()
+    got = _to_np(out)
+    if repeat_bitwise:
+        out2 = decode(w, cache, qt, lens_t, max_len)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out2), "decode is not bitwise deterministic"
+
+    results = []
+    for b in sample:
+        L = int(lens[b])
+        if L == 0:
+            assert np.all(got[b] == 0.0), "empty sequence must give a zero output row"
+            continue
+        c, kr = oracle_cache(cfg, layer, xs[b])
+        if cfg.cache_fmt == "int4_g32":
+            codes = oracle.unpack_nibbles(cache.ckv[b, :L].cpu().numpy())
+            scales = cache.ckv_scale[b, :L].cpu().numpy()
+            check_int4_cache(c, codes, scales)
+            oc, osc = oracle.quantize_int4_g32(c.astype(np.float32))
+            c_used = oracle.dequant_int4(oc, osc)  # attention over the oracle's own dequantised cache
+        else:
+            c_used = c
+            if check_cache:
+                assert_close(_to_np(cache.ckv[b, :L]), c, cfg.dtype, f"c_kv b={b}")
+        if check_cache and cfg.r_pairs > 0:
+            assert_close(_to_np(cache.krope[b, :L]).reshape(L, cfg.n_heads, -1), kr, cfg.dtype, f"k_rope b={b}")
+        ref = oracle.decode_ref(q[b], c_used, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head, cfg.theta)
+        r, a = assert_close(got[b], ref, cfg.dtype, f"decode out b={b} L={L}")
+        results.append((b, L, r, a))
+        log(f"  b={b} L={L} rel-L2={r:.2e} max-abs={a:.2e}")
+    return results
+
+
+def check_int4_cache(c, codes, scales):
+    """GPU int4 codes against the oracle's codec applied to the oracle's fp32 latent.  The GPU quantises its
+    own fp32 accumulator, which differs from the oracle's latent by accumulation order, so a code may differ
+    only where the oracle's quotient lies within 1e-3 of a rounding boundary (or the absmax itself sits at an
+    fp16 rounding boundary of the scale); every dequantised value stays within half a step of the latent."""
+    c32 = c.astype(np.float32)
+    oc, osc = oracle.quantize_int4_g32(c32)
+    s_gpu = scales.astype(np.float32)
+    assert np.all(np.isfinite(s_gpu))
+    same_scale = s_gpu == osc.astype(np.float32)
+    assert same_scale.mean() > 0.999, f"scales differ in {1 - same_scale.mean():.2e} of groups"
+    g_codes = codes.reshape(codes.shape[0], -1, 32)
+    o_codes = oc.reshape(oc.shape[0], -1, 32)
+    quot = (c32.reshape(c.shape[0], -1, 32) / osc.astype(np.float32)[..., None])
+    near = np.abs(np.abs(quot - np.floor(quot)) - 0.5) < 1e-3
+    diff = (g_codes != o_codes) & same_scale[..., None]
+    assert not np.any(diff & ~near), f"{np.count_nonzero(diff & ~near)} int4 codes differ away from a tie"
+    deq = g_codes.astype(np.float64) * s_gpu[..., None]
+    err = np.abs(deq - c.reshape(deq.shape))
+    bound = s_gpu[..., None] * 0.5 + 1e-6 * np.abs(c.reshape(deq.shape)) + 1e-6
+    assert np.all(err <= bound + s_gpu[..., None] * 1e-3)
+    log(f"  int4: {np.count_nonzero(diff)} tie-adjacent code differences of {diff.size}")
+
+
+# ------------------------------------------------------------------ small cases
+
+def test_tiny_f32_config_exact_shape():
+    """The tiny fp32 configuration as specified: batch 1, context 256."""
+    run_decode_case(CONFIGS[0], [256], 256)
+
+
+def test_tiny_f32_ragged():
+    run_decode_case(CONFIGS[0], [256, 1, 100, 0, 65], 300)
+
+
+def test_tiny_bf16_generic_path():
+    cfg = scaled(CONFIGS[0], dtype="bf16")
+    run_decode_case(cfg, [200, 57, 1], 256)
+
+
+def test_mid_bf16_dkv512_r4():
+    cfg = scaled(CONFIGS[1], family="mid", batch=5)
+    run_decode_case(cfg, [1000, 1, 0, 333, 64], 1024)
+
+
+def test_mid_bf16_dkv256_r2():
+    cfg = scaled(CONFIGS[3], family="mid", batch=4, ctx_range=None)
+    run_decode_case(cfg, [2000, 777, 31, 1500], 2048)
+
+
+def test_mid_int4():
+    cfg = scaled(CONFIGS[4], family="mid", batch=4)
+    run_decode_case(cfg, [1000, 65, 512, 3], 1024)
+
+
+def test_quantize_int4_bit_exact():
+    from mla_latent_kv_cache_amd import quantize_int4
+
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((4096, 32)) * rng.uniform(1e-4, 50, (4096, 1))).astype(np.float32)
+    # exact ties x/s = k + 1/2 with s = 0.25, absmax elements, zero groups, fp16-subnormal scales
+    x[0] = 0
+    x[1, :] = np.float32(0.125) * np.arange(-16, 16, dtype=np.float32) / 2
+    x[1, 0] = np.float32(1.75)
+    x[2] = rng.standard_normal(32).astype(np.float32) * np.float32(1e-6)
+    x[3] = -x[3]
+    x[4] = np.float32(7 * 2.0 ** -20)
+    x[5] = np.float32(1e-9)
+    codes_g, scales_g = quantize_int4(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    codes_o, scales_o = oracle.quantize_int4_g32(x)
+    np.testing.assert_array_equal(scales_g.cpu().numpy().view(np.uint16).reshape(-1),
+                                  scales_o.view(np.uint16).reshape(-1))
+    np.testing.assert_array_equal(codes_g.cpu().numpy(), oracle.pack_nibbles(codes_o))
+
+
+# ------------------------------------------------------------------ full-size sampled cases
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_full_llama_bf16_decode_b32_l4096():
+    cfg = CONFIGS[1]
+    run_decode_case(cfg, synth.seq_lens(cfg), cfg.context, sample=[0, 31], check_cache=True)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_full_llama_longctx_decode():
+    cfg = CONFIGS[3]
+    lens = synth.seq_lens(cfg)
+    run_decode_case(cfg, lens, int(lens.max()), sample=[int(np.argmin(lens)), int(np.argmax(lens))])
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_full_llama_int4_decode_b64_l8192():
+    cfg = CONFIGS[4]
+    run_decode_case(cfg, synth.seq_lens(cfg), cfg.context, sample=[0, 63], repeat_bitwise=False)
