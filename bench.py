@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Throughput of the MHA2MLA latent-cache hot path on one MI355X (gfx950).
+
+One step of the headline workload (Llama-2-7B-shaped layer, bf16, d_kv 512, r 4, batch 32, every
+sequence at context 4096) is one decode step of serving: mla_cache_append of the new token of every
+sequence (position 4095) followed by mla_decode over the 4096 cached tokens.  `value` is the latent-cache
+bytes one decode must read (batch x context x bytes per cache row) divided by the step time.
+
+Timing: inputs are resident in HBM before the timed region; `--warmup` untimed steps, then `--steps`
+timed steps bracketed by device synchronisation and HIP events on the launch stream.  Three independent
+cache copies are used in rotation so that the 256 MB last-level cache cannot serve a step's reads from
+the previous step.  The roofline object times the dominant kernel (the split-K attention launch, phase 2
+of mla_decode) with HIP events around each of its launches in a separate loop.
+
+The cpu_baseline object times the oracle (plain fp64 numpy; the library never uses it) on a bounded
+sample of the same workload on the host's cores.  Secondary workloads (long-context variable-length
+decode, int4-latent decode, causal prefill) are reported in `secondary`.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only c1,c3,c4,c2] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode latent-cache GB/s (% of HBM peak); prefill MFMA TFLOP/s"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure (no sparsity)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", default="c1,c3,c4,c2")
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- workloads
+
+def converted(family, r, d_kv):
+    import synth
+    from mla_latent_kv_cache_amd import convert_layer
+
+    d, n_h, d_h, _ = synth.FAMILIES[family]
+    wq, wk, wv, xc = synth.layer_weights(family)
+    t = time.time()
+    conv = convert_layer(wq, wk, wv, xc, n_h, d_h, r, d_kv)
+    log(f"[bench] converted {family} r={r} d_kv={d_kv} in {time.time() - t:.1f}s")
+    conv["w_q"] = wq
+    return conv
+
+
+def make_decode_workload(cfg, conv, lens, copies, seed):
+    """Weights, `copies` filled caches (through mla_cache_append), the step's new-token activations, queries
+    and one BoundDecode per copy.  Activations are seeded N(0,1) generated on the device."""
+    import torch
+
+    from mla_latent_kv_cache_amd import BoundDecode, LatentCache, LayerShape, append, pack_weights
+
+    shape = LayerShape(cfg.d_model, cfg.n_heads, cfg.d_head, cfg.r_pairs, cfg.d_kv, cfg.dtype, cfg.cache_fmt)
+    B = len(lens)
+    t_max = int(max(lens))
+    w = pack_weights(shape, conv, rope_len=t_max, theta=cfg.theta)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    caches = []
+    for c in range(copies):
+        cache = LatentCache.allocate(shape, B, t_max)
+        for b in range(B):
+            L = int(lens[b])
+            x = torch.randn((1, L, cfg.d_model), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+            view = LatentCache(shape, cache.ckv[b:b + 1], None if cache.ckv_scale is None else cache.ckv_scale[b:b + 1],
+                               cache.krope[b:b + 1], 1, t_max)
+            append(w, view, x, torch.zeros(1, dtype=torch.int32, device="cuda"), 0)
+            del x
+        caches.append(cache)
+    torch.cuda.synchronize()
+    x_new = torch.randn((B, 1, cfg.d_model), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    wq = torch.from_numpy(conv["w_q"].astype(np.float32)).cuda()
+    q = (x_new[:, 0].float() @ wq).to(torch.bfloat16).reshape(B, cfg.n_heads, cfg.d_head).contiguous()
+    del wq
+    lens_t = torch.tensor(np.asarray(lens, dtype=np.int32), device="cuda")
+    start = (lens_t - 1).contiguous()
+    out = torch.empty_like(q)
+    ws = None
+    bound = []
+    for cache in caches:
+        bd = BoundDecode(w, cache, x_new, start, t_max - 1, q, lens_t, t_max, out, ws)
+        ws = bd._keep[-1]
+        bound.append(bd)
+    bytes_per_row = caches[0].nbytes_per_token()
+    return dict(w=w, caches=caches, bound=bound, lens=lens, bytes=int(bytes_per_row * int(np.sum(lens))),
+                bytes_per_row=bytes_per_row)
+
+
+def time_decode(wl, steps, warmup):
+    """Whole-step time (append + decode) and the attention kernel's average launch duration."""
+    import torch
+
+    bound = wl["bound"]
+    n = len(bound)
+    for i in range(warmup):
+        bd = bound[i % n]
+        bd.append()
+        bd.decode()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        bd = bound[i % n]
+        bd.append()
+        bd.decode()
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    # dominant kernel: events around phase 2 only (phases 1 and 3 run untimed around it)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(warmup):
+        bd = bound[i % n]
+        bd.phase(1)
+        bd.phase(2)
+        bd.phase(3)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        bd = bound[i % n]
+        bd.phase(1)
+        evs[i][0].record()
+        bd.phase(2)
+        evs[i][1].record()
+        bd.phase(3)
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return step_ms, k_ms
+
+
+def decode_result(name, cfg, wl, steps, warmup):
+    step_ms, k_ms = time_decode(wl, steps, warmup)
+    gbs = wl["bytes"] / (step_ms * 1e-3) / 1e9
+    kgbs = wl["bytes"] / (k_ms * 1e-3) / 1e9
+    log(f"[bench] {name}: step {step_ms * 1e3:.1f} us -> {gbs:.0f} GB/s; attention kernel {k_ms * 1e3:.1f} us -> "
+        f"{kgbs:.0f} GB/s ({100 * kgbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
+    return dict(step_ms=step_ms, kernel_ms=k_ms, gbs=gbs, kernel_gbs=kgbs, bytes=wl["bytes"])
+
+
+# ---------------------------------------------------------------- cpu baseline
+
+def cpu_baseline(cfg, conv, seconds):
+    """The oracle's cache fill + unabsorbed decode for whole sequences of the workload, on the host."""
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    L = cfg.context
+    w = {k: synth.round_to_device(conv[k], cfg.dtype) for k in ("w_dkv", "w_krope", "w_uk", "w_uv")}
+    done, t_all = 0, 0.0
+    while done < cfg.batch and (t_all < seconds or done == 0):
+        x = synth.context_x(cfg, done, L)
+        q = synth.query_rows(x[-1:], conv["w_q"], cfg.dtype).reshape(cfg.n_heads, cfg.d_head)
+        t = time.perf_counter()
+        c, kr = oracle.append_ref(x, w["w_dkv"], w["w_krope"], conv["pair_idx"], np.arange(L), cfg.d_head, cfg.theta)
+        oracle.decode_ref(q, c, kr, w["w_uk"], w["w_uv"], conv["pair_idx"], cfg.d_head, cfg.theta)
+        t_all += time.perf_counter() - t
+        done += 1
+    row = cfg.d_kv * 2 + cfg.n_heads * 2 * cfg.r_pairs * 2
+    gbs = done * L * row / t_all / 1e9
+    log(f"[bench] cpu oracle: {done} sequence(s) in {t_all:.1f}s -> {gbs:.5f} GB/s on {threads} threads")
+    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {cfg.batch} sequences (context {L}) of the same workload: oracle cache fill "
+                      f"(down-projection + partial RoPE) and unabsorbed decode, fp64, conversion excluded; "
+                      f"{t_all:.1f} s"}
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (decode shards by sequence with no "
+              "exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    from mla_latent_kv_cache_amd import _lib
+
+    _lib.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    only = set(args.only.split(","))
+    C = synth.CONFIGS
+
+    conv_main = converted("llama", 4, 512)
+    cfg1 = C[1]
+    wl1 = make_decode_workload(cfg1, conv_main, synth.seq_lens(cfg1), args.copies, seed=1001)
+    main_res = decode_result("llama_bf16_decode", cfg1, wl1, args.steps, args.warmup)
+    del wl1
+    torch.cuda.empty_cache()
+
+    secondary = {}
+    if "c3" in only:
+        cfg3 = C[3]
+        conv3 = converted("llama", 2, 256)
+        lens3 = synth.seq_lens(cfg3)
+        wl3 = make_decode_workload(cfg3, conv3, lens3, args.copies, seed=1003)
+        r3 = decode_result("llama_bf16_longctx_decode", cfg3, wl3, args.steps, args.warmup)
+        r3.update(lens=[int(v) for v in lens3], hbm_frac=r3["kernel_gbs"] / HBM_PEAK_GBS)
+        secondary["llama_bf16_longctx_decode"] = r3
+        del wl3, conv3
+        torch.cuda.empty_cache()
+    if "c4" in only:
+        cfg4 = C[4]
+        wl4 = make_decode_workload(cfg4, conv_main, synth.seq_lens(cfg4), args.copies, seed=1004)
+        r4 = decode_result("llama_int4_decode", cfg4, wl4, args.steps, args.warmup)
+        r4.update(hbm_frac=r4["kernel_gbs"] / HBM_PEAK_GBS)
+        secondary["llama_int4_decode"] = r4
+        del wl4
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg1, conv_main, args.cpu_seconds)
+
+    kgbs = main_res["kernel_gbs"]
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama_bf16_decode: Llama-2-7B-shaped layer (d_model 4096, 32 heads x 128), r 4 pairs/head, "
+                               "d_kv 512, bf16 latent cache, batch 32, every sequence at context 4096; step = append "
+                               "of the new token + decode",
+                   "batch": 32, "context": 4096, "d_kv": 512, "r_pairs": 4, "cache_bytes_per_step": main_res["bytes"],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_attn_mfma (mla_decode phase 2)",
+                     "kernel_us": round(main_res["kernel_ms"] * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -129,6 +129,17 @@ int mla_decode(const mla_config *cfg, const mla_weights *w, const mla_cache *cac
                const int32_t *seq_lens, int32_t max_seq_len, void *out, void *workspace, size_t ws_bytes,
                hipStream_t stream);
 
+/* The three launches of mla_decode one at a time, for callers that interleave other work between
+ * them or time them separately.  Same arguments as mla_decode; the phases share the workspace and
+ * must run in order 1, 2, 3 on the same stream:
+ *   phase 1  latent query q~ = W_uk,h q_nope and the rotated retained query pairs
+ *   phase 2  split-K attention over the cache (partial max / sum / latent output per split)
+ *   phase 3  merge of the splits and the W_uv,h up-projection into `out`
+ * phase outside 1..3 returns MLA_ERR_INVALID_ARG.                                               */
+int mla_decode_phase(int phase, const mla_config *cfg, const mla_weights *w, const mla_cache *cache,
+                     const void *q, const int32_t *seq_lens, int32_t max_seq_len, void *out, void *workspace,
+                     size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- prefill
  * Causal attention of seq_len query tokens per sequence, at positions 0..seq_len-1, over the
  * cache rows 0..seq_len-1 (append them first).  Unabsorbed form: K_nope and V of every head are

@@ -4,12 +4,14 @@
 """
 
 from .api import (  # noqa: F401
+    BoundDecode,
     LatentCache,
     LayerShape,
     LayerWeights,
     MlaError,
     append,
     decode,
+    decode_phase,
     decode_workspace_bytes,
     pack_weights,
     prefill,

@@ -16,6 +16,7 @@ EXPORTED = [
     "mla_cache_append",
     "mla_decode_workspace_bytes",
     "mla_decode",
+    "mla_decode_phase",
     "mla_prefill_workspace_bytes",
     "mla_prefill",
     "mla_quantize_int4",
@@ -74,6 +75,8 @@ def load():
     lib.mla_decode_workspace_bytes.restype = sz
     lib.mla_decode.argtypes = [C, W, K, P, P, i32, P, P, sz, P]
     lib.mla_decode.restype = ctypes.c_int
+    lib.mla_decode_phase.argtypes = [ctypes.c_int, C, W, K, P, P, i32, P, P, sz, P]
+    lib.mla_decode_phase.restype = ctypes.c_int
     lib.mla_prefill_workspace_bytes.argtypes = [C, i32, i32]
     lib.mla_prefill_workspace_bytes.restype = sz
     lib.mla_prefill.argtypes = [C, W, K, P, i32, P, P, sz, P]

@@ -192,6 +192,16 @@ def decode(w: LayerWeights, cache: LatentCache, q: torch.Tensor, seq_lens: torch
     return out
 
 
+def decode_phase(phase: int, w: LayerWeights, cache: LatentCache, q: torch.Tensor, seq_lens: torch.Tensor,
+                 max_seq_len: int, out: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    """mla_decode_phase: one of the three launches of mla_decode (1 q-prep, 2 attention, 3 combine)."""
+    lib = _lib.load()
+    cfg, cw, cc = w.shape.c(), w.c(), cache.c()
+    _check("mla_decode_phase", lib.mla_decode_phase(phase, ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc),
+                                                    _ptr(q), _ptr(seq_lens), int(max_seq_len), _ptr(out),
+                                                    _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
 def prefill_workspace_bytes(shape: LayerShape, batch: int, seq_len: int) -> int:
     cfg = shape.c()
     return _lib.load().mla_prefill_workspace_bytes(ctypes.byref(cfg), batch, seq_len)
@@ -223,3 +233,32 @@ def quantize_int4(x: torch.Tensor, stream=None):
     scales = torch.empty(x.shape[:-1] + (x.shape[-1] // 32,), dtype=torch.float16, device=x.device)
     _check("mla_quantize_int4", lib.mla_quantize_int4(_ptr(x), n_groups, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
+
+
+class BoundDecode:
+    """A decode step whose C structs are built once: append of the new token(s) followed by the three
+    decode launches, for serving loops and timing where per-call marshalling would dominate."""
+
+    def __init__(self, w: LayerWeights, cache: LatentCache, x_new: torch.Tensor, start_pos: torch.Tensor,
+                 max_start_pos: int, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                 out: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+        self.lib = _lib.load()
+        self.cfg, self.cw, self.cc = w.shape.c(), w.c(), cache.c()
+        nbytes = self.lib.mla_decode_workspace_bytes(ctypes.byref(self.cfg), cache.batch, int(max_seq_len))
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+        self._keep = (w, cache, x_new, start_pos, q, seq_lens, out, workspace)
+        self.args_append = (ctypes.byref(self.cfg), ctypes.byref(self.cw), ctypes.byref(self.cc), _ptr(x_new),
+                            _ptr(start_pos), x_new.shape[1], int(max_start_pos))
+        self.args_decode = (ctypes.byref(self.cfg), ctypes.byref(self.cw), ctypes.byref(self.cc), _ptr(q),
+                            _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(workspace), workspace.numel())
+        self.out = out
+
+    def append(self, stream=None):
+        _check("mla_cache_append", self.lib.mla_cache_append(*self.args_append, _stream(stream)))
+
+    def decode(self, stream=None):
+        _check("mla_decode", self.lib.mla_decode(*self.args_decode, _stream(stream)))
+
+    def phase(self, p: int, stream=None):
+        _check("mla_decode_phase", self.lib.mla_decode_phase(p, *self.args_decode, _stream(stream)))

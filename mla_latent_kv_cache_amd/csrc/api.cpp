@@ -114,9 +114,9 @@ size_t mla_decode_workspace_bytes(const mla_config* cfg, int32_t batch, int32_t 
   return mla::plan_decode(shape_of(cfg), batch, max_seq_len).total;
 }
 
-int mla_decode(const mla_config* cfg, const mla_weights* w, const mla_cache* cache, const void* q,
-               const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace, size_t ws_bytes,
-               hipStream_t stream) {
+static int decode_impl(int phase_mask, const mla_config* cfg, const mla_weights* w, const mla_cache* cache,
+                       const void* q, const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace,
+                       size_t ws_bytes, hipStream_t stream) {
   MLA_TRY(check_config(cfg));
   MLA_TRY(check_weights(cfg, w, false, true));
   MLA_TRY(check_cache(cfg, cache));
@@ -134,7 +134,20 @@ int mla_decode(const mla_config* cfg, const mla_weights* w, const mla_cache* cac
   mla::DecodeArgs a{s, q, w->w_uk, w->w_uv, w->pair_idx, w->rope_cos, w->rope_sin,
                     cache->ckv, cache->ckv_scale, cache->krope, cache->batch, cache->t_max, max_seq_len,
                     seq_lens, out, (char*)workspace, plan};
-  return from_hip(mla::launch_decode(a, stream));
+  return from_hip(mla::launch_decode(a, stream, phase_mask));
+}
+
+int mla_decode(const mla_config* cfg, const mla_weights* w, const mla_cache* cache, const void* q,
+               const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace, size_t ws_bytes,
+               hipStream_t stream) {
+  return decode_impl(7, cfg, w, cache, q, seq_lens, max_seq_len, out, workspace, ws_bytes, stream);
+}
+
+int mla_decode_phase(int phase, const mla_config* cfg, const mla_weights* w, const mla_cache* cache,
+                     const void* q, const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace,
+                     size_t ws_bytes, hipStream_t stream) {
+  if (phase < 1 || phase > 3) return MLA_ERR_INVALID_ARG;
+  return decode_impl(1 << (phase - 1), cfg, w, cache, q, seq_lens, max_seq_len, out, workspace, ws_bytes, stream);
 }
 
 size_t mla_prefill_workspace_bytes(const mla_config* cfg, int32_t batch, int32_t seq_len) {

@@ -19,7 +19,7 @@ namespace mla {
 
 namespace {
 
-constexpr int QB = 8;      // batch rows per qprep workgroup
+constexpr int QB = 16;     // batch rows per qprep workgroup
 constexpr int CB = 8;      // batch rows per combine workgroup
 constexpr int MAX_DH = 256;
 
@@ -29,12 +29,17 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
 }
 
 // ------------------------------------------------------------------ 1. query preparation
+// Workgroup (head h, 64 latent columns, up to QB batch rows): the 4 waves split the NoPE dims, each
+// lane owns one latent column, and the partial sums meet in LDS.  Workgroups with blockIdx.y == 0
+// also rotate the retained query pairs.
 template <typename T>
 __global__ __launch_bounds__(256) void decode_qprep(DecodeArgs a) {
-  const int h = blockIdx.x, b0 = blockIdx.y * QB;
+  const int h = blockIdx.x, k = blockIdx.y * 64 + (threadIdx.x & 63), b0 = blockIdx.z * QB;
+  const int ty = threadIdx.x >> 6;
   const int D = a.s.d_kv, dh = a.s.d_head, r = a.s.r_pairs, dn = a.s.d_nope(), half = dh / 2, NH = a.s.n_heads;
   __shared__ int nope_idx[MAX_DH];
-  __shared__ float qn[QB][MAX_DH];
+  __shared__ float qn[MAX_DH][QB];
+  __shared__ float red[4][QB][64];
   if (threadIdx.x == 0) {
     int n = 0;
     for (int i = 0; i < half; ++i) {
@@ -50,25 +55,44 @@ __global__ __launch_bounds__(256) void decode_qprep(DecodeArgs a) {
   const T* q = (const T*)a.q;
   for (int idx = threadIdx.x; idx < QB * dn; idx += blockDim.x) {
     int bb = idx / dn, i = idx - bb * dn, b = b0 + bb;
-    qn[bb][i] = b < a.batch ? to_f32(q[((size_t)b * NH + h) * dh + nope_idx[i]]) : 0.f;
+    qn[i][bb] = b < a.batch ? to_f32(q[((size_t)b * NH + h) * dh + nope_idx[i]]) : 0.f;
   }
   __syncthreads();
-  const float scale = kLog2e / sqrtf((float)dh);
-  const T* wuk = (const T*)a.w_uk + (size_t)h * dn * D;
-  T* qt = (T*)(a.ws + a.plan.off_qt);
-  for (int k = threadIdx.x; k < D; k += blockDim.x) {
-    float acc[QB];
+  float acc[QB];
 #pragma unroll
-    for (int bb = 0; bb < QB; ++bb) acc[bb] = 0.f;
-    for (int i = 0; i < dn; ++i) {
-      float wv = to_f32(wuk[(size_t)i * D + k]);
+  for (int bb = 0; bb < QB; ++bb) acc[bb] = 0.f;
+  const int per = (dn + 3) / 4, i0 = ty * per, i1 = min(dn, i0 + per);
+  const T* wuk = (const T*)a.w_uk + (size_t)h * dn * D + k;
+  if (k < D) {
+    int i = i0;
+    for (; i + 4 <= i1; i += 4) {
+      float wv[4];
 #pragma unroll
-      for (int bb = 0; bb < QB; ++bb) acc[bb] = fmaf(wv, qn[bb][i], acc[bb]);
+      for (int u = 0; u < 4; ++u) wv[u] = to_f32(wuk[(size_t)(i + u) * D]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int bb = 0; bb < QB; ++bb) acc[bb] = fmaf(wv[u], qn[i + u][bb], acc[bb]);
     }
+    for (; i < i1; ++i) {
+      float wv = to_f32(wuk[(size_t)i * D]);
 #pragma unroll
-    for (int bb = 0; bb < QB; ++bb)
-      if (b0 + bb < a.batch) qt[((size_t)(b0 + bb) * NH + h) * D + k] = from_f32<T>(acc[bb] * scale);
+      for (int bb = 0; bb < QB; ++bb) acc[bb] = fmaf(wv, qn[i][bb], acc[bb]);
+    }
   }
+#pragma unroll
+  for (int bb = 0; bb < QB; ++bb) red[ty][bb][threadIdx.x & 63] = acc[bb];
+  __syncthreads();
+  const float scale = kLog2e / sqrtf((float)dh);
+  T* qt = (T*)(a.ws + a.plan.off_qt);
+  for (int idx = threadIdx.x; idx < QB * 64; idx += blockDim.x) {
+    int bb = idx >> 6, kk = idx & 63, b = b0 + bb, kc = blockIdx.y * 64 + kk;
+    if (b < a.batch && kc < D) {
+      float v = red[0][bb][kk] + red[1][bb][kk] + red[2][bb][kk] + red[3][bb][kk];
+      qt[((size_t)b * NH + h) * D + kc] = from_f32<T>(v * scale);
+    }
+  }
+  if (blockIdx.y != 0) return;
   float* qr = (float*)(a.ws + a.plan.off_qr);
   for (int idx = threadIdx.x; idx < QB * r; idx += blockDim.x) {
     int bb = idx / r, j = idx - bb * r, b = b0 + bb;
@@ -374,6 +398,9 @@ __global__ __launch_bounds__(256, 2) void decode_attn_mfma(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ 3. combine + W_uv
+// Workgroup (head h, CB batch rows).  Merge weights per (row, split) from the split maxima, the merged
+// normalised latent output of every row in LDS, then out = o . W_uv,h^T with each thread pair sharing
+// one output dim (16-byte weight loads, halves of the latent width, one shuffle).
 template <typename T>
 __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
   const int h = blockIdx.x, b0 = blockIdx.y * CB;
@@ -384,7 +411,6 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
   __shared__ float inv_den[CB];
   const float* ml = (const float*)(a.ws + a.plan.off_ml);
   const float* po = (const float*)(a.ws + a.plan.off_o);
-  // merge weights per (row, split): exp2(m_s - M); denominator sum_s w_s l_s
   if (threadIdx.x < CB) {
     int bb = threadIdx.x, b = b0 + bb;
     float den = 0.f;
@@ -403,31 +429,62 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
     inv_den[bb] = den > 0.f ? 1.f / den : 0.f;
   }
   __syncthreads();
+  const size_t sstride = (size_t)NH * D;
   for (int idx = threadIdx.x; idx < CB * D; idx += blockDim.x) {
     int bb = idx / D, k = idx - bb * D, b = b0 + bb;
     float o = 0.f;
-    if (b < a.batch)
-      for (int s = 0; s < S; ++s) o = fmaf(wts[bb * S + s], po[(((size_t)b * S + s) * NH + h) * D + k], o);
+    if (b < a.batch) {
+      const float* p = po + ((size_t)b * S * NH + h) * D + k;
+      const float* wr = wts + bb * S;
+      int s = 0;
+      for (; s + 4 <= S; s += 4) {
+        float v0 = p[(size_t)s * sstride], v1 = p[(size_t)(s + 1) * sstride];
+        float v2 = p[(size_t)(s + 2) * sstride], v3 = p[(size_t)(s + 3) * sstride];
+        o = fmaf(wr[s], v0, o);
+        o = fmaf(wr[s + 1], v1, o);
+        o = fmaf(wr[s + 2], v2, o);
+        o = fmaf(wr[s + 3], v3, o);
+      }
+      for (; s < S; ++s) o = fmaf(wr[s], p[(size_t)s * sstride], o);
+    }
     ob[idx] = o * inv_den[bb];
   }
   __syncthreads();
   const T* wuv = (const T*)a.w_uv + (size_t)h * dh * D;
   T* out = (T*)a.out;
-  const int G = blockDim.x >= dh ? blockDim.x / dh : 1;
-  for (int idx = threadIdx.x; idx < G * dh; idx += blockDim.x) {
-    int e = idx % dh, g = idx / dh;
+  const int hk = D / 2;
+  for (int e2 = threadIdx.x; e2 < 2 * dh; e2 += blockDim.x) {
+    const int e = e2 >> 1, part = e2 & 1;
+    const int k0 = part * hk, k1 = part ? D : hk;
     float acc[CB];
 #pragma unroll
     for (int bb = 0; bb < CB; ++bb) acc[bb] = 0.f;
     const T* wr = wuv + (size_t)e * D;
-    for (int k = 0; k < D; ++k) {
+    int k = k0;
+    if (sizeof(T) == 2 && (D % 16) == 0) {
+      for (; k + 8 <= k1; k += 8) {
+        bf16x8 wv = *(const bf16x8*)(wr + k);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          float wf = (float)wv[u];
+#pragma unroll
+          for (int bb = 0; bb < CB; ++bb) acc[bb] = fmaf(wf, ob[bb * D + k + u], acc[bb]);
+        }
+      }
+    }
+    for (; k < k1; ++k) {
       float wv = to_f32(wr[k]);
 #pragma unroll
       for (int bb = 0; bb < CB; ++bb) acc[bb] = fmaf(wv, ob[bb * D + k], acc[bb]);
     }
-    for (int bb = g; bb < CB; bb += G) {
-      int b = b0 + bb;
-      if (b < a.batch) out[((size_t)b * NH + h) * dh + e] = from_f32<T>(acc[bb]);
+#pragma unroll
+    for (int bb = 0; bb < CB; ++bb) acc[bb] += __shfl_xor(acc[bb], 1, 64);
+    if (part == 0) {
+#pragma unroll
+      for (int bb = 0; bb < CB; ++bb) {
+        int b = b0 + bb;
+        if (b < a.batch) out[((size_t)b * NH + h) * dh + e] = from_f32<T>(acc[bb]);
+      }
     }
   }
 }
@@ -489,29 +546,35 @@ DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len) {
   return p;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask) {
   const int nh = a.s.n_heads;
-  dim3 gq(nh, (a.batch + QB - 1) / QB);
-  if (a.s.dtype == 0)
-    hipLaunchKernelGGL(decode_qprep<float>, gq, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(decode_qprep<bf16>, gq, dim3(256), 0, st, a);
-  if (decode_uses_mfma(a.s)) {
-    if (a.s.d_kv == 512 && a.s.r_pairs == 4) launch_mfma_attn<128, 8>(a, st);
-    else if (a.s.d_kv == 512 && a.s.r_pairs == 2) launch_mfma_attn<128, 4>(a, st);
-    else if (a.s.d_kv == 256 && a.s.r_pairs == 4) launch_mfma_attn<64, 8>(a, st);
-    else launch_mfma_attn<64, 4>(a, st);
-  } else if (a.s.dtype == 0) {
-    launch_generic_attn<float>(a, st);
-  } else {
-    launch_generic_attn<bf16>(a, st);
+  if (phase_mask & 1) {
+    dim3 gq(nh, (a.s.d_kv + 63) / 64, (a.batch + QB - 1) / QB);
+    if (a.s.dtype == 0)
+      hipLaunchKernelGGL(decode_qprep<float>, gq, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(decode_qprep<bf16>, gq, dim3(256), 0, st, a);
   }
-  size_t shc = (size_t)(CB * a.s.d_kv + CB * a.plan.n_splits) * sizeof(float);
-  dim3 gc(nh, (a.batch + CB - 1) / CB);
-  if (a.s.dtype == 0)
-    hipLaunchKernelGGL(decode_combine<float>, gc, dim3(256), shc, st, a);
-  else
-    hipLaunchKernelGGL(decode_combine<bf16>, gc, dim3(256), shc, st, a);
+  if (phase_mask & 2) {
+    if (decode_uses_mfma(a.s)) {
+      if (a.s.d_kv == 512 && a.s.r_pairs == 4) launch_mfma_attn<128, 8>(a, st);
+      else if (a.s.d_kv == 512 && a.s.r_pairs == 2) launch_mfma_attn<128, 4>(a, st);
+      else if (a.s.d_kv == 256 && a.s.r_pairs == 4) launch_mfma_attn<64, 8>(a, st);
+      else launch_mfma_attn<64, 4>(a, st);
+    } else if (a.s.dtype == 0) {
+      launch_generic_attn<float>(a, st);
+    } else {
+      launch_generic_attn<bf16>(a, st);
+    }
+  }
+  if (phase_mask & 4) {
+    size_t shc = (size_t)(CB * a.s.d_kv + CB * a.plan.n_splits) * sizeof(float);
+    dim3 gc(nh, (a.batch + CB - 1) / CB);
+    if (a.s.dtype == 0)
+      hipLaunchKernelGGL(decode_combine<float>, gc, dim3(256), shc, st, a);
+    else
+      hipLaunchKernelGGL(decode_combine<bf16>, gc, dim3(256), shc, st, a);
+  }
   return hipGetLastError();
 }
 

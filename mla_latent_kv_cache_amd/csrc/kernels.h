@@ -66,7 +66,8 @@ struct PrefillArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+// phase_mask bit 0: q-prep, bit 1: attention, bit 2: combine
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask = 7);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_quantize_int4(const float* in, int64_t n_groups, uint8_t* codes, uint16_t* scales, hipStream_t st);
 
