@@ -216,6 +216,97 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ MFMA path for few tokens (decode steps)
+// M = batch * t_new <= 64 tokens: the GEMM is a weight read.  One workgroup per 32 output columns,
+// 8 waves splitting the model width, MFMA 32x32x16 on up to two 32-token blocks, partial sums reduced
+// in LDS, then the same epilogues as the large path (RoPE pairs, int4 groups of 32 columns).
+constexpr int SM_WAVES = 8, SM_MAXM = 64;
+
+__global__ __launch_bounds__(512, 1) void append_small_bf16(AppendArgs a) {
+  __shared__ float red[SM_WAVES][SM_MAXM][32];
+  __shared__ float fin[SM_MAXM][33];
+  const int K = a.s.d_model, D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR;
+  const int M = a.batch * a.t_new;
+  const int MB = (M + 31) / 32;
+  const int n0 = blockIdx.x * 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int kw = K / SM_WAVES, k0 = w * kw;
+  const bf16* x = (const bf16*)a.x;
+  const int gn = n0 + (lane & 31);
+  const bf16* wrow = gn < D ? (const bf16*)a.w_dkv + (size_t)gn * K : (const bf16*)a.w_krope + (size_t)(gn - D) * K;
+  const bool nok = gn < N;
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  const bf16x8 zero8 = {};
+  for (int k = k0; k < k0 + kw; k += 64) {  // four 16-wide K steps, loads first
+    bf16x8 bv[4], a0[4], a1[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kk = k + 16 * u + 8 * (lane >> 5);
+      const int m0 = lane & 31, m1 = 32 + (lane & 31);
+      bv[u] = nok ? *(const bf16x8*)(wrow + kk) : zero8;
+      a0[u] = m0 < M ? *(const bf16x8*)(x + (size_t)m0 * K + kk) : zero8;
+      a1[u] = (MB > 1 && m1 < M) ? *(const bf16x8*)(x + (size_t)m1 * K + kk) : zero8;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[0] = mfma32(a0[u], bv[u], acc[0]);
+      if (MB > 1) acc[1] = mfma32(a1[u], bv[u], acc[1]);
+    }
+  }
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[w][mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][lane & 31] = acc[mb][e];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < MB * 32 * 32; idx += blockDim.x) {
+    int m = idx >> 5, c = idx & 31;
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < SM_WAVES; ++ww) v += red[ww][m][c];
+    fin[m][c] = v;
+  }
+  __syncthreads();
+  if (n0 < D) {
+    if (a.s.fmt == 0) {
+      for (int idx = threadIdx.x; idx < M * 32; idx += blockDim.x) {
+        int m = idx >> 5, c = idx & 31;
+        int pos;
+        size_t row = (size_t)cache_row(a, m, &pos);
+        ((bf16*)a.ckv)[row * D + n0 + c] = (bf16)fin[m][c];
+      }
+    } else {
+      for (int m = threadIdx.x; m < M; m += blockDim.x) {
+        float am = 0.f;
+        for (int c = 0; c < 32; ++c) am = fmaxf(am, fabsf(fin[m][c]));
+        __half s = int4_scale(am);
+        float sf = __half2float(s);
+        int pos;
+        size_t row = (size_t)cache_row(a, m, &pos);
+        uint8_t* codes = (uint8_t*)a.ckv + row * (D / 2) + n0 / 2;
+        for (int i = 0; i < 16; ++i) {
+          int c0 = int4_code(fin[m][2 * i], sf), c1 = int4_code(fin[m][2 * i + 1], sf);
+          codes[i] = (uint8_t)((c0 & 15) | ((c1 & 15) << 4));
+        }
+        ((__half*)a.ckv_scale)[row * (D / 32) + n0 / 32] = s;
+      }
+    }
+  } else {
+    const int r = a.s.r_pairs, R2 = a.s.r2(), half = a.s.d_head / 2;
+    for (int idx = threadIdx.x; idx < M * 16; idx += blockDim.x) {
+      int m = idx >> 4, cp = 2 * (idx & 15);
+      int rel = n0 + cp - D;
+      if (rel >= NR) continue;
+      int h = rel / R2, jj = (rel - h * R2) >> 1;
+      int p = load_pair(a.pair_idx, h * r + jj, half);
+      int pos;
+      size_t row = (size_t)cache_row(a, m, &pos);
+      float cs = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
+      float x0 = fin[m][cp], x1 = fin[m][cp + 1];
+      ((bf16*)a.krope)[row * NR + rel] = (bf16)(x0 * cs - x1 * sn);
+      ((bf16*)a.krope)[row * NR + rel + 1] = (bf16)(x0 * sn + x1 * cs);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ standalone int4 quantiser
 __global__ __launch_bounds__(256) void quantize_int4_kernel(const float* in, int64_t n_groups, uint8_t* codes,
                                                             uint16_t* scales) {
@@ -252,7 +343,9 @@ bool append_fits(const Shape& s) {
 hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   const int M = a.batch * a.t_new;
   const int N = a.s.d_kv + a.s.n_rope_cols();
-  if (append_uses_mfma(a.s)) {
+  if (append_uses_mfma(a.s) && M <= SM_MAXM && a.s.d_model % (SM_WAVES * 64) == 0) {
+    hipLaunchKernelGGL(append_small_bf16, dim3((N + 31) / 32), dim3(SM_WAVES * 64), 0, st, a);
+  } else if (append_uses_mfma(a.s)) {
     int grid = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
     hipLaunchKernelGGL(append_mfma_bf16, dim3(grid), dim3(256), 0, st, a);
   } else {

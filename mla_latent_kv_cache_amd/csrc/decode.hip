@@ -199,9 +199,10 @@ __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
 //                                                     transpose read, B = P straight from the
 //                                                     score registers (same lane -> head mapping)
 // Lane l owns head l%32 in both products, so the per-head max / sum / rescale stay in registers
-// (one cross-half shuffle).  The next tile's rows and RoPE keys are prefetched into registers.
+// (one cross-half shuffle).  The next tile's rows and RoPE keys are prefetched into registers.  The
+// dense 512-wide variant needs more than 256 registers per lane and runs at one wave per SIMD.
 template <int DW, int R2, int FMT>
-__global__ __launch_bounds__(256, 2) void decode_attn_mfma(DecodeArgs a) {
+__global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_attn_mfma(DecodeArgs a) {
   constexpr int CP = DW + 16;  // LDS row pitch in elements (conflict-free b128 and transpose reads)
   constexpr int NS = DW / 16;  // score k-steps per wave
   constexpr int NB = DW / 32;  // output blocks per wave
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void decode_attn_mfma(DecodeArgs a) {
   // ---- register prefetch of one tile: this wave's latent slice and its share of the RoPE keys
   constexpr int CPR = (FMT == 0) ? DW / 8 : DW / 32;  // 16-byte chunks per row
   constexpr int CCH = 32 * CPR / 64;                  // chunks per lane
-  uint4 creg[CCH];
+  u32x4 creg[CCH];
   uint16_t sreg[CCH];
   typedef bf16 kv_t __attribute__((ext_vector_type(R2)));
   kv_t kreg[4];
@@ -266,13 +267,13 @@ __global__ __launch_bounds__(256, 2) void decode_attn_mfma(DecodeArgs a) {
       int tok = tt + row;
       if (tok < t1) {
         if (FMT == 0) {
-          creg[it] = *(const uint4*)((const bf16*)a.ckv + (rowb + tok) * D + w * DW + 8 * q);
+          creg[it] = *(const u32x4*)((const bf16*)a.ckv + (rowb + tok) * D + w * DW + 8 * q);
         } else {
-          creg[it] = *(const uint4*)((const uint8_t*)a.ckv + (rowb + tok) * (D / 2) + (w * DW + 32 * q) / 2);
+          creg[it] = *(const u32x4*)((const uint8_t*)a.ckv + (rowb + tok) * (D / 2) + (w * DW + 32 * q) / 2);
           sreg[it] = ((const uint16_t*)a.ckv_scale)[(rowb + tok) * (D / 32) + (w * DW) / 32 + q];
         }
       } else {
-        creg[it] = uint4{0u, 0u, 0u, 0u};
+        creg[it] = u32x4{0u, 0u, 0u, 0u};
         sreg[it] = 0;
       }
     }
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void decode_attn_mfma(DecodeArgs a) {
     for (int it = 0; it < CCH; ++it) {
       int c = it * 64 + lane, row = c / CPR, q = c - row * CPR;
       if (FMT == 0) {
-        *(uint4*)&cw[row * CP + 8 * q] = creg[it];
+        *(u32x4*)&cw[row * CP + 8 * q] = creg[it];
       } else {
         float s = __half2float(__ushort_as_half(sreg[it]));
         const uint32_t wd[4] = {creg[it].x, creg[it].y, creg[it].z, creg[it].w};

@@ -179,3 +179,45 @@ def test_full_llama_longctx_decode():
 def test_full_llama_int4_decode_b64_l8192():
     cfg = CONFIGS[4]
     run_decode_case(cfg, synth.seq_lens(cfg), cfg.context, sample=[0, 63], repeat_bitwise=False)
+
+
+@pytest.mark.parametrize("variant", ["bf16", "int4", "f32"])
+def test_step_append_batched_positions(variant):
+    """A decode step's append: one new token per sequence, each at its own position, in one call."""
+    from mla_latent_kv_cache_amd import LatentCache, append, pack_weights
+
+    if variant == "f32":
+        cfg = scaled(CONFIGS[0], batch=4)
+    elif variant == "int4":
+        cfg = scaled(CONFIGS[4], family="mid", batch=4)
+    else:
+        cfg = scaled(CONFIGS[1], family="mid", batch=4)
+    lens = [97, 2, 64, 200]
+    t_max = 256
+    log(f"[step-append] {variant} lens={lens}")
+    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    shape = shape_of(cfg)
+    w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
+    cache = LatentCache.allocate(shape, len(lens), t_max, fill=float("nan"))
+    xs = [synth.context_x(cfg, b, L) for b, L in enumerate(lens)]
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for b, L in enumerate(lens):
+        xt = torch.from_numpy(xs[b][: L - 1].astype(np.float32)).cuda().to(torch_dtype(cfg)).reshape(1, L - 1, -1)
+        view = LatentCache(shape, cache.ckv[b:b + 1], None if cache.ckv_scale is None else cache.ckv_scale[b:b + 1],
+                           cache.krope[b:b + 1], 1, t_max)
+        append(w, view, xt, zero, 0)
+    x_new = np.stack([x[-1] for x in xs])[:, None, :]
+    start = torch.tensor([L - 1 for L in lens], dtype=torch.int32, device="cuda")
+    append(w, cache, torch.from_numpy(x_new.astype(np.float32)).cuda().to(torch_dtype(cfg)).contiguous(), start,
+           max(lens) - 1)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        c, kr = oracle_cache(cfg, layer, xs[b])
+        assert_close(_to_np(cache.krope[b, :L]).reshape(L, cfg.n_heads, -1), kr, cfg.dtype, f"k_rope b={b}")
+        if variant == "int4":
+            check_int4_cache(c, oracle.unpack_nibbles(cache.ckv[b, :L].cpu().numpy()), cache.ckv_scale[b, :L].cpu().numpy())
+        else:
+            assert_close(_to_np(cache.ckv[b, :L]), c, cfg.dtype, f"c_kv b={b}")
+        # rows past the sequence were never written
+        if L < t_max and variant != "int4":
+            assert torch.isnan(cache.ckv[b, L:].float()).all()
