@@ -160,6 +160,51 @@ def decode_result(name, cfg, wl, steps, warmup):
     return dict(step_ms=step_ms, kernel_ms=k_ms, gbs=gbs, kernel_gbs=kgbs, bytes=wl["bytes"])
 
 
+def prefill_result(cfg, conv, steps, warmup):
+    """Causal prefill of the whole prompt: mla_cache_append of every token followed by mla_prefill."""
+    import torch
+
+    from mla_latent_kv_cache_amd import LatentCache, LayerShape, append, pack_weights, prefill, prefill_workspace_bytes
+
+    shape = LayerShape(cfg.d_model, cfg.n_heads, cfg.d_head, cfg.r_pairs, cfg.d_kv, cfg.dtype, cfg.cache_fmt)
+    B, S = cfg.batch, cfg.context
+    w = pack_weights(shape, conv, rope_len=S, theta=cfg.theta)
+    cache = LatentCache.allocate(shape, B, S)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1002)
+    x = torch.randn((B, S, cfg.d_model), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    wq = torch.from_numpy(conv["w_q"].astype(np.float32)).cuda().to(torch.bfloat16)
+    q = (x.reshape(B * S, -1) @ wq).reshape(B, S, cfg.n_heads, cfg.d_head).contiguous()
+    del wq
+    out = torch.empty_like(q)
+    ws = torch.empty(prefill_workspace_bytes(shape, B, S), dtype=torch.uint8, device="cuda")
+    start = torch.zeros(B, dtype=torch.int32, device="cuda")
+
+    def step():
+        append(w, cache, x, start, 0)
+        prefill(w, cache, q, out, ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    flop_append = 2.0 * B * S * cfg.d_model * (cfg.d_kv + cfg.n_heads * 2 * cfg.r_pairs)
+    flop_rec = 2.0 * B * S * cfg.d_kv * cfg.n_heads * (2 * cfg.d_head - 2 * cfg.r_pairs)
+    flop_attn = 4.0 * cfg.d_head * S * (S + 1) / 2 * B * cfg.n_heads
+    total = flop_append + flop_rec + flop_attn
+    tfs = total / (ms * 1e-3) / 1e12
+    log(f"[bench] llama_bf16_prefill: {ms * 1e3:.1f} us per append+prefill -> {tfs:.0f} TFLOP/s "
+        f"({100 * tfs / BF16_PEAK_TFLOPS:.1f}% of bf16 dense peak)")
+    return dict(step_ms=ms, tflops=tfs, mfma_frac=tfs / BF16_PEAK_TFLOPS, flop=total,
+                flop_parts={"append": flop_append, "reconstruction": flop_rec, "attention": flop_attn})
+
+
 # ---------------------------------------------------------------- cpu baseline
 
 def cpu_baseline(cfg, conv, seconds):
@@ -239,6 +284,10 @@ def main():
         r4.update(hbm_frac=r4["kernel_gbs"] / HBM_PEAK_GBS)
         secondary["llama_int4_decode"] = r4
         del wl4
+        torch.cuda.empty_cache()
+
+    if "c2" in only:
+        secondary["llama_bf16_prefill"] = prefill_result(C[2], conv_main, max(2, args.steps // 5), max(1, args.warmup // 5))
         torch.cuda.empty_cache()
 
     cpu = None

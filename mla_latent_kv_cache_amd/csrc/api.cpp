@@ -129,6 +129,8 @@ static int decode_impl(int phase_mask, const mla_config* cfg, const mla_weights*
   const Shape s = shape_of(cfg);
   const mla::DecodePlan plan = mla::plan_decode(s, cache->batch, max_seq_len);
   if (!mla::decode_fits(s, plan)) return MLA_ERR_UNSUPPORTED;
+  // the specialised kernel addresses one sequence's cache rows with 32-bit byte offsets
+  if (mla::decode_uses_mfma(s) && (size_t)cache->t_max * s.d_kv * 2 >= ((size_t)1 << 31)) return MLA_ERR_UNSUPPORTED;
   if (!workspace || ws_bytes < plan.total) return MLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
   mla::DecodeArgs a{s, q, w->w_uk, w->w_uv, w->pair_idx, w->rope_cos, w->rope_sin,

@@ -237,20 +237,32 @@ __global__ __launch_bounds__(512, 1) void append_small_bf16(AppendArgs a) {
   const bool nok = gn < N;
   f32x16 acc[2] = {f32x16{}, f32x16{}};
   const bf16x8 zero8 = {};
-  for (int k = k0; k < k0 + kw; k += 64) {  // four 16-wide K steps, loads first
-    bf16x8 bv[4], a0[4], a1[4];
+  // four 16-wide K steps per stage; the next stage's loads are issued before this stage's MFMAs
+  bf16x8 bv[2][4], a0[2][4], a1[2][4];
+  auto load_stage = [&](int st, int k) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int kk = k + 16 * u + 8 * (lane >> 5);
       const int m0 = lane & 31, m1 = 32 + (lane & 31);
-      bv[u] = nok ? *(const bf16x8*)(wrow + kk) : zero8;
-      a0[u] = m0 < M ? *(const bf16x8*)(x + (size_t)m0 * K + kk) : zero8;
-      a1[u] = (MB > 1 && m1 < M) ? *(const bf16x8*)(x + (size_t)m1 * K + kk) : zero8;
+      bv[st][u] = nok ? *(const bf16x8*)(wrow + kk) : zero8;
+      a0[st][u] = m0 < M ? *(const bf16x8*)(x + (size_t)m0 * K + kk) : zero8;
+      a1[st][u] = (MB > 1 && m1 < M) ? *(const bf16x8*)(x + (size_t)m1 * K + kk) : zero8;
     }
+  };
+  load_stage(0, k0);
+  for (int k = k0; k < k0 + kw; k += 128) {
+    if (k + 64 < k0 + kw) load_stage(1, k + 64);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      acc[0] = mfma32(a0[u], bv[u], acc[0]);
-      if (MB > 1) acc[1] = mfma32(a1[u], bv[u], acc[1]);
+      acc[0] = mfma32(a0[0][u], bv[0][u], acc[0]);
+      if (MB > 1) acc[1] = mfma32(a1[0][u], bv[0][u], acc[1]);
+    }
+    if (k + 64 >= k0 + kw) break;
+    if (k + 128 < k0 + kw) load_stage(0, k + 128);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[0] = mfma32(a0[1][u], bv[1][u], acc[0]);
+      if (MB > 1) acc[1] = mfma32(a1[1][u], bv[1][u], acc[1]);
     }
   }
   for (int mb = 0; mb < MB; ++mb)

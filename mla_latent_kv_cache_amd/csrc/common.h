@@ -57,6 +57,17 @@ __device__ __forceinline__ int load_pair(const int32_t* pair_idx, int i, int hal
   return p < 0 ? 0 : (p >= half ? half - 1 : p);
 }
 
+// Workgroup barrier for LDS data exchanged between waves that does not wait for outstanding global or
+// LDS-DMA loads (__syncthreads would, draining in-flight prefetches).  This wave's own LDS operations
+// complete (lgkmcnt 0) before the barrier; the asm clobbers keep the compiler from moving memory
+// accesses across it.  LDS written by DMA is waited for separately with vmcnt.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Float equivalents of __shfl_xor for a full 64-lane wave.
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 

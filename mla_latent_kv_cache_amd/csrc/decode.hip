@@ -12,6 +12,8 @@
 //   3. combine: merges the splits and applies W_uv,h.
 #include <hip/hip_fp16.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -29,17 +31,19 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
 }
 
 // ------------------------------------------------------------------ 1. query preparation
-// Workgroup (head h, 64 latent columns, up to QB batch rows): the 4 waves split the NoPE dims, each
-// lane owns one latent column, and the partial sums meet in LDS.  Workgroups with blockIdx.y == 0
-// also rotate the retained query pairs.
+// Workgroup (head h, 64 latent columns, up to QB batch rows), 8 waves splitting the NoPE dims: every
+// lane issues all of its W_uk loads at once, accumulates QB rows, and the partial sums meet in LDS.
+// Workgroups with blockIdx.y == 0 also rotate the retained query pairs.
+constexpr int QW = 8, QMAXI = 32;  // waves per workgroup, NoPE dims per wave (d_h - 2r <= 256)
+
 template <typename T>
-__global__ __launch_bounds__(256) void decode_qprep(DecodeArgs a) {
-  const int h = blockIdx.x, k = blockIdx.y * 64 + (threadIdx.x & 63), b0 = blockIdx.z * QB;
+__global__ __launch_bounds__(512) void decode_qprep(DecodeArgs a) {
+  const int h = blockIdx.x, kk = threadIdx.x & 63, k = blockIdx.y * 64 + kk, b0 = blockIdx.z * QB;
   const int ty = threadIdx.x >> 6;
   const int D = a.s.d_kv, dh = a.s.d_head, r = a.s.r_pairs, dn = a.s.d_nope(), half = dh / 2, NH = a.s.n_heads;
   __shared__ int nope_idx[MAX_DH];
-  __shared__ float qn[MAX_DH][QB];
-  __shared__ float red[4][QB][64];
+  __shared__ __attribute__((aligned(16))) float qn[MAX_DH][QB];
+  __shared__ float red[QW][QB][64];
   if (threadIdx.x == 0) {
     int n = 0;
     for (int i = 0; i < half; ++i) {
@@ -57,38 +61,37 @@ __global__ __launch_bounds__(256) void decode_qprep(DecodeArgs a) {
     int bb = idx / dn, i = idx - bb * dn, b = b0 + bb;
     qn[i][bb] = b < a.batch ? to_f32(q[((size_t)b * NH + h) * dh + nope_idx[i]]) : 0.f;
   }
+  const int per = (dn + QW - 1) / QW, i0 = ty * per, i1 = min(dn, i0 + per);
+  const T* wuk = (const T*)a.w_uk + (size_t)h * dn * D + k;
+  float wv[QMAXI];
+#pragma unroll
+  for (int u = 0; u < QMAXI; ++u) wv[u] = (i0 + u < i1 && k < D) ? to_f32(wuk[(size_t)(i0 + u) * D]) : 0.f;
   __syncthreads();
   float acc[QB];
 #pragma unroll
   for (int bb = 0; bb < QB; ++bb) acc[bb] = 0.f;
-  const int per = (dn + 3) / 4, i0 = ty * per, i1 = min(dn, i0 + per);
-  const T* wuk = (const T*)a.w_uk + (size_t)h * dn * D + k;
-  if (k < D) {
-    int i = i0;
-    for (; i + 4 <= i1; i += 4) {
-      float wv[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) wv[u] = to_f32(wuk[(size_t)(i + u) * D]);
+  for (int u = 0; u < QMAXI; ++u) {
+    if (i0 + u >= i1) break;
+    const f32x4* qrow = (const f32x4*)qn[i0 + u];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+    for (int b4 = 0; b4 < QB / 4; ++b4) {
+      f32x4 qq = qrow[b4];
 #pragma unroll
-        for (int bb = 0; bb < QB; ++bb) acc[bb] = fmaf(wv[u], qn[i + u][bb], acc[bb]);
-    }
-    for (; i < i1; ++i) {
-      float wv = to_f32(wuk[(size_t)i * D]);
-#pragma unroll
-      for (int bb = 0; bb < QB; ++bb) acc[bb] = fmaf(wv, qn[i][bb], acc[bb]);
+      for (int c = 0; c < 4; ++c) acc[4 * b4 + c] = fmaf(wv[u], qq[c], acc[4 * b4 + c]);
     }
   }
 #pragma unroll
-  for (int bb = 0; bb < QB; ++bb) red[ty][bb][threadIdx.x & 63] = acc[bb];
+  for (int bb = 0; bb < QB; ++bb) red[ty][bb][kk] = acc[bb];
   __syncthreads();
   const float scale = kLog2e / sqrtf((float)dh);
   T* qt = (T*)(a.ws + a.plan.off_qt);
   for (int idx = threadIdx.x; idx < QB * 64; idx += blockDim.x) {
-    int bb = idx >> 6, kk = idx & 63, b = b0 + bb, kc = blockIdx.y * 64 + kk;
+    int bb = idx >> 6, c = idx & 63, b = b0 + bb, kc = blockIdx.y * 64 + c;
     if (b < a.batch && kc < D) {
-      float v = red[0][bb][kk] + red[1][bb][kk] + red[2][bb][kk] + red[3][bb][kk];
+      float v = 0.f;
+#pragma unroll
+      for (int t = 0; t < QW; ++t) v += red[t][bb][c];
       qt[((size_t)b * NH + h) * D + kc] = from_f32<T>(v * scale);
     }
   }
@@ -252,46 +255,43 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   const bf16* krb = (const bf16*)a.krope + rowb * 32 * R2;
   bf16* cw = cbuf[w];
 
-  // ---- register prefetch of one tile: this wave's latent slice and its share of the RoPE keys
+  // ---- register prefetch, two tiles deep: this wave's latent slice and its share of the RoPE keys
   constexpr int CPR = (FMT == 0) ? DW / 8 : DW / 32;  // 16-byte chunks per row
   constexpr int CCH = 32 * CPR / 64;                  // chunks per lane
-  u32x4 creg[CCH];
-  uint16_t sreg[CCH];
   typedef bf16 kv_t __attribute__((ext_vector_type(R2)));
-  kv_t kreg[4];
+  u32x4 creg[2][CCH];
+  uint16_t sreg[2][CCH];
+  kv_t kreg[2][4];
 
-  auto load_tile = [&](int tt) {
+  auto load_tile = [&](auto bsel, int tt) {
+    constexpr int B = decltype(bsel)::value;
 #pragma unroll
     for (int it = 0; it < CCH; ++it) {
       int c = it * 64 + lane, row = c / CPR, q = c - row * CPR;
-      int tok = tt + row;
-      if (tok < t1) {
-        if (FMT == 0) {
-          creg[it] = *(const u32x4*)((const bf16*)a.ckv + (rowb + tok) * D + w * DW + 8 * q);
-        } else {
-          creg[it] = *(const u32x4*)((const uint8_t*)a.ckv + (rowb + tok) * (D / 2) + (w * DW + 32 * q) / 2);
-          sreg[it] = ((const uint16_t*)a.ckv_scale)[(rowb + tok) * (D / 32) + (w * DW) / 32 + q];
-        }
+      int tok = min(tt + row, t1 - 1);  // rows past the sequence repeat its last row (masked below)
+      if (FMT == 0) {
+        creg[B][it] = *(const u32x4*)((const bf16*)a.ckv + (rowb + tok) * D + w * DW + 8 * q);
       } else {
-        creg[it] = u32x4{0u, 0u, 0u, 0u};
-        sreg[it] = 0;
+        creg[B][it] = *(const u32x4*)((const uint8_t*)a.ckv + (rowb + tok) * (D / 2) + (w * DW + 32 * q) / 2);
+        sreg[B][it] = ((const uint16_t*)a.ckv_scale)[(rowb + tok) * (D / 32) + (w * DW) / 32 + q];
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int tok = tt + 8 * w + 4 * hb + i;
-      kreg[i] = tok < t1 ? *(const kv_t*)(krb + ((size_t)tok * 32 + h) * R2) : kv_t{};
+      int tok = min(tt + 8 * w + 4 * hb + i, t1 - 1);
+      kreg[B][i] = *(const kv_t*)(krb + ((size_t)tok * 32 + h) * R2);
     }
   };
-  auto stage_tile = [&]() {
+  auto stage_tile = [&](auto bsel) {
+    constexpr int B = decltype(bsel)::value;
 #pragma unroll
     for (int it = 0; it < CCH; ++it) {
       int c = it * 64 + lane, row = c / CPR, q = c - row * CPR;
       if (FMT == 0) {
-        *(u32x4*)&cw[row * CP + 8 * q] = creg[it];
+        *(u32x4*)&cw[row * CP + 8 * q] = creg[B][it];
       } else {
-        float s = __half2float(__ushort_as_half(sreg[it]));
-        const uint32_t wd[4] = {creg[it].x, creg[it].y, creg[it].z, creg[it].w};
+        float s = __half2float(__ushort_as_half(sreg[B][it]));
+        const uint32_t wd[4] = {creg[B][it].x, creg[B][it].y, creg[B][it].z, creg[B][it].w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           bf16x8 v;
@@ -303,20 +303,21 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
     }
   };
 
-  load_tile(t0);
   int par = 0;
-  for (int tt = t0; tt < t1; tt += 32, par ^= 1) {
-    stage_tile();
+  // one 32-token tile: stage registers -> LDS, refill them with the tile two ahead, then both products
+  auto step = [&](auto bsel, int tt) {
+    constexpr int B = decltype(bsel)::value;
+    stage_tile(bsel);
     // RoPE term of rows 8w + 4hb + i (result elements 4w + i), taken before the registers refill
     float rt[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < R2; ++c) acc = fmaf(qr[c], (float)kreg[i][c], acc);
+      for (int c = 0; c < R2; ++c) acc = fmaf(qr[c], (float)kreg[B][i][c], acc);
       rt[i] = acc;
     }
-    if (tt + 32 < t1) load_tile(tt + 32);
+    if (tt + 64 < t1) load_tile(bsel, tt + 64);
     __builtin_amdgcn_wave_barrier();
 
     // scores over this wave's latent columns
@@ -345,6 +346,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[4 * e4 + i] = v[i];
     }
+    par ^= 1;
     float mt = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -382,6 +384,15 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
       }
     }
     asm volatile("" ::: "memory");
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  load_tile(B0{}, t0);
+  if (t0 + 32 < t1) load_tile(B1{}, t0 + 32);
+  for (int tt = t0; tt < t1; tt += 64) {
+    step(B0{}, tt);
+    if (tt + 32 < t1) step(B1{}, tt + 32);
   }
 
 #pragma unroll
@@ -398,92 +409,402 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   }
 }
 
-// ------------------------------------------------------------------ 3. combine + W_uv
-// Workgroup (head h, CB batch rows).  Merge weights per (row, split) from the split maxima, the merged
-// normalised latent output of every row in LDS, then out = o . W_uv,h^T with each thread pair sharing
-// one output dim (16-byte weight loads, halves of the latent width, one shuffle).
-template <typename T>
-__global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
-  const int h = blockIdx.x, b0 = blockIdx.y * CB;
-  const int D = a.s.d_kv, dh = a.s.d_head, NH = a.s.n_heads, S = a.plan.n_splits;
-  extern __shared__ float sh[];
-  float* ob = sh;                // [CB][D]
-  float* wts = ob + CB * D;      // [CB][S]
-  __shared__ float inv_den[CB];
-  const float* ml = (const float*)(a.ws + a.plan.off_ml);
-  const float* po = (const float*)(a.ws + a.plan.off_o);
-  if (threadIdx.x < CB) {
-    int bb = threadIdx.x, b = b0 + bb;
-    float den = 0.f;
-    if (b < a.batch) {
-      float M = -INFINITY;
-      for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(((size_t)b * S + s) * NH + h) * 2]);
-      for (int s = 0; s < S; ++s) {
-        float ms = ml[(((size_t)b * S + s) * NH + h) * 2], ls = ml[(((size_t)b * S + s) * NH + h) * 2 + 1];
-        float wv = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
-        wts[bb * S + s] = wv;
-        den += wv * ls;
+// ------------------------------------------------------------------ 2c. attention, dense MFMA path with LDS DMA
+// Same math and lane mapping as 2b, but every tile reaches LDS through global_load_lds_dwordx4 (no
+// staging registers): a ring of three tile slots (separate LDS arrays, so the compiler can tell the
+// slot being read from the slots still being filled), two tiles in flight while the third is used,
+// explicit vmcnt waits.  Each wave moves only what it reads: its latent column slice (rows XOR-swizzled
+// in 16-byte chunks so that both the row reads and the transpose reads are bank-conflict free) and the
+// RoPE keys of its 8 rows of the tile.  Rows past the sequence repeat its last row and are masked.
+template <int DW>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  if (DW == 128) return chunk ^ (((row & 7) << 1) | ((row >> 3) & 1));
+  const int m = row >> 1;
+  return chunk ^ (((m & 3) << 1) | ((m >> 2) & 1));
+}
+// byte offset of element (row, col) inside one wave's slice of a tile
+template <int DW>
+__device__ __forceinline__ int slice_off(int row, int col) {
+  return row * (DW * 2) + 16 * swz<DW>(row, col >> 3) + (col & 7) * 2;
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_addr + 16 * lane (global_load_lds_dwordx4),
+// global address = base (wave-uniform, SGPRs) + voff (per lane, 32-bit).  Written as asm so that the
+// compiler does not guard every later LDS read with a full vmcnt(0) drain: the asm has no output
+// registers, and its completion is awaited explicitly with MLA_WAIT_VMCNT before the slot it fills is
+// read.  (Loads the compiler does not see only make its own vmcnt waits stricter.)
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds_addr)
+      : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// s_waitcnt with only the vector-memory counter constrained (expcnt 7, lgkmcnt 15 = no wait)
+#define MLA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 0xF) | (((n) >> 4) << 14))
+
+// NSLOT tile slots in the DMA ring (2: one tile in flight while one is used; 3: two in flight), NSB
+// buffers for the cross-wave exchange of partial scores (2 saves one barrier per tile).
+template <int DW, int R2, int NSLOT, int NSB>
+__global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a) {
+  constexpr int NS = DW / 16, NB = DW / 32, D = 4 * DW;
+  constexpr int CSL = 32 * DW * 2;       // bytes of one wave's latent slice of a tile
+  constexpr int KSL = 8 * 32 * R2 * 2;   // bytes of one wave's RoPE rows of a tile
+  constexpr int NC = CSL / 1024, NK = KSL / 1024;
+  constexpr int RB = DW * 2;             // bytes per slice row
+  constexpr float kRescale = 8.f;        // log2 headroom before the running max must be raised
+  __shared__ __attribute__((aligned(1024))) char cs0[4 * CSL], cs1[4 * CSL], cs2[NSLOT > 2 ? 4 * CSL : 16];
+  __shared__ __attribute__((aligned(1024))) char ks0[4 * KSL], ks1[4 * KSL], ks2[NSLOT > 2 ? 4 * KSL : 16];
+  __shared__ f32x4 sbuf[NSB][4][4][64];
+
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5, h = lane & 31;
+  const int S = a.plan.n_splits;
+  const int L = clamp_len(a, b);
+  const int t0 = split * a.plan.chunk;
+  const int t1 = min(t0 + a.plan.chunk, L);
+  float* pml = (float*)(a.ws + a.plan.off_ml) + ((size_t)b * S + split) * 32 * 2;
+  float* po = (float*)(a.ws + a.plan.off_o) + ((size_t)b * S + split) * 32 * D;
+
+  if (t0 >= t1) {
+    for (int idx = lane; idx < 32 * DW / 4; idx += 64) {
+      int hh = idx / (DW / 4), c4 = idx - hh * (DW / 4);
+      *(f32x4*)&po[(size_t)hh * D + w * DW + 4 * c4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (w == 0 && lane < 32) {
+      pml[2 * lane] = -INFINITY;
+      pml[2 * lane + 1] = 0.f;
+    }
+    return;
+  }
+
+  // DMA addresses: a wave-uniform tile base (SGPRs) plus per-lane offsets that do not change per tile
+  const size_t rowb = (size_t)b * a.t_max;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const char* cbase = (const char*)a.ckv + (rowb * D + wu * DW) * 2;
+  const char* kseq = (const char*)a.krope + rowb * 32 * R2 * 2;  // this sequence's RoPE rows
+  const char* kbase = kseq + 8 * wu * 32 * R2 * 2;                 // ... from the wave's first row
+  uint32_t coff[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int off = 1024 * j + 16 * lane, row = off / RB;
+    coff[j] = row * (D * 2) + 16 * swz<DW>(row, (off % RB) / 16);
+  }
+  const uint32_t c_lds[3] = {lds_addr_of(cs0) + wu * CSL, lds_addr_of(cs1) + wu * CSL, lds_addr_of(cs2) + wu * CSL};
+  const uint32_t k_lds[3] = {lds_addr_of(ks0) + wu * KSL, lds_addr_of(ks1) + wu * KSL, lds_addr_of(ks2) + wu * KSL};
+  auto issue_slot = [&](auto ssel, int tt) {
+    constexpr int SL = decltype(ssel)::value;
+    if (tt + 32 <= t1) {
+      const char* cb = cbase + (size_t)tt * (D * 2);
+#pragma unroll
+      for (int j = 0; j < NC; ++j) dma16(cb, coff[j], c_lds[SL] + 1024 * j);
+    } else {  // last, partial tile: rows past the sequence repeat its last row (masked later)
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const int off = 1024 * j + 16 * lane, row = off / RB;
+        const int tok = min(tt + row, t1 - 1);
+        dma16(cbase, (uint32_t)(tok * (D * 2) + 16 * swz<DW>(row, (off % RB) / 16)), c_lds[SL] + 1024 * j);
+      }
+    }
+    // the wave's RoPE rows 8w .. 8w+7 of the tile are one contiguous block
+    if (tt + 8 * wu + 8 <= t1) {
+      const char* kb = kbase + (size_t)tt * (32 * R2 * 2);
+#pragma unroll
+      for (int j = 0; j < NK; ++j) dma16(kb, (uint32_t)(1024 * j + 16 * lane), k_lds[SL] + 1024 * j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        const int off = 1024 * j + 16 * lane, tk = off / (64 * R2), within = off % (64 * R2);
+        const int tok = min(tt + 8 * wu + tk, t1 - 1);  // absolute position, >= 0
+        dma16(kseq, (uint32_t)(tok * (64 * R2) + within), k_lds[SL] + 1024 * j);
+      }
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  issue_slot(S0{}, t0);
+  const bf16* qt = (const bf16*)(a.ws + a.plan.off_qt) + ((size_t)b * 32 + h) * D + w * DW + 8 * hb;
+  bf16x8 qv[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) qv[s] = *(const bf16x8*)(qt + 16 * s);
+  float qr[R2];
+  {
+    const float* qrp = (const float*)(a.ws + a.plan.off_qr) + ((size_t)b * 32 + h) * R2;
+#pragma unroll
+    for (int c = 0; c < R2; ++c) qr[c] = qrp[c];
+  }
+  // the query operands (and the first tile) must be complete before the loop: the compiler would
+  // otherwise guard their first use inside the loop with a vmcnt(0) on every iteration
+  MLA_WAIT_VMCNT(0);
+  if (NSLOT > 2 && t0 + 32 < t1) issue_slot(S1{}, t0 + 32);
+
+  f32x16 oacc[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) oacc[i] = f32x16{};
+  // running max per head (log2 domain), raised lazily: p = exp2(s - m_run) may reach 2^kRescale
+  float m_run = -INFINITY, l_run = 0.f;
+  typedef bf16 kv_t __attribute__((ext_vector_type(R2)));
+  int par = 0;
+
+  auto step = [&](auto ssel, int tt) {
+    constexpr int SL = decltype(ssel)::value;
+    char* cs = SL == 0 ? cs0 : (SL == 1 ? cs1 : cs2);
+    char* kss = SL == 0 ? ks0 : (SL == 1 ? ks1 : ks2);
+    constexpr int NX = (SL + NSLOT - 1) % NSLOT;  // slot that receives the tile NSLOT-1 ahead
+    const int ahead = tt + 32 * (NSLOT - 1);
+    if (NSLOT > 2) {
+      // this tile is complete once at most the next tile's loads (NC + NK) are outstanding
+      if (tt + 32 < t1) {
+        MLA_WAIT_VMCNT(NC + NK);
+      } else {
+        MLA_WAIT_VMCNT(0);
       }
     } else {
-      for (int s = 0; s < S; ++s) wts[bb * S + s] = 0.f;
+      MLA_WAIT_VMCNT(0);
     }
-    inv_den[bb] = den > 0.f ? 1.f / den : 0.f;
+    __builtin_amdgcn_wave_barrier();
+    if (ahead < t1) issue_slot(std::integral_constant<int, NX>{}, ahead);
+
+    const char* cw = cs + w * CSL;
+    float rt[4];
+    {
+      const char* kw = kss + w * KSL;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kv_t kk = *(const kv_t*)(kw + ((4 * hb + i) * 32 + h) * R2 * 2);
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < R2; ++c) acc = fmaf(qr[c], (float)kk[c], acc);
+        rt[i] = acc;
+      }
+    }
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      bf16x8 av = *(const bf16x8*)(cw + slice_off<DW>(lane & 31, 16 * s + 8 * hb));
+      sacc = mfma32(av, qv[s], sacc);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (w == j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[4 * j + i] += rt[i];
+      }
+    if (NSB == 1) lds_barrier();  // every wave has read the previous tile's partial scores
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4)
+      sbuf[NSB == 1 ? 0 : par][w][e4][lane] = f32x4{sacc[4 * e4], sacc[4 * e4 + 1], sacc[4 * e4 + 2], sacc[4 * e4 + 3]};
+    lds_barrier();
+    float sc[16];
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int pb_ = NSB == 1 ? 0 : par;
+      f32x4 v = sbuf[pb_][0][e4][lane];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) v += sbuf[pb_][ww][e4][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[4 * e4 + i] = v[i];
+    }
+    par ^= 1;
+    if (tt + 32 > t1) {  // last, partial tile: mask rows past the sequence
+      asm volatile("" ::: "memory");  // keep this a branch (not if-converted into every tile)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (tt + 8 * (e >> 2) + 4 * hb + (e & 3) >= t1) sc[e] = -INFINITY;
+    }
+    float mt = sc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mt = fmaxf(mt, sc[e]);
+    mt = fmaxf(mt, shfl_xor(mt, 32));
+    // raise the running max only when this tile exceeds it by more than the headroom (rare after the
+    // first tile); a raise rescales the latent accumulators of that head
+    const bool raise = mt > m_run + kRescale;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      asm volatile("" ::: "memory");  // keep this a branch (not if-converted into every tile)
+      const float m_new = raise ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) oacc[blk] *= alpha;
+      m_run = m_new;
+    }
+    float p[16], rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
+      rs += p[e];
+    }
+    rs += shfl_xor(rs, 32);
+    l_run += rs;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[c][e] = (bf16)p[8 * c + e];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const int col = blk * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row0 = 16 * c + 4 * hb + ((lane & 15) >> 2);
+        bf16x4 x0 = lds_read_tr16((const bf16*)(cw + slice_off<DW>(row0, col)));
+        bf16x4 x1 = lds_read_tr16((const bf16*)(cw + slice_off<DW>(row0 + 8, col)));
+        oacc[blk] = mfma32(cat(x0, x1), pb[c], oacc[blk]);
+      }
+    }
+  };
+
+  if (NSLOT > 2) {
+    for (int tt = t0; tt < t1; tt += 96) {
+      step(S0{}, tt);
+      if (tt + 32 < t1) step(S1{}, tt + 32);
+      if (tt + 64 < t1) step(S2{}, tt + 64);
+    }
+  } else {
+    for (int tt = t0; tt < t1; tt += 64) {
+      step(S0{}, tt);
+      if (tt + 32 < t1) step(S1{}, tt + 32);
+    }
   }
-  __syncthreads();
-  const size_t sstride = (size_t)NH * D;
+
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      int k = w * DW + blk * 32 + 8 * e4 + 4 * hb;
+      *(f32x4*)&po[(size_t)h * D + k] =
+          f32x4{oacc[blk][4 * e4], oacc[blk][4 * e4 + 1], oacc[blk][4 * e4 + 2], oacc[blk][4 * e4 + 3]};
+    }
+  if (w == 0 && hb == 0) {
+    pml[2 * h] = m_run;
+    pml[2 * h + 1] = l_run;
+  }
+}
+
+// ------------------------------------------------------------------ 3. combine: merge, then W_uv
+// 3a. merge: one wave per (sequence, head).  Weights exp2(m_s - M) from the split maxima, denominator
+//     sum_s w_s l_s, normalised latent output o = sum_s w_s o_s / den into the workspace (fp32).  Each
+//     lane owns KPL latent columns and keeps the loads of four splits in flight.
+template <int KPL>
+__global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int D = a.s.d_kv, NH = a.s.n_heads, S = a.plan.n_splits;
+  if (pair >= a.batch * NH) return;
+  const int b = pair / NH, h = pair - b * NH;
+  const float* ml = (const float*)(a.ws + a.plan.off_ml) + ((size_t)b * S * NH + h) * 2;
+  const float* po = (const float*)(a.ws + a.plan.off_o) + ((size_t)b * S * NH + h) * D;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(size_t)s * NH * 2]);
+  float acc[KPL], den = 0.f;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) acc[i] = 0.f;
+  int s = 0;
+  for (; s + 4 <= S; s += 4) {
+    float wsplit[4], v[4][KPL];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float ms = ml[(size_t)(s + u) * NH * 2], ls = ml[(size_t)(s + u) * NH * 2 + 1];
+      wsplit[u] = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      den = fmaf(wsplit[u], ls, den);
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        const int k = lane + 64 * i;
+        v[u][i] = k < D ? po[(size_t)(s + u) * NH * D + k] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) acc[i] = fmaf(wsplit[u], v[u][i], acc[i]);
+  }
+  for (; s < S; ++s) {
+    const float ms = ml[(size_t)s * NH * 2], ls = ml[(size_t)s * NH * 2 + 1];
+    const float wsv = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+    den = fmaf(wsv, ls, den);
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int k = lane + 64 * i;
+      if (k < D) acc[i] = fmaf(wsv, po[(size_t)s * NH * D + k], acc[i]);
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  float* ob = (float*)(a.ws + a.plan.off_ob) + ((size_t)b * NH + h) * D;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int k = lane + 64 * i;
+    if (k < D) ob[k] = acc[i] * inv;
+  }
+}
+
+// 3b. out[b,h,:] = o[b,h,:] . W_uv,h^T: workgroup (head, CB rows); the rows' merged outputs sit in LDS,
+//     four threads share one output dim (quarters of the latent width, weight loads issued up front).
+constexpr int PQ = 4, PMAX = 16;  // latent quarters; 8-element weight chunks per quarter (d_kv <= 512)
+
+template <typename T>
+__global__ __launch_bounds__(512) void decode_project(DecodeArgs a) {
+  const int h = blockIdx.x, b0 = blockIdx.y * CB;
+  const int D = a.s.d_kv, dh = a.s.d_head, NH = a.s.n_heads;
+  extern __shared__ float sh[];
+  float* ob = sh;  // [CB][D]
+  const float* src = (const float*)(a.ws + a.plan.off_ob);
   for (int idx = threadIdx.x; idx < CB * D; idx += blockDim.x) {
     int bb = idx / D, k = idx - bb * D, b = b0 + bb;
-    float o = 0.f;
-    if (b < a.batch) {
-      const float* p = po + ((size_t)b * S * NH + h) * D + k;
-      const float* wr = wts + bb * S;
-      int s = 0;
-      for (; s + 4 <= S; s += 4) {
-        float v0 = p[(size_t)s * sstride], v1 = p[(size_t)(s + 1) * sstride];
-        float v2 = p[(size_t)(s + 2) * sstride], v3 = p[(size_t)(s + 3) * sstride];
-        o = fmaf(wr[s], v0, o);
-        o = fmaf(wr[s + 1], v1, o);
-        o = fmaf(wr[s + 2], v2, o);
-        o = fmaf(wr[s + 3], v3, o);
-      }
-      for (; s < S; ++s) o = fmaf(wr[s], p[(size_t)s * sstride], o);
-    }
-    ob[idx] = o * inv_den[bb];
+    ob[idx] = b < a.batch ? src[((size_t)b * NH + h) * D + k] : 0.f;
   }
   __syncthreads();
   const T* wuv = (const T*)a.w_uv + (size_t)h * dh * D;
   T* out = (T*)a.out;
-  const int hk = D / 2;
-  for (int e2 = threadIdx.x; e2 < 2 * dh; e2 += blockDim.x) {
-    const int e = e2 >> 1, part = e2 & 1;
-    const int k0 = part * hk, k1 = part ? D : hk;
+  const int qk = (D + PQ - 1) / PQ;
+  const bool vec = sizeof(T) == 2 && (D % (8 * PQ)) == 0 && qk <= 8 * PMAX;
+  for (int e4 = threadIdx.x; e4 < PQ * dh; e4 += blockDim.x) {
+    const int e = e4 / PQ, part = e4 % PQ;
+    const int k0 = part * qk, k1 = min(D, k0 + qk);
+    const T* wr = wuv + (size_t)e * D;
     float acc[CB];
 #pragma unroll
     for (int bb = 0; bb < CB; ++bb) acc[bb] = 0.f;
-    const T* wr = wuv + (size_t)e * D;
-    int k = k0;
-    if (sizeof(T) == 2 && (D % 16) == 0) {
-      for (; k + 8 <= k1; k += 8) {
-        bf16x8 wv = *(const bf16x8*)(wr + k);
+    if (vec) {
+      bf16x8 wv[PMAX];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          float wf = (float)wv[u];
+      for (int c = 0; c < PMAX; ++c) wv[c] = (k0 + 8 * c < k1) ? *(const bf16x8*)((const bf16*)wr + k0 + 8 * c) : bf16x8{};
 #pragma unroll
-          for (int bb = 0; bb < CB; ++bb) acc[bb] = fmaf(wf, ob[bb * D + k + u], acc[bb]);
+      for (int c = 0; c < PMAX; ++c) {
+        if (k0 + 8 * c >= k1) break;
+#pragma unroll
+        for (int bb = 0; bb < CB; ++bb) {
+          const f32x4 o0 = *(const f32x4*)&ob[bb * D + k0 + 8 * c];
+          const f32x4 o1 = *(const f32x4*)&ob[bb * D + k0 + 8 * c + 4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            acc[bb] = fmaf((float)wv[c][u], o0[u], acc[bb]);
+            acc[bb] = fmaf((float)wv[c][4 + u], o1[u], acc[bb]);
+          }
         }
       }
-    }
-    for (; k < k1; ++k) {
-      float wv = to_f32(wr[k]);
+    } else {
+      for (int k = k0; k < k1; ++k) {
+        const float wf = to_f32(wr[k]);
 #pragma unroll
-      for (int bb = 0; bb < CB; ++bb) acc[bb] = fmaf(wv, ob[bb * D + k], acc[bb]);
+        for (int bb = 0; bb < CB; ++bb) acc[bb] = fmaf(wf, ob[bb * D + k], acc[bb]);
+      }
     }
 #pragma unroll
-    for (int bb = 0; bb < CB; ++bb) acc[bb] += __shfl_xor(acc[bb], 1, 64);
+    for (int bb = 0; bb < CB; ++bb) {
+      acc[bb] += __shfl_xor(acc[bb], 1, 64);
+      acc[bb] += __shfl_xor(acc[bb], 2, 64);
+    }
     if (part == 0) {
 #pragma unroll
       for (int bb = 0; bb < CB; ++bb) {
-        int b = b0 + bb;
+        const int b = b0 + bb;
         if (b < a.batch) out[((size_t)b * NH + h) * dh + e] = from_f32<T>(acc[bb]);
       }
     }
@@ -504,7 +825,7 @@ template <int DW, int R2>
 void launch_mfma_attn(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.plan.n_splits, a.batch);
   if (a.s.fmt == 0)
-    hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 0>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_attn_dma<DW, R2, (DW == 128 && R2 == 8) ? 3 : 3, (DW == 128 && R2 == 8) ? 1 : 2>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 1>), grid, dim3(256), 0, st, a);
 }
@@ -517,7 +838,8 @@ bool decode_uses_mfma(const Shape& s) {
 
 bool decode_fits(const Shape& s, const DecodePlan& p) {
   const size_t lim = 65536;
-  if ((size_t)(CB * s.d_kv + CB * p.n_splits) * sizeof(float) > lim) return false;
+  if (s.d_kv > 1024) return false;
+  if ((size_t)CB * s.d_kv * sizeof(float) > lim) return false;
   if (!decode_uses_mfma(s) && (size_t)(s.d_kv + s.r2() + 1 + p.chunk) * sizeof(float) > lim) return false;
   return true;
 }
@@ -526,7 +848,8 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len) {
   DecodePlan p{};
-  const long long target_wg = 512;
+  // one workgroup per CU for the specialised kernels (their LDS ring fills a CU), two otherwise
+  const long long target_wg = (decode_uses_mfma(s) && s.fmt == 0) ? 256 : 512;
   long long per = ((long long)max_seq_len * batch + target_wg - 1) / target_wg;
   int chunk = (int)(((per + 63) / 64) * 64);
   if (chunk < 64) chunk = 64;
@@ -543,6 +866,8 @@ DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len) {
   off = align256(off + (size_t)batch * p.n_splits * s.n_heads * 2 * 4);
   p.off_o = off;
   off = align256(off + (size_t)batch * p.n_splits * s.n_heads * s.d_kv * 4);
+  p.off_ob = off;
+  off = align256(off + (size_t)batch * s.n_heads * s.d_kv * 4);
   p.total = off;
   return p;
 }
@@ -552,9 +877,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask) {
   if (phase_mask & 1) {
     dim3 gq(nh, (a.s.d_kv + 63) / 64, (a.batch + QB - 1) / QB);
     if (a.s.dtype == 0)
-      hipLaunchKernelGGL(decode_qprep<float>, gq, dim3(256), 0, st, a);
+      hipLaunchKernelGGL(decode_qprep<float>, gq, dim3(64 * QW), 0, st, a);
     else
-      hipLaunchKernelGGL(decode_qprep<bf16>, gq, dim3(256), 0, st, a);
+      hipLaunchKernelGGL(decode_qprep<bf16>, gq, dim3(64 * QW), 0, st, a);
   }
   if (phase_mask & 2) {
     if (decode_uses_mfma(a.s)) {
@@ -569,12 +894,18 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask) {
     }
   }
   if (phase_mask & 4) {
-    size_t shc = (size_t)(CB * a.s.d_kv + CB * a.plan.n_splits) * sizeof(float);
-    dim3 gc(nh, (a.batch + CB - 1) / CB);
+    const int pairs = a.batch * nh, gm = (pairs + 3) / 4, kpl = (a.s.d_kv + 63) / 64;
+    if (kpl <= 1) hipLaunchKernelGGL(decode_merge<1>, dim3(gm), dim3(256), 0, st, a);
+    else if (kpl <= 2) hipLaunchKernelGGL(decode_merge<2>, dim3(gm), dim3(256), 0, st, a);
+    else if (kpl <= 4) hipLaunchKernelGGL(decode_merge<4>, dim3(gm), dim3(256), 0, st, a);
+    else if (kpl <= 8) hipLaunchKernelGGL(decode_merge<8>, dim3(gm), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(decode_merge<16>, dim3(gm), dim3(256), 0, st, a);
+    size_t shp = (size_t)CB * a.s.d_kv * sizeof(float);
+    dim3 gp(nh, (a.batch + CB - 1) / CB);
     if (a.s.dtype == 0)
-      hipLaunchKernelGGL(decode_combine<float>, gc, dim3(256), shc, st, a);
+      hipLaunchKernelGGL(decode_project<float>, gp, dim3(512), shp, st, a);
     else
-      hipLaunchKernelGGL(decode_combine<bf16>, gc, dim3(256), shc, st, a);
+      hipLaunchKernelGGL(decode_project<bf16>, gp, dim3(512), shp, st, a);
   }
   return hipGetLastError();
 }

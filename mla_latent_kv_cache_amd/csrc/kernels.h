@@ -31,7 +31,7 @@ struct AppendArgs {
 struct DecodePlan {
   int chunk;     // tokens per split (multiple of 64)
   int n_splits;  // ceil(max_seq_len / chunk), >= 1
-  size_t off_qt, off_qr, off_ml, off_o, total;
+  size_t off_qt, off_qr, off_ml, off_o, off_ob, total;
 };
 DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len);
 

@@ -92,6 +92,8 @@ def fill_cache_per_sequence(cfg, layer, w, cache, lens, keep_x=()):
                            cache.krope[b:b + 1], 1, cache.t_max)
         append(w, view, xt, zero, 0)
         del xt
+        if b % 8 == 7:
+            log(f"    filled {b + 1}/{len(lens)} sequences")
     torch.cuda.synchronize()
     return kept, last
 

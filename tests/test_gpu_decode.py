@@ -131,6 +131,16 @@ def test_mid_bf16_dkv256_r2():
     run_decode_case(cfg, [2000, 777, 31, 1500], 2048)
 
 
+def test_mid_bf16_dkv512_r2():
+    cfg = scaled(CONFIGS[1], family="mid", batch=3, r_pairs=2)
+    run_decode_case(cfg, [700, 33, 96], 768)
+
+
+def test_mid_bf16_dkv256_r4():
+    cfg = scaled(CONFIGS[3], family="mid", batch=3, r_pairs=4, ctx_range=None)
+    run_decode_case(cfg, [129, 1200, 64], 1280)
+
+
 def test_mid_int4():
     cfg = scaled(CONFIGS[4], family="mid", batch=4)
     run_decode_case(cfg, [1000, 65, 512, 3], 1024)
