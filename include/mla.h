@@ -114,6 +114,16 @@ typedef struct {
 int mla_cache_append(const mla_config *cfg, const mla_weights *w, mla_cache *cache, const void *x,
                      const int32_t *start_pos, int32_t t_new, int32_t max_start_pos, hipStream_t stream);
 
+/* The same append with a caller workspace.  For a few tokens (batch * t_new <= 64, the decode-step
+ * case) the down-projection is then split over the model width across many workgroups, with partial
+ * sums in the workspace and a second launch that reduces them and stores the rows; otherwise the call
+ * behaves like mla_cache_append and ignores the workspace.
+ * Workspace: mla_cache_append_workspace_bytes(cfg, batch, t_new) bytes (0: none needed, may be NULL).  */
+size_t mla_cache_append_workspace_bytes(const mla_config *cfg, int32_t batch, int32_t t_new);
+int mla_cache_append_ws(const mla_config *cfg, const mla_weights *w, mla_cache *cache, const void *x,
+                        const int32_t *start_pos, int32_t t_new, int32_t max_start_pos, void *workspace,
+                        size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- decode
  * One query token per sequence attends to its cached tokens (the absorbed form of the
  * key-designs section: W_uk,h folded into the query, W_uv,h applied after the weighted latent sum).

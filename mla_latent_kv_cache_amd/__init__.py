@@ -10,6 +10,8 @@ from .api import (  # noqa: F401
     LayerWeights,
     MlaError,
     append,
+    append_workspace_bytes,
+    append_ws,
     decode,
     decode_phase,
     decode_workspace_bytes,

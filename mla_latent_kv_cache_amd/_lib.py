@@ -14,6 +14,8 @@ MLA_CACHE_DENSE, MLA_CACHE_INT4_G32 = 0, 1
 
 EXPORTED = [
     "mla_cache_append",
+    "mla_cache_append_workspace_bytes",
+    "mla_cache_append_ws",
     "mla_decode_workspace_bytes",
     "mla_decode",
     "mla_decode_phase",
@@ -71,6 +73,10 @@ def load():
     i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.mla_cache_append.argtypes = [C, W, K, P, P, i32, i32, P]
     lib.mla_cache_append.restype = ctypes.c_int
+    lib.mla_cache_append_workspace_bytes.argtypes = [C, i32, i32]
+    lib.mla_cache_append_workspace_bytes.restype = sz
+    lib.mla_cache_append_ws.argtypes = [C, W, K, P, P, i32, i32, P, sz, P]
+    lib.mla_cache_append_ws.restype = ctypes.c_int
     lib.mla_decode_workspace_bytes.argtypes = [C, i32, i32]
     lib.mla_decode_workspace_bytes.restype = sz
     lib.mla_decode.argtypes = [C, W, K, P, P, i32, P, P, sz, P]

@@ -171,6 +171,25 @@ def append(w: LayerWeights, cache: LatentCache, x: torch.Tensor, start_pos: torc
                                                     _ptr(start_pos), t_new, int(max_start_pos), _stream(stream)))
 
 
+def append_workspace_bytes(shape: LayerShape, batch: int, t_new: int) -> int:
+    cfg = shape.c()
+    return _lib.load().mla_cache_append_workspace_bytes(ctypes.byref(cfg), batch, t_new)
+
+
+def append_ws(w: LayerWeights, cache: LatentCache, x: torch.Tensor, start_pos: torch.Tensor, max_start_pos: int,
+              workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """mla_cache_append_ws: the same append, with a workspace that spreads few-token appends over the GPU."""
+    lib = _lib.load()
+    cfg, cw, cc = w.shape.c(), w.c(), cache.c()
+    t_new = x.shape[1]
+    need = lib.mla_cache_append_workspace_bytes(ctypes.byref(cfg), cache.batch, t_new)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check("mla_cache_append_ws", lib.mla_cache_append_ws(
+        ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc), _ptr(x), _ptr(start_pos), t_new, int(max_start_pos),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
 def decode_workspace_bytes(shape: LayerShape, batch: int, max_seq_len: int) -> int:
     cfg = shape.c()
     return _lib.load().mla_decode_workspace_bytes(ctypes.byref(cfg), batch, max_seq_len)
@@ -236,8 +255,9 @@ def quantize_int4(x: torch.Tensor, stream=None):
 
 
 class BoundDecode:
-    """A decode step whose C structs are built once: append of the new token(s) followed by the three
-    decode launches, for serving loops and timing where per-call marshalling would dominate."""
+    """A decode step whose C structs are built once: append of the new token(s) (with its workspace)
+    followed by the three decode launches, for serving loops and timing where per-call marshalling would
+    dominate."""
 
     def __init__(self, w: LayerWeights, cache: LatentCache, x_new: torch.Tensor, start_pos: torch.Tensor,
                  max_start_pos: int, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
@@ -247,15 +267,18 @@ class BoundDecode:
         nbytes = self.lib.mla_decode_workspace_bytes(ctypes.byref(self.cfg), cache.batch, int(max_seq_len))
         if workspace is None:
             workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-        self._keep = (w, cache, x_new, start_pos, q, seq_lens, out, workspace)
+        na = self.lib.mla_cache_append_workspace_bytes(ctypes.byref(self.cfg), cache.batch, x_new.shape[1])
+        append_ws_buf = torch.empty(max(na, 16), dtype=torch.uint8, device=q.device)
+        self._keep = (w, cache, x_new, start_pos, q, seq_lens, out, append_ws_buf, workspace)
         self.args_append = (ctypes.byref(self.cfg), ctypes.byref(self.cw), ctypes.byref(self.cc), _ptr(x_new),
-                            _ptr(start_pos), x_new.shape[1], int(max_start_pos))
+                            _ptr(start_pos), x_new.shape[1], int(max_start_pos), _ptr(append_ws_buf),
+                            append_ws_buf.numel())
         self.args_decode = (ctypes.byref(self.cfg), ctypes.byref(self.cw), ctypes.byref(self.cc), _ptr(q),
                             _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(workspace), workspace.numel())
         self.out = out
 
     def append(self, stream=None):
-        _check("mla_cache_append", self.lib.mla_cache_append(*self.args_append, _stream(stream)))
+        _check("mla_cache_append_ws", self.lib.mla_cache_append_ws(*self.args_append, _stream(stream)))
 
     def decode(self, stream=None):
         _check("mla_decode", self.lib.mla_decode(*self.args_decode, _stream(stream)))

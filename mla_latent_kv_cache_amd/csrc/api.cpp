@@ -91,8 +91,9 @@ const char* mla_status_string(int status) {
   }
 }
 
-int mla_cache_append(const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
-                     const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, hipStream_t stream) {
+static int append_impl(const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
+                       const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, void* workspace,
+                       size_t ws_bytes, bool use_ws, hipStream_t stream) {
   MLA_TRY(check_config(cfg));
   MLA_TRY(check_weights(cfg, w, true, false));
   MLA_TRY(check_cache(cfg, cache));
@@ -102,11 +103,37 @@ int mla_cache_append(const mla_config* cfg, const mla_weights* w, mla_cache* cac
   MLA_TRY(check_ptr(start_pos, true));
   MLA_TRY(check_positions(cfg, w, cache, (long long)max_start_pos + t_new));
   if ((long long)cache->batch * t_new > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
-  if (!mla::append_fits(shape_of(cfg))) return MLA_ERR_UNSUPPORTED;
-  mla::AppendArgs a{shape_of(cfg), x, w->w_dkv, w->w_krope, w->pair_idx, w->rope_cos, w->rope_sin,
+  const Shape s = shape_of(cfg);
+  if (!mla::append_fits(s)) return MLA_ERR_UNSUPPORTED;
+  char* ws = nullptr;
+  if (use_ws) {
+    const size_t need = mla::append_workspace_bytes(s, cache->batch * t_new);
+    if (need > 0) {
+      if (!workspace || ws_bytes < need) return MLA_ERR_WORKSPACE;
+      if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
+      ws = (char*)workspace;
+    }
+  }
+  mla::AppendArgs a{s, x, w->w_dkv, w->w_krope, w->pair_idx, w->rope_cos, w->rope_sin,
                     start_pos, cache->batch, t_new, max_start_pos, cache->t_max,
-                    cache->ckv, cache->ckv_scale, cache->krope};
+                    cache->ckv, cache->ckv_scale, cache->krope, ws};
   return from_hip(mla::launch_append(a, stream));
+}
+
+int mla_cache_append(const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
+                     const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, hipStream_t stream) {
+  return append_impl(cfg, w, cache, x, start_pos, t_new, max_start_pos, nullptr, 0, false, stream);
+}
+
+size_t mla_cache_append_workspace_bytes(const mla_config* cfg, int32_t batch, int32_t t_new) {
+  if (check_config(cfg) != MLA_OK || batch < 0 || t_new < 0) return 0;
+  return mla::append_workspace_bytes(shape_of(cfg), batch * t_new);
+}
+
+int mla_cache_append_ws(const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
+                        const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, void* workspace,
+                        size_t ws_bytes, hipStream_t stream) {
+  return append_impl(cfg, w, cache, x, start_pos, t_new, max_start_pos, workspace, ws_bytes, true, stream);
 }
 
 size_t mla_decode_workspace_bytes(const mla_config* cfg, int32_t batch, int32_t max_seq_len) {

@@ -216,74 +216,16 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ MFMA path for few tokens (decode steps)
-// M = batch * t_new <= 64 tokens: the GEMM is a weight read.  One workgroup per 32 output columns,
-// 8 waves splitting the model width, MFMA 32x32x16 on up to two 32-token blocks, partial sums reduced
-// in LDS, then the same epilogues as the large path (RoPE pairs, int4 groups of 32 columns).
-constexpr int SM_WAVES = 8, SM_MAXM = 64;
-
-__global__ __launch_bounds__(512, 1) void append_small_bf16(AppendArgs a) {
-  __shared__ float red[SM_WAVES][SM_MAXM][32];
-  __shared__ float fin[SM_MAXM][33];
-  const int K = a.s.d_model, D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR;
-  const int M = a.batch * a.t_new;
-  const int MB = (M + 31) / 32;
-  const int n0 = blockIdx.x * 32;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int kw = K / SM_WAVES, k0 = w * kw;
-  const bf16* x = (const bf16*)a.x;
-  const int gn = n0 + (lane & 31);
-  const bf16* wrow = gn < D ? (const bf16*)a.w_dkv + (size_t)gn * K : (const bf16*)a.w_krope + (size_t)(gn - D) * K;
-  const bool nok = gn < N;
-  f32x16 acc[2] = {f32x16{}, f32x16{}};
-  const bf16x8 zero8 = {};
-  // four 16-wide K steps per stage; the next stage's loads are issued before this stage's MFMAs
-  bf16x8 bv[2][4], a0[2][4], a1[2][4];
-  auto load_stage = [&](int st, int k) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int kk = k + 16 * u + 8 * (lane >> 5);
-      const int m0 = lane & 31, m1 = 32 + (lane & 31);
-      bv[st][u] = nok ? *(const bf16x8*)(wrow + kk) : zero8;
-      a0[st][u] = m0 < M ? *(const bf16x8*)(x + (size_t)m0 * K + kk) : zero8;
-      a1[st][u] = (MB > 1 && m1 < M) ? *(const bf16x8*)(x + (size_t)m1 * K + kk) : zero8;
-    }
-  };
-  load_stage(0, k0);
-  for (int k = k0; k < k0 + kw; k += 128) {
-    if (k + 64 < k0 + kw) load_stage(1, k + 64);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc[0] = mfma32(a0[0][u], bv[0][u], acc[0]);
-      if (MB > 1) acc[1] = mfma32(a1[0][u], bv[0][u], acc[1]);
-    }
-    if (k + 64 >= k0 + kw) break;
-    if (k + 128 < k0 + kw) load_stage(0, k + 128);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc[0] = mfma32(a0[1][u], bv[1][u], acc[0]);
-      if (MB > 1) acc[1] = mfma32(a1[1][u], bv[1][u], acc[1]);
-    }
-  }
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) red[w][mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][lane & 31] = acc[mb][e];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < MB * 32 * 32; idx += blockDim.x) {
-    int m = idx >> 5, c = idx & 31;
-    float v = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < SM_WAVES; ++ww) v += red[ww][m][c];
-    fin[m][c] = v;
-  }
-  __syncthreads();
+// Epilogue shared by the few-token paths: fin[m][c] holds output column n0 + c of token m (fp32);
+// rows[m] / poss[m] are the token's cache row and position.
+__device__ __forceinline__ void append_epilogue(const AppendArgs& a, float (*fin)[33], const int* rows,
+                                                const int* poss, int n0, int M) {
+  const int D = a.s.d_kv, NR = a.s.n_rope_cols();
   if (n0 < D) {
     if (a.s.fmt == 0) {
       for (int idx = threadIdx.x; idx < M * 32; idx += blockDim.x) {
         int m = idx >> 5, c = idx & 31;
-        int pos;
-        size_t row = (size_t)cache_row(a, m, &pos);
-        ((bf16*)a.ckv)[row * D + n0 + c] = (bf16)fin[m][c];
+        ((bf16*)a.ckv)[(size_t)rows[m] * D + n0 + c] = (bf16)fin[m][c];
       }
     } else {
       for (int m = threadIdx.x; m < M; m += blockDim.x) {
@@ -291,8 +233,7 @@ __global__ __launch_bounds__(512, 1) void append_small_bf16(AppendArgs a) {
         for (int c = 0; c < 32; ++c) am = fmaxf(am, fabsf(fin[m][c]));
         __half s = int4_scale(am);
         float sf = __half2float(s);
-        int pos;
-        size_t row = (size_t)cache_row(a, m, &pos);
+        const size_t row = (size_t)rows[m];
         uint8_t* codes = (uint8_t*)a.ckv + row * (D / 2) + n0 / 2;
         for (int i = 0; i < 16; ++i) {
           int c0 = int4_code(fin[m][2 * i], sf), c1 = int4_code(fin[m][2 * i + 1], sf);
@@ -309,14 +250,162 @@ __global__ __launch_bounds__(512, 1) void append_small_bf16(AppendArgs a) {
       if (rel >= NR) continue;
       int h = rel / R2, jj = (rel - h * R2) >> 1;
       int p = load_pair(a.pair_idx, h * r + jj, half);
-      int pos;
-      size_t row = (size_t)cache_row(a, m, &pos);
+      const size_t row = (size_t)rows[m];
+      const int pos = poss[m];
       float cs = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
       float x0 = fin[m][cp], x1 = fin[m][cp + 1];
       ((bf16*)a.krope)[row * NR + rel] = (bf16)(x0 * cs - x1 * sn);
       ((bf16*)a.krope)[row * NR + rel + 1] = (bf16)(x0 * sn + x1 * cs);
     }
   }
+}
+
+// ------------------------------------------------------------------ MFMA path for few tokens (decode steps)
+// M = batch * t_new <= 64 tokens: the GEMM is a weight read.  One workgroup per 32 output columns,
+// 8 waves splitting the model width, MFMA 32x32x16 on up to two 32-token blocks, partial sums reduced
+// in LDS, then the same epilogues as the large path (RoPE pairs, int4 groups of 32 columns).
+constexpr int SM_WAVES = 8, SM_MAXM = 64;
+
+__global__ __launch_bounds__(512, 1) void append_small_bf16(AppendArgs a) {
+  __shared__ float red[SM_WAVES][SM_MAXM][32];
+  __shared__ float fin[SM_MAXM][33];
+  __shared__ int rows[SM_MAXM], poss[SM_MAXM];
+  const int K = a.s.d_model, D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR;
+  const int M = a.batch * a.t_new;
+  const int MB = (M + 31) / 32;
+  const int n0 = blockIdx.x * 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int kw = K / SM_WAVES, k0 = w * kw;
+  if (threadIdx.x < M) {  // cache row and position of every token, resolved once
+    int pos;
+    rows[threadIdx.x] = cache_row(a, threadIdx.x, &pos);
+    poss[threadIdx.x] = pos;
+  }
+  const bf16* x = (const bf16*)a.x;
+  const int gn = n0 + (lane & 31);
+  const bf16* wrow = gn < D ? (const bf16*)a.w_dkv + (size_t)gn * K : (const bf16*)a.w_krope + (size_t)(gn - D) * K;
+  const bool nok = gn < N;
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  const bf16x8 zero8 = {};
+  // the wave's slice of the model width in batches of 8 K-steps (128 wide); every load of a batch is
+  // issued before its MFMAs, and the next batch's loads before this batch's MFMAs
+  constexpr int SB = 8;
+  bf16x8 bv[2][SB], a0[2][SB];
+  auto load_batch = [&](int st, int k) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int kk = k + 16 * u + 8 * (lane >> 5);
+      const bool kin = k + 16 * u < k0 + kw;
+      bv[st][u] = (nok && kin) ? *(const bf16x8*)(wrow + kk) : zero8;
+      a0[st][u] = ((lane & 31) < M && kin) ? *(const bf16x8*)(x + (size_t)(lane & 31) * K + kk) : zero8;
+    }
+  };
+  auto mma_batch = [&](int st, int k) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) acc[0] = mfma32(a0[st][u], bv[st][u], acc[0]);
+    if (MB > 1) {  // second block of 32 tokens: its activations are read as they are used
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int kk = k + 16 * u + 8 * (lane >> 5);
+        const int m1 = 32 + (lane & 31);
+        bf16x8 a1 = (m1 < M && k + 16 * u < k0 + kw) ? *(const bf16x8*)(x + (size_t)m1 * K + kk) : zero8;
+        acc[1] = mfma32(a1, bv[st][u], acc[1]);
+      }
+    }
+  };
+  load_batch(0, k0);
+  for (int k = k0; k < k0 + kw; k += 2 * 16 * SB) {
+    if (k + 16 * SB < k0 + kw) load_batch(1, k + 16 * SB);
+    mma_batch(0, k);
+    if (k + 16 * SB >= k0 + kw) break;
+    if (k + 32 * SB < k0 + kw) load_batch(0, k + 32 * SB);
+    mma_batch(1, k + 16 * SB);
+  }
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[w][mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][lane & 31] = acc[mb][e];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < MB * 32 * 32; idx += blockDim.x) {
+    int m = idx >> 5, c = idx & 31;
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < SM_WAVES; ++ww) v += red[ww][m][c];
+    fin[m][c] = v;
+  }
+  __syncthreads();
+  append_epilogue(a, fin, rows, poss, n0, M);
+}
+
+// ------------------------------------------------------------------ few tokens with a workspace
+// Phase 1: workgroup (32 output columns, one of KS slices of the model width); 4 waves split the
+// slice, MFMA 32x32x16 on up to two 32-token blocks, partial sums of the slice -> workspace (fp32,
+// [KS][M][N]).  Phase 2: one workgroup of 1024 threads per 32 columns sums the KS partials (one
+// output element per thread, all KS loads in one round) and runs the epilogue.
+constexpr int KS_MAX = 16;
+
+__global__ __launch_bounds__(256) void append_splitk_bf16(AppendArgs a, int KS) {
+  __shared__ float red[4][SM_MAXM][32];
+  const int K = a.s.d_model, D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR;
+  const int M = a.batch * a.t_new, MB = (M + 31) / 32;
+  const int n0 = blockIdx.x * 32, ks = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int kslice = K / KS, kw = kslice / 4, k0 = ks * kslice + w * kw;
+  const bf16* x = (const bf16*)a.x;
+  const int gn = n0 + (lane & 31);
+  const bf16* wrow = gn < D ? (const bf16*)a.w_dkv + (size_t)gn * K : (const bf16*)a.w_krope + (size_t)(gn - D) * K;
+  const bool nok = gn < N;
+  const bf16x8 zero8 = {};
+  constexpr int SB = 8;  // K steps of 16 per lane issued together (kw <= 128)
+  bf16x8 bv[SB], a0[SB], a1[SB];
+#pragma unroll
+  for (int u = 0; u < SB; ++u) {
+    const int kk = k0 + 16 * u + 8 * (lane >> 5);
+    const bool kin = 16 * u < kw;
+    bv[u] = (nok && kin) ? *(const bf16x8*)(wrow + kk) : zero8;
+    a0[u] = ((lane & 31) < M && kin) ? *(const bf16x8*)(x + (size_t)(lane & 31) * K + kk) : zero8;
+    a1[u] = (MB > 1 && 32 + (lane & 31) < M && kin) ? *(const bf16x8*)(x + (size_t)(32 + (lane & 31)) * K + kk) : zero8;
+  }
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int u = 0; u < SB; ++u) {
+    acc[0] = mfma32(a0[u], bv[u], acc[0]);
+    if (MB > 1) acc[1] = mfma32(a1[u], bv[u], acc[1]);
+  }
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[w][mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][lane & 31] = acc[mb][e];
+  __syncthreads();
+  float* part = (float*)a.ws + (size_t)ks * M * N;
+  for (int idx = threadIdx.x; idx < M * 32; idx += blockDim.x) {
+    const int m = idx >> 5, c = idx & 31;
+    if (n0 + c < N) part[(size_t)m * N + n0 + c] = red[0][m][c] + red[1][m][c] + red[2][m][c] + red[3][m][c];
+  }
+}
+
+__global__ __launch_bounds__(1024) void append_reduce(AppendArgs a, int KS) {
+  __shared__ float fin[SM_MAXM][33];
+  __shared__ int rows[SM_MAXM], poss[SM_MAXM];
+  const int D = a.s.d_kv, N = D + a.s.n_rope_cols();
+  const int M = a.batch * a.t_new;
+  const int n0 = blockIdx.x * 32;
+  if (threadIdx.x < M) {
+    int pos;
+    rows[threadIdx.x] = cache_row(a, threadIdx.x, &pos);
+    poss[threadIdx.x] = pos;
+  }
+  const float* part = (const float*)a.ws;
+  for (int idx = threadIdx.x; idx < M * 32; idx += blockDim.x) {
+    const int m = idx >> 5, c = idx & 31;
+    float v[KS_MAX];
+#pragma unroll
+    for (int ks = 0; ks < KS_MAX; ++ks) v[ks] = (ks < KS && n0 + c < N) ? part[((size_t)ks * M + m) * N + n0 + c] : 0.f;
+    float sum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS_MAX; ++ks) sum += v[ks];
+    fin[m][c] = sum;
+  }
+  __syncthreads();
+  append_epilogue(a, fin, rows, poss, n0, M);
 }
 
 // ------------------------------------------------------------------ standalone int4 quantiser
@@ -348,6 +437,20 @@ bool append_uses_mfma(const Shape& s) {
   return s.dtype == 1 && s.d_model % TK == 0 && s.d_kv % 32 == 0;
 }
 
+int append_ksplit(const Shape& s, int tokens) {
+  if (!append_uses_mfma(s) || tokens > SM_MAXM || tokens <= 0) return 0;
+  // as many model-width slices as possible (<= KS_MAX), each 4 waves x <= 8 K-steps of 16 (<= 512 wide)
+  for (int ks = KS_MAX; ks >= 1; ks /= 2)
+    if (s.d_model % (ks * 64) == 0 && s.d_model / ks <= 512) return ks;
+  return 0;
+}
+
+size_t append_workspace_bytes(const Shape& s, int tokens) {
+  const int ks = append_ksplit(s, tokens);
+  return ks ? (size_t)ks * tokens * (s.d_kv + s.n_rope_cols()) * sizeof(float) : 0;
+}
+
+
 bool append_fits(const Shape& s) {
   return append_uses_mfma(s) || (size_t)(s.d_model + s.d_kv + s.n_rope_cols()) * sizeof(float) <= 65536;
 }
@@ -355,7 +458,11 @@ bool append_fits(const Shape& s) {
 hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   const int M = a.batch * a.t_new;
   const int N = a.s.d_kv + a.s.n_rope_cols();
-  if (append_uses_mfma(a.s) && M <= SM_MAXM && a.s.d_model % (SM_WAVES * 64) == 0) {
+  const int ks = a.ws ? append_ksplit(a.s, M) : 0;
+  if (ks > 0) {
+    hipLaunchKernelGGL(append_splitk_bf16, dim3((N + 31) / 32, ks), dim3(256), 0, st, a, ks);
+    hipLaunchKernelGGL(append_reduce, dim3((N + 31) / 32), dim3(1024), 0, st, a, ks);
+  } else if (append_uses_mfma(a.s) && M <= SM_MAXM && a.s.d_model % (SM_WAVES * 16) == 0) {
     hipLaunchKernelGGL(append_small_bf16, dim3((N + 31) / 32), dim3(SM_WAVES * 64), 0, st, a);
   } else if (append_uses_mfma(a.s)) {
     int grid = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);

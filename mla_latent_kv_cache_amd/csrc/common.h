@@ -68,6 +68,34 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// nope_idx[0 .. d_h-2r) = ascending dims of head h whose pair is not retained, built by the first wave
+// of the workgroup from two 64-bit ballots (d_h/2 <= 128; kept[] is LDS scratch of d_h/2 ints).  The
+// caller synchronises after the call.  Duplicate or out-of-range retained indices cannot push an entry
+// outside [0, d_h).
+__device__ __forceinline__ void build_nope_idx(const int32_t* pair_idx, int h, int r, int half, int* kept,
+                                               int* nope_idx) {
+  for (int i = threadIdx.x; i < half; i += blockDim.x) kept[i] = 0;
+  __syncthreads();
+  for (int j = threadIdx.x; j < r; j += blockDim.x) kept[load_pair(pair_idx, h * r + j, half)] = 1;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    const bool k0 = l < half && kept[l], k1 = 64 + l < half && kept[64 + l];
+    const uint64_t m0 = __builtin_amdgcn_ballot_w64(k0), m1 = __builtin_amdgcn_ballot_w64(k1);
+    const uint64_t below = l ? (~0ull >> (64 - l)) : 0ull;
+    if (l < half && !k0) {
+      const int pos = l - __builtin_popcountll(m0 & below);
+      nope_idx[2 * pos] = 2 * l;
+      nope_idx[2 * pos + 1] = 2 * l + 1;
+    }
+    if (64 + l < half && !k1) {
+      const int pos = 64 + l - __builtin_popcountll(m0) - __builtin_popcountll(m1 & below);
+      nope_idx[2 * pos] = 2 * (64 + l);
+      nope_idx[2 * pos + 1] = 2 * (64 + l) + 1;
+    }
+  }
+}
+
 // Float equivalents of __shfl_xor for a full 64-lane wave.
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 

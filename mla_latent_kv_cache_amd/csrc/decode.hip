@@ -21,8 +21,7 @@ namespace mla {
 
 namespace {
 
-constexpr int QB = 16;     // batch rows per qprep workgroup
-constexpr int CB = 8;      // batch rows per combine workgroup
+constexpr int QB = 16;     // batch rows per qprep workgroup (QB * d_nope <= 4 * 512)
 constexpr int MAX_DH = 256;
 
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
@@ -42,37 +41,40 @@ __global__ __launch_bounds__(512) void decode_qprep(DecodeArgs a) {
   const int ty = threadIdx.x >> 6;
   const int D = a.s.d_kv, dh = a.s.d_head, r = a.s.r_pairs, dn = a.s.d_nope(), half = dh / 2, NH = a.s.n_heads;
   __shared__ int nope_idx[MAX_DH];
+  __shared__ int kept[MAX_DH / 2];
   __shared__ __attribute__((aligned(16))) float qn[MAX_DH][QB];
   __shared__ float red[QW][QB][64];
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int i = 0; i < half; ++i) {
-      bool kept = false;
-      for (int j = 0; j < r; ++j) kept |= (load_pair(a.pair_idx, h * r + j, half) == i);
-      if (!kept) {
-        nope_idx[n++] = 2 * i;
-        nope_idx[n++] = 2 * i + 1;
-      }
-    }
-  }
-  __syncthreads();
-  const T* q = (const T*)a.q;
-  for (int idx = threadIdx.x; idx < QB * dn; idx += blockDim.x) {
-    int bb = idx / dn, i = idx - bb * dn, b = b0 + bb;
-    qn[i][bb] = b < a.batch ? to_f32(q[((size_t)b * NH + h) * dh + nope_idx[i]]) : 0.f;
-  }
+  // this thread's W_uk column over its share of the NoPE dims, loaded first (independent of the rest)
   const int per = (dn + QW - 1) / QW, i0 = ty * per, i1 = min(dn, i0 + per);
-  const T* wuk = (const T*)a.w_uk + (size_t)h * dn * D + k;
+  const T* wuk = (const T*)a.w_uk + (size_t)h * dn * D + min(k, D - 1);
   float wv[QMAXI];
 #pragma unroll
-  for (int u = 0; u < QMAXI; ++u) wv[u] = (i0 + u < i1 && k < D) ? to_f32(wuk[(size_t)(i0 + u) * D]) : 0.f;
+  for (int u = 0; u < QMAXI; ++u) {
+    if (u < per) wv[u] = to_f32(wuk[(size_t)min(i0 + u, dn - 1) * D]);
+  }
+  build_nope_idx(a.pair_idx, h, r, half, kept, nope_idx);
+  __syncthreads();
+  const T* q = (const T*)a.q;
+  {  // gather the NoPE query dims of the QB rows in one round (QB * d_nope <= 4 * blockDim)
+    float g[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = threadIdx.x + u * blockDim.x, bb = idx / max(dn, 1), i = idx - bb * max(dn, 1), b = b0 + bb;
+      g[u] = (idx < QB * dn && b < a.batch) ? to_f32(q[((size_t)b * NH + h) * dh + nope_idx[i]]) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = threadIdx.x + u * blockDim.x, bb = idx / max(dn, 1), i = idx - bb * max(dn, 1);
+      if (idx < QB * dn) qn[i][bb] = g[u];
+    }
+  }
   __syncthreads();
   float acc[QB];
 #pragma unroll
   for (int bb = 0; bb < QB; ++bb) acc[bb] = 0.f;
 #pragma unroll
   for (int u = 0; u < QMAXI; ++u) {
-    if (i0 + u >= i1) break;
+    if (i0 + u >= i1 || k >= D) break;
     const f32x4* qrow = (const f32x4*)qn[i0 + u];
 #pragma unroll
     for (int b4 = 0; b4 < QB / 4; ++b4) {
@@ -107,6 +109,80 @@ __global__ __launch_bounds__(512) void decode_qprep(DecodeArgs a) {
     float c = a.rope_cos[(size_t)pos * half + p], s = a.rope_sin[(size_t)pos * half + p];
     qr[((size_t)b * NH + h) * 2 * r + 2 * j] = (x0 * c - x1 * s) * scale;
     qr[((size_t)b * NH + h) * 2 * r + 2 * j + 1] = (x0 * s + x1 * c) * scale;
+  }
+}
+
+// 1b. query preparation on MFMA (bf16, d_h - 2r <= 128, latent width a multiple of 128).
+// Workgroup (head h, 128 latent columns, 32 sequences); wave w owns 32 of the columns.
+//   q~[b][k] = sum_i q_nope[b][i] W_uk,h[i][k]:  A = gathered NoPE query rows (LDS, rows b),
+//   B = W_uk tile (LDS, rows i, k contiguous) through the transpose read; K = NoPE dims padded to 128.
+__global__ __launch_bounds__(256) void decode_qprep_mfma(DecodeArgs a) {
+  constexpr int WP = 128 + 8;  // LDS pitch of both tiles (elements)
+  __shared__ __attribute__((aligned(16))) bf16 wt[128 * WP];
+  __shared__ __attribute__((aligned(16))) bf16 qa[32 * WP];
+  __shared__ int nope_idx[MAX_DH];
+  __shared__ int kept[MAX_DH / 2];
+  const int h = blockIdx.x, kb = blockIdx.y * 128, b0 = blockIdx.z * 32;
+  const int D = a.s.d_kv, dh = a.s.d_head, r = a.s.r_pairs, dn = a.s.d_nope(), half = dh / 2, NH = a.s.n_heads;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5;
+  // W_uk rows i < dn, columns kb .. kb+127: 16 chunks of 16 bytes per row, issued first
+  const bf16* wuk = (const bf16*)a.w_uk + (size_t)h * dn * D + kb;
+  u32x4 wreg[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int c = u * 256 + tid, row = c >> 4, ch = c & 15;
+    wreg[u] = row < dn ? *(const u32x4*)(wuk + (size_t)row * D + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+  build_nope_idx(a.pair_idx, h, r, half, kept, nope_idx);
+  __syncthreads();
+  const bf16* q = (const bf16*)a.q;
+  bf16 g[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {  // q_nope of 32 rows x 128 padded dims: 16 per thread
+    const int c = u * 256 + tid, bb = c >> 7, i = c & 127, b = b0 + bb;
+    g[u] = (i < dn && b < a.batch) ? q[((size_t)b * NH + h) * dh + nope_idx[i]] : (bf16)0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int c = u * 256 + tid, row = c >> 4, ch = c & 15;
+    *(u32x4*)&wt[row * WP + ch * 8] = wreg[u];
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int c = u * 256 + tid, bb = c >> 7, i = c & 127;
+    qa[bb * WP + i] = g[u];
+  }
+  __syncthreads();
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const bf16x8 av = *(const bf16x8*)&qa[(lane & 31) * WP + 16 * s + 8 * hb];
+    const int col = 32 * w + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int row0 = 16 * s + 8 * hb + ((lane & 15) >> 2);
+    const bf16x4 x0 = lds_read_tr16(&wt[row0 * WP + col]);
+    const bf16x4 x1 = lds_read_tr16(&wt[(row0 + 4) * WP + col]);
+    acc = mfma32(av, cat(x0, x1), acc);
+  }
+  const float scale = kLog2e / sqrtf((float)dh);
+  bf16* qt = (bf16*)(a.ws + a.plan.off_qt);
+  const int k = kb + 32 * w + (lane & 31);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int b = b0 + 8 * (e >> 2) + 4 * hb + (e & 3);
+    if (b < a.batch) qt[((size_t)b * NH + h) * D + k] = (bf16)(acc[e] * scale);
+  }
+  if (blockIdx.y != 0) return;
+  float* qr = (float*)(a.ws + a.plan.off_qr);
+  for (int idx = tid; idx < 32 * r; idx += blockDim.x) {
+    const int bb = idx / r, j = idx - bb * r, b = b0 + bb;
+    if (b >= a.batch) continue;
+    const int L = clamp_len(a, b);
+    const int pos = L > 0 ? L - 1 : 0;
+    const int p = load_pair(a.pair_idx, h * r + j, half);
+    const float x0 = (float)q[((size_t)b * NH + h) * dh + 2 * p], x1 = (float)q[((size_t)b * NH + h) * dh + 2 * p + 1];
+    const float c = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
+    qr[((size_t)b * NH + h) * 2 * r + 2 * j] = (x0 * c - x1 * sn) * scale;
+    qr[((size_t)b * NH + h) * 2 * r + 2 * j + 1] = (x0 * sn + x1 * c) * scale;
   }
 }
 
@@ -440,7 +516,7 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
       "global_load_lds_dwordx4 %0, %1"
       :
       : "v"(voff), "s"(base), "s"(lds_addr)
-      : "memory", "m0");
+      : "memory");  // M0 is rewritten here; no other instruction in these kernels reads M0
 }
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
@@ -701,39 +777,39 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   const int b = pair / NH, h = pair - b * NH;
   const float* ml = (const float*)(a.ws + a.plan.off_ml) + ((size_t)b * S * NH + h) * 2;
   const float* po = (const float*)(a.ws + a.plan.off_o) + ((size_t)b * S * NH + h) * D;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(size_t)s * NH * 2]);
-  float acc[KPL], den = 0.f;
+  // running merge over groups of 8 splits; each group's (m, l) and latent rows are loaded in one round
+  float M = -INFINITY, den = 0.f, acc[KPL];
 #pragma unroll
   for (int i = 0; i < KPL; ++i) acc[i] = 0.f;
-  int s = 0;
-  for (; s + 4 <= S; s += 4) {
-    float wsplit[4], v[4][KPL];
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float ms[8], ls[8], v[8][KPL];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float ms = ml[(size_t)(s + u) * NH * 2], ls = ml[(size_t)(s + u) * NH * 2 + 1];
-      wsplit[u] = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      den = fmaf(wsplit[u], ls, den);
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = s0 + u < S;
+      ms[u] = ok ? ml[(size_t)(s0 + u) * NH * 2] : -INFINITY;
+      ls[u] = ok ? ml[(size_t)(s0 + u) * NH * 2 + 1] : 0.f;
 #pragma unroll
       for (int i = 0; i < KPL; ++i) {
         const int k = lane + 64 * i;
-        v[u][i] = k < D ? po[(size_t)(s + u) * NH * D + k] : 0.f;
+        v[u][i] = (ok && k < D) ? po[(size_t)(s0 + u) * NH * D + k] : 0.f;
       }
     }
+    float gm = M;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 8; ++u) gm = fmaxf(gm, ms[u]);
+    if (gm == -INFINITY) continue;  // nothing seen yet (empty splits only)
+    const float c = exp2f(M - gm);  // rescale of what was merged so far (0 when M = -inf)
+    den *= c;
 #pragma unroll
-      for (int i = 0; i < KPL; ++i) acc[i] = fmaf(wsplit[u], v[u][i], acc[i]);
-  }
-  for (; s < S; ++s) {
-    const float ms = ml[(size_t)s * NH * 2], ls = ml[(size_t)s * NH * 2 + 1];
-    const float wsv = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
-    den = fmaf(wsv, ls, den);
+    for (int i = 0; i < KPL; ++i) acc[i] *= c;
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const int k = lane + 64 * i;
-      if (k < D) acc[i] = fmaf(wsv, po[(size_t)s * NH * D + k], acc[i]);
+    for (int u = 0; u < 8; ++u) {
+      const float wv = ms[u] == -INFINITY ? 0.f : exp2f(ms[u] - gm);
+      den = fmaf(wv, ls[u], den);
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) acc[i] = fmaf(wv, v[u][i], acc[i]);
     }
+    M = gm;
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   float* ob = (float*)(a.ws + a.plan.off_ob) + ((size_t)b * NH + h) * D;
@@ -744,71 +820,73 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   }
 }
 
-// 3b. out[b,h,:] = o[b,h,:] . W_uv,h^T: workgroup (head, CB rows); the rows' merged outputs sit in LDS,
-//     four threads share one output dim (quarters of the latent width, weight loads issued up front).
-constexpr int PQ = 4, PMAX = 16;  // latent quarters; 8-element weight chunks per quarter (d_kv <= 512)
+// 3b. out[b,h,:] = o[b,h,:] . W_uv,h^T.
+//   bf16 path: MFMA.  Workgroup (head h, 32 output dims, 32 sequences), 4 waves splitting the latent
+//   width.  Each merged fp32 row is split exactly into bf16 hi + lo parts (two MFMAs), so the product
+//   keeps ~16 significant bits of o; W_uv rows are read once as 16-byte operand loads.
+//   other shapes (fp32, latent widths not a multiple of 64): one thread per (row, output dim).
+__global__ __launch_bounds__(256) void decode_project_mfma(DecodeArgs a) {
+  __shared__ float red[4][32][33];
+  const int h = blockIdx.x, e0 = blockIdx.y * 32, b0 = blockIdx.z * 32;
+  const int D = a.s.d_kv, dh = a.s.d_head, NH = a.s.n_heads;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int kw = D / 4, k0 = w * kw;  // this wave's quarter of the latent width (multiple of 16)
+  const float* ob = (const float*)(a.ws + a.plan.off_ob);
+  const bf16* wuv = (const bf16*)a.w_uv + (size_t)h * dh * D;
+  const int b = b0 + (lane & 31), e = e0 + (lane & 31);
+  const bool bok = b < a.batch, eok = e < dh;
+  const float* orow = ob + ((size_t)b * NH + h) * D;
+  const bf16* wrow = wuv + (size_t)e * D;
+  f32x16 acc = f32x16{};
+  constexpr int MAXS = 8;  // K steps of 16 per batch of loads
+  for (int kb = k0; kb < k0 + kw; kb += 16 * MAXS) {
+    f32x4 o0[MAXS], o1[MAXS];
+    bf16x8 wv[MAXS];
+#pragma unroll
+    for (int u = 0; u < MAXS; ++u) {
+      const int k = kb + 16 * u + 8 * (lane >> 5);
+      const bool kin = kb + 16 * u < k0 + kw;
+      o0[u] = (bok && kin) ? *(const f32x4*)(orow + k) : f32x4{0.f, 0.f, 0.f, 0.f};
+      o1[u] = (bok && kin) ? *(const f32x4*)(orow + k + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      wv[u] = (eok && kin) ? *(const bf16x8*)(wrow + k) : bf16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < MAXS; ++u) {
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        hi[c] = (bf16)o0[u][c];
+        lo[c] = (bf16)(o0[u][c] - (float)hi[c]);
+        hi[4 + c] = (bf16)o1[u][c];
+        lo[4 + c] = (bf16)(o1[u][c] - (float)hi[4 + c]);
+      }
+      acc = mfma32(hi, wv[u], acc);
+      acc = mfma32(lo, wv[u], acc);
+    }
+  }
+  // D[row = sequence][col = output dim]: lane holds col lane%32, rows 8(i/4) + 4(lane/32) + i%4
+#pragma unroll
+  for (int i = 0; i < 16; ++i) red[w][8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)][lane & 31] = acc[i];
+  __syncthreads();
+  bf16* out = (bf16*)a.out;
+  for (int idx = threadIdx.x; idx < 32 * 32; idx += blockDim.x) {
+    const int bb = idx >> 5, ee = idx & 31;
+    const float v = red[0][bb][ee] + red[1][bb][ee] + red[2][bb][ee] + red[3][bb][ee];
+    if (b0 + bb < a.batch && e0 + ee < dh) out[((size_t)(b0 + bb) * NH + h) * dh + e0 + ee] = (bf16)v;
+  }
+}
 
 template <typename T>
-__global__ __launch_bounds__(512) void decode_project(DecodeArgs a) {
-  const int h = blockIdx.x, b0 = blockIdx.y * CB;
+__global__ __launch_bounds__(256) void decode_project_vec(DecodeArgs a) {
   const int D = a.s.d_kv, dh = a.s.d_head, NH = a.s.n_heads;
-  extern __shared__ float sh[];
-  float* ob = sh;  // [CB][D]
-  const float* src = (const float*)(a.ws + a.plan.off_ob);
-  for (int idx = threadIdx.x; idx < CB * D; idx += blockDim.x) {
-    int bb = idx / D, k = idx - bb * D, b = b0 + bb;
-    ob[idx] = b < a.batch ? src[((size_t)b * NH + h) * D + k] : 0.f;
-  }
-  __syncthreads();
-  const T* wuv = (const T*)a.w_uv + (size_t)h * dh * D;
-  T* out = (T*)a.out;
-  const int qk = (D + PQ - 1) / PQ;
-  const bool vec = sizeof(T) == 2 && (D % (8 * PQ)) == 0 && qk <= 8 * PMAX;
-  for (int e4 = threadIdx.x; e4 < PQ * dh; e4 += blockDim.x) {
-    const int e = e4 / PQ, part = e4 % PQ;
-    const int k0 = part * qk, k1 = min(D, k0 + qk);
-    const T* wr = wuv + (size_t)e * D;
-    float acc[CB];
-#pragma unroll
-    for (int bb = 0; bb < CB; ++bb) acc[bb] = 0.f;
-    if (vec) {
-      bf16x8 wv[PMAX];
-#pragma unroll
-      for (int c = 0; c < PMAX; ++c) wv[c] = (k0 + 8 * c < k1) ? *(const bf16x8*)((const bf16*)wr + k0 + 8 * c) : bf16x8{};
-#pragma unroll
-      for (int c = 0; c < PMAX; ++c) {
-        if (k0 + 8 * c >= k1) break;
-#pragma unroll
-        for (int bb = 0; bb < CB; ++bb) {
-          const f32x4 o0 = *(const f32x4*)&ob[bb * D + k0 + 8 * c];
-          const f32x4 o1 = *(const f32x4*)&ob[bb * D + k0 + 8 * c + 4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            acc[bb] = fmaf((float)wv[c][u], o0[u], acc[bb]);
-            acc[bb] = fmaf((float)wv[c][4 + u], o1[u], acc[bb]);
-          }
-        }
-      }
-    } else {
-      for (int k = k0; k < k1; ++k) {
-        const float wf = to_f32(wr[k]);
-#pragma unroll
-        for (int bb = 0; bb < CB; ++bb) acc[bb] = fmaf(wf, ob[bb * D + k], acc[bb]);
-      }
-    }
-#pragma unroll
-    for (int bb = 0; bb < CB; ++bb) {
-      acc[bb] += __shfl_xor(acc[bb], 1, 64);
-      acc[bb] += __shfl_xor(acc[bb], 2, 64);
-    }
-    if (part == 0) {
-#pragma unroll
-      for (int bb = 0; bb < CB; ++bb) {
-        const int b = b0 + bb;
-        if (b < a.batch) out[((size_t)b * NH + h) * dh + e] = from_f32<T>(acc[bb]);
-      }
-    }
-  }
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.batch * NH * dh) return;
+  const int e = idx % dh, bh = idx / dh, h = bh % NH;
+  const float* o = (const float*)(a.ws + a.plan.off_ob) + (size_t)bh * D;
+  const T* wr = (const T*)a.w_uv + ((size_t)h * dh + e) * D;
+  float acc = 0.f;
+  for (int k = 0; k < D; ++k) acc = fmaf(o[k], to_f32(wr[k]), acc);
+  ((T*)a.out)[idx] = from_f32<T>(acc);
 }
 
 template <typename T>
@@ -839,7 +917,6 @@ bool decode_uses_mfma(const Shape& s) {
 bool decode_fits(const Shape& s, const DecodePlan& p) {
   const size_t lim = 65536;
   if (s.d_kv > 1024) return false;
-  if ((size_t)CB * s.d_kv * sizeof(float) > lim) return false;
   if (!decode_uses_mfma(s) && (size_t)(s.d_kv + s.r2() + 1 + p.chunk) * sizeof(float) > lim) return false;
   return true;
 }
@@ -876,7 +953,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask) {
   const int nh = a.s.n_heads;
   if (phase_mask & 1) {
     dim3 gq(nh, (a.s.d_kv + 63) / 64, (a.batch + QB - 1) / QB);
-    if (a.s.dtype == 0)
+    if (a.s.dtype == 1 && a.s.d_nope() <= 128 && a.s.d_kv % 128 == 0)
+      hipLaunchKernelGGL(decode_qprep_mfma, dim3(nh, a.s.d_kv / 128, (a.batch + 31) / 32), dim3(256), 0, st, a);
+    else if (a.s.dtype == 0)
       hipLaunchKernelGGL(decode_qprep<float>, gq, dim3(64 * QW), 0, st, a);
     else
       hipLaunchKernelGGL(decode_qprep<bf16>, gq, dim3(64 * QW), 0, st, a);
@@ -900,12 +979,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask) {
     else if (kpl <= 4) hipLaunchKernelGGL(decode_merge<4>, dim3(gm), dim3(256), 0, st, a);
     else if (kpl <= 8) hipLaunchKernelGGL(decode_merge<8>, dim3(gm), dim3(256), 0, st, a);
     else hipLaunchKernelGGL(decode_merge<16>, dim3(gm), dim3(256), 0, st, a);
-    size_t shp = (size_t)CB * a.s.d_kv * sizeof(float);
-    dim3 gp(nh, (a.batch + CB - 1) / CB);
-    if (a.s.dtype == 0)
-      hipLaunchKernelGGL(decode_project<float>, gp, dim3(512), shp, st, a);
-    else
-      hipLaunchKernelGGL(decode_project<bf16>, gp, dim3(512), shp, st, a);
+    const int n = a.batch * nh * a.s.d_head;
+    if (a.s.dtype == 0) {
+      hipLaunchKernelGGL(decode_project_vec<float>, dim3((n + 255) / 256), dim3(256), 0, st, a);
+    } else if (a.s.d_kv % 64 == 0) {
+      dim3 gp(nh, (a.s.d_head + 31) / 32, (a.batch + 31) / 32);
+      hipLaunchKernelGGL(decode_project_mfma, gp, dim3(256), 0, st, a);
+    } else {
+      hipLaunchKernelGGL(decode_project_vec<bf16>, dim3((n + 255) / 256), dim3(256), 0, st, a);
+    }
   }
   return hipGetLastError();
 }

@@ -25,7 +25,13 @@ struct AppendArgs {
   const int32_t* start_pos;
   int batch, t_new, max_start, t_max;
   void *ckv, *ckv_scale, *krope;
+  char* ws = nullptr;  // optional workspace (few-token appends split the model width over workgroups)
 };
+
+// Few-token append with a workspace: number of model-width slices and the workspace it needs
+// (0 when the shape does not use the split path).
+int append_ksplit(const Shape& s, int tokens);
+size_t append_workspace_bytes(const Shape& s, int tokens);
 
 // Decode split plan: every sequence's positions [0, max_seq_len) are cut into n_splits chunks.
 struct DecodePlan {
@@ -65,7 +71,7 @@ struct PrefillArgs {
   PrefillPlan plan;
 };
 
-hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);  // uses a.ws when set and useful
 // phase_mask bit 0: q-prep, bit 1: attention, bit 2: combine
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask = 7);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);

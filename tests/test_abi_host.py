@@ -140,6 +140,22 @@ def test_append_checks(lib):
     assert call(c=c0, w=w0, x=None) == INVALID  # fails on x, not on the absent RoPE pointers
 
 
+def test_append_ws_checks(lib):
+    c, w, k = cfg(), weights(), cache()
+    need = lib.mla_cache_append_workspace_bytes(ctypes.byref(c), 32, 1)
+    assert need > 0  # a few-token append on this shape splits the model width
+    assert lib.mla_cache_append_workspace_bytes(ctypes.byref(c), 32, 4096) == 0  # large appends need none
+    assert lib.mla_cache_append_workspace_bytes(ctypes.byref(cfg(dtype=0)), 32, 1) == 0
+
+    def call(ws=FAKE, nbytes=need):
+        return lib.mla_cache_append_ws(ctypes.byref(c), ctypes.byref(w), ctypes.byref(k), FAKE, FAKE, 1, 4095, ws,
+                                       nbytes, None)
+
+    assert call(ws=None) == WORKSPACE
+    assert call(nbytes=need - 1) == WORKSPACE
+    assert call(ws=FAKE + 4) == ALIGN
+
+
 def test_prefill_checks(lib):
     c, w, k = cfg(), weights(), cache()
 

@@ -191,10 +191,12 @@ def test_full_llama_int4_decode_b64_l8192():
     run_decode_case(cfg, synth.seq_lens(cfg), cfg.context, sample=[0, 63], repeat_bitwise=False)
 
 
-@pytest.mark.parametrize("variant", ["bf16", "int4", "f32"])
-def test_step_append_batched_positions(variant):
-    """A decode step's append: one new token per sequence, each at its own position, in one call."""
-    from mla_latent_kv_cache_amd import LatentCache, append, pack_weights
+@pytest.mark.parametrize("variant,use_ws", [("bf16", False), ("bf16", True), ("int4", False), ("int4", True),
+                                             ("f32", False)])
+def test_step_append_batched_positions(variant, use_ws):
+    """A decode step's append: one new token per sequence, each at its own position, in one call (with and
+    without the workspace that splits the down-projection over the model width)."""
+    from mla_latent_kv_cache_amd import LatentCache, append, append_ws, pack_weights
 
     if variant == "f32":
         cfg = scaled(CONFIGS[0], batch=4)
@@ -204,7 +206,7 @@ def test_step_append_batched_positions(variant):
         cfg = scaled(CONFIGS[1], family="mid", batch=4)
     lens = [97, 2, 64, 200]
     t_max = 256
-    log(f"[step-append] {variant} lens={lens}")
+    log(f"[step-append] {variant} ws={use_ws} lens={lens}")
     layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
     shape = shape_of(cfg)
     w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
@@ -218,8 +220,11 @@ def test_step_append_batched_positions(variant):
         append(w, view, xt, zero, 0)
     x_new = np.stack([x[-1] for x in xs])[:, None, :]
     start = torch.tensor([L - 1 for L in lens], dtype=torch.int32, device="cuda")
-    append(w, cache, torch.from_numpy(x_new.astype(np.float32)).cuda().to(torch_dtype(cfg)).contiguous(), start,
-           max(lens) - 1)
+    xn = torch.from_numpy(x_new.astype(np.float32)).cuda().to(torch_dtype(cfg)).contiguous()
+    if use_ws:
+        append_ws(w, cache, xn, start, max(lens) - 1)
+    else:
+        append(w, cache, xn, start, max(lens) - 1)
     torch.cuda.synchronize()
     for b, L in enumerate(lens):
         c, kr = oracle_cache(cfg, layer, xs[b])
