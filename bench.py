@@ -10,11 +10,15 @@ Timing: inputs are resident in HBM before the timed region; `--warmup` untimed s
 timed steps bracketed by device synchronisation and HIP events on the launch stream.  Three independent
 cache copies are used in rotation so that the 256 MB last-level cache cannot serve a step's reads from
 the previous step.  The roofline object times the dominant kernel (the split-K attention launch, phase 2
-of mla_decode) with HIP events around each of its launches in a separate loop.
+of mla_decode) separately: `--steps` back-to-back launches of it between two HIP events.
 
 The cpu_baseline object times the oracle (plain fp64 numpy; the library never uses it) on a bounded
 sample of the same workload on the host's cores.  Secondary workloads (long-context variable-length
 decode, int4-latent decode, causal prefill) are reported in `secondary`.
+
+`roofline.traffic` is the HBM traffic of one launch of that kernel from FETCH_SIZE / WRITE_SIZE counter
+runs (profiles/pmc_traffic.json, scaled by the counters of a plain copy of known size, see
+--copy-calibration); it is null when those counters were taken on different decode sources.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only c1,c3,c4,c2] [--no-cpu-baseline]
 """
@@ -35,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode latent-cache GB/s (% of HBM peak); prefill MFMA TFLOP/s"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure (no sparsity)
+DOMINANT_KERNEL = "decode_attn_dma<128, 8, 3, 1>"
 
 
 def log(msg):
@@ -50,7 +55,54 @@ def parse():
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 10 plain device copies of 256 MiB (reference kernel for byte counters)")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------- traffic from byte counters
+
+DECODE_SOURCES = ("mla_latent_kv_cache_amd/csrc/decode.hip", "mla_latent_kv_cache_amd/csrc/common.h",
+                  "mla_latent_kv_cache_amd/csrc/kernels.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+
+
+def decode_source_digest():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed byte-counter summary, or None when the summary is
+    missing or was taken on other kernel sources (the digest of the decode sources no longer matches)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != decode_source_digest():
+        return None
+    return int(rec["traffic_bytes"])
+
+
+def copy_calibration():
+    """A plain device-to-device copy of known size: the byte counters of this kernel give the scale
+    factors between FETCH_SIZE / WRITE_SIZE and the bytes actually moved."""
+    import torch
+
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 10 copies of {n} bytes")
+    del src, dst
 
 
 # ---------------------------------------------------------------- workloads
@@ -131,23 +183,20 @@ def time_decode(wl, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
-    # dominant kernel: events around phase 2 only (phases 1 and 3 run untimed around it)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # dominant kernel: phase 1 (query preparation) once, then back-to-back launches of phase 2 (the split-K
+    # attention) over the rotating cache copies, bracketed by two events on the launch stream
+    for i in range(n):
+        bound[i].phase(1)
     for i in range(warmup):
-        bd = bound[i % n]
-        bd.phase(1)
-        bd.phase(2)
-        bd.phase(3)
+        bound[i % n].phase(2)
     torch.cuda.synchronize()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record()
     for i in range(steps):
-        bd = bound[i % n]
-        bd.phase(1)
-        evs[i][0].record()
-        bd.phase(2)
-        evs[i][1].record()
-        bd.phase(3)
+        bound[i % n].phase(2)
+    k1.record()
     torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    k_ms = k0.elapsed_time(k1) / steps
     return step_ms, k_ms
 
 
@@ -258,6 +307,8 @@ def main():
         sys.exit(1)
     only = set(args.only.split(","))
     C = synth.CONFIGS
+    if args.copy_calibration:
+        copy_calibration()
 
     conv_main = converted("llama", 4, 512)
     cfg1 = C[1]
@@ -314,8 +365,8 @@ def main():
                    "batch": 32, "context": 4096, "d_kv": 512, "r_pairs": 4, "cache_bytes_per_step": main_res["bytes"],
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_attn_mfma (mla_decode phase 2)",
+                     "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(DOMINANT_KERNEL),
+                     "kernel": DOMINANT_KERNEL + " (mla_decode phase 2)",
                      "kernel_us": round(main_res["kernel_ms"] * 1e3, 2)},
         "cpu_baseline": cpu,
         "secondary": secondary,
