@@ -153,6 +153,8 @@ static int decode_impl(int phase_mask, const mla_config* cfg, const mla_weights*
   MLA_TRY(check_ptr(seq_lens, true));
   MLA_TRY(check_ptr(out, true));
   MLA_TRY(check_positions(cfg, w, cache, max_seq_len));
+  // the kernels count the batch's tokens in 32-bit integers
+  if ((long long)cache->batch * max_seq_len >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
   const Shape s = shape_of(cfg);
   const mla::DecodePlan plan = mla::plan_decode(s, cache->batch, max_seq_len);
   if (!mla::decode_fits(s, plan)) return MLA_ERR_UNSUPPORTED;

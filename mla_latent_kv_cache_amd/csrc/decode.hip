@@ -29,6 +29,65 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
   return L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
 }
 
+// ------------------------------------------------------------------ work split (see DecodePlan)
+// Every function below is called by all 64 lanes of a wave and returns wave-uniform values.
+__device__ __forceinline__ int wave_isum(int v) {
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_iscan(int v) {  // inclusive prefix sum over lanes
+  const int lane = threadIdx.x & 63;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+__device__ int work_chunk(const DecodeArgs& a) {
+  int tot = 0;
+  for (int i = threadIdx.x & 63; i < a.batch; i += 64) tot += clamp_len(a, i);
+  tot = wave_isum(tot);
+  const int per = (tot + a.plan.target - 1) / a.plan.target;
+  const int chunk = ((per + 63) / 64) * 64;
+  return __builtin_amdgcn_readfirstlane(chunk < 64 ? 64 : (chunk > a.plan.cmax ? a.plan.cmax : chunk));
+}
+struct WorkItem {
+  int b, t0, t1;  // sequence and token range [t0, t1), non-empty when found
+};
+// Item `item` of the split; false when the batch has fewer items.
+__device__ bool locate_item(const DecodeArgs& a, int item, WorkItem& wi) {
+  const int chunk = work_chunk(a), lane = threadIdx.x & 63;
+  int base = 0;
+  for (int c0 = 0; c0 < a.batch; c0 += 64) {
+    const int i = c0 + lane;
+    const int L = i < a.batch ? clamp_len(a, i) : 0;
+    const int cnt = (L + chunk - 1) / chunk;
+    const int incl = wave_iscan(cnt);
+    const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+    if (item < base + total) {
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(base + incl > item);
+      const int ln = (int)__builtin_ctzll(hit);
+      const int first = base + __shfl(incl - cnt, ln, 64);
+      // the values are wave-uniform; readfirstlane lets the compiler keep them (and the addresses
+      // derived from them) in scalar registers
+      wi.b = __builtin_amdgcn_readfirstlane(c0 + ln);
+      wi.t0 = __builtin_amdgcn_readfirstlane((item - first) * chunk);
+      wi.t1 = __builtin_amdgcn_readfirstlane(min(wi.t0 + chunk, __shfl(L, ln, 64)));
+      return true;
+    }
+    base += total;
+  }
+  return false;
+}
+// First item and item count of sequence b.
+__device__ void sequence_items(const DecodeArgs& a, int b, int& first, int& count) {
+  const int chunk = work_chunk(a), lane = threadIdx.x & 63;
+  int before = 0;
+  for (int i = lane; i < b; i += 64) before += (clamp_len(a, i) + chunk - 1) / chunk;
+  first = __builtin_amdgcn_readfirstlane(wave_isum(before));
+  count = (clamp_len(a, b) + chunk - 1) / chunk;
+}
+
 // ------------------------------------------------------------------ 1. query preparation
 // Workgroup (head h, 64 latent columns, up to QB batch rows), 8 waves splitting the NoPE dims: every
 // lane issues all of its W_uk loads at once, accumulates QB rows, and the partial sums meet in LDS.
@@ -210,18 +269,17 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 // ------------------------------------------------------------------ 2a. attention, generic VALU path
 template <typename T, int FMT>
 __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
-  const int split = blockIdx.x, b = blockIdx.y;
-  const int D = a.s.d_kv, NH = a.s.n_heads, R2 = a.s.r2(), S = a.plan.n_splits;
-  const int L = clamp_len(a, b);
-  const int t0 = split * a.plan.chunk;
-  const int n = min(t0 + a.plan.chunk, L) - t0;
+  WorkItem wi;
+  if (!locate_item(a, blockIdx.x, wi)) return;
+  const int b = wi.b, t0 = wi.t0, n = wi.t1 - wi.t0;
+  const int D = a.s.d_kv, NH = a.s.n_heads, R2 = a.s.r2();
   extern __shared__ float sh[];
   float* qs = sh;              // D
   float* qrs = qs + D;         // R2
   float* sc = qrs + R2 + 1;    // chunk
   __shared__ float red[8];
-  float* ml = (float*)(a.ws + a.plan.off_ml) + ((size_t)b * S + split) * NH * 2;
-  float* po = (float*)(a.ws + a.plan.off_o) + ((size_t)b * S + split) * NH * D;
+  float* ml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * NH * 2;
+  float* po = (float*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * NH * D;
   const T* qt = (const T*)(a.ws + a.plan.off_qt) + (size_t)b * NH * D;
   const float* qr = (const float*)(a.ws + a.plan.off_qr) + (size_t)b * NH * R2;
   const size_t row0 = (size_t)b * a.t_max + t0;
@@ -289,26 +347,12 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   __shared__ __attribute__((aligned(16))) bf16 cbuf[4][32 * CP];
   __shared__ f32x4 sbuf[2][4][4][64];
 
-  const int split = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5, h = lane & 31;
-  const int S = a.plan.n_splits;
-  const int L = clamp_len(a, b);
-  const int t0 = split * a.plan.chunk;
-  const int t1 = min(t0 + a.plan.chunk, L);
-  float* pml = (float*)(a.ws + a.plan.off_ml) + ((size_t)b * S + split) * 32 * 2;
-  float* po = (float*)(a.ws + a.plan.off_o) + ((size_t)b * S + split) * 32 * D;
-
-  if (t0 >= t1) {
-    for (int idx = lane; idx < 32 * DW / 4; idx += 64) {
-      int hh = idx / (DW / 4), c4 = idx - hh * (DW / 4);
-      *(f32x4*)&po[(size_t)hh * D + w * DW + 4 * c4] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    if (w == 0 && lane < 32) {
-      pml[2 * lane] = -INFINITY;
-      pml[2 * lane + 1] = 0.f;
-    }
-    return;
-  }
+  WorkItem wi;
+  if (!locate_item(a, blockIdx.x, wi)) return;
+  const int b = wi.b, t0 = wi.t0, t1 = wi.t1;
+  float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * 2;
+  float* po = (float*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * 32 * D;
 
   // latent query operands (B of the score product) and the rotated query pairs
   const bf16* qt = (const bf16*)(a.ws + a.plan.off_qt) + ((size_t)b * 32 + h) * D + w * DW + 8 * hb;
@@ -539,26 +583,12 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char ks0[4 * KSL], ks1[4 * KSL], ks2[NSLOT > 2 ? 4 * KSL : 16];
   __shared__ f32x4 sbuf[NSB][4][4][64];
 
-  const int split = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5, h = lane & 31;
-  const int S = a.plan.n_splits;
-  const int L = clamp_len(a, b);
-  const int t0 = split * a.plan.chunk;
-  const int t1 = min(t0 + a.plan.chunk, L);
-  float* pml = (float*)(a.ws + a.plan.off_ml) + ((size_t)b * S + split) * 32 * 2;
-  float* po = (float*)(a.ws + a.plan.off_o) + ((size_t)b * S + split) * 32 * D;
-
-  if (t0 >= t1) {
-    for (int idx = lane; idx < 32 * DW / 4; idx += 64) {
-      int hh = idx / (DW / 4), c4 = idx - hh * (DW / 4);
-      *(f32x4*)&po[(size_t)hh * D + w * DW + 4 * c4] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    if (w == 0 && lane < 32) {
-      pml[2 * lane] = -INFINITY;
-      pml[2 * lane + 1] = 0.f;
-    }
-    return;
-  }
+  WorkItem wi;
+  if (!locate_item(a, blockIdx.x, wi)) return;
+  const int b = wi.b, t0 = wi.t0, t1 = wi.t1;
+  float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * 2;
+  float* po = (float*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * 32 * D;
 
   // DMA addresses: a wave-uniform tile base (SGPRs) plus per-lane offsets that do not change per tile
   const size_t rowb = (size_t)b * a.t_max;
@@ -772,11 +802,13 @@ template <int KPL>
 __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int D = a.s.d_kv, NH = a.s.n_heads, S = a.plan.n_splits;
+  const int D = a.s.d_kv, NH = a.s.n_heads;
   if (pair >= a.batch * NH) return;
   const int b = pair / NH, h = pair - b * NH;
-  const float* ml = (const float*)(a.ws + a.plan.off_ml) + ((size_t)b * S * NH + h) * 2;
-  const float* po = (const float*)(a.ws + a.plan.off_o) + ((size_t)b * S * NH + h) * D;
+  int first, S;
+  sequence_items(a, b, first, S);
+  const float* ml = (const float*)(a.ws + a.plan.off_ml) + ((size_t)first * NH + h) * 2;
+  const float* po = (const float*)(a.ws + a.plan.off_o) + ((size_t)first * NH + h) * D;
   // running merge over groups of 8 splits; each group's (m, l) and latent rows are loaded in one round
   float M = -INFINITY, den = 0.f, acc[KPL];
 #pragma unroll
@@ -891,8 +923,8 @@ __global__ __launch_bounds__(256) void decode_project_vec(DecodeArgs a) {
 
 template <typename T>
 void launch_generic_attn(const DecodeArgs& a, hipStream_t st) {
-  size_t shmem = (size_t)(a.s.d_kv + a.s.r2() + 1 + a.plan.chunk) * sizeof(float);
-  dim3 grid(a.plan.n_splits, a.batch);
+  size_t shmem = (size_t)(a.s.d_kv + a.s.r2() + 1 + a.plan.cmax) * sizeof(float);
+  dim3 grid(a.plan.max_items);
   if (a.s.fmt == 0)
     hipLaunchKernelGGL((decode_attn_generic<T, 0>), grid, dim3(256), shmem, st, a);
   else
@@ -901,7 +933,7 @@ void launch_generic_attn(const DecodeArgs& a, hipStream_t st) {
 
 template <int DW, int R2>
 void launch_mfma_attn(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.plan.n_splits, a.batch);
+  dim3 grid(a.plan.max_items);
   if (a.s.fmt == 0)
     hipLaunchKernelGGL((decode_attn_dma<DW, R2, (DW == 128 && R2 == 8) ? 3 : 3, (DW == 128 && R2 == 8) ? 1 : 2>), grid, dim3(256), 0, st, a);
   else
@@ -915,9 +947,8 @@ bool decode_uses_mfma(const Shape& s) {
 }
 
 bool decode_fits(const Shape& s, const DecodePlan& p) {
-  const size_t lim = 65536;
   if (s.d_kv > 1024) return false;
-  if (!decode_uses_mfma(s) && (size_t)(s.d_kv + s.r2() + 1 + p.chunk) * sizeof(float) > lim) return false;
+  if (!decode_uses_mfma(s) && (size_t)(s.d_kv + s.r2() + 1 + p.cmax) * sizeof(float) > 65536) return false;
   return true;
 }
 
@@ -925,14 +956,21 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len) {
   DecodePlan p{};
-  // one workgroup per CU for the specialised kernels (their LDS ring fills a CU), two otherwise
-  const long long target_wg = (decode_uses_mfma(s) && s.fmt == 0) ? 256 : 512;
-  long long per = ((long long)max_seq_len * batch + target_wg - 1) / target_wg;
-  int chunk = (int)(((per + 63) / 64) * 64);
-  if (chunk < 64) chunk = 64;
-  if (chunk > 2048) chunk = 2048;
-  p.chunk = chunk;
-  p.n_splits = max_seq_len > 0 ? (max_seq_len + chunk - 1) / chunk : 1;
+  // one workgroup per CU for the specialised dense kernels (their LDS ring fills a CU), two otherwise
+  p.target = (decode_uses_mfma(s) && s.fmt == 0) ? 256 : 512;
+  p.cmax = 2048;
+  if (!decode_uses_mfma(s)) {  // the generic kernel keeps a chunk of scores in LDS
+    const long long room = 65536 / 4 - (long long)s.d_kv - s.r2() - 1;
+    const long long c = room > 0 ? (room / 64) * 64 : 64;
+    if (c < p.cmax) p.cmax = (int)(c < 64 ? 64 : c);
+  }
+  // items = sum_b ceil(L_b / chunk) < sum_b L_b / chunk + batch; chunk >= sum / target unless clamped
+  const long long B = batch, Lm = max_seq_len;
+  long long by_min = B * ((Lm + 63) / 64);                          // chunk = 64
+  long long by_max = (B * Lm + p.cmax - 1) / p.cmax;                // chunk = cmax
+  long long bound = (by_max > p.target ? by_max : p.target) + B;
+  long long items = by_min < bound ? by_min : bound;
+  p.max_items = (int)(items < 1 ? 1 : items);
   const size_t esz = s.dtype == 0 ? 4 : 2;
   size_t off = 0;
   p.off_qt = off;
@@ -940,9 +978,9 @@ DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len) {
   p.off_qr = off;
   off = align256(off + (size_t)batch * s.n_heads * (s.r2() > 0 ? s.r2() : 1) * 4);
   p.off_ml = off;
-  off = align256(off + (size_t)batch * p.n_splits * s.n_heads * 2 * 4);
+  off = align256(off + (size_t)p.max_items * s.n_heads * 2 * 4);
   p.off_o = off;
-  off = align256(off + (size_t)batch * p.n_splits * s.n_heads * s.d_kv * 4);
+  off = align256(off + (size_t)p.max_items * s.n_heads * s.d_kv * 4);
   p.off_ob = off;
   off = align256(off + (size_t)batch * s.n_heads * s.d_kv * 4);
   p.total = off;

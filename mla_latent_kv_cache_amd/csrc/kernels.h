@@ -33,10 +33,15 @@ struct AppendArgs {
 int append_ksplit(const Shape& s, int tokens);
 size_t append_workspace_bytes(const Shape& s, int tokens);
 
-// Decode split plan: every sequence's positions [0, max_seq_len) are cut into n_splits chunks.
+// Decode work split.  The kernels read the batch's lengths L_b on the device and cut its tokens into
+// work items of `chunk` tokens: chunk = clamp(round_up(ceil(sum_b L_b / target), 64), 64, cmax), and
+// sequence b owns ceil(L_b / chunk) consecutive items (in batch order).  Ragged batches therefore
+// spread over about `target` workgroups like uniform ones.  max_items bounds the item count for any
+// lengths within max_seq_len; the per-item partial results are laid out by item.
 struct DecodePlan {
-  int chunk;     // tokens per split (multiple of 64)
-  int n_splits;  // ceil(max_seq_len / chunk), >= 1
+  int target;     // desired number of work items
+  int cmax;       // largest chunk (multiple of 64)
+  int max_items;  // grid size of the attention launch, >= 1
   size_t off_qt, off_qr, off_ml, off_o, off_ob, total;
 };
 DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len);

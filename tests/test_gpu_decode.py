@@ -141,6 +141,17 @@ def test_mid_bf16_dkv256_r4():
     run_decode_case(cfg, [129, 1200, 64], 1280)
 
 
+def test_mid_bf16_many_sequences():
+    """More sequences than one wave scans at once (the work split walks the batch 64 lengths at a time),
+    lengths from 0 to 300, so that work items of one sequence straddle those groups."""
+    cfg = scaled(CONFIGS[1], family="mid", batch=70)
+    lens = np.random.default_rng(11).integers(0, 301, size=70)
+    lens[[3, 64]] = 0
+    lens[[5, 65]] = 1
+    sample = sorted({0, 1, 5, 63, 64, 65, 69, int(np.argmax(lens))})
+    run_decode_case(cfg, [int(v) for v in lens], 320, sample=sample)
+
+
 def test_mid_int4():
     cfg = scaled(CONFIGS[4], family="mid", batch=4)
     run_decode_case(cfg, [1000, 65, 512, 3], 1024)
