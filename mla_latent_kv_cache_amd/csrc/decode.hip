@@ -548,26 +548,6 @@ __device__ __forceinline__ int slice_off(int row, int col) {
   return row * (DW * 2) + 16 * swz<DW>(row, col >> 3) + (col & 7) * 2;
 }
 
-// 16 bytes per lane from global memory straight into LDS at lds_addr + 16 * lane (global_load_lds_dwordx4),
-// global address = base (wave-uniform, SGPRs) + voff (per lane, 32-bit).  Written as asm so that the
-// compiler does not guard every later LDS read with a full vmcnt(0) drain: the asm has no output
-// registers, and its completion is awaited explicitly with MLA_WAIT_VMCNT before the slot it fills is
-// read.  (Loads the compiler does not see only make its own vmcnt waits stricter.)
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(base), "s"(lds_addr)
-      : "memory");  // M0 is rewritten here; no other instruction in these kernels reads M0
-}
-__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// s_waitcnt with only the vector-memory counter constrained (expcnt 7, lgkmcnt 15 = no wait)
-#define MLA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 0xF) | (((n) >> 4) << 14))
 
 // NSLOT tile slots in the DMA ring (2: one tile in flight while one is used; 3: two in flight), NSB
 // buffers for the cross-wave exchange of partial scores (2 saves one barrier per tile).

@@ -59,8 +59,11 @@ struct DecodeArgs {
   DecodePlan plan;
 };
 
+// Prefill workspace: K [b, h, s_pad, 128] and V^T [b, h, 128, s_pad] bf16, s_pad = seq_len rounded up
+// to the 64-key tile.
 struct PrefillPlan {
-  size_t off_k, off_vt, off_q, total;
+  int s_pad;
+  size_t off_k, off_vt, total;
 };
 PrefillPlan plan_prefill(const Shape& s, int batch, int seq_len);
 

@@ -4,372 +4,471 @@
 // from the latent: K_nope = c_kv . W_uk,h and V = c_kv . W_uv,h, with the retained RoPE keys cached
 // separately.  For a whole prompt the minimum-work form rebuilds K and V once per token and runs plain
 // causal attention with d_h = 128:
-//   1. reconstruction GEMMs (MFMA):  K^[b,h,t, 0:dn] = c_kv[b,t] . W_uk,h        (dn = d_h - 2r)
-//                                     V^T[b,h, :, t] = W_uv,h^T . c_kv[b,t]      (stored transposed)
-//   2. causal flash attention (MFMA): head dims in the order [nope(h) | rope(h)], so the key row is
-//      K^ followed by the cache's k_rope (already rotated) and the query row is q[nope(h)] followed by
-//      the rotated retained pairs; q . k is unchanged by applying the same permutation to both.
+//   1. reconstruction GEMMs (MFMA): K[b,h,t,:] = NoPE dims from c_kv[b,t] . W_uk,h and the retained
+//      dims copied from the cache's rotated k_rope, in the original head-dim order;
+//      V^T[b,h,:,t] = W_uv,h^T . c_kv[b,t] (stored transposed, keys permuted within groups of 16)
+//   2. causal flash attention (MFMA) over those rows with the query's retained pairs rotated.
 #include <hip/hip_fp16.h>
 
 #include "common.h"
+#include "gemm.h"
 #include "kernels.h"
 
 namespace mla {
 
 namespace {
 
-// ------------------------------------------------------------------ 1. reconstruction GEMM
-// out = A . B^T over the latent width, tile 128 x 128, K step 64, 4 waves of 64 x 64.
-//   MODE 0: A = latent rows of the cache (token m = (b, t)), B = W_uk rows (n = h*dn + i) -> K^
-//   MODE 1: A = W_uv rows (m = h*d_h + e), B = latent rows (token n = (b, t))             -> V^T
-constexpr int GT = 128, GK = 64, GP = GK + 8;
+// ------------------------------------------------------------------ 1. reconstruction GEMMs
+// Through the shared GEMM main loop (gemm.h), K = d_kv, three stages (72 KB of LDS, two workgroups per
+// CU so that one's epilogue overlaps the other's main loop).  The tile is staged in LDS in the output
+// layout and written as whole 16-byte row chunks.
+//   keys:   tile = 256 tokens x one head.  A = latent rows of the cache (token m = (b, t)), B = W_uk,h
+//           rows: column e < d_nope is the GEMM result for NoPE dim nope_idx[e]; the remaining dims
+//           come from the cache's rotated RoPE keys (pair j -> dims 2p_j, 2p_j + 1).  Written to
+//           K[b, h, t, 0:128] in the ORIGINAL head-dim order, so queries need no permutation.
+//   values: tile = one head's 128 dims x 256 tokens.  A = W_uv,h rows, B = latent rows (token n = (b, t),
+//           t < s_pad; columns t >= S are written as zeros) -> V^T[b, h, e, pos(t)], keys permuted
+//           within every 16 by pos() below.
+using RecK = GemmCfg<256, 128, 3>;
+using RecV = GemmCfg<128, 256, 3>;
 
-template <int MODE>
-__global__ __launch_bounds__(256, 2) void rec_gemm(PrefillArgs a, int M, int N) {
-  __shared__ __attribute__((aligned(16))) bf16 sA[2][GT * GP];
-  __shared__ __attribute__((aligned(16))) bf16 sB[2][GT * GP];
-  const int K = a.s.d_kv, S = a.seq_len, dn = a.s.d_nope(), dh = a.s.d_head, NH = a.s.n_heads;
-  const int n_tiles = (N + GT - 1) / GT;
-  const int total = gridDim.x;
-  int bid = blockIdx.x;
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-  const int m0 = (bid / n_tiles) * GT, n0 = (bid % n_tiles) * GT;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-  const bf16* ckv = (const bf16*)a.ckv;
-  const bf16* wmat = MODE == 0 ? (const bf16*)a.w_uk : (const bf16*)a.w_uv;
+// Position of key t in a V^T row: within each group of 16 keys the second and third runs of 4 swap
+// places, which is the order in which the score MFMA's result registers hand out the keys (see the
+// attention kernel), so P feeds the PV MFMA without any data movement.
+__device__ __forceinline__ int vt_pos(int t) {
+  const int k = t & 15;
+  return (t & ~15) | (((k >> 2) & 1) << 3) | ((k >> 3) << 2) | (k & 3);
+}
 
-  auto latent_row = [&](int tok) -> const bf16* {
-    int b = tok / S, t = tok - b * S;
-    return ckv + ((size_t)b * a.t_max + t) * K;
-  };
-  auto a_row = [&](int m) -> const bf16* { return MODE == 0 ? latent_row(m) : wmat + (size_t)m * K; };
-  auto b_row = [&](int n) -> const bf16* { return MODE == 0 ? wmat + (size_t)n * K : latent_row(n); };
+// Byte offset of element `col` of row `row` in a staging tile with `pitch`-byte rows, 16-byte chunks
+// XOR-swizzled by the low row bits (rows 4 apart land in different banks).
+__device__ __forceinline__ int stage_off(int row, int col, int pitch) {
+  return row * pitch + 16 * ((col >> 3) ^ (row & 7)) + 2 * (col & 7);
+}
 
-  bf16x8 ra[4], rb[4];
-  const bf16x8 zero8 = {};
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      int c = it * 256 + tid, row = c >> 3, kc = (c & 7) * 8;
-      int gm = m0 + row, gn = n0 + row;
-      ra[it] = gm < M ? *(const bf16x8*)(a_row(gm) + kt * GK + kc) : zero8;
-      rb[it] = gn < N ? *(const bf16x8*)(b_row(gn) + kt * GK + kc) : zero8;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      int c = it * 256 + tid, row = c >> 3, kc = (c & 7) * 8;
-      *(bf16x8*)&sA[buf][row * GP + kc] = ra[it];
-      *(bf16x8*)&sB[buf][row * GP + kc] = rb[it];
-    }
-  };
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  const int KT = K / GK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < GK / 16; ++ks) {
-      bf16x8 av[2], bv[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        av[i] = *(const bf16x8*)&sA[buf][(wm * 64 + i * 32 + (lane & 31)) * GP + ks * 16 + (lane >> 5) * 8];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bv[j] = *(const bf16x8*)&sB[buf][(wn * 64 + j * 32 + (lane & 31)) * GP + ks * 16 + (lane >> 5) * 8];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(av[i], bv[j], acc[i][j]);
-    }
-    if (kt + 1 < KT) sstore(buf ^ 1);
-    __syncthreads();
+// Hardware dispatch places workgroup k on XCD k % 8; logical tile t runs on XCD t / (total / 8), so
+// consecutive logical tiles (which share an operand tile) share an L2.
+__device__ __forceinline__ int xcd_tile(int bid, int total) {
+  return (total & 7) == 0 ? (bid & 7) * (total >> 3) + (bid >> 3) : bid;
+}
+
+__global__ __launch_bounds__(256, 2) void rec_k_gemm(PrefillArgs a, int M) {
+  __shared__ __attribute__((aligned(1024))) char lds[RecK::LDS_BYTES];
+  __shared__ int dim_of[128];
+  __shared__ int kept[64];
+  __shared__ int crow[256], orow[256];  // cache row and output row of every token of the tile (-1: none)
+  const int K = a.s.d_kv, S = a.seq_len, SP = a.plan.s_pad, dn = a.s.d_nope(), NH = a.s.n_heads;
+  const int r = a.s.r_pairs, R2 = a.s.r2();
+  const int bid = xcd_tile(blockIdx.x, gridDim.x);
+  const int hh = bid % NH, m0 = (bid / NH) * 256;  // consecutive tiles share the token rows
+  const int tid = threadIdx.x;
+  if (tid < 128) dim_of[tid] = 0;  // duplicate pairs leave entries unset: keep them in range
+  {
+    const int m = m0 + tid;
+    const int b = m / S, t = m - b * S;
+    crow[tid] = m < M ? b * a.t_max + t : -1;
+    orow[tid] = m < M ? (b * NH + hh) * SP + t : -1;
   }
+  build_nope_idx(a.pair_idx, hh, r, 64, kept, dim_of);
+  if (tid < R2) dim_of[dn + tid] = 2 * load_pair(a.pair_idx, hh * r + (tid >> 1), 64) + (tid & 1);
+  __syncthreads();
+  const bf16* ckv = (const bf16*)a.ckv;
+  const int last = crow[min(M - 1 - m0, 255)];
+  auto a_row = [&](int i) {
+    const int c = crow[i];
+    return ckv + (size_t)(c >= 0 ? c : last) * K;
+  };
+  auto b_row = [&](int i) -> const bf16* {  // rows past d_nope load valid rows (their results are unused)
+    if (dn == 0) return ckv;
+    return (const bf16*)a.w_uk + ((size_t)hh * dn + min(i, dn - 1)) * K;
+  };
+  f32x16 acc[RecK::FM][RecK::FN];
+  gemm_tile<256, 128, 3>(lds, K, a_row, b_row, acc);
+  __syncthreads();  // the ring is idle; its LDS becomes the staging tile [256 tokens][128 dims]
+
+  const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+#pragma unroll
+  for (int j = 0; j < RecK::FN; ++j) {
+    const int col = wn * 64 + 32 * j + (lane & 31);
+    if (col < dn) {
+      const int d = dim_of[col];
+#pragma unroll
+      for (int i = 0; i < RecK::FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = wm * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          *(bf16*)(lds + stage_off(row, d, 256)) = (bf16)acc[i][j][e];
+        }
+    }
+  }
+  // retained dims: the cache's rotated k_rope of (token, head).  Up to 16 of them per row: each thread
+  // owns one row and issues all its (4-byte) loads before the first use; more take a slower loop.
+  const bf16* kr = (const bf16*)a.krope;
+  if (R2 <= 16) {
+    const int c = crow[tid];
+    const uint32_t* src = (const uint32_t*)(kr + ((size_t)(c >= 0 ? c : 0) * NH + hh) * R2);
+    uint32_t kv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) kv[q] = (c >= 0 && 2 * q < R2) ? src[q] : 0u;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (2 * q < R2) *(uint32_t*)(lds + stage_off(tid, dim_of[dn + 2 * q], 256)) = kv[q];
+  } else {
+    for (int idx = tid; idx < 256 * R2; idx += 256) {
+      const int row = idx / R2, q = idx - row * R2, c = crow[row];
+      const bf16 v = c >= 0 ? kr[((size_t)c * NH + hh) * R2 + q] : (bf16)0.f;
+      *(bf16*)(lds + stage_off(row, dim_of[dn + q], 256)) = v;
+    }
+  }
+  __syncthreads();
   bf16* outk = (bf16*)(a.ws + a.plan.off_k);
-  bf16* outv = (bf16*)(a.ws + a.plan.off_vt);
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int row = it * 16 + (tid >> 4), ch = tid & 15, o = orow[row];
+    if (o >= 0) *(u32x4*)(outk + (size_t)o * 128 + ch * 8) = *(const u32x4*)(lds + row * 256 + 16 * (ch ^ (row & 7)));
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void rec_vt_gemm(PrefillArgs a, int N) {
+  __shared__ __attribute__((aligned(1024))) char lds[RecV::LDS_BYTES];
+  __shared__ int crow[256];  // cache row of every token column of the tile (clamped to valid rows)
+  __shared__ size_t orow[32];  // output offset of every 8-position chunk (-1: none)
+  const int K = a.s.d_kv, S = a.seq_len, SP = a.plan.s_pad, NH = a.s.n_heads;
+  const int bid = xcd_tile(blockIdx.x, gridDim.x);
+  const int hh = bid % NH, n0 = (bid / NH) * 256;  // consecutive tiles share the token tile
+  const int tid = threadIdx.x;
+  {
+    const int n = min(n0 + tid, N - 1), b = n / SP, t = n - b * SP;
+    crow[tid] = b * a.t_max + min(t, S - 1);
+    if (tid < 32) {
+      const int nc = n0 + 8 * tid, bc = nc / SP, tc = nc - bc * SP;
+      orow[tid] = nc < N ? ((size_t)(bc * NH + hh) * 128) * SP + tc : ~(size_t)0;
+    }
+  }
+  __syncthreads();
+  const bf16* ckv = (const bf16*)a.ckv;
+  auto a_row = [&](int i) { return (const bf16*)a.w_uv + ((size_t)hh * 128 + i) * K; };
+  auto b_row = [&](int i) { return ckv + (size_t)crow[i] * K; };
+  f32x16 acc[RecV::FM][RecV::FN];
+  gemm_tile<128, 256, 3>(lds, K, a_row, b_row, acc);
+  __syncthreads();  // staging tile [128 dims][256 positions]
+
+  const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < RecV::FN; ++j) {
+    const int col = wn * 128 + 32 * j + (lane & 31), n = n0 + col, t = n % SP;
+    const bool live = n < N && t < S;
+    const int p = vt_pos(col);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-      if (n >= N) continue;
+    for (int i = 0; i < RecV::FM; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (m >= M) continue;
-        const bf16 v = (bf16)acc[i][j][e];
-        if (MODE == 0) {
-          int b = m / S, t = m - b * S, h = n / dn, ii = n - h * dn;
-          outk[(((size_t)b * NH + h) * S + t) * dn + ii] = v;
-        } else {
-          int h = m / dh, e2 = m - h * dh, b = n / S, t = n - b * S;
-          outv[(((size_t)b * NH + h) * dh + e2) * S + t] = v;
-        }
+        const int row = wm * 64 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        *(bf16*)(lds + stage_off(row, p, 512)) = live ? (bf16)acc[i][j][e] : (bf16)0.f;
       }
-    }
+  }
+  __syncthreads();
+  bf16* outv = (bf16*)(a.ws + a.plan.off_vt);
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int row = it * 8 + (tid >> 5), ch = tid & 31;
+    const size_t o = orow[ch];  // eight positions never straddle two sequences (s_pad is a multiple of 64)
+    if (o != ~(size_t)0) *(u32x4*)(outv + o + (size_t)row * SP) = *(const u32x4*)(lds + row * 512 + 16 * (ch ^ (row & 7)));
+  }
 }
 
 // ------------------------------------------------------------------ 2. causal flash attention, d_h = 128
-// Workgroup = (query tile of 128 rows, head, sequence); 4 waves of 32 query rows; key tiles of 64.
-//   S^T[key][q] = K^[key] . Q^[q]      MFMA 32x32x16, A = key rows (LDS), B = query rows (registers):
-//                                       lane l owns query l%32, so row max / sum stay in the lane
-//                                       plus one cross-half shuffle
-//   O^T[e][q]  += V^T[e][key] P[q][key] MFMA 32x32x16, A = V^T rows (LDS), B = P from the score
-//                                       registers; within every 16 keys the V^T tile stores keys in
-//                                       the order the score layout hands them out
-// Query tiles are scheduled longest first (causal work grows with the tile index).
-constexpr int FQ = 128, FKV = 64, KP = 128 + 8, VP = FKV + 8;
+// Workgroup = (256 query rows, head, sequence), 8 waves of 32 rows, two per SIMD running half a tile
+// apart so that one wave's softmax overlaps the other's MFMAs.  Key tiles of 64 stream through a 4-slot
+// LDS ring by direct-to-LDS DMA (two tiles in flight), one workgroup barrier per tile:
+//   S^T[key][q] = K[key] . Q[q]       MFMA 32x32x16, A = key rows from LDS, B = query rows in registers;
+//                                      lane l owns query l%32, so row max / sum need one cross-half shuffle
+//   O^T[e][q]  += V^T[e][key] P[q][key] MFMA 32x32x16, A = V^T rows from LDS, B = P straight from the
+//                                      score registers (V^T keys are stored in the matching order)
+// K rows (256 B) are stored with their 16-byte chunks XOR-swizzled by row, V^T rows (128 B) by row/2, so
+// both operand reads are bank-conflict free.  The running max is raised lazily (only when a tile
+// exceeds it by more than 2^8), so O is rarely rescaled.  All query tiles of one (sequence, head) run
+// on one XCD, longest first, so their shared K / V^T reads hit that XCD's L2.
+constexpr int FQ = 256, FKV = 64, FNS = 4;
+constexpr int KT_BYTES = FKV * 256, VT_BYTES = 128 * FKV * 2, SLOT = KT_BYTES + VT_BYTES;
 
-__global__ __launch_bounds__(256, 2) void prefill_attn(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 ks[2][FKV * KP];
-  __shared__ __attribute__((aligned(16))) bf16 vs[2][128 * VP];
-  __shared__ int nope_idx[128];
-  __shared__ int pairs[64];
-  const int S = a.seq_len, NH = a.s.n_heads, dn = a.s.d_nope(), r = a.s.r_pairs, R2 = a.s.r2(), half = 64;
-  const int nqt = (S + FQ - 1) / FQ;
-  const int qt = nqt - 1 - (int)blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+// One query tile of one (sequence, head) pair, all 8 waves of the workgroup.
+__device__ __forceinline__ void attend_query_tile(const PrefillArgs& a, char* ring, int pair, int qt) {
+  const int S = a.seq_len, SP = a.plan.s_pad, NH = a.s.n_heads, r = a.s.r_pairs;
+  const int b = pair / NH, h = pair - b * NH;
   const int q0 = qt * FQ;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5, ql = lane & 31;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int myq = q0 + 32 * w + ql;
+  const int n_kv = min(SP / FKV, (min(q0 + FQ, S) - 1) / FKV + 1);
 
-  if (tid == 0) {
-    int n = 0;
-    for (int j = 0; j < r; ++j) pairs[j] = load_pair(a.pair_idx, h * r + j, half);
-    for (int i = 0; i < half; ++i) {
-      bool kept = false;
-      for (int j = 0; j < r; ++j) kept |= (pairs[j] == i);
-      if (!kept) {
-        nope_idx[n++] = 2 * i;
-        nope_idx[n++] = 2 * i + 1;
-      }
-    }
+  // ---- DMA: wave w fills K rows 8w..8w+7 (two 1 KB instructions) and V^T rows 16w..16w+15 (two)
+  const char* kg = (const char*)(a.ws + a.plan.off_k) + (size_t)pair * SP * 256;
+  const char* vg = (const char*)(a.ws + a.plan.off_vt) + (size_t)pair * 128 * SP * 2;
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int krow = 8 * wu + 4 * i + (lane >> 4), kpos = lane & 15;
+    koff[i] = krow * 256 + 16 * (kpos ^ (krow & 15));
+    const int vrow = 16 * wu + 8 * i + (lane >> 3), vpos = lane & 7;
+    voff[i] = vrow * SP * 2 + 16 * (vpos ^ ((vrow >> 1) & 7));
   }
-  // ---- stage the raw query rows of the tile in LDS (reusing the key buffers)
-  bf16* qs = &ks[0][0];  // [128][128], 32 KB
-  const bf16* qg = (const bf16*)a.q;
-  for (int c = tid; c < FQ * 16; c += 256) {
-    int row = c >> 4, ch = c & 15;
-    int t = min(q0 + row, S - 1);
-    *(uint4*)&qs[row * 128 + ch * 8] = *(const uint4*)(qg + (((size_t)b * S + t) * NH + h) * 128 + ch * 8);
-  }
-  __syncthreads();
-  // ---- query operands: dims [nope(h) | rotated retained pairs], scaled by log2(e)/sqrt(d_h)
-  const float scale = kLog2e / sqrtf(128.f);
+  // the first eight retained pairs of the head, read before anything else is in flight
+  constexpr int RP = 8;
+  int pp[RP];
+#pragma unroll
+  for (int j = 0; j < RP; ++j)
+    if (j < r) pp[j] = load_pair(a.pair_idx, h * r + j, 64);
+  MLA_WAIT_VMCNT(0);
+  const uint32_t ring_lds = lds_addr_of(ring);
+  auto issue = [&](int kt) {
+    const int slot = kt % FNS;
+    const uint32_t kl = ring_lds + slot * SLOT + wu * 2048, vl = ring_lds + slot * SLOT + KT_BYTES + wu * 2048;
+    const char* kb = kg + (size_t)kt * FKV * 256;
+    const char* vb = vg + (size_t)kt * FKV * 2;
+    dma16(kb, koff[0], kl);
+    dma16(kb, koff[1], kl + 1024);
+    dma16(vb, voff[0], vl);
+    dma16(vb, voff[1], vl + 1024);
+  };
+  issue(0);
+  if (n_kv > 1) issue(1);
+
+  // ---- query operand: Q[row][16s + 8hb .. +7] in the original dim order, retained pairs rotated at the
+  // row's position, scaled by log2(e)/sqrt(d_h)
+  const int pos = min(myq, S - 1);
+  const bf16* qrow = (const bf16*)a.q + (((size_t)b * S + pos) * NH + h) * 128 + 8 * hb;
   bf16x8 qv[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qv[s] = *(const bf16x8*)(qrow + 16 * s);
+  // rotation factors of the first eight retained pairs, loaded in the same round as the query rows
+  float pc[RP], ps[RP];
+#pragma unroll
+  for (int j = 0; j < RP; ++j)
+    if (j < r) {
+      pc[j] = a.rope_cos[(size_t)pos * 64 + pp[j]];
+      ps[j] = a.rope_sin[(size_t)pos * 64 + pp[j]];
+    }
+  MLA_WAIT_VMCNT(0);  // query rows (and tiles 0, 1) complete before the loop
   {
-    const bf16* qrow = qs + (32 * w + ql) * 128;
-    const int pos = min(myq, S - 1);
+    float x[8][8];
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
+    for (int s = 0; s < 8; ++s)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = 16 * s8 + 8 * hb + u;
-        float v;
-        if (e < dn) {
-          v = (float)qrow[nope_idx[e]];
-        } else {
-          const int j = (e - dn) >> 1, c = (e - dn) & 1;
-          const int p = pairs[j];
-          const float x0 = (float)qrow[2 * p], x1 = (float)qrow[2 * p + 1];
-          const float cs = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
-          v = c ? (x0 * sn + x1 * cs) : (x0 * cs - x1 * sn);
-        }
-        qv[s8][u] = (bf16)(v * scale);
-      }
+      for (int u = 0; u < 8; ++u) x[s][u] = (float)qv[s][u];
+    // pair p = dims 2p, 2p+1 sits in k-step p/8, half-wave (p/4)%2, elements 2(p%4), 2(p%4)+1
+    auto rotate = [&](int p, float cs, float sn) {
+      if (hb != ((p >> 2) & 1)) return;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2)
+          if ((p >> 3) == s && (p & 3) == u2) {
+            const float x0 = x[s][2 * u2], x1 = x[s][2 * u2 + 1];
+            x[s][2 * u2] = x0 * cs - x1 * sn;
+            x[s][2 * u2 + 1] = x0 * sn + x1 * cs;
+          }
+    };
+#pragma unroll
+    for (int j = 0; j < RP; ++j)
+      if (j < r) rotate(pp[j], pc[j], ps[j]);
+    for (int j = RP; j < r; ++j) {
+      const int p = load_pair(a.pair_idx, h * r + j, 64);
+      rotate(p, a.rope_cos[(size_t)pos * 64 + p], a.rope_sin[(size_t)pos * 64 + p]);
     }
+    const float scale = kLog2e / sqrtf(128.f);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) qv[s][u] = (bf16)(x[s][u] * scale);
   }
-  __syncthreads();
-
-  const bf16* khat = (const bf16*)(a.ws + a.plan.off_k) + ((size_t)b * NH + h) * S * dn;
-  const bf16* vt = (const bf16*)(a.ws + a.plan.off_vt) + ((size_t)b * NH + h) * 128 * S;
-  const bf16* kr = (const bf16*)a.krope;
-  const int nkc = dn / 8;  // 16-byte chunks of a key row that come from K^
-  const int n_kv = min((S + FKV - 1) / FKV, (q0 + FQ - 1) / FKV + 1);
-
-  u32x4 kreg[4], vreg[2][2];
-  // every load of a thread reads the same 16-byte column chunk: from K^ (nope dims) or from k_rope
-  const int kch = tid & 15;
-  const bool from_rope = kch >= nkc;
-  const bf16* kbase = from_rope ? kr + (size_t)h * R2 + (kch - nkc) * 8 : khat + kch * 8;
-  const size_t krow_stride = from_rope ? (size_t)NH * R2 : (size_t)dn;
-  const size_t kseq_off = from_rope ? (size_t)b * a.t_max * NH * R2 : 0;
-  auto gload = [&](int kv0) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      int t = min(kv0 + it * 16 + (tid >> 4), S - 1);
-      kreg[it] = *(const u32x4*)(kbase + kseq_off + (size_t)t * krow_stride);
-    }
-    if (kv0 + FKV <= S) {
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        int pidx = it * 256 + tid, row = pidx >> 2, g = pidx & 3;
-        const bf16* src = vt + (size_t)row * S + kv0 + 16 * g;
-        vreg[it][0] = *(const u32x4*)(src);
-        vreg[it][1] = *(const u32x4*)(src + 8);
-      }
-    } else {
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        int pidx = it * 256 + tid, row = pidx >> 2, g = pidx & 3;
-        int k0 = kv0 + 16 * g;
-        const bf16* src = vt + (size_t)row * S;
-        bf16x8 lo, hi;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          lo[u] = k0 + u < S ? src[k0 + u] : (bf16)0.f;
-          hi[u] = k0 + 8 + u < S ? src[k0 + 8 + u] : (bf16)0.f;
-        }
-        vreg[it][0] = __builtin_bit_cast(u32x4, lo);
-        vreg[it][1] = __builtin_bit_cast(u32x4, hi);
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      int c = it * 256 + tid, row = c >> 4, ch = c & 15;
-      *(u32x4*)&ks[buf][row * KP + ch * 8] = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      int pidx = it * 256 + tid, row = pidx >> 2, g = pidx & 3;
-      // keys 16g + {0..3, 8..11} first, then {4..7, 12..15}
-      u32x4 x = vreg[it][0], y = vreg[it][1];
-      *(u32x4*)&vs[buf][row * VP + 16 * g] = u32x4{x.x, x.y, y.x, y.y};
-      *(u32x4*)&vs[buf][row * VP + 16 * g + 8] = u32x4{x.z, x.w, y.z, y.w};
-    }
-  };
 
   f32x16 oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-  const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
+  const int wq_lo = q0 + 32 * wu, wq_hi = wq_lo + 31;  // wave-uniform (scalar) bounds
+  constexpr float kRescale = 8.f;
+  f32x16 sacc[2];
+  bf16x8 pb[2][2];
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int it = 0; it < n_kv; ++it) {
-    const int buf = it & 1, kv0 = it * FKV;
-    if (it + 1 < n_kv) gload(kv0 + FKV);
-    if (kv0 <= wq_hi) {  // wave-uniform: some key of the tile is visible to some row of the wave
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-#pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) {
-          bf16x8 av = *(const bf16x8*)&ks[buf][(kb * 32 + ql) * KP + 16 * s8 + 8 * hb];
-          sacc[kb] = mfma32(av, qv[s8], sacc[kb]);
-        }
-      }
-      const bool need_mask = kv0 + FKV - 1 > wq_lo || kv0 + FKV > S;
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          if (need_mask) {
-            int key = kv0 + kb * 32 + 8 * (e >> 2) + 4 * hb + (e & 3);
-            if (key > myq || key >= S) sacc[kb][e] = -INFINITY;
-          }
-          mt = fmaxf(mt, sacc[kb][e]);
-        }
-      mt = fmaxf(mt, shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
-      float rs = 0.f;
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float p = exp2f(sacc[kb][e] - m_new);
-          rs += p;
-          pb[kb][e >> 3][e & 7] = (bf16)p;
-        }
-      rs += shfl_xor(rs, 32);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
+  // M phase of tile kt: O += P(kt-1) V(kt-1) (when tile kt-1 was visible), then S = K(kt) Q (when visible)
+  auto phase_m = [&](int kt) {
+    if (kt > 0 && (kt - 1) * FKV <= wq_hi) {
+      const char* vs = ring + ((kt - 1) % FNS) * SLOT + KT_BYTES;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        oacc[db] *= alpha;
+        const int row = db * 32 + ql;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            bf16x8 av = *(const bf16x8*)&vs[buf][(db * 32 + ql) * VP + kb * 32 + 16 * c + 8 * hb];
+            const bf16x8 av = *(const bf16x8*)(vs + row * 128 + 16 * ((4 * kb + 2 * c + hb) ^ ((row >> 1) & 7)));
             oacc[db] = mfma32(av, pb[kb][c], oacc[db]);
           }
       }
     }
-    if (it + 1 < n_kv) sstore(buf ^ 1);
-    __syncthreads();
+    // keep the two products apart: hoisting the score operands above the PV product would raise the
+    // register pressure past two waves per SIMD
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt < n_kv && kt * FKV <= wq_hi) {
+      const char* ks = ring + (kt % FNS) * SLOT;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x16{};
+        const int row = kb * 32 + ql;
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+          const bf16x8 av = *(const bf16x8*)(ks + row * 256 + 16 * ((2 * s8 + hb) ^ (row & 15)));
+          sacc[kb] = mfma32(av, qv[s8], sacc[kb]);
+        }
+      }
+    }
+  };
+  // V phase of tile kt: mask, online softmax (lazy rescale), P(kt) in bf16 for the next M phase
+  auto phase_v = [&](int kt) {
+    if (kt < 0 || kt * FKV > wq_hi) return;
+    const int kv0 = kt * FKV;
+    if (kv0 + FKV - 1 > wq_lo || kv0 + FKV > S) {
+      asm volatile("" ::: "memory");  // keep this a branch (only diagonal / last tiles pay for it)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kv0 + kb * 32 + 8 * (e >> 2) + 4 * hb + (e & 3);
+          if (key > myq || key >= S) sacc[kb][e] = -INFINITY;
+        }
+    }
+    float mt = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
+    mt = fmaxf(mt, shfl_xor(mt, 32));
+    const bool raise = mt > m_run + kRescale;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      asm volatile("" ::: "memory");  // keep this a branch (rare after the first tile)
+      const float m_new = raise ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(sacc[kb][e] - m_run);
+        rs += p;
+        pb[kb][e >> 3][e & 7] = (bf16)p;
+      }
+    rs += shfl_xor(rs, 32);
+    l_run += rs;
+  };
+
+  // The two waves sharing a SIMD (w and w + 4) run half a tile apart: waves 0-3 pass the barrier of
+  // tile kt before M(kt), waves 4-7 after M(kt-1), so that waves 4-7 run V(kt-1) while waves 0-3 run
+  // M(kt) and M(kt) while waves 0-3 run V(kt).  Every wave meets the same n_kv + 1 barriers.  A slot is
+  // refilled two tiles later, after barrier kt; the last reads of tile kt-2 (PV in M(kt-1)) precede that
+  // barrier in both groups, so four slots suffice.
+  const bool lagging = wu >= 4;
+  auto sync_tile = [&](int kt) {
+    // the own part of tile kt is complete once only tile kt+1's 4 loads may be outstanding
+    if (kt + 1 < n_kv) {
+      MLA_WAIT_VMCNT(4);
+    } else {
+      MLA_WAIT_VMCNT(0);
+    }
+    lds_barrier();
+    if (kt + 2 < n_kv) issue(kt + 2);
+  };
+  if (lagging) sync_tile(0);
+  for (int kt = 0; kt < n_kv; ++kt) {
+    if (!lagging) sync_tile(kt);
+    phase_m(kt);
+    if (lagging) sync_tile(kt + 1);
+    phase_v(kt);
   }
+  if (!lagging) sync_tile(n_kv);
+  phase_m(n_kv);  // PV of the last tile
 
   // ---- normalise and store through LDS (rows of 128 output dims, 16-byte stores)
+  __syncthreads();  // all waves are done with the ring (no DMA is outstanding after the last tile)
   const float inv = 1.f / l_run;
-  bf16* os = &ks[0][0] + w * 32 * KP;  // [32][KP] per wave
+  constexpr int OP = 136;  // row pitch in elements
+  bf16* os = (bf16*)ring + w * 32 * OP;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) os[ql * KP + db * 32 + 8 * (e >> 2) + 4 * hb + (e & 3)] = (bf16)(oacc[db][e] * inv);
+    for (int e4 = 0; e4 < 4; ++e4) {
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = (bf16)(oacc[db][4 * e4 + i] * inv);
+      *(bf16x4*)&os[ql * OP + db * 32 + 8 * e4 + 4 * hb] = v;
+    }
   __builtin_amdgcn_wave_barrier();
-  __syncthreads();
+  asm volatile("" ::: "memory");
   bf16* og = (bf16*)a.out;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    int c = i * 64 + lane, row = c >> 4, ch = c & 15;
-    int t = q0 + 32 * w + row;
-    if (t < S) *(uint4*)(og + (((size_t)b * S + t) * NH + h) * 128 + ch * 8) = *(const uint4*)&os[row * KP + ch * 8];
+    const int c = i * 64 + lane, row = c >> 4, ch = c & 15;
+    const int t = q0 + 32 * w + row;
+    if (t < S) *(u32x4*)(og + (((size_t)b * S + t) * NH + h) * 128 + ch * 8) = *(const u32x4*)&os[row * OP + ch * 8];
+  }
+}
+
+// Workgroup i of a (sequence, head) pair takes query tiles nqt-1-i and i, so every workgroup carries
+// the same causal work (nqt + 1 units of 256 x 256); a middle tile of an odd count runs alone.
+// Hardware dispatch places workgroup k on XCD k % 8: all workgroups of a pair share one XCD (and its
+// L2) when the pair count is a multiple of 8.
+__global__ __launch_bounds__(512, 1) void prefill_attn(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char ring[FNS * SLOT];
+  const int nqt = (a.seq_len + FQ - 1) / FQ, npw = (nqt + 1) / 2, pairs = a.batch * a.s.n_heads;
+  const int k = blockIdx.x;
+  int pair, i;
+  if ((pairs & 7) == 0) {
+    const int j = k >> 3;
+    pair = (k & 7) + 8 * (j / npw);
+    i = j % npw;
+  } else {
+    pair = k / npw;
+    i = k % npw;
+  }
+  attend_query_tile(a, ring, pair, nqt - 1 - i);
+  if (nqt - 1 - i != i) {
+    __syncthreads();  // the ring and the output staging area are reused
+    attend_query_tile(a, ring, pair, i);
   }
 }
 
 }  // namespace
 
 bool prefill_supported(const Shape& s) {
-  return s.dtype == 1 && s.fmt == 0 && s.d_head == 128 && (s.r2() % 8) == 0 && s.d_kv % GK == 0;
+  return s.dtype == 1 && s.fmt == 0 && s.d_head == 128 && s.d_kv % 64 == 0;
 }
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 PrefillPlan plan_prefill(const Shape& s, int batch, int seq_len) {
   PrefillPlan p{};
+  p.s_pad = ((seq_len + FKV - 1) / FKV) * FKV;
   size_t off = 0;
   p.off_k = off;
-  off = align256(off + (size_t)batch * s.n_heads * seq_len * s.d_nope() * 2);
+  off = align256(off + (size_t)batch * s.n_heads * p.s_pad * 128 * 2);
   p.off_vt = off;
-  off = align256(off + (size_t)batch * s.n_heads * s.d_head * seq_len * 2);
-  p.off_q = off;
+  off = align256(off + (size_t)batch * s.n_heads * 128 * p.s_pad * 2);
   p.total = off;
   return p;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
-  const int S = a.seq_len, B = a.batch, NH = a.s.n_heads;
-  {
-    const int M = B * S, N = NH * a.s.d_nope();
-    if (N > 0) {
-      int grid = ((M + GT - 1) / GT) * ((N + GT - 1) / GT);
-      hipLaunchKernelGGL(rec_gemm<0>, dim3(grid), dim3(256), 0, st, a, M, N);
-    }
-  }
-  {
-    const int M = NH * a.s.d_head, N = B * S;
-    int grid = ((M + GT - 1) / GT) * ((N + GT - 1) / GT);
-    hipLaunchKernelGGL(rec_gemm<1>, dim3(grid), dim3(256), 0, st, a, M, N);
-  }
-  dim3 g((S + FQ - 1) / FQ, NH, B);
-  hipLaunchKernelGGL(prefill_attn, g, dim3(256), 0, st, a);
+  const int S = a.seq_len, B = a.batch, NH = a.s.n_heads, SP = a.plan.s_pad;
+  hipLaunchKernelGGL(rec_k_gemm, dim3(((B * S + 255) / 256) * NH), dim3(256), 0, st, a, B * S);
+  hipLaunchKernelGGL(rec_vt_gemm, dim3(NH * ((B * SP + 255) / 256)), dim3(256), 0, st, a, B * SP);
+  const int nqt = (S + FQ - 1) / FQ;
+  hipLaunchKernelGGL(prefill_attn, dim3(B * NH * ((nqt + 1) / 2)), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

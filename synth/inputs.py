@@ -27,6 +27,7 @@ FAMILIES = {
     "tiny": (576, 9, 64, 0),  # SmolLM-135M-shaped layer
     "llama": (4096, 32, 128, 1),  # Llama-2-7B-shaped layer
     "mid": (1024, 32, 128, 2),  # Llama head shapes with a narrower model width (fast tests)
+    "odd": (640, 5, 128, 3),  # Llama head dim, a head count that is not a multiple of 8 (tests)
 }
 
 

@@ -1,6 +1,6 @@
 """GPU parity of mla_cache_append + mla_prefill (causal, unabsorbed) against the oracle, through the C ABI.
 
-Small cases compare every query row; lengths that are not multiples of the 64-key / 128-query tiles
+Small cases compare every query row; lengths that are not multiples of the 64-key / 256-query tiles
 exercise the ragged tails, and a one-token prompt reduces to the first value row.  The full-size case
 (4 sequences x 4096 tokens, Llama-2-7B shapes) compares sampled query rows, including both ends of the
 causal range and tile boundaries."""
@@ -61,6 +61,21 @@ def test_prefill_single_token_and_one_past_tile():
     cfg = scaled(CONFIGS[2], family="mid")
     run_prefill_case(cfg, S=1, B=1)
     run_prefill_case(cfg, S=65, B=1)
+
+
+def test_prefill_mid_several_query_tiles():
+    """Three 256-row query tiles, the last one ragged: every row against the oracle."""
+    run_prefill_case(scaled(CONFIGS[2], family="mid"), S=600, B=1)
+
+
+def test_prefill_two_pairs_per_head():
+    """r = 2: four retained dims per head, the RoPE keys fill only part of a 16-byte chunk."""
+    run_prefill_case(scaled(CONFIGS[2], family="mid", r_pairs=2), S=130, B=2)
+
+
+def test_prefill_head_count_not_multiple_of_8():
+    """5 heads x 3 sequences = 15 (sequence, head) pairs: the scheduler's non-XCD-grouped order."""
+    run_prefill_case(scaled(CONFIGS[2], family="odd"), S=300, B=3)
 
 
 @pytest.mark.slow
