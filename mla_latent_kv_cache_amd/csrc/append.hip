@@ -9,6 +9,7 @@
 #include <hip/hip_fp16.h>
 
 #include "common.h"
+#include "gemm.h"
 #include "kernels.h"
 
 namespace mla {
@@ -214,6 +215,107 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
       }
     }
   }
+}
+
+using AppCfg = GemmCfg<256, 192, 4>;
+
+// Epilogue of accumulator block (I, J): 32 output columns (one per lane, mod 32) x 32 tokens.
+template <int I, int J>
+__device__ __forceinline__ void append_gemm_block(const AppendArgs& a, const f32x16& v, const int* rows,
+                                                  const int* poss, int m0, int n0, int M) {
+  const int D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int c0 = n0 + wn * AppCfg::WN + J * 32;
+  const int n = c0 + (lane & 31);
+  if (c0 >= N) return;  // uniform across the wave
+  const int r = a.s.r_pairs, R2 = a.s.r2(), half = a.s.d_head / 2;
+  if (c0 < D) {
+    if (a.s.fmt == 0) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (m0 + ml < M) ((bf16*)a.ckv)[(size_t)rows[ml] * D + n] = (bf16)v[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float am = fabsf(v[e]);
+#pragma unroll
+        for (int msk = 1; msk < 32; msk <<= 1) am = fmaxf(am, shfl_xor(am, msk));
+        const __half s = int4_scale(am);
+        const int code = int4_code(v[e], __half2float(s));
+        const int partner = __shfl_xor(code, 1, 64);
+        const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (m0 + ml < M) {
+          const size_t row = (size_t)rows[ml];
+          if ((lane & 1) == 0)
+            ((uint8_t*)a.ckv)[row * (D / 2) + (n >> 1)] = (uint8_t)((code & 15) | ((partner & 15) << 4));
+          if ((lane & 31) == 0) ((__half*)a.ckv_scale)[row * (D / 32) + (n >> 5)] = s;
+        }
+      }
+    }
+  } else {
+    const int rel = n - D;
+    const int h = rel / (R2 > 0 ? R2 : 1);
+    const int jj = (rel - h * R2) >> 1, comp = rel & 1;
+    const bool colok = rel < NR;
+    const int p = colok ? load_pair(a.pair_idx, h * r + jj, half) : 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float partner = shfl_xor(v[e], 1);
+      const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (m0 + ml < M && colok) {
+        const int pos = poss[ml];
+        const float cs = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
+        const float x0 = comp ? partner : v[e], x1 = comp ? v[e] : partner;
+        const float o = comp ? (x0 * sn + x1 * cs) : (x0 * cs - x1 * sn);
+        ((bf16*)a.krope)[(size_t)rows[ml] * NR + rel] = (bf16)o;
+      }
+    }
+  }
+}
+// All blocks, unrolled at compile time (the accumulators stay in registers).
+template <int I, int J>
+__device__ __forceinline__ void append_gemm_blocks(const AppendArgs& a, f32x16 (&acc)[AppCfg::FM][AppCfg::FN],
+                                                   const int* rows, const int* poss, int m0, int n0, int M) {
+  append_gemm_block<I, J>(a, acc[I][J], rows, poss, m0, n0, M);
+  if constexpr (J + 1 < AppCfg::FN) {
+    append_gemm_blocks<I, J + 1>(a, acc, rows, poss, m0, n0, M);
+  } else if constexpr (I + 1 < AppCfg::FM) {
+    append_gemm_blocks<I + 1, 0>(a, acc, rows, poss, m0, n0, M);
+  }
+}
+
+// ------------------------------------------------------------------ MFMA path for long prompts (bf16)
+// Tiles of 256 tokens x 192 output columns through the shared GEMM main loop (gemm.h, four stages,
+// one workgroup per CU, a K loop over the whole model width); the tokens' cache rows and positions
+// are resolved once per tile.  Same epilogue as the 128 x 128 path.
+__global__ __launch_bounds__(256, 1) void append_gemm_bf16(AppendArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[AppCfg::LDS_BYTES];
+  __shared__ int rows[256], poss[256];
+  const int K = a.s.d_model, D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR;
+  const int M = a.batch * a.t_new;
+  const int n_tiles = (N + 191) / 192;
+  const int total = gridDim.x;
+  int bid = blockIdx.x;
+  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  const int m0 = (bid / n_tiles) * 256, n0 = (bid % n_tiles) * 192;  // consecutive tiles share tokens
+  const int tid = threadIdx.x;
+  if (m0 + tid < M) {
+    int pos;
+    rows[tid] = cache_row(a, m0 + tid, &pos);
+    poss[tid] = pos;
+  }
+  __syncthreads();
+  const bf16* x = (const bf16*)a.x;
+  auto a_row = [&](int i) { return x + (size_t)min(m0 + i, M - 1) * K; };
+  auto b_row = [&](int i) {
+    const int n = min(n0 + i, N - 1);
+    return n < D ? (const bf16*)a.w_dkv + (size_t)n * K : (const bf16*)a.w_krope + (size_t)(n - D) * K;
+  };
+  f32x16 acc[AppCfg::FM][AppCfg::FN];
+  gemm_tile<256, 192, 4>(lds, K, a_row, b_row, acc);
+  append_gemm_blocks<0, 0>(a, acc, rows, poss, m0, n0, M);
 }
 
 // Epilogue shared by the few-token paths: fin[m][c] holds output column n0 + c of token m (fp32);
@@ -464,6 +566,10 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(append_reduce, dim3((N + 31) / 32), dim3(1024), 0, st, a, ks);
   } else if (append_uses_mfma(a.s) && M <= SM_MAXM && a.s.d_model % (SM_WAVES * 16) == 0) {
     hipLaunchKernelGGL(append_small_bf16, dim3((N + 31) / 32), dim3(SM_WAVES * 64), 0, st, a);
+  } else if (append_uses_mfma(a.s) && a.s.d_model % 32 == 0 && ((M + 255) / 256) * ((N + 191) / 192) >= 192) {
+    // long prompts: enough 256 x 192 tiles to fill most CUs
+    const int grid = ((M + 255) / 256) * ((N + 191) / 192);
+    hipLaunchKernelGGL(append_gemm_bf16, dim3(grid), dim3(256), 0, st, a);
   } else if (append_uses_mfma(a.s)) {
     int grid = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
     hipLaunchKernelGGL(append_mfma_bf16, dim3(grid), dim3(256), 0, st, a);

@@ -70,17 +70,10 @@ __device__ __forceinline__ void gemm_tile(char* lds, int K, ARow a_row, BRow b_r
 #pragma unroll
     for (int i = 0; i < C::B_IPW; ++i) dma16_ptr(bsrc[i] + kt * 64, base + C::A_BYTES + (w * C::B_IPW + i) * 1024);
   };
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
   const int KT = K / C::BK;
-#pragma unroll
-  for (int s = 0; s < C::NSTG - 1; ++s)
-    if (s < KT) issue(s);
-  for (int kt = 0; kt < KT; ++kt) {
-    // own part of stage kt is complete once only the later issued stages may be outstanding
-    const int later = min(KT - 1, kt + C::NSTG - 2) - kt;
+  // own part of stage s is complete once only the stages issued after it may be outstanding
+  auto wait_stage = [&](int s) {
+    const int later = min(KT - 1, s + C::NSTG - 2) - s;
     if (C::NSTG > 3 && later >= 2) {
       MLA_WAIT_VMCNT(2 * C::IPW);
     } else if (later >= 1) {
@@ -88,24 +81,53 @@ __device__ __forceinline__ void gemm_tile(char* lds, int K, ARow a_row, BRow b_r
     } else {
       MLA_WAIT_VMCNT(0);
     }
-    lds_barrier();  // every wave's part of stage kt has landed; every wave is done with stage kt-1
-    if (kt + C::NSTG - 1 < KT) issue(kt + C::NSTG - 1);
-    const char* sa = lds + (kt % C::NSTG) * C::STAGE;
+  };
+  // operands of one k-slice of 16 (ks = 0, 1) of stage s
+  struct Frag {
+    bf16x8 a[C::FM], b[C::FN];
+  };
+  auto load = [&](Frag& f, int s, int ks) {
+    const char* sa = lds + (s % C::NSTG) * C::STAGE;
     const char* sb = sa + C::A_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[C::FM], bfr[C::FN];
+    for (int i = 0; i < C::FM; ++i)
+      f.a[i] = *(const bf16x8*)(sa + gemm_swz(wm * C::WM + 32 * i + (lane & 31), 2 * ks + (lane >> 5)));
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-        af[i] = *(const bf16x8*)(sa + gemm_swz(wm * C::WM + 32 * i + (lane & 31), 2 * ks + (lane >> 5)));
+    for (int j = 0; j < C::FN; ++j)
+      f.b[j] = *(const bf16x8*)(sb + gemm_swz(wn * C::WN + 32 * j + (lane & 31), 2 * ks + (lane >> 5)));
+  };
+  auto mma = [&](const Frag& f) {
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        bfr[j] = *(const bf16x8*)(sb + gemm_swz(wn * C::WN + 32 * j + (lane & 31), 2 * ks + (lane >> 5)));
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
+      for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
+  };
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
+  // Stage s is read after the barrier that follows every wave's wait for its part of s; that barrier
+  // also ends all reads of stage s-1, whose slot then receives stage s + NSTG - 1.  The second slice
+  // of a stage is loaded before the first slice's MFMAs, the next stage's first slice right after its
+  // barrier, so LDS latency hides under MFMAs that are already issued.
+#pragma unroll
+  for (int s = 0; s < C::NSTG - 1; ++s)
+    if (s < KT) issue(s);
+  wait_stage(0);
+  lds_barrier();
+  if (C::NSTG - 1 < KT) issue(C::NSTG - 1);
+  Frag f0, f1;
+  load(f0, 0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    load(f1, kt, 1);
+    mma(f0);
+    if (kt + 1 < KT) {
+      wait_stage(kt + 1);
+      lds_barrier();
+      if (kt + C::NSTG < KT) issue(kt + C::NSTG);
+      load(f0, kt + 1, 0);
     }
+    mma(f1);
   }
 }
 

@@ -107,3 +107,27 @@ def oracle_cache(cfg, layer, x):
 def decode_query(cfg, layer, x_last):
     """Raw query of the decode token (the sequence's last token), rounded to the device dtype."""
     return synth.query_rows(x_last[None, :], layer["w_q"], cfg.dtype).reshape(cfg.n_heads, cfg.d_head)
+
+
+def check_int4_cache(c, codes, scales):
+    """GPU int4 codes against the oracle's codec applied to the oracle's fp32 latent.  The GPU quantises its
+    own fp32 accumulator, which differs from the oracle's latent by accumulation order, so a code may differ
+    only where the oracle's quotient lies within 1e-3 of a rounding boundary (or the absmax itself sits at an
+    fp16 rounding boundary of the scale); every dequantised value stays within half a step of the latent."""
+    c32 = c.astype(np.float32)
+    oc, osc = oracle.quantize_int4_g32(c32)
+    s_gpu = scales.astype(np.float32)
+    assert np.all(np.isfinite(s_gpu))
+    same_scale = s_gpu == osc.astype(np.float32)
+    assert same_scale.mean() > 0.999, f"scales differ in {1 - same_scale.mean():.2e} of groups"
+    g_codes = codes.reshape(codes.shape[0], -1, 32)
+    o_codes = oc.reshape(oc.shape[0], -1, 32)
+    quot = (c32.reshape(c.shape[0], -1, 32) / osc.astype(np.float32)[..., None])
+    near = np.abs(np.abs(quot - np.floor(quot)) - 0.5) < 1e-3
+    diff = (g_codes != o_codes) & same_scale[..., None]
+    assert not np.any(diff & ~near), f"{np.count_nonzero(diff & ~near)} int4 codes differ away from a tie"
+    deq = g_codes.astype(np.float64) * s_gpu[..., None]
+    err = np.abs(deq - c.reshape(deq.shape))
+    bound = s_gpu[..., None] * 0.5 + 1e-6 * np.abs(c.reshape(deq.shape)) + 1e-6
+    assert np.all(err <= bound + s_gpu[..., None] * 1e-3)
+    log(f"  int4: {np.count_nonzero(diff)} tie-adjacent code differences of {diff.size}")
