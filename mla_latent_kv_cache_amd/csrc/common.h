@@ -37,6 +37,12 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x32 fp16 MFMA (same lane layout as mfma16).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma16h(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 // LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane j supplies the
 // address of 4 consecutive 16-bit elements; lane i receives element (i % 4) of the chunks addressed
 // by lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4.  With lane j addressing row (r0 + j/4), columns
@@ -109,6 +115,16 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
       :
       : "v"(voff), "s"(base), "s"(lds_addr)
       : "memory");  // M0 is rewritten here; no other instruction in these kernels reads M0
+}
+// 4 bytes per lane (global_load_lds_dword) into LDS at lds_addr + 4 * lane; otherwise as dma16.
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds_addr)
+      : "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;

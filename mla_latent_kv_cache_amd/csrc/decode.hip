@@ -774,6 +774,409 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ 2d. attention, one tile stream per wave
+// For shapes whose 16-token tiles are small (latent width 256 in bf16, int4 latents): the workgroup takes
+// a work item and each wave a quarter of it in whole tiles, streamed through the wave's own LDS ring by
+// direct-to-LDS DMA with no barrier.  Scores and the softmax are computed once per tile (no exchange
+// between waves); the four waves merge (m, l, O) through LDS at the end, so the workspace holds one
+// partial result per work item as for the other kernels.
+//   scores  S[t][h] = C[t] . q~[h]: MFMA 16x16x32, A = latent rows (int4: dequantised in registers with
+//           the (token, group) scale), B = q~ in registers, two blocks of 16 heads.  Lane chunk c of a
+//           32-wide k-step covers latent columns [c D/4, (c+1) D/4), so its operands are contiguous.
+//   PV      O^T[k][h] += C^T[k][t] P[t][h]: MFMA 32x32x16 over the tile's 16 tokens, A = transposed
+//           latent reads (bf16: 16-bit transpose read; int4: 4-bit transpose read giving two column
+//           blocks at once, codes scaled per token), B = P from a per-wave LDS scratch (P^T rows).
+// Latent rows keep their 16-byte chunks XOR-swizzled by token so that both operand reads avoid bank
+// conflicts.  Softmax uses a per-head reference set from the first tile's maximum; it is only raised
+// when a head's tile sum leaves [0, 2^64] (scores 64 log2-units above it), which restarts the wave's
+// range instead of rescaling O (the accumulators fill half the register file).
+template <int D, int R2, int FMT, int NSLOT>
+struct WaveTile {
+  static constexpr int TT = 16;
+  static constexpr int RB = FMT == 0 ? D * 2 : D / 2;      // latent bytes per token
+  static constexpr int LB = TT * RB;
+  static constexpr int SRB = FMT == 1 ? (D / 32) * 2 : 0;  // scale bytes per token
+  static constexpr int SB = TT * SRB;
+  static constexpr int KRB = 32 * R2 * 2;                  // RoPE key bytes per token
+  static constexpr int KB = TT * KRB;
+  static constexpr int SLOT = LB + SB + KB;
+  static constexpr int PS = 32 * TT * 2;                   // P^T scratch [32 heads][16 tokens] bf16
+  static constexpr int ST = FMT == 1 ? (D / 32) * TT * 2 : 0;  // scales transposed [group][token]
+  static constexpr int WAVE_BYTES = NSLOT * SLOT + PS + ST;
+  static constexpr int LDS_BYTES = 4 * WAVE_BYTES;
+  static constexpr int NL = LB / 1024, NK = KB / 1024, NSC = SB / 256;  // DMA instructions per tile
+  static constexpr int IPT = NL + NK + NSC;
+  static constexpr int NSK = D / 32;  // score k-steps (lane chunks of D/4 columns, 8 per k-step)
+  static constexpr int NB = D / 32;   // 32-column output blocks
+  static constexpr int SWM = (RB / 16 < 16 ? RB / 16 : 16) - 1;
+  static_assert(LB % 1024 == 0 && KB % 1024 == 0 && SB % 256 == 0, "DMA granularity");
+  static_assert(LDS_BYTES <= 160 * 1024 && 4 * WAVE_BYTES >= 65536 + 2048, "LDS");  // merge: 2 KB + 64 KB
+  static_assert(NSLOT == 2 || NSLOT == 3, "ring depth");
+};
+
+// Score operand from eight int4 codes in fp16, in the element order (n0, n4, n1, n5, n2, n6, n3, n7):
+// each 16-bit half is built as fp16(1024 + (n ^ 8)) from the bits, 1032 subtracted exactly, then scaled
+// (one rounding, 11-bit mantissa) with packed fp16 arithmetic.
+__device__ __forceinline__ f16x8 dequant8h(uint32_t wd, uint32_t s2) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t u = wd ^ 0x88888888u;
+  const f16x2 off = {(_Float16)1032.f, (_Float16)1032.f}, sc = __builtin_bit_cast(f16x2, s2);
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 v = (__builtin_bit_cast(f16x2, ((u >> (4 * i)) & 0x000F000Fu) | 0x64006400u) - off) * sc;
+    r[2 * i] = v[0];
+    r[2 * i + 1] = v[1];
+  }
+  return r;
+}
+// Eight signed nibbles of `wd` (low first), element i times s[i], as bf16 (PV operand).
+__device__ __forceinline__ bf16x8 dequant8v(uint32_t wd, const float* s) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)((float)(((int)(wd << (28 - 4 * i))) >> 28) * s[i]);
+  return r;
+}
+
+template <int D, int R2, int FMT, int NSLOT>
+__global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a) {
+  using W = WaveTile<D, R2, FMT, NSLOT>;
+  constexpr int TT = W::TT, SWM = W::SWM;
+  constexpr float kSumLimit = 18446744073709551616.f;  // 2^64
+  __shared__ __attribute__((aligned(1024))) char lds[W::LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  WorkItem wi;
+  if (!locate_item(a, blockIdx.x, wi)) return;
+  const int b = wi.b;
+  // the wave's quarter of the item, in whole tiles
+  const int ntile = (wi.t1 - wi.t0 + TT - 1) / TT, per = (ntile + 3) / 4;
+  const int u0 = wi.t0 + TT * min(ntile, w * per);
+  const int u1 = min(wi.t1, wi.t0 + TT * min(ntile, (w + 1) * per));
+  const int nt = u1 > u0 ? (u1 - u0 + TT - 1) / TT : 0;
+
+  char* mine = lds + w * W::WAVE_BYTES;
+  char* pscr = mine + NSLOT * W::SLOT;  // P^T [32 heads][16 tokens]
+  char* stp = pscr + W::PS;             // scales [group][16 tokens] (int4)
+  const uint32_t mine_lds = lds_addr_of(mine);
+  const size_t rowb = (size_t)b * a.t_max;
+  const char* lat = (const char*)a.ckv + rowb * W::RB;
+  const char* scl = FMT == 1 ? (const char*)a.ckv_scale + rowb * W::SRB : (const char*)a.ckv;
+  const char* kro = (const char*)a.krope + rowb * W::KRB;
+  // tile j of the wave -> slot j % NSLOT; rows past the wave's range repeat its last row (masked later)
+  auto issue = [&](int j) {
+    // per-lane offsets are recomputed at every call (an opaque copy of the lane id keeps the compiler
+    // from hoisting ~NL + NSC + NK of them into registers for the whole loop)
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int tt = u0 + TT * j;
+    const uint32_t base = mine_lds + (j % NSLOT) * W::SLOT;
+    const int last = u1 - 1;
+#pragma unroll
+    for (int i = 0; i < W::NL; ++i) {
+      const int off = 1024 * i + 16 * lane, row = off / W::RB, pos = (off % W::RB) / 16;
+      const int tok = min(tt + row, last);
+      dma16(lat, (uint32_t)(tok * W::RB + 16 * (pos ^ (row & SWM))), base + 1024 * i);
+    }
+#pragma unroll
+    for (int i = 0; i < W::NSC; ++i) {
+      constexpr int SRB1 = W::SRB > 0 ? W::SRB : 1;  // (no scale rows for bf16 latents: NSC == 0)
+      const int off = 256 * i + 4 * lane, row = off / SRB1, within = off % SRB1;
+      const int tok = min(tt + row, last);
+      dma4(scl, (uint32_t)(tok * W::SRB + within), base + W::LB + 256 * i);
+    }
+#pragma unroll
+    for (int i = 0; i < W::NK; ++i) {
+      const int off = 1024 * i + 16 * lane, row = off / W::KRB, within = off % W::KRB;
+      const int tok = min(tt + row, last);
+      dma16(kro, (uint32_t)(tok * W::KRB + within), base + W::LB + W::SB + 1024 * i);
+    }
+  };
+  constexpr int PF = NSLOT - 1;  // tiles in flight ahead of the one being computed
+
+  // q~ operands (B of the score MFMA): head 16 hb2 + lane%16, columns c D/4 + 8 s .. +7 (c = lane/16);
+  // int4 latents use fp16 operands with the columns in the dequantiser's order (0,4,1,5,2,6,3,7).
+  // And the rotated query pairs of the lane's two heads.
+  const int hl = lane & 15, c4 = lane >> 4;
+  const bf16* qt = (const bf16*)(a.ws + a.plan.off_qt) + (size_t)b * 32 * D;
+  bf16x8 qv[2][FMT == 0 ? W::NSK : 1];
+  f16x8 qh[2][FMT == 1 ? W::NSK : 1];
+#pragma unroll
+  for (int hb2 = 0; hb2 < 2; ++hb2)
+#pragma unroll
+    for (int s = 0; s < W::NSK; ++s) {
+      const bf16x8 v = *(const bf16x8*)(qt + (size_t)(16 * hb2 + hl) * D + c4 * (D / 4) + 8 * s);
+      if (FMT == 0) {
+        qv[hb2][FMT == 0 ? s : 0] = v;
+      } else {
+        constexpr int PERM[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qh[hb2][FMT == 1 ? s : 0][i] = (_Float16)(float)v[PERM[i]];
+      }
+    }
+  float qr[2][R2];
+  {
+    const float* qrp = (const float*)(a.ws + a.plan.off_qr) + (size_t)b * 32 * R2;
+#pragma unroll
+    for (int hb2 = 0; hb2 < 2; ++hb2)
+#pragma unroll
+      for (int c = 0; c < R2; ++c) qr[hb2][c] = qrp[(16 * hb2 + hl) * R2 + c];
+  }
+  MLA_WAIT_VMCNT(0);  // query operands complete before the loop
+  asm volatile("" ::: "memory");
+
+  f32x16 oacc[W::NB];
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  typedef bf16 kv_t __attribute__((ext_vector_type(R2)));
+
+  bool restart;
+  do {  // runs again only after a restart (see below)
+  restart = false;
+#pragma unroll
+  for (int j = 0; j < PF; ++j)
+    if (j < nt) issue(j);
+#pragma unroll
+  for (int g = 0; g < W::NB; ++g) oacc[g] = f32x16{};
+  l_run[0] = l_run[1] = 0.f;
+  bool any_pv = false;  // some tile has been added to O since the last (re)start
+  for (int j = 0; j < nt; ++j) {
+    // own DMA of tile j complete once only the later issued tiles may be outstanding
+    if (NSLOT == 3 && j + 1 < nt) {
+      MLA_WAIT_VMCNT(W::IPT);
+    } else {
+      MLA_WAIT_VMCNT(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // the previous tile's LDS reads are done: its slot is free
+    asm volatile("" ::: "memory");
+    if (j + PF < nt) issue(j + PF);
+    const char* lt = mine + (j % NSLOT) * W::SLOT;
+    const char* sct = lt + W::LB;
+    const char* kt = lt + W::LB + W::SB;
+    const int tt = u0 + TT * j;
+    const int st = lane & 15;  // this lane's token row for the score operand
+
+    // ---- scores
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (FMT == 0) {
+#pragma unroll
+      for (int s = 0; s < W::NSK; ++s) {
+        const int chunk = c4 * (D / 32) + s;
+        const bf16x8 av = *(const bf16x8*)(lt + st * W::RB + 16 * (chunk ^ (st & SWM)));
+        sacc[0] = mfma16(av, qv[0][FMT == 0 ? s : 0], sacc[0]);
+        sacc[1] = mfma16(av, qv[1][FMT == 0 ? s : 0], sacc[1]);
+      }
+    } else {
+      constexpr int GPC = D / 128;  // 32-column groups per lane chunk (16-byte code chunks)
+      uint32_t sc2[GPC];            // the token's scale of each group, in both fp16 halves
+#pragma unroll
+      for (int q4 = 0; q4 < GPC; ++q4) {
+        const uint32_t hs = *(const unsigned short*)(sct + st * W::SRB + 2 * (c4 * GPC + q4));
+        sc2[q4] = hs | (hs << 16);
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < GPC; ++q4) {
+        const int chunk = c4 * GPC + q4;
+        const u32x4 cw = *(const u32x4*)(lt + st * W::RB + 16 * (chunk ^ (st & SWM)));
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const f16x8 av = dequant8h(cw[s2], sc2[q4]);
+          sacc[0] = mfma16h(av, qh[0][FMT == 1 ? 4 * q4 + s2 : 0], sacc[0]);
+          sacc[1] = mfma16h(av, qh[1][FMT == 1 ? 4 * q4 + s2 : 0], sacc[1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // this tile's scales, transposed to [group][token] for the PV operand
+      constexpr int GPL = (D / 32) / 4;  // groups per lane (64 lanes = 16 tokens x 4)
+#pragma unroll
+      for (int u = 0; u < GPL; ++u) {
+        const int t = lane >> 2, g = GPL * (lane & 3) + u;
+        *(__half*)(stp + (g * TT + t) * 2) = *(const __half*)(sct + t * W::SRB + 2 * g);
+      }
+    }
+    // RoPE term of the lane's 2 x 4 (token, head) pairs: tokens 4 c4 + e, heads hl + 16 hb2
+#pragma unroll
+    for (int hb2 = 0; hb2 < 2; ++hb2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const kv_t kk = *(const kv_t*)(kt + (4 * c4 + e) * W::KRB + (16 * hb2 + hl) * R2 * 2);
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < R2; ++c) acc = fmaf(qr[hb2][c], (float)kk[c], acc);
+        sacc[hb2][e] += acc;
+      }
+    if (tt + TT > u1) {  // last, partial tile: mask rows past the range
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int hb2 = 0; hb2 < 2; ++hb2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (tt + 4 * c4 + e >= u1) sacc[hb2][e] = -INFINITY;
+    }
+
+    // ---- softmax with a lazily raised reference (per head: lanes hl, hl+16, hl+32, hl+48 share it)
+    float p[2][4], rs[2];
+#pragma unroll
+    for (int hb2 = 0; hb2 < 2; ++hb2) {
+      rs[hb2] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[hb2][e] = __builtin_amdgcn_exp2f(sacc[hb2][e] - m_run[hb2]);
+        rs[hb2] += p[hb2][e];
+      }
+      rs[hb2] += shfl_xor(rs[hb2], 16);
+      rs[hb2] += shfl_xor(rs[hb2], 32);
+    }
+    const bool raise0 = !(rs[0] <= kSumLimit), raise1 = !(rs[1] <= kSumLimit);
+    if (__builtin_amdgcn_ballot_w64(raise0 || raise1)) {
+      asm volatile("" ::: "memory");  // keep this a branch (first tile; later only for extreme inputs)
+#pragma unroll
+      for (int hb2 = 0; hb2 < 2; ++hb2) {
+        float mt = fmaxf(fmaxf(sacc[hb2][0], sacc[hb2][1]), fmaxf(sacc[hb2][2], sacc[hb2][3]));
+        mt = fmaxf(mt, shfl_xor(mt, 16));
+        mt = fmaxf(mt, shfl_xor(mt, 32));
+        if (hb2 == 0 ? raise0 : raise1) m_run[hb2] = fmaxf(m_run[hb2], mt);
+      }
+      if (any_pv) {
+        // a head's scores outgrew its reference by ~2^64 after tiles were accumulated: start the
+        // wave's range again with the raised references (O and l restart from zero; the loop only
+        // comes back here after a further jump of that size, so restarts are bounded)
+        MLA_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        asm volatile("" ::: "memory");
+        restart = true;
+        break;
+      }
+#pragma unroll
+      for (int hb2 = 0; hb2 < 2; ++hb2) {
+        rs[hb2] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[hb2][e] = __builtin_amdgcn_exp2f(sacc[hb2][e] - m_run[hb2]);
+          rs[hb2] += p[hb2][e];
+        }
+        rs[hb2] += shfl_xor(rs[hb2], 16);
+        rs[hb2] += shfl_xor(rs[hb2], 32);
+      }
+    }
+    l_run[0] += rs[0];
+    l_run[1] += rs[1];
+    // P^T[head][token] in bf16: the lane's 4 tokens of each of its two heads
+#pragma unroll
+    for (int hb2 = 0; hb2 < 2; ++hb2) {
+      bf16x4 pv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[e] = (bf16)p[hb2][e];
+      *(bf16x4*)(pscr + ((16 * hb2 + hl) * TT + 4 * c4) * 2) = pv;
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+
+    // ---- PV: B = P^T[head l%32][tokens 8 hb .. +7]
+    const int hb = lane >> 5, grp = lane >> 4, jl = lane & 15;
+    const bf16x8 pbv = *(const bf16x8*)(pscr + ((lane & 31) * TT + 8 * hb) * 2);
+    if (FMT == 0) {
+#pragma unroll
+      for (int g = 0; g < W::NB; ++g) {
+        const int c0 = 32 * g + 16 * (grp & 1);
+        const int col = c0 + 4 * (jl & 3);
+        const int r0 = 8 * hb + (jl >> 2), r1 = r0 + 4;
+        const bf16x4 x0 = lds_read_tr16((const bf16*)(lt + r0 * W::RB + 16 * ((col >> 3) ^ (r0 & SWM)) + 2 * (col & 7)));
+        const bf16x4 x1 = lds_read_tr16((const bf16*)(lt + r1 * W::RB + 16 * ((col >> 3) ^ (r1 & SWM)) + 2 * (col & 7)));
+        oacc[g] = mfma32(cat(x0, x1), pbv, oacc[g]);
+      }
+    } else {
+      __builtin_amdgcn_wave_barrier();  // the transposed scales were written by other lanes
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int g = 0; g < W::NB; g += 2) {
+        // addressing lane jl: token 8 hb + (jl & 7), block g + (jl >> 3), 16 columns from 16 (grp & 1)
+        const int r = 8 * hb + (jl & 7), gg = g + (jl >> 3);
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        const v2i t4 = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(lt + r * W::RB + 16 * (gg ^ (r & SWM)) + 8 * (grp & 1)));
+        float s0[8], s1[8];
+        {
+          typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+          const f16x8 f0 = *(const f16x8*)(stp + (g * TT + 8 * hb) * 2);
+          const f16x8 f1 = *(const f16x8*)(stp + ((g + 1) * TT + 8 * hb) * 2);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            s0[q] = (float)f0[q];
+            s1[q] = (float)f1[q];
+          }
+        }
+        oacc[g] = mfma32(dequant8v((uint32_t)t4.x, s0), pbv, oacc[g]);
+        oacc[g + 1] = mfma32(dequant8v((uint32_t)t4.y, s1), pbv, oacc[g + 1]);
+        __builtin_amdgcn_sched_barrier(0);  // bound the live operands (the accumulators fill half the file)
+      }
+    }
+    any_pv = true;
+  }
+  } while (restart);
+
+  // ---- merge the four waves: weights exp2(m_w - M) per head, then O summed over waves in LDS
+  __syncthreads();  // every wave is done with its ring (its last wait drained its DMA)
+  float* mm = (float*)lds;  // [4][32] references, then [4][32] weights
+  float* ll = mm + 128;     // [4][32]
+  float* wt = mm + 256;     // [4][32]
+  if (lane < 16) {
+    mm[w * 32 + lane] = m_run[0];
+    mm[w * 32 + 16 + lane] = m_run[1];
+    ll[w * 32 + lane] = l_run[0];
+    ll[w * 32 + 16 + lane] = l_run[1];
+  }
+  __syncthreads();
+  float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * 2;
+  float* po = (float*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * 32 * D;
+  if (w == 0 && lane < 32) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, mm[ww * 32 + lane]);
+    float L = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float mw = mm[ww * 32 + lane];
+      const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      wt[ww * 32 + lane] = f;
+      L = fmaf(f, ll[ww * 32 + lane], L);
+    }
+    pml[2 * lane] = M;
+    pml[2 * lane + 1] = L;
+  }
+  __syncthreads();
+  // O in rounds of 128 columns: every wave stores its raw accumulators (straight from the accumulation
+  // registers), then wave w forms columns [32 w, 32 w + 32) as the weighted sum over the four waves
+  float* ob = (float*)(lds + 2048);  // [4 waves][32 heads][128 columns]
+  const int h = lane & 31, hb = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < D / 128; ++r) {
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const f32x16& o = oacc[4 * r + gg];
+        const int col = 32 * gg + 8 * e4 + 4 * hb;
+        *(f32x4*)&ob[(w * 32 + h) * 128 + col] = f32x4{o[4 * e4], o[4 * e4 + 1], o[4 * e4 + 2], o[4 * e4 + 3]};
+      }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = it * 64 + lane, hh = idx >> 3, c4x = idx & 7;  // 32 heads x 8 groups of 4 columns
+      const int col = 32 * w + 4 * c4x;
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) v += wt[ww * 32 + hh] * *(const f32x4*)&ob[(ww * 32 + hh) * 128 + col];
+      *(f32x4*)&po[(size_t)hh * D + 128 * r + col] = v;
+    }
+    __syncthreads();
+  }
+}
+
+template <int D, int R2, int FMT, int NSLOT>
+void launch_wave_attn(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_attn_wave<D, R2, FMT, NSLOT>), dim3(a.plan.max_items), dim3(256), 0, st, a);
+}
+
 // ------------------------------------------------------------------ 3. combine: merge, then W_uv
 // 3a. merge: one wave per (sequence, head).  Weights exp2(m_s - M) from the split maxima, denominator
 //     sum_s w_s l_s, normalised latent output o = sum_s w_s o_s / den into the workspace (fp32).  Each
@@ -922,6 +1325,12 @@ void launch_mfma_attn(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// Latent width 256 (bf16 or int4).  At width 512 the register-staged kernel is as fast for int4 (its
+// dequantisation runs on two workgroups per CU) and the DMA ring kernel faster for bf16.
+bool decode_uses_wave(const Shape& s) {
+  return s.dtype == 1 && s.n_heads == 32 && (s.r_pairs == 2 || s.r_pairs == 4) && s.d_kv == 256;
+}
+
 bool decode_uses_mfma(const Shape& s) {
   return s.dtype == 1 && s.n_heads == 32 && (s.d_kv == 256 || s.d_kv == 512) && (s.r_pairs == 2 || s.r_pairs == 4);
 }
@@ -937,7 +1346,7 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len) {
   DecodePlan p{};
   // one workgroup per CU for the specialised dense kernels (their LDS ring fills a CU), two otherwise
-  p.target = (decode_uses_mfma(s) && s.fmt == 0) ? 256 : 512;
+  p.target = (decode_uses_wave(s) || (decode_uses_mfma(s) && s.fmt == 0)) ? 256 : 512;
   p.cmax = 2048;
   if (!decode_uses_mfma(s)) {  // the generic kernel keeps a chunk of scores in LDS
     const long long room = 65536 / 4 - (long long)s.d_kv - s.r2() - 1;
@@ -979,7 +1388,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask) {
       hipLaunchKernelGGL(decode_qprep<bf16>, gq, dim3(64 * QW), 0, st, a);
   }
   if (phase_mask & 2) {
-    if (decode_uses_mfma(a.s)) {
+    if (decode_uses_wave(a.s)) {
+      const int r = a.s.r_pairs;
+      if (a.s.fmt == 1 && r == 4) launch_wave_attn<256, 8, 1, 3>(a, st);
+      else if (a.s.fmt == 1) launch_wave_attn<256, 4, 1, 3>(a, st);
+      else if (r == 4) launch_wave_attn<256, 8, 0, 2>(a, st);
+      else launch_wave_attn<256, 4, 0, 3>(a, st);
+    } else if (decode_uses_mfma(a.s)) {
       if (a.s.d_kv == 512 && a.s.r_pairs == 4) launch_mfma_attn<128, 8>(a, st);
       else if (a.s.d_kv == 512 && a.s.r_pairs == 2) launch_mfma_attn<128, 4>(a, st);
       else if (a.s.d_kv == 256 && a.s.r_pairs == 4) launch_mfma_attn<64, 8>(a, st);

@@ -88,6 +88,7 @@ hipError_t launch_quantize_int4(const float* in, int64_t n_groups, uint8_t* code
 // Shape predicates for the specialised paths (host side, used for dispatch and tests).
 bool append_uses_mfma(const Shape& s);
 bool decode_uses_mfma(const Shape& s);
+bool decode_uses_wave(const Shape& s);  // per-wave tile streams (int4 latents, latent width 256)
 bool prefill_supported(const Shape& s);
 // Dynamic LDS of the generic kernels fits the 64 KiB a launch may request.
 bool append_fits(const Shape& s);

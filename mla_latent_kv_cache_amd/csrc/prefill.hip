@@ -186,8 +186,8 @@ __global__ __launch_bounds__(256, 2) void rec_vt_gemm(PrefillArgs a, int N) {
 //   O^T[e][q]  += V^T[e][key] P[q][key] MFMA 32x32x16, A = V^T rows from LDS, B = P straight from the
 //                                      score registers (V^T keys are stored in the matching order)
 // K rows (256 B) are stored with their 16-byte chunks XOR-swizzled by row, V^T rows (128 B) by row/2, so
-// both operand reads are bank-conflict free.  The running max is raised lazily (only when a tile
-// exceeds it by more than 2^8), so O is rarely rescaled.  All query tiles of one (sequence, head) run
+// both operand reads are bank-conflict free.  Softmax uses a lazily raised reference instead of the
+// running max: the tile's maximum is computed (and O rescaled) only when a row sum leaves [0, 2^16].  All query tiles of one (sequence, head) run
 // on one XCD, longest first, so their shared K / V^T reads hit that XCD's L2.
 constexpr int FQ = 256, FKV = 64, FNS = 4;
 constexpr int KT_BYTES = FKV * 256, VT_BYTES = 128 * FKV * 2, SLOT = KT_BYTES + VT_BYTES;
@@ -288,7 +288,7 @@ __device__ __forceinline__ void attend_query_tile(const PrefillArgs& a, char* ri
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const int wq_lo = q0 + 32 * wu, wq_hi = wq_lo + 31;  // wave-uniform (scalar) bounds
-  constexpr float kRescale = 8.f;
+  constexpr float kSumLimit = 65536.f;
   f32x16 sacc[2];
   bf16x8 pb[2][2];
 
@@ -339,22 +339,10 @@ __device__ __forceinline__ void attend_query_tile(const PrefillArgs& a, char* ri
           if (key > myq || key >= S) sacc[kb][e] = -INFINITY;
         }
     }
-    float mt = sacc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
-    mt = fmaxf(mt, shfl_xor(mt, 32));
-    const bool raise = mt > m_run + kRescale;
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      asm volatile("" ::: "memory");  // keep this a branch (rare after the first tile)
-      const float m_new = raise ? mt : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-      m_run = m_new;
-    }
+    // p = exp2(s - m_run) with the running reference m_run; the exact tile maximum is only needed when
+    // a row's sum leaves [0, 2^16] (its largest term grew past 2^16, or m_run is still -inf on the
+    // first tile, which gives inf / NaN): then m_run is raised to the maximum seen, O and l are
+    // rescaled and the tile is recomputed.  The reference cancels in O / l either way.
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -365,6 +353,32 @@ __device__ __forceinline__ void attend_query_tile(const PrefillArgs& a, char* ri
         pb[kb][e >> 3][e & 7] = (bf16)p;
       }
     rs += shfl_xor(rs, 32);
+    const bool raise = !(rs <= kSumLimit);
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      asm volatile("" ::: "memory");  // keep this a branch (rare after the first tile)
+      float mt = sacc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
+      mt = fmaxf(mt, shfl_xor(mt, 32));
+      const float m_new = raise ? fmaxf(m_run, mt) : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+      rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = __builtin_amdgcn_exp2f(sacc[kb][e] - m_run);
+          rs += p;
+          pb[kb][e >> 3][e & 7] = (bf16)p;
+        }
+      rs += shfl_xor(rs, 32);
+    }
     l_run += rs;
   };
 

@@ -128,6 +128,20 @@ def test_mid_bf16_many_sequences():
     run_decode_case(cfg, [int(v) for v in lens], 320, sample=sample)
 
 
+@pytest.mark.parametrize("d_kv,r", [(512, 2), (256, 4), (256, 2)])
+def test_mid_int4_shapes(d_kv, r):
+    """The other int4 latent shapes of the per-wave kernel (latent width 256 / 512, 2 or 4 pairs)."""
+    cfg = scaled(CONFIGS[4], family="mid", batch=3, d_kv=d_kv, r_pairs=r)
+    run_decode_case(cfg, [700, 17, 130], 768)
+
+
+def test_mid_short_ragged_lengths():
+    """Lengths around the 16-token tile and the per-wave quarters of a work item (latent width 256)."""
+    cfg = scaled(CONFIGS[3], family="mid", batch=13, ctx_range=None)
+    lens = [1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 127, 200, 513]
+    run_decode_case(cfg, lens, 520, sample=[0, 2, 3, 4, 6, 9, 11, 12])
+
+
 def test_mid_int4():
     cfg = scaled(CONFIGS[4], family="mid", batch=4)
     run_decode_case(cfg, [1000, 65, 512, 3], 1024)
