@@ -2,8 +2,8 @@
 """Throughput of the MHA2MLA latent-cache hot path on one MI355X (gfx950).
 
 One step of the headline workload (Llama-2-7B-shaped layer, bf16, d_kv 512, r 4, batch 32, every
-sequence at context 4096) is one decode step of serving: mla_cache_append of the new token of every
-sequence (position 4095) followed by mla_decode over the 4096 cached tokens.  `value` is the latent-cache
+sequence at context 4096) is one decode step of serving, mla_decode_step: the append of the new token of
+every sequence (position 4095) and the decode over the 4096 cached tokens.  `value` is the latent-cache
 bytes one decode must read (batch x context x bytes per cache row) divided by the step time.
 
 Timing: inputs are resident in HBM before the timed region; `--warmup` untimed steps, then `--steps`
@@ -170,16 +170,12 @@ def time_decode(wl, steps, warmup):
     bound = wl["bound"]
     n = len(bound)
     for i in range(warmup):
-        bd = bound[i % n]
-        bd.append()
-        bd.decode()
+        bound[i % n].step()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(steps):
-        bd = bound[i % n]
-        bd.append()
-        bd.decode()
+        bound[i % n].step()
     t1.record()
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
@@ -360,8 +356,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "llama_bf16_decode: Llama-2-7B-shaped layer (d_model 4096, 32 heads x 128), r 4 pairs/head, "
-                               "d_kv 512, bf16 latent cache, batch 32, every sequence at context 4096; step = append "
-                               "of the new token + decode",
+                               "d_kv 512, bf16 latent cache, batch 32, every sequence at context 4096; step = "
+                               "mla_decode_step (append of the new token + decode)",
                    "batch": 32, "context": 4096, "d_kv": 512, "r_pairs": 4, "cache_bytes_per_step": main_res["bytes"],
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

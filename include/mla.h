@@ -150,6 +150,20 @@ int mla_decode_phase(int phase, const mla_config *cfg, const mla_weights *w, con
                      const void *q, const int32_t *seq_lens, int32_t max_seq_len, void *out, void *workspace,
                      size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------- decode step
+ * One serving step: mla_cache_append_ws of the new tokens (t_new per sequence) followed by
+ * mla_decode over the updated cache, in one call.  The append's first phase and the decode's query
+ * preparation do not depend on each other and share one launch; results are identical to the two
+ * calls.  Arguments as for those calls; seq_lens[b] must count the appended tokens (normally
+ * start_pos[b] + t_new) and max_seq_len bound them.
+ * Workspace: mla_decode_step_workspace_bytes(cfg, batch, t_new, max_seq_len) bytes, 16-byte aligned
+ * (the append's partial sums followed by the decode workspace).                                 */
+size_t mla_decode_step_workspace_bytes(const mla_config *cfg, int32_t batch, int32_t t_new, int32_t max_seq_len);
+int mla_decode_step(const mla_config *cfg, const mla_weights *w, mla_cache *cache, const void *x,
+                    const int32_t *start_pos, int32_t t_new, int32_t max_start_pos, const void *q,
+                    const int32_t *seq_lens, int32_t max_seq_len, void *out, void *workspace, size_t ws_bytes,
+                    hipStream_t stream);
+
 /* ---------------------------------------------------------------- prefill
  * Causal attention of seq_len query tokens per sequence, at positions 0..seq_len-1, over the
  * cache rows 0..seq_len-1 (append them first).  Unabsorbed form: K_nope and V of every head are

@@ -14,6 +14,8 @@ from .api import (  # noqa: F401
     append_ws,
     decode,
     decode_phase,
+    decode_step,
+    decode_step_workspace_bytes,
     decode_workspace_bytes,
     pack_weights,
     prefill,

@@ -19,6 +19,8 @@ EXPORTED = [
     "mla_decode_workspace_bytes",
     "mla_decode",
     "mla_decode_phase",
+    "mla_decode_step_workspace_bytes",
+    "mla_decode_step",
     "mla_prefill_workspace_bytes",
     "mla_prefill",
     "mla_quantize_int4",
@@ -83,6 +85,10 @@ def load():
     lib.mla_decode.restype = ctypes.c_int
     lib.mla_decode_phase.argtypes = [ctypes.c_int, C, W, K, P, P, i32, P, P, sz, P]
     lib.mla_decode_phase.restype = ctypes.c_int
+    lib.mla_decode_step_workspace_bytes.argtypes = [C, i32, i32, i32]
+    lib.mla_decode_step_workspace_bytes.restype = sz
+    lib.mla_decode_step.argtypes = [C, W, K, P, P, i32, i32, P, P, i32, P, P, sz, P]
+    lib.mla_decode_step.restype = ctypes.c_int
     lib.mla_prefill_workspace_bytes.argtypes = [C, i32, i32]
     lib.mla_prefill_workspace_bytes.restype = sz
     lib.mla_prefill.argtypes = [C, W, K, P, i32, P, P, sz, P]

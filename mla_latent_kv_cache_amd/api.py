@@ -221,6 +221,29 @@ def decode_phase(phase: int, w: LayerWeights, cache: LatentCache, q: torch.Tenso
                                                     _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
+def decode_step_workspace_bytes(shape: LayerShape, batch: int, t_new: int, max_seq_len: int) -> int:
+    cfg = shape.c()
+    return _lib.load().mla_decode_step_workspace_bytes(ctypes.byref(cfg), batch, t_new, max_seq_len)
+
+
+def decode_step(w: LayerWeights, cache: LatentCache, x_new: torch.Tensor, start_pos: torch.Tensor, max_start_pos: int,
+                q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """mla_decode_step: append x_new [batch, t_new, d_model] at start_pos, then decode q -> out."""
+    lib = _lib.load()
+    cfg, cw, cc = w.shape.c(), w.c(), cache.c()
+    if out is None:
+        out = torch.empty_like(q)
+    t_new = x_new.shape[1]
+    nbytes = lib.mla_decode_step_workspace_bytes(ctypes.byref(cfg), cache.batch, t_new, int(max_seq_len))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check("mla_decode_step", lib.mla_decode_step(
+        ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc), _ptr(x_new), _ptr(start_pos), t_new, int(max_start_pos),
+        _ptr(q), _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
 def prefill_workspace_bytes(shape: LayerShape, batch: int, seq_len: int) -> int:
     cfg = shape.c()
     return _lib.load().mla_prefill_workspace_bytes(ctypes.byref(cfg), batch, seq_len)
@@ -269,7 +292,13 @@ class BoundDecode:
             workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
         na = self.lib.mla_cache_append_workspace_bytes(ctypes.byref(self.cfg), cache.batch, x_new.shape[1])
         append_ws_buf = torch.empty(max(na, 16), dtype=torch.uint8, device=q.device)
-        self._keep = (w, cache, x_new, start_pos, q, seq_lens, out, append_ws_buf, workspace)
+        ns = self.lib.mla_decode_step_workspace_bytes(ctypes.byref(self.cfg), cache.batch, x_new.shape[1],
+                                                      int(max_seq_len))
+        step_ws = torch.empty(max(ns, 16), dtype=torch.uint8, device=q.device)
+        self.args_step = (ctypes.byref(self.cfg), ctypes.byref(self.cw), ctypes.byref(self.cc), _ptr(x_new),
+                          _ptr(start_pos), x_new.shape[1], int(max_start_pos), _ptr(q), _ptr(seq_lens),
+                          int(max_seq_len), _ptr(out), _ptr(step_ws), step_ws.numel())
+        self._keep = (w, cache, x_new, start_pos, q, seq_lens, out, append_ws_buf, step_ws, workspace)
         self.args_append = (ctypes.byref(self.cfg), ctypes.byref(self.cw), ctypes.byref(self.cc), _ptr(x_new),
                             _ptr(start_pos), x_new.shape[1], int(max_start_pos), _ptr(append_ws_buf),
                             append_ws_buf.numel())
@@ -282,6 +311,10 @@ class BoundDecode:
 
     def decode(self, stream=None):
         _check("mla_decode", self.lib.mla_decode(*self.args_decode, _stream(stream)))
+
+    def step(self, stream=None):
+        """mla_decode_step: the append and the decode in one call (prologue launches fused)."""
+        _check("mla_decode_step", self.lib.mla_decode_step(*self.args_step, _stream(stream)))
 
     def phase(self, p: int, stream=None):
         _check("mla_decode_phase", self.lib.mla_decode_phase(p, *self.args_decode, _stream(stream)))

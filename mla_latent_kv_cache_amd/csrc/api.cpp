@@ -181,6 +181,56 @@ int mla_decode_phase(int phase, const mla_config* cfg, const mla_weights* w, con
   return decode_impl(1 << (phase - 1), cfg, w, cache, q, seq_lens, max_seq_len, out, workspace, ws_bytes, stream);
 }
 
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t mla_decode_step_workspace_bytes(const mla_config* cfg, int32_t batch, int32_t t_new, int32_t max_seq_len) {
+  if (check_config(cfg) != MLA_OK || batch < 0 || t_new < 0 || max_seq_len < 0) return 0;
+  const Shape s = shape_of(cfg);
+  return align256(mla::append_workspace_bytes(s, batch * t_new)) + mla::plan_decode(s, batch, max_seq_len).total;
+}
+
+int mla_decode_step(const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
+                    const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, const void* q,
+                    const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace, size_t ws_bytes,
+                    hipStream_t stream) {
+  // validation of both halves, as the separate calls do it
+  MLA_TRY(check_config(cfg));
+  MLA_TRY(check_weights(cfg, w, true, true));
+  MLA_TRY(check_cache(cfg, cache));
+  if (t_new < 0 || max_start_pos < 0 || max_seq_len < 0) return MLA_ERR_INVALID_ARG;
+  if (cache->batch == 0) return MLA_OK;
+  const Shape s = shape_of(cfg);
+  if (t_new > 0) {
+    MLA_TRY(check_ptr(x, true));
+    MLA_TRY(check_ptr(start_pos, true));
+    MLA_TRY(check_positions(cfg, w, cache, (long long)max_start_pos + t_new));
+    if ((long long)cache->batch * t_new > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+    if (!mla::append_fits(s)) return MLA_ERR_UNSUPPORTED;
+  }
+  MLA_TRY(check_ptr(q, true));
+  MLA_TRY(check_ptr(seq_lens, true));
+  MLA_TRY(check_ptr(out, true));
+  MLA_TRY(check_positions(cfg, w, cache, max_seq_len));
+  if ((long long)cache->batch * max_seq_len >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
+  const mla::DecodePlan plan = mla::plan_decode(s, cache->batch, max_seq_len);
+  if (!mla::decode_fits(s, plan)) return MLA_ERR_UNSUPPORTED;
+  if (mla::decode_uses_mfma(s) && (size_t)cache->t_max * s.d_kv * 2 >= ((size_t)1 << 31)) return MLA_ERR_UNSUPPORTED;
+  const size_t app_bytes = align256(mla::append_workspace_bytes(s, cache->batch * t_new));
+  if (!workspace || ws_bytes < app_bytes + plan.total) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
+  char* wsa = (char*)workspace;
+  char* wsd = wsa + app_bytes;
+  mla::AppendArgs aa{s, x, w->w_dkv, w->w_krope, w->pair_idx, w->rope_cos, w->rope_sin,
+                     start_pos, cache->batch, t_new, max_start_pos, cache->t_max,
+                     cache->ckv, cache->ckv_scale, cache->krope, app_bytes > 0 ? wsa : nullptr};
+  mla::DecodeArgs da{s, q, w->w_uk, w->w_uv, w->pair_idx, w->rope_cos, w->rope_sin,
+                     cache->ckv, cache->ckv_scale, cache->krope, cache->batch, cache->t_max, max_seq_len,
+                     seq_lens, out, wsd, plan};
+  if (t_new > 0 && mla::decode_step_fusable(aa, da)) return from_hip(mla::launch_decode_step(aa, da, stream));
+  if (t_new > 0) MLA_TRY(from_hip(mla::launch_append(aa, stream)));
+  return from_hip(mla::launch_decode(da, stream, 7));
+}
+
 size_t mla_prefill_workspace_bytes(const mla_config* cfg, int32_t batch, int32_t seq_len) {
   if (check_config(cfg) != MLA_OK || batch < 0 || seq_len < 0) return 0;
   return mla::plan_prefill(shape_of(cfg), batch, seq_len).total;

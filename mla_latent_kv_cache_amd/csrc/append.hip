@@ -11,6 +11,7 @@
 #include "common.h"
 #include "gemm.h"
 #include "kernels.h"
+#include "step.h"
 
 namespace mla {
 
@@ -366,7 +367,7 @@ __device__ __forceinline__ void append_epilogue(const AppendArgs& a, float (*fin
 // M = batch * t_new <= 64 tokens: the GEMM is a weight read.  One workgroup per 32 output columns,
 // 8 waves splitting the model width, MFMA 32x32x16 on up to two 32-token blocks, partial sums reduced
 // in LDS, then the same epilogues as the large path (RoPE pairs, int4 groups of 32 columns).
-constexpr int SM_WAVES = 8, SM_MAXM = 64;
+constexpr int SM_WAVES = 8;
 
 __global__ __launch_bounds__(512, 1) void append_small_bf16(AppendArgs a) {
   __shared__ float red[SM_WAVES][SM_MAXM][32];
@@ -443,45 +444,9 @@ __global__ __launch_bounds__(512, 1) void append_small_bf16(AppendArgs a) {
 // slice, MFMA 32x32x16 on up to two 32-token blocks, partial sums of the slice -> workspace (fp32,
 // [KS][M][N]).  Phase 2: one workgroup of 1024 threads per 32 columns sums the KS partials (one
 // output element per thread, all KS loads in one round) and runs the epilogue.
-constexpr int KS_MAX = 16;
 
 __global__ __launch_bounds__(256) void append_splitk_bf16(AppendArgs a, int KS) {
-  __shared__ float red[4][SM_MAXM][32];
-  const int K = a.s.d_model, D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR;
-  const int M = a.batch * a.t_new, MB = (M + 31) / 32;
-  const int n0 = blockIdx.x * 32, ks = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int kslice = K / KS, kw = kslice / 4, k0 = ks * kslice + w * kw;
-  const bf16* x = (const bf16*)a.x;
-  const int gn = n0 + (lane & 31);
-  const bf16* wrow = gn < D ? (const bf16*)a.w_dkv + (size_t)gn * K : (const bf16*)a.w_krope + (size_t)(gn - D) * K;
-  const bool nok = gn < N;
-  const bf16x8 zero8 = {};
-  constexpr int SB = 8;  // K steps of 16 per lane issued together (kw <= 128)
-  bf16x8 bv[SB], a0[SB], a1[SB];
-#pragma unroll
-  for (int u = 0; u < SB; ++u) {
-    const int kk = k0 + 16 * u + 8 * (lane >> 5);
-    const bool kin = 16 * u < kw;
-    bv[u] = (nok && kin) ? *(const bf16x8*)(wrow + kk) : zero8;
-    a0[u] = ((lane & 31) < M && kin) ? *(const bf16x8*)(x + (size_t)(lane & 31) * K + kk) : zero8;
-    a1[u] = (MB > 1 && 32 + (lane & 31) < M && kin) ? *(const bf16x8*)(x + (size_t)(32 + (lane & 31)) * K + kk) : zero8;
-  }
-  f32x16 acc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-  for (int u = 0; u < SB; ++u) {
-    acc[0] = mfma32(a0[u], bv[u], acc[0]);
-    if (MB > 1) acc[1] = mfma32(a1[u], bv[u], acc[1]);
-  }
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) red[w][mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][lane & 31] = acc[mb][e];
-  __syncthreads();
-  float* part = (float*)a.ws + (size_t)ks * M * N;
-  for (int idx = threadIdx.x; idx < M * 32; idx += blockDim.x) {
-    const int m = idx >> 5, c = idx & 31;
-    if (n0 + c < N) part[(size_t)m * N + n0 + c] = red[0][m][c] + red[1][m][c] + red[2][m][c] + red[3][m][c];
-  }
+  append_splitk_tile(a, KS, blockIdx.x, blockIdx.y);
 }
 
 __global__ __launch_bounds__(1024) void append_reduce(AppendArgs a, int KS) {
@@ -555,6 +520,12 @@ size_t append_workspace_bytes(const Shape& s, int tokens) {
 
 bool append_fits(const Shape& s) {
   return append_uses_mfma(s) || (size_t)(s.d_model + s.d_kv + s.n_rope_cols()) * sizeof(float) <= 65536;
+}
+
+hipError_t launch_append_reduce(const AppendArgs& a, int ks, hipStream_t st) {
+  const int N = a.s.d_kv + a.s.n_rope_cols();
+  hipLaunchKernelGGL(append_reduce, dim3((N + 31) / 32), dim3(1024), 0, st, a, ks);
+  return hipGetLastError();
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st) {

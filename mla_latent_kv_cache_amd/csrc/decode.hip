@@ -16,6 +16,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "step.h"
 
 namespace mla {
 
@@ -175,13 +176,13 @@ __global__ __launch_bounds__(512) void decode_qprep(DecodeArgs a) {
 // Workgroup (head h, 128 latent columns, 32 sequences); wave w owns 32 of the columns.
 //   q~[b][k] = sum_i q_nope[b][i] W_uk,h[i][k]:  A = gathered NoPE query rows (LDS, rows b),
 //   B = W_uk tile (LDS, rows i, k contiguous) through the transpose read; K = NoPE dims padded to 128.
-__global__ __launch_bounds__(256) void decode_qprep_mfma(DecodeArgs a) {
+__device__ __forceinline__ void qprep_mfma_tile(const DecodeArgs& a, int bx, int by, int bz) {
   constexpr int WP = 128 + 8;  // LDS pitch of both tiles (elements)
   __shared__ __attribute__((aligned(16))) bf16 wt[128 * WP];
   __shared__ __attribute__((aligned(16))) bf16 qa[32 * WP];
   __shared__ int nope_idx[MAX_DH];
   __shared__ int kept[MAX_DH / 2];
-  const int h = blockIdx.x, kb = blockIdx.y * 128, b0 = blockIdx.z * 32;
+  const int h = bx, kb = by * 128, b0 = bz * 32;
   const int D = a.s.d_kv, dh = a.s.d_head, r = a.s.r_pairs, dn = a.s.d_nope(), half = dh / 2, NH = a.s.n_heads;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5;
   // W_uk rows i < dn, columns kb .. kb+127: 16 chunks of 16 bytes per row, issued first
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256) void decode_qprep_mfma(DecodeArgs a) {
     const int b = b0 + 8 * (e >> 2) + 4 * hb + (e & 3);
     if (b < a.batch) qt[((size_t)b * NH + h) * D + k] = (bf16)(acc[e] * scale);
   }
-  if (blockIdx.y != 0) return;
+  if (by != 0) return;
   float* qr = (float*)(a.ws + a.plan.off_qr);
   for (int idx = tid; idx < 32 * r; idx += blockDim.x) {
     const int bb = idx / r, j = idx - bb * r, b = b0 + bb;
@@ -242,6 +243,24 @@ __global__ __launch_bounds__(256) void decode_qprep_mfma(DecodeArgs a) {
     const float c = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
     qr[((size_t)b * NH + h) * 2 * r + 2 * j] = (x0 * c - x1 * sn) * scale;
     qr[((size_t)b * NH + h) * 2 * r + 2 * j + 1] = (x0 * sn + x1 * c) * scale;
+  }
+}
+
+__global__ __launch_bounds__(256) void decode_qprep_mfma(DecodeArgs a) {
+  qprep_mfma_tile(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Decode-step prologue: the new tokens' split-K append (phase 1) and the query preparation depend on
+// nothing of each other, so one launch runs both: workgroups [0, n_app) take append tiles, the rest
+// query-preparation tiles.
+__global__ __launch_bounds__(256) void decode_step_prologue(AppendArgs aa, int ks, DecodeArgs da) {
+  const int nx = (aa.s.d_kv + aa.s.n_rope_cols() + 31) / 32, n_app = nx * ks;
+  const int bid = blockIdx.x;
+  if (bid < n_app) {
+    append_splitk_tile(aa, ks, bid % nx, bid / nx);
+  } else {
+    const int j = bid - n_app, nh = da.s.n_heads, ny = da.s.d_kv / 128;
+    qprep_mfma_tile(da, j % nh, (j / nh) % ny, j / (nh * ny));
   }
 }
 
@@ -1374,6 +1393,23 @@ DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len) {
   off = align256(off + (size_t)batch * s.n_heads * s.d_kv * 4);
   p.total = off;
   return p;
+}
+
+bool decode_step_fusable(const AppendArgs& aa, const DecodeArgs& da) {
+  const int M = aa.batch * aa.t_new;
+  return aa.ws != nullptr && append_ksplit(aa.s, M) > 0 && da.s.dtype == 1 && da.s.d_nope() <= 128 &&
+         da.s.d_kv % 128 == 0;
+}
+
+hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, hipStream_t st) {
+  const int M = aa.batch * aa.t_new;
+  const int ks = append_ksplit(aa.s, M);
+  const int nx = (aa.s.d_kv + aa.s.n_rope_cols() + 31) / 32;
+  const int n_qp = da.s.n_heads * (da.s.d_kv / 128) * ((da.batch + 31) / 32);
+  hipLaunchKernelGGL(decode_step_prologue, dim3(nx * ks + n_qp), dim3(256), 0, st, aa, ks, da);
+  hipError_t e = launch_append_reduce(aa, ks, st);
+  if (e != hipSuccess) return e;
+  return launch_decode(da, st, 2 | 4);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask) {

@@ -83,6 +83,11 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st);  // uses a.ws whe
 // phase_mask bit 0: q-prep, bit 1: attention, bit 2: combine
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask = 7);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+// Decode step: split-K append of the new tokens (aa.ws = its partial sums) and decode (da), with the
+// append's first phase and the query preparation in one launch.  Requires decode_step_fusable().
+hipError_t launch_append_reduce(const AppendArgs& a, int ks, hipStream_t st);
+bool decode_step_fusable(const AppendArgs& aa, const DecodeArgs& da);
+hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, hipStream_t st);
 hipError_t launch_quantize_int4(const float* in, int64_t n_groups, uint8_t* codes, uint16_t* scales, hipStream_t st);
 
 // Shape predicates for the specialised paths (host side, used for dispatch and tests).

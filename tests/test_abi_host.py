@@ -156,6 +156,35 @@ def test_append_ws_checks(lib):
     assert call(ws=FAKE + 4) == ALIGN
 
 
+def test_decode_step_checks(lib):
+    c, w, k = cfg(), weights(), cache()
+    na = lib.mla_cache_append_workspace_bytes(ctypes.byref(c), 32, 1)
+    nd = lib.mla_decode_workspace_bytes(ctypes.byref(c), 32, 4096)
+    need = lib.mla_decode_step_workspace_bytes(ctypes.byref(c), 32, 1, 4096)
+    assert need == ((na + 255) // 256) * 256 + nd  # the append's partial sums, then the decode workspace
+    assert lib.mla_decode_step_workspace_bytes(ctypes.byref(c), -1, 1, 4096) == 0
+    assert lib.mla_decode_step_workspace_bytes(ctypes.byref(cfg(d_kv=0)), 32, 1, 4096) == 0
+
+    def call(x=FAKE, sp=FAKE, t_new=1, max_start=4095, q=FAKE, lens=FAKE, max_len=4096, out=FAKE, ws=FAKE,
+             nbytes=need, c=c, w=w, k=k):
+        return lib.mla_decode_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(k), x, sp, t_new, max_start, q, lens,
+                                   max_len, out, ws, nbytes, None)
+
+    assert call(ws=None) == WORKSPACE
+    assert call(nbytes=need - 1) == WORKSPACE
+    assert call(ws=FAKE + 4) == ALIGN
+    assert call(x=None) == INVALID
+    assert call(q=None) == INVALID
+    assert call(lens=None) == INVALID
+    assert call(out=FAKE + 2) == ALIGN
+    assert call(t_new=2, max_start=4095) == CAPACITY
+    assert call(max_len=4097) == CAPACITY
+    assert call(t_new=-1) == INVALID
+    assert call(w=weights(w_dkv=None)) == INVALID  # the append half needs the down-projection
+    assert call(w=weights(w_uv=None)) == INVALID   # the decode half needs the up-projection
+    assert call(k=cache(batch=0), x=None, q=None, lens=None, out=None, ws=None) == OK
+
+
 def test_prefill_checks(lib):
     c, w, k = cfg(), weights(), cache()
 

@@ -237,3 +237,55 @@ def test_step_append_batched_positions(variant, use_ws):
         # rows past the sequence were never written
         if L < t_max and variant != "int4":
             assert torch.isnan(cache.ckv[b, L:].float()).all()
+
+
+@pytest.mark.parametrize("variant", ["bf16", "int4", "f32"])
+def test_decode_step_matches_separate_calls(variant):
+    """mla_decode_step (append + decode with the fused prologue) equals mla_cache_append_ws followed by
+    mla_decode bit for bit, and the oracle within tolerance (f32 takes the unfused path)."""
+    from mla_latent_kv_cache_amd import LatentCache, append, append_ws, decode, decode_step, pack_weights
+
+    if variant == "f32":
+        cfg = scaled(CONFIGS[0], batch=4)
+    elif variant == "int4":
+        cfg = scaled(CONFIGS[4], family="mid", batch=4)
+    else:
+        cfg = scaled(CONFIGS[1], family="mid", batch=4)
+    lens = [97, 2, 64, 200]
+    t_max = 256
+    log(f"[decode-step] {variant} lens={lens}")
+    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    shape = shape_of(cfg)
+    w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
+    caches = [LatentCache.allocate(shape, len(lens), t_max, fill=float("nan")) for _ in range(2)]
+    xs = [synth.context_x(cfg, b, L) for b, L in enumerate(lens)]
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for cache in caches:
+        for b, L in enumerate(lens):
+            xt = torch.from_numpy(xs[b][: L - 1].astype(np.float32)).cuda().to(torch_dtype(cfg)).reshape(1, L - 1, -1)
+            view = LatentCache(shape, cache.ckv[b:b + 1], None if cache.ckv_scale is None else cache.ckv_scale[b:b + 1],
+                               cache.krope[b:b + 1], 1, t_max)
+            append(w, view, xt, zero, 0)
+    x_new = torch.from_numpy(np.stack([x[-1] for x in xs])[:, None, :].astype(np.float32)).cuda().to(torch_dtype(cfg))
+    start = torch.tensor([L - 1 for L in lens], dtype=torch.int32, device="cuda")
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    q = np.stack([decode_query(cfg, layer, x[-1]) for x in xs])
+    qt = torch.from_numpy(q.astype(np.float32)).cuda().to(torch_dtype(cfg))
+    out_step = decode_step(w, caches[0], x_new.contiguous(), start, max(lens) - 1, qt, lens_t, max(lens))
+    append_ws(w, caches[1], x_new.contiguous(), start, max(lens) - 1)
+    out_sep = decode(w, caches[1], qt, lens_t, max(lens))
+    torch.cuda.synchronize()
+    assert torch.equal(out_step, out_sep), "decode_step differs from append_ws + decode"
+    def same_bits(u, v):  # the unwritten rows hold NaN, which == never matches
+        return torch.equal(u.contiguous().view(torch.uint8), v.contiguous().view(torch.uint8))
+
+    assert same_bits(caches[0].ckv, caches[1].ckv) and same_bits(caches[0].krope, caches[1].krope)
+    got = _to_np(out_step)
+    for b, L in enumerate(lens):
+        c, kr = oracle_cache(cfg, layer, xs[b])
+        if cfg.cache_fmt == "int4_g32":
+            oc, osc = oracle.quantize_int4_g32(c.astype(np.float32))
+            c = oracle.dequant_int4(oc, osc)
+        ref = oracle.decode_ref(q[b], c, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head, cfg.theta)
+        r, a = assert_close(got[b], ref, cfg.dtype, f"decode_step b={b}")
+        log(f"  b={b} rel-L2={r:.2e} max-abs={a:.2e}")
