@@ -12,6 +12,7 @@
 //   3. combine: merges the splits and applies W_uv,h.
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -23,6 +24,7 @@ namespace mla {
 namespace {
 
 constexpr int QB = 16;     // batch rows per qprep workgroup (QB * d_nope <= 4 * 512)
+constexpr int MLS = 4;     // floats per (work item, head) entry of the split statistics: m, l, A, unused
 constexpr int MAX_DH = 256;
 
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
   float* qrs = qs + D;         // R2
   float* sc = qrs + R2 + 1;    // chunk
   __shared__ float red[8];
-  float* ml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * NH * 2;
+  float* ml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * NH * MLS;
   float* po = (float*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * NH * D;
   const T* qt = (const T*)(a.ws + a.plan.off_qt) + (size_t)b * NH * D;
   const float* qr = (const float*)(a.ws + a.plan.off_qr) + (size_t)b * NH * R2;
@@ -306,8 +308,8 @@ __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
     if (n <= 0) {
       for (int k = threadIdx.x; k < D; k += blockDim.x) po[(size_t)h * D + k] = 0.f;
       if (threadIdx.x == 0) {
-        ml[2 * h] = -INFINITY;
-        ml[2 * h + 1] = 0.f;
+        ml[MLS * h] = -INFINITY;
+        ml[MLS * h + 1] = 0.f;
       }
       continue;
     }
@@ -338,10 +340,64 @@ __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
       po[(size_t)h * D + k] = o;
     }
     if (threadIdx.x == 0) {
-      ml[2 * h] = m;
-      ml[2 * h + 1] = l;
+      ml[MLS * h] = m;
+      ml[MLS * h + 1] = l;
     }
     __syncthreads();
+  }
+}
+
+// Partial result of one work item for the kernels whose four waves each hold DW latent columns of all
+// 32 heads in the 32x32x16 MFMA accumulator layout (lane (h, hb): rows 8(e/4) + 4 hb + e%4 of each
+// 32-column block).  fp32 format: O as is.  fp16 format: A = max |O| over the head's row (the four
+// waves meet in `red`, LDS for 128 floats that no wave uses between the two barriers here) and O / A
+// rounded to fp16, so the stored values lie in [-1, 1] whatever the latent magnitudes.  Split
+// statistics: (m, l, A) per head.
+template <int DW>
+__device__ __forceinline__ void store_partial(const DecodeArgs& a, const f32x16 (&oacc)[DW / 32], float* red,
+                                              float m_run, float l_run) {
+  constexpr int NB = DW / 32, D = 4 * DW;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hb = lane >> 5, h = lane & 31;
+  float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * MLS;
+  float A = 1.f;
+  if (a.plan.f16) {
+    float am = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(oacc[blk][e]));
+    am = fmaxf(am, shfl_xor(am, 32));
+    lds_barrier();
+    if (hb == 0) red[w * 32 + h] = am;
+    lds_barrier();
+    A = fmaxf(fmaxf(red[h], red[32 + h]), fmaxf(red[64 + h], red[96 + h]));
+    const float inv = A > 0.f ? 1.f / A : 0.f;
+    _Float16* po = (_Float16*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * 32 * D;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int k = w * DW + blk * 32 + 8 * e4 + 4 * hb;
+        f16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (_Float16)(oacc[blk][4 * e4 + i] * inv);
+        *(f16x4*)&po[(size_t)h * D + k] = v;
+      }
+  } else {
+    float* po = (float*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * 32 * D;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int k = w * DW + blk * 32 + 8 * e4 + 4 * hb;
+        *(f32x4*)&po[(size_t)h * D + k] =
+            f32x4{oacc[blk][4 * e4], oacc[blk][4 * e4 + 1], oacc[blk][4 * e4 + 2], oacc[blk][4 * e4 + 3]};
+      }
+  }
+  if (w == 0 && hb == 0) {
+    pml[MLS * h] = m_run;
+    pml[MLS * h + 1] = l_run;
+    pml[MLS * h + 2] = A;
   }
 }
 
@@ -370,8 +426,6 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   WorkItem wi;
   if (!locate_item(a, blockIdx.x, wi)) return;
   const int b = wi.b, t0 = wi.t0, t1 = wi.t1;
-  float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * 2;
-  float* po = (float*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * 32 * D;
 
   // latent query operands (B of the score product) and the rotated query pairs
   const bf16* qt = (const bf16*)(a.ws + a.plan.off_qt) + ((size_t)b * 32 + h) * D + w * DW + 8 * hb;
@@ -534,18 +588,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
     if (tt + 32 < t1) step(B1{}, tt + 32);
   }
 
-#pragma unroll
-  for (int blk = 0; blk < NB; ++blk)
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      int k = w * DW + blk * 32 + 8 * e4 + 4 * hb;
-      *(f32x4*)&po[(size_t)h * D + k] =
-          f32x4{oacc[blk][4 * e4], oacc[blk][4 * e4 + 1], oacc[blk][4 * e4 + 2], oacc[blk][4 * e4 + 3]};
-    }
-  if (w == 0 && hb == 0) {
-    pml[2 * h] = m_run;
-    pml[2 * h + 1] = l_run;
-  }
+  store_partial<DW>(a, oacc, (float*)sbuf, m_run, l_run);
 }
 
 // ------------------------------------------------------------------ 2c. attention, dense MFMA path with LDS DMA
@@ -586,8 +629,6 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a) {
   WorkItem wi;
   if (!locate_item(a, blockIdx.x, wi)) return;
   const int b = wi.b, t0 = wi.t0, t1 = wi.t1;
-  float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * 2;
-  float* po = (float*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * 32 * D;
 
   // DMA addresses: a wave-uniform tile base (SGPRs) plus per-lane offsets that do not change per tile
   const size_t rowb = (size_t)b * a.t_max;
@@ -779,18 +820,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a) {
     }
   }
 
-#pragma unroll
-  for (int blk = 0; blk < NB; ++blk)
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      int k = w * DW + blk * 32 + 8 * e4 + 4 * hb;
-      *(f32x4*)&po[(size_t)h * D + k] =
-          f32x4{oacc[blk][4 * e4], oacc[blk][4 * e4 + 1], oacc[blk][4 * e4 + 2], oacc[blk][4 * e4 + 3]};
-    }
-  if (w == 0 && hb == 0) {
-    pml[2 * h] = m_run;
-    pml[2 * h + 1] = l_run;
-  }
+  store_partial<DW>(a, oacc, (float*)sbuf, m_run, l_run);
 }
 
 // ------------------------------------------------------------------ 2d. attention, one tile stream per wave
@@ -1145,8 +1175,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a) {
     ll[w * 32 + 16 + lane] = l_run[1];
   }
   __syncthreads();
-  float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * 2;
-  float* po = (float*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * 32 * D;
+  float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * MLS;
   if (w == 0 && lane < 32) {
     float M = -INFINITY;
 #pragma unroll
@@ -1159,14 +1188,16 @@ __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a) {
       wt[ww * 32 + lane] = f;
       L = fmaf(f, ll[ww * 32 + lane], L);
     }
-    pml[2 * lane] = M;
-    pml[2 * lane + 1] = L;
+    pml[MLS * lane] = M;
+    pml[MLS * lane + 1] = L;
   }
   __syncthreads();
   // O in rounds of 128 columns: every wave stores its raw accumulators (straight from the accumulation
   // registers), then wave w forms columns [32 w, 32 w + 32) as the weighted sum over the four waves
   float* ob = (float*)(lds + 2048);  // [4 waves][32 heads][128 columns]
   const int h = lane & 31, hb = lane >> 5;
+  // lane's heads: 8 it + lane / 8 (it = 0..3), 4 columns 32 w + 4 (lane % 8) of every 128-column round
+  f32x4 vr[D / 128][4];
 #pragma unroll
   for (int r = 0; r < D / 128; ++r) {
 #pragma unroll
@@ -1180,14 +1211,55 @@ __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a) {
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int idx = it * 64 + lane, hh = idx >> 3, c4x = idx & 7;  // 32 heads x 8 groups of 4 columns
-      const int col = 32 * w + 4 * c4x;
+      const int hh = 8 * it + (lane >> 3), col = 32 * w + 4 * (lane & 7);
       f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ww = 0; ww < 4; ++ww) v += wt[ww * 32 + hh] * *(const f32x4*)&ob[(ww * 32 + hh) * 128 + col];
-      *(f32x4*)&po[(size_t)hh * D + 128 * r + col] = v;
+      vr[r][it] = v;
     }
     __syncthreads();
+  }
+  const int col = 32 * w + 4 * (lane & 7);
+  if (a.plan.f16) {  // A = max |O| per head: 4 columns x 8 lanes x rounds in a wave, then the 4 waves
+    float* red = ob;  // [4 waves][32 heads]
+    float am[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      float m = 0.f;
+#pragma unroll
+      for (int r = 0; r < D / 128; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) m = fmaxf(m, fabsf(vr[r][it][c]));
+      m = fmaxf(m, shfl_xor(m, 1));
+      m = fmaxf(m, shfl_xor(m, 2));
+      am[it] = fmaxf(m, shfl_xor(m, 4));
+      if ((lane & 7) == 0) red[w * 32 + 8 * it + (lane >> 3)] = am[it];
+    }
+    __syncthreads();
+    _Float16* po = (_Float16*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * 32 * D;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int hh = 8 * it + (lane >> 3);
+      const float A = fmaxf(fmaxf(red[hh], red[32 + hh]), fmaxf(red[64 + hh], red[96 + hh]));
+      const float inv = A > 0.f ? 1.f / A : 0.f;
+#pragma unroll
+      for (int r = 0; r < D / 128; ++r) {
+        f16x4 v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = (_Float16)(vr[r][it][c] * inv);
+        *(f16x4*)&po[(size_t)hh * D + 128 * r + col] = v;
+      }
+      if (w == 0 && (lane & 7) == 0) pml[MLS * hh + 2] = A;
+    }
+  } else {
+    float* po = (float*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * 32 * D;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int hh = 8 * it + (lane >> 3);
+#pragma unroll
+      for (int r = 0; r < D / 128; ++r) *(f32x4*)&po[(size_t)hh * D + 128 * r + col] = vr[r][it];
+      if (w == 0 && (lane & 7) == 0) pml[MLS * hh + 2] = 1.f;
+    }
   }
 }
 
@@ -1209,7 +1281,7 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   const int b = pair / NH, h = pair - b * NH;
   int first, S;
   sequence_items(a, b, first, S);
-  const float* ml = (const float*)(a.ws + a.plan.off_ml) + ((size_t)first * NH + h) * 2;
+  const float* ml = (const float*)(a.ws + a.plan.off_ml) + ((size_t)first * NH + h) * MLS;
   const float* po = (const float*)(a.ws + a.plan.off_o) + ((size_t)first * NH + h) * D;
   // running merge over groups of 8 splits; each group's (m, l) and latent rows are loaded in one round
   float M = -INFINITY, den = 0.f, acc[KPL];
@@ -1220,8 +1292,8 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const bool ok = s0 + u < S;
-      ms[u] = ok ? ml[(size_t)(s0 + u) * NH * 2] : -INFINITY;
-      ls[u] = ok ? ml[(size_t)(s0 + u) * NH * 2 + 1] : 0.f;
+      ms[u] = ok ? ml[(size_t)(s0 + u) * NH * MLS] : -INFINITY;
+      ls[u] = ok ? ml[(size_t)(s0 + u) * NH * MLS + 1] : 0.f;
 #pragma unroll
       for (int i = 0; i < KPL; ++i) {
         const int k = lane + 64 * i;
@@ -1323,6 +1395,186 @@ __global__ __launch_bounds__(256) void decode_project_vec(DecodeArgs a) {
   ((T*)a.out)[idx] = from_f32<T>(acc);
 }
 
+// o = hi + lo, hi = bf16(o), lo = bf16(o - hi): KPL consecutive values to two LDS rows
+template <int KPL>
+__device__ __forceinline__ void write_hilo(bf16* hi, bf16* lo, const float (&v)[KPL]) {
+  constexpr int NE = KPL < 8 ? KPL : 8;
+  typedef __bf16 vec_t __attribute__((ext_vector_type(NE)));
+#pragma unroll
+  for (int c = 0; c < KPL / NE; ++c) {
+    vec_t hv, lv;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      hv[e] = (bf16)v[NE * c + e];
+      lv[e] = (bf16)(v[NE * c + e] - (float)hv[e]);
+    }
+    *(vec_t*)(hi + NE * c) = hv;
+    *(vec_t*)(lo + NE * c) = lv;
+  }
+}
+
+// 3c. merge and W_uv in one launch (bf16, latent width 256 or 512, head dim a multiple of 16).
+//   Workgroup (head h, up to 16 consecutive sequences).  Each wave first issues the W_uv,h loads of its
+//   blocks of 16 output dims (they do not depend on the merge), then merges: waves are spread over the
+//   sequences (1, 2 or 4 waves per sequence, the waves of one sequence taking every wps-th group of 8
+//   splits), each lane owning KPL = d_kv / 64 consecutive latent columns; waves sharing a sequence meet
+//   in LDS.  The normalised row is split exactly into bf16 hi + lo parts (o = hi + lo up to the rounding
+//   of lo) kept in LDS.  Projection: MFMA 16x16x32 with A = rows of W_uv,h (16 output dims) and B = the
+//   sequences' hi and lo rows (16 columns, unused ones ignored).
+constexpr int CB_MAXS = 16;  // sequences per combine workgroup (MFMA columns)
+
+template <int KPL, bool F16>
+__device__ __forceinline__ void merge_splits(const DecodeArgs& a, int first, int g0, int gstep, int S, int h,
+                                             float& M, float& den, float (&acc)[KPL]) {
+  constexpr int D = 64 * KPL;
+  const int NH = a.s.n_heads, lane = threadIdx.x & 63;
+  typedef _Float16 hv_t __attribute__((ext_vector_type(KPL)));
+  typedef float fv_t __attribute__((ext_vector_type(KPL)));
+  const float* ml = (const float*)(a.ws + a.plan.off_ml) + ((size_t)first * NH + h) * MLS;
+  const size_t row0 = ((size_t)first * NH + h) * D + KPL * lane;
+  M = -INFINITY;
+  den = 0.f;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) acc[i] = 0.f;
+  for (int s0 = 8 * g0; s0 < S; s0 += 8 * gstep) {
+    float ms[8], ls[8], as[8];
+    fv_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = s0 + u < S;
+      const float* e = ml + (size_t)(s0 + u) * NH * MLS;
+      ms[u] = ok ? e[0] : -INFINITY;
+      ls[u] = ok ? e[1] : 0.f;
+      const size_t at = row0 + (size_t)(s0 + u) * NH * D;
+      if (F16) {
+        as[u] = ok ? e[2] : 0.f;
+        v[u] = ok ? __builtin_convertvector(*(const hv_t*)((const _Float16*)(a.ws + a.plan.off_o) + at), fv_t) : fv_t{};
+      } else {
+        as[u] = 1.f;
+        v[u] = ok ? *(const fv_t*)((const float*)(a.ws + a.plan.off_o) + at) : fv_t{};
+      }
+    }
+    float gm = M;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) gm = fmaxf(gm, ms[u]);
+    if (gm == -INFINITY) continue;  // nothing seen yet (empty splits only)
+    const float c = exp2f(M - gm);  // rescale of what was merged so far (0 when M = -inf)
+    den *= c;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) acc[i] *= c;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wv = ms[u] == -INFINITY ? 0.f : exp2f(ms[u] - gm);
+      den = fmaf(wv, ls[u], den);
+      const float wa = wv * as[u];
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) acc[i] = fmaf(wa, v[u][i], acc[i]);
+    }
+    M = gm;
+  }
+}
+
+template <int KPL>
+__global__ __launch_bounds__(256) void decode_combine(DecodeArgs a, int sb) {
+  constexpr int D = 64 * KPL, PITCH = D + 8;  // LDS row pitch in bf16 (16-byte shift per row)
+  constexpr int NKS = D / 32, PF = 2;          // k-steps per output block; blocks prefetched per wave
+  __shared__ __attribute__((aligned(16))) bf16 ohi[CB_MAXS][PITCH], olo[CB_MAXS][PITCH];
+  __shared__ float st_m[4], st_d[4];
+  __shared__ __attribute__((aligned(16))) float st_acc[4][64 * KPL];
+  const int h = blockIdx.x, b0 = blockIdx.y * sb;
+  const int NH = a.s.n_heads, dh = a.s.d_head, nblk = dh / 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nseq = min(sb, a.batch - b0);
+  const bf16* wuv = (const bf16*)a.w_uv + (size_t)h * dh * D;
+  const int col = lane & 15, kq = 8 * (lane >> 4);
+  bf16x8 wv[PF][NKS];
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (w + 4 * p < nblk) {
+      const bf16* wrow = wuv + (size_t)(16 * (w + 4 * p) + col) * D + kq;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) wv[p][ks] = *(const bf16x8*)(wrow + 32 * ks);
+    }
+
+  // waves per sequence: 4 for one sequence, 2 for two, else 1 (each wave's state slot holds one sequence)
+  const int wps = nseq >= 3 ? 1 : (nseq == 2 ? 2 : 4);
+  const int chunk = work_chunk(a);
+  for (int j = w / wps; j < nseq; j += 4 / wps) {
+    const int b = b0 + j, q = w % wps;
+    int before = 0;
+    for (int i = lane; i < b; i += 64) before += (clamp_len(a, i) + chunk - 1) / chunk;
+    const int first = __builtin_amdgcn_readfirstlane(wave_isum(before));
+    const int S = (clamp_len(a, b) + chunk - 1) / chunk;
+    float M, den, acc[KPL];
+    if (a.plan.f16)
+      merge_splits<KPL, true>(a, first, q, wps, S, h, M, den, acc);
+    else
+      merge_splits<KPL, false>(a, first, q, wps, S, h, M, den, acc);
+    if (wps > 1) {  // partial state of this wave's split groups to LDS (one sequence per wave group)
+      if (lane == 0) {
+        st_m[w] = M;
+        st_d[w] = den;
+      }
+#pragma unroll
+      for (int i = 0; i < KPL / 4; ++i)
+        *(f32x4*)&st_acc[w][KPL * lane + 4 * i] = f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+      continue;
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) acc[i] *= inv;
+    write_hilo<KPL>(&ohi[j][KPL * lane], &olo[j][KPL * lane], acc);
+  }
+  if (wps > 1) {
+    __syncthreads();
+    const int w0 = w;  // first wave of each group combines its group's states
+    if (w0 % wps == 0 && w0 / wps < nseq) {
+      float Mt = -INFINITY;
+      for (int u = 0; u < wps; ++u) Mt = fmaxf(Mt, st_m[w0 + u]);
+      float den = 0.f, acc[KPL];
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) acc[i] = 0.f;
+      for (int u = 0; u < wps; ++u) {
+        const float c = st_m[w0 + u] == -INFINITY ? 0.f : exp2f(st_m[w0 + u] - Mt);
+        den = fmaf(c, st_d[w0 + u], den);
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) acc[i] = fmaf(c, st_acc[w0 + u][KPL * lane + i], acc[i]);
+      }
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) acc[i] *= inv;
+      const int j = w0 / wps;
+      write_hilo<KPL>(&ohi[j][KPL * lane], &olo[j][KPL * lane], acc);
+    }
+  }
+  __syncthreads();
+
+  auto project = [&](int eb, const bf16x8(&wk)[NKS]) {
+    f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      r = mfma16(wk[ks], *(const bf16x8*)&ohi[col][32 * ks + kq], r);
+      r = mfma16(wk[ks], *(const bf16x8*)&olo[col][32 * ks + kq], r);
+    }
+    // D[row = output dim 16 eb + 4 (lane / 16) + i][col = sequence b0 + lane % 16]
+    if (col < nseq) {
+      bf16x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = (bf16)r[i];
+      *(bf16x4*)((bf16*)a.out + ((size_t)(b0 + col) * NH + h) * dh + 16 * eb + 4 * (lane >> 4)) = o;
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (w + 4 * p < nblk) project(w + 4 * p, wv[p]);
+  for (int eb = w + 4 * PF; eb < nblk; eb += 4) {  // head dims beyond 16 * 4 * PF
+    const bf16* wrow = wuv + (size_t)(16 * eb + col) * D + kq;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) wv[0][ks] = *(const bf16x8*)(wrow + 32 * ks);
+    project(eb, wv[0]);
+  }
+}
+
 template <typename T>
 void launch_generic_attn(const DecodeArgs& a, hipStream_t st) {
   size_t shmem = (size_t)(a.s.d_kv + a.s.r2() + 1 + a.plan.cmax) * sizeof(float);
@@ -1354,6 +1606,10 @@ bool decode_uses_mfma(const Shape& s) {
   return s.dtype == 1 && s.n_heads == 32 && (s.d_kv == 256 || s.d_kv == 512) && (s.r_pairs == 2 || s.r_pairs == 4);
 }
 
+bool decode_uses_combine(const Shape& s) {
+  return s.dtype == 1 && (s.d_kv == 256 || s.d_kv == 512) && s.d_head % 16 == 0 && s.d_head <= 512;
+}
+
 bool decode_fits(const Shape& s, const DecodePlan& p) {
   if (s.d_kv > 1024) return false;
   if (!decode_uses_mfma(s) && (size_t)(s.d_kv + s.r2() + 1 + p.cmax) * sizeof(float) > 65536) return false;
@@ -1367,6 +1623,7 @@ DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len) {
   // one workgroup per CU for the specialised dense kernels (their LDS ring fills a CU), two otherwise
   p.target = (decode_uses_wave(s) || (decode_uses_mfma(s) && s.fmt == 0)) ? 256 : 512;
   p.cmax = 2048;
+  p.f16 = decode_uses_combine(s) && (decode_uses_mfma(s) || decode_uses_wave(s)) ? 1 : 0;
   if (!decode_uses_mfma(s)) {  // the generic kernel keeps a chunk of scores in LDS
     const long long room = 65536 / 4 - (long long)s.d_kv - s.r2() - 1;
     const long long c = room > 0 ? (room / 64) * 64 : 64;
@@ -1386,7 +1643,7 @@ DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len) {
   p.off_qr = off;
   off = align256(off + (size_t)batch * s.n_heads * (s.r2() > 0 ? s.r2() : 1) * 4);
   p.off_ml = off;
-  off = align256(off + (size_t)p.max_items * s.n_heads * 2 * 4);
+  off = align256(off + (size_t)p.max_items * s.n_heads * MLS * 4);
   p.off_o = off;
   off = align256(off + (size_t)p.max_items * s.n_heads * s.d_kv * 4);
   p.off_ob = off;
@@ -1441,7 +1698,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask) {
       launch_generic_attn<bf16>(a, st);
     }
   }
-  if (phase_mask & 4) {
+  if ((phase_mask & 4) && decode_uses_combine(a.s)) {
+    // sequences per workgroup: about one workgroup per CU, at most 16 (the MFMA width)
+    const int sb = std::max(1, std::min(CB_MAXS, a.batch * nh / 256));
+    dim3 g(nh, (a.batch + sb - 1) / sb);
+    if (a.s.d_kv == 512)
+      hipLaunchKernelGGL(decode_combine<8>, g, dim3(256), 0, st, a, sb);
+    else
+      hipLaunchKernelGGL(decode_combine<4>, g, dim3(256), 0, st, a, sb);
+  } else if (phase_mask & 4) {
     const int pairs = a.batch * nh, gm = (pairs + 3) / 4, kpl = (a.s.d_kv + 63) / 64;
     if (kpl <= 1) hipLaunchKernelGGL(decode_merge<1>, dim3(gm), dim3(256), 0, st, a);
     else if (kpl <= 2) hipLaunchKernelGGL(decode_merge<2>, dim3(gm), dim3(256), 0, st, a);

@@ -42,6 +42,7 @@ struct DecodePlan {
   int target;     // desired number of work items
   int cmax;       // largest chunk (multiple of 64)
   int max_items;  // grid size of the attention launch, >= 1
+  int f16;        // partial latent rows stored as fp16 O / A with A = max |O| of the row (else fp32 O)
   size_t off_qt, off_qr, off_ml, off_o, off_ob, total;
 };
 DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len);
@@ -94,6 +95,7 @@ hipError_t launch_quantize_int4(const float* in, int64_t n_groups, uint8_t* code
 bool append_uses_mfma(const Shape& s);
 bool decode_uses_mfma(const Shape& s);
 bool decode_uses_wave(const Shape& s);  // per-wave tile streams (int4 latents, latent width 256)
+bool decode_uses_combine(const Shape& s);  // merge and W_uv projection in one launch
 bool prefill_supported(const Shape& s);
 // Dynamic LDS of the generic kernels fits the 64 KiB a launch may request.
 bool append_fits(const Shape& s);
