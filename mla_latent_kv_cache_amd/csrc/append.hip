@@ -17,16 +17,6 @@ namespace mla {
 
 namespace {
 
-__device__ __forceinline__ int cache_row(const AppendArgs& a, int m, int* pos_out) {
-  int b = m / a.t_new;
-  int i = m - b * a.t_new;
-  int sp = a.start_pos[b];
-  sp = sp < 0 ? 0 : (sp > a.max_start ? a.max_start : sp);
-  int pos = sp + i;
-  *pos_out = pos;
-  return b * a.t_max + pos;
-}
-
 // ------------------------------------------------------------------ generic path (any dtype / format)
 // One workgroup per token: x row staged in LDS, one thread per output column, then the epilogue.
 template <typename T>
@@ -319,50 +309,6 @@ __global__ __launch_bounds__(256, 1) void append_gemm_bf16(AppendArgs a) {
   append_gemm_blocks<0, 0>(a, acc, rows, poss, m0, n0, M);
 }
 
-// Epilogue shared by the few-token paths: fin[m][c] holds output column n0 + c of token m (fp32);
-// rows[m] / poss[m] are the token's cache row and position.
-__device__ __forceinline__ void append_epilogue(const AppendArgs& a, float (*fin)[33], const int* rows,
-                                                const int* poss, int n0, int M) {
-  const int D = a.s.d_kv, NR = a.s.n_rope_cols();
-  if (n0 < D) {
-    if (a.s.fmt == 0) {
-      for (int idx = threadIdx.x; idx < M * 32; idx += blockDim.x) {
-        int m = idx >> 5, c = idx & 31;
-        ((bf16*)a.ckv)[(size_t)rows[m] * D + n0 + c] = (bf16)fin[m][c];
-      }
-    } else {
-      for (int m = threadIdx.x; m < M; m += blockDim.x) {
-        float am = 0.f;
-        for (int c = 0; c < 32; ++c) am = fmaxf(am, fabsf(fin[m][c]));
-        __half s = int4_scale(am);
-        float sf = __half2float(s);
-        const size_t row = (size_t)rows[m];
-        uint8_t* codes = (uint8_t*)a.ckv + row * (D / 2) + n0 / 2;
-        for (int i = 0; i < 16; ++i) {
-          int c0 = int4_code(fin[m][2 * i], sf), c1 = int4_code(fin[m][2 * i + 1], sf);
-          codes[i] = (uint8_t)((c0 & 15) | ((c1 & 15) << 4));
-        }
-        ((__half*)a.ckv_scale)[row * (D / 32) + n0 / 32] = s;
-      }
-    }
-  } else {
-    const int r = a.s.r_pairs, R2 = a.s.r2(), half = a.s.d_head / 2;
-    for (int idx = threadIdx.x; idx < M * 16; idx += blockDim.x) {
-      int m = idx >> 4, cp = 2 * (idx & 15);
-      int rel = n0 + cp - D;
-      if (rel >= NR) continue;
-      int h = rel / R2, jj = (rel - h * R2) >> 1;
-      int p = load_pair(a.pair_idx, h * r + jj, half);
-      const size_t row = (size_t)rows[m];
-      const int pos = poss[m];
-      float cs = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
-      float x0 = fin[m][cp], x1 = fin[m][cp + 1];
-      ((bf16*)a.krope)[row * NR + rel] = (bf16)(x0 * cs - x1 * sn);
-      ((bf16*)a.krope)[row * NR + rel + 1] = (bf16)(x0 * sn + x1 * cs);
-    }
-  }
-}
-
 // ------------------------------------------------------------------ MFMA path for few tokens (decode steps)
 // M = batch * t_new <= 64 tokens: the GEMM is a weight read.  One workgroup per 32 output columns,
 // 8 waves splitting the model width, MFMA 32x32x16 on up to two 32-token blocks, partial sums reduced
@@ -436,7 +382,7 @@ __global__ __launch_bounds__(512, 1) void append_small_bf16(AppendArgs a) {
     fin[m][c] = v;
   }
   __syncthreads();
-  append_epilogue(a, fin, rows, poss, n0, M);
+  append_epilogue(a, &fin[0][0], 33, rows, poss, n0, M);
 }
 
 // ------------------------------------------------------------------ few tokens with a workspace
@@ -472,7 +418,7 @@ __global__ __launch_bounds__(1024) void append_reduce(AppendArgs a, int KS) {
     fin[m][c] = sum;
   }
   __syncthreads();
-  append_epilogue(a, fin, rows, poss, n0, M);
+  append_epilogue(a, &fin[0][0], 33, rows, poss, n0, M);
 }
 
 // ------------------------------------------------------------------ standalone int4 quantiser

@@ -91,6 +91,25 @@ __device__ void sequence_items(const DecodeArgs& a, int b, int& first, int& coun
   count = (clamp_len(a, b) + chunk - 1) / chunk;
 }
 
+// Rows of a fused split-K append (FuseArgs) at positions [t0, t1) of sequence b, written by the calling
+// workgroup from the LDS scratch `lds`; true when there were any (the caller then waits for vmcnt 0
+// before loading them).
+__device__ __forceinline__ bool fused_rows(const FuseArgs& f, int b, int t0, int t1, float* lds) {
+  if (f.ks == 0) return false;
+  int sp = f.a.start_pos[b];
+  sp = sp < 0 ? 0 : (sp > f.a.max_start ? f.a.max_start : sp);
+  const int lo = max(t0, sp), hi = min(t1, sp + f.a.t_new);
+  if (lo >= hi) return false;
+  append_rows_fused(f.a, f.ks, b, lo, hi, lds);
+  return true;
+}
+// Extra workgroup max_items + b of a fused launch: the new rows of sequence b past its decode range.
+__device__ __forceinline__ void fused_orphans(const DecodeArgs& a, const FuseArgs& f, float* lds) {
+  const int b = blockIdx.x - a.plan.max_items;
+  if (f.ks == 0 || b >= a.batch) return;
+  fused_rows(f, b, clamp_len(a, b), 0x7fffffff, lds);
+}
+
 // ------------------------------------------------------------------ 1. query preparation
 // Workgroup (head h, 64 latent columns, up to QB batch rows), 8 waves splitting the NoPE dims: every
 // lane issues all of its W_uk loads at once, accumulates QB rows, and the partial sums meet in LDS.
@@ -414,7 +433,7 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, const f32x16 
 // (one cross-half shuffle).  The next tile's rows and RoPE keys are prefetched into registers.  The
 // dense 512-wide variant needs more than 256 registers per lane and runs at one wave per SIMD.
 template <int DW, int R2, int FMT>
-__global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_attn_mfma(DecodeArgs a) {
+__global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_attn_mfma(DecodeArgs a, FuseArgs f) {
   constexpr int CP = DW + 16;  // LDS row pitch in elements (conflict-free b128 and transpose reads)
   constexpr int NS = DW / 16;  // score k-steps per wave
   constexpr int NB = DW / 32;  // output blocks per wave
@@ -423,9 +442,15 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   __shared__ f32x4 sbuf[2][4][4][64];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5, h = lane & 31;
+  static_assert(sizeof(cbuf) >= FUSE_MAXR * (D + 32 * R2 + 4) * 4 + 64, "fused append scratch");
+  if (blockIdx.x >= a.plan.max_items) {
+    fused_orphans(a, f, (float*)cbuf);
+    return;
+  }
   WorkItem wi;
   if (!locate_item(a, blockIdx.x, wi)) return;
   const int b = wi.b, t0 = wi.t0, t1 = wi.t1;
+  if (fused_rows(f, b, t0, t1, (float*)cbuf)) MLA_WAIT_VMCNT(0);
 
   // latent query operands (B of the score product) and the rotated query pairs
   const bf16* qt = (const bf16*)(a.ws + a.plan.off_qt) + ((size_t)b * 32 + h) * D + w * DW + 8 * hb;
@@ -614,7 +639,7 @@ __device__ __forceinline__ int slice_off(int row, int col) {
 // NSLOT tile slots in the DMA ring (2: one tile in flight while one is used; 3: two in flight), NSB
 // buffers for the cross-wave exchange of partial scores (2 saves one barrier per tile).
 template <int DW, int R2, int NSLOT, int NSB>
-__global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a) {
+__global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs f) {
   constexpr int NS = DW / 16, NB = DW / 32, D = 4 * DW;
   constexpr int CSL = 32 * DW * 2;       // bytes of one wave's latent slice of a tile
   constexpr int KSL = 8 * 32 * R2 * 2;   // bytes of one wave's RoPE rows of a tile
@@ -626,9 +651,26 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a) {
   __shared__ f32x4 sbuf[NSB][4][4][64];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5, h = lane & 31;
+  // a fused append's rows are formed in slot 2 (its first DMA is issued after the wait before the loop)
+  constexpr bool CAN_FUSE = NSLOT > 2 && 4 * CSL >= FUSE_MAXR * (D + 32 * R2 + 4) * 4 + 64;
+  if (blockIdx.x >= a.plan.max_items) {
+    if constexpr (CAN_FUSE) fused_orphans(a, f, (float*)cs2);
+    return;
+  }
   WorkItem wi;
   if (!locate_item(a, blockIdx.x, wi)) return;
   const int b = wi.b, t0 = wi.t0, t1 = wi.t1;
+  // new rows of a fused append: before the first tile's DMA when they lie in it, else while it loads
+  bool fuse_late = CAN_FUSE && f.ks > 0;
+  if (fuse_late) {
+    int sp = f.a.start_pos[b];
+    sp = sp < 0 ? 0 : (sp > f.a.max_start ? f.a.max_start : sp);
+    if (sp < t0 + 32 && sp + f.a.t_new > t0) {  // a new row in the first tile
+      fused_rows(f, b, t0, t1, (float*)cs2);
+      MLA_WAIT_VMCNT(0);
+      fuse_late = false;
+    }
+  }
 
   // DMA addresses: a wave-uniform tile base (SGPRs) plus per-lane offsets that do not change per tile
   const size_t rowb = (size_t)b * a.t_max;
@@ -676,6 +718,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a) {
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
   issue_slot(S0{}, t0);
+  if constexpr (CAN_FUSE)
+    if (fuse_late) fused_rows(f, b, t0, t1, (float*)cs2);  // waited for with the first tile below
   const bf16* qt = (const bf16*)(a.ws + a.plan.off_qt) + ((size_t)b * 32 + h) * D + w * DW + 8 * hb;
   bf16x8 qv[NS];
 #pragma unroll
@@ -888,16 +932,22 @@ __device__ __forceinline__ bf16x8 dequant8v(uint32_t wd, const float* s) {
 }
 
 template <int D, int R2, int FMT, int NSLOT>
-__global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a) {
+__global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a, FuseArgs f) {
   using W = WaveTile<D, R2, FMT, NSLOT>;
   constexpr int TT = W::TT, SWM = W::SWM;
   constexpr float kSumLimit = 18446744073709551616.f;  // 2^64
   __shared__ __attribute__((aligned(1024))) char lds[W::LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  static_assert(W::LDS_BYTES >= FUSE_MAXR * (D + 32 * R2 + 4) * 4 + 64, "fused append scratch");
+  if (blockIdx.x >= a.plan.max_items) {
+    fused_orphans(a, f, (float*)lds);
+    return;
+  }
   WorkItem wi;
   if (!locate_item(a, blockIdx.x, wi)) return;
   const int b = wi.b;
+  if (fused_rows(f, b, wi.t0, wi.t1, (float*)lds)) MLA_WAIT_VMCNT(0);
   // the wave's quarter of the item, in whole tiles
   const int ntile = (wi.t1 - wi.t0 + TT - 1) / TT, per = (ntile + 3) / 4;
   const int u0 = wi.t0 + TT * min(ntile, w * per);
@@ -1263,9 +1313,13 @@ __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a) {
   }
 }
 
+// Grid of the specialised attention kernels: the work items, plus one workgroup per sequence for the
+// rows of a fused append that lie past its decode range.
+inline dim3 attn_grid(const DecodeArgs& a, const FuseArgs& f) { return dim3(a.plan.max_items + (f.ks ? a.batch : 0)); }
+
 template <int D, int R2, int FMT, int NSLOT>
-void launch_wave_attn(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_attn_wave<D, R2, FMT, NSLOT>), dim3(a.plan.max_items), dim3(256), 0, st, a);
+void launch_wave_attn(const DecodeArgs& a, const FuseArgs& f, hipStream_t st) {
+  hipLaunchKernelGGL((decode_attn_wave<D, R2, FMT, NSLOT>), attn_grid(a, f), dim3(256), 0, st, a, f);
 }
 
 // ------------------------------------------------------------------ 3. combine: merge, then W_uv
@@ -1586,12 +1640,11 @@ void launch_generic_attn(const DecodeArgs& a, hipStream_t st) {
 }
 
 template <int DW, int R2>
-void launch_mfma_attn(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.plan.max_items);
+void launch_mfma_attn(const DecodeArgs& a, const FuseArgs& f, hipStream_t st) {
   if (a.s.fmt == 0)
-    hipLaunchKernelGGL((decode_attn_dma<DW, R2, (DW == 128 && R2 == 8) ? 3 : 3, (DW == 128 && R2 == 8) ? 1 : 2>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_attn_dma<DW, R2, 3, (DW == 128 && R2 == 8) ? 1 : 2>), attn_grid(a, f), dim3(256), 0, st, a, f);
   else
-    hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 1>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 1>), attn_grid(a, f), dim3(256), 0, st, a, f);
 }
 
 }  // namespace
@@ -1600,6 +1653,11 @@ void launch_mfma_attn(const DecodeArgs& a, hipStream_t st) {
 // dequantisation runs on two workgroups per CU) and the DMA ring kernel faster for bf16.
 bool decode_uses_wave(const Shape& s) {
   return s.dtype == 1 && s.n_heads == 32 && (s.r_pairs == 2 || s.r_pairs == 4) && s.d_kv == 256;
+}
+
+// Specialised attention kernels that run the second phase of a split-K append (see FuseArgs).
+static bool attn_takes_append(const Shape& s) {
+  return decode_uses_wave(s) || (decode_uses_mfma(s) && (s.fmt == 1 || s.d_kv == 512));
 }
 
 bool decode_uses_mfma(const Shape& s) {
@@ -1664,12 +1722,20 @@ hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, hipStr
   const int nx = (aa.s.d_kv + aa.s.n_rope_cols() + 31) / 32;
   const int n_qp = da.s.n_heads * (da.s.d_kv / 128) * ((da.batch + 31) / 32);
   hipLaunchKernelGGL(decode_step_prologue, dim3(nx * ks + n_qp), dim3(256), 0, st, aa, ks, da);
+  // the split-K reduction runs inside the attention launch when its kernel takes it
+  if (aa.t_new <= FUSE_MAXR && attn_takes_append(da.s)) {
+    FuseArgs f{aa, ks};
+    return launch_decode(da, st, 2 | 4, &f);
+  }
   hipError_t e = launch_append_reduce(aa, ks, st);
   if (e != hipSuccess) return e;
   return launch_decode(da, st, 2 | 4);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask) {
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask, const FuseArgs* fuse) {
+  FuseArgs nf{};
+  nf.ks = 0;
+  const FuseArgs& f = fuse ? *fuse : nf;
   const int nh = a.s.n_heads;
   if (phase_mask & 1) {
     dim3 gq(nh, (a.s.d_kv + 63) / 64, (a.batch + QB - 1) / QB);
@@ -1683,15 +1749,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask) {
   if (phase_mask & 2) {
     if (decode_uses_wave(a.s)) {
       const int r = a.s.r_pairs;
-      if (a.s.fmt == 1 && r == 4) launch_wave_attn<256, 8, 1, 3>(a, st);
-      else if (a.s.fmt == 1) launch_wave_attn<256, 4, 1, 3>(a, st);
-      else if (r == 4) launch_wave_attn<256, 8, 0, 2>(a, st);
-      else launch_wave_attn<256, 4, 0, 3>(a, st);
+      if (a.s.fmt == 1 && r == 4) launch_wave_attn<256, 8, 1, 3>(a, f, st);
+      else if (a.s.fmt == 1) launch_wave_attn<256, 4, 1, 3>(a, f, st);
+      else if (r == 4) launch_wave_attn<256, 8, 0, 2>(a, f, st);
+      else launch_wave_attn<256, 4, 0, 3>(a, f, st);
     } else if (decode_uses_mfma(a.s)) {
-      if (a.s.d_kv == 512 && a.s.r_pairs == 4) launch_mfma_attn<128, 8>(a, st);
-      else if (a.s.d_kv == 512 && a.s.r_pairs == 2) launch_mfma_attn<128, 4>(a, st);
-      else if (a.s.d_kv == 256 && a.s.r_pairs == 4) launch_mfma_attn<64, 8>(a, st);
-      else launch_mfma_attn<64, 4>(a, st);
+      if (a.s.d_kv == 512 && a.s.r_pairs == 4) launch_mfma_attn<128, 8>(a, f, st);
+      else if (a.s.d_kv == 512 && a.s.r_pairs == 2) launch_mfma_attn<128, 4>(a, f, st);
+      else if (a.s.d_kv == 256 && a.s.r_pairs == 4) launch_mfma_attn<64, 8>(a, f, st);
+      else launch_mfma_attn<64, 4>(a, f, st);
     } else if (a.s.dtype == 0) {
       launch_generic_attn<float>(a, st);
     } else {

@@ -82,7 +82,14 @@ struct PrefillArgs {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);  // uses a.ws when set and useful
 // phase_mask bit 0: q-prep, bit 1: attention, bit 2: combine
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask = 7);
+// Split-K append whose second phase runs inside the decode attention launch (ks == 0: none): the
+// workgroup whose token range holds a new token writes its cache row first; rows outside every range
+// go to `batch` extra workgroups.
+struct FuseArgs {
+  AppendArgs a;
+  int ks;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask = 7, const FuseArgs* fuse = nullptr);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 // Decode step: split-K append of the new tokens (aa.ws = its partial sums) and decode (da), with the
 // append's first phase and the query preparation in one launch.  Requires decode_step_fusable().

@@ -1,5 +1,7 @@
-// Device pieces shared by the append kernels and the fused decode-step prologue (gfx950).
+// Device pieces shared by the append kernels and the fused decode step (gfx950).
 #pragma once
+
+#include <hip/hip_fp16.h>
 
 #include "common.h"
 #include "kernels.h"
@@ -8,6 +10,130 @@ namespace mla {
 
 constexpr int SM_MAXM = 64;  // few-token appends: at most 64 tokens (two 32-row MFMA blocks)
 constexpr int KS_MAX = 16;   // model-width slices of the split-K append
+
+// Cache row and position of token m of an append (t_new consecutive tokens per sequence).
+__device__ __forceinline__ int cache_row(const AppendArgs& a, int m, int* pos_out) {
+  int b = m / a.t_new;
+  int i = m - b * a.t_new;
+  int sp = a.start_pos[b];
+  sp = sp < 0 ? 0 : (sp > a.max_start ? a.max_start : sp);
+  int pos = sp + i;
+  *pos_out = pos;
+  return b * a.t_max + pos;
+}
+
+// Output elements of the append epilogue, one function per kind so that every path that writes cache
+// rows from fp32 projections runs the same arithmetic.
+// Latent column n of a dense cache row.
+__device__ __forceinline__ void store_latent(const AppendArgs& a, size_t row, int n, float v) {
+  ((bf16*)a.ckv)[row * a.s.d_kv + n] = (bf16)v;
+}
+// int4 group g of a cache row from its 32 projected values v(c) = vals[c * stride].
+__device__ __forceinline__ void store_group(const AppendArgs& a, size_t row, int g, const float* vals, int stride) {
+  const int D = a.s.d_kv;
+  float am = 0.f;
+  for (int c = 0; c < 32; ++c) am = fmaxf(am, fabsf(vals[c * stride]));
+  __half s = int4_scale(am);
+  float sf = __half2float(s);
+  uint8_t* codes = (uint8_t*)a.ckv + row * (D / 2) + 16 * g;
+  for (int i = 0; i < 16; ++i) {
+    int c0 = int4_code(vals[2 * i * stride], sf), c1 = int4_code(vals[(2 * i + 1) * stride], sf);
+    codes[i] = (uint8_t)((c0 & 15) | ((c1 & 15) << 4));
+  }
+  ((__half*)a.ckv_scale)[row * (D / 32) + g] = s;
+}
+// Retained RoPE pair at offset rel (even) of a row's RoPE block: rotate (x0, x1) at position pos.
+__device__ __forceinline__ void store_rope_pair(const AppendArgs& a, size_t row, int pos, int rel, float x0, float x1) {
+  const int r = a.s.r_pairs, R2 = a.s.r2(), NR = a.s.n_rope_cols(), half = a.s.d_head / 2;
+  int h = rel / R2, jj = (rel - h * R2) >> 1;
+  int p = load_pair(a.pair_idx, h * r + jj, half);
+  float cs = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
+  ((bf16*)a.krope)[row * NR + rel] = (bf16)(x0 * cs - x1 * sn);
+  ((bf16*)a.krope)[row * NR + rel + 1] = (bf16)(x0 * sn + x1 * cs);
+}
+
+// Epilogue of the few-token paths for output columns n0 .. n0 + 31 (one int4 group or 16 RoPE pairs):
+// element (m, c) of fin[m * ld + c] is column n0 + c of token m (fp32); rows[m] / poss[m] are the
+// token's cache row and position.
+__device__ __forceinline__ void append_epilogue(const AppendArgs& a, const float* fin, int ld, const int* rows,
+                                                const int* poss, int n0, int M) {
+  const int D = a.s.d_kv, NR = a.s.n_rope_cols();
+  if (n0 < D) {
+    if (a.s.fmt == 0) {
+      for (int idx = threadIdx.x; idx < M * 32; idx += blockDim.x) {
+        int m = idx >> 5, c = idx & 31;
+        store_latent(a, (size_t)rows[m], n0 + c, fin[m * ld + c]);
+      }
+    } else {
+      for (int m = threadIdx.x; m < M; m += blockDim.x) store_group(a, (size_t)rows[m], n0 / 32, fin + m * ld, 1);
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < M * 16; idx += blockDim.x) {
+      int m = idx >> 4, cp = 2 * (idx & 15);
+      int rel = n0 + cp - D;
+      if (rel >= NR) continue;
+      store_rope_pair(a, (size_t)rows[m], poss[m], rel, fin[m * ld + cp], fin[m * ld + cp + 1]);
+    }
+  }
+}
+
+// Split-K append, phase 2 for the tokens of sequence b at cache positions [p_lo, p_hi) (at most
+// FUSE_MAXR, all of them new tokens of this append): each output column's KS partial sums are added in
+// the order append_reduce uses, then the epilogue writes the cache rows, all columns at once.  `lds`
+// holds FUSE_MAXR * (N + 4) floats plus 2 * FUSE_MAXR ints.  Called by every thread of the workgroup.
+// The stores are not waited for: the caller waits for vmcnt 0 before any load that reads the rows.
+constexpr int FUSE_MAXR = 8;
+__device__ __forceinline__ void append_rows_fused(const AppendArgs& a, int KS, int b, int p_lo, int p_hi, float* lds) {
+  const int D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR, M = a.batch * a.t_new, ld = N + 4;
+  const int R = p_hi - p_lo;
+  int* rows = (int*)(lds + FUSE_MAXR * ld);
+  int* poss = rows + FUSE_MAXR;
+  int sp = a.start_pos[b];
+  sp = sp < 0 ? 0 : (sp > a.max_start ? a.max_start : sp);
+  const int m0 = b * a.t_new + (p_lo - sp);
+  if ((int)threadIdx.x < R) {
+    int pos;
+    rows[threadIdx.x] = cache_row(a, m0 + threadIdx.x, &pos);
+    poss[threadIdx.x] = pos;
+  }
+  const float* part = (const float*)a.ws;
+  for (int base = 0; base < R * N; base += 4 * (int)blockDim.x) {
+    float v[4][KS_MAX];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = base + it * blockDim.x + threadIdx.x;
+      const int m = idx / N, n = idx - m * N;
+#pragma unroll
+      for (int ks = 0; ks < KS_MAX; ++ks)
+        v[it][ks] = (ks < KS && idx < R * N) ? part[((size_t)ks * M + m0 + m) * N + n] : 0.f;
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = base + it * blockDim.x + threadIdx.x;
+      float sum = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS_MAX; ++ks) sum += v[it][ks];
+      if (idx < R * N) lds[(idx / N) * ld + idx % N] = sum;
+    }
+  }
+  lds_barrier();
+  if (a.s.fmt == 0) {
+    for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x) {
+      const int m = idx / D, n = idx - m * D;
+      store_latent(a, (size_t)rows[m], n, lds[m * ld + n]);
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < R * (D / 32); idx += blockDim.x) {
+      const int m = idx / (D / 32), g = idx - m * (D / 32);
+      store_group(a, (size_t)rows[m], g, lds + m * ld + 32 * g, 1);
+    }
+  }
+  for (int idx = threadIdx.x; idx < R * (NR / 2); idx += blockDim.x) {
+    const int m = idx / (NR / 2), rel = 2 * (idx - m * (NR / 2));
+    store_rope_pair(a, (size_t)rows[m], poss[m], rel, lds[m * ld + D + rel], lds[m * ld + D + rel + 1]);
+  }
+  lds_barrier();  // the scratch may be reused
+}
 
 // Split-K append, phase 1, workgroup (bx: 32 output columns, by: one of KS slices of the model width):
 // 4 waves split the slice, MFMA 32x32x16 over up to two 32-token blocks, and the workgroup's partial

@@ -289,3 +289,64 @@ def test_decode_step_matches_separate_calls(variant):
         ref = oracle.decode_ref(q[b], c, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head, cfg.theta)
         r, a = assert_close(got[b], ref, cfg.dtype, f"decode_step b={b}")
         log(f"  b={b} rel-L2={r:.2e} max-abs={a:.2e}")
+
+
+@pytest.mark.parametrize("variant", ["wave_bf16", "wave_int4", "multi_bf16", "multi_int4"])
+def test_decode_step_fused_rows(variant):
+    """Decode steps whose append reduction runs inside the attention launch: the latent-256 per-wave kernel
+    (bf16 and int4), and several new tokens per sequence with new rows in a first tile, straddling two work
+    items, at the end of a range, and past a sequence's decode length (written by the extra workgroups).
+    Output and cache rows equal mla_cache_append_ws followed by mla_decode bit for bit."""
+    from mla_latent_kv_cache_amd import LatentCache, append, append_ws, decode, decode_step, pack_weights
+
+    fmt = "int4_g32" if variant.endswith("int4") else "dense"
+    if variant.startswith("wave"):
+        cfg = scaled(CONFIGS[3], family="mid", batch=4, cache_fmt=fmt, ctx_range=None)
+        t_new, ctx = 1, [300, 1, 77, 129]          # tokens already cached per sequence
+        extra = [0, 0, 0, 0]                         # new rows past the decode length
+    else:
+        cfg = scaled(CONFIGS[1], family="mid", batch=5, cache_fmt=fmt)
+        t_new, ctx = 3, [0, 61, 126, 250, 40]
+        extra = [0, 0, 0, 0, 2]
+    B = len(ctx)
+    t_max = 320
+    start = [c for c in ctx]
+    lens = [c + t_new - e for c, e in zip(ctx, extra)]
+    log(f"[decode-step-fused] {variant} ctx={ctx} t_new={t_new} lens={lens}")
+    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    shape = shape_of(cfg)
+    w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
+    caches = [LatentCache.allocate(shape, B, t_max, fill=float("nan")) for _ in range(2)]
+    xs = [synth.context_x(cfg, b, c + t_new) for b, c in enumerate(ctx)]
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for cache in caches:
+        if cache.ckv_scale is not None:
+            cache.ckv_scale.fill_(float("nan"))
+        for b, c in enumerate(ctx):
+            if c == 0:
+                continue
+            xt = torch.from_numpy(xs[b][:c].astype(np.float32)).cuda().to(torch_dtype(cfg)).reshape(1, c, -1)
+            view = LatentCache(shape, cache.ckv[b:b + 1], None if cache.ckv_scale is None else cache.ckv_scale[b:b + 1],
+                               cache.krope[b:b + 1], 1, t_max)
+            append(w, view, xt, zero, 0)
+    x_new = torch.from_numpy(np.stack([x[c:c + t_new] for x, c in zip(xs, ctx)]).astype(np.float32))
+    x_new = x_new.cuda().to(torch_dtype(cfg)).contiguous()
+    start_t = torch.tensor(start, dtype=torch.int32, device="cuda")
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    q = np.stack([decode_query(cfg, layer, x[c + t_new - 1]) for x, c in zip(xs, ctx)])
+    qt = torch.from_numpy(q.astype(np.float32)).cuda().to(torch_dtype(cfg))
+    out_step = decode_step(w, caches[0], x_new, start_t, max(start), qt, lens_t, max(lens))
+    append_ws(w, caches[1], x_new, start_t, max(start))
+    out_sep = decode(w, caches[1], qt, lens_t, max(lens))
+    torch.cuda.synchronize()
+
+    def same_bits(u, v):  # rows never written hold NaN, which == never matches
+        return torch.equal(u.contiguous().view(torch.uint8), v.contiguous().view(torch.uint8))
+
+    assert torch.equal(out_step, out_sep), "decode_step differs from append_ws + decode"
+    assert same_bits(caches[0].ckv, caches[1].ckv) and same_bits(caches[0].krope, caches[1].krope)
+    if caches[0].ckv_scale is not None:
+        assert same_bits(caches[0].ckv_scale, caches[1].ckv_scale)
+    # the new rows were written (not NaN) for every sequence, including rows past the decode length
+    for b, c in enumerate(ctx):
+        assert not torch.isnan(caches[0].krope[b, c:c + t_new].float()).any(), f"new RoPE rows of b={b} missing"
