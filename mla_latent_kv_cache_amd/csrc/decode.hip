@@ -481,8 +481,31 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   uint16_t sreg[2][CCH];
   kv_t kreg[2][4];
 
+  // full tiles: a wave-uniform tile base plus per-lane offsets that do not change per tile
+  constexpr int RBY = FMT == 0 ? D * 2 : D / 2;  // latent bytes per cache row
+  uint32_t coff[CCH], soff[CCH];
+#pragma unroll
+  for (int it = 0; it < CCH; ++it) {
+    const int c = it * 64 + lane, row = c / CPR, q = c - row * CPR;
+    coff[it] = row * RBY + (FMT == 0 ? 2 * (w * DW + 8 * q) : (w * DW + 32 * q) / 2);
+    soff[it] = 2 * (row * (D / 32) + (w * DW) / 32 + q);
+  }
+  const uint32_t koff = (((8 * w + 4 * hb) * 32 + h) * R2) * 2;
   auto load_tile = [&](auto bsel, int tt) {
     constexpr int B = decltype(bsel)::value;
+    if (tt + 32 <= t1) {
+      const char* cb = (const char*)a.ckv + (rowb + tt) * RBY;
+      const char* sb = (const char*)a.ckv_scale + (rowb + tt) * (D / 32) * 2;
+      const char* kb = (const char*)krb + (size_t)tt * 32 * R2 * 2 + koff;
+#pragma unroll
+      for (int it = 0; it < CCH; ++it) {
+        creg[B][it] = *(const u32x4*)(cb + coff[it]);
+        if (FMT == 1) sreg[B][it] = *(const uint16_t*)(sb + soff[it]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kreg[B][i] = *(const kv_t*)(kb + i * 32 * R2 * 2);
+      return;
+    }
 #pragma unroll
     for (int it = 0; it < CCH; ++it) {
       int c = it * 64 + lane, row = c / CPR, q = c - row * CPR;
@@ -514,7 +537,12 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
         for (int u = 0; u < 4; ++u) {
           bf16x8 v;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (bf16)int4_dequant(nibble(wd[u] >> (8 * (e >> 1)), e & 1), s);
+          for (int e = 0; e < 8; ++e) {
+            // code + 2^23 + 8 as an fp32 bit pattern (nibble e of the word, sign bit flipped), minus
+            // 2^23 + 8: the signed code exactly, then times the scale as int4_dequant
+            const float code = __uint_as_float(((wd[u] >> (4 * e)) & 15u) ^ 0x4B000008u) - 8388616.0f;
+            v[e] = (bf16)(code * s);
+          }
           *(bf16x8*)&cw[row * CP + 32 * q + 8 * u] = v;
         }
       }
@@ -565,25 +593,36 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
       for (int i = 0; i < 4; ++i) sc[4 * e4 + i] = v[i];
     }
     par ^= 1;
-    float mt = -INFINITY;
+    if (tt + 32 > t1) {  // last, partial tile: mask rows past the sequence
+      asm volatile("" ::: "memory");  // keep this a branch (not if-converted into every tile)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      int n = 8 * (e >> 2) + 4 * hb + (e & 3);
-      if (tt + n >= t1) sc[e] = -INFINITY;
-      mt = fmaxf(mt, sc[e]);
+      for (int e = 0; e < 16; ++e)
+        if (tt + 8 * (e >> 2) + 4 * hb + (e & 3) >= t1) sc[e] = -INFINITY;
     }
+    float mt = sc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mt = fmaxf(mt, sc[e]);
     mt = fmaxf(mt, shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
+    // the running max is raised only when a tile exceeds it by more than 2^8 (rare after the first
+    // tile); a raise rescales the latent accumulators of that head
+    const bool raise = mt > m_run + 8.f;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      asm volatile("" ::: "memory");  // keep this a branch (not if-converted into every tile)
+      const float m_new = raise ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) oacc[blk] *= alpha;
+      m_run = m_new;
+    }
     float p[16], rs = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      p[e] = exp2f(sc[e] - m_new);
+      p[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
       rs += p[e];
     }
     rs += shfl_xor(rs, 32);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
+    l_run += rs;
     bf16x8 pb[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -591,7 +630,6 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
       for (int e = 0; e < 8; ++e) pb[c][e] = (bf16)p[8 * c + e];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
-      oacc[blk] *= alpha;
       const int col = blk * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
