@@ -192,6 +192,18 @@ __global__ __launch_bounds__(256, 2) void rec_vt_gemm(PrefillArgs a, int N) {
 constexpr int FQ = 256, FKV = 64, FNS = 4;
 constexpr int KT_BYTES = FKV * 256, VT_BYTES = 128 * FKV * 2, SLOT = KT_BYTES + VT_BYTES;
 
+// Schedule of a block of 16 operand reads from LDS and the 16 MFMAs that use them: six reads ahead,
+// then one MFMA per read, so that the matrix core does not wait for LDS latency between MFMAs.
+__device__ __forceinline__ void lds_ahead_16() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);  // MFMA
+}
+
 // One query tile of one (sequence, head) pair, all 8 waves of the workgroup.
 __device__ __forceinline__ void attend_query_tile(const PrefillArgs& a, char* ring, int pair, int qt) {
   const int S = a.seq_len, SP = a.plan.s_pad, NH = a.s.n_heads, r = a.s.r_pairs;
@@ -307,6 +319,7 @@ __device__ __forceinline__ void attend_query_tile(const PrefillArgs& a, char* ri
             oacc[db] = mfma32(av, pb[kb][c], oacc[db]);
           }
       }
+      lds_ahead_16();
     }
     // keep the two products apart: hoisting the score operands above the PV product would raise the
     // register pressure past two waves per SIMD
@@ -323,6 +336,7 @@ __device__ __forceinline__ void attend_query_tile(const PrefillArgs& a, char* ri
           sacc[kb] = mfma32(av, qv[s8], sacc[kb]);
         }
       }
+      lds_ahead_16();
     }
   };
   // V phase of tile kt: mask, online softmax (lazy rescale), P(kt) in bf16 for the next M phase
