@@ -1,6 +1,7 @@
 // Device-side helpers shared by the gfx950 kernels of the latent-cache library.
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -1792,10 +1792,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask, co
       else if (r == 4) launch_wave_attn<256, 8, 0, 2>(a, f, st);
       else launch_wave_attn<256, 4, 0, 3>(a, f, st);
     } else if (decode_uses_mfma(a.s)) {
-      if (a.s.d_kv == 512 && a.s.r_pairs == 4) launch_mfma_attn<128, 8>(a, f, st);
-      else if (a.s.d_kv == 512 && a.s.r_pairs == 2) launch_mfma_attn<128, 4>(a, f, st);
-      else if (a.s.d_kv == 256 && a.s.r_pairs == 4) launch_mfma_attn<64, 8>(a, f, st);
-      else launch_mfma_attn<64, 4>(a, f, st);
+      // latent width 512 (width 256 takes the per-wave kernel above)
+      if (a.s.r_pairs == 4) launch_mfma_attn<128, 8>(a, f, st);
+      else launch_mfma_attn<128, 4>(a, f, st);
     } else if (a.s.dtype == 0) {
       launch_generic_attn<float>(a, st);
     } else {

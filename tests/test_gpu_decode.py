@@ -97,6 +97,14 @@ def test_tiny_bf16_generic_path():
     run_decode_case(cfg, [200, 57, 1], 256)
 
 
+@pytest.mark.parametrize("d_kv,r", [(512, 4), (256, 2)])
+def test_odd_heads_bf16_generic_attention_combine(d_kv, r):
+    """Five heads: the generic attention kernel writes fp32 split results, which the one-launch merge and
+    W_uv projection reads (the MFMA kernels write the fp16 form); ragged lengths across several splits."""
+    cfg = scaled(CONFIGS[1], family="odd", batch=4, d_kv=d_kv, r_pairs=r)
+    run_decode_case(cfg, [700, 1, 129, 0], 768)
+
+
 def test_mid_bf16_dkv512_r4():
     cfg = scaled(CONFIGS[1], family="mid", batch=5)
     run_decode_case(cfg, [1000, 1, 0, 333, 64], 1024)
