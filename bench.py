@@ -63,7 +63,7 @@ def parse():
 # ---------------------------------------------------------------- traffic from byte counters
 
 DECODE_SOURCES = ("mla_latent_kv_cache_amd/csrc/decode.hip", "mla_latent_kv_cache_amd/csrc/common.h",
-                  "mla_latent_kv_cache_amd/csrc/kernels.h")
+                  "mla_latent_kv_cache_amd/csrc/kernels.h", "mla_latent_kv_cache_amd/csrc/step.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
