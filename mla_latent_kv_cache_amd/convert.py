@@ -8,6 +8,9 @@ Implements the two steps of the MHA2MLA key-designs section (Paper-Notes ACL2025
     NoPE key columns, then all value columns); W_dkv spans its top-d_kv left singular subspace
     (orthonormal columns) and the up-projections are W_dkv^T [W_k,nope | W_v] split per head.
 
+The pages' ablation variants are options of convert_layer: the fixed partial-RoPE strategies S_high,
+S_low and S_uniform (kept_pairs), and SVD_split at the same latent width.
+
 The subspace is found from the eigen-decomposition of the smaller Gram matrix, which gives the same
 truncated factorisation as an SVD up to the signs of the basis vectors.  This runs once per layer,
 outside the inference path.
@@ -54,11 +57,39 @@ def low_rank_factors(m, rank):
     return u, sig
 
 
-def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv):
+def kept_pairs(strategy, scores, r):
+    """Kept RoPE subspaces [n_h, r] (ascending, int32) under one of the partial-RoPE strategies the pages
+    compare (README strategy list; ablation table of the Paper-Notes page).  Subspace p turns at
+    frequency theta^(-2p/d_h), decreasing in p:
+      "2-norm"  -- head-wise top-r by score (the method's own choice),
+      "high"    -- the r highest frequencies, p = 0 .. r-1, for every head,
+      "low"     -- the r lowest, p = d_h/2 - r .. d_h/2 - 1,
+      "uniform" -- every (d_h/2)/r-th subspace from p = 0, p_k = floor(k d_h / (2r))."""
+    n_heads, n_pairs = scores.shape
+    if strategy == "2-norm":
+        return top_pairs(scores, r)
+    table = {
+        "high": np.arange(r),
+        "low": np.arange(n_pairs - r, n_pairs),
+        "uniform": np.arange(r) * n_pairs // max(r, 1),
+    }
+    if strategy not in table:
+        raise ValueError(f"unknown partial-RoPE strategy {strategy!r}; expected one of 2-norm, high, low, uniform")
+    return np.broadcast_to(table[strategy].astype(np.int32), (n_heads, r)).copy()
+
+
+def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv, strategy="2-norm", svd="joint"):
     """Returns the converted layer in math layouts:
     pair_idx [n_h, r], w_dkv [d, d_kv], w_krope [d, n_h*2r], w_uk [n_h, d_kv, d_h-2r], w_uv [n_h, d_kv, d_h],
-    sigma (all singular values of [W_k,nope | W_v])."""
-    pair_idx = top_pairs(pair_scores(x_cal, w_q, w_k, n_heads, d_head), r)
+    and the singular values: sigma (all of [W_k,nope | W_v]) for the joint SVD, sigma_k / sigma_v (of W_k,nope
+    and of W_v) for the split one.
+
+    svd="joint" is the method's joint low-rank step.  svd="split" is the SVD_split ablation at the same latent
+    width: the first d_kv/2 latent dims span the top left singular subspace of W_k,nope alone and the other
+    d_kv - d_kv/2 that of W_v alone, so W_uk is zero on the value half and W_uv on the key half; the
+    result is an ordinary MLA layer that the attention kernels run unchanged."""
+    scores = pair_scores(x_cal, w_q, w_k, n_heads, d_head)
+    pair_idx = kept_pairs(strategy, scores, r)
     d = w_k.shape[0]
     wk = w_k.reshape(d, n_heads, d_head // 2, 2)
     keep = np.zeros((n_heads, d_head // 2), dtype=bool)
@@ -66,11 +97,27 @@ def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv):
         keep[h, pair_idx[h]] = True
     w_krope = np.stack([wk[:, h, pair_idx[h], :] for h in range(n_heads)], axis=1).reshape(d, n_heads * 2 * r)
     w_knope = np.stack([wk[:, h, ~keep[h], :].reshape(d, -1) for h in range(n_heads)], axis=1).reshape(d, -1)
-    m = np.hstack([w_knope, w_v])
-    u, sig = low_rank_factors(m, d_kv)
-    z = u.T @ m
     dn = d_head - 2 * r
-    w_uk = z[:, : n_heads * dn].reshape(d_kv, n_heads, dn).transpose(1, 0, 2)
-    w_uv = z[:, n_heads * dn:].reshape(d_kv, n_heads, d_head).transpose(1, 0, 2)
-    return dict(pair_idx=pair_idx, w_dkv=u, w_krope=w_krope, w_uk=np.ascontiguousarray(w_uk),
-                w_uv=np.ascontiguousarray(w_uv), sigma=sig)
+    out = dict(pair_idx=pair_idx, w_krope=w_krope, scores=scores)
+    if svd == "joint":
+        m = np.hstack([w_knope, w_v])
+        u, sig = low_rank_factors(m, d_kv)
+        z = u.T @ m
+        w_uk = z[:, : n_heads * dn].reshape(d_kv, n_heads, dn).transpose(1, 0, 2)
+        w_uv = z[:, n_heads * dn:].reshape(d_kv, n_heads, d_head).transpose(1, 0, 2)
+        out.update(w_dkv=u, sigma=sig)
+    elif svd == "split":
+        rk = d_kv // 2
+        if rk > min(w_knope.shape) or d_kv - rk > min(w_v.shape):
+            raise ValueError("svd='split': d_kv/2 exceeds the rank W_k,nope or W_v can have")
+        uk, sig_k = low_rank_factors(w_knope, rk)
+        uv, sig_v = low_rank_factors(w_v, d_kv - rk)
+        w_uk = np.zeros((n_heads, d_kv, dn))
+        w_uv = np.zeros((n_heads, d_kv, d_head))
+        w_uk[:, :rk, :] = (uk.T @ w_knope).reshape(rk, n_heads, dn).transpose(1, 0, 2)
+        w_uv[:, rk:, :] = (uv.T @ w_v).reshape(d_kv - rk, n_heads, d_head).transpose(1, 0, 2)
+        out.update(w_dkv=np.hstack([uk, uv]), sigma_k=sig_k, sigma_v=sig_v)
+    else:
+        raise ValueError(f"unknown SVD variant {svd!r}; expected joint or split")
+    out.update(w_uk=np.ascontiguousarray(w_uk), w_uv=np.ascontiguousarray(w_uv))
+    return out

@@ -9,7 +9,8 @@ It is written from the method as the pages state it (Paper-Notes ACL2025 page
 "method / key designs"), as plainly as possible:
 
 * convert.py   -- 2-norm pair scores, head-wise top-r selection, joint SVD of
-                  [W_k,nope ; W_v] (and the split-SVD variant used as a bound)
+                  [W_k,nope ; W_v]; the ablation variants (fixed S_high / S_low /
+                  S_uniform subspaces, SVD_split at the same latent width)
 * attention.py -- latent-cache append (down-projection + partial RoPE) and the
                   UNABSORBED attention in which K_nope and V are rebuilt per head;
                   the absorbed form is kept separately only to pin the algebra
@@ -27,8 +28,10 @@ from .convert import (  # noqa: F401
     joint_svd,
     pair_scores,
     select_pairs,
+    select_pairs_by,
     split_dims,
     split_svd,
+    split_svd_layer,
 )
 from .attention import (  # noqa: F401
     absorbed_decode_ref,

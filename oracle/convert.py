@@ -12,6 +12,9 @@ Follows the Paper-Notes ACL2025 page on MHA2MLA, section 关键设计 ("key desi
    W_dkv = U_trunc is the down-projection to the latent c_kv, and S V^T is split
    per head into the up-projections W_uk and W_uv.
 
+The ablation variants of the pages (partial-RoPE strategies S_high / S_low / S_uniform, and SVD_split
+at the same latent width) are select_pairs_by and split_svd_layer.
+
 Readings where the page leaves a step open (each also listed in the design notes):
 * scores aggregate over calibration tokens as the product of the mean pair norms,
   which is exactly the mean of the bound over every (query token, key token) pair;
@@ -60,6 +63,28 @@ def select_pairs(scores, r):
         order = sorted(range(n_pairs), key=lambda p: (-scores[h, p], p))
         out[h] = sorted(order[:r])
     return out
+
+
+def select_pairs_by(strategy, scores, r):
+    """Kept RoPE subspaces of every head under the partial-RoPE strategies the pages compare
+    (README strategy list: S_high, S_uniform, S_2-norm, S_low; ablation table of the Paper-Notes page).
+
+    Subspace p rotates at frequency theta^(-2p/d_h), which falls with p, so S_high keeps p = 0..r-1 and
+    S_low keeps the last r.  S_uniform keeps r subspaces evenly spaced from p = 0 with stride (d_h/2)/r
+    (reading: the page does not fix the offset).  S_2-norm is the head-wise top-r of the scores.
+    All strategies but S_2-norm give every head the same subspaces.  int32 [n_heads, r], ascending."""
+    n_heads, n_pairs = scores.shape
+    if strategy == "2-norm":
+        return select_pairs(scores, r)
+    if strategy == "high":
+        idx = list(range(r))
+    elif strategy == "low":
+        idx = list(range(n_pairs - r, n_pairs))
+    elif strategy == "uniform":
+        idx = [(k * n_pairs) // r for k in range(r)]
+    else:
+        raise ValueError(f"unknown partial-RoPE strategy {strategy!r}")
+    return np.array([idx] * n_heads, dtype=np.int32)
 
 
 def split_dims(pair_idx, d_head):
@@ -115,11 +140,41 @@ def split_svd(w_k, w_v, pair_idx, n_heads, d_head, rank_k, rank_v):
     return trunc(w_knope, rank_k), trunc(w_v, rank_v), w_knope
 
 
-def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv):
-    """Full conversion: calibration -> scores -> head-wise top-r -> joint SVD."""
+def split_svd_layer(w_k, w_v, pair_idx, n_heads, d_head, d_kv):
+    """SVD_split as an MLA layer of the same latent width (the pages' SVD ablation: separate SVDs of
+    the NoPE keys and of the values, same cache size).  Reading: the latent is split evenly, d_kv/2
+    dims from the truncated SVD of W_k,nope and d_kv - d_kv/2 from that of W_v:
+        W_dkv = [U_k | U_v],  W_uk,h = [S_k V_k^T restricted to head h ; 0],  W_uv,h = [0 ; S_v V_v^T of head h],
+    so keys read only the first half of c_kv and values only the second.  Same layouts as joint_svd."""
+    r = pair_idx.shape[1]
+    dn = d_head - 2 * r
+    rk = d_kv // 2
+    rv = d_kv - rk
+    w_knope, w_krope = _nope_and_rope_columns(w_k, pair_idx, n_heads, d_head)
+    if rk > min(w_knope.shape) or rv > min(w_v.shape):
+        raise ValueError("SVD_split: d_kv/2 exceeds the rank W_k,nope or W_v can have")
+    uk, sk, vtk = np.linalg.svd(w_knope, full_matrices=False)
+    uv, sv, vtv = np.linalg.svd(w_v, full_matrices=False)
+    w_dkv = np.concatenate([uk[:, :rk], uv[:, :rv]], axis=1)
+    zk = sk[:rk, None] * vtk[:rk]
+    zv = sv[:rv, None] * vtv[:rv]
+    w_uk = np.stack([np.concatenate([zk[:, h * dn:(h + 1) * dn], np.zeros((rv, dn))]) for h in range(n_heads)])
+    w_uv = np.stack([np.concatenate([np.zeros((rk, d_head)), zv[:, h * d_head:(h + 1) * d_head]]) for h in range(n_heads)])
+    return dict(w_dkv=w_dkv, w_uk=w_uk, w_uv=w_uv, w_krope=w_krope, sigma_k=sk, sigma_v=sv,
+                m=np.concatenate([w_knope, w_v], axis=1))
+
+
+def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv, strategy="2-norm", svd="joint"):
+    """Full conversion: calibration -> scores -> kept subspaces (S_2-norm by default, see
+    select_pairs_by) -> joint SVD (or SVD_split, see split_svd_layer)."""
     q, k = calibration_qk(x_cal, w_q, w_k, n_heads, d_head)
     scores = pair_scores(q, k)
-    pair_idx = select_pairs(scores, r)
-    out = joint_svd(w_k, w_v, pair_idx, n_heads, d_head, d_kv)
+    pair_idx = select_pairs_by(strategy, scores, r)
+    if svd == "joint":
+        out = joint_svd(w_k, w_v, pair_idx, n_heads, d_head, d_kv)
+    elif svd == "split":
+        out = split_svd_layer(w_k, w_v, pair_idx, n_heads, d_head, d_kv)
+    else:
+        raise ValueError(f"unknown SVD variant {svd!r}")
     out.update(pair_idx=pair_idx, scores=scores)
     return out

@@ -13,9 +13,11 @@ from .inputs import (  # noqa: F401
     bf16_bits,
     bits_to_f64,
     context_x,
+    eval_x,
     layer_weights,
     query_rows,
     round_to_device,
     scaled,
     seq_lens,
+    structured_layer_weights,
 )

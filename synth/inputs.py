@@ -4,7 +4,9 @@ Stream layout (numpy PCG64 seeded from a SeedSequence with an explicit spawn key
 
 * layer weights, keyed by shape family (tiny -> 0, mid -> 2, llama -> 1):
   spawn key (0,) W_q, (1,) W_k, (2,) W_v, each [d_model, n_heads*d_head] ~ N(0,1)*0.02;
-  spawn key (3,) calibration activations X_cal [n_calib, d_model] ~ N(0,1).
+  spawn key (3,) calibration activations X_cal [n_calib, d_model] ~ N(0,1);
+  spawn keys (4,), (5,) the structured layer and its X_cal, (6,) evaluation activations
+  (structured_layer_weights, eval_x).
 * per-configuration inputs, entropy 100 + config index:
   spawn key (0,) per-sequence context lengths (variable-length configs only);
   spawn key (1, b) the activations x_b [L_b, d_model] ~ N(0,1) of sequence b.
@@ -88,6 +90,41 @@ def layer_weights(family: str):
     w = [_gen(seed, (i,)).standard_normal((d, n_h * d_h)) * 0.02 for i in range(3)]
     x_cal = _gen(seed, (3,)).standard_normal((64, d))
     return w[0], w[1], w[2], x_cal
+
+
+def structured_layer_weights(family: str):
+    """W_q, W_k, W_v [d_model, n_heads*d_head] and X_cal [64, d_model] (fp64) with two kinds of structure
+    that i.i.d. weights lack (stream keys (4,) for the weights, (5,) for X_cal of the family's seed):
+
+    * a shared input subspace: each W = A diag(s) G_W + 0.05 N_W with one A [d, d/4] ~ N(0, 1/d) for all
+      three, s_i = exp(-3 i / (d/4)), and G_W, N_W ~ N(0, 1) of their own;
+    * a frequency band per head: the q and k columns of subspace p (dims 2p, 2p+1) of head h are scaled by
+      0.25 + 2 exp(-((p - c_h) / w)^2 / 2), c_h ~ uniform over the d_head/2 subspaces, w = d_head/32.
+    Each W is then scaled to an entry RMS of 0.02."""
+    d, n_h, d_h, seed = FAMILIES[family]
+    g = _gen(seed, (4,))
+    rho = d // 4
+    a = g.standard_normal((d, rho)) / np.sqrt(d)
+    spec = np.exp(-3.0 * np.arange(rho) / rho)
+    ws = []
+    for _ in range(3):
+        ws.append((a * spec) @ g.standard_normal((rho, n_h * d_h)) + 0.05 * g.standard_normal((d, n_h * d_h)) / np.sqrt(d))
+    n_pairs = d_h // 2
+    centre = g.integers(0, n_pairs, size=n_h)
+    p = np.arange(n_pairs)
+    gain = 0.25 + 2.0 * np.exp(-0.5 * ((p[None, :] - centre[:, None]) / (d_h / 32)) ** 2)  # [n_h, n_pairs]
+    col_gain = np.repeat(gain, 2, axis=1).reshape(n_h * d_h)
+    ws[0] = ws[0] * col_gain
+    ws[1] = ws[1] * col_gain
+    ws = [w * (0.02 / np.sqrt(np.mean(w * w))) for w in ws]
+    x_cal = _gen(seed, (5,)).standard_normal((64, d))
+    return ws[0], ws[1], ws[2], x_cal
+
+
+def eval_x(family: str, length: int) -> np.ndarray:
+    """Evaluation activations [length, d_model] ~ N(0, 1), fp64 (stream key (6,) of the family's seed)."""
+    d = FAMILIES[family][0]
+    return _gen(FAMILIES[family][3], (6,)).standard_normal((length, d))
 
 
 def seq_lens(cfg: Config) -> np.ndarray:

@@ -44,16 +44,17 @@ def assert_close(got, ref, dtype, what=""):
 
 
 @functools.lru_cache(maxsize=4)
-def converted_layer(family: str, r: int, d_kv: int, dtype: str):
+def converted_layer(family: str, r: int, d_kv: int, dtype: str, strategy: str = "2-norm", svd: str = "joint"):
     """The oracle's conversion of the family's seeded layer, with every weight rounded to the device dtype
-    (the GPU gets exactly these values; the oracle consumes them upcast to fp64)."""
+    (the GPU gets exactly these values; the oracle consumes them upcast to fp64).  strategy / svd select
+    the pages' ablation variants (partial-RoPE strategy, joint or split SVD)."""
     d, n_h, d_h, _ = FAMILIES[family]
     wq, wk, wv, xc = synth.layer_weights(family)
-    conv = oracle.convert_layer(wq, wk, wv, xc, n_h, d_h, r, d_kv)
+    conv = oracle.convert_layer(wq, wk, wv, xc, n_h, d_h, r, d_kv, strategy=strategy, svd=svd)
     out = {k: synth.round_to_device(conv[k], dtype) for k in ("w_dkv", "w_krope", "w_uk", "w_uv")}
     out["pair_idx"] = conv["pair_idx"]
     out["w_q"] = wq
-    out["sigma"] = conv["sigma"]
+    out["sigma"] = conv.get("sigma")
     return out
 
 

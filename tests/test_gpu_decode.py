@@ -22,13 +22,13 @@ def _to_np(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def run_decode_case(cfg, lens, t_max, sample=None, check_cache=True, repeat_bitwise=True):
+def run_decode_case(cfg, lens, t_max, sample=None, check_cache=True, repeat_bitwise=True, variant=("2-norm", "joint")):
     from mla_latent_kv_cache_amd import LatentCache, decode, pack_weights
 
     log(f"[decode] {cfg.name} family={cfg.family} d_kv={cfg.d_kv} r={cfg.r_pairs} fmt={cfg.cache_fmt} "
-        f"B={len(lens)} lens={list(lens)[:8]} t_max={t_max}")
+        f"B={len(lens)} lens={list(lens)[:8]} t_max={t_max} conversion={variant}")
     B = len(lens)
-    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype, *variant)
     shape = shape_of(cfg)
     w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
     cache = LatentCache.allocate(shape, B, t_max, fill=float("nan"))
@@ -148,6 +148,16 @@ def test_mid_short_ragged_lengths():
     cfg = scaled(CONFIGS[3], family="mid", batch=13, ctx_range=None)
     lens = [1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 127, 200, 513]
     run_decode_case(cfg, lens, 520, sample=[0, 2, 3, 4, 6, 9, 11, 12])
+
+
+@pytest.mark.parametrize("strategy,svd,fmt", [("high", "split", "dense"), ("low", "joint", "dense"),
+                                              ("uniform", "split", "int4_g32")])
+def test_ablation_variant_layers(strategy, svd, fmt):
+    """Layers converted with the pages' ablation variants (fixed partial-RoPE subspaces, SVD_split at the same
+    latent width) run through the same append and decode kernels; SVD_split leaves half of each
+    up-projection zero."""
+    cfg = scaled(CONFIGS[1], family="mid", batch=3, context=0, cache_fmt=fmt)
+    run_decode_case(cfg, [700, 33, 260], 704, variant=(strategy, svd))
 
 
 def test_mid_int4():

@@ -18,11 +18,12 @@ from parity_lib import assert_close, converted_layer, log, shape_of, torch_dtype
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill_case(cfg, S, B, rows=None, sample_b=None):
+def run_prefill_case(cfg, S, B, rows=None, sample_b=None, variant=("2-norm", "joint")):
     from mla_latent_kv_cache_amd import LatentCache, append, pack_weights, prefill
 
-    log(f"[prefill] family={cfg.family} r={cfg.r_pairs} d_kv={cfg.d_kv} B={B} S={S} rows={'all' if rows is None else rows}")
-    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    log(f"[prefill] family={cfg.family} r={cfg.r_pairs} d_kv={cfg.d_kv} B={B} S={S} "
+        f"rows={'all' if rows is None else rows} conversion={variant}")
+    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype, *variant)
     shape = shape_of(cfg)
     t_max = S + 3
     w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
@@ -76,6 +77,12 @@ def test_prefill_two_pairs_per_head():
 def test_prefill_head_count_not_multiple_of_8():
     """5 heads x 3 sequences = 15 (sequence, head) pairs: the scheduler's non-XCD-grouped order."""
     run_prefill_case(scaled(CONFIGS[2], family="odd"), S=300, B=3)
+
+
+@pytest.mark.parametrize("strategy,svd", [("high", "split"), ("uniform", "joint")])
+def test_prefill_ablation_variant_layers(strategy, svd):
+    """Layers converted with the pages' ablation variants run through the same append and prefill kernels."""
+    run_prefill_case(scaled(CONFIGS[2], family="mid"), S=300, B=2, variant=(strategy, svd))
 
 
 @pytest.mark.slow
