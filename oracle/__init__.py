@@ -15,6 +15,8 @@ It is written from the method as the pages state it (Paper-Notes ACL2025 page
                   UNABSORBED attention in which K_nope and V are rebuilt per head;
                   the absorbed form is kept separately only to pin the algebra
 * int4.py      -- group-32 absmax int4 codec of the latent (4-bit cache)
+* int2.py      -- group-32 affine 2-bit codec and the window of recent bf16 rows
+                  (2-bit cache)
 * cache_bytes.py -- KV-cache bytes per token and the reduction percentages
 
 All floating point is fp64 except the int4 codec, which emulates IEEE fp32 /
