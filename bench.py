@@ -139,8 +139,7 @@ def make_decode_workload(cfg, conv, lens, copies, seed):
         for b in range(B):
             L = int(lens[b])
             x = torch.randn((1, L, cfg.d_model), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-            view = LatentCache(shape, cache.ckv[b:b + 1], None if cache.ckv_scale is None else cache.ckv_scale[b:b + 1],
-                               cache.krope[b:b + 1], 1, t_max)
+            view = cache.view(b, b + 1)
             append(w, view, x, torch.zeros(1, dtype=torch.int32, device="cuda"), 0)
             del x
         caches.append(cache)

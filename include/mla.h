@@ -10,8 +10,9 @@
  *     the 2-norm contribution score), already rotated at the token's position.
  * K_nope and V of head h are recovered from c_kv through that head's up-projections W_uk,h and
  * W_uv,h (the split of Sigma V^T); the RoPE part is computed separately because it cannot be
- * merged into the matrices.  The optional 4-bit latent follows the page's remark that the
- * latent composes with KV-cache quantisation.
+ * merged into the matrices.  The optional 4-bit and 2-bit latents follow the page's remark that
+ * the latent composes with 4-bit or 2-bit KV-cache quantisation; the 2-bit one keeps the most recent
+ * tokens unquantised, as the README page's quantised-cache evaluation does (residual length 128).
  *
  * Conventions for every entry point
  *   - All pointers to tensors are DEVICE pointers to caller-owned memory unless marked [host].
@@ -56,12 +57,16 @@ typedef enum {
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
 
 typedef enum {
-  MLA_CACHE_DENSE = 0,   /* c_kv stored in the config dtype                                    */
-  MLA_CACHE_INT4_G32 = 1 /* c_kv as int4 codes, groups of 32 latent dims, fp16 absmax scale;
-                            k_rope stays in the config dtype (BF16 only)                        */
+  MLA_CACHE_DENSE = 0,       /* c_kv stored in the config dtype                                */
+  MLA_CACHE_INT4_G32 = 1,    /* c_kv as int4 codes, groups of 32 latent dims, fp16 absmax scale;
+                                k_rope stays in the config dtype (BF16 only)                    */
+  MLA_CACHE_INT2_G32_WIN = 2 /* c_kv of the last `window` positions of each sequence as bf16 rows
+                                in a ring, older positions as affine 2-bit codes (groups of 32
+                                latent dims, fp16 scale and offset); k_rope bf16 (BF16 only)    */
 } mla_cache_fmt;
 
-/* Layer shape.  d_head even; 0 <= r_pairs <= d_head/2; d_kv >= 1 (multiple of 32 for INT4_G32). */
+/* Layer shape.  d_head even; 0 <= r_pairs <= d_head/2; d_kv >= 1 (multiple of 32 for the INT4_G32
+ * and INT2_G32_WIN formats). */
 typedef struct {
   int32_t d_model;   /* model width d                                            */
   int32_t n_heads;   /* attention heads n_h                                      */
@@ -91,13 +96,24 @@ typedef struct {
  *   INT4_G32: ckv   [batch, t_max, d_kv/2]    uint8, byte i = (code[2i] & 15) | (code[2i+1] & 15) << 4,
  *                                             codes two's-complement in [-7, 7]
  *             ckv_scale [batch, t_max, d_kv/32] fp16 (ignored / may be NULL for DENSE)
- *   both:     krope [batch, t_max, n_h, 2r]   config dtype, pair (j, c) of head h at index h*2r + 2j + c */
+ *   INT2_G32_WIN:
+ *             ckv   [batch, t_max, d_kv/4]    uint8, byte i = code[4i] | code[4i+1] << 2 | code[4i+2] << 4
+ *                                             | code[4i+3] << 6, codes in [0, 3]; row pos holds position
+ *                                             pos once it has left the window
+ *             ckv_scale [batch, t_max, d_kv/32, 2] fp16 (s, z) per group; value = fp32(z + code * s)
+ *             ckv_window [batch, window, d_kv] bf16 ring: slot pos % window holds position pos while
+ *                                             pos >= L - window (L = the sequence's length)
+ *             window >= 0 (0: every row is codes); ckv_window may be NULL when window == 0
+ *   all:      krope [batch, t_max, n_h, 2r]   config dtype, pair (j, c) of head h at index h*2r + 2j + c
+ * ckv_window and window are read for INT2_G32_WIN only.                                          */
 typedef struct {
   void *ckv;
   void *ckv_scale;
   void *krope;
   int32_t batch;
   int32_t t_max;
+  void *ckv_window;
+  int32_t window;
 } mla_cache;
 
 /* ---------------------------------------------------------------- append
@@ -110,6 +126,12 @@ typedef struct {
  * Per token:  c_kv = x . W_dkv (fp32 accumulate, then rounded to the dtype, or quantised:
  *             s = fp16(absmax/7), code = clamp(rint(c/s), -7, 7), IEEE fp32 divisions);
  *             k_rope[h, j] = rotate((x . W_krope)[h, j, 0:2], pos * theta^(-2p/d_h)).
+ * INT2_G32_WIN: each append must extend its sequences (start_pos[b] = the current length, all earlier
+ *             positions written by earlier appends).  A row c_kv is rounded to bf16; rows that end up
+ *             among the last `window` positions go to the ring, every other row (a new one, or one
+ *             pushed out of the ring) is quantised from its bf16 value per group of 32:
+ *             z = fp16(min), s = fp16(max(max - z, 0) / 3), code = clamp(rint((c - z) / s), 0, 3)
+ *             (fp32 arithmetic, IEEE division; s == 0 gives codes 0; infinite fp16 values saturate).
  * t_new == 0 or batch == 0 is a no-op returning MLA_OK.                                        */
 int mla_cache_append(const mla_config *cfg, const mla_weights *w, mla_cache *cache, const void *x,
                      const int32_t *start_pos, int32_t t_new, int32_t max_start_pos, hipStream_t stream);
@@ -129,7 +151,8 @@ int mla_cache_append_ws(const mla_config *cfg, const mla_weights *w, mla_cache *
  * key-designs section: W_uk,h folded into the query, W_uv,h applied after the weighted latent sum).
  *   q          [batch, n_h, d_h] raw query (x . W_q, before RoPE, original head-dim order)
  *   seq_lens   [batch] int32 (device): L_b cached tokens, the query sits at position L_b - 1
- *              (append it first); L_b == 0 gives a zero output row
+ *              (append it first); L_b == 0 gives a zero output row.  INT2_G32_WIN: L_b must be the
+ *              sequence's appended length (the ring holds its last `window` positions)
  *   max_seq_len  host bound on seq_lens[], 0 <= max_seq_len <= t_max and <= rope_len
  *   out        [batch, n_h, d_h] per-head attention outputs (before the output projection)
  * Scores are (q_hat . k_hat) / sqrt(d_h) with softmax over positions 0..L_b-1.
@@ -179,6 +202,13 @@ int mla_prefill(const mla_config *cfg, const mla_weights *w, const mla_cache *ca
  * The latent quantiser of the INT4_G32 cache on its own, for bit-exact checks of the codes.
  *   in [n_groups*32] fp32 -> codes [n_groups*16] uint8 (packed as above), scales [n_groups] fp16 bits. */
 int mla_quantize_int4(const float *in, int64_t n_groups, uint8_t *codes, uint16_t *scales, hipStream_t stream);
+
+/* ---------------------------------------------------------------- 2-bit codec
+ * The latent quantiser of the INT2_G32_WIN cache on its own (values already on the bf16 grid in the
+ * cache; any fp32 values here), for bit-exact checks of the codes.
+ *   in [n_groups*32] fp32 -> codes [n_groups*8] uint8 (packed as above), meta [n_groups*2] fp16 bits
+ *   (s, z per group).                                                                           */
+int mla_quantize_int2(const float *in, int64_t n_groups, uint8_t *codes, uint16_t *meta, hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
 const char *mla_status_string(int status);

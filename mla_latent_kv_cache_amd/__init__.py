@@ -20,6 +20,7 @@ from .api import (  # noqa: F401
     pack_weights,
     prefill,
     prefill_workspace_bytes,
+    quantize_int2,
     quantize_int4,
     rope_tables,
 )

@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(PKG, "libmla_latent.so")
 
 MLA_OK = 0
 MLA_F32, MLA_BF16 = 0, 1
-MLA_CACHE_DENSE, MLA_CACHE_INT4_G32 = 0, 1
+MLA_CACHE_DENSE, MLA_CACHE_INT4_G32, MLA_CACHE_INT2_G32_WIN = 0, 1, 2
 
 EXPORTED = [
     "mla_cache_append",
@@ -24,6 +24,7 @@ EXPORTED = [
     "mla_prefill_workspace_bytes",
     "mla_prefill",
     "mla_quantize_int4",
+    "mla_quantize_int2",
     "mla_status_string",
 ]
 
@@ -52,6 +53,8 @@ class MlaCache(ctypes.Structure):
         ("krope", ctypes.c_void_p),
         ("batch", ctypes.c_int32),
         ("t_max", ctypes.c_int32),
+        ("ckv_window", ctypes.c_void_p),
+        ("window", ctypes.c_int32),
     ]
 
 
@@ -95,6 +98,8 @@ def load():
     lib.mla_prefill.restype = ctypes.c_int
     lib.mla_quantize_int4.argtypes = [P, i64, P, P, P]
     lib.mla_quantize_int4.restype = ctypes.c_int
+    lib.mla_quantize_int2.argtypes = [P, i64, P, P, P]
+    lib.mla_quantize_int2.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     _lib = lib

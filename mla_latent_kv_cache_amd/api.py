@@ -15,7 +15,10 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import MLA_BF16, MLA_CACHE_DENSE, MLA_CACHE_INT4_G32, MLA_F32, MlaCache, MlaConfig, MlaWeights
+from ._lib import (MLA_BF16, MLA_CACHE_DENSE, MLA_CACHE_INT2_G32_WIN, MLA_CACHE_INT4_G32, MLA_F32, MlaCache, MlaConfig,
+                   MlaWeights)
+
+_FMT = {"dense": MLA_CACHE_DENSE, "int4_g32": MLA_CACHE_INT4_G32, "int2_g32_win": MLA_CACHE_INT2_G32_WIN}
 
 
 class MlaError(RuntimeError):
@@ -40,7 +43,7 @@ class LayerShape:
     r_pairs: int
     d_kv: int
     dtype: str = "bf16"  # "bf16" or "f32"
-    cache_fmt: str = "dense"  # "dense" or "int4_g32"
+    cache_fmt: str = "dense"  # "dense", "int4_g32" or "int2_g32_win"
 
     @property
     def torch_dtype(self):
@@ -54,7 +57,7 @@ class LayerShape:
             self.r_pairs,
             self.d_kv,
             MLA_BF16 if self.dtype == "bf16" else MLA_F32,
-            MLA_CACHE_INT4_G32 if self.cache_fmt == "int4_g32" else MLA_CACHE_DENSE,
+            _FMT[self.cache_fmt],
         )
 
 
@@ -121,7 +124,9 @@ def pack_weights(shape: LayerShape, conv: dict, rope_len: int, theta: float = 1e
 
 @dataclass
 class LatentCache:
-    """Latent cache for `batch` sequences of up to t_max tokens (layouts of mla_cache)."""
+    """Latent cache for `batch` sequences of up to t_max tokens (layouts of mla_cache).  For the
+    "int2_g32_win" format, ckv holds 2-bit codes, ckv_scale (s, z) pairs per group of 32, and ckv_window
+    the bf16 ring of each sequence's last `window` rows."""
 
     shape: LayerShape
     ckv: torch.Tensor
@@ -129,13 +134,22 @@ class LatentCache:
     krope: torch.Tensor
     batch: int
     t_max: int
+    ckv_window: Optional[torch.Tensor] = None
+    window: int = 0
 
     @staticmethod
-    def allocate(shape: LayerShape, batch: int, t_max: int, device="cuda", fill: Optional[float] = None):
+    def allocate(shape: LayerShape, batch: int, t_max: int, device="cuda", fill: Optional[float] = None,
+                 window: int = 128):
+        """`window` (int2_g32_win only) is the number of recent rows kept in bf16 per sequence."""
         nr = shape.n_heads * 2 * shape.r_pairs
+        ring = None
         if shape.cache_fmt == "int4_g32":
             ckv = torch.zeros((batch, t_max, shape.d_kv // 2), dtype=torch.uint8, device=device)
             scale = torch.zeros((batch, t_max, shape.d_kv // 32), dtype=torch.float16, device=device)
+        elif shape.cache_fmt == "int2_g32_win":
+            ckv = torch.zeros((batch, t_max, shape.d_kv // 4), dtype=torch.uint8, device=device)
+            scale = torch.zeros((batch, t_max, shape.d_kv // 32, 2), dtype=torch.float16, device=device)
+            ring = torch.empty((batch, max(window, 1), shape.d_kv), dtype=torch.bfloat16, device=device)
         else:
             ckv = torch.empty((batch, t_max, shape.d_kv), dtype=shape.torch_dtype, device=device)
             scale = None
@@ -143,13 +157,25 @@ class LatentCache:
         if fill is not None:
             if scale is None:
                 ckv.fill_(fill)
+            if ring is not None:
+                ring.fill_(fill)
             krope.fill_(fill)
-        return LatentCache(shape, ckv, scale, krope, batch, t_max)
+        return LatentCache(shape, ckv, scale, krope, batch, t_max, ring,
+                           window if shape.cache_fmt == "int2_g32_win" else 0)
+
+    def view(self, b0: int, b1: int) -> "LatentCache":
+        """The cache of sequences b0 .. b1-1 (views of the same memory)."""
+        sl = slice(b0, b1)
+        return LatentCache(self.shape, self.ckv[sl], None if self.ckv_scale is None else self.ckv_scale[sl],
+                           self.krope[sl], b1 - b0, self.t_max, None if self.ckv_window is None else self.ckv_window[sl],
+                           self.window)
 
     def c(self) -> MlaCache:
-        return MlaCache(_ptr(self.ckv), _ptr(self.ckv_scale), _ptr(self.krope), self.batch, self.t_max)
+        return MlaCache(_ptr(self.ckv), _ptr(self.ckv_scale), _ptr(self.krope), self.batch, self.t_max,
+                        _ptr(self.ckv_window), self.window)
 
     def nbytes_per_token(self) -> int:
+        """Bytes per cached position (the ring of an int2_g32_win cache is a fixed extra per sequence)."""
         n = self.ckv[0, 0].numel() * self.ckv.element_size() + self.krope[0, 0].numel() * self.krope.element_size()
         if self.ckv_scale is not None:
             n += self.ckv_scale[0, 0].numel() * 2
@@ -275,6 +301,18 @@ def quantize_int4(x: torch.Tensor, stream=None):
     scales = torch.empty(x.shape[:-1] + (x.shape[-1] // 32,), dtype=torch.float16, device=x.device)
     _check("mla_quantize_int4", lib.mla_quantize_int4(_ptr(x), n_groups, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
+
+
+def quantize_int2(x: torch.Tensor, stream=None):
+    """mla_quantize_int2 on fp32 x [..., 32*g] -> (codes uint8 [..., 8*g], meta float16 [..., g, 2] = (s, z))."""
+    lib = _lib.load()
+    if x.dtype != torch.float32:
+        raise ValueError("quantize_int2 takes fp32 input")
+    n_groups = x.numel() // 32
+    codes = torch.empty(x.shape[:-1] + (x.shape[-1] // 4,), dtype=torch.uint8, device=x.device)
+    meta = torch.empty(x.shape[:-1] + (x.shape[-1] // 32, 2), dtype=torch.float16, device=x.device)
+    _check("mla_quantize_int2", lib.mla_quantize_int2(_ptr(x), n_groups, _ptr(codes), _ptr(meta), _stream(stream)))
+    return codes, meta
 
 
 class BoundDecode:

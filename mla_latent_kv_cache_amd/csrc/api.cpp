@@ -18,9 +18,10 @@ int check_config(const mla_config* c) {
   if (c->d_model <= 0 || c->n_heads <= 0 || c->d_head <= 0 || c->d_kv <= 0) return MLA_ERR_INVALID_ARG;
   if (c->d_head % 2 != 0 || c->r_pairs < 0 || 2 * c->r_pairs > c->d_head) return MLA_ERR_INVALID_ARG;
   if (c->dtype != MLA_F32 && c->dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
-  if (c->cache_fmt != MLA_CACHE_DENSE && c->cache_fmt != MLA_CACHE_INT4_G32) return MLA_ERR_INVALID_ARG;
+  if (c->cache_fmt != MLA_CACHE_DENSE && c->cache_fmt != MLA_CACHE_INT4_G32 && c->cache_fmt != MLA_CACHE_INT2_G32_WIN)
+    return MLA_ERR_INVALID_ARG;
   if (c->d_head > 256) return MLA_ERR_UNSUPPORTED;
-  if (c->cache_fmt == MLA_CACHE_INT4_G32 && (c->dtype != MLA_BF16 || c->d_kv % 32 != 0)) return MLA_ERR_UNSUPPORTED;
+  if (c->cache_fmt != MLA_CACHE_DENSE && (c->dtype != MLA_BF16 || c->d_kv % 32 != 0)) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 
@@ -61,7 +62,11 @@ int check_cache(const mla_config* c, const mla_cache* k) {
   if (k->batch < 0 || k->t_max <= 0) return MLA_ERR_INVALID_ARG;
   MLA_TRY(check_ptr(k->ckv, true));
   MLA_TRY(check_ptr(k->krope, c->r_pairs > 0));
-  MLA_TRY(check_ptr(k->ckv_scale, c->cache_fmt == MLA_CACHE_INT4_G32));
+  MLA_TRY(check_ptr(k->ckv_scale, c->cache_fmt != MLA_CACHE_DENSE));
+  if (c->cache_fmt == MLA_CACHE_INT2_G32_WIN) {
+    if (k->window < 0) return MLA_ERR_INVALID_ARG;
+    MLA_TRY(check_ptr(k->ckv_window, k->window > 0));
+  }
   return MLA_OK;
 }
 
@@ -73,6 +78,14 @@ int check_positions(const mla_config* c, const mla_weights* w, const mla_cache* 
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+// The bf16 ring of the 2-bit format (nothing for the other formats).
+template <typename Args>
+void set_window(Args& a, const mla_config* c, const mla_cache* k) {
+  if (c->cache_fmt != MLA_CACHE_INT2_G32_WIN) return;
+  a.ckv_win = k->ckv_window;
+  a.win = k->window;
+}
 
 }  // namespace
 
@@ -117,6 +130,7 @@ static int append_impl(const mla_config* cfg, const mla_weights* w, mla_cache* c
   mla::AppendArgs a{s, x, w->w_dkv, w->w_krope, w->pair_idx, w->rope_cos, w->rope_sin,
                     start_pos, cache->batch, t_new, max_start_pos, cache->t_max,
                     cache->ckv, cache->ckv_scale, cache->krope, ws};
+  set_window(a, cfg, cache);
   return from_hip(mla::launch_append(a, stream));
 }
 
@@ -165,6 +179,7 @@ static int decode_impl(int phase_mask, const mla_config* cfg, const mla_weights*
   mla::DecodeArgs a{s, q, w->w_uk, w->w_uv, w->pair_idx, w->rope_cos, w->rope_sin,
                     cache->ckv, cache->ckv_scale, cache->krope, cache->batch, cache->t_max, max_seq_len,
                     seq_lens, out, (char*)workspace, plan};
+  set_window(a, cfg, cache);
   return from_hip(mla::launch_decode(a, stream, phase_mask));
 }
 
@@ -226,6 +241,8 @@ int mla_decode_step(const mla_config* cfg, const mla_weights* w, mla_cache* cach
   mla::DecodeArgs da{s, q, w->w_uk, w->w_uv, w->pair_idx, w->rope_cos, w->rope_sin,
                      cache->ckv, cache->ckv_scale, cache->krope, cache->batch, cache->t_max, max_seq_len,
                      seq_lens, out, wsd, plan};
+  set_window(aa, cfg, cache);
+  set_window(da, cfg, cache);
   if (t_new > 0 && mla::decode_step_fusable(aa, da)) return from_hip(mla::launch_decode_step(aa, da, stream));
   if (t_new > 0) MLA_TRY(from_hip(mla::launch_append(aa, stream)));
   return from_hip(mla::launch_decode(da, stream, 7));
@@ -263,6 +280,15 @@ int mla_quantize_int4(const float* in, int64_t n_groups, uint8_t* codes, uint16_
   if (!aligned16(in) || !aligned16(codes) || !aligned16(scales)) return MLA_ERR_ALIGNMENT;
   if (n_groups > ((int64_t)1 << 36)) return MLA_ERR_UNSUPPORTED;
   return from_hip(mla::launch_quantize_int4(in, n_groups, codes, scales, stream));
+}
+
+int mla_quantize_int2(const float* in, int64_t n_groups, uint8_t* codes, uint16_t* meta, hipStream_t stream) {
+  if (n_groups < 0) return MLA_ERR_INVALID_ARG;
+  if (n_groups == 0) return MLA_OK;
+  if (!in || !codes || !meta) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(in) || !aligned16(codes) || !aligned16(meta)) return MLA_ERR_ALIGNMENT;
+  if (n_groups > ((int64_t)1 << 36)) return MLA_ERR_UNSUPPORTED;
+  return from_hip(mla::launch_quantize_int2(in, n_groups, codes, meta, stream));
 }
 
 }  // extern "C"

@@ -41,6 +41,8 @@ __global__ __launch_bounds__(256) void append_generic(AppendArgs a) {
   if (a.s.fmt == 0) {
     T* ckv = (T*)a.ckv + row * D;
     for (int n = threadIdx.x; n < D; n += blockDim.x) ckv[n] = from_f32<T>(outs[n]);
+  } else if (a.s.fmt == 2) {
+    for (int g = threadIdx.x; g < D / 32; g += blockDim.x) store_group_win2(a, m / a.t_new, pos, g, outs + 32 * g, 1);
   } else {
     uint8_t* codes = (uint8_t*)a.ckv + row * (D / 2);
     __half* scales = (__half*)a.ckv_scale + row * (D / 32);
@@ -145,6 +147,34 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
 
   // ---- epilogue
   const int r = a.s.r_pairs, R2 = a.s.r2(), half = a.s.d_head / 2;
+  if (a.s.fmt == 2 && n0 < D) {
+    // 2-bit latent: the tile's latent columns go to LDS (token rows 0-63 in sA, 64-127 in sB, which the
+    // main loop no longer reads), then one thread per (token, group of 32 columns) codes or windows it
+    constexpr int SP = TN + 1;
+    float* stg0 = (float*)&sA[0][0];
+    float* stg1 = (float*)&sB[0][0];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int cl = wn * 64 + j * 32;
+        if (n0 + cl >= D) continue;  // uniform across the wave
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int ml = wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          (ml < 64 ? stg0 : stg1)[(ml & 63) * SP + cl + (lane & 31)] = acc[i][j][e];
+        }
+      }
+    __syncthreads();
+    const int ng = min(TN, D - n0) / 32;
+    for (int idx = threadIdx.x; idx < TM * ng; idx += blockDim.x) {
+      const int ml = idx / ng, g = idx - ml * ng, m = m0 + ml;
+      if (m >= M) continue;
+      int pos;
+      cache_row(a, m, &pos);
+      store_group_win2(a, m / a.t_new, pos, n0 / 32 + g, (ml < 64 ? stg0 : stg1) + (ml & 63) * SP + 32 * g, 1);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -163,6 +193,8 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
               ((bf16*)a.ckv)[row * D + n] = (bf16)acc[i][j][e];
             }
           }
+        } else if (a.s.fmt == 2) {
+          // staged through LDS below
         } else {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
@@ -226,6 +258,13 @@ __device__ __forceinline__ void append_gemm_block(const AppendArgs& a, const f32
       for (int e = 0; e < 16; ++e) {
         const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         if (m0 + ml < M) ((bf16*)a.ckv)[(size_t)rows[ml] * D + n] = (bf16)v[e];
+      }
+    } else if (a.s.fmt == 2) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const bool ok = m0 + ml < M;
+        store_lane_win2(a, ok, (m0 + ml) / a.t_new, ok ? poss[ml] : 0, n >> 5, v[e]);
       }
     } else {
 #pragma unroll
@@ -444,6 +483,17 @@ __global__ __launch_bounds__(256) void quantize_int4_kernel(const float* in, int
   scales[g] = __half_as_ushort(s);
 }
 
+// ------------------------------------------------------------------ standalone 2-bit quantiser
+__global__ __launch_bounds__(256) void quantize_int2_kernel(const float* in, int64_t n_groups, uint8_t* codes,
+                                                            uint16_t* meta) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= n_groups) return;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = in[g * 32 + i];
+  code_group2(v, codes + g * 8, (uint32_t*)meta + g);
+}
+
 }  // namespace
 
 bool append_uses_mfma(const Shape& s) {
@@ -503,6 +553,12 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
 hipError_t launch_quantize_int4(const float* in, int64_t n_groups, uint8_t* codes, uint16_t* scales, hipStream_t st) {
   int64_t blocks = (n_groups + 255) / 256;
   hipLaunchKernelGGL(quantize_int4_kernel, dim3((unsigned)blocks), dim3(256), 0, st, in, n_groups, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_int2(const float* in, int64_t n_groups, uint8_t* codes, uint16_t* meta, hipStream_t st) {
+  const int64_t blocks = (n_groups + 255) / 256;
+  hipLaunchKernelGGL(quantize_int2_kernel, dim3((unsigned)blocks), dim3(256), 0, st, in, n_groups, codes, meta);
   return hipGetLastError();
 }
 

@@ -46,6 +46,12 @@ __device__ __forceinline__ int wave_iscan(int v) {  // inclusive prefix sum over
   }
   return v;
 }
+// Items of a sequence of L tokens: its coded positions and its window of bf16 rows (fmt 2, a.win > 0) are
+// cut into chunks separately, so that an item reads one kind of row.
+__device__ __forceinline__ int item_count(const DecodeArgs& a, int L, int chunk) {
+  const int lw = min(L, a.win), lq = L - lw;
+  return (lq + chunk - 1) / chunk + (lw + chunk - 1) / chunk;
+}
 __device__ int work_chunk(const DecodeArgs& a) {
   int tot = 0;
   for (int i = threadIdx.x & 63; i < a.batch; i += 64) tot += clamp_len(a, i);
@@ -56,6 +62,7 @@ __device__ int work_chunk(const DecodeArgs& a) {
 }
 struct WorkItem {
   int b, t0, t1;  // sequence and token range [t0, t1), non-empty when found
+  int win;        // 1: the range lies in the sequence's window of bf16 rows (fmt 2)
 };
 // Item `item` of the split; false when the batch has fewer items.
 __device__ bool locate_item(const DecodeArgs& a, int item, WorkItem& wi) {
@@ -64,18 +71,21 @@ __device__ bool locate_item(const DecodeArgs& a, int item, WorkItem& wi) {
   for (int c0 = 0; c0 < a.batch; c0 += 64) {
     const int i = c0 + lane;
     const int L = i < a.batch ? clamp_len(a, i) : 0;
-    const int cnt = (L + chunk - 1) / chunk;
+    const int cnt = item_count(a, L, chunk);
     const int incl = wave_iscan(cnt);
     const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
     if (item < base + total) {
       const unsigned long long hit = __builtin_amdgcn_ballot_w64(base + incl > item);
       const int ln = (int)__builtin_ctzll(hit);
       const int first = base + __shfl(incl - cnt, ln, 64);
+      const int Lb = __shfl(L, ln, 64), lq = Lb - min(Lb, a.win), nq = (lq + chunk - 1) / chunk;
+      const int j = item - first;
       // the values are wave-uniform; readfirstlane lets the compiler keep them (and the addresses
       // derived from them) in scalar registers
       wi.b = __builtin_amdgcn_readfirstlane(c0 + ln);
-      wi.t0 = __builtin_amdgcn_readfirstlane((item - first) * chunk);
-      wi.t1 = __builtin_amdgcn_readfirstlane(min(wi.t0 + chunk, __shfl(L, ln, 64)));
+      wi.win = __builtin_amdgcn_readfirstlane(j >= nq ? 1 : 0);
+      wi.t0 = __builtin_amdgcn_readfirstlane(j < nq ? j * chunk : lq + (j - nq) * chunk);
+      wi.t1 = __builtin_amdgcn_readfirstlane(min(wi.t0 + chunk, j < nq ? lq : Lb));
       return true;
     }
     base += total;
@@ -86,9 +96,9 @@ __device__ bool locate_item(const DecodeArgs& a, int item, WorkItem& wi) {
 __device__ void sequence_items(const DecodeArgs& a, int b, int& first, int& count) {
   const int chunk = work_chunk(a), lane = threadIdx.x & 63;
   int before = 0;
-  for (int i = lane; i < b; i += 64) before += (clamp_len(a, i) + chunk - 1) / chunk;
+  for (int i = lane; i < b; i += 64) before += item_count(a, clamp_len(a, i), chunk);
   first = __builtin_amdgcn_readfirstlane(wave_isum(before));
-  count = (clamp_len(a, b) + chunk - 1) / chunk;
+  count = item_count(a, clamp_len(a, b), chunk);
 }
 
 // Rows of a fused split-K append (FuseArgs) at positions [t0, t1) of sequence b, written by the calling
@@ -286,6 +296,19 @@ __global__ __launch_bounds__(256) void decode_step_prologue(AppendArgs aa, int k
 }
 
 // ------------------------------------------------------------------ latent element access
+// Element k of the latent of position pos of sequence b in the 2-bit format: a bf16 ring row inside the
+// window, else fp32(z + code * s) of the coded row.
+__device__ __forceinline__ float latent2(const DecodeArgs& a, int b, int pos, bool win, int k) {
+  const int D = a.s.d_kv;
+  if (win) return (float)((const bf16*)a.ckv_win)[((size_t)b * a.win + pos % a.win) * D + k];
+  const size_t row = (size_t)b * a.t_max + pos;
+  const uint32_t byte = ((const uint8_t*)a.ckv)[row * (D / 4) + (k >> 2)];
+  const uint32_t m = ((const uint32_t*)a.ckv_scale)[row * (D / 32) + (k >> 5)];
+  const float sc = __half2float(__ushort_as_half((unsigned short)(m & 0xFFFF)));
+  const float z = __half2float(__ushort_as_half((unsigned short)(m >> 16)));
+  return fmaf((float)((byte >> (2 * (k & 3))) & 3u), sc, z);
+}
+
 template <typename T, int FMT>
 __device__ __forceinline__ float latent(const DecodeArgs& a, size_t row, int k) {
   const int D = a.s.d_kv;
@@ -323,6 +346,10 @@ __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
   const T* qt = (const T*)(a.ws + a.plan.off_qt) + (size_t)b * NH * D;
   const float* qr = (const float*)(a.ws + a.plan.off_qr) + (size_t)b * NH * R2;
   const size_t row0 = (size_t)b * a.t_max + t0;
+  auto lat = [&](int t, int k) {
+    if constexpr (FMT == 2) return latent2(a, b, t0 + t, wi.win != 0, k);
+    else return latent<T, FMT>(a, row0 + t, k);
+  };
   for (int h = 0; h < NH; ++h) {
     if (n <= 0) {
       for (int k = threadIdx.x; k < D; k += blockDim.x) po[(size_t)h * D + k] = 0.f;
@@ -338,7 +365,7 @@ __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
     float mloc = -INFINITY;
     for (int t = threadIdx.x; t < n; t += blockDim.x) {
       float s = 0.f;
-      for (int k = 0; k < D; ++k) s = fmaf(qs[k], latent<T, FMT>(a, row0 + t, k), s);
+      for (int k = 0; k < D; ++k) s = fmaf(qs[k], lat(t, k), s);
       const T* kr = (const T*)a.krope + ((row0 + t) * NH + h) * R2;
       for (int j = 0; j < R2; ++j) s = fmaf(qrs[j], to_f32(kr[j]), s);
       sc[t] = s;
@@ -355,7 +382,7 @@ __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
     __syncthreads();
     for (int k = threadIdx.x; k < D; k += blockDim.x) {
       float o = 0.f;
-      for (int t = 0; t < n; ++t) o = fmaf(sc[t], latent<T, FMT>(a, row0 + t, k), o);
+      for (int t = 0; t < n; ++t) o = fmaf(sc[t], lat(t, k), o);
       po[(size_t)h * D + k] = o;
     }
     if (threadIdx.x == 0) {
@@ -450,6 +477,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   WorkItem wi;
   if (!locate_item(a, blockIdx.x, wi)) return;
   const int b = wi.b, t0 = wi.t0, t1 = wi.t1;
+  const bool wwin = FMT == 2 && wi.win;  // rows from the window ring (bf16), not the code store
   if (fused_rows(f, b, t0, t1, (float*)cbuf)) MLA_WAIT_VMCNT(0);
 
   // latent query operands (B of the score product) and the rotated query pairs
@@ -474,47 +502,55 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   bf16* cw = cbuf[w];
 
   // ---- register prefetch, two tiles deep: this wave's latent slice and its share of the RoPE keys
-  constexpr int CPR = (FMT == 0) ? DW / 8 : DW / 32;  // 16-byte chunks per row
+  // 16-byte chunks per row of the wave's slice: 8 bf16, 32 int4 or 64 2-bit latents each
+  constexpr int CPR = (FMT == 0) ? DW / 8 : (FMT == 1 ? DW / 32 : DW / 64);
   constexpr int CCH = 32 * CPR / 64;                  // chunks per lane
   typedef bf16 kv_t __attribute__((ext_vector_type(R2)));
+  // per chunk: one fp16 scale (int4) or two (s, z) pairs of fp16 (2-bit: two groups of 32)
+  using meta_t = std::conditional_t<FMT == 2, uint2, uint16_t>;
   u32x4 creg[2][CCH];
-  uint16_t sreg[2][CCH];
+  meta_t sreg[2][CCH];
   kv_t kreg[2][4];
 
   // full tiles: a wave-uniform tile base plus per-lane offsets that do not change per tile
-  constexpr int RBY = FMT == 0 ? D * 2 : D / 2;  // latent bytes per cache row
+  constexpr int RBY = FMT == 0 ? D * 2 : (FMT == 1 ? D / 2 : D / 4);  // latent bytes per cache row
+  constexpr int MBY = FMT == 2 ? 4 : 2;                                // metadata bytes per group
   uint32_t coff[CCH], soff[CCH];
 #pragma unroll
   for (int it = 0; it < CCH; ++it) {
     const int c = it * 64 + lane, row = c / CPR, q = c - row * CPR;
-    coff[it] = row * RBY + (FMT == 0 ? 2 * (w * DW + 8 * q) : (w * DW + 32 * q) / 2);
-    soff[it] = 2 * (row * (D / 32) + (w * DW) / 32 + q);
+    coff[it] = row * RBY + (FMT == 0 ? 2 * (w * DW + 8 * q) : (FMT == 1 ? (w * DW + 32 * q) / 2 : (w * DW + 64 * q) / 4));
+    soff[it] = MBY * (row * (D / 32) + (w * DW) / 32 + (FMT == 2 ? 2 * q : q));
   }
   const uint32_t koff = (((8 * w + 4 * hb) * 32 + h) * R2) * 2;
+  // window items (2-bit format) stage their bf16 rows straight from the ring in stage_window and
+  // prefetch only the RoPE keys here
   auto load_tile = [&](auto bsel, int tt) {
     constexpr int B = decltype(bsel)::value;
     if (tt + 32 <= t1) {
       const char* cb = (const char*)a.ckv + (rowb + tt) * RBY;
-      const char* sb = (const char*)a.ckv_scale + (rowb + tt) * (D / 32) * 2;
+      const char* sb = (const char*)a.ckv_scale + (rowb + tt) * (D / 32) * MBY;
       const char* kb = (const char*)krb + (size_t)tt * 32 * R2 * 2 + koff;
+      if (!wwin) {
 #pragma unroll
-      for (int it = 0; it < CCH; ++it) {
-        creg[B][it] = *(const u32x4*)(cb + coff[it]);
-        if (FMT == 1) sreg[B][it] = *(const uint16_t*)(sb + soff[it]);
+        for (int it = 0; it < CCH; ++it) {
+          creg[B][it] = *(const u32x4*)(cb + coff[it]);
+          if constexpr (FMT != 0) sreg[B][it] = *(const meta_t*)(sb + soff[it]);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) kreg[B][i] = *(const kv_t*)(kb + i * 32 * R2 * 2);
       return;
     }
+    if (!wwin) {
 #pragma unroll
-    for (int it = 0; it < CCH; ++it) {
-      int c = it * 64 + lane, row = c / CPR, q = c - row * CPR;
-      int tok = min(tt + row, t1 - 1);  // rows past the sequence repeat its last row (masked below)
-      if (FMT == 0) {
-        creg[B][it] = *(const u32x4*)((const bf16*)a.ckv + (rowb + tok) * D + w * DW + 8 * q);
-      } else {
-        creg[B][it] = *(const u32x4*)((const uint8_t*)a.ckv + (rowb + tok) * (D / 2) + (w * DW + 32 * q) / 2);
-        sreg[B][it] = ((const uint16_t*)a.ckv_scale)[(rowb + tok) * (D / 32) + (w * DW) / 32 + q];
+      for (int it = 0; it < CCH; ++it) {
+        const int row = (it * 64 + lane) / CPR;
+        const int tok = min(tt + row, t1 - 1);  // rows past the sequence repeat its last row (masked below)
+        const char* cb = (const char*)a.ckv + (rowb + tok) * RBY;
+        const char* sb = (const char*)a.ckv_scale + (rowb + tok) * (D / 32) * MBY;
+        creg[B][it] = *(const u32x4*)(cb + coff[it] - row * RBY);
+        if constexpr (FMT != 0) sreg[B][it] = *(const meta_t*)(sb + soff[it] - MBY * row * (D / 32));
       }
     }
 #pragma unroll
@@ -528,8 +564,27 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
 #pragma unroll
     for (int it = 0; it < CCH; ++it) {
       int c = it * 64 + lane, row = c / CPR, q = c - row * CPR;
-      if (FMT == 0) {
+      if constexpr (FMT == 0) {
         *(u32x4*)&cw[row * CP + 8 * q] = creg[B][it];
+      } else if constexpr (FMT == 2) {
+        const uint32_t wd[4] = {creg[B][it].x, creg[B][it].y, creg[B][it].z, creg[B][it].w};
+        const uint32_t mg[2] = {sreg[B][it].x, sreg[B][it].y};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {  // word u: latents 16u .. 16u+15 of the chunk, group u / 2
+          const float sc = __half2float(__ushort_as_half((unsigned short)(mg[u >> 1] & 0xFFFF)));
+          const float z = __half2float(__ushort_as_half((unsigned short)(mg[u >> 1] >> 16)));
+#pragma unroll
+          for (int hlf = 0; hlf < 2; ++hlf) {
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              // the 2-bit code as an fp32 bit pattern 2^23 + code, minus 2^23: the code exactly
+              const float code = __uint_as_float(((wd[u] >> (2 * (8 * hlf + e))) & 3u) | 0x4B000000u) - 8388608.0f;
+              v[e] = (bf16)fmaf(code, sc, z);
+            }
+            *(bf16x8*)&cw[row * CP + 64 * q + 16 * u + 8 * hlf] = v;
+          }
+        }
       } else {
         float s = __half2float(__ushort_as_half(sreg[B][it]));
         const uint32_t wd[4] = {creg[B][it].x, creg[B][it].y, creg[B][it].z, creg[B][it].w};
@@ -549,11 +604,30 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
     }
   };
 
+  // a tile of window rows: this wave's slice of rows tt .. tt+31 from the ring, global -> LDS
+  auto stage_window = [&](int tt) {
+    constexpr int WCPR = DW / 8, WCH = 32 * WCPR / 64;  // 16-byte chunks per row slice, per lane
+    const bf16* ring = (const bf16*)a.ckv_win + (size_t)b * a.win * D + w * DW;
+    u32x4 tmp[WCH];
+#pragma unroll
+    for (int it = 0; it < WCH; ++it) {
+      const int c = it * 64 + lane, row = c / WCPR, q = c - row * WCPR;
+      const int tok = min(tt + row, t1 - 1);  // rows past the range repeat its last row (masked below)
+      tmp[it] = *(const u32x4*)(ring + (size_t)(tok % a.win) * D + 8 * q);
+    }
+#pragma unroll
+    for (int it = 0; it < WCH; ++it) {
+      const int c = it * 64 + lane, row = c / WCPR, q = c - row * WCPR;
+      *(u32x4*)&cw[row * CP + 8 * q] = tmp[it];
+    }
+  };
+
   int par = 0;
   // one 32-token tile: stage registers -> LDS, refill them with the tile two ahead, then both products
   auto step = [&](auto bsel, int tt) {
     constexpr int B = decltype(bsel)::value;
-    stage_tile(bsel);
+    if (wwin) stage_window(tt);
+    else stage_tile(bsel);
     // RoPE term of rows 8w + 4hb + i (result elements 4w + i), taken before the registers refill
     float rt[4];
 #pragma unroll
@@ -1673,16 +1747,20 @@ void launch_generic_attn(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.plan.max_items);
   if (a.s.fmt == 0)
     hipLaunchKernelGGL((decode_attn_generic<T, 0>), grid, dim3(256), shmem, st, a);
-  else
+  else if (a.s.fmt == 1)
     hipLaunchKernelGGL((decode_attn_generic<T, 1>), grid, dim3(256), shmem, st, a);
+  else
+    hipLaunchKernelGGL((decode_attn_generic<T, 2>), grid, dim3(256), shmem, st, a);
 }
 
 template <int DW, int R2>
 void launch_mfma_attn(const DecodeArgs& a, const FuseArgs& f, hipStream_t st) {
   if (a.s.fmt == 0)
     hipLaunchKernelGGL((decode_attn_dma<DW, R2, 3, (DW == 128 && R2 == 8) ? 1 : 2>), attn_grid(a, f), dim3(256), 0, st, a, f);
-  else
+  else if (a.s.fmt == 1)
     hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 1>), attn_grid(a, f), dim3(256), 0, st, a, f);
+  else
+    hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 2>), attn_grid(a, f), dim3(256), 0, st, a, f);
 }
 
 }  // namespace
@@ -1690,16 +1768,19 @@ void launch_mfma_attn(const DecodeArgs& a, const FuseArgs& f, hipStream_t st) {
 // Latent width 256 (bf16 or int4).  At width 512 the register-staged kernel is as fast for int4 (its
 // dequantisation runs on two workgroups per CU) and the DMA ring kernel faster for bf16.
 bool decode_uses_wave(const Shape& s) {
-  return s.dtype == 1 && s.n_heads == 32 && (s.r_pairs == 2 || s.r_pairs == 4) && s.d_kv == 256;
+  return s.dtype == 1 && s.fmt <= 1 && s.n_heads == 32 && (s.r_pairs == 2 || s.r_pairs == 4) && s.d_kv == 256;
 }
 
 // Specialised attention kernels that run the second phase of a split-K append (see FuseArgs).
 static bool attn_takes_append(const Shape& s) {
-  return decode_uses_wave(s) || (decode_uses_mfma(s) && (s.fmt == 1 || s.d_kv == 512));
+  return s.fmt <= 1 && (decode_uses_wave(s) || (decode_uses_mfma(s) && (s.fmt == 1 || s.d_kv == 512)));
 }
 
+// (at latent width 256 the dense and int4 formats take the per-wave kernel; the 2-bit format runs the
+// register-staged kernel at width 512 only)
 bool decode_uses_mfma(const Shape& s) {
-  return s.dtype == 1 && s.n_heads == 32 && (s.d_kv == 256 || s.d_kv == 512) && (s.r_pairs == 2 || s.r_pairs == 4);
+  return s.dtype == 1 && s.n_heads == 32 && (s.d_kv == 512 || (s.d_kv == 256 && s.fmt <= 1)) &&
+         (s.r_pairs == 2 || s.r_pairs == 4);
 }
 
 bool decode_uses_combine(const Shape& s) {
@@ -1725,11 +1806,12 @@ DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len) {
     const long long c = room > 0 ? (room / 64) * 64 : 64;
     if (c < p.cmax) p.cmax = (int)(c < 64 ? 64 : c);
   }
-  // items = sum_b ceil(L_b / chunk) < sum_b L_b / chunk + batch; chunk >= sum / target unless clamped
-  const long long B = batch, Lm = max_seq_len;
-  long long by_min = B * ((Lm + 63) / 64);                          // chunk = 64
+  // items = sum_b ceil(L_b / chunk) < sum_b L_b / chunk + batch; chunk >= sum / target unless clamped.
+  // A window of bf16 rows (fmt 2) is cut separately from the coded rows: at most one more item each.
+  const long long B = batch, Lm = max_seq_len, extra = s.fmt == 2 ? B : 0;
+  long long by_min = B * ((Lm + 63) / 64) + extra;                  // chunk = 64
   long long by_max = (B * Lm + p.cmax - 1) / p.cmax;                // chunk = cmax
-  long long bound = (by_max > p.target ? by_max : p.target) + B;
+  long long bound = (by_max > p.target ? by_max : p.target) + B + extra;
   long long items = by_min < bound ? by_min : bound;
   p.max_items = (int)(items < 1 ? 1 : items);
   const size_t esz = s.dtype == 0 ? 4 : 2;

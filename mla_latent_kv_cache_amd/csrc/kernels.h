@@ -11,7 +11,7 @@ namespace mla {
 struct Shape {
   int d_model, n_heads, d_head, r_pairs, d_kv;
   int dtype;  // 0 f32, 1 bf16
-  int fmt;    // 0 dense, 1 int4 g32
+  int fmt;    // 0 dense, 1 int4 g32, 2 int2 g32 with a bf16 window of recent rows
   __host__ __device__ int r2() const { return 2 * r_pairs; }
   __host__ __device__ int d_nope() const { return d_head - 2 * r_pairs; }
   __host__ __device__ int n_rope_cols() const { return n_heads * 2 * r_pairs; }
@@ -26,6 +26,8 @@ struct AppendArgs {
   int batch, t_new, max_start, t_max;
   void *ckv, *ckv_scale, *krope;
   char* ws = nullptr;  // optional workspace (few-token appends split the model width over workgroups)
+  void* ckv_win = nullptr;  // fmt 2: ring of the last `win` rows per sequence [batch, win, d_kv] bf16
+  int win = 0;
 };
 
 // Few-token append with a workspace: number of model-width slices and the workspace it needs
@@ -35,7 +37,9 @@ size_t append_workspace_bytes(const Shape& s, int tokens);
 
 // Decode work split.  The kernels read the batch's lengths L_b on the device and cut its tokens into
 // work items of `chunk` tokens: chunk = clamp(round_up(ceil(sum_b L_b / target), 64), 64, cmax), and
-// sequence b owns ceil(L_b / chunk) consecutive items (in batch order).  Ragged batches therefore
+// sequence b owns ceil(L_b / chunk) consecutive items (in batch order).  With a window of bf16 rows
+// (fmt 2) the coded positions [0, L_b - W_b) and the window [L_b - W_b, L_b), W_b = min(L_b, win), are
+// cut separately: ceil((L_b - W_b) / chunk) + ceil(W_b / chunk) items.  Ragged batches therefore
 // spread over about `target` workgroups like uniform ones.  max_items bounds the item count for any
 // lengths within max_seq_len; the per-item partial results are laid out by item.
 struct DecodePlan {
@@ -58,6 +62,8 @@ struct DecodeArgs {
   void* out;
   char* ws;
   DecodePlan plan;
+  const void* ckv_win = nullptr;  // fmt 2: ring of the last `win` rows per sequence [batch, win, d_kv] bf16
+  int win = 0;
 };
 
 // Prefill workspace: K [b, h, s_pad, 128] and V^T [b, h, 128, s_pad] bf16, s_pad = seq_len rounded up
@@ -97,6 +103,7 @@ hipError_t launch_append_reduce(const AppendArgs& a, int ks, hipStream_t st);
 bool decode_step_fusable(const AppendArgs& aa, const DecodeArgs& da);
 hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, hipStream_t st);
 hipError_t launch_quantize_int4(const float* in, int64_t n_groups, uint8_t* codes, uint16_t* scales, hipStream_t st);
+hipError_t launch_quantize_int2(const float* in, int64_t n_groups, uint8_t* codes, uint16_t* meta, hipStream_t st);
 
 // Shape predicates for the specialised paths (host side, used for dispatch and tests).
 bool append_uses_mfma(const Shape& s);

@@ -42,6 +42,121 @@ __device__ __forceinline__ void store_group(const AppendArgs& a, size_t row, int
   }
   ((__half*)a.ckv_scale)[row * (D / 32) + g] = s;
 }
+// ---- 2-bit latent with a window of recent bf16 rows (fmt 2)
+// Group of 32 latent values of one token (already rounded to bf16): z = fp16(min), s = fp16(max(max - z,
+// 0) / 3), both saturating at the largest finite fp16; code = clamp(rint((x - z) / s), 0, 3) with an fp32
+// subtraction and an IEEE fp32 division (s == 0: code 0).  Row `row` of the code store holds 8 bytes per
+// group (element 4i + j at bits 2j of byte i) and one (s, z) pair of fp16 per group.
+__device__ __forceinline__ __half sat_half(float v) {
+  __half h = __float2half_rn(v);
+  if (__hisinf(h)) h = __ushort_as_half((unsigned short)(v > 0.f ? 0x7BFF : 0xFBFF));
+  return h;
+}
+__device__ __forceinline__ int int2_code(float x, float z, float s) {
+  if (s == 0.f) return 0;
+  const float q = rintf(__fdiv_rn(x - z, s));
+  return (int)fminf(fmaxf(q, 0.f), 3.f);
+}
+__device__ __forceinline__ void code_group2(const float* v, uint8_t* codes, uint32_t* meta) {
+  float lo = v[0], hi = v[0];
+  for (int c = 1; c < 32; ++c) {
+    lo = fminf(lo, v[c]);
+    hi = fmaxf(hi, v[c]);
+  }
+  const __half zh = sat_half(lo);
+  const float z = __half2float(zh);
+  const __half sh = sat_half(__fdiv_rn(fmaxf(hi - z, 0.f), 3.0f));
+  const float sc = __half2float(sh);
+  for (int i = 0; i < 8; ++i) {
+    int byte = 0;
+    for (int j = 0; j < 4; ++j) byte |= int2_code(v[4 * i + j], z, sc) << (2 * j);
+    codes[i] = (uint8_t)byte;
+  }
+  *meta = (uint32_t)__half_as_ushort(sh) | ((uint32_t)__half_as_ushort(zh) << 16);
+}
+__device__ __forceinline__ void store_group2(const AppendArgs& a, size_t row, int g, const float* v) {
+  const int D = a.s.d_kv;
+  code_group2(v, (uint8_t*)a.ckv + row * (D / 4) + 8 * g, (uint32_t*)a.ckv_scale + row * (D / 32) + g);
+}
+// Position that ring slot `slot` holds before an append that starts at position sp: the one in
+// [sp - W, sp) congruent to slot modulo W (negative: the slot has not been used yet).
+__device__ __forceinline__ int ring_occupant(int sp, int W, int slot) {
+  const int base = sp - W;
+  return base + (((slot - base) % W) + W) % W;
+}
+__device__ __forceinline__ int clamped_start(const AppendArgs& a, int b) {
+  const int sp = a.start_pos[b];
+  return sp < 0 ? 0 : (sp > a.max_start ? a.max_start : sp);
+}
+// Latent group g of the new token at position pos of sequence b, fp32 projections v(c) = vals[c * stride].
+// The append ends at end = start + t_new.  A token at pos < end - W is coded at once; any other goes to
+// ring slot pos % W, whose previous occupant (a position that leaves the window now) is coded first.
+// Each (token, group) is handled by exactly one caller, and only it reads or writes that ring slot's
+// group, so the read-before-write order needs no synchronisation.
+__device__ __forceinline__ void store_group_win2(const AppendArgs& a, int b, int pos, int g, const float* vals,
+                                                 int stride) {
+  const int D = a.s.d_kv, W = a.win;
+  const int sp = clamped_start(a, b);
+  float v[32];
+  for (int c = 0; c < 32; ++c) v[c] = (float)(bf16)vals[c * stride];
+  if (pos < sp + a.t_new - W) {
+    store_group2(a, (size_t)b * a.t_max + pos, g, v);
+    return;
+  }
+  const int slot = pos % W;
+  bf16* ring = (bf16*)a.ckv_win + ((size_t)b * W + slot) * D + 32 * g;
+  const int p_old = ring_occupant(sp, W, slot);
+  if (p_old >= 0) {
+    float o[32];
+    for (int c = 0; c < 32; ++c) o[c] = (float)ring[c];
+    store_group2(a, (size_t)b * a.t_max + p_old, g, o);
+  }
+  for (int c = 0; c < 32; ++c) ring[c] = (bf16)v[c];
+}
+// The same for accumulator layouts in which the 32 lanes of each half-wave hold the 32 columns of one
+// group of one token (column = lane % 32); `ok` is false for lanes past the last token.  Called by all 64
+// lanes (the group reductions and the code packing are shuffles within each half).
+__device__ __forceinline__ void store_lane_win2(const AppendArgs& a, bool ok, int b, int pos, int g, float val) {
+  const int c = threadIdx.x & 31, D = a.s.d_kv, W = a.win;
+  const float vb = (float)(bf16)val;
+  bool direct = false, evict = false;
+  int p_old = 0;
+  float x = vb;
+  bf16* ring = nullptr;
+  if (ok) {
+    const int sp = clamped_start(a, b);
+    direct = pos < sp + a.t_new - W;
+    if (!direct) {
+      const int slot = pos % W;
+      ring = (bf16*)a.ckv_win + ((size_t)b * W + slot) * D + 32 * g;
+      p_old = ring_occupant(sp, W, slot);
+      evict = p_old >= 0;
+      if (evict) x = (float)ring[c];
+    }
+  }
+  float lo = x, hi = x;
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) {
+    lo = fminf(lo, shfl_xor(lo, m));
+    hi = fmaxf(hi, shfl_xor(hi, m));
+  }
+  const __half zh = sat_half(lo);
+  const float z = __half2float(zh);
+  const __half sh = sat_half(__fdiv_rn(fmaxf(hi - z, 0.f), 3.0f));
+  const float sc = __half2float(sh);
+  const int code = int2_code(x, z, sc);
+  const int c1 = __shfl_xor(code, 1, 64), c2 = __shfl_xor(code, 2, 64), c3 = __shfl_xor(code, 3, 64);
+  if (direct || evict) {
+    const size_t row = (size_t)b * a.t_max + (direct ? pos : p_old);
+    if ((c & 3) == 0)
+      ((uint8_t*)a.ckv)[row * (D / 4) + 8 * g + (c >> 2)] = (uint8_t)(code | (c1 << 2) | (c2 << 4) | (c3 << 6));
+    if (c == 0)
+      ((uint32_t*)a.ckv_scale)[row * (D / 32) + g] =
+          (uint32_t)__half_as_ushort(sh) | ((uint32_t)__half_as_ushort(zh) << 16);
+  }
+  if (ok && !direct) ring[c] = (bf16)vb;
+}
+
 // Retained RoPE pair at offset rel (even) of a row's RoPE block: rotate (x0, x1) at position pos.
 __device__ __forceinline__ void store_rope_pair(const AppendArgs& a, size_t row, int pos, int rel, float x0, float x1) {
   const int r = a.s.r_pairs, R2 = a.s.r2(), NR = a.s.n_rope_cols(), half = a.s.d_head / 2;
@@ -64,8 +179,10 @@ __device__ __forceinline__ void append_epilogue(const AppendArgs& a, const float
         int m = idx >> 5, c = idx & 31;
         store_latent(a, (size_t)rows[m], n0 + c, fin[m * ld + c]);
       }
-    } else {
+    } else if (a.s.fmt == 1) {
       for (int m = threadIdx.x; m < M; m += blockDim.x) store_group(a, (size_t)rows[m], n0 / 32, fin + m * ld, 1);
+    } else {
+      for (int m = threadIdx.x; m < M; m += blockDim.x) store_group_win2(a, m / a.t_new, poss[m], n0 / 32, fin + m * ld, 1);
     }
   } else {
     for (int idx = threadIdx.x; idx < M * 16; idx += blockDim.x) {
@@ -79,7 +196,8 @@ __device__ __forceinline__ void append_epilogue(const AppendArgs& a, const float
 
 // Split-K append, phase 2 for the tokens of sequence b at cache positions [p_lo, p_hi) (at most
 // FUSE_MAXR, all of them new tokens of this append): each output column's KS partial sums are added in
-// the order append_reduce uses, then the epilogue writes the cache rows, all columns at once.  `lds`
+// the order append_reduce uses, then the epilogue writes the cache rows, all columns at once.  Dense and
+// int4 latents only (the 2-bit format's append is never fused into the attention launch).  `lds`
 // holds FUSE_MAXR * (N + 4) floats plus 2 * FUSE_MAXR ints.  Called by every thread of the workgroup.
 // The stores are not waited for: the caller waits for vmcnt 0 before any load that reads the rows.
 constexpr int FUSE_MAXR = 8;

@@ -89,8 +89,7 @@ def fill_cache_per_sequence(cfg, layer, w, cache, lens, keep_x=()):
         if b in keep_x:
             kept[b] = x
         xt = torch.from_numpy(x.astype(np.float32)).to("cuda").to(torch_dtype(cfg)).reshape(1, L, cfg.d_model)
-        view = LatentCache(cache.shape, cache.ckv[b:b + 1], None if cache.ckv_scale is None else cache.ckv_scale[b:b + 1],
-                           cache.krope[b:b + 1], 1, cache.t_max)
+        view = cache.view(b, b + 1)
         append(w, view, xt, zero, 0)
         del xt
         if b % 8 == 7:

@@ -50,7 +50,7 @@ def weights(**kw):
 
 
 def cache(**kw):
-    base = dict(ckv=FAKE, ckv_scale=FAKE, krope=FAKE, batch=32, t_max=4096)
+    base = dict(ckv=FAKE, ckv_scale=FAKE, krope=FAKE, batch=32, t_max=4096, ckv_window=FAKE, window=128)
     base.update(kw)
     return MlaCache(**base)
 
@@ -88,6 +88,9 @@ def test_workspace_sizes(lib):
         (dict(d_head=512, r_pairs=4), UNSUPPORTED),
         (dict(cache_fmt=1, dtype=0), UNSUPPORTED),
         (dict(cache_fmt=1, d_kv=48), UNSUPPORTED),
+        (dict(cache_fmt=2, dtype=0), UNSUPPORTED),
+        (dict(cache_fmt=2, d_kv=48), UNSUPPORTED),
+        (dict(cache_fmt=3), INVALID),
     ],
 )
 def test_decode_rejects_bad_config(lib, kw, expected):
@@ -116,6 +119,15 @@ def test_decode_rejects_bad_pointers_and_sizes(lib):
     # int4 cache needs its scale buffer
     c4 = cfg(cache_fmt=1)
     assert decode_call(lib, c=c4, k=cache(ckv_scale=None), ws_bytes=1 << 40) == INVALID
+    # the 2-bit cache needs its (s, z) buffer, a window >= 0 and, for a window > 0, the bf16 ring
+    c2 = cfg(cache_fmt=2)
+    assert decode_call(lib, c=c2, k=cache(ckv_scale=None), ws_bytes=1 << 40) == INVALID
+    assert decode_call(lib, c=c2, k=cache(window=-1), ws_bytes=1 << 40) == INVALID
+    assert decode_call(lib, c=c2, k=cache(ckv_window=None), ws_bytes=1 << 40) == INVALID
+    assert decode_call(lib, c=c2, k=cache(ckv_window=FAKE + 2), ws_bytes=1 << 40) == ALIGN
+    assert decode_call(lib, c=c2, k=cache(ckv_window=None, window=0), q=None, ws_bytes=1 << 40) == INVALID  # fails on q
+    # the ring is not read for the other formats
+    assert decode_call(lib, k=cache(ckv_window=None, window=-1), q=None) == INVALID  # fails on q
     # zero batch is a no-op
     assert decode_call(lib, k=cache(batch=0), q=None, lens=None, out=None) == OK
 
@@ -193,6 +205,7 @@ def test_prefill_checks(lib):
 
     assert call(c=cfg(dtype=0)) == UNSUPPORTED
     assert call(c=cfg(cache_fmt=1)) == UNSUPPORTED
+    assert call(c=cfg(cache_fmt=2)) == UNSUPPORTED
     assert call(s=-1) == INVALID
 
 
@@ -201,6 +214,17 @@ def test_quantize_checks(lib):
     assert lib.mla_quantize_int4(None, 4, FAKE, FAKE, None) == INVALID
     assert lib.mla_quantize_int4(FAKE, 4, FAKE + 1, FAKE, None) == ALIGN
     assert lib.mla_quantize_int4(None, 0, None, None, None) == OK
+    assert lib.mla_quantize_int2(FAKE, -1, FAKE, FAKE, None) == INVALID
+    assert lib.mla_quantize_int2(FAKE, 4, None, FAKE, None) == INVALID
+    assert lib.mla_quantize_int2(FAKE, 4, FAKE, FAKE + 2, None) == ALIGN
+    assert lib.mla_quantize_int2(None, 0, None, None, None) == OK
+
+
+def test_window_format_workspace(lib):
+    """The 2-bit format cuts each sequence's window into its own work items: at most one more per sequence."""
+    n1 = lib.mla_decode_workspace_bytes(ctypes.byref(cfg(cache_fmt=1)), 64, 8192)
+    n2 = lib.mla_decode_workspace_bytes(ctypes.byref(cfg(cache_fmt=2)), 64, 8192)
+    assert n2 > n1
 
 
 def test_status_strings(lib):

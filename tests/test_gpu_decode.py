@@ -234,8 +234,7 @@ def test_step_append_batched_positions(variant, use_ws):
     zero = torch.zeros(1, dtype=torch.int32, device="cuda")
     for b, L in enumerate(lens):
         xt = torch.from_numpy(xs[b][: L - 1].astype(np.float32)).cuda().to(torch_dtype(cfg)).reshape(1, L - 1, -1)
-        view = LatentCache(shape, cache.ckv[b:b + 1], None if cache.ckv_scale is None else cache.ckv_scale[b:b + 1],
-                           cache.krope[b:b + 1], 1, t_max)
+        view = cache.view(b, b + 1)
         append(w, view, xt, zero, 0)
     x_new = np.stack([x[-1] for x in xs])[:, None, :]
     start = torch.tensor([L - 1 for L in lens], dtype=torch.int32, device="cuda")
@@ -281,8 +280,7 @@ def test_decode_step_matches_separate_calls(variant):
     for cache in caches:
         for b, L in enumerate(lens):
             xt = torch.from_numpy(xs[b][: L - 1].astype(np.float32)).cuda().to(torch_dtype(cfg)).reshape(1, L - 1, -1)
-            view = LatentCache(shape, cache.ckv[b:b + 1], None if cache.ckv_scale is None else cache.ckv_scale[b:b + 1],
-                               cache.krope[b:b + 1], 1, t_max)
+            view = cache.view(b, b + 1)
             append(w, view, xt, zero, 0)
     x_new = torch.from_numpy(np.stack([x[-1] for x in xs])[:, None, :].astype(np.float32)).cuda().to(torch_dtype(cfg))
     start = torch.tensor([L - 1 for L in lens], dtype=torch.int32, device="cuda")
@@ -344,8 +342,7 @@ def test_decode_step_fused_rows(variant):
             if c == 0:
                 continue
             xt = torch.from_numpy(xs[b][:c].astype(np.float32)).cuda().to(torch_dtype(cfg)).reshape(1, c, -1)
-            view = LatentCache(shape, cache.ckv[b:b + 1], None if cache.ckv_scale is None else cache.ckv_scale[b:b + 1],
-                               cache.krope[b:b + 1], 1, t_max)
+            view = cache.view(b, b + 1)
             append(w, view, xt, zero, 0)
     x_new = torch.from_numpy(np.stack([x[c:c + t_new] for x, c in zip(xs, ctx)]).astype(np.float32))
     x_new = x_new.cuda().to(torch_dtype(cfg)).contiguous()
