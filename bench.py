@@ -14,13 +14,14 @@ of mla_decode) separately: `--steps` back-to-back launches of it between two HIP
 
 The cpu_baseline object times the oracle (plain fp64 numpy; the library never uses it) on a bounded
 sample of the same workload on the host's cores.  Secondary workloads (long-context variable-length
-decode, int4-latent decode, causal prefill) are reported in `secondary`.
+decode, int4-latent decode, 2-bit-latent decode with a 128-row bf16 window, causal prefill) are reported
+in `secondary`.
 
 `roofline.traffic` is the HBM traffic of one launch of that kernel from FETCH_SIZE / WRITE_SIZE counter
 runs (profiles/pmc_traffic.json, scaled by the counters of a plain copy of known size, see
 --copy-calibration); it is null when those counters were taken on different decode sources.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only c1,c3,c4,c2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only c1,c3,c4,c5,c2] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -51,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="c1,c3,c4,c2")
+    ap.add_argument("--only", default="c1,c3,c4,c5,c2")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -158,8 +159,13 @@ def make_decode_workload(cfg, conv, lens, copies, seed):
         ws = bd._keep[-1]
         bound.append(bd)
     bytes_per_row = caches[0].nbytes_per_token()
-    return dict(w=w, caches=caches, bound=bound, lens=lens, bytes=int(bytes_per_row * int(np.sum(lens))),
-                bytes_per_row=bytes_per_row)
+    total = bytes_per_row * int(np.sum(lens))
+    if caches[0].window:
+        # the last min(L, W) rows of each sequence are read from the bf16 ring instead of the code store
+        ring_row = cfg.d_kv * 2
+        code_row = caches[0].ckv[0, 0].numel() + caches[0].ckv_scale[0, 0].numel() * 2
+        total += sum(min(int(L), caches[0].window) for L in lens) * (ring_row - code_row)
+    return dict(w=w, caches=caches, bound=bound, lens=lens, bytes=int(total), bytes_per_row=bytes_per_row)
 
 
 def time_decode(wl, steps, warmup):
@@ -330,6 +336,17 @@ def main():
         r4.update(hbm_frac=r4["kernel_gbs"] / HBM_PEAK_GBS)
         secondary["llama_int4_decode"] = r4
         del wl4
+        torch.cuda.empty_cache()
+
+    if "c5" in only:
+        # the int4 workload's shape with the 2-bit latent and a bf16 window of the last 128 rows
+        cfg5 = synth.scaled(C[4], name="llama_int2w_decode", cache_fmt="int2_g32_win")
+        wl5 = make_decode_workload(cfg5, conv_main, synth.seq_lens(cfg5), args.copies, seed=1005)
+        r5 = decode_result("llama_int2w_decode", cfg5, wl5, args.steps, args.warmup)
+        r5.update(hbm_frac=r5["kernel_gbs"] / HBM_PEAK_GBS, window=wl5["caches"][0].window,
+                  kernel="decode_attn_mfma<128, 8, 2>")
+        secondary["llama_int2w_decode"] = r5
+        del wl5
         torch.cuda.empty_cache()
 
     if "c2" in only:

@@ -46,11 +46,12 @@ __device__ __forceinline__ int wave_iscan(int v) {  // inclusive prefix sum over
   }
   return v;
 }
-// Items of a sequence of L tokens: its coded positions and its window of bf16 rows (fmt 2, a.win > 0) are
-// cut into chunks separately, so that an item reads one kind of row.
+// Items of a sequence of L tokens.  With a window of bf16 rows (fmt 2, a.win > 0) only the coded positions
+// [0, L - min(L, win)) are cut into chunks, and the sequence's last item also takes the window; a sequence
+// with no coded rows has one item, its window.
 __device__ __forceinline__ int item_count(const DecodeArgs& a, int L, int chunk) {
-  const int lw = min(L, a.win), lq = L - lw;
-  return (lq + chunk - 1) / chunk + (lw + chunk - 1) / chunk;
+  const int lq = L - min(L, a.win), nq = (lq + chunk - 1) / chunk;
+  return (nq == 0 && L > 0) ? 1 : nq;
 }
 __device__ int work_chunk(const DecodeArgs& a) {
   int tot = 0;
@@ -61,8 +62,8 @@ __device__ int work_chunk(const DecodeArgs& a) {
   return __builtin_amdgcn_readfirstlane(chunk < 64 ? 64 : (chunk > a.plan.cmax ? a.plan.cmax : chunk));
 }
 struct WorkItem {
-  int b, t0, t1;  // sequence and token range [t0, t1), non-empty when found
-  int win;        // 1: the range lies in the sequence's window of bf16 rows (fmt 2)
+  int b, t0, t1;  // sequence and coded (or dense) token range [t0, t1)
+  int w0, w1;     // window rows [w0, w1) of the sequence's last item (fmt 2), else empty
 };
 // Item `item` of the split; false when the batch has fewer items.
 __device__ bool locate_item(const DecodeArgs& a, int item, WorkItem& wi) {
@@ -80,12 +81,14 @@ __device__ bool locate_item(const DecodeArgs& a, int item, WorkItem& wi) {
       const int first = base + __shfl(incl - cnt, ln, 64);
       const int Lb = __shfl(L, ln, 64), lq = Lb - min(Lb, a.win), nq = (lq + chunk - 1) / chunk;
       const int j = item - first;
+      const bool last = j + 1 >= nq;
       // the values are wave-uniform; readfirstlane lets the compiler keep them (and the addresses
       // derived from them) in scalar registers
       wi.b = __builtin_amdgcn_readfirstlane(c0 + ln);
-      wi.win = __builtin_amdgcn_readfirstlane(j >= nq ? 1 : 0);
-      wi.t0 = __builtin_amdgcn_readfirstlane(j < nq ? j * chunk : lq + (j - nq) * chunk);
-      wi.t1 = __builtin_amdgcn_readfirstlane(min(wi.t0 + chunk, j < nq ? lq : Lb));
+      wi.t0 = __builtin_amdgcn_readfirstlane(min(j * chunk, lq));
+      wi.t1 = __builtin_amdgcn_readfirstlane(min(j * chunk + chunk, lq));
+      wi.w0 = __builtin_amdgcn_readfirstlane(last ? lq : 0);
+      wi.w1 = __builtin_amdgcn_readfirstlane(last ? Lb : 0);
       return true;
     }
     base += total;
@@ -330,64 +333,81 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 }
 
 // ------------------------------------------------------------------ 2a. attention, generic VALU path
+// One workgroup per work item, all heads in turn.  The item's rows (its coded or dense range, then for the
+// 2-bit format the window of its sequence's last item) are taken in runs of at most plan.cmax rows, whose
+// scores fit the LDS buffer; runs after the first merge into the head's running max / sum / output
+// (a single run, the usual case, computes exactly the one-pass result).
 template <typename T, int FMT>
 __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
   WorkItem wi;
   if (!locate_item(a, blockIdx.x, wi)) return;
-  const int b = wi.b, t0 = wi.t0, n = wi.t1 - wi.t0;
+  const int b = wi.b;
   const int D = a.s.d_kv, NH = a.s.n_heads, R2 = a.s.r2();
+  constexpr int KPT = 4;  // latent columns per thread (d_kv <= 1024)
   extern __shared__ float sh[];
   float* qs = sh;              // D
   float* qrs = qs + D;         // R2
-  float* sc = qrs + R2 + 1;    // chunk
+  float* sc = qrs + R2 + 1;    // cmax
   __shared__ float red[8];
   float* ml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * NH * MLS;
   float* po = (float*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * NH * D;
   const T* qt = (const T*)(a.ws + a.plan.off_qt) + (size_t)b * NH * D;
   const float* qr = (const float*)(a.ws + a.plan.off_qr) + (size_t)b * NH * R2;
-  const size_t row0 = (size_t)b * a.t_max + t0;
-  auto lat = [&](int t, int k) {
-    if constexpr (FMT == 2) return latent2(a, b, t0 + t, wi.win != 0, k);
-    else return latent<T, FMT>(a, row0 + t, k);
+  const size_t rowb = (size_t)b * a.t_max;
+  // element k of the latent at position pos (from the window when `win`)
+  auto lat = [&](int pos, bool win, int k) {
+    if constexpr (FMT == 2) return latent2(a, b, pos, win, k);
+    else return latent<T, FMT>(a, rowb + pos, k);
   };
   for (int h = 0; h < NH; ++h) {
-    if (n <= 0) {
-      for (int k = threadIdx.x; k < D; k += blockDim.x) po[(size_t)h * D + k] = 0.f;
-      if (threadIdx.x == 0) {
-        ml[MLS * h] = -INFINITY;
-        ml[MLS * h + 1] = 0.f;
-      }
-      continue;
-    }
     for (int k = threadIdx.x; k < D; k += blockDim.x) qs[k] = to_f32(qt[(size_t)h * D + k]);
     for (int j = threadIdx.x; j < R2; j += blockDim.x) qrs[j] = qr[h * R2 + j];
     __syncthreads();
-    float mloc = -INFINITY;
-    for (int t = threadIdx.x; t < n; t += blockDim.x) {
-      float s = 0.f;
-      for (int k = 0; k < D; ++k) s = fmaf(qs[k], lat(t, k), s);
-      const T* kr = (const T*)a.krope + ((row0 + t) * NH + h) * R2;
-      for (int j = 0; j < R2; ++j) s = fmaf(qrs[j], to_f32(kr[j]), s);
-      sc[t] = s;
-      mloc = fmaxf(mloc, s);
+    float m_run = -INFINITY, l_run = 0.f, o[KPT] = {0.f, 0.f, 0.f, 0.f};
+    for (int seg = 0; seg < 2; ++seg) {
+      const int s0 = seg ? wi.w0 : wi.t0, s1 = seg ? wi.w1 : wi.t1;
+      const bool win = seg == 1;
+      for (int r0 = s0; r0 < s1; r0 += a.plan.cmax) {
+        const int n = min(s1 - r0, a.plan.cmax);
+        float mloc = -INFINITY;
+        for (int t = threadIdx.x; t < n; t += blockDim.x) {
+          float s = 0.f;
+          for (int k = 0; k < D; ++k) s = fmaf(qs[k], lat(r0 + t, win, k), s);
+          const T* kr = (const T*)a.krope + ((rowb + r0 + t) * NH + h) * R2;
+          for (int j = 0; j < R2; ++j) s = fmaf(qrs[j], to_f32(kr[j]), s);
+          sc[t] = s;
+          mloc = fmaxf(mloc, s);
+        }
+        const float m_new = fmaxf(m_run, block_reduce(mloc, red, true));
+        const float alpha = exp2f(m_run - m_new);  // 0 before the first run
+        float lloc = 0.f;
+        for (int t = threadIdx.x; t < n; t += blockDim.x) {
+          const float p = exp2f(sc[t] - m_new);
+          sc[t] = p;
+          lloc += p;
+        }
+        l_run = l_run * alpha + block_reduce(lloc, red, false);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+          const int k = threadIdx.x + i * blockDim.x;
+          if (k >= D) continue;
+          float acc = 0.f;
+          for (int t = 0; t < n; ++t) acc = fmaf(sc[t], lat(r0 + t, win, k), acc);
+          o[i] = o[i] * alpha + acc;
+        }
+        m_run = m_new;
+        __syncthreads();  // sc is rewritten by the next run
+      }
     }
-    const float m = block_reduce(mloc, red, true);
-    float lloc = 0.f;
-    for (int t = threadIdx.x; t < n; t += blockDim.x) {
-      float p = exp2f(sc[t] - m);
-      sc[t] = p;
-      lloc += p;
-    }
-    const float l = block_reduce(lloc, red, false);
-    __syncthreads();
-    for (int k = threadIdx.x; k < D; k += blockDim.x) {
-      float o = 0.f;
-      for (int t = 0; t < n; ++t) o = fmaf(sc[t], lat(t, k), o);
-      po[(size_t)h * D + k] = o;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int k = threadIdx.x + i * blockDim.x;
+      if (k < D) po[(size_t)h * D + k] = o[i];
     }
     if (threadIdx.x == 0) {
-      ml[MLS * h] = m;
-      ml[MLS * h + 1] = l;
+      ml[MLS * h] = m_run;
+      ml[MLS * h + 1] = l_run;
     }
     __syncthreads();
   }
@@ -476,9 +496,11 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   }
   WorkItem wi;
   if (!locate_item(a, blockIdx.x, wi)) return;
-  const int b = wi.b, t0 = wi.t0, t1 = wi.t1;
-  const bool wwin = FMT == 2 && wi.win;  // rows from the window ring (bf16), not the code store
-  if (fused_rows(f, b, t0, t1, (float*)cbuf)) MLA_WAIT_VMCNT(0);
+  const int b = wi.b;
+  // the tile loop runs over [wi.t0, wi.t1) and then (2-bit format) over the window [wi.w0, wi.w1), whose rows
+  // come from the ring (the WIN instances of load_tile / step); t1 is the end of the current run
+  int t1 = wi.t1;
+  if (fused_rows(f, b, wi.t0, wi.t1, (float*)cbuf)) MLA_WAIT_VMCNT(0);
 
   // latent query operands (B of the score product) and the rotated query pairs
   const bf16* qt = (const bf16*)(a.ws + a.plan.off_qt) + ((size_t)b * 32 + h) * D + w * DW + 8 * hb;
@@ -525,13 +547,14 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   const uint32_t koff = (((8 * w + 4 * hb) * 32 + h) * R2) * 2;
   // window items (2-bit format) stage their bf16 rows straight from the ring in stage_window and
   // prefetch only the RoPE keys here
-  auto load_tile = [&](auto bsel, int tt) {
+  auto load_tile = [&](auto bsel, auto winsel, int tt) {
     constexpr int B = decltype(bsel)::value;
+    constexpr bool WIN = decltype(winsel)::value;
     if (tt + 32 <= t1) {
       const char* cb = (const char*)a.ckv + (rowb + tt) * RBY;
       const char* sb = (const char*)a.ckv_scale + (rowb + tt) * (D / 32) * MBY;
       const char* kb = (const char*)krb + (size_t)tt * 32 * R2 * 2 + koff;
-      if (!wwin) {
+      if constexpr (!WIN) {
 #pragma unroll
         for (int it = 0; it < CCH; ++it) {
           creg[B][it] = *(const u32x4*)(cb + coff[it]);
@@ -542,7 +565,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
       for (int i = 0; i < 4; ++i) kreg[B][i] = *(const kv_t*)(kb + i * 32 * R2 * 2);
       return;
     }
-    if (!wwin) {
+    if constexpr (!WIN) {
 #pragma unroll
       for (int it = 0; it < CCH; ++it) {
         const int row = (it * 64 + lane) / CPR;
@@ -605,28 +628,32 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   };
 
   // a tile of window rows: this wave's slice of rows tt .. tt+31 from the ring, global -> LDS
+  // (in two halves of four 16-byte chunks per lane, to stay within the registers the prefetch leaves)
   auto stage_window = [&](int tt) {
-    constexpr int WCPR = DW / 8, WCH = 32 * WCPR / 64;  // 16-byte chunks per row slice, per lane
+    constexpr int WCPR = DW / 8, WCH = 32 * WCPR / 64, HALF = WCH / 2;  // chunks per row slice, per lane
     const bf16* ring = (const bf16*)a.ckv_win + (size_t)b * a.win * D + w * DW;
-    u32x4 tmp[WCH];
 #pragma unroll
-    for (int it = 0; it < WCH; ++it) {
-      const int c = it * 64 + lane, row = c / WCPR, q = c - row * WCPR;
-      const int tok = min(tt + row, t1 - 1);  // rows past the range repeat its last row (masked below)
-      tmp[it] = *(const u32x4*)(ring + (size_t)(tok % a.win) * D + 8 * q);
-    }
+    for (int hf = 0; hf < 2; ++hf) {
+      u32x4 tmp[HALF];
 #pragma unroll
-    for (int it = 0; it < WCH; ++it) {
-      const int c = it * 64 + lane, row = c / WCPR, q = c - row * WCPR;
-      *(u32x4*)&cw[row * CP + 8 * q] = tmp[it];
+      for (int it = 0; it < HALF; ++it) {
+        const int c = (hf * HALF + it) * 64 + lane, row = c / WCPR, q = c - row * WCPR;
+        const int tok = min(tt + row, t1 - 1);  // rows past the range repeat its last row (masked below)
+        tmp[it] = *(const u32x4*)(ring + (size_t)(tok % a.win) * D + 8 * q);
+      }
+#pragma unroll
+      for (int it = 0; it < HALF; ++it) {
+        const int c = (hf * HALF + it) * 64 + lane, row = c / WCPR, q = c - row * WCPR;
+        *(u32x4*)&cw[row * CP + 8 * q] = tmp[it];
+      }
     }
   };
 
   int par = 0;
   // one 32-token tile: stage registers -> LDS, refill them with the tile two ahead, then both products
-  auto step = [&](auto bsel, int tt) {
+  auto step = [&](auto bsel, auto winsel, int tt) {
     constexpr int B = decltype(bsel)::value;
-    if (wwin) stage_window(tt);
+    if constexpr (decltype(winsel)::value) stage_window(tt);
     else stage_tile(bsel);
     // RoPE term of rows 8w + 4hb + i (result elements 4w + i), taken before the registers refill
     float rt[4];
@@ -637,7 +664,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
       for (int c = 0; c < R2; ++c) acc = fmaf(qr[c], (float)kreg[B][i][c], acc);
       rt[i] = acc;
     }
-    if (tt + 64 < t1) load_tile(bsel, tt + 64);
+    if (tt + 64 < t1) load_tile(bsel, winsel, tt + 64);
     __builtin_amdgcn_wave_barrier();
 
     // scores over this wave's latent columns
@@ -718,11 +745,18 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  load_tile(B0{}, t0);
-  if (t0 + 32 < t1) load_tile(B1{}, t0 + 32);
-  for (int tt = t0; tt < t1; tt += 64) {
-    step(B0{}, tt);
-    if (tt + 32 < t1) step(B1{}, tt + 32);
+  auto run = [&](auto winsel, int ra, int rb) {
+    t1 = rb;
+    load_tile(B0{}, winsel, ra);
+    if (ra + 32 < rb) load_tile(B1{}, winsel, ra + 32);
+    for (int tt = ra; tt < rb; tt += 64) {
+      step(B0{}, winsel, tt);
+      if (tt + 32 < rb) step(B1{}, winsel, tt + 32);
+    }
+  };
+  if (wi.t0 < wi.t1) run(std::false_type{}, wi.t0, wi.t1);
+  if constexpr (FMT == 2) {
+    if (wi.w0 < wi.w1) run(std::true_type{}, wi.w0, wi.w1);
   }
 
   store_partial<DW>(a, oacc, (float*)sbuf, m_run, l_run);
@@ -1668,9 +1702,9 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a, int sb) {
   for (int j = w / wps; j < nseq; j += 4 / wps) {
     const int b = b0 + j, q = w % wps;
     int before = 0;
-    for (int i = lane; i < b; i += 64) before += (clamp_len(a, i) + chunk - 1) / chunk;
+    for (int i = lane; i < b; i += 64) before += item_count(a, clamp_len(a, i), chunk);
     const int first = __builtin_amdgcn_readfirstlane(wave_isum(before));
-    const int S = (clamp_len(a, b) + chunk - 1) / chunk;
+    const int S = item_count(a, clamp_len(a, b), chunk);
     float M, den, acc[KPL];
     if (a.plan.f16)
       merge_splits<KPL, true>(a, first, q, wps, S, h, M, den, acc);
@@ -1806,12 +1840,12 @@ DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len) {
     const long long c = room > 0 ? (room / 64) * 64 : 64;
     if (c < p.cmax) p.cmax = (int)(c < 64 ? 64 : c);
   }
-  // items = sum_b ceil(L_b / chunk) < sum_b L_b / chunk + batch; chunk >= sum / target unless clamped.
-  // A window of bf16 rows (fmt 2) is cut separately from the coded rows: at most one more item each.
-  const long long B = batch, Lm = max_seq_len, extra = s.fmt == 2 ? B : 0;
-  long long by_min = B * ((Lm + 63) / 64) + extra;                  // chunk = 64
+  // items = sum_b ceil(L_b / chunk) < sum_b L_b / chunk + batch; chunk >= sum / target unless clamped
+  // (with a window, fmt 2, a sequence has at most that many: only its coded rows are cut)
+  const long long B = batch, Lm = max_seq_len;
+  long long by_min = B * ((Lm + 63) / 64);                          // chunk = 64
   long long by_max = (B * Lm + p.cmax - 1) / p.cmax;                // chunk = cmax
-  long long bound = (by_max > p.target ? by_max : p.target) + B + extra;
+  long long bound = (by_max > p.target ? by_max : p.target) + B;
   long long items = by_min < bound ? by_min : bound;
   p.max_items = (int)(items < 1 ? 1 : items);
   const size_t esz = s.dtype == 0 ? 4 : 2;

@@ -38,8 +38,8 @@ size_t append_workspace_bytes(const Shape& s, int tokens);
 // Decode work split.  The kernels read the batch's lengths L_b on the device and cut its tokens into
 // work items of `chunk` tokens: chunk = clamp(round_up(ceil(sum_b L_b / target), 64), 64, cmax), and
 // sequence b owns ceil(L_b / chunk) consecutive items (in batch order).  With a window of bf16 rows
-// (fmt 2) the coded positions [0, L_b - W_b) and the window [L_b - W_b, L_b), W_b = min(L_b, win), are
-// cut separately: ceil((L_b - W_b) / chunk) + ceil(W_b / chunk) items.  Ragged batches therefore
+// (fmt 2) only the coded positions [0, L_b - W_b), W_b = min(L_b, win), are cut, and the sequence's last
+// item also reads the window [L_b - W_b, L_b) (one item when there are no coded positions).  Ragged batches therefore
 // spread over about `target` workgroups like uniform ones.  max_items bounds the item count for any
 // lengths within max_seq_len; the per-item partial results are laid out by item.
 struct DecodePlan {

@@ -221,10 +221,12 @@ def test_quantize_checks(lib):
 
 
 def test_window_format_workspace(lib):
-    """The 2-bit format cuts each sequence's window into its own work items: at most one more per sequence."""
-    n1 = lib.mla_decode_workspace_bytes(ctypes.byref(cfg(cache_fmt=1)), 64, 8192)
-    n2 = lib.mla_decode_workspace_bytes(ctypes.byref(cfg(cache_fmt=2)), 64, 8192)
-    assert n2 > n1
+    """The 2-bit format's window rides on each sequence's last work item, so it needs no more split
+    results than the int4 format."""
+    for batch, ctx in ((64, 8192), (1, 100), (8, 32768)):
+        n1 = lib.mla_decode_workspace_bytes(ctypes.byref(cfg(cache_fmt=1)), batch, ctx)
+        n2 = lib.mla_decode_workspace_bytes(ctypes.byref(cfg(cache_fmt=2)), batch, ctx)
+        assert n2 == n1 > 0
 
 
 def test_status_strings(lib):
