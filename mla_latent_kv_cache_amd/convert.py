@@ -9,7 +9,8 @@ Implements the two steps of the MHA2MLA key-designs section (Paper-Notes ACL2025
     (orthonormal columns) and the up-projections are W_dkv^T [W_k,nope | W_v] split per head.
 
 The pages' ablation variants are options of convert_layer: the fixed partial-RoPE strategies S_high,
-S_low and S_uniform (kept_pairs), and SVD_split at the same latent width.
+S_low and S_uniform (kept_pairs), and SVD_split at the same latent width; n_kv_heads converts a
+grouped-query source layer (the pages convert Llama3-8B, a GQA model).
 
 The subspace is found from the eigen-decomposition of the smaller Gram matrix, which gives the same
 truncated factorisation as an SVD up to the signs of the basis vectors.  This runs once per layer,
@@ -21,12 +22,14 @@ from __future__ import annotations
 import numpy as np
 
 
-def pair_scores(x_cal, w_q, w_k, n_heads, d_head):
-    """[n_heads, d_head/2] scores: mean pair norm of q times mean pair norm of k over calibration tokens."""
+def pair_scores(x_cal, w_q, w_k, n_heads, d_head, n_kv=None):
+    """[n_kv, d_head/2] scores: mean pair norm of q times mean pair norm of k over calibration tokens; with
+    grouped-query keys (n_kv < n_heads) the q factor is averaged over the n_heads / n_kv heads of a group."""
+    n_kv = n_heads if n_kv is None else n_kv
     t = x_cal.shape[0]
-    qn = np.hypot(*np.moveaxis((x_cal @ w_q).reshape(t, n_heads, d_head // 2, 2), -1, 0))
-    kn = np.hypot(*np.moveaxis((x_cal @ w_k).reshape(t, n_heads, d_head // 2, 2), -1, 0))
-    return qn.mean(axis=0) * kn.mean(axis=0)
+    qn = np.hypot(*np.moveaxis((x_cal @ w_q).reshape(t, n_heads, d_head // 2, 2), -1, 0)).mean(axis=0)
+    kn = np.hypot(*np.moveaxis((x_cal @ w_k).reshape(t, n_kv, d_head // 2, 2), -1, 0)).mean(axis=0)
+    return qn.reshape(n_kv, n_heads // n_kv, d_head // 2).mean(axis=1) * kn
 
 
 def top_pairs(scores, r):
@@ -78,7 +81,43 @@ def kept_pairs(strategy, scores, r):
     return np.broadcast_to(table[strategy].astype(np.int32), (n_heads, r)).copy()
 
 
-def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv, strategy="2-norm", svd="joint"):
+def _factor(w_k, w_v, pair_idx, n_kv, d_head, d_kv, svd):
+    """Kept RoPE columns and the low-rank factors of one layer whose keys and values have n_kv heads."""
+    r = pair_idx.shape[1]
+    d = w_k.shape[0]
+    wk = w_k.reshape(d, n_kv, d_head // 2, 2)
+    keep = np.zeros((n_kv, d_head // 2), dtype=bool)
+    for h in range(n_kv):
+        keep[h, pair_idx[h]] = True
+    w_krope = np.stack([wk[:, h, pair_idx[h], :] for h in range(n_kv)], axis=1).reshape(d, n_kv * 2 * r)
+    w_knope = np.stack([wk[:, h, ~keep[h], :].reshape(d, -1) for h in range(n_kv)], axis=1).reshape(d, -1)
+    dn = d_head - 2 * r
+    out = dict(w_krope=w_krope)
+    if svd == "joint":
+        m = np.hstack([w_knope, w_v])
+        u, sig = low_rank_factors(m, d_kv)
+        z = u.T @ m
+        w_uk = z[:, : n_kv * dn].reshape(d_kv, n_kv, dn).transpose(1, 0, 2)
+        w_uv = z[:, n_kv * dn:].reshape(d_kv, n_kv, d_head).transpose(1, 0, 2)
+        out.update(w_dkv=u, sigma=sig)
+    elif svd == "split":
+        rk = d_kv // 2
+        if rk > min(w_knope.shape) or d_kv - rk > min(w_v.shape):
+            raise ValueError("svd='split': d_kv/2 exceeds the rank W_k,nope or W_v can have")
+        uk, sig_k = low_rank_factors(w_knope, rk)
+        uv, sig_v = low_rank_factors(w_v, d_kv - rk)
+        w_uk = np.zeros((n_kv, d_kv, dn))
+        w_uv = np.zeros((n_kv, d_kv, d_head))
+        w_uk[:, :rk, :] = (uk.T @ w_knope).reshape(rk, n_kv, dn).transpose(1, 0, 2)
+        w_uv[:, rk:, :] = (uv.T @ w_v).reshape(d_kv - rk, n_kv, d_head).transpose(1, 0, 2)
+        out.update(w_dkv=np.hstack([uk, uv]), sigma_k=sig_k, sigma_v=sig_v)
+    else:
+        raise ValueError(f"unknown SVD variant {svd!r}; expected joint or split")
+    out.update(w_uk=np.ascontiguousarray(w_uk), w_uv=np.ascontiguousarray(w_uv))
+    return out
+
+
+def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv, strategy="2-norm", svd="joint", n_kv_heads=None):
     """Returns the converted layer in math layouts:
     pair_idx [n_h, r], w_dkv [d, d_kv], w_krope [d, n_h*2r], w_uk [n_h, d_kv, d_h-2r], w_uv [n_h, d_kv, d_h],
     and the singular values: sigma (all of [W_k,nope | W_v]) for the joint SVD, sigma_k / sigma_v (of W_k,nope
@@ -87,37 +126,26 @@ def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv, strategy="2-no
     svd="joint" is the method's joint low-rank step.  svd="split" is the SVD_split ablation at the same latent
     width: the first d_kv/2 latent dims span the top left singular subspace of W_k,nope alone and the other
     d_kv - d_kv/2 that of W_v alone, so W_uk is zero on the value half and W_uv on the key half; the
-    result is an ordinary MLA layer that the attention kernels run unchanged."""
-    scores = pair_scores(x_cal, w_q, w_k, n_heads, d_head)
+    result is an ordinary MLA layer that the attention kernels run unchanged.
+
+    n_kv_heads < n_heads converts a grouped-query layer (w_k, w_v [d, n_kv*d_h]; query head h reads KV head
+    h // (n_heads / n_kv)): subspaces are kept per KV head by the group's mean score, the low-rank step runs
+    over the n_kv heads' columns, and the result is expanded per query head (each head takes its group's
+    kept subspaces, RoPE key columns and up-projections; the per-group factors are under `group_*`)."""
+    n_kv = n_heads if n_kv_heads is None else int(n_kv_heads)
+    if n_kv <= 0 or n_heads % n_kv:
+        raise ValueError("n_kv_heads must divide n_heads")
+    scores = pair_scores(x_cal, w_q, w_k, n_heads, d_head, n_kv)
     pair_idx = kept_pairs(strategy, scores, r)
+    f = _factor(w_k, w_v, pair_idx, n_kv, d_head, d_kv, svd)
+    if n_kv == n_heads:
+        f.update(pair_idx=pair_idx, scores=scores)
+        return f
+    grp = np.arange(n_heads) // (n_heads // n_kv)
     d = w_k.shape[0]
-    wk = w_k.reshape(d, n_heads, d_head // 2, 2)
-    keep = np.zeros((n_heads, d_head // 2), dtype=bool)
-    for h in range(n_heads):
-        keep[h, pair_idx[h]] = True
-    w_krope = np.stack([wk[:, h, pair_idx[h], :] for h in range(n_heads)], axis=1).reshape(d, n_heads * 2 * r)
-    w_knope = np.stack([wk[:, h, ~keep[h], :].reshape(d, -1) for h in range(n_heads)], axis=1).reshape(d, -1)
-    dn = d_head - 2 * r
-    out = dict(pair_idx=pair_idx, w_krope=w_krope, scores=scores)
-    if svd == "joint":
-        m = np.hstack([w_knope, w_v])
-        u, sig = low_rank_factors(m, d_kv)
-        z = u.T @ m
-        w_uk = z[:, : n_heads * dn].reshape(d_kv, n_heads, dn).transpose(1, 0, 2)
-        w_uv = z[:, n_heads * dn:].reshape(d_kv, n_heads, d_head).transpose(1, 0, 2)
-        out.update(w_dkv=u, sigma=sig)
-    elif svd == "split":
-        rk = d_kv // 2
-        if rk > min(w_knope.shape) or d_kv - rk > min(w_v.shape):
-            raise ValueError("svd='split': d_kv/2 exceeds the rank W_k,nope or W_v can have")
-        uk, sig_k = low_rank_factors(w_knope, rk)
-        uv, sig_v = low_rank_factors(w_v, d_kv - rk)
-        w_uk = np.zeros((n_heads, d_kv, dn))
-        w_uv = np.zeros((n_heads, d_kv, d_head))
-        w_uk[:, :rk, :] = (uk.T @ w_knope).reshape(rk, n_heads, dn).transpose(1, 0, 2)
-        w_uv[:, rk:, :] = (uv.T @ w_v).reshape(d_kv - rk, n_heads, d_head).transpose(1, 0, 2)
-        out.update(w_dkv=np.hstack([uk, uv]), sigma_k=sig_k, sigma_v=sig_v)
-    else:
-        raise ValueError(f"unknown SVD variant {svd!r}; expected joint or split")
-    out.update(w_uk=np.ascontiguousarray(w_uk), w_uv=np.ascontiguousarray(w_uv))
+    out = dict(f)
+    out.update(pair_idx=pair_idx[grp], scores=scores, group_pair_idx=pair_idx,
+               w_krope=f["w_krope"].reshape(d, n_kv, 2 * r)[:, grp, :].reshape(d, n_heads * 2 * r),
+               w_uk=np.ascontiguousarray(f["w_uk"][grp]), w_uv=np.ascontiguousarray(f["w_uv"][grp]),
+               group_w_uk=f["w_uk"], group_w_uv=f["w_uv"], group_w_krope=f["w_krope"])
     return out

@@ -26,7 +26,10 @@ in that precision.
 
 from .convert import (  # noqa: F401
     calibration_qk,
+    convert_gqa_layer,
     convert_layer,
+    gqa_pair_scores,
+    group_of,
     joint_svd,
     pair_scores,
     select_pairs,

@@ -13,7 +13,9 @@ errors that the conversion itself makes, before any fine-tuning, on a seeded lay
 * end to end      -- the converted layer's attention (latent cache, unabsorbed) against full-RoPE MHA.
 
 Run as `python -m oracle.ablation [--family llama] [--r 4] [--d-kv 512] [--tokens 512] [--iid]`
-from the repository root; it prints one table row per (strategy, SVD variant).
+from the repository root; it prints one table row per (strategy, SVD variant).  `--gqa llama3` measures a
+grouped-query source layer instead (synth.GQA_FAMILIES; the reference is its own grouped-query attention,
+the conversion convert_gqa_layer), for the 2-norm strategy and the joint SVD.
 """
 
 from __future__ import annotations
@@ -24,7 +26,8 @@ import time
 import numpy as np
 
 from .attention import append_ref, prefill_ref, rope_rotate
-from .convert import calibration_qk, convert_layer, pair_scores, select_pairs_by
+from .convert import (calibration_qk, convert_gqa_layer, convert_layer, group_of, pair_scores,
+                      select_pairs_by)
 
 STRATEGIES = ("2-norm", "high", "uniform", "low")
 SVDS = ("joint", "split")
@@ -50,6 +53,32 @@ def mha_ref(x, w_q, w_k, w_v, n_heads, d_head, theta, kept=None):
         e = np.exp(s - s.max(axis=1, keepdims=True))
         out[:, h, :] = (e / e.sum(axis=1, keepdims=True)) @ v
     return out
+
+
+def gqa_ref(x, w_q, w_k, w_v, n_heads, n_kv, d_head, theta, kept=None):
+    """Grouped-query attention: mha_ref with each query head reading its group's K and V columns (kept[g]:
+    the RoPE subspaces of KV head g, all when None)."""
+    grp = [group_of(h, n_heads, n_kv) for h in range(n_heads)]
+
+    def expand(w):
+        return np.concatenate([w[:, g * d_head:(g + 1) * d_head] for g in grp], axis=1)
+
+    kept_h = None if kept is None else [kept[g] for g in grp]
+    return mha_ref(x, w_q, expand(w_k), expand(w_v), n_heads, d_head, theta, kept=kept_h)
+
+
+def gqa_rows(w_q, w_k, w_v, x_cal, x_eval, n_heads, n_kv, d_head, r, d_kv, theta=1e4):
+    """The four errors for the grouped-query conversion (2-norm subspaces per KV head, joint SVD)."""
+    full = gqa_ref(x_eval, w_q, w_k, w_v, n_heads, n_kv, d_head, theta)
+    conv = convert_gqa_layer(w_q, w_k, w_v, x_cal, n_heads, n_kv, d_head, r, d_kv)
+    kept = conv["group_pair_idx"]
+    m = conv["m"]
+    z = np.concatenate([np.concatenate(list(conv["group_w_uk"]), axis=1),
+                        np.concatenate(list(conv["group_w_uv"]), axis=1)], axis=1)
+    return [dict(strategy="2-norm", svd="joint", dropped_score=dropped_score(conv["scores"], kept),
+                 partial_rope_err=rel_l2(gqa_ref(x_eval, w_q, w_k, w_v, n_heads, n_kv, d_head, theta, kept=kept), full),
+                 kv_fit_err=float(np.linalg.norm(m - conv["w_dkv"] @ z) / np.linalg.norm(m)),
+                 end_to_end_err=rel_l2(converted_ref(x_eval, w_q, conv, d_head, theta), full))]
 
 
 def converted_ref(x, w_q, conv, d_head, theta):
@@ -107,14 +136,23 @@ def main(argv=None):
     ap.add_argument("--d-kv", type=int, default=512)
     ap.add_argument("--tokens", type=int, default=512)
     ap.add_argument("--iid", action="store_true", help="i.i.d. N(0, 0.02^2) weights instead of the structured layer")
+    ap.add_argument("--gqa", default=None, help="a grouped-query family of synth.GQA_FAMILIES (i.i.d. weights)")
     args = ap.parse_args(argv)
-    d, n_h, d_h, _ = synth.FAMILIES[args.family]
-    wq, wk, wv, xc = (synth.layer_weights if args.iid else synth.structured_layer_weights)(args.family)
-    x = synth.eval_x(args.family, args.tokens)
     t0 = time.time()
-    rows = ablation_rows(wq, wk, wv, xc, x, n_h, d_h, args.r, args.d_kv)
-    print(f"family {args.family} (d={d}, n_h={n_h}, d_h={d_h}), r={args.r}, d_kv={args.d_kv}, "
-          f"{args.tokens} tokens, {'iid' if args.iid else 'structured'} weights, {time.time() - t0:.0f} s")
+    if args.gqa:
+        d, n_h, n_kv, d_h, _ = synth.GQA_FAMILIES[args.gqa]
+        wq, wk, wv, xc = synth.gqa_layer_weights(args.gqa)
+        x = np.random.default_rng(0).standard_normal((args.tokens, d))
+        rows = gqa_rows(wq, wk, wv, xc, x, n_h, n_kv, d_h, args.r, args.d_kv)
+        print(f"grouped-query family {args.gqa} (d={d}, n_h={n_h}, n_kv={n_kv}, d_h={d_h}), r={args.r}, "
+              f"d_kv={args.d_kv}, {args.tokens} tokens, {time.time() - t0:.0f} s")
+    else:
+        d, n_h, d_h, _ = synth.FAMILIES[args.family]
+        wq, wk, wv, xc = (synth.layer_weights if args.iid else synth.structured_layer_weights)(args.family)
+        x = synth.eval_x(args.family, args.tokens)
+        rows = ablation_rows(wq, wk, wv, xc, x, n_h, d_h, args.r, args.d_kv)
+        print(f"family {args.family} (d={d}, n_h={n_h}, d_h={d_h}), r={args.r}, d_kv={args.d_kv}, "
+              f"{args.tokens} tokens, {'iid' if args.iid else 'structured'} weights, {time.time() - t0:.0f} s")
     print("| strategy | SVD | dropped score | partial-RoPE err | K/V fit err | end-to-end err |")
     print("|---|---|---|---|---|---|")
     for row in rows:

@@ -13,7 +13,8 @@ Follows the Paper-Notes ACL2025 page on MHA2MLA, section 关键设计 ("key desi
    per head into the up-projections W_uk and W_uv.
 
 The ablation variants of the pages (partial-RoPE strategies S_high / S_low / S_uniform, and SVD_split
-at the same latent width) are select_pairs_by and split_svd_layer.
+at the same latent width) are select_pairs_by and split_svd_layer.  Grouped-query source layers (the
+pages convert Llama3-8B, a GQA model, as well as MHA ones) are convert_gqa_layer.
 
 Readings where the page leaves a step open (each also listed in the design notes):
 * scores aggregate over calibration tokens as the product of the mean pair norms,
@@ -162,6 +163,53 @@ def split_svd_layer(w_k, w_v, pair_idx, n_heads, d_head, d_kv):
     w_uv = np.stack([np.concatenate([np.zeros((rk, d_head)), zv[:, h * d_head:(h + 1) * d_head]]) for h in range(n_heads)])
     return dict(w_dkv=w_dkv, w_uk=w_uk, w_uv=w_uv, w_krope=w_krope, sigma_k=sk, sigma_v=sv,
                 m=np.concatenate([w_knope, w_v], axis=1))
+
+
+def group_of(h, n_heads, n_kv):
+    """KV head (group) that query head h reads in a grouped-query layer: n_heads / n_kv consecutive heads each."""
+    return h // (n_heads // n_kv)
+
+
+def gqa_pair_scores(q, k, n_heads, n_kv):
+    """[n_kv, d_head/2] scores of a grouped-query layer: for KV head g and subspace p, the mean over the query
+    heads h of the group of the 2-norm score of (h, p) against the group's keys (q [T, n_heads, d_h],
+    k [T, n_kv, d_h]).  Reading: the kept subspaces are cached once per KV head, so they are chosen per
+    group, by the mean of the Cauchy-Schwarz bounds of the heads that read them."""
+    t, _, d_head = q.shape
+    n_pairs = d_head // 2
+    s = np.zeros((n_kv, n_pairs))
+    for g in range(n_kv):
+        heads = [h for h in range(n_heads) if group_of(h, n_heads, n_kv) == g]
+        for p in range(n_pairs):
+            kn = np.sqrt(k[:, g, 2 * p] ** 2 + k[:, g, 2 * p + 1] ** 2).mean()
+            acc = 0.0
+            for h in heads:
+                acc += np.sqrt(q[:, h, 2 * p] ** 2 + q[:, h, 2 * p + 1] ** 2).mean() * kn
+            s[g, p] = acc / len(heads)
+    return s
+
+
+def convert_gqa_layer(w_q, w_k, w_v, x_cal, n_heads, n_kv, d_head, r, d_kv):
+    """Conversion of a grouped-query layer (n_kv KV heads, each read by n_heads / n_kv query heads).
+
+    Per KV head: top-r subspaces by gqa_pair_scores; joint SVD of [W_k,nope | W_v] over the n_kv KV heads
+    (n_kv (d_h - 2r) + n_kv d_h columns).  The result is given per query head, in the layouts of
+    convert_layer, so that it is an ordinary MLA layer: query head h takes its group's kept subspaces,
+    RoPE key columns and up-projections (pair_idx [n_heads, r], w_krope [d, n_heads*2r] with each group's
+    columns repeated for its heads, w_uk [n_heads, d_kv, d_h-2r], w_uv [n_heads, d_kv, d_h]).  The per-group
+    factors are returned too (`group_*`)."""
+    t = x_cal.shape[0]
+    q = (x_cal @ w_q).reshape(t, n_heads, d_head)
+    k = (x_cal @ w_k).reshape(t, n_kv, d_head)
+    scores = gqa_pair_scores(q, k, n_heads, n_kv)
+    gidx = select_pairs(scores, r)
+    j = joint_svd(w_k, w_v, gidx, n_kv, d_head, d_kv)
+    grp = [group_of(h, n_heads, n_kv) for h in range(n_heads)]
+    two_r = 2 * r
+    w_krope = np.concatenate([j["w_krope"][:, g * two_r:(g + 1) * two_r] for g in grp], axis=1)
+    return dict(pair_idx=gidx[grp], w_dkv=j["w_dkv"], w_krope=w_krope, w_uk=j["w_uk"][grp], w_uv=j["w_uv"][grp],
+                sigma=j["sigma"], m=j["m"], scores=scores, group_pair_idx=gidx, group_w_uk=j["w_uk"],
+                group_w_uv=j["w_uv"], group_w_krope=j["w_krope"])
 
 
 def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv, strategy="2-norm", svd="joint"):

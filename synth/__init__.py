@@ -10,10 +10,12 @@ from .inputs import (  # noqa: F401
     Config,
     CONFIGS,
     FAMILIES,
+    GQA_FAMILIES,
     bf16_bits,
     bits_to_f64,
     context_x,
     eval_x,
+    gqa_layer_weights,
     layer_weights,
     query_rows,
     round_to_device,

@@ -92,6 +92,24 @@ def layer_weights(family: str):
     return w[0], w[1], w[2], x_cal
 
 
+# Grouped-query shape families: (d_model, n_heads, n_kv_heads, d_head, weight-stream seed).
+GQA_FAMILIES = {
+    "gqa_mid": (1024, 32, 8, 128, 5),  # Llama head shapes, 8 KV heads, narrow model width (tests)
+    "llama3": (4096, 32, 8, 128, 6),  # Llama-3-8B-shaped attention layer
+}
+
+
+def gqa_layer_weights(family: str):
+    """W_q [d, n_heads*d_head], W_k, W_v [d, n_kv*d_head] ~ N(0, 0.02^2) and X_cal [64, d] ~ N(0, 1), fp64
+    (stream keys (0,) .. (3,) of the family's seed, as layer_weights)."""
+    d, n_h, n_kv, d_h, seed = GQA_FAMILIES[family]
+    wq = _gen(seed, (0,)).standard_normal((d, n_h * d_h)) * 0.02
+    wk = _gen(seed, (1,)).standard_normal((d, n_kv * d_h)) * 0.02
+    wv = _gen(seed, (2,)).standard_normal((d, n_kv * d_h)) * 0.02
+    x_cal = _gen(seed, (3,)).standard_normal((64, d))
+    return wq, wk, wv, x_cal
+
+
 def structured_layer_weights(family: str):
     """W_q, W_k, W_v [d_model, n_heads*d_head] and X_cal [64, d_model] (fp64) with two kinds of structure
     that i.i.d. weights lack (stream keys (4,) for the weights, (5,) for X_cal of the family's seed):

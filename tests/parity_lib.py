@@ -58,6 +58,20 @@ def converted_layer(family: str, r: int, d_kv: int, dtype: str, strategy: str = 
     return out
 
 
+@functools.lru_cache(maxsize=2)
+def gqa_converted_layer(family: str, r: int, d_kv: int, dtype: str):
+    """The oracle's conversion of a seeded grouped-query layer (synth.GQA_FAMILIES), expanded per query head
+    and rounded to the device dtype like converted_layer."""
+    d, n_h, n_kv, d_h, _ = synth.GQA_FAMILIES[family]
+    wq, wk, wv, xc = synth.gqa_layer_weights(family)
+    conv = oracle.convert_gqa_layer(wq, wk, wv, xc, n_h, n_kv, d_h, r, d_kv)
+    out = {k: synth.round_to_device(conv[k], dtype) for k in ("w_dkv", "w_krope", "w_uk", "w_uv")}
+    out["pair_idx"] = conv["pair_idx"]
+    out["w_q"] = wq
+    out["sigma"] = conv["sigma"]
+    return out
+
+
 def shape_of(cfg):
     from mla_latent_kv_cache_amd import LayerShape
 

@@ -22,13 +22,15 @@ def _to_np(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def run_decode_case(cfg, lens, t_max, sample=None, check_cache=True, repeat_bitwise=True, variant=("2-norm", "joint")):
+def run_decode_case(cfg, lens, t_max, sample=None, check_cache=True, repeat_bitwise=True, variant=("2-norm", "joint"),
+                    layer=None):
     from mla_latent_kv_cache_amd import LatentCache, decode, pack_weights
 
     log(f"[decode] {cfg.name} family={cfg.family} d_kv={cfg.d_kv} r={cfg.r_pairs} fmt={cfg.cache_fmt} "
-        f"B={len(lens)} lens={list(lens)[:8]} t_max={t_max} conversion={variant}")
+        f"B={len(lens)} lens={list(lens)[:8]} t_max={t_max} conversion={variant if layer is None else 'given'}")
     B = len(lens)
-    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype, *variant)
+    if layer is None:
+        layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype, *variant)
     shape = shape_of(cfg)
     w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
     cache = LatentCache.allocate(shape, B, t_max, fill=float("nan"))
@@ -158,6 +160,17 @@ def test_ablation_variant_layers(strategy, svd, fmt):
     up-projection zero."""
     cfg = scaled(CONFIGS[1], family="mid", batch=3, context=0, cache_fmt=fmt)
     run_decode_case(cfg, [700, 33, 260], 704, variant=(strategy, svd))
+
+
+@pytest.mark.parametrize("fmt", ["dense", "int4_g32"])
+def test_gqa_source_layer(fmt):
+    """A layer converted from a grouped-query source (32 query heads, 8 KV heads, Llama head shapes) runs
+    through the same append and decode kernels: every head of a group shares its subspaces and maps."""
+    from parity_lib import gqa_converted_layer
+
+    cfg = scaled(CONFIGS[1], family="mid", batch=3, context=0, cache_fmt=fmt)
+    layer = gqa_converted_layer("gqa_mid", cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    run_decode_case(cfg, [640, 1, 333], 640, layer=layer)
 
 
 def test_mid_int4():

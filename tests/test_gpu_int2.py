@@ -187,6 +187,38 @@ def test_int2_ragged_per_sequence(family):
         log(f"  b={b} L={L} rel-L2={r:.2e} max-abs={a:.2e}")
 
 
+def test_int2_gqa_source_layer():
+    """A grouped-query-source layer (8 KV heads) on the 2-bit cache with a window: cache rows and decode."""
+    from mla_latent_kv_cache_amd import LatentCache, append, decode, pack_weights
+    from parity_lib import gqa_converted_layer
+
+    cfg = scaled(CONFIGS[4], family="mid", batch=2, cache_fmt="int2_g32_win")
+    W, lens = 128, [500, 90]
+    t_max = max(lens)
+    log(f"[int2-gqa] lens={lens} W={W}")
+    layer = gqa_converted_layer("gqa_mid", cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    shape = shape_of(cfg)
+    w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
+    cache = LatentCache.allocate(shape, len(lens), t_max, fill=float("nan"), window=W)
+    xs = [synth.context_x(cfg, b, L) for b, L in enumerate(lens)]
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for b, L in enumerate(lens):
+        xt = torch.from_numpy(xs[b].astype(np.float32)).cuda().to(torch_dtype(cfg)).reshape(1, L, -1)
+        append(w, cache.view(b, b + 1), xt, zero, 0)
+    q = np.stack([decode_query(cfg, layer, x[-1]) for x in xs])
+    qt = torch.from_numpy(q.astype(np.float32)).cuda().to(torch_dtype(cfg))
+    out = decode(w, cache, qt, torch.tensor(lens, dtype=torch.int32, device="cuda"), t_max)
+    torch.cuda.synchronize()
+    got = _np(out)
+    for b, L in enumerate(lens):
+        c, kr = oracle_cache(cfg, layer, xs[b])
+        c_bf, eff = _oracle_effective(c, W)
+        _check_int2_sequence(cache, b, c_bf, W)
+        ref = oracle.decode_ref(q[b], eff, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head, cfg.theta)
+        r, a = assert_close(got[b], ref, cfg.dtype, f"decode b={b}")
+        log(f"  b={b} L={L} rel-L2={r:.2e} max-abs={a:.2e}")
+
+
 def test_int2_decode_step_matches_separate_calls():
     """mla_decode_step on the 2-bit cache equals mla_cache_append_ws followed by mla_decode bit for bit (cache
     codes, (s, z), ring and output)."""

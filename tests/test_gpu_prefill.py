@@ -18,12 +18,13 @@ from parity_lib import assert_close, converted_layer, log, shape_of, torch_dtype
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill_case(cfg, S, B, rows=None, sample_b=None, variant=("2-norm", "joint")):
+def run_prefill_case(cfg, S, B, rows=None, sample_b=None, variant=("2-norm", "joint"), layer=None):
     from mla_latent_kv_cache_amd import LatentCache, append, pack_weights, prefill
 
     log(f"[prefill] family={cfg.family} r={cfg.r_pairs} d_kv={cfg.d_kv} B={B} S={S} "
-        f"rows={'all' if rows is None else rows} conversion={variant}")
-    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype, *variant)
+        f"rows={'all' if rows is None else rows} conversion={variant if layer is None else 'given'}")
+    if layer is None:
+        layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype, *variant)
     shape = shape_of(cfg)
     t_max = S + 3
     w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
@@ -83,6 +84,14 @@ def test_prefill_head_count_not_multiple_of_8():
 def test_prefill_ablation_variant_layers(strategy, svd):
     """Layers converted with the pages' ablation variants run through the same append and prefill kernels."""
     run_prefill_case(scaled(CONFIGS[2], family="mid"), S=300, B=2, variant=(strategy, svd))
+
+
+def test_prefill_gqa_source_layer():
+    """A layer converted from a grouped-query source (8 KV heads for 32 query heads) through append + prefill."""
+    from parity_lib import gqa_converted_layer
+
+    cfg = scaled(CONFIGS[2], family="mid")
+    run_prefill_case(cfg, S=300, B=2, layer=gqa_converted_layer("gqa_mid", cfg.r_pairs, cfg.d_kv, cfg.dtype))
 
 
 @pytest.mark.slow
