@@ -17,6 +17,7 @@ It is written from the method as the pages state it (Paper-Notes ACL2025 page
 * int4.py      -- group-32 absmax int4 codec of the latent (4-bit cache)
 * int2.py      -- group-32 affine 2-bit codec and the window of recent bf16 rows
                   (2-bit cache)
+* paged.py     -- page-table gather of a paged cache and multi-query (causal) decode
 * cache_bytes.py -- KV-cache bytes per token and the reduction percentages
 
 All floating point is fp64 except the int4 codec, which emulates IEEE fp32 /
@@ -48,4 +49,5 @@ from .attention import (  # noqa: F401
     rope_rotate,
 )
 from .int4 import dequant_int4, pack_nibbles, quantize_int4_g32, unpack_nibbles  # noqa: F401
+from .paged import gather_pages, multi_query_decode_ref  # noqa: F401
 from .cache_bytes import cache_bytes_per_token, mha_bytes_per_token, reduction_pct  # noqa: F401
