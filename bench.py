@@ -14,14 +14,15 @@ of mla_decode) separately: `--steps` back-to-back launches of it between two HIP
 
 The cpu_baseline object times the oracle (plain fp64 numpy; the library never uses it) on a bounded
 sample of the same workload on the host's cores.  Secondary workloads (long-context variable-length
-decode, int4-latent decode, 2-bit-latent decode with a 128-row bf16 window, causal prefill) are reported
+decode, int4-latent decode, 2-bit-latent decode with a 128-row bf16 window, the headline decode on a
+paged cache of 64-token pages in random order, a 4-query multi-query decode, causal prefill) are reported
 in `secondary`.
 
 `roofline.traffic` is the HBM traffic of one launch of that kernel from FETCH_SIZE / WRITE_SIZE counter
 runs (profiles/pmc_traffic.json, scaled by the counters of a plain copy of known size, see
 --copy-calibration); it is null when those counters were taken on different decode sources.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only c1,c3,c4,c5,c2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only c1,c3,c4,c5,c6,c7,c2] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -40,7 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode latent-cache GB/s (% of HBM peak); prefill MFMA TFLOP/s"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure (no sparsity)
-DOMINANT_KERNEL = "decode_attn_dma<128, 8, 3, 1>"
+DOMINANT_KERNEL = "decode_attn_dma<128, 8, 3, 1, false>"
 
 
 def log(msg):
@@ -52,7 +53,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="c1,c3,c4,c5,c2")
+    ap.add_argument("--only", default="c1,c3,c4,c5,c6,c7,c2")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -121,9 +122,10 @@ def converted(family, r, d_kv):
     return conv
 
 
-def make_decode_workload(cfg, conv, lens, copies, seed):
+def make_decode_workload(cfg, conv, lens, copies, seed, page_size=0):
     """Weights, `copies` filled caches (through mla_cache_append), the step's new-token activations, queries
-    and one BoundDecode per copy.  Activations are seeded N(0,1) generated on the device."""
+    and one BoundDecode per copy.  Activations are seeded N(0,1) generated on the device.  page_size > 0:
+    paged caches whose pages are a random permutation of the pool."""
     import torch
 
     from mla_latent_kv_cache_amd import BoundDecode, LatentCache, LayerShape, append, pack_weights
@@ -136,7 +138,12 @@ def make_decode_workload(cfg, conv, lens, copies, seed):
     g.manual_seed(seed)
     caches = []
     for c in range(copies):
-        cache = LatentCache.allocate(shape, B, t_max)
+        if page_size:
+            pps = (t_max + page_size - 1) // page_size
+            perm = torch.randperm(B * pps, generator=g, device="cuda").to(torch.int32).reshape(B, pps)
+            cache = LatentCache.allocate_paged(shape, perm, page_size, B * pps)
+        else:
+            cache = LatentCache.allocate(shape, B, t_max)
         for b in range(B):
             L = int(lens[b])
             x = torch.randn((1, L, cfg.d_model), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
@@ -199,6 +206,38 @@ def time_decode(wl, steps, warmup):
     torch.cuda.synchronize()
     k_ms = k0.elapsed_time(k1) / steps
     return step_ms, k_ms
+
+
+def multi_query_result(cfg, wl, q_len, steps, warmup):
+    """mla_decode_multi with q_len queries per sequence over the workload's caches (rotating copies), each
+    query causal: whole-call time (q-prep, attention, combine) and the cache bytes it covers once."""
+    import torch
+
+    from mla_latent_kv_cache_amd import decode_multi, decode_workspace_bytes
+
+    B = len(wl["lens"])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    q = (torch.randn((B, q_len, cfg.n_heads, cfg.d_head), generator=g, device="cuda") * 2).to(torch.bfloat16)
+    lens_t = torch.tensor(np.asarray(wl["lens"], dtype=np.int32), device="cuda")
+    t_max = int(max(wl["lens"]))
+    out = torch.empty_like(q)
+    ws = torch.empty(decode_workspace_bytes(wl["w"].shape, B * q_len, t_max), dtype=torch.uint8, device="cuda")
+    n = len(wl["caches"])
+    for i in range(warmup):
+        decode_multi(wl["w"], wl["caches"][i % n], q, lens_t, t_max, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        decode_multi(wl["w"], wl["caches"][i % n], q, lens_t, t_max, out=out, workspace=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    gbs = wl["bytes"] / (ms * 1e-3) / 1e9
+    log(f"[bench] multi-query decode, {q_len} queries x {B} sequences: {ms * 1e3:.1f} us per call -> {gbs:.0f} GB/s "
+        f"of cache covered once ({q_len * B / (ms * 1e-3):.0f} queries/s)")
+    return dict(call_ms=ms, q_len=q_len, gbs_cache_once=gbs, queries_per_s=q_len * B / (ms * 1e-3), bytes=wl["bytes"])
 
 
 def decode_result(name, cfg, wl, steps, warmup):
@@ -315,10 +354,20 @@ def main():
     cfg1 = C[1]
     wl1 = make_decode_workload(cfg1, conv_main, synth.seq_lens(cfg1), args.copies, seed=1001)
     main_res = decode_result("llama_bf16_decode", cfg1, wl1, args.steps, args.warmup)
+    secondary = {}
+    if "c7" in only:
+        secondary["llama_bf16_multiquery4"] = multi_query_result(cfg1, wl1, 4, args.steps, args.warmup)
     del wl1
     torch.cuda.empty_cache()
+    if "c6" in only:
+        wl6 = make_decode_workload(cfg1, conv_main, synth.seq_lens(cfg1), args.copies, seed=1006, page_size=64)
+        r6 = decode_result("llama_bf16_decode_paged64", cfg1, wl6, args.steps, args.warmup)
+        r6.update(hbm_frac=r6["kernel_gbs"] / HBM_PEAK_GBS, page_size=64,
+                  kernel="decode_attn_dma<128, 8, 3, 1, true>")
+        secondary["llama_bf16_decode_paged64"] = r6
+        del wl6
+        torch.cuda.empty_cache()
 
-    secondary = {}
     if "c3" in only:
         cfg3 = C[3]
         conv3 = converted("llama", 2, 256)

@@ -105,7 +105,16 @@ typedef struct {
  *                                             pos >= L - window (L = the sequence's length)
  *             window >= 0 (0: every row is codes); ckv_window may be NULL when window == 0
  *   all:      krope [batch, t_max, n_h, 2r]   config dtype, pair (j, c) of head h at index h*2r + 2j + c
- * ckv_window and window are read for INT2_G32_WIN only.                                          */
+ * ckv_window and window are read for INT2_G32_WIN only.
+ *
+ * Paged caches (block_table != NULL; DENSE and INT4_G32): ckv, ckv_scale and krope hold a pool of
+ * n_pages pages of page_size rows each (the row layouts above, n_pages * page_size rows in place of
+ * batch * t_max), and position pos of sequence b is pool row
+ *     block_table[b * pages_per_seq + pos / page_size] * page_size + pos % page_size.
+ * page_size is a multiple of 64; t_max must equal pages_per_seq * page_size; n_pages * page_size <= 2^31 - 1.
+ * block_table [batch, pages_per_seq] int32 (device, 4-byte aligned); entries are clamped to
+ * [0, n_pages), so a bad entry cannot make a kernel leave the pool.  Sequences may share pages (the
+ * multi-query decode below reads one sequence's pages from several queries).                    */
 typedef struct {
   void *ckv;
   void *ckv_scale;
@@ -114,6 +123,10 @@ typedef struct {
   int32_t t_max;
   void *ckv_window;
   int32_t window;
+  const int32_t *block_table; /* NULL: sequence b's position pos is row b * t_max + pos              */
+  int32_t page_size;
+  int32_t pages_per_seq;
+  int32_t n_pages;
 } mla_cache;
 
 /* ---------------------------------------------------------------- append
@@ -186,6 +199,19 @@ int mla_decode_step(const mla_config *cfg, const mla_weights *w, mla_cache *cach
                     const int32_t *start_pos, int32_t t_new, int32_t max_start_pos, const void *q,
                     const int32_t *seq_lens, int32_t max_seq_len, void *out, void *workspace, size_t ws_bytes,
                     hipStream_t stream);
+
+/* ---------------------------------------------------------------- multi-query decode
+ * q_len query tokens per sequence at once (e.g. tokens proposed for speculative decoding), each attending
+ * causally: with L_b cached tokens (the q_len new ones appended first), query i sits at position
+ * L_b - q_len + i and attends to positions 0 .. L_b - q_len + i; a query at a negative position gives a
+ * zero output row.  Same computation per query as mla_decode (q_len == 1 is mla_decode).
+ *   q    [batch, q_len, n_h, d_h] raw queries;   out [batch, q_len, n_h, d_h]
+ * DENSE and INT4_G32 caches, contiguous or paged (INT2_G32_WIN with q_len > 1: MLA_ERR_UNSUPPORTED).
+ * Workspace: mla_decode_multi_workspace_bytes(cfg, batch, q_len, max_seq_len) bytes.               */
+size_t mla_decode_multi_workspace_bytes(const mla_config *cfg, int32_t batch, int32_t q_len, int32_t max_seq_len);
+int mla_decode_multi(const mla_config *cfg, const mla_weights *w, const mla_cache *cache, const void *q, int32_t q_len,
+                     const int32_t *seq_lens, int32_t max_seq_len, void *out, void *workspace, size_t ws_bytes,
+                     hipStream_t stream);
 
 /* ---------------------------------------------------------------- prefill
  * Causal attention of seq_len query tokens per sequence, at positions 0..seq_len-1, over the

@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     append_workspace_bytes,
     append_ws,
     decode,
+    decode_multi,
     decode_phase,
     decode_step,
     decode_step_workspace_bytes,

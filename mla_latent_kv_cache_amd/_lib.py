@@ -19,6 +19,8 @@ EXPORTED = [
     "mla_decode_workspace_bytes",
     "mla_decode",
     "mla_decode_phase",
+    "mla_decode_multi_workspace_bytes",
+    "mla_decode_multi",
     "mla_decode_step_workspace_bytes",
     "mla_decode_step",
     "mla_prefill_workspace_bytes",
@@ -55,6 +57,10 @@ class MlaCache(ctypes.Structure):
         ("t_max", ctypes.c_int32),
         ("ckv_window", ctypes.c_void_p),
         ("window", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32),
+        ("pages_per_seq", ctypes.c_int32),
+        ("n_pages", ctypes.c_int32),
     ]
 
 
@@ -88,6 +94,10 @@ def load():
     lib.mla_decode.restype = ctypes.c_int
     lib.mla_decode_phase.argtypes = [ctypes.c_int, C, W, K, P, P, i32, P, P, sz, P]
     lib.mla_decode_phase.restype = ctypes.c_int
+    lib.mla_decode_multi_workspace_bytes.argtypes = [C, i32, i32, i32]
+    lib.mla_decode_multi_workspace_bytes.restype = sz
+    lib.mla_decode_multi.argtypes = [C, W, K, P, i32, P, i32, P, P, sz, P]
+    lib.mla_decode_multi.restype = ctypes.c_int
     lib.mla_decode_step_workspace_bytes.argtypes = [C, i32, i32, i32]
     lib.mla_decode_step_workspace_bytes.restype = sz
     lib.mla_decode_step.argtypes = [C, W, K, P, P, i32, i32, P, P, i32, P, P, sz, P]

@@ -136,6 +136,11 @@ class LatentCache:
     t_max: int
     ckv_window: Optional[torch.Tensor] = None
     window: int = 0
+    # paged caches: ckv / ckv_scale / krope are pools [n_pages, page_size, ...] and block_table [batch,
+    # pages_per_seq] int32 maps sequence b's page j to a pool page
+    block_table: Optional[torch.Tensor] = None
+    page_size: int = 0
+    n_pages: int = 0
 
     @staticmethod
     def allocate(shape: LayerShape, batch: int, t_max: int, device="cuda", fill: Optional[float] = None,
@@ -163,16 +168,45 @@ class LatentCache:
         return LatentCache(shape, ckv, scale, krope, batch, t_max, ring,
                            window if shape.cache_fmt == "int2_g32_win" else 0)
 
+    @staticmethod
+    def allocate_paged(shape: LayerShape, block_table: torch.Tensor, page_size: int, n_pages: int, device="cuda",
+                       fill: Optional[float] = None):
+        """A paged cache: pools of n_pages pages of page_size rows and the page table block_table [batch,
+        pages_per_seq] (int32, device); each sequence holds up to pages_per_seq * page_size tokens."""
+        if shape.cache_fmt == "int2_g32_win":
+            raise ValueError("paged caches hold dense or int4 latents")
+        batch, pps = block_table.shape
+        nr = shape.n_heads * 2 * shape.r_pairs
+        if shape.cache_fmt == "int4_g32":
+            ckv = torch.zeros((n_pages, page_size, shape.d_kv // 2), dtype=torch.uint8, device=device)
+            scale = torch.zeros((n_pages, page_size, shape.d_kv // 32), dtype=torch.float16, device=device)
+        else:
+            ckv = torch.empty((n_pages, page_size, shape.d_kv), dtype=shape.torch_dtype, device=device)
+            scale = None
+        krope = torch.empty((n_pages, page_size, max(nr, 1)), dtype=shape.torch_dtype, device=device)
+        if fill is not None:
+            if scale is None:
+                ckv.fill_(fill)
+            krope.fill_(fill)
+        return LatentCache(shape, ckv, scale, krope, batch, pps * page_size, None, 0,
+                           block_table.to(device=device, dtype=torch.int32).contiguous(), page_size, n_pages)
+
     def view(self, b0: int, b1: int) -> "LatentCache":
-        """The cache of sequences b0 .. b1-1 (views of the same memory)."""
+        """The cache of sequences b0 .. b1-1 (views of the same memory; a paged cache keeps its pools and
+        takes those sequences' page-table rows)."""
         sl = slice(b0, b1)
+        if self.block_table is not None:
+            return LatentCache(self.shape, self.ckv, self.ckv_scale, self.krope, b1 - b0, self.t_max, None, 0,
+                               self.block_table[sl], self.page_size, self.n_pages)
         return LatentCache(self.shape, self.ckv[sl], None if self.ckv_scale is None else self.ckv_scale[sl],
                            self.krope[sl], b1 - b0, self.t_max, None if self.ckv_window is None else self.ckv_window[sl],
                            self.window)
 
     def c(self) -> MlaCache:
+        pps = 0 if self.block_table is None else self.block_table.shape[1]
         return MlaCache(_ptr(self.ckv), _ptr(self.ckv_scale), _ptr(self.krope), self.batch, self.t_max,
-                        _ptr(self.ckv_window), self.window)
+                        _ptr(self.ckv_window), self.window, _ptr(self.block_table), self.page_size, pps,
+                        self.n_pages)
 
     def nbytes_per_token(self) -> int:
         """Bytes per cached position (the ring of an int2_g32_win cache is a fixed extra per sequence)."""
@@ -234,6 +268,23 @@ def decode(w: LayerWeights, cache: LatentCache, q: torch.Tensor, seq_lens: torch
     _check("mla_decode", lib.mla_decode(ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc), _ptr(q),
                                         _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(workspace),
                                         workspace.numel(), _stream(stream)))
+    return out
+
+
+def decode_multi(w: LayerWeights, cache: LatentCache, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """mla_decode_multi: q [batch, q_len, n_h, d_h] (query i of sequence b at position L_b - q_len + i) -> out."""
+    lib = _lib.load()
+    cfg, cw, cc = w.shape.c(), w.c(), cache.c()
+    q_len = q.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = lib.mla_decode_multi_workspace_bytes(ctypes.byref(cfg), cache.batch, q_len, int(max_seq_len))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check("mla_decode_multi", lib.mla_decode_multi(ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc), _ptr(q),
+                                                    q_len, _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(workspace),
+                                                    workspace.numel(), _stream(stream)))
     return out
 
 

@@ -67,6 +67,16 @@ int check_cache(const mla_config* c, const mla_cache* k) {
     if (k->window < 0) return MLA_ERR_INVALID_ARG;
     MLA_TRY(check_ptr(k->ckv_window, k->window > 0));
   }
+  if (k->block_table) {
+    if (((uintptr_t)k->block_table & 3u) != 0) return MLA_ERR_ALIGNMENT;
+    if (k->page_size <= 0 || k->page_size % 64 != 0 || k->pages_per_seq <= 0 || k->n_pages <= 0)
+      return MLA_ERR_INVALID_ARG;
+    if ((long long)k->pages_per_seq * k->page_size != k->t_max) return MLA_ERR_INVALID_ARG;
+    if ((long long)k->n_pages * k->page_size > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+    if (c->cache_fmt == MLA_CACHE_INT2_G32_WIN) return MLA_ERR_UNSUPPORTED;
+  } else if ((long long)k->batch * k->t_max > 0x7fffffffLL) {
+    return MLA_ERR_UNSUPPORTED;  // cache rows are indexed with 32-bit integers
+  }
   return MLA_OK;
 }
 
@@ -79,9 +89,16 @@ int check_positions(const mla_config* c, const mla_weights* w, const mla_cache* 
 
 int from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
-// The bf16 ring of the 2-bit format (nothing for the other formats).
+// The page table of a paged cache (nothing for a contiguous one).
+template <typename Args>
+void set_pages(Args& a, const mla_cache* k) {
+  if (!k->block_table) return;
+  a.pm = mla::PageMap{k->block_table, k->page_size, k->pages_per_seq, k->n_pages};
+}
+// The bf16 ring of the 2-bit format (nothing for the other formats), and the page table.
 template <typename Args>
 void set_window(Args& a, const mla_config* c, const mla_cache* k) {
+  set_pages(a, k);
   if (c->cache_fmt != MLA_CACHE_INT2_G32_WIN) return;
   a.ckv_win = k->ckv_window;
   a.win = k->window;
@@ -157,29 +174,32 @@ size_t mla_decode_workspace_bytes(const mla_config* cfg, int32_t batch, int32_t 
 
 static int decode_impl(int phase_mask, const mla_config* cfg, const mla_weights* w, const mla_cache* cache,
                        const void* q, const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace,
-                       size_t ws_bytes, hipStream_t stream) {
+                       size_t ws_bytes, hipStream_t stream, int q_len = 1) {
   MLA_TRY(check_config(cfg));
   MLA_TRY(check_weights(cfg, w, false, true));
   MLA_TRY(check_cache(cfg, cache));
-  if (max_seq_len < 0) return MLA_ERR_INVALID_ARG;
+  if (max_seq_len < 0 || q_len < 1) return MLA_ERR_INVALID_ARG;
+  if (q_len > 1 && cfg->cache_fmt == MLA_CACHE_INT2_G32_WIN) return MLA_ERR_UNSUPPORTED;
   if (cache->batch == 0) return MLA_OK;
   MLA_TRY(check_ptr(q, true));
   MLA_TRY(check_ptr(seq_lens, true));
   MLA_TRY(check_ptr(out, true));
   MLA_TRY(check_positions(cfg, w, cache, max_seq_len));
-  // the kernels count the batch's tokens in 32-bit integers
-  if ((long long)cache->batch * max_seq_len >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
+  // the kernels count the batch's queries and tokens in 32-bit integers
+  const long long nq = (long long)cache->batch * q_len;
+  if (nq * (max_seq_len > 0 ? max_seq_len : 1) >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
   const Shape s = shape_of(cfg);
-  const mla::DecodePlan plan = mla::plan_decode(s, cache->batch, max_seq_len);
+  const mla::DecodePlan plan = mla::plan_decode(s, (int)nq, max_seq_len);
   if (!mla::decode_fits(s, plan)) return MLA_ERR_UNSUPPORTED;
   // the specialised kernel addresses one sequence's cache rows with 32-bit byte offsets
   if (mla::decode_uses_mfma(s) && (size_t)cache->t_max * s.d_kv * 2 >= ((size_t)1 << 31)) return MLA_ERR_UNSUPPORTED;
   if (!workspace || ws_bytes < plan.total) return MLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
   mla::DecodeArgs a{s, q, w->w_uk, w->w_uv, w->pair_idx, w->rope_cos, w->rope_sin,
-                    cache->ckv, cache->ckv_scale, cache->krope, cache->batch, cache->t_max, max_seq_len,
+                    cache->ckv, cache->ckv_scale, cache->krope, (int)nq, cache->t_max, max_seq_len,
                     seq_lens, out, (char*)workspace, plan};
   set_window(a, cfg, cache);
+  a.qn = q_len;
   return from_hip(mla::launch_decode(a, stream, phase_mask));
 }
 
@@ -187,6 +207,18 @@ int mla_decode(const mla_config* cfg, const mla_weights* w, const mla_cache* cac
                const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace, size_t ws_bytes,
                hipStream_t stream) {
   return decode_impl(7, cfg, w, cache, q, seq_lens, max_seq_len, out, workspace, ws_bytes, stream);
+}
+
+size_t mla_decode_multi_workspace_bytes(const mla_config* cfg, int32_t batch, int32_t q_len, int32_t max_seq_len) {
+  if (check_config(cfg) != MLA_OK || batch < 0 || q_len < 1 || max_seq_len < 0) return 0;
+  if ((long long)batch * q_len > 0x7fffffffLL) return 0;
+  return mla::plan_decode(shape_of(cfg), batch * q_len, max_seq_len).total;
+}
+
+int mla_decode_multi(const mla_config* cfg, const mla_weights* w, const mla_cache* cache, const void* q, int32_t q_len,
+                     const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace, size_t ws_bytes,
+                     hipStream_t stream) {
+  return decode_impl(7, cfg, w, cache, q, seq_lens, max_seq_len, out, workspace, ws_bytes, stream, q_len);
 }
 
 int mla_decode_phase(int phase, const mla_config* cfg, const mla_weights* w, const mla_cache* cache,
@@ -270,6 +302,7 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const mla_cache* ca
   if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
   mla::PrefillArgs a{s, q, w->w_uk, w->w_uv, w->pair_idx, w->rope_cos, w->rope_sin, cache->ckv, cache->krope,
                      cache->batch, cache->t_max, seq_len, out, (char*)workspace, plan};
+  set_pages(a, cache);
   return from_hip(mla::launch_prefill(a, stream));
 }
 

@@ -79,6 +79,7 @@ constexpr int TM = 128, TN = 128, TK = 64, PITCH = TK + 8;
 __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sA[2][TM * PITCH];
   __shared__ __attribute__((aligned(16))) bf16 sB[2][TN * PITCH];
+  __shared__ int rows[TM], poss[TM];  // cache row and position of every token of the tile
   const int K = a.s.d_model, D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR;
   const int M = a.batch * a.t_new;
   const int n_tiles = (N + TN - 1) / TN;
@@ -88,6 +89,11 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
   const int m0 = (bid / n_tiles) * TM, n0 = (bid % n_tiles) * TN;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (tid < TM && m0 + tid < M) {
+    int pos;
+    rows[tid] = cache_row(a, m0 + tid, &pos);
+    poss[tid] = pos;
+  }  // read in the epilogue, after the main loop's barriers
   const int wm = wid >> 1, wn = wid & 1;
   const bf16* x = (const bf16*)a.x;
   const bf16* wd = (const bf16*)a.w_dkv;
@@ -170,9 +176,7 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
     for (int idx = threadIdx.x; idx < TM * ng; idx += blockDim.x) {
       const int ml = idx / ng, g = idx - ml * ng, m = m0 + ml;
       if (m >= M) continue;
-      int pos;
-      cache_row(a, m, &pos);
-      store_group_win2(a, m / a.t_new, pos, n0 / 32 + g, (ml < 64 ? stg0 : stg1) + (ml & 63) * SP + 32 * g, 1);
+      store_group_win2(a, m / a.t_new, poss[ml], n0 / 32 + g, (ml < 64 ? stg0 : stg1) + (ml & 63) * SP + 32 * g, 1);
     }
   }
 #pragma unroll
@@ -186,12 +190,8 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
         if (a.s.fmt == 0) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            if (m < M) {
-              int pos;
-              size_t row = (size_t)cache_row(a, m, &pos);
-              ((bf16*)a.ckv)[row * D + n] = (bf16)acc[i][j][e];
-            }
+            const int ml = wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            if (m0 + ml < M) ((bf16*)a.ckv)[(size_t)rows[ml] * D + n] = (bf16)acc[i][j][e];
           }
         } else if (a.s.fmt == 2) {
           // staged through LDS below
@@ -205,10 +205,9 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
             __half s = int4_scale(am);
             int code = int4_code(v, __half2float(s));
             int partner = __shfl_xor(code, 1, 64);
-            int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            if (m < M) {
-              int pos;
-              size_t row = (size_t)cache_row(a, m, &pos);
+            const int ml = wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            if (m0 + ml < M) {
+              const size_t row = (size_t)rows[ml];
               if ((lane & 1) == 0)
                 ((uint8_t*)a.ckv)[row * (D / 2) + (n >> 1)] = (uint8_t)((code & 15) | ((partner & 15) << 4));
               if ((lane & 31) == 0) ((__half*)a.ckv_scale)[row * (D / 32) + (n >> 5)] = s;
@@ -225,10 +224,10 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
         for (int e = 0; e < 16; ++e) {
           float v = acc[i][j][e];
           float partner = shfl_xor(v, 1);
-          int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          if (m < M && colok) {
-            int pos;
-            size_t row = (size_t)cache_row(a, m, &pos);
+          const int ml = wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          if (m0 + ml < M && colok) {
+            const int pos = poss[ml];
+            const size_t row = (size_t)rows[ml];
             float cs = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
             float x0 = comp ? partner : v, x1 = comp ? v : partner;
             float o = comp ? (x0 * sn + x1 * cs) : (x0 * cs - x1 * sn);

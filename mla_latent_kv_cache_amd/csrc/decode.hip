@@ -27,9 +27,22 @@ constexpr int QB = 16;     // batch rows per qprep workgroup (QB * d_nope <= 4 *
 constexpr int MLS = 4;     // floats per (work item, head) entry of the split statistics: m, l, A, unused
 constexpr int MAX_DH = 256;
 
+// Cache sequence read by query sequence b (several queries per cache sequence in multi-query decode).
+__device__ __forceinline__ int cseq(const DecodeArgs& a, int b) { return a.qn > 1 ? b / a.qn : b; }
+// Keys visible to query sequence b: its cache sequence's length (clamped to the host bound), less the
+// newer queries of the same sequence.
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
-  int L = a.seq_lens[b];
-  return L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  int L = a.seq_lens[cseq(a, b)];
+  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  if (a.qn > 1) {
+    L -= a.qn - 1 - b % a.qn;
+    L = L < 0 ? 0 : L;
+  }
+  return L;
+}
+// Cache row of position pos of query sequence b (contiguous or through the page table).
+__device__ __forceinline__ int seq_row(const DecodeArgs& a, int b, int pos) {
+  return cache_row_of(a.pm, a.t_max, cseq(a, b), pos);
 }
 
 // ------------------------------------------------------------------ work split (see DecodePlan)
@@ -303,8 +316,8 @@ __global__ __launch_bounds__(256) void decode_step_prologue(AppendArgs aa, int k
 // window, else fp32(z + code * s) of the coded row.
 __device__ __forceinline__ float latent2(const DecodeArgs& a, int b, int pos, bool win, int k) {
   const int D = a.s.d_kv;
-  if (win) return (float)((const bf16*)a.ckv_win)[((size_t)b * a.win + pos % a.win) * D + k];
-  const size_t row = (size_t)b * a.t_max + pos;
+  if (win) return (float)((const bf16*)a.ckv_win)[((size_t)cseq(a, b) * a.win + pos % a.win) * D + k];
+  const size_t row = (size_t)seq_row(a, b, pos);
   const uint32_t byte = ((const uint8_t*)a.ckv)[row * (D / 4) + (k >> 2)];
   const uint32_t m = ((const uint32_t*)a.ckv_scale)[row * (D / 32) + (k >> 5)];
   const float sc = __half2float(__ushort_as_half((unsigned short)(m & 0xFFFF)));
@@ -353,11 +366,10 @@ __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
   float* po = (float*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * NH * D;
   const T* qt = (const T*)(a.ws + a.plan.off_qt) + (size_t)b * NH * D;
   const float* qr = (const float*)(a.ws + a.plan.off_qr) + (size_t)b * NH * R2;
-  const size_t rowb = (size_t)b * a.t_max;
   // element k of the latent at position pos (from the window when `win`)
   auto lat = [&](int pos, bool win, int k) {
     if constexpr (FMT == 2) return latent2(a, b, pos, win, k);
-    else return latent<T, FMT>(a, rowb + pos, k);
+    else return latent<T, FMT>(a, (size_t)seq_row(a, b, pos), k);
   };
   for (int h = 0; h < NH; ++h) {
     for (int k = threadIdx.x; k < D; k += blockDim.x) qs[k] = to_f32(qt[(size_t)h * D + k]);
@@ -373,7 +385,7 @@ __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
         for (int t = threadIdx.x; t < n; t += blockDim.x) {
           float s = 0.f;
           for (int k = 0; k < D; ++k) s = fmaf(qs[k], lat(r0 + t, win, k), s);
-          const T* kr = (const T*)a.krope + ((rowb + r0 + t) * NH + h) * R2;
+          const T* kr = (const T*)a.krope + ((size_t)seq_row(a, b, r0 + t) * NH + h) * R2;
           for (int j = 0; j < R2; ++j) s = fmaf(qrs[j], to_f32(kr[j]), s);
           sc[t] = s;
           mloc = fmaxf(mloc, s);
@@ -479,7 +491,7 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, const f32x16 
 // Lane l owns head l%32 in both products, so the per-head max / sum / rescale stay in registers
 // (one cross-half shuffle).  The next tile's rows and RoPE keys are prefetched into registers.  The
 // dense 512-wide variant needs more than 256 registers per lane and runs at one wave per SIMD.
-template <int DW, int R2, int FMT>
+template <int DW, int R2, int FMT, bool PG>
 __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_attn_mfma(DecodeArgs a, FuseArgs f) {
   constexpr int CP = DW + 16;  // LDS row pitch in elements (conflict-free b128 and transpose reads)
   constexpr int NS = DW / 16;  // score k-steps per wave
@@ -519,8 +531,10 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   for (int i = 0; i < NB; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const size_t rowb = (size_t)b * a.t_max;
-  const bf16* krb = (const bf16*)a.krope + rowb * 32 * R2;
+  // a tile's 32 rows are consecutive cache rows (a page holds a multiple of 64 positions and tiles start
+  // at multiples of 32 from the item's start), so a paged cache (PG) needs one row lookup per tile
+  const size_t rowb = (size_t)cseq(a, b) * a.t_max;
+  const bf16* krb = (const bf16*)a.krope;
   bf16* cw = cbuf[w];
 
   // ---- register prefetch, two tiles deep: this wave's latent slice and its share of the RoPE keys
@@ -550,10 +564,13 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   auto load_tile = [&](auto bsel, auto winsel, int tt) {
     constexpr int B = decltype(bsel)::value;
     constexpr bool WIN = decltype(winsel)::value;
+    // row0: the tile's first row (paged) or the sequence's (contiguous); tb: the tile's offset from it
+    const size_t row0 = PG ? (size_t)__builtin_amdgcn_readfirstlane(seq_row(a, b, tt)) : rowb;
+    const int tb = PG ? 0 : tt;
     if (tt + 32 <= t1) {
-      const char* cb = (const char*)a.ckv + (rowb + tt) * RBY;
-      const char* sb = (const char*)a.ckv_scale + (rowb + tt) * (D / 32) * MBY;
-      const char* kb = (const char*)krb + (size_t)tt * 32 * R2 * 2 + koff;
+      const char* cb = (const char*)a.ckv + (row0 + tb) * RBY;
+      const char* sb = (const char*)a.ckv_scale + (row0 + tb) * (D / 32) * MBY;
+      const char* kb = (const char*)(krb + row0 * 32 * R2) + (size_t)tb * 32 * R2 * 2 + koff;
       if constexpr (!WIN) {
 #pragma unroll
         for (int it = 0; it < CCH; ++it) {
@@ -570,8 +587,8 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
       for (int it = 0; it < CCH; ++it) {
         const int row = (it * 64 + lane) / CPR;
         const int tok = min(tt + row, t1 - 1);  // rows past the sequence repeat its last row (masked below)
-        const char* cb = (const char*)a.ckv + (rowb + tok) * RBY;
-        const char* sb = (const char*)a.ckv_scale + (rowb + tok) * (D / 32) * MBY;
+        const char* cb = (const char*)a.ckv + (row0 + tok - tt + tb) * RBY;
+        const char* sb = (const char*)a.ckv_scale + (row0 + tok - tt + tb) * (D / 32) * MBY;
         creg[B][it] = *(const u32x4*)(cb + coff[it] - row * RBY);
         if constexpr (FMT != 0) sreg[B][it] = *(const meta_t*)(sb + soff[it] - MBY * row * (D / 32));
       }
@@ -579,7 +596,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int tok = min(tt + 8 * w + 4 * hb + i, t1 - 1);
-      kreg[B][i] = *(const kv_t*)(krb + ((size_t)tok * 32 + h) * R2);
+      kreg[B][i] = *(const kv_t*)(krb + row0 * 32 * R2 + ((size_t)(tok - tt + tb) * 32 + h) * R2);
     }
   };
   auto stage_tile = [&](auto bsel) {
@@ -784,7 +801,7 @@ __device__ __forceinline__ int slice_off(int row, int col) {
 
 // NSLOT tile slots in the DMA ring (2: one tile in flight while one is used; 3: two in flight), NSB
 // buffers for the cross-wave exchange of partial scores (2 saves one barrier per tile).
-template <int DW, int R2, int NSLOT, int NSB>
+template <int DW, int R2, int NSLOT, int NSB, bool PG>
 __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs f) {
   constexpr int NS = DW / 16, NB = DW / 32, D = 4 * DW;
   constexpr int CSL = 32 * DW * 2;       // bytes of one wave's latent slice of a tile
@@ -819,11 +836,15 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
   }
 
   // DMA addresses: a wave-uniform tile base (SGPRs) plus per-lane offsets that do not change per tile
-  const size_t rowb = (size_t)b * a.t_max;
+  // a tile's 32 rows are consecutive cache rows (pages hold multiples of 64 positions, tiles start at
+  // multiples of 32 from the item's start): a paged cache (PG) needs one row lookup per tile, then
+  // per-lane offsets from it
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  const size_t rowb = (size_t)cseq(a, b) * a.t_max;
+  // contiguous cache: the sequence's bases, a tile at a fixed offset from them
   const char* cbase = (const char*)a.ckv + (rowb * D + wu * DW) * 2;
-  const char* kseq = (const char*)a.krope + rowb * 32 * R2 * 2;  // this sequence's RoPE rows
-  const char* kbase = kseq + 8 * wu * 32 * R2 * 2;                 // ... from the wave's first row
+  const char* kseq = (const char*)a.krope + rowb * 32 * R2 * 2;
+  const char* kbase = kseq + 8 * wu * 32 * R2 * 2;
   uint32_t coff[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
@@ -834,29 +855,43 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
   const uint32_t k_lds[3] = {lds_addr_of(ks0) + wu * KSL, lds_addr_of(ks1) + wu * KSL, lds_addr_of(ks2) + wu * KSL};
   auto issue_slot = [&](auto ssel, int tt) {
     constexpr int SL = decltype(ssel)::value;
+    // bases: the tile's rows (paged) or the sequence's rows (contiguous); tb = the tile's first position
+    // relative to the base
+    const char *cb0, *kt;
+    int tb;
+    if constexpr (PG) {
+      const size_t prow = (size_t)__builtin_amdgcn_readfirstlane(seq_row(a, b, tt));
+      cb0 = (const char*)a.ckv + (prow * D + wu * DW) * 2;
+      kt = (const char*)a.krope + prow * (32 * R2 * 2);
+      tb = 0;
+    } else {
+      cb0 = cbase;
+      kt = kseq;
+      tb = tt;
+    }
     if (tt + 32 <= t1) {
-      const char* cb = cbase + (size_t)tt * (D * 2);
+      const char* cb = cb0 + (size_t)tb * (D * 2);
 #pragma unroll
       for (int j = 0; j < NC; ++j) dma16(cb, coff[j], c_lds[SL] + 1024 * j);
     } else {  // last, partial tile: rows past the sequence repeat its last row (masked later)
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int off = 1024 * j + 16 * lane, row = off / RB;
-        const int tok = min(tt + row, t1 - 1);
-        dma16(cbase, (uint32_t)(tok * (D * 2) + 16 * swz<DW>(row, (off % RB) / 16)), c_lds[SL] + 1024 * j);
+        const int tok = min(tt + row, t1 - 1) - tt + tb;
+        dma16(cb0, (uint32_t)(tok * (D * 2) + 16 * swz<DW>(row, (off % RB) / 16)), c_lds[SL] + 1024 * j);
       }
     }
     // the wave's RoPE rows 8w .. 8w+7 of the tile are one contiguous block
     if (tt + 8 * wu + 8 <= t1) {
-      const char* kb = kbase + (size_t)tt * (32 * R2 * 2);
+      const char* kb = (PG ? kt + 8 * wu * 32 * R2 * 2 : kbase) + (size_t)tb * (32 * R2 * 2);
 #pragma unroll
       for (int j = 0; j < NK; ++j) dma16(kb, (uint32_t)(1024 * j + 16 * lane), k_lds[SL] + 1024 * j);
     } else {
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
         const int off = 1024 * j + 16 * lane, tk = off / (64 * R2), within = off % (64 * R2);
-        const int tok = min(tt + 8 * wu + tk, t1 - 1);  // absolute position, >= 0
-        dma16(kseq, (uint32_t)(tok * (64 * R2) + within), k_lds[SL] + 1024 * j);
+        const int tok = min(tt + 8 * wu + tk, t1 - 1) - tt + tb;  // row relative to the base, >= 0
+        dma16(kt, (uint32_t)(tok * (64 * R2) + within), k_lds[SL] + 1024 * j);
       }
     }
   };
@@ -1077,7 +1112,7 @@ __device__ __forceinline__ bf16x8 dequant8v(uint32_t wd, const float* s) {
   return r;
 }
 
-template <int D, int R2, int FMT, int NSLOT>
+template <int D, int R2, int FMT, int NSLOT, bool PG>
 __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a, FuseArgs f) {
   using W = WaveTile<D, R2, FMT, NSLOT>;
   constexpr int TT = W::TT, SWM = W::SWM;
@@ -1104,10 +1139,9 @@ __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a, FuseArg
   char* pscr = mine + NSLOT * W::SLOT;  // P^T [32 heads][16 tokens]
   char* stp = pscr + W::PS;             // scales [group][16 tokens] (int4)
   const uint32_t mine_lds = lds_addr_of(mine);
-  const size_t rowb = (size_t)b * a.t_max;
-  const char* lat = (const char*)a.ckv + rowb * W::RB;
-  const char* scl = FMT == 1 ? (const char*)a.ckv_scale + rowb * W::SRB : (const char*)a.ckv;
-  const char* kro = (const char*)a.krope + rowb * W::KRB;
+  // a tile's TT rows are consecutive cache rows (pages hold multiples of 64 positions; tiles start at
+  // multiples of TT from the item's start): a paged cache (PG) needs one row lookup per tile
+  const size_t rowb = (size_t)cseq(a, b) * a.t_max;
   // tile j of the wave -> slot j % NSLOT; rows past the wave's range repeat its last row (masked later)
   auto issue = [&](int j) {
     // per-lane offsets are recomputed at every call (an opaque copy of the lane id keeps the compiler
@@ -1117,24 +1151,30 @@ __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a, FuseArg
     const int tt = u0 + TT * j;
     const uint32_t base = mine_lds + (j % NSLOT) * W::SLOT;
     const int last = u1 - 1;
+    size_t prow;
+    if constexpr (PG) prow = (size_t)__builtin_amdgcn_readfirstlane(seq_row(a, b, tt));
+    else prow = rowb + tt;
+    const char* lat = (const char*)a.ckv + prow * W::RB;
+    const char* scl = FMT == 1 ? (const char*)a.ckv_scale + prow * W::SRB : (const char*)a.ckv;
+    const char* kro = (const char*)a.krope + prow * W::KRB;
 #pragma unroll
     for (int i = 0; i < W::NL; ++i) {
       const int off = 1024 * i + 16 * lane, row = off / W::RB, pos = (off % W::RB) / 16;
       const int tok = min(tt + row, last);
-      dma16(lat, (uint32_t)(tok * W::RB + 16 * (pos ^ (row & SWM))), base + 1024 * i);
+      dma16(lat, (uint32_t)((tok - tt) * W::RB + 16 * (pos ^ (row & SWM))), base + 1024 * i);
     }
 #pragma unroll
     for (int i = 0; i < W::NSC; ++i) {
       constexpr int SRB1 = W::SRB > 0 ? W::SRB : 1;  // (no scale rows for bf16 latents: NSC == 0)
       const int off = 256 * i + 4 * lane, row = off / SRB1, within = off % SRB1;
       const int tok = min(tt + row, last);
-      dma4(scl, (uint32_t)(tok * W::SRB + within), base + W::LB + 256 * i);
+      dma4(scl, (uint32_t)((tok - tt) * W::SRB + within), base + W::LB + 256 * i);
     }
 #pragma unroll
     for (int i = 0; i < W::NK; ++i) {
       const int off = 1024 * i + 16 * lane, row = off / W::KRB, within = off % W::KRB;
       const int tok = min(tt + row, last);
-      dma16(kro, (uint32_t)(tok * W::KRB + within), base + W::LB + W::SB + 1024 * i);
+      dma16(kro, (uint32_t)((tok - tt) * W::KRB + within), base + W::LB + W::SB + 1024 * i);
     }
   };
   constexpr int PF = NSLOT - 1;  // tiles in flight ahead of the one being computed
@@ -1465,7 +1505,10 @@ inline dim3 attn_grid(const DecodeArgs& a, const FuseArgs& f) { return dim3(a.pl
 
 template <int D, int R2, int FMT, int NSLOT>
 void launch_wave_attn(const DecodeArgs& a, const FuseArgs& f, hipStream_t st) {
-  hipLaunchKernelGGL((decode_attn_wave<D, R2, FMT, NSLOT>), attn_grid(a, f), dim3(256), 0, st, a, f);
+  if (a.pm.bt)
+    hipLaunchKernelGGL((decode_attn_wave<D, R2, FMT, NSLOT, true>), attn_grid(a, f), dim3(256), 0, st, a, f);
+  else
+    hipLaunchKernelGGL((decode_attn_wave<D, R2, FMT, NSLOT, false>), attn_grid(a, f), dim3(256), 0, st, a, f);
 }
 
 // ------------------------------------------------------------------ 3. combine: merge, then W_uv
@@ -1790,11 +1833,17 @@ void launch_generic_attn(const DecodeArgs& a, hipStream_t st) {
 template <int DW, int R2>
 void launch_mfma_attn(const DecodeArgs& a, const FuseArgs& f, hipStream_t st) {
   if (a.s.fmt == 0)
-    hipLaunchKernelGGL((decode_attn_dma<DW, R2, 3, (DW == 128 && R2 == 8) ? 1 : 2>), attn_grid(a, f), dim3(256), 0, st, a, f);
+    if (a.pm.bt)
+      hipLaunchKernelGGL((decode_attn_dma<DW, R2, 3, (DW == 128 && R2 == 8) ? 1 : 2, true>), attn_grid(a, f), dim3(256), 0, st, a, f);
+    else
+      hipLaunchKernelGGL((decode_attn_dma<DW, R2, 3, (DW == 128 && R2 == 8) ? 1 : 2, false>), attn_grid(a, f), dim3(256), 0, st, a, f);
   else if (a.s.fmt == 1)
-    hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 1>), attn_grid(a, f), dim3(256), 0, st, a, f);
+    if (a.pm.bt)
+      hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 1, true>), attn_grid(a, f), dim3(256), 0, st, a, f);
+    else
+      hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 1, false>), attn_grid(a, f), dim3(256), 0, st, a, f);
   else
-    hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 2>), attn_grid(a, f), dim3(256), 0, st, a, f);
+    hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 2, false>), attn_grid(a, f), dim3(256), 0, st, a, f);  // never paged
 }
 
 }  // namespace
@@ -1877,7 +1926,7 @@ hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, hipStr
   const int n_qp = da.s.n_heads * (da.s.d_kv / 128) * ((da.batch + 31) / 32);
   hipLaunchKernelGGL(decode_step_prologue, dim3(nx * ks + n_qp), dim3(256), 0, st, aa, ks, da);
   // the split-K reduction runs inside the attention launch when its kernel takes it
-  if (aa.t_new <= FUSE_MAXR && attn_takes_append(da.s)) {
+  if (aa.t_new <= FUSE_MAXR && attn_takes_append(da.s) && !aa.pm.bt) {
     FuseArgs f{aa, ks};
     return launch_decode(da, st, 2 | 4, &f);
   }

@@ -17,6 +17,19 @@ struct Shape {
   __host__ __device__ int n_rope_cols() const { return n_heads * 2 * r_pairs; }
 };
 
+// Where the rows of a cache sequence live: contiguous (b * t_max + pos) when bt is null, else through a
+// page table [sequences, pps] of page ids (clamped to [0, n_pages)) over a pool of `page`-row pages.
+struct PageMap {
+  const int32_t* bt;
+  int page, pps, n_pages;
+};
+__device__ __forceinline__ int cache_row_of(const PageMap& pm, int t_max, int cb, int pos) {
+  if (!pm.bt) return cb * t_max + pos;
+  int pg = pm.bt[(size_t)cb * pm.pps + pos / pm.page];
+  pg = pg < 0 ? 0 : (pg >= pm.n_pages ? pm.n_pages - 1 : pg);
+  return pg * pm.page + pos % pm.page;
+}
+
 struct AppendArgs {
   Shape s;
   const void *x, *w_dkv, *w_krope;
@@ -28,6 +41,7 @@ struct AppendArgs {
   char* ws = nullptr;  // optional workspace (few-token appends split the model width over workgroups)
   void* ckv_win = nullptr;  // fmt 2: ring of the last `win` rows per sequence [batch, win, d_kv] bf16
   int win = 0;
+  PageMap pm{};
 };
 
 // Few-token append with a workspace: number of model-width slices and the workspace it needs
@@ -64,6 +78,10 @@ struct DecodeArgs {
   DecodePlan plan;
   const void* ckv_win = nullptr;  // fmt 2: ring of the last `win` rows per sequence [batch, win, d_kv] bf16
   int win = 0;
+  PageMap pm{};
+  // queries per cache sequence: `batch` counts queries, query v reads cache sequence v / qn with
+  // length seq_lens[v / qn] - (qn - 1 - v % qn) (multi-query decode; 1 otherwise)
+  int qn = 1;
 };
 
 // Prefill workspace: K [b, h, s_pad, 128] and V^T [b, h, 128, s_pad] bf16, s_pad = seq_len rounded up
@@ -84,6 +102,7 @@ struct PrefillArgs {
   void* out;
   char* ws;
   PrefillPlan plan;
+  PageMap pm{};
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);  // uses a.ws when set and useful

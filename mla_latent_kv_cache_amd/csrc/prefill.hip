@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256, 2) void rec_k_gemm(PrefillArgs a, int M) {
   {
     const int m = m0 + tid;
     const int b = m / S, t = m - b * S;
-    crow[tid] = m < M ? b * a.t_max + t : -1;
+    crow[tid] = m < M ? cache_row_of(a.pm, a.t_max, b, t) : -1;
     orow[tid] = m < M ? (b * NH + hh) * SP + t : -1;
   }
   build_nope_idx(a.pair_idx, hh, r, 64, kept, dim_of);
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void rec_vt_gemm(PrefillArgs a, int N) {
   const int tid = threadIdx.x;
   {
     const int n = min(n0 + tid, N - 1), b = n / SP, t = n - b * SP;
-    crow[tid] = b * a.t_max + min(t, S - 1);
+    crow[tid] = cache_row_of(a.pm, a.t_max, b, min(t, S - 1));
     if (tid < 32) {
       const int nc = n0 + 8 * tid, bc = nc / SP, tc = nc - bc * SP;
       orow[tid] = nc < N ? ((size_t)(bc * NH + hh) * 128) * SP + tc : ~(size_t)0;

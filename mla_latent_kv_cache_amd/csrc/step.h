@@ -11,7 +11,8 @@ namespace mla {
 constexpr int SM_MAXM = 64;  // few-token appends: at most 64 tokens (two 32-row MFMA blocks)
 constexpr int KS_MAX = 16;   // model-width slices of the split-K append
 
-// Cache row and position of token m of an append (t_new consecutive tokens per sequence).
+// Cache row (contiguous or through the page table) and position of token m of an append (t_new
+// consecutive tokens per sequence).
 __device__ __forceinline__ int cache_row(const AppendArgs& a, int m, int* pos_out) {
   int b = m / a.t_new;
   int i = m - b * a.t_new;
@@ -19,7 +20,7 @@ __device__ __forceinline__ int cache_row(const AppendArgs& a, int m, int* pos_ou
   sp = sp < 0 ? 0 : (sp > a.max_start ? a.max_start : sp);
   int pos = sp + i;
   *pos_out = pos;
-  return b * a.t_max + pos;
+  return cache_row_of(a.pm, a.t_max, b, pos);
 }
 
 // Output elements of the append epilogue, one function per kind so that every path that writes cache
@@ -100,7 +101,7 @@ __device__ __forceinline__ void store_group_win2(const AppendArgs& a, int b, int
   float v[32];
   for (int c = 0; c < 32; ++c) v[c] = (float)(bf16)vals[c * stride];
   if (pos < sp + a.t_new - W) {
-    store_group2(a, (size_t)b * a.t_max + pos, g, v);
+    store_group2(a, (size_t)cache_row_of(a.pm, a.t_max, b, pos), g, v);
     return;
   }
   const int slot = pos % W;
@@ -109,7 +110,7 @@ __device__ __forceinline__ void store_group_win2(const AppendArgs& a, int b, int
   if (p_old >= 0) {
     float o[32];
     for (int c = 0; c < 32; ++c) o[c] = (float)ring[c];
-    store_group2(a, (size_t)b * a.t_max + p_old, g, o);
+    store_group2(a, (size_t)cache_row_of(a.pm, a.t_max, b, p_old), g, o);
   }
   for (int c = 0; c < 32; ++c) ring[c] = (bf16)v[c];
 }
@@ -147,7 +148,7 @@ __device__ __forceinline__ void store_lane_win2(const AppendArgs& a, bool ok, in
   const int code = int2_code(x, z, sc);
   const int c1 = __shfl_xor(code, 1, 64), c2 = __shfl_xor(code, 2, 64), c3 = __shfl_xor(code, 3, 64);
   if (direct || evict) {
-    const size_t row = (size_t)b * a.t_max + (direct ? pos : p_old);
+    const size_t row = (size_t)cache_row_of(a.pm, a.t_max, b, direct ? pos : p_old);
     if ((c & 3) == 0)
       ((uint8_t*)a.ckv)[row * (D / 4) + 8 * g + (c >> 2)] = (uint8_t)(code | (c1 << 2) | (c2 << 4) | (c3 << 6));
     if (c == 0)
@@ -197,7 +198,8 @@ __device__ __forceinline__ void append_epilogue(const AppendArgs& a, const float
 // Split-K append, phase 2 for the tokens of sequence b at cache positions [p_lo, p_hi) (at most
 // FUSE_MAXR, all of them new tokens of this append): each output column's KS partial sums are added in
 // the order append_reduce uses, then the epilogue writes the cache rows, all columns at once.  Dense and
-// int4 latents only (the 2-bit format's append is never fused into the attention launch).  `lds`
+// int4 latents in contiguous caches only: the 2-bit format's append and a paged cache's are never fused
+// into the attention launch (which keeps the page lookup out of the attention kernels).  `lds`
 // holds FUSE_MAXR * (N + 4) floats plus 2 * FUSE_MAXR ints.  Called by every thread of the workgroup.
 // The stores are not waited for: the caller waits for vmcnt 0 before any load that reads the rows.
 constexpr int FUSE_MAXR = 8;
@@ -210,9 +212,8 @@ __device__ __forceinline__ void append_rows_fused(const AppendArgs& a, int KS, i
   sp = sp < 0 ? 0 : (sp > a.max_start ? a.max_start : sp);
   const int m0 = b * a.t_new + (p_lo - sp);
   if ((int)threadIdx.x < R) {
-    int pos;
-    rows[threadIdx.x] = cache_row(a, m0 + threadIdx.x, &pos);
-    poss[threadIdx.x] = pos;
+    rows[threadIdx.x] = b * a.t_max + p_lo + threadIdx.x;
+    poss[threadIdx.x] = p_lo + threadIdx.x;
   }
   const float* part = (const float*)a.ws;
   for (int base = 0; base < R * N; base += 4 * (int)blockDim.x) {

@@ -233,3 +233,41 @@ def test_status_strings(lib):
     for s in range(-6, 1):
         assert lib.mla_status_string(s)
     assert lib.mla_status_string(-99) == b"unknown status"
+
+
+def test_paged_cache_checks(lib):
+    """A paged cache: page size a multiple of 64, t_max = pages_per_seq * page_size, a 4-byte aligned table,
+    a pool of at most 2^31 - 1 rows, dense or int4 latents."""
+    def paged(**kw):
+        base = dict(block_table=FAKE, page_size=64, pages_per_seq=64, n_pages=2048, t_max=4096)
+        base.update(kw)
+        return cache(**base)
+
+    big = 1 << 40
+    assert decode_call(lib, k=paged(page_size=32, t_max=2048), ws_bytes=big, q=None) == INVALID
+    assert decode_call(lib, k=paged(t_max=4000), ws_bytes=big, max_len=4000, q=None) == INVALID
+    assert decode_call(lib, k=paged(pages_per_seq=0), ws_bytes=big, q=None) == INVALID
+    assert decode_call(lib, k=paged(n_pages=0), ws_bytes=big, q=None) == INVALID
+    assert decode_call(lib, k=paged(block_table=FAKE + 2), ws_bytes=big) == ALIGN
+    assert decode_call(lib, k=paged(block_table=FAKE + 4), ws_bytes=big, q=None) == INVALID  # 4-byte aligned is fine
+    assert decode_call(lib, k=paged(n_pages=1 << 26), ws_bytes=big) == UNSUPPORTED
+    assert decode_call(lib, c=cfg(cache_fmt=2), k=paged(), ws_bytes=big) == UNSUPPORTED
+    # a contiguous cache with more than 2^31 - 1 rows
+    assert decode_call(lib, k=cache(batch=1 << 17, t_max=1 << 15), max_len=1, ws_bytes=big) == UNSUPPORTED
+
+
+def test_decode_multi_checks(lib):
+    c, w, k = cfg(), weights(), cache()
+    n1 = lib.mla_decode_workspace_bytes(ctypes.byref(c), 32 * 4, 4096)
+    assert lib.mla_decode_multi_workspace_bytes(ctypes.byref(c), 32, 4, 4096) == n1  # 4 queries = 4x the sequences
+    assert lib.mla_decode_multi_workspace_bytes(ctypes.byref(c), 32, 0, 4096) == 0
+
+    def call(q=FAKE, q_len=4, lens=FAKE, out=FAKE, ws=FAKE, nbytes=n1, c=c, k=k):
+        return lib.mla_decode_multi(ctypes.byref(c), ctypes.byref(w), ctypes.byref(k), q, q_len, lens, 4096, out, ws,
+                                    nbytes, None)
+
+    assert call(q_len=0) == INVALID
+    assert call(q=None) == INVALID
+    assert call(nbytes=n1 - 1) == WORKSPACE
+    assert call(c=cfg(cache_fmt=2), nbytes=1 << 40) == UNSUPPORTED
+    assert call(k=cache(batch=0), q=None, lens=None, out=None) == OK
