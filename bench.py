@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode latent-cache GB/s (% of HBM peak); prefill MFMA TFLOP/s"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure (no sparsity)
-DOMINANT_KERNEL = "decode_attn_dma<128, 8, 3, 1, false>"
+DOMINANT_KERNEL = "decode_attn_dma<128, 8, 3, false>"
 
 
 def log(msg):
@@ -363,7 +363,7 @@ def main():
         wl6 = make_decode_workload(cfg1, conv_main, synth.seq_lens(cfg1), args.copies, seed=1006, page_size=64)
         r6 = decode_result("llama_bf16_decode_paged64", cfg1, wl6, args.steps, args.warmup)
         r6.update(hbm_frac=r6["kernel_gbs"] / HBM_PEAK_GBS, page_size=64,
-                  kernel="decode_attn_dma<128, 8, 3, 1, true>")
+                  kernel="decode_attn_dma<128, 8, 3, true>")
         secondary["llama_bf16_decode_paged64"] = r6
         del wl6
         torch.cuda.empty_cache()

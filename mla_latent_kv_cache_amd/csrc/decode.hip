@@ -433,7 +433,7 @@ __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
 // statistics: (m, l, A) per head.
 template <int DW>
 __device__ __forceinline__ void store_partial(const DecodeArgs& a, const f32x16 (&oacc)[DW / 32], float* red,
-                                              float m_run, float l_run) {
+                                              float m_run, float l_run, bool write_ml = true) {
   constexpr int NB = DW / 32, D = 4 * DW;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hb = lane >> 5, h = lane & 31;
   float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * MLS;
@@ -473,8 +473,10 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, const f32x16 
       }
   }
   if (w == 0 && hb == 0) {
-    pml[MLS * h] = m_run;
-    pml[MLS * h + 1] = l_run;
+    if (write_ml) {
+      pml[MLS * h] = m_run;
+      pml[MLS * h + 1] = l_run;
+    }
     pml[MLS * h + 2] = A;
   }
 }
@@ -780,12 +782,13 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
 }
 
 // ------------------------------------------------------------------ 2c. attention, dense MFMA path with LDS DMA
-// Same math and lane mapping as 2b, but every tile reaches LDS through global_load_lds_dwordx4 (no
-// staging registers): a ring of three tile slots (separate LDS arrays, so the compiler can tell the
-// slot being read from the slots still being filled), two tiles in flight while the third is used,
-// explicit vmcnt waits.  Each wave moves only what it reads: its latent column slice (rows XOR-swizzled
-// in 16-byte chunks so that both the row reads and the transpose reads are bank-conflict free) and the
-// RoPE keys of its 8 rows of the tile.  Rows past the sequence repeat its last row and are masked.
+// Same math as 2b, but every tile reaches LDS through global_load_lds_dwordx4 (no staging registers): a
+// ring of three tile slots (separate LDS arrays, so the compiler can tell the slot being read from the
+// slots still being filled), two tiles in flight while the third is used, explicit vmcnt waits.  Each
+// wave moves its latent column slice, which only it reads (rows XOR-swizzled in 16-byte chunks so that
+// both the row reads and the transpose reads are bank-conflict free), and the RoPE keys of rows
+// 8w .. 8w+7 of the tile, which every wave reads after the tile's first barrier.  Rows past the sequence
+// repeat its last row and are masked.
 template <int DW>
 __device__ __forceinline__ int swz(int row, int chunk) {
   if (DW == 128) return chunk ^ (((row & 7) << 1) | ((row >> 3) & 1));
@@ -799,9 +802,21 @@ __device__ __forceinline__ int slice_off(int row, int col) {
 }
 
 
-// NSLOT tile slots in the DMA ring (2: one tile in flight while one is used; 3: two in flight), NSB
-// buffers for the cross-wave exchange of partial scores (2 saves one barrier per tile).
-template <int DW, int R2, int NSLOT, int NSB, bool PG>
+// Byte L of wave w's block inside a RoPE tile slot of the DMA kernel: the keys of heads 8w .. 8w+7, i.e.
+// 32 pieces of 16*R2 bytes, one per token row of 64*R2 bytes.
+template <int R2>
+__device__ __forceinline__ char* own_at(char* kss, int w, int L) {
+  return kss + (L / (16 * R2)) * (64 * R2) + w * (16 * R2) + L % (16 * R2);
+}
+
+// NSLOT tile slots in the DMA ring (2: one tile in flight while one is used; 3: two in flight).
+// Partial scores are reduced per head: wave w sums, over the four column slices, the scores of heads
+// 8w .. 8w+7 only (4 per lane), adds their RoPE terms and owns their softmax (running max, lazy raise,
+// exp, row sum).  It hands the other waves bf16 probabilities (and, after a raise, the per-head rescale
+// factors) through the part of the RoPE slot that only it reads, its own heads' keys, once it has read
+// them; the next RoPE load into that slot therefore waits for the following tile's first barrier.  Per
+// lane and tile: 4 partial-score reads, 4 exponentials, two probability reads, two barriers.
+template <int DW, int R2, int NSLOT, bool PG>
 __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs f) {
   constexpr int NS = DW / 16, NB = DW / 32, D = 4 * DW;
   constexpr int CSL = 32 * DW * 2;       // bytes of one wave's latent slice of a tile
@@ -811,7 +826,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
   constexpr float kRescale = 8.f;        // log2 headroom before the running max must be raised
   __shared__ __attribute__((aligned(1024))) char cs0[4 * CSL], cs1[4 * CSL], cs2[NSLOT > 2 ? 4 * CSL : 16];
   __shared__ __attribute__((aligned(1024))) char ks0[4 * KSL], ks1[4 * KSL], ks2[NSLOT > 2 ? 4 * KSL : 16];
-  __shared__ f32x4 sbuf[NSB][4][4][64];
+  __shared__ f32x4 sbuf[4][4][64];  // partial scores of every wave, then the end-of-item reduction
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5, h = lane & 31;
   // a fused append's rows are formed in slot 2 (its first DMA is issued after the wait before the loop)
@@ -851,16 +866,28 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
     const int off = 1024 * j + 16 * lane, row = off / RB;
     coff[j] = row * (D * 2) + 16 * swz<DW>(row, (off % RB) / 16);
   }
+  // paged cache: lane i holds the pool page of the item's i-th page (an item of at most 2048 rows spans
+  // at most 33 pages of 64 or more rows), read once here instead of once per tile
+  int pid = 0, pg0 = 0;
+  if constexpr (PG) {
+    pg0 = t0 / a.pm.page;
+    if ((pg0 + lane) * a.pm.page < t1 && pg0 + lane < a.pm.pps) {
+      const int pg = a.pm.bt[(size_t)cseq(a, b) * a.pm.pps + pg0 + lane];
+      pid = pg < 0 ? 0 : (pg >= a.pm.n_pages ? a.pm.n_pages - 1 : pg);
+    }
+  }
   const uint32_t c_lds[3] = {lds_addr_of(cs0) + wu * CSL, lds_addr_of(cs1) + wu * CSL, lds_addr_of(cs2) + wu * CSL};
   const uint32_t k_lds[3] = {lds_addr_of(ks0) + wu * KSL, lds_addr_of(ks1) + wu * KSL, lds_addr_of(ks2) + wu * KSL};
-  auto issue_slot = [&](auto ssel, int tt) {
+  auto issue_slot = [&](auto ssel, int tt, auto parts) {
     constexpr int SL = decltype(ssel)::value;
+    constexpr int PARTS = decltype(parts)::value;  // 1: latent rows, 2: RoPE rows, 3: both
     // bases: the tile's rows (paged) or the sequence's rows (contiguous); tb = the tile's first position
     // relative to the base
     const char *cb0, *kt;
     int tb;
     if constexpr (PG) {
-      const size_t prow = (size_t)__builtin_amdgcn_readfirstlane(seq_row(a, b, tt));
+      const int pi = __builtin_amdgcn_readfirstlane(tt / a.pm.page - pg0);
+      const size_t prow = (size_t)__builtin_amdgcn_readlane(pid, pi) * a.pm.page + tt % a.pm.page;
       cb0 = (const char*)a.ckv + (prow * D + wu * DW) * 2;
       kt = (const char*)a.krope + prow * (32 * R2 * 2);
       tb = 0;
@@ -869,7 +896,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
       kt = kseq;
       tb = tt;
     }
-    if (tt + 32 <= t1) {
+    if (!(PARTS & 1)) {
+    } else if (tt + 32 <= t1) {
       const char* cb = cb0 + (size_t)tb * (D * 2);
 #pragma unroll
       for (int j = 0; j < NC; ++j) dma16(cb, coff[j], c_lds[SL] + 1024 * j);
@@ -882,7 +910,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
       }
     }
     // the wave's RoPE rows 8w .. 8w+7 of the tile are one contiguous block
-    if (tt + 8 * wu + 8 <= t1) {
+    if (!(PARTS & 2)) {
+    } else if (tt + 8 * wu + 8 <= t1) {
       const char* kb = (PG ? kt + 8 * wu * 32 * R2 * 2 : kbase) + (size_t)tb * (32 * R2 * 2);
 #pragma unroll
       for (int j = 0; j < NK; ++j) dma16(kb, (uint32_t)(1024 * j + 16 * lane), k_lds[SL] + 1024 * j);
@@ -898,23 +927,32 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
-  issue_slot(S0{}, t0);
+  using PC = std::integral_constant<int, 1>;
+  using PK = std::integral_constant<int, 2>;
+  using PB = std::integral_constant<int, 3>;
+  issue_slot(S0{}, t0, PB{});
   if constexpr (CAN_FUSE)
     if (fuse_late) fused_rows(f, b, t0, t1, (float*)cs2);  // waited for with the first tile below
   const bf16* qt = (const bf16*)(a.ws + a.plan.off_qt) + ((size_t)b * 32 + h) * D + w * DW + 8 * hb;
   bf16x8 qv[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) qv[s] = *(const bf16x8*)(qt + 16 * s);
+  // this lane reduces head xh = 8w + lane%8 at tokens xt0 .. xt0+3 of each tile (from the partial
+  // scores of source lane xsrc, entry xe4) and writes their probabilities at byte xpo of the wave's
+  // probability block (the K order of the PV product, see pb below)
+  const int xg = lane >> 3, xe4 = xg & 3, xhb = xg >> 2, xh = 8 * w + (lane & 7);
+  const int xsrc = 32 * xhb + xh, xt0 = 8 * xe4 + 4 * xhb;
+  const int xpo = ((2 * (xe4 >> 1) + xhb) * 8 + (lane & 7)) * 16 + 8 * (xe4 & 1);
   float qr[R2];
   {
-    const float* qrp = (const float*)(a.ws + a.plan.off_qr) + ((size_t)b * 32 + h) * R2;
+    const float* qrp = (const float*)(a.ws + a.plan.off_qr) + ((size_t)b * 32 + xh) * R2;
 #pragma unroll
     for (int c = 0; c < R2; ++c) qr[c] = qrp[c];
   }
   // the query operands (and the first tile) must be complete before the loop: the compiler would
   // otherwise guard their first use inside the loop with a vmcnt(0) on every iteration
   MLA_WAIT_VMCNT(0);
-  if (NSLOT > 2 && t0 + 32 < t1) issue_slot(S1{}, t0 + 32);
+  if (NSLOT > 2 && t0 + 32 < t1) issue_slot(S1{}, t0 + 32, PB{});
 
   f32x16 oacc[NB];
 #pragma unroll
@@ -922,7 +960,6 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
   // running max per head (log2 domain), raised lazily: p = exp2(s - m_run) may reach 2^kRescale
   float m_run = -INFINITY, l_run = 0.f;
   typedef bf16 kv_t __attribute__((ext_vector_type(R2)));
-  int par = 0;
 
   auto step = [&](auto ssel, int tt) {
     constexpr int SL = decltype(ssel)::value;
@@ -941,21 +978,9 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
       MLA_WAIT_VMCNT(0);
     }
     __builtin_amdgcn_wave_barrier();
-    if (ahead < t1) issue_slot(std::integral_constant<int, NX>{}, ahead);
+    if (ahead < t1) issue_slot(std::integral_constant<int, NX>{}, ahead, PC{});
 
     const char* cw = cs + w * CSL;
-    float rt[4];
-    {
-      const char* kw = kss + w * KSL;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kv_t kk = *(const kv_t*)(kw + ((4 * hb + i) * 32 + h) * R2 * 2);
-        float acc = 0.f;
-#pragma unroll
-        for (int c = 0; c < R2; ++c) acc = fmaf(qr[c], (float)kk[c], acc);
-        rt[i] = acc;
-      }
-    }
     f32x16 sacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -963,62 +988,63 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
       sacc = mfma32(av, qv[s], sacc);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (w == j) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[4 * j + i] += rt[i];
-      }
-    if (NSB == 1) lds_barrier();  // every wave has read the previous tile's partial scores
-#pragma unroll
     for (int e4 = 0; e4 < 4; ++e4)
-      sbuf[NSB == 1 ? 0 : par][w][e4][lane] = f32x4{sacc[4 * e4], sacc[4 * e4 + 1], sacc[4 * e4 + 2], sacc[4 * e4 + 3]};
-    lds_barrier();
-    float sc[16];
+      sbuf[w][e4][lane] = f32x4{sacc[4 * e4], sacc[4 * e4 + 1], sacc[4 * e4 + 2], sacc[4 * e4 + 3]};
+    lds_barrier();  // partial scores and every wave's RoPE rows of this tile are in LDS
+    // the RoPE slot of the previous tile is free now: every wave has read its probabilities
+    if (ahead < t1) issue_slot(std::integral_constant<int, NX>{}, ahead, PK{});
+    f32x4 v = sbuf[0][xe4][xsrc];
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const int pb_ = NSB == 1 ? 0 : par;
-      f32x4 v = sbuf[pb_][0][e4][lane];
+    for (int ww = 1; ww < 4; ++ww) v += sbuf[ww][xe4][xsrc];
+    float sc[4];
 #pragma unroll
-      for (int ww = 1; ww < 4; ++ww) v += sbuf[pb_][ww][e4][lane];
+    for (int i = 0; i < 4; ++i) {
+      kv_t kk = *(const kv_t*)(kss + ((xt0 + i) * 32 + xh) * R2 * 2);
+      float acc = v[i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[4 * e4 + i] = v[i];
+      for (int c = 0; c < R2; ++c) acc = fmaf(qr[c], (float)kk[c], acc);
+      sc[i] = acc;
     }
-    par ^= 1;
     if (tt + 32 > t1) {  // last, partial tile: mask rows past the sequence
-      asm volatile("" ::: "memory");  // keep this a branch (not if-converted into every tile)
+      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (tt + 8 * (e >> 2) + 4 * hb + (e & 3) >= t1) sc[e] = -INFINITY;
+      for (int i = 0; i < 4; ++i)
+        if (tt + xt0 + i >= t1) sc[i] = -INFINITY;
     }
-    float mt = sc[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mt = fmaxf(mt, sc[e]);
+    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mt = fmaxf(mt, shfl_xor(mt, 8));
+    mt = fmaxf(mt, shfl_xor(mt, 16));
     mt = fmaxf(mt, shfl_xor(mt, 32));
-    // raise the running max only when this tile exceeds it by more than the headroom (rare after the
-    // first tile); a raise rescales the latent accumulators of that head
     const bool raise = mt > m_run + kRescale;
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      asm volatile("" ::: "memory");  // keep this a branch (not if-converted into every tile)
+    const bool any = __builtin_amdgcn_ballot_w64(raise) != 0;
+    if (any) {
+      asm volatile("" ::: "memory");
       const float m_new = raise ? mt : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
-#pragma unroll
-      for (int blk = 0; blk < NB; ++blk) oacc[blk] *= alpha;
       m_run = m_new;
+      if (lane < 8) *(float*)own_at<R2>(kss, w, 512 + 4 * lane) = alpha;
     }
-    float p[16], rs = 0.f;
+    if (lane == 0) *(int*)own_at<R2>(kss, w, 544) = any ? 1 : 0;
+    float p[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
-      rs += p[e];
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_run);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    bf16x4 pv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = (bf16)p[i];
+    *(bf16x4*)own_at<R2>(kss, w, xpo) = pv;
+    lds_barrier();  // probabilities of every head
+    const int fl = *(const int*)own_at<R2>(kss, h >> 3, 544);
+    if (__builtin_amdgcn_ballot_w64(fl != 0)) {  // a raise in this tile: rescale those heads
+      asm volatile("" ::: "memory");
+      const float al = fl ? *(const float*)own_at<R2>(kss, h >> 3, 512 + 4 * (h & 7)) : 1.f;
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) oacc[blk] *= al;
     }
-    rs += shfl_xor(rs, 32);
-    l_run += rs;
     bf16x8 pb[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[c][e] = (bf16)p[8 * c + e];
+    for (int c = 0; c < 2; ++c) pb[c] = *(const bf16x8*)own_at<R2>(kss, h >> 3, ((2 * c + hb) * 8 + (h & 7)) * 16);
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       const int col = blk * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -1045,7 +1071,16 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
     }
   }
 
-  store_partial<DW>(a, oacc, (float*)sbuf, m_run, l_run);
+  // row sums were kept per lane: sum the 8 lanes of each head, then its owner writes m and l
+  l_run += shfl_xor(l_run, 8);
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  store_partial<DW>(a, oacc, (float*)sbuf, m_run, l_run, false);
+  if (lane < 8) {
+    float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * MLS;
+    pml[MLS * xh] = m_run;
+    pml[MLS * xh + 1] = l_run;
+  }
 }
 
 // ------------------------------------------------------------------ 2d. attention, one tile stream per wave
@@ -1834,9 +1869,9 @@ template <int DW, int R2>
 void launch_mfma_attn(const DecodeArgs& a, const FuseArgs& f, hipStream_t st) {
   if (a.s.fmt == 0)
     if (a.pm.bt)
-      hipLaunchKernelGGL((decode_attn_dma<DW, R2, 3, (DW == 128 && R2 == 8) ? 1 : 2, true>), attn_grid(a, f), dim3(256), 0, st, a, f);
+      hipLaunchKernelGGL((decode_attn_dma<DW, R2, 3, true>), attn_grid(a, f), dim3(256), 0, st, a, f);
     else
-      hipLaunchKernelGGL((decode_attn_dma<DW, R2, 3, (DW == 128 && R2 == 8) ? 1 : 2, false>), attn_grid(a, f), dim3(256), 0, st, a, f);
+      hipLaunchKernelGGL((decode_attn_dma<DW, R2, 3, false>), attn_grid(a, f), dim3(256), 0, st, a, f);
   else if (a.s.fmt == 1)
     if (a.pm.bt)
       hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 1, true>), attn_grid(a, f), dim3(256), 0, st, a, f);
