@@ -71,7 +71,7 @@ __device__ int work_chunk(const DecodeArgs& a) {
   for (int i = threadIdx.x & 63; i < a.batch; i += 64) tot += clamp_len(a, i);
   tot = wave_isum(tot);
   const int per = (tot + a.plan.target - 1) / a.plan.target;
-  const int chunk = ((per + 63) / 64) * 64;
+  const int chunk = ((per + 31) / 32) * 32;  // whole 32-row tiles (a 64-row minimum below)
   return __builtin_amdgcn_readfirstlane(chunk < 64 ? 64 : (chunk > a.plan.cmax ? a.plan.cmax : chunk));
 }
 struct WorkItem {
@@ -931,8 +931,6 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
   using PK = std::integral_constant<int, 2>;
   using PB = std::integral_constant<int, 3>;
   issue_slot(S0{}, t0, PB{});
-  if constexpr (CAN_FUSE)
-    if (fuse_late) fused_rows(f, b, t0, t1, (float*)cs2);  // waited for with the first tile below
   const bf16* qt = (const bf16*)(a.ws + a.plan.off_qt) + ((size_t)b * 32 + h) * D + w * DW + 8 * hb;
   bf16x8 qv[NS];
 #pragma unroll
@@ -949,6 +947,10 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
 #pragma unroll
     for (int c = 0; c < R2; ++c) qr[c] = qrp[c];
   }
+  // new rows of a fused append later in the item: reduced while the first tile and the query operands
+  // load (issued above, so that their round trips overlap the reduction's), waited for with them below
+  if constexpr (CAN_FUSE)
+    if (fuse_late) fused_rows(f, b, t0, t1, (float*)cs2);
   // the query operands (and the first tile) must be complete before the loop: the compiler would
   // otherwise guard their first use inside the loop with a vmcnt(0) on every iteration
   MLA_WAIT_VMCNT(0);
@@ -1700,90 +1702,103 @@ __device__ __forceinline__ void write_hilo(bf16* hi, bf16* lo, const float (&v)[
 //   of lo) kept in LDS.  Projection: MFMA 16x16x32 with A = rows of W_uv,h (16 output dims) and B = the
 //   sequences' hi and lo rows (16 columns, unused ones ignored).
 constexpr int CB_MAXS = 16;  // sequences per combine workgroup (MFMA columns)
+constexpr int CB_NW = 8;     // waves per combine workgroup
 
+// Merge of the split partials (stats m, l, A and the row O/A) of one (sequence, head): groups g0,
+// g0 + gstep, ... of G splits, the loads of a group all issued before any is used.  Returns the running
+// max M, the denominator and the unnormalised row.
 template <int KPL, bool F16>
 __device__ __forceinline__ void merge_splits(const DecodeArgs& a, int first, int g0, int gstep, int S, int h,
                                              float& M, float& den, float (&acc)[KPL]) {
-  constexpr int D = 64 * KPL;
+  constexpr int D = 64 * KPL, G = F16 ? 8 : 4;  // splits per group (loads in flight: 32 registers)
   const int NH = a.s.n_heads, lane = threadIdx.x & 63;
   typedef _Float16 hv_t __attribute__((ext_vector_type(KPL)));
   typedef float fv_t __attribute__((ext_vector_type(KPL)));
+  typedef typename std::conditional<F16, hv_t, fv_t>::type pv_t;
   const float* ml = (const float*)(a.ws + a.plan.off_ml) + ((size_t)first * NH + h) * MLS;
   const size_t row0 = ((size_t)first * NH + h) * D + KPL * lane;
   M = -INFINITY;
   den = 0.f;
 #pragma unroll
   for (int i = 0; i < KPL; ++i) acc[i] = 0.f;
-  for (int s0 = 8 * g0; s0 < S; s0 += 8 * gstep) {
-    float ms[8], ls[8], as[8];
-    fv_t v[8];
+  for (int s0 = G * g0; s0 < S; s0 += G * gstep) {
+    float ms[G], ls[G], as[G];
+    pv_t v[G];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < G; ++u) {
       const bool ok = s0 + u < S;
       const float* e = ml + (size_t)(s0 + u) * NH * MLS;
       ms[u] = ok ? e[0] : -INFINITY;
       ls[u] = ok ? e[1] : 0.f;
+      as[u] = F16 && ok ? e[2] : 1.f;
       const size_t at = row0 + (size_t)(s0 + u) * NH * D;
-      if (F16) {
-        as[u] = ok ? e[2] : 0.f;
-        v[u] = ok ? __builtin_convertvector(*(const hv_t*)((const _Float16*)(a.ws + a.plan.off_o) + at), fv_t) : fv_t{};
-      } else {
-        as[u] = 1.f;
-        v[u] = ok ? *(const fv_t*)((const float*)(a.ws + a.plan.off_o) + at) : fv_t{};
-      }
+      v[u] = ok ? *(const pv_t*)((const typename std::conditional<F16, _Float16, float>::type*)(a.ws + a.plan.off_o) + at)
+                : pv_t{};
     }
     float gm = M;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) gm = fmaxf(gm, ms[u]);
+    for (int u = 0; u < G; ++u) gm = fmaxf(gm, ms[u]);
     if (gm == -INFINITY) continue;  // nothing seen yet (empty splits only)
     const float c = exp2f(M - gm);  // rescale of what was merged so far (0 when M = -inf)
     den *= c;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) acc[i] *= c;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < G; ++u) {
       const float wv = ms[u] == -INFINITY ? 0.f : exp2f(ms[u] - gm);
       den = fmaf(wv, ls[u], den);
       const float wa = wv * as[u];
 #pragma unroll
-      for (int i = 0; i < KPL; ++i) acc[i] = fmaf(wa, v[u][i], acc[i]);
+      for (int i = 0; i < KPL; ++i) acc[i] = fmaf(wa, (float)v[u][i], acc[i]);
     }
     M = gm;
   }
 }
 
+// One workgroup of CB_NW waves per (head, part of the head's output dims, block of up to CB_MAXS
+// sequences).  Waves share the sequences (CB_NW / nseq waves per sequence, each merging every wps-th
+// group of splits, the groups' states combined through LDS), then project the block's merged rows with
+// W_uv on MFMA: wave w computes 16 output dims of the workgroup's part (and more if the part is wider
+// than 16 CB_NW) for all sequences of the block at once.  Splitting the output dims over gridDim.y
+// workgroups repeats the merge but divides the W_uv rows each workgroup reads (the larger cost).
 template <int KPL>
-__global__ __launch_bounds__(256) void decode_combine(DecodeArgs a, int sb) {
+__global__ __launch_bounds__(64 * CB_NW) void decode_combine(DecodeArgs a, int sb) {
   constexpr int D = 64 * KPL, PITCH = D + 8;  // LDS row pitch in bf16 (16-byte shift per row)
-  constexpr int NKS = D / 32, PF = 2;          // k-steps per output block; blocks prefetched per wave
+  constexpr int NKS = D / 32;                  // k-steps per output block
   __shared__ __attribute__((aligned(16))) bf16 ohi[CB_MAXS][PITCH], olo[CB_MAXS][PITCH];
-  __shared__ float st_m[4], st_d[4];
-  __shared__ __attribute__((aligned(16))) float st_acc[4][64 * KPL];
-  const int h = blockIdx.x, b0 = blockIdx.y * sb;
-  const int NH = a.s.n_heads, dh = a.s.d_head, nblk = dh / 16;
+  __shared__ float st_m[CB_NW], st_d[CB_NW];
+  __shared__ __attribute__((aligned(16))) float st_acc[CB_NW][64 * KPL];
+  const int h = blockIdx.x, b0 = blockIdx.z * sb;
+  const int NH = a.s.n_heads, dh = a.s.d_head, nblk = dh / 16 / gridDim.y, eb0 = blockIdx.y * nblk;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nseq = min(sb, a.batch - b0);
   const bf16* wuv = (const bf16*)a.w_uv + (size_t)h * dh * D;
   const int col = lane & 15, kq = 8 * (lane >> 4);
-  bf16x8 wv[PF][NKS];
+  bf16x8 wv[NKS];  // W_uv rows of output block w, loaded together with the wave's first merge loads
+  auto load_wuv = [&]() {
+    if (w < nblk) {
+      const bf16* wrow = wuv + (size_t)(16 * (eb0 + w) + col) * D + kq;
 #pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (w + 4 * p < nblk) {
-      const bf16* wrow = wuv + (size_t)(16 * (w + 4 * p) + col) * D + kq;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) wv[p][ks] = *(const bf16x8*)(wrow + 32 * ks);
+      for (int ks = 0; ks < NKS; ++ks) wv[ks] = *(const bf16x8*)(wrow + 32 * ks);
     }
+  };
 
-  // waves per sequence: 4 for one sequence, 2 for two, else 1 (each wave's state slot holds one sequence)
-  const int wps = nseq >= 3 ? 1 : (nseq == 2 ? 2 : 4);
+  // waves per sequence: a power of two, CB_NW / wps sequences in flight
+  int wps = 1;
+  while (wps < CB_NW && nseq * wps * 2 <= CB_NW) wps *= 2;
   const int chunk = work_chunk(a);
-  for (int j = w / wps; j < nseq; j += 4 / wps) {
+  bool loaded = false;
+  for (int j = w / wps; j < nseq; j += CB_NW / wps) {
     const int b = b0 + j, q = w % wps;
     int before = 0;
     for (int i = lane; i < b; i += 64) before += item_count(a, clamp_len(a, i), chunk);
     const int first = __builtin_amdgcn_readfirstlane(wave_isum(before));
     const int S = item_count(a, clamp_len(a, b), chunk);
     float M, den, acc[KPL];
+    if (!loaded) {  // after the sequence lengths: waiting for them does not wait for these
+      load_wuv();
+      loaded = true;
+    }
     if (a.plan.f16)
       merge_splits<KPL, true>(a, first, q, wps, S, h, M, den, acc);
     else
@@ -1803,6 +1818,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a, int sb) {
     for (int i = 0; i < KPL; ++i) acc[i] *= inv;
     write_hilo<KPL>(&ohi[j][KPL * lane], &olo[j][KPL * lane], acc);
   }
+  if (!loaded) load_wuv();
   if (wps > 1) {
     __syncthreads();
     const int w0 = w;  // first wave of each group combines its group's states
@@ -1842,14 +1858,12 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a, int sb) {
       *(bf16x4*)((bf16*)a.out + ((size_t)(b0 + col) * NH + h) * dh + 16 * eb + 4 * (lane >> 4)) = o;
     }
   };
-#pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (w + 4 * p < nblk) project(w + 4 * p, wv[p]);
-  for (int eb = w + 4 * PF; eb < nblk; eb += 4) {  // head dims beyond 16 * 4 * PF
+  if (w < nblk) project(eb0 + w, wv);
+  for (int eb = eb0 + w + CB_NW; eb < eb0 + nblk; eb += CB_NW) {  // parts wider than 16 * CB_NW
     const bf16* wrow = wuv + (size_t)(16 * eb + col) * D + kq;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) wv[0][ks] = *(const bf16x8*)(wrow + 32 * ks);
-    project(eb, wv[0]);
+    for (int ks = 0; ks < NKS; ++ks) wv[ks] = *(const bf16x8*)(wrow + 32 * ks);
+    project(eb, wv);
   }
 }
 
@@ -2002,13 +2016,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask, co
     }
   }
   if ((phase_mask & 4) && decode_uses_combine(a.s)) {
-    // sequences per workgroup: about one workgroup per CU, at most 16 (the MFMA width)
-    const int sb = std::max(1, std::min(CB_MAXS, a.batch * nh / 256));
-    dim3 g(nh, (a.batch + sb - 1) / sb);
+    // output dims in two parts when they split into whole 16-wide blocks; sequences per workgroup: about
+    // one workgroup per CU, at most 16 (the MFMA width)
+    const int parts = (a.s.d_head / 16) % 2 == 0 ? 2 : 1;
+    const int sb = std::max(1, std::min(CB_MAXS, a.batch * nh * parts / 256));
+    dim3 g(nh, parts, (a.batch + sb - 1) / sb);
     if (a.s.d_kv == 512)
-      hipLaunchKernelGGL(decode_combine<8>, g, dim3(256), 0, st, a, sb);
+      hipLaunchKernelGGL(decode_combine<8>, g, dim3(64 * CB_NW), 0, st, a, sb);
     else
-      hipLaunchKernelGGL(decode_combine<4>, g, dim3(256), 0, st, a, sb);
+      hipLaunchKernelGGL(decode_combine<4>, g, dim3(64 * CB_NW), 0, st, a, sb);
   } else if (phase_mask & 4) {
     const int pairs = a.batch * nh, gm = (pairs + 3) / 4, kpl = (a.s.d_kv + 63) / 64;
     if (kpl <= 1) hipLaunchKernelGGL(decode_merge<1>, dim3(gm), dim3(256), 0, st, a);

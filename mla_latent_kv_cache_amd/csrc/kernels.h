@@ -50,7 +50,7 @@ int append_ksplit(const Shape& s, int tokens);
 size_t append_workspace_bytes(const Shape& s, int tokens);
 
 // Decode work split.  The kernels read the batch's lengths L_b on the device and cut its tokens into
-// work items of `chunk` tokens: chunk = clamp(round_up(ceil(sum_b L_b / target), 64), 64, cmax), and
+// work items of `chunk` tokens: chunk = clamp(round_up(ceil(sum_b L_b / target), 32), 64, cmax), and
 // sequence b owns ceil(L_b / chunk) consecutive items (in batch order).  With a window of bf16 rows
 // (fmt 2) only the coded positions [0, L_b - W_b), W_b = min(L_b, win), are cut, and the sequence's last
 // item also reads the window [L_b - W_b, L_b) (one item when there are no coded positions).  Ragged batches therefore
