@@ -30,6 +30,7 @@ FAMILIES = {
     "llama": (4096, 32, 128, 1),  # Llama-2-7B-shaped layer
     "mid": (1024, 32, 128, 2),  # Llama head shapes with a narrower model width (fast tests)
     "odd": (640, 5, 128, 3),  # Llama head dim, a head count that is not a multiple of 8 (tests)
+    "head80": (640, 4, 80, 7),  # a head dim of five 16-wide blocks (tests)
 }
 
 

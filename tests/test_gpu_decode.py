@@ -107,6 +107,14 @@ def test_odd_heads_bf16_generic_attention_combine(d_kv, r):
     run_decode_case(cfg, [700, 1, 129, 0], 768)
 
 
+def test_head_dim_80_single_part_combine():
+    """d_head 80: five 16-wide output blocks, so the combine projects each head in one part; one long
+    sequence on the generic kernel gives 63 fp32 split results, which the combine's 8 waves merge in
+    groups of 4 (two groups per wave, the waves' states met in LDS)."""
+    cfg = scaled(CONFIGS[1], family="head80", batch=1, d_kv=256, r_pairs=2)
+    run_decode_case(cfg, [4000], 4096)
+
+
 def test_mid_bf16_dkv512_r4():
     cfg = scaled(CONFIGS[1], family="mid", batch=5)
     run_decode_case(cfg, [1000, 1, 0, 333, 64], 1024)
