@@ -500,7 +500,12 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   constexpr int NB = DW / 32;  // output blocks per wave
   constexpr int D = 4 * DW;
   __shared__ __attribute__((aligned(16))) bf16 cbuf[4][32 * CP];
-  __shared__ f32x4 sbuf[2][4][4][64];
+  __shared__ f32x4 sbuf[4][4][64];  // partial scores of every wave (then the end-of-item reduction)
+  // per tile, from the owner of each head: bf16 probabilities [head][40] (the K order of the PV product),
+  // and after a raise the per-head rescale factors with a flag per owner wave
+  __shared__ __attribute__((aligned(16))) bf16 pbuf[32 * 40];
+  __shared__ float abuf[32];
+  __shared__ int fbuf[4];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5, h = lane & 31;
   static_assert(sizeof(cbuf) >= FUSE_MAXR * (D + 32 * R2 + 4) * 4 + 64, "fused append scratch");
@@ -521,9 +526,15 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   bf16x8 qv[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) qv[s] = *(const bf16x8*)(qt + 16 * s);
+  // partial scores are reduced per head: this lane sums head xh = 8w + lane%8 at tokens xt0 .. xt0+3 of
+  // each tile (source lane xsrc, entry xe4 of every wave's partial tile), adds their RoPE terms and runs
+  // their softmax; its probabilities go to row xh of pbuf at kq .. kq+3
+  const int xe4 = (lane >> 3) & 3, xhb = lane >> 5, xh = 8 * w + (lane & 7);
+  const int xsrc = 32 * xhb + xh, xt0 = 8 * xe4 + 4 * xhb;
+  const int kq = 16 * (xe4 >> 1) + 8 * xhb + 4 * (xe4 & 1);
   float qr[R2];
   {
-    const float* qrp = (const float*)(a.ws + a.plan.off_qr) + ((size_t)b * 32 + h) * R2;
+    const float* qrp = (const float*)(a.ws + a.plan.off_qr) + ((size_t)b * 32 + xh) * R2;
 #pragma unroll
     for (int c = 0; c < R2; ++c) qr[c] = qrp[c];
   }
@@ -560,7 +571,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
     coff[it] = row * RBY + (FMT == 0 ? 2 * (w * DW + 8 * q) : (FMT == 1 ? (w * DW + 32 * q) / 2 : (w * DW + 64 * q) / 4));
     soff[it] = MBY * (row * (D / 32) + (w * DW) / 32 + (FMT == 2 ? 2 * q : q));
   }
-  const uint32_t koff = (((8 * w + 4 * hb) * 32 + h) * R2) * 2;
+  const uint32_t koff = ((xt0 * 32 + xh) * R2) * 2;  // RoPE keys of the lane's 4 tokens, head xh
   // window items (2-bit format) stage their bf16 rows straight from the ring in stage_window and
   // prefetch only the RoPE keys here
   auto load_tile = [&](auto bsel, auto winsel, int tt) {
@@ -597,8 +608,8 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int tok = min(tt + 8 * w + 4 * hb + i, t1 - 1);
-      kreg[B][i] = *(const kv_t*)(krb + row0 * 32 * R2 + ((size_t)(tok - tt + tb) * 32 + h) * R2);
+      int tok = min(tt + xt0 + i, t1 - 1);
+      kreg[B][i] = *(const kv_t*)(krb + row0 * 32 * R2 + ((size_t)(tok - tt + tb) * 32 + xh) * R2);
     }
   };
   auto stage_tile = [&](auto bsel) {
@@ -635,9 +646,9 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
           bf16x8 v;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            // code + 2^23 + 8 as an fp32 bit pattern (nibble e of the word, sign bit flipped), minus
-            // 2^23 + 8: the signed code exactly, then times the scale as int4_dequant
-            const float code = __uint_as_float(((wd[u] >> (4 * e)) & 15u) ^ 0x4B000008u) - 8388616.0f;
+            // nibble e of the word as a signed 4-bit code (sign-extending bit-field extract), converted
+            // exactly, then times the scale as int4_dequant
+            const float code = (float)(((int)(wd[u] << (28 - 4 * e))) >> 28);
             v[e] = (bf16)(code * s);
           }
           *(bf16x8*)&cw[row * CP + 32 * q + 8 * u] = v;
@@ -668,13 +679,12 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
     }
   };
 
-  int par = 0;
   // one 32-token tile: stage registers -> LDS, refill them with the tile two ahead, then both products
   auto step = [&](auto bsel, auto winsel, int tt) {
     constexpr int B = decltype(bsel)::value;
     if constexpr (decltype(winsel)::value) stage_window(tt);
     else stage_tile(bsel);
-    // RoPE term of rows 8w + 4hb + i (result elements 4w + i), taken before the registers refill
+    // RoPE terms of the lane's 4 tokens of head xh, taken before the registers refill
     float rt[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -686,7 +696,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
     if (tt + 64 < t1) load_tile(bsel, winsel, tt + 64);
     __builtin_amdgcn_wave_barrier();
 
-    // scores over this wave's latent columns
+    // partial scores over this wave's latent columns, reduced per head through LDS
     f32x16 sacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -694,60 +704,57 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
       sacc = mfma32(av, qv[s], sacc);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (w == j) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[4 * j + i] += rt[i];
-      }
-#pragma unroll
     for (int e4 = 0; e4 < 4; ++e4)
-      sbuf[par][w][e4][lane] = f32x4{sacc[4 * e4], sacc[4 * e4 + 1], sacc[4 * e4 + 2], sacc[4 * e4 + 3]};
+      sbuf[w][e4][lane] = f32x4{sacc[4 * e4], sacc[4 * e4 + 1], sacc[4 * e4 + 2], sacc[4 * e4 + 3]};
     __syncthreads();
-    float sc[16];
+    f32x4 v = sbuf[0][xe4][xsrc];
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      f32x4 v = sbuf[par][0][e4][lane];
+    for (int ww = 1; ww < 4; ++ww) v += sbuf[ww][xe4][xsrc];
+    float sc[4];
 #pragma unroll
-      for (int ww = 1; ww < 4; ++ww) v += sbuf[par][ww][e4][lane];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[4 * e4 + i] = v[i];
-    }
-    par ^= 1;
+    for (int i = 0; i < 4; ++i) sc[i] = v[i] + rt[i];
     if (tt + 32 > t1) {  // last, partial tile: mask rows past the sequence
       asm volatile("" ::: "memory");  // keep this a branch (not if-converted into every tile)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (tt + 8 * (e >> 2) + 4 * hb + (e & 3) >= t1) sc[e] = -INFINITY;
+      for (int i = 0; i < 4; ++i)
+        if (tt + xt0 + i >= t1) sc[i] = -INFINITY;
     }
-    float mt = sc[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mt = fmaxf(mt, sc[e]);
+    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mt = fmaxf(mt, shfl_xor(mt, 8));
+    mt = fmaxf(mt, shfl_xor(mt, 16));
     mt = fmaxf(mt, shfl_xor(mt, 32));
     // the running max is raised only when a tile exceeds it by more than 2^8 (rare after the first
-    // tile); a raise rescales the latent accumulators of that head
+    // tile); a raise rescales the latent accumulators of that head (in every wave, through abuf)
     const bool raise = mt > m_run + 8.f;
-    if (__builtin_amdgcn_ballot_w64(raise)) {
+    const bool any = __builtin_amdgcn_ballot_w64(raise) != 0;
+    if (any) {
       asm volatile("" ::: "memory");  // keep this a branch (not if-converted into every tile)
       const float m_new = raise ? mt : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
-#pragma unroll
-      for (int blk = 0; blk < NB; ++blk) oacc[blk] *= alpha;
       m_run = m_new;
+      if (lane < 8) abuf[xh] = alpha;
     }
-    float p[16], rs = 0.f;
+    if (lane == 0) fbuf[w] = any ? 1 : 0;
+    float p[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
-      rs += p[e];
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_run);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);  // per lane; the 8 lanes of a head are summed at the end
+    bf16x4 pw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pw[i] = (bf16)p[i];
+    *(bf16x4*)&pbuf[xh * 40 + kq] = pw;
+    __syncthreads();
+    const int fl = fbuf[h >> 3];
+    if (__builtin_amdgcn_ballot_w64(fl != 0)) {  // a raise in this tile: rescale those heads
+      asm volatile("" ::: "memory");
+      const float al = fl ? abuf[h] : 1.f;
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) oacc[blk] *= al;
     }
-    rs += shfl_xor(rs, 32);
-    l_run += rs;
     bf16x8 pb[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[c][e] = (bf16)p[8 * c + e];
+    for (int c = 0; c < 2; ++c) pb[c] = *(const bf16x8*)&pbuf[h * 40 + 16 * c + 8 * hb];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       const int col = blk * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -778,7 +785,16 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
     if (wi.w0 < wi.w1) run(std::true_type{}, wi.w0, wi.w1);
   }
 
-  store_partial<DW>(a, oacc, (float*)sbuf, m_run, l_run);
+  // row sums were kept per lane: sum the 8 lanes of each head, then its owner writes m and l
+  l_run += shfl_xor(l_run, 8);
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  store_partial<DW>(a, oacc, (float*)sbuf, m_run, l_run, false);
+  if (lane < 8) {
+    float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * MLS;
+    pml[MLS * xh] = m_run;
+    pml[MLS * xh + 1] = l_run;
+  }
 }
 
 // ------------------------------------------------------------------ 2c. attention, dense MFMA path with LDS DMA
