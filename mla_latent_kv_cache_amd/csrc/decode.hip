@@ -126,7 +126,7 @@ __device__ __forceinline__ bool fused_rows(const FuseArgs& f, int b, int t0, int
   sp = sp < 0 ? 0 : (sp > f.a.max_start ? f.a.max_start : sp);
   const int lo = max(t0, sp), hi = min(t1, sp + f.a.t_new);
   if (lo >= hi) return false;
-  append_rows_fused(f.a, f.ks, b, lo, hi, lds);
+  append_rows_fused(f.a, f.ks, b, sp, lo, hi, lds);
   return true;
 }
 // Extra workgroup max_items + b of a fused launch: the new rows of sequence b past its decode range.
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   __shared__ int fbuf[4];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5, h = lane & 31;
-  static_assert(sizeof(cbuf) >= FUSE_MAXR * (D + 32 * R2 + 4) * 4 + 64, "fused append scratch");
+  static_assert(sizeof(cbuf) >= fuse_scratch_bytes(D, 32 * R2), "fused append scratch");
   if (blockIdx.x >= a.plan.max_items) {
     fused_orphans(a, f, (float*)cbuf);
     return;
@@ -846,7 +846,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5, h = lane & 31;
   // a fused append's rows are formed in slot 2 (its first DMA is issued after the wait before the loop)
-  constexpr bool CAN_FUSE = NSLOT > 2 && 4 * CSL >= FUSE_MAXR * (D + 32 * R2 + 4) * 4 + 64;
+  constexpr bool CAN_FUSE = NSLOT > 2 && 4 * CSL >= fuse_scratch_bytes(D, 32 * R2);
   if (blockIdx.x >= a.plan.max_items) {
     if constexpr (CAN_FUSE) fused_orphans(a, f, (float*)cs2);
     return;
@@ -854,17 +854,6 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
   WorkItem wi;
   if (!locate_item(a, blockIdx.x, wi)) return;
   const int b = wi.b, t0 = wi.t0, t1 = wi.t1;
-  // new rows of a fused append: before the first tile's DMA when they lie in it, else while it loads
-  bool fuse_late = CAN_FUSE && f.ks > 0;
-  if (fuse_late) {
-    int sp = f.a.start_pos[b];
-    sp = sp < 0 ? 0 : (sp > f.a.max_start ? f.a.max_start : sp);
-    if (sp < t0 + 32 && sp + f.a.t_new > t0) {  // a new row in the first tile
-      fused_rows(f, b, t0, t1, (float*)cs2);
-      MLA_WAIT_VMCNT(0);
-      fuse_late = false;
-    }
-  }
 
   // DMA addresses: a wave-uniform tile base (SGPRs) plus per-lane offsets that do not change per tile
   // a tile's 32 rows are consecutive cache rows (pages hold multiples of 64 positions, tiles start at
@@ -946,6 +935,9 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
   using PC = std::integral_constant<int, 1>;
   using PK = std::integral_constant<int, 2>;
   using PB = std::integral_constant<int, 3>;
+  // the first tile is issued before the item's new rows (if any) are known, so that no workgroup waits
+  // for that look-up before its stream starts; a tile that holds a new row is loaded again once the
+  // row is formed (below)
   issue_slot(S0{}, t0, PB{});
   const bf16* qt = (const bf16*)(a.ws + a.plan.off_qt) + ((size_t)b * 32 + h) * D + w * DW + 8 * hb;
   bf16x8 qv[NS];
@@ -963,10 +955,19 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
 #pragma unroll
     for (int c = 0; c < R2; ++c) qr[c] = qrp[c];
   }
-  // new rows of a fused append later in the item: reduced while the first tile and the query operands
-  // load (issued above, so that their round trips overlap the reduction's), waited for with them below
-  if constexpr (CAN_FUSE)
-    if (fuse_late) fused_rows(f, b, t0, t1, (float*)cs2);
+  // new rows of a fused append in this item: reduced while the first tile and the query operands load
+  // (issued above, so that their round trips overlap the reduction's) and waited for with them below;
+  // when one lies in the first tile, that tile is loaded again after the rows are written
+  if constexpr (CAN_FUSE) {
+    if (f.ks > 0 && fused_rows(f, b, t0, t1, (float*)cs2)) {
+      int sp = f.a.start_pos[b];  // the value fused_rows used (a cached re-read)
+      sp = sp < 0 ? 0 : (sp > f.a.max_start ? f.a.max_start : sp);
+      if (sp < t0 + 32) {  // a new row in the first tile (fused_rows only writes rows in [t0, t1))
+        MLA_WAIT_VMCNT(0);  // the rows are written and the first load has landed
+        issue_slot(S0{}, t0, PB{});
+      }
+    }
+  }
   // the query operands (and the first tile) must be complete before the loop: the compiler would
   // otherwise guard their first use inside the loop with a vmcnt(0) on every iteration
   MLA_WAIT_VMCNT(0);
@@ -1173,7 +1174,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a, FuseArg
   __shared__ __attribute__((aligned(1024))) char lds[W::LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  static_assert(W::LDS_BYTES >= FUSE_MAXR * (D + 32 * R2 + 4) * 4 + 64, "fused append scratch");
+  static_assert(W::LDS_BYTES >= fuse_scratch_bytes(D, 32 * R2), "fused append scratch");
   if (blockIdx.x >= a.plan.max_items) {
     fused_orphans(a, f, (float*)lds);
     return;
@@ -2032,9 +2033,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask, co
     }
   }
   if ((phase_mask & 4) && decode_uses_combine(a.s)) {
-    // output dims in two parts when they split into whole 16-wide blocks; sequences per workgroup: about
-    // one workgroup per CU, at most 16 (the MFMA width)
-    const int parts = (a.s.d_head / 16) % 2 == 0 ? 2 : 1;
+    // output dims in two parts when a head's W_uv rows exceed 64 KB and split into whole 16-wide blocks
+    // (the rows each workgroup pulls through its CU bound the launch); sequences per workgroup: about one
+    // workgroup per CU, at most 16 (the MFMA width)
+    const bool wide = (size_t)a.s.d_head * a.s.d_kv * 2 > 65536;
+    const int parts = wide && (a.s.d_head / 16) % 2 == 0 ? 2 : 1;
     const int sb = std::max(1, std::min(CB_MAXS, a.batch * nh * parts / 256));
     dim3 g(nh, parts, (a.batch + sb - 1) / sb);
     if (a.s.d_kv == 512)

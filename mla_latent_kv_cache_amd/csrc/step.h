@@ -196,24 +196,55 @@ __device__ __forceinline__ void append_epilogue(const AppendArgs& a, const float
 }
 
 // Split-K append, phase 2 for the tokens of sequence b at cache positions [p_lo, p_hi) (at most
-// FUSE_MAXR, all of them new tokens of this append): each output column's KS partial sums are added in
-// the order append_reduce uses, then the epilogue writes the cache rows, all columns at once.  Dense and
-// int4 latents in contiguous caches only: the 2-bit format's append and a paged cache's are never fused
-// into the attention launch (which keeps the page lookup out of the attention kernels).  `lds`
-// holds FUSE_MAXR * (N + 4) floats plus 2 * FUSE_MAXR ints.  Called by every thread of the workgroup.
-// The stores are not waited for: the caller waits for vmcnt 0 before any load that reads the rows.
+// FUSE_MAXR, all of them new tokens of this append; sp = the sequence's clamped start position): each
+// output column's KS partial sums are added in the order append_reduce uses, then the epilogue writes the
+// cache rows, all columns at once.  Dense and int4 latents in contiguous caches only: the 2-bit format's
+// append and a paged cache's are never fused into the attention launch (which keeps the page lookup out
+// of the attention kernels).  The rows' RoPE tables (every pair of the rows' positions, when d_head <=
+// 2 FUSE_HALF_MAX and there are at most 4 rows) and this thread's pair indices are loaded together with
+// the partial sums, so that the whole reduction waits for one round of loads.  `lds` holds fuse_scratch_bytes(D, NR) bytes.  Called by
+// every thread of the workgroup.  The stores are not waited for: the caller waits for vmcnt 0 before any
+// load that reads the rows.
 constexpr int FUSE_MAXR = 8;
-__device__ __forceinline__ void append_rows_fused(const AppendArgs& a, int KS, int b, int p_lo, int p_hi, float* lds) {
+constexpr int FUSE_HALF_MAX = 64;  // RoPE pairs per head whose tables are staged (d_head <= 128)
+constexpr int fuse_scratch_bytes(int D, int NR) {
+  return FUSE_MAXR * (D + NR + 4) * 4 + 2 * FUSE_MAXR * 4 + 2 * FUSE_MAXR * FUSE_HALF_MAX * 4;
+}
+__device__ __forceinline__ void append_rows_fused(const AppendArgs& a, int KS, int b, int sp, int p_lo, int p_hi,
+                                                  float* lds) {
   const int D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR, M = a.batch * a.t_new, ld = N + 4;
-  const int R = p_hi - p_lo;
+  const int R = p_hi - p_lo, half = a.s.d_head / 2, r = a.s.r_pairs, R2 = a.s.r2();
   int* rows = (int*)(lds + FUSE_MAXR * ld);
   int* poss = rows + FUSE_MAXR;
-  int sp = a.start_pos[b];
-  sp = sp < 0 ? 0 : (sp > a.max_start ? a.max_start : sp);
+  float* cst = (float*)(poss + FUSE_MAXR);  // [R][half] cos, then [R][half] sin of the rows' positions
+  float* sst = cst + FUSE_MAXR * FUSE_HALF_MAX;
   const int m0 = b * a.t_new + (p_lo - sp);
   if ((int)threadIdx.x < R) {
     rows[threadIdx.x] = b * a.t_max + p_lo + threadIdx.x;
     poss[threadIdx.x] = p_lo + threadIdx.x;
+  }
+  // loads that do not depend on the partial sums, issued first: the pair index of each RoPE pair this
+  // thread writes, and the rows' cos / sin tables (up to 4 rows: more take the per-pair loads below)
+  constexpr int RPT = 2;  // RoPE pairs per thread: 4 rows x 128 pairs over 256 threads
+  constexpr int CPT = 1;  // table entries per thread: 4 rows x FUSE_HALF_MAX over 256 threads
+  const bool staged = half <= FUSE_HALF_MAX && R * (NR / 2) <= RPT * (int)blockDim.x &&
+                      R * half <= CPT * (int)blockDim.x;
+  int pidx[RPT];
+  float cv[CPT], sv[CPT];
+  if (staged) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int idx = threadIdx.x + i * blockDim.x;
+      const int rel = 2 * (idx % (NR / 2)), hh = rel / R2, jj = (rel - hh * R2) >> 1;
+      pidx[i] = idx < R * (NR / 2) ? load_pair(a.pair_idx, hh * r + jj, half) : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = threadIdx.x + i * blockDim.x, m = idx / half;
+      const size_t at = (size_t)(p_lo + m) * half + (idx - m * half);
+      cv[i] = idx < R * half ? a.rope_cos[at] : 0.f;
+      sv[i] = idx < R * half ? a.rope_sin[at] : 0.f;
+    }
   }
   const float* part = (const float*)a.ws;
   for (int base = 0; base < R * N; base += 4 * (int)blockDim.x) {
@@ -235,6 +266,16 @@ __device__ __forceinline__ void append_rows_fused(const AppendArgs& a, int KS, i
       if (idx < R * N) lds[(idx / N) * ld + idx % N] = sum;
     }
   }
+  if (staged) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = threadIdx.x + i * blockDim.x;
+      if (idx < R * half) {
+        cst[idx] = cv[i];
+        sst[idx] = sv[i];
+      }
+    }
+  }
   lds_barrier();
   if (a.s.fmt == 0) {
     for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x) {
@@ -247,9 +288,24 @@ __device__ __forceinline__ void append_rows_fused(const AppendArgs& a, int KS, i
       store_group(a, (size_t)rows[m], g, lds + m * ld + 32 * g, 1);
     }
   }
-  for (int idx = threadIdx.x; idx < R * (NR / 2); idx += blockDim.x) {
-    const int m = idx / (NR / 2), rel = 2 * (idx - m * (NR / 2));
-    store_rope_pair(a, (size_t)rows[m], poss[m], rel, lds[m * ld + D + rel], lds[m * ld + D + rel + 1]);
+  if (staged) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int idx = threadIdx.x + i * blockDim.x;
+      if (idx < R * (NR / 2)) {
+        const int m = idx / (NR / 2), rel = 2 * (idx - m * (NR / 2));
+        const float x0 = lds[m * ld + D + rel], x1 = lds[m * ld + D + rel + 1];
+        const float cs = cst[m * half + pidx[i]], sn = sst[m * half + pidx[i]];
+        bf16* kr = (bf16*)a.krope + (size_t)rows[m] * NR + rel;
+        kr[0] = (bf16)(x0 * cs - x1 * sn);
+        kr[1] = (bf16)(x0 * sn + x1 * cs);
+      }
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < R * (NR / 2); idx += blockDim.x) {
+      const int m = idx / (NR / 2), rel = 2 * (idx - m * (NR / 2));
+      store_rope_pair(a, (size_t)rows[m], poss[m], rel, lds[m * ld + D + rel], lds[m * ld + D + rel + 1]);
+    }
   }
   lds_barrier();  // the scratch may be reused
 }
