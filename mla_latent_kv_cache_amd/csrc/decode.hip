@@ -66,25 +66,35 @@ __device__ __forceinline__ int item_count(const DecodeArgs& a, int L, int chunk)
   const int lq = L - min(L, a.win), nq = (lq + chunk - 1) / chunk;
   return (nq == 0 && L > 0) ? 1 : nq;
 }
-__device__ int work_chunk(const DecodeArgs& a) {
-  int tot = 0;
-  for (int i = threadIdx.x & 63; i < a.batch; i += 64) tot += clamp_len(a, i);
+// Lengths of sequences lane, lane + 64, ... : the first block's is returned in L0 (the callers reuse it,
+// so that batches of up to 64 sequences read their lengths once), the chunk from their sum.
+__device__ int work_chunk(const DecodeArgs& a, int& L0) {
+  const int lane = threadIdx.x & 63;
+  L0 = lane < a.batch ? clamp_len(a, lane) : 0;
+  int tot = L0;
+  for (int i = lane + 64; i < a.batch; i += 64) tot += clamp_len(a, i);
   tot = wave_isum(tot);
   const int per = (tot + a.plan.target - 1) / a.plan.target;
   const int chunk = ((per + 31) / 32) * 32;  // whole 32-row tiles (a 64-row minimum below)
   return __builtin_amdgcn_readfirstlane(chunk < 64 ? 64 : (chunk > a.plan.cmax ? a.plan.cmax : chunk));
 }
+__device__ int work_chunk(const DecodeArgs& a) {
+  int L0;
+  return work_chunk(a, L0);
+}
 struct WorkItem {
   int b, t0, t1;  // sequence and coded (or dense) token range [t0, t1)
   int w0, w1;     // window rows [w0, w1) of the sequence's last item (fmt 2), else empty
+  int L;          // the sequence's (clamped) length
 };
 // Item `item` of the split; false when the batch has fewer items.
 __device__ bool locate_item(const DecodeArgs& a, int item, WorkItem& wi) {
-  const int chunk = work_chunk(a), lane = threadIdx.x & 63;
+  int L0;
+  const int chunk = work_chunk(a, L0), lane = threadIdx.x & 63;
   int base = 0;
   for (int c0 = 0; c0 < a.batch; c0 += 64) {
     const int i = c0 + lane;
-    const int L = i < a.batch ? clamp_len(a, i) : 0;
+    const int L = c0 == 0 ? L0 : (i < a.batch ? clamp_len(a, i) : 0);
     const int cnt = item_count(a, L, chunk);
     const int incl = wave_iscan(cnt);
     const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
@@ -102,6 +112,7 @@ __device__ bool locate_item(const DecodeArgs& a, int item, WorkItem& wi) {
       wi.t1 = __builtin_amdgcn_readfirstlane(min(j * chunk + chunk, lq));
       wi.w0 = __builtin_amdgcn_readfirstlane(last ? lq : 0);
       wi.w1 = __builtin_amdgcn_readfirstlane(last ? Lb : 0);
+      wi.L = __builtin_amdgcn_readfirstlane(Lb);
       return true;
     }
     base += total;
@@ -128,6 +139,17 @@ __device__ __forceinline__ bool fused_rows(const FuseArgs& f, int b, int t0, int
   if (lo >= hi) return false;
   append_rows_fused(f.a, f.ks, b, sp, lo, hi, lds);
   return true;
+}
+// As fused_rows for the sequence's last item [t0, L), guessing that the new rows are the sequence's last
+// t_new positions (a decode step's usual layout): the reduction's loads are issued together with the
+// start position's instead of after it.  Returns 1 when the guess held (the rows are written), -1 when
+// it does not apply or the start position differs (nothing written: the caller runs fused_rows).
+// between() runs once the reduction's first loads are in flight (the caller issues its own loads there).
+template <class Between>
+__device__ __forceinline__ int fused_rows_last(const FuseArgs& f, int b, int t0, int L, float* lds, Between&& between) {
+  const int g = L - f.a.t_new;
+  if (f.ks == 0 || g < t0 || g < 0 || g > f.a.max_start) return -1;
+  return append_rows_fused(f.a, f.ks, b, g, g, L, lds, true, between) ? 1 : -1;
 }
 // Extra workgroup max_items + b of a fused launch: the new rows of sequence b past its decode range.
 __device__ __forceinline__ void fused_orphans(const DecodeArgs& a, const FuseArgs& f, float* lds) {
@@ -935,14 +957,11 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
   using PC = std::integral_constant<int, 1>;
   using PK = std::integral_constant<int, 2>;
   using PB = std::integral_constant<int, 3>;
-  // the first tile is issued before the item's new rows (if any) are known, so that no workgroup waits
-  // for that look-up before its stream starts; a tile that holds a new row is loaded again once the
-  // row is formed (below)
-  issue_slot(S0{}, t0, PB{});
+  // the first tile and the query operands; issued before the item's new rows (if any) are known, so
+  // that no workgroup waits for that look-up before its stream starts (a tile that holds a new row is
+  // loaded again once the row is formed, below)
   const bf16* qt = (const bf16*)(a.ws + a.plan.off_qt) + ((size_t)b * 32 + h) * D + w * DW + 8 * hb;
   bf16x8 qv[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) qv[s] = *(const bf16x8*)(qt + 16 * s);
   // this lane reduces head xh = 8w + lane%8 at tokens xt0 .. xt0+3 of each tile (from the partial
   // scores of source lane xsrc, entry xe4) and writes their probabilities at byte xpo of the wave's
   // probability block (the K order of the PV product, see pb below)
@@ -950,19 +969,34 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
   const int xsrc = 32 * xhb + xh, xt0 = 8 * xe4 + 4 * xhb;
   const int xpo = ((2 * (xe4 >> 1) + xhb) * 8 + (lane & 7)) * 16 + 8 * (xe4 & 1);
   float qr[R2];
-  {
-    const float* qrp = (const float*)(a.ws + a.plan.off_qr) + ((size_t)b * 32 + xh) * R2;
+  const float* qrp = (const float*)(a.ws + a.plan.off_qr) + ((size_t)b * 32 + xh) * R2;
+  bool started = false;
+  auto start_loads = [&]() {
+    if (started) return;
+    started = true;
+    issue_slot(S0{}, t0, PB{});
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qv[s] = *(const bf16x8*)(qt + 16 * s);
 #pragma unroll
     for (int c = 0; c < R2; ++c) qr[c] = qrp[c];
-  }
-  // new rows of a fused append in this item: reduced while the first tile and the query operands load
-  // (issued above, so that their round trips overlap the reduction's) and waited for with them below;
-  // when one lies in the first tile, that tile is loaded again after the rows are written
+  };
+  // new rows of a fused append in this item: reduced while the first tile and the query operands load,
+  // and waited for with them below; when one lies in the first tile, that tile is loaded again after the
+  // rows are written.  The sequence's last item first assumes a decode step's layout (the new rows are
+  // the sequence's last t_new positions): its reduction's loads go out first, with the start position's,
+  // and the item's own loads follow while they are in flight.
+  int sp = -1;
   if constexpr (CAN_FUSE) {
-    if (f.ks > 0 && fused_rows(f, b, t0, t1, (float*)cs2)) {
-      int sp = f.a.start_pos[b];  // the value fused_rows used (a cached re-read)
-      sp = sp < 0 ? 0 : (sp > f.a.max_start ? f.a.max_start : sp);
-      if (sp < t0 + 32) {  // a new row in the first tile (fused_rows only writes rows in [t0, t1))
+    if (f.ks > 0 && t1 == wi.L && fused_rows_last(f, b, t0, wi.L, (float*)cs2, start_loads) > 0) sp = wi.L - f.a.t_new;
+  }
+  start_loads();
+  if constexpr (CAN_FUSE) {
+    if (f.ks > 0) {
+      if (sp < 0 && fused_rows(f, b, t0, t1, (float*)cs2)) {
+        sp = f.a.start_pos[b];  // the value fused_rows used (a cached re-read)
+        sp = sp < 0 ? 0 : (sp > f.a.max_start ? f.a.max_start : sp);
+      }
+      if (sp >= 0 && sp < t0 + 32) {  // a new row in the first tile (only rows in [t0, t1) are written)
         MLA_WAIT_VMCNT(0);  // the rows are written and the first load has landed
         issue_slot(S0{}, t0, PB{});
       }
@@ -1803,14 +1837,16 @@ __global__ __launch_bounds__(64 * CB_NW) void decode_combine(DecodeArgs a, int s
   // waves per sequence: a power of two, CB_NW / wps sequences in flight
   int wps = 1;
   while (wps < CB_NW && nseq * wps * 2 <= CB_NW) wps *= 2;
-  const int chunk = work_chunk(a);
+  int L0;  // length of sequence `lane` (one read serves the chunk, the item offsets and the counts)
+  const int chunk = work_chunk(a, L0);
+  const int cnt0 = item_count(a, L0, chunk);
   bool loaded = false;
   for (int j = w / wps; j < nseq; j += CB_NW / wps) {
     const int b = b0 + j, q = w % wps;
-    int before = 0;
-    for (int i = lane; i < b; i += 64) before += item_count(a, clamp_len(a, i), chunk);
+    int before = lane < b ? cnt0 : 0;
+    for (int i = lane + 64; i < b; i += 64) before += item_count(a, clamp_len(a, i), chunk);
     const int first = __builtin_amdgcn_readfirstlane(wave_isum(before));
-    const int S = item_count(a, clamp_len(a, b), chunk);
+    const int S = b < 64 ? __builtin_amdgcn_readfirstlane(__shfl(cnt0, b, 64)) : item_count(a, clamp_len(a, b), chunk);
     float M, den, acc[KPL];
     if (!loaded) {  // after the sequence lengths: waiting for them does not wait for these
       load_wuv();

@@ -202,16 +202,22 @@ __device__ __forceinline__ void append_epilogue(const AppendArgs& a, const float
 // append and a paged cache's are never fused into the attention launch (which keeps the page lookup out
 // of the attention kernels).  The rows' RoPE tables (every pair of the rows' positions, when d_head <=
 // 2 FUSE_HALF_MAX and there are at most 4 rows) and this thread's pair indices are loaded together with
-// the partial sums, so that the whole reduction waits for one round of loads.  `lds` holds fuse_scratch_bytes(D, NR) bytes.  Called by
-// every thread of the workgroup.  The stores are not waited for: the caller waits for vmcnt 0 before any
-// load that reads the rows.
+// the partial sums, so that the whole reduction waits for one round of loads.  With `verify`, sp is a
+// guess: the start position is loaded with the rest and, when its clamped value differs, the function
+// returns false before writing anything.  `lds` holds fuse_scratch_bytes(D, NR) bytes.  Called by every
+// thread of the workgroup.  The stores are not waited for: the caller waits for vmcnt 0 before any load
+// that reads the rows.
 constexpr int FUSE_MAXR = 8;
 constexpr int FUSE_HALF_MAX = 64;  // RoPE pairs per head whose tables are staged (d_head <= 128)
 constexpr int fuse_scratch_bytes(int D, int NR) {
   return FUSE_MAXR * (D + NR + 4) * 4 + 2 * FUSE_MAXR * 4 + 2 * FUSE_MAXR * FUSE_HALF_MAX * 4;
 }
-__device__ __forceinline__ void append_rows_fused(const AppendArgs& a, int KS, int b, int sp, int p_lo, int p_hi,
-                                                  float* lds) {
+struct NoLoads {
+  __device__ void operator()() const {}
+};
+template <class Between = NoLoads>
+__device__ __forceinline__ bool append_rows_fused(const AppendArgs& a, int KS, int b, int sp, int p_lo, int p_hi,
+                                                  float* lds, bool verify = false, Between&& between = Between{}) {
   const int D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR, M = a.batch * a.t_new, ld = N + 4;
   const int R = p_hi - p_lo, half = a.s.d_head / 2, r = a.s.r_pairs, R2 = a.s.r2();
   int* rows = (int*)(lds + FUSE_MAXR * ld);
@@ -219,6 +225,7 @@ __device__ __forceinline__ void append_rows_fused(const AppendArgs& a, int KS, i
   float* cst = (float*)(poss + FUSE_MAXR);  // [R][half] cos, then [R][half] sin of the rows' positions
   float* sst = cst + FUSE_MAXR * FUSE_HALF_MAX;
   const int m0 = b * a.t_new + (p_lo - sp);
+  const int sp_src = verify ? a.start_pos[b] : sp;  // issued with the loads below
   if ((int)threadIdx.x < R) {
     rows[threadIdx.x] = b * a.t_max + p_lo + threadIdx.x;
     poss[threadIdx.x] = p_lo + threadIdx.x;
@@ -246,24 +253,44 @@ __device__ __forceinline__ void append_rows_fused(const AppendArgs& a, int KS, i
       sv[i] = idx < R * half ? a.rope_sin[at] : 0.f;
     }
   }
+  // partial sums: rounds of 4 blockDim columns, 16 bytes per thread and slice when rows hold whole 16-byte
+  // chunks; the first round's loads are in flight when between() issues the caller's own loads
   const float* part = (const float*)a.ws;
-  for (int base = 0; base < R * N; base += 4 * (int)blockDim.x) {
-    float v[4][KS_MAX];
+  if (N % 4 == 0) {
+    for (int base = 0; base < R * N; base += 4 * (int)blockDim.x) {
+      const int f0 = base + 4 * (int)threadIdx.x, m = f0 / N, n = f0 - m * N;
+      const bool ok = f0 < R * N;
+      const f32x4* src = (const f32x4*)(part + (size_t)(m0 + (ok ? m : 0)) * N + (ok ? n : 0));
+      const size_t slice = (size_t)M * N / 4;  // one model-width slice of partial sums, in float4
+      f32x4 v[KS_MAX];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = base + it * blockDim.x + threadIdx.x;
-      const int m = idx / N, n = idx - m * N;
+      for (int ks = 0; ks < KS_MAX; ++ks) v[ks] = (ks < KS && ok) ? src[ks * slice] : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (base == 0) between();
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS_MAX; ++ks)
-        v[it][ks] = (ks < KS && idx < R * N) ? part[((size_t)ks * M + m0 + m) * N + n] : 0.f;
+      for (int ks = 0; ks < KS_MAX; ++ks) sum += v[ks];
+      if (ok) *(f32x4*)&lds[m * ld + n] = sum;
     }
+  } else {
+    between();
+    for (int base = 0; base < R * N; base += 4 * (int)blockDim.x) {
+      float v[4][KS_MAX];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = base + it * blockDim.x + threadIdx.x;
-      float sum = 0.f;
+      for (int it = 0; it < 4; ++it) {
+        const int idx = base + it * blockDim.x + threadIdx.x;
+        const int m = idx / N, n = idx - m * N;
 #pragma unroll
-      for (int ks = 0; ks < KS_MAX; ++ks) sum += v[it][ks];
-      if (idx < R * N) lds[(idx / N) * ld + idx % N] = sum;
+        for (int ks = 0; ks < KS_MAX; ++ks)
+          v[it][ks] = (ks < KS && idx < R * N) ? part[((size_t)ks * M + m0 + m) * N + n] : 0.f;
+      }
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int idx = base + it * blockDim.x + threadIdx.x;
+        float sum = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS_MAX; ++ks) sum += v[it][ks];
+        if (idx < R * N) lds[(idx / N) * ld + idx % N] = sum;
+      }
     }
   }
   if (staged) {
@@ -277,6 +304,10 @@ __device__ __forceinline__ void append_rows_fused(const AppendArgs& a, int KS, i
     }
   }
   lds_barrier();
+  if (verify) {
+    const int spc = sp_src < 0 ? 0 : (sp_src > a.max_start ? a.max_start : sp_src);
+    if (spc != sp) return false;  // the same value in every thread: nothing was written to memory
+  }
   if (a.s.fmt == 0) {
     for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x) {
       const int m = idx / D, n = idx - m * D;
@@ -308,6 +339,7 @@ __device__ __forceinline__ void append_rows_fused(const AppendArgs& a, int KS, i
     }
   }
   lds_barrier();  // the scratch may be reused
+  return true;
 }
 
 // Split-K append, phase 1, workgroup (bx: 32 output columns, by: one of KS slices of the model width):
