@@ -508,13 +508,15 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, const f32x16 
 // for both products, so each wave stages only its own slice of every 32-token tile in LDS.
 //   scores   S^T[n][h] = sum_k C[n][k] q~[h][k]      MFMA 32x32x16, A = C rows (ds_read_b128),
 //                                                     B = q~ (registers); partial over the wave's
-//                                                     columns, summed across waves through LDS
+//                                                     columns, reduced per head through LDS: wave w
+//                                                     sums heads 8w .. 8w+7 (4 scores per lane), adds
+//                                                     their RoPE terms and owns their softmax
 //   output   O^T[k][h] += sum_n C[n][k] P[h][n]      MFMA 32x32x16, A = C^T through the LDS
-//                                                     transpose read, B = P straight from the
-//                                                     score registers (same lane -> head mapping)
-// Lane l owns head l%32 in both products, so the per-head max / sum / rescale stay in registers
-// (one cross-half shuffle).  The next tile's rows and RoPE keys are prefetched into registers.  The
-// dense 512-wide variant needs more than 256 registers per lane and runs at one wave per SIMD.
+//                                                     transpose read, B = the owners' bf16 P from LDS
+// Lane l owns head l%32 of the output accumulators; a raise of a head's running max reaches every wave
+// as a rescale factor with a flag.  The next tile's rows and the RoPE keys of the lane's own head and
+// tokens are prefetched into registers.  The dense 512-wide variant needs more than 256 registers per
+// lane and runs at one wave per SIMD.
 template <int DW, int R2, int FMT, bool PG>
 __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_attn_mfma(DecodeArgs a, FuseArgs f) {
   constexpr int CP = DW + 16;  // LDS row pitch in elements (conflict-free b128 and transpose reads)
