@@ -328,6 +328,48 @@ def test_decode_step_matches_separate_calls(variant):
         log(f"  b={b} rel-L2={r:.2e} max-abs={a:.2e}")
 
 
+@pytest.mark.parametrize("variant", ["bf16", "int4"])
+def test_decode_step_new_row_inside_context(variant):
+    """A step whose new token goes inside the decoded range (start = L - 3 for two sequences: the row is
+    overwritten and two later rows stay in the context): the fused step's guess that the new rows end the
+    sequence fails there and its general path runs; the result equals mla_cache_append_ws followed by
+    mla_decode bit for bit, for the cache and the outputs."""
+    from mla_latent_kv_cache_amd import LatentCache, append, append_ws, decode, decode_step, pack_weights
+
+    cfg = scaled(CONFIGS[4], family="mid", batch=4) if variant == "int4" else scaled(CONFIGS[1], family="mid", batch=4)
+    lens = [97, 40, 64, 200]
+    starts = [94, 39, 61, 199]  # sequences 0 and 2 rewrite a row inside their context
+    t_max = 256
+    log(f"[decode-step-inside] {variant} lens={lens} starts={starts}")
+    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    shape = shape_of(cfg)
+    w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
+    caches = [LatentCache.allocate(shape, len(lens), t_max, fill=float("nan")) for _ in range(2)]
+    xs = [synth.context_x(cfg, b, L) for b, L in enumerate(lens)]
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for cache in caches:
+        for b, L in enumerate(lens):
+            xt = torch.from_numpy(xs[b].astype(np.float32)).cuda().to(torch_dtype(cfg)).reshape(1, L, -1)
+            append(w, cache.view(b, b + 1), xt, zero, 0)
+    rng = np.random.default_rng(11)
+    x_new = torch.from_numpy(rng.standard_normal((len(lens), 1, cfg.d_model)).astype(np.float32)).cuda().to(torch_dtype(cfg))
+    start = torch.tensor(starts, dtype=torch.int32, device="cuda")
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    q = np.stack([decode_query(cfg, layer, x[-1]) for x in xs])
+    qt = torch.from_numpy(q.astype(np.float32)).cuda().to(torch_dtype(cfg))
+    before = [caches[0].krope[b, starts[b]].clone() for b in range(len(lens))]
+    out_step = decode_step(w, caches[0], x_new.contiguous(), start, max(starts), qt, lens_t, max(lens))
+    append_ws(w, caches[1], x_new.contiguous(), start, max(starts))
+    out_sep = decode(w, caches[1], qt, lens_t, max(lens))
+    torch.cuda.synchronize()
+    assert torch.equal(out_step, out_sep), "decode_step differs from append_ws + decode"
+    assert torch.equal(caches[0].ckv.contiguous().view(torch.uint8), caches[1].ckv.contiguous().view(torch.uint8))
+    assert torch.equal(caches[0].krope.contiguous().view(torch.uint8), caches[1].krope.contiguous().view(torch.uint8))
+    # every sequence's row at its start position was rewritten with the new token's keys
+    for b in range(len(lens)):
+        assert not torch.equal(caches[0].krope[b, starts[b]], before[b]), f"row {starts[b]} of sequence {b} unchanged"
+
+
 @pytest.mark.parametrize("variant", ["wave_bf16", "wave_int4", "multi_bf16", "multi_int4"])
 def test_decode_step_fused_rows(variant):
     """Decode steps whose append reduction runs inside the attention launch: the latent-256 per-wave kernel
