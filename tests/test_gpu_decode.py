@@ -328,6 +328,60 @@ def test_decode_step_matches_separate_calls(variant):
         log(f"  b={b} rel-L2={r:.2e} max-abs={a:.2e}")
 
 
+@pytest.mark.parametrize("fmt", ["dense", "int4_g32"])
+def test_running_max_raised_mid_item(fmt):
+    """The first 32 rows of every 64-row block get a latent whose score is -20 for every head at once
+    (minimum-norm solution of the 32 heads' absorbed queries, RoPE keys zero).  The work items here are 64
+    rows long, so each item's first tile sets a very low running max and its second tile raises it by far
+    more than the 2^8 headroom, mid-item: the owner waves' rescale factors and flags must reach every
+    wave's accumulators, or the low tile's rows would weigh about e^20 too much."""
+    from mla_latent_kv_cache_amd import LatentCache, decode, pack_weights, quantize_int4
+
+    cfg = scaled(CONFIGS[4] if fmt == "int4_g32" else CONFIGS[1], family="mid", batch=3)
+    lens, t_max = [600, 257, 130], 640
+    log(f"[raise] fmt={fmt} lens={lens}")
+    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    shape = shape_of(cfg)
+    w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
+    cache = LatentCache.allocate(shape, len(lens), t_max, fill=0.0)
+    _, last = fill_cache_per_sequence(cfg, layer, w, cache, lens)
+    q = np.stack([decode_query(cfg, layer, last[b]) for b in range(len(lens))])
+    d_h = cfg.d_head
+    qas = {}
+    for b, L in enumerate(lens):
+        qa = qas[b] = np.zeros((cfg.n_heads, cfg.d_kv))  # absorbed queries W_uk,h q_nope(h)
+        for h in range(cfg.n_heads):
+            kept = {2 * int(p_) + c for p_ in layer["pair_idx"][h] for c in (0, 1)}
+            nope = [i for i in range(d_h) if i not in kept]
+            qa[h] = layer["w_uk"][h] @ q[b, h, nope]
+        c_low = qa.T @ np.linalg.solve(qa @ qa.T, -20.0 * np.sqrt(d_h) * np.ones(cfg.n_heads))
+        rows = torch.tensor([t for t in range(L) if t % 64 < 32], device="cuda")
+        cl = torch.from_numpy(c_low.astype(np.float32)).cuda()
+        if fmt == "int4_g32":
+            codes, scales = quantize_int4(cl[None].contiguous())
+            cache.ckv[b, rows] = codes[0]
+            cache.ckv_scale[b, rows] = scales[0]
+        else:
+            cache.ckv[b, rows] = cl.to(torch.bfloat16)
+        cache.krope[b, rows] = 0
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    qt = torch.from_numpy(q.astype(np.float32)).cuda().to(torch_dtype(cfg))
+    got = _to_np(decode(w, cache, qt, lens_t, max(lens)))
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        if fmt == "int4_g32":
+            c = oracle.dequant_int4(oracle.unpack_nibbles(cache.ckv[b, :L].cpu().numpy()), cache.ckv_scale[b, :L].cpu().numpy())
+        else:
+            c = _to_np(cache.ckv[b, :L])
+        kr = _to_np(cache.krope[b, :L]).reshape(L, cfg.n_heads, -1)
+        ref = oracle.decode_ref(q[b], c, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], d_h, cfg.theta)
+        r, a = assert_close(got[b], ref, cfg.dtype, f"raise b={b}")
+        log(f"  b={b} rel-L2={r:.2e} max-abs={a:.2e}")
+        # the stored low rows score far below the others for every head (NoPE part; their RoPE keys are 0)
+        low = [t for t in range(L) if t % 64 < 32]
+        assert (c[low] @ qas[b].T / np.sqrt(d_h) < -12.0).all()
+
+
 @pytest.mark.parametrize("variant", ["bf16", "int4"])
 def test_decode_step_new_row_inside_context(variant):
     """A step whose new token goes inside the decoded range (start = L - 3 for two sequences: the row is
