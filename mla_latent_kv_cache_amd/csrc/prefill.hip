@@ -192,16 +192,17 @@ __global__ __launch_bounds__(256, 2) void rec_vt_gemm(PrefillArgs a, int N) {
 constexpr int FQ = 256, FKV = 64, FNS = 4;
 constexpr int KT_BYTES = FKV * 256, VT_BYTES = 128 * FKV * 2, SLOT = KT_BYTES + VT_BYTES;
 
-// Schedule of a block of 16 operand reads from LDS and the 16 MFMAs that use them: six reads ahead,
-// then one MFMA per read, so that the matrix core does not wait for LDS latency between MFMAs.
+// Schedule of a block of 16 operand reads from LDS and the 16 MFMAs that use them: ten reads ahead,
+// then one MFMA per read, so that the matrix core does not wait for LDS latency between MFMAs (four
+// waves of a CU read LDS at once; ten ahead measured ~5% faster than six).
 __device__ __forceinline__ void lds_ahead_16() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS reads
+  __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);  // DS reads
 #pragma unroll
-  for (int i = 0; i < 10; ++i) {
+  for (int i = 0; i < 6; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);  // MFMA
+  __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);  // MFMA
 }
 
 // One query tile of one (sequence, head) pair, all 8 waves of the workgroup.
