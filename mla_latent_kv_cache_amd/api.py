@@ -69,6 +69,34 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _expect(*specs) -> None:
+    """Each spec is (tensor, name, dtype, shape, device) (None: not checked).  Raise ValueError unless every
+    tensor has its dtype and shape (checked for all of them first), and then unless every one is a contiguous
+    GPU tensor on its device.  The library reads raw device pointers, so a host tensor, a wrong element type
+    or a short buffer would be read or written past its end rather than rejected."""
+    for t, name, dtype, shape, _ in specs:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    for t, name, _, _, device in specs:
+        if not t.is_cuda:
+            raise ValueError(f"{name}: on {t.device}, the library takes GPU tensors")
+        if device is not None and t.device != device:
+            raise ValueError(f"{name}: on {t.device}, the cache is on {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: not contiguous")
+
+
+def _expect_ws(ws, name: str, need: int, device) -> None:
+    """A caller workspace: uint8 on the cache's device, at least `need` bytes."""
+    _expect((ws, name, torch.uint8, None, device))
+    if ws.numel() < need:
+        raise ValueError(f"{name}: {ws.numel()} bytes, {need} needed")
+
+
 def rope_tables(rope_len: int, d_head: int, theta: float = 1e4):
     """cos / sin tables [rope_len, d_head/2] (fp32) of the angle pos * theta^(-2p/d_head), built in fp64."""
     pos = np.arange(rope_len, dtype=np.float64)[:, None]
@@ -221,9 +249,48 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _weight_specs(w: LayerWeights, cache: LatentCache):
+    if w.shape != cache.shape:
+        raise ValueError(f"weights are for {w.shape}, the cache for {cache.shape}")
+    dev, s = cache.ckv.device, w.shape
+    rope = (w.rope_cos.shape[0], s.d_head // 2)
+    return ([(getattr(w, n), n, s.torch_dtype, None, dev) for n in ("w_dkv", "w_krope", "w_uk", "w_uv")] +
+            [(w.pair_idx, "pair_idx", torch.int32, (s.n_heads, s.r_pairs), dev),
+             (w.rope_cos, "rope_cos", torch.float32, rope, dev), (w.rope_sin, "rope_sin", torch.float32, rope, dev)])
+
+
+def _append_specs(w: LayerWeights, cache: LatentCache, x, start_pos):
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        raise ValueError("x: expected a [batch, t_new, d_model] tensor")
+    dev, s = cache.ckv.device, w.shape
+    return [(x, "x", s.torch_dtype, (cache.batch, x.shape[1], s.d_model), dev),
+            (start_pos, "start_pos", torch.int32, (cache.batch,), dev)]
+
+
+def _decode_specs(w: LayerWeights, cache: LatentCache, q, seq_lens, out, q_len: Optional[int] = None):
+    dev, s = cache.ckv.device, w.shape
+    qs = (cache.batch, s.n_heads, s.d_head) if q_len is None else (cache.batch, q_len, s.n_heads, s.d_head)
+    return [(q, "q", s.torch_dtype, qs, dev), (seq_lens, "seq_lens", torch.int32, (cache.batch,), dev),
+            (out, "out", s.torch_dtype, qs, dev)]
+
+
+def _check_append_args(w: LayerWeights, cache: LatentCache, x, start_pos) -> None:
+    _expect(*_append_specs(w, cache, x, start_pos), *_weight_specs(w, cache))
+
+
+def _check_decode_args(w: LayerWeights, cache: LatentCache, q, seq_lens, out, q_len: Optional[int] = None) -> None:
+    _expect(*_decode_specs(w, cache, q, seq_lens, out, q_len), *_weight_specs(w, cache))
+
+
+def _check_step_args(w: LayerWeights, cache: LatentCache, x, start_pos, q, seq_lens, out) -> None:
+    _expect(*_append_specs(w, cache, x, start_pos), *_decode_specs(w, cache, q, seq_lens, out),
+            *_weight_specs(w, cache))
+
+
 def append(w: LayerWeights, cache: LatentCache, x: torch.Tensor, start_pos: torch.Tensor, max_start_pos: int,
            stream=None) -> None:
     """mla_cache_append: x [batch, t_new, d_model] at positions start_pos[b] + i."""
+    _check_append_args(w, cache, x, start_pos)
     lib = _lib.load()
     cfg, cw, cc = w.shape.c(), w.c(), cache.c()
     t_new = x.shape[1]
@@ -239,12 +306,15 @@ def append_workspace_bytes(shape: LayerShape, batch: int, t_new: int) -> int:
 def append_ws(w: LayerWeights, cache: LatentCache, x: torch.Tensor, start_pos: torch.Tensor, max_start_pos: int,
               workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """mla_cache_append_ws: the same append, with a workspace that spreads few-token appends over the GPU."""
+    _check_append_args(w, cache, x, start_pos)
     lib = _lib.load()
     cfg, cw, cc = w.shape.c(), w.c(), cache.c()
     t_new = x.shape[1]
     need = lib.mla_cache_append_workspace_bytes(ctypes.byref(cfg), cache.batch, t_new)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        _expect_ws(workspace, "workspace", need, x.device)
     _check("mla_cache_append_ws", lib.mla_cache_append_ws(
         ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc), _ptr(x), _ptr(start_pos), t_new, int(max_start_pos),
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
@@ -258,13 +328,15 @@ def decode_workspace_bytes(shape: LayerShape, batch: int, max_seq_len: int) -> i
 def decode(w: LayerWeights, cache: LatentCache, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """mla_decode: q [batch, n_h, d_h] -> out [batch, n_h, d_h]."""
+    if out is None and isinstance(q, torch.Tensor):
+        out = torch.empty_like(q)
+    _check_decode_args(w, cache, q, seq_lens, out)
     lib = _lib.load()
     cfg, cw, cc = w.shape.c(), w.c(), cache.c()
-    if out is None:
-        out = torch.empty_like(q)
     nbytes = lib.mla_decode_workspace_bytes(ctypes.byref(cfg), cache.batch, int(max_seq_len))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _expect_ws(workspace, "workspace", nbytes, q.device)
     _check("mla_decode", lib.mla_decode(ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc), _ptr(q),
                                         _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(workspace),
                                         workspace.numel(), _stream(stream)))
@@ -274,14 +346,18 @@ def decode(w: LayerWeights, cache: LatentCache, q: torch.Tensor, seq_lens: torch
 def decode_multi(w: LayerWeights, cache: LatentCache, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """mla_decode_multi: q [batch, q_len, n_h, d_h] (query i of sequence b at position L_b - q_len + i) -> out."""
-    lib = _lib.load()
-    cfg, cw, cc = w.shape.c(), w.c(), cache.c()
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q: expected a [batch, q_len, n_heads, d_head] tensor")
     q_len = q.shape[1]
     if out is None:
         out = torch.empty_like(q)
+    _check_decode_args(w, cache, q, seq_lens, out, q_len=q_len)
+    lib = _lib.load()
+    cfg, cw, cc = w.shape.c(), w.c(), cache.c()
     nbytes = lib.mla_decode_multi_workspace_bytes(ctypes.byref(cfg), cache.batch, q_len, int(max_seq_len))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _expect_ws(workspace, "workspace", nbytes, q.device)
     _check("mla_decode_multi", lib.mla_decode_multi(ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc), _ptr(q),
                                                     q_len, _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(workspace),
                                                     workspace.numel(), _stream(stream)))
@@ -291,6 +367,7 @@ def decode_multi(w: LayerWeights, cache: LatentCache, q: torch.Tensor, seq_lens:
 def decode_phase(phase: int, w: LayerWeights, cache: LatentCache, q: torch.Tensor, seq_lens: torch.Tensor,
                  max_seq_len: int, out: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
     """mla_decode_phase: one of the three launches of mla_decode (1 q-prep, 2 attention, 3 combine)."""
+    _check_decode_args(w, cache, q, seq_lens, out)
     lib = _lib.load()
     cfg, cw, cc = w.shape.c(), w.c(), cache.c()
     _check("mla_decode_phase", lib.mla_decode_phase(phase, ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc),
@@ -307,14 +384,16 @@ def decode_step(w: LayerWeights, cache: LatentCache, x_new: torch.Tensor, start_
                 q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, out: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """mla_decode_step: append x_new [batch, t_new, d_model] at start_pos, then decode q -> out."""
+    if out is None and isinstance(q, torch.Tensor):
+        out = torch.empty_like(q)
+    _check_step_args(w, cache, x_new, start_pos, q, seq_lens, out)
     lib = _lib.load()
     cfg, cw, cc = w.shape.c(), w.c(), cache.c()
-    if out is None:
-        out = torch.empty_like(q)
     t_new = x_new.shape[1]
     nbytes = lib.mla_decode_step_workspace_bytes(ctypes.byref(cfg), cache.batch, t_new, int(max_seq_len))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _expect_ws(workspace, "workspace", nbytes, q.device)
     _check("mla_decode_step", lib.mla_decode_step(
         ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc), _ptr(x_new), _ptr(start_pos), t_new, int(max_start_pos),
         _ptr(q), _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -329,14 +408,21 @@ def prefill_workspace_bytes(shape: LayerShape, batch: int, seq_len: int) -> int:
 def prefill(w: LayerWeights, cache: LatentCache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """mla_prefill: q [batch, S, n_h, d_h] at positions 0..S-1 -> out [batch, S, n_h, d_h]."""
-    lib = _lib.load()
-    cfg, cw, cc = w.shape.c(), w.c(), cache.c()
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q: expected a [batch, seq_len, n_heads, d_head] tensor")
     seq_len = q.shape[1]
+    s = w.shape
+    qs = (cache.batch, seq_len, s.n_heads, s.d_head)
     if out is None:
         out = torch.empty_like(q)
+    dev = cache.ckv.device
+    _expect((q, "q", s.torch_dtype, qs, dev), (out, "out", s.torch_dtype, qs, dev), *_weight_specs(w, cache))
+    lib = _lib.load()
+    cfg, cw, cc = w.shape.c(), w.c(), cache.c()
     nbytes = lib.mla_prefill_workspace_bytes(ctypes.byref(cfg), cache.batch, seq_len)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _expect_ws(workspace, "workspace", nbytes, q.device)
     _check("mla_prefill", lib.mla_prefill(ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc), _ptr(q), seq_len,
                                           _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
@@ -344,9 +430,10 @@ def prefill(w: LayerWeights, cache: LatentCache, q: torch.Tensor, out: Optional[
 
 def quantize_int4(x: torch.Tensor, stream=None):
     """mla_quantize_int4 on fp32 x [..., 32*g] -> (codes uint8 [..., 16*g], scales float16 [..., g])."""
+    if isinstance(x, torch.Tensor) and (x.dim() < 1 or x.shape[-1] % 32 != 0):
+        raise ValueError("x: the last dim must be a multiple of 32")
+    _expect((x, "x", torch.float32, None, None))
     lib = _lib.load()
-    if x.dtype != torch.float32:
-        raise ValueError("quantize_int4 takes fp32 input")
     n_groups = x.numel() // 32
     codes = torch.empty(x.shape[:-1] + (x.shape[-1] // 2,), dtype=torch.uint8, device=x.device)
     scales = torch.empty(x.shape[:-1] + (x.shape[-1] // 32,), dtype=torch.float16, device=x.device)
@@ -356,9 +443,10 @@ def quantize_int4(x: torch.Tensor, stream=None):
 
 def quantize_int2(x: torch.Tensor, stream=None):
     """mla_quantize_int2 on fp32 x [..., 32*g] -> (codes uint8 [..., 8*g], meta float16 [..., g, 2] = (s, z))."""
+    if isinstance(x, torch.Tensor) and (x.dim() < 1 or x.shape[-1] % 32 != 0):
+        raise ValueError("x: the last dim must be a multiple of 32")
+    _expect((x, "x", torch.float32, None, None))
     lib = _lib.load()
-    if x.dtype != torch.float32:
-        raise ValueError("quantize_int2 takes fp32 input")
     n_groups = x.numel() // 32
     codes = torch.empty(x.shape[:-1] + (x.shape[-1] // 4,), dtype=torch.uint8, device=x.device)
     meta = torch.empty(x.shape[:-1] + (x.shape[-1] // 32, 2), dtype=torch.float16, device=x.device)
@@ -374,6 +462,7 @@ class BoundDecode:
     def __init__(self, w: LayerWeights, cache: LatentCache, x_new: torch.Tensor, start_pos: torch.Tensor,
                  max_start_pos: int, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                  out: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+        _check_step_args(w, cache, x_new, start_pos, q, seq_lens, out)
         self.lib = _lib.load()
         self.cfg, self.cw, self.cc = w.shape.c(), w.c(), cache.c()
         nbytes = self.lib.mla_decode_workspace_bytes(ctypes.byref(self.cfg), cache.batch, int(max_seq_len))

@@ -36,20 +36,37 @@ def _sat16(v32):
     return np.where(np.isinf(v16), np.copysign(FP16_MAX, v16), v16).astype(np.float16)
 
 
+def int2_offset(group_min):
+    """Group offset z = fp16_rne(min x) of the group's fp32 minimum (saturating).  Returns float16."""
+    return _sat16(group_min)
+
+
+def int2_scale(group_max, z16):
+    """Group scale s = fp16_rne(max(max x - z, 0) / 3) from the group's fp32 maximum and its fp16 offset (fp32
+    subtraction, IEEE fp32 division, saturating).  Returns float16."""
+    z32 = np.asarray(z16, dtype=np.float16).astype(np.float32)
+    span = np.maximum(np.asarray(group_max, dtype=np.float32) - z32, np.float32(0.0))
+    return _sat16(span / np.float32(LEVELS))
+
+
+def int2_codes(x, s16, z16):
+    """Codes of fp32 values x [..., 32] under their group's (s, z): clamp(rint_half_even((x - z) / s), 0, 3)
+    in fp32 (subtraction, IEEE division); a zero scale gives zero codes.  Returns uint8."""
+    g = np.asarray(x, dtype=np.float32)
+    s32 = np.asarray(s16, dtype=np.float16).astype(np.float32)[..., None]
+    z32 = np.asarray(z16, dtype=np.float16).astype(np.float32)[..., None]
+    q = np.divide(g - z32, np.where(s32 > 0, s32, np.float32(1.0)), dtype=np.float32)
+    return np.where(np.broadcast_to(s32 > 0, g.shape), np.clip(np.rint(q), 0, LEVELS), 0).astype(np.uint8)
+
+
 def quantize_int2_g32(x):
     """x: fp32 array [..., n*32].  Returns (codes uint8 [..., n*32] in 0..3, meta float16 [..., n, 2] = (s, z))."""
     x = np.asarray(x, dtype=np.float32)
     shp = x.shape
     g = x.reshape(-1, GROUP)
-    z16 = _sat16(np.min(g, axis=1))
-    z32 = z16.astype(np.float32)
-    span = np.maximum(np.max(g, axis=1) - z32, np.float32(0.0))
-    s16 = _sat16(span / np.float32(LEVELS))
-    s32 = s16.astype(np.float32)
-    codes = np.zeros(g.shape, dtype=np.uint8)
-    nz = s32 > 0
-    qv = (g[nz] - z32[nz, None]) / s32[nz, None]
-    codes[nz] = np.clip(np.rint(qv), 0, LEVELS).astype(np.uint8)
+    z16 = int2_offset(np.min(g, axis=1))
+    s16 = int2_scale(np.max(g, axis=1), z16)
+    codes = int2_codes(g, s16, z16)
     meta = np.stack([s16, z16], axis=1)
     return codes.reshape(shp), meta.reshape(shp[:-1] + (shp[-1] // GROUP, 2))
 

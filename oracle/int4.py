@@ -23,19 +23,32 @@ GROUP = 32
 QMAX = 7
 
 
+def int4_scale(absmax):
+    """Group scale from the group's fp32 absmax: fp16_rne(absmax / 7), the division in IEEE fp32, an infinite
+    result saturated to 65504.  Returns float16."""
+    a = np.asarray(absmax, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        s16 = (a / np.float32(QMAX)).astype(np.float16)
+    return np.where(np.isinf(s16), np.float16(65504.0), s16).astype(np.float16)
+
+
+def int4_codes(x, s16):
+    """Codes of fp32 values x [..., 32] under their group's fp16 scale s16 [...]: clamp(rint_half_even(x / s),
+    -7, 7) with an IEEE fp32 division; a zero scale gives zero codes.  Returns int8."""
+    g = np.asarray(x, dtype=np.float32)
+    s32 = np.asarray(s16, dtype=np.float16).astype(np.float32)[..., None]
+    nz = np.broadcast_to(s32 > 0, g.shape)
+    q = np.divide(g, np.where(s32 > 0, s32, np.float32(1.0)), dtype=np.float32)
+    return np.where(nz, np.clip(np.rint(q), -QMAX, QMAX), 0).astype(np.int8)
+
+
 def quantize_int4_g32(x):
     """x: fp32 array [..., n*32].  Returns (codes int8 [..., n*32] in [-7, 7], scales float16 [..., n])."""
     x = np.asarray(x, dtype=np.float32)
     shp = x.shape
     g = x.reshape(-1, GROUP)
-    a = np.max(np.abs(g), axis=1)
-    s16 = (a / np.float32(QMAX)).astype(np.float16)
-    s16 = np.where(np.isinf(s16), np.float16(65504.0), s16).astype(np.float16)
-    s32 = s16.astype(np.float32)
-    codes = np.zeros(g.shape, dtype=np.int8)
-    nz = s32 > 0
-    qv = g[nz] / s32[nz, None]
-    codes[nz] = np.clip(np.rint(qv), -QMAX, QMAX).astype(np.int8)
+    s16 = int4_scale(np.max(np.abs(g), axis=1))
+    codes = int4_codes(g, s16)
     return codes.reshape(shp), s16.reshape(shp[:-1] + (shp[-1] // GROUP,))
 
 

@@ -12,8 +12,8 @@ import oracle
 import synth
 from synth import CONFIGS, scaled
 
-from parity_lib import (assert_close, check_int4_cache, converted_layer, decode_query, fill_cache_per_sequence, log,
-                        max_abs, oracle_cache, rel_l2, shape_of, torch_dtype)
+from parity_lib import (assert_close, assert_finite, check_int4_cache, check_rows, converted_layer, decode_query,
+                        fill_cache_per_sequence, log, max_abs, oracle_cache, rel_l2, shape_of, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,10 @@ def run_decode_case(cfg, lens, t_max, sample=None, check_cache=True, repeat_bitw
     if cache.ckv_scale is not None:
         cache.ckv_scale.fill_(float("nan"))
     sample = list(range(B)) if sample is None else list(sample)
-    xs, last = fill_cache_per_sequence(cfg, layer, w, cache, lens, keep_x=sample)
+    # activations are regenerated from their seeds when checked unless the batch is small (full-size batches
+    # would hold gigabytes of them)
+    keep = sample if sum(int(lens[b]) for b in sample) * cfg.d_model <= (1 << 28) else ()
+    xs, last = fill_cache_per_sequence(cfg, layer, w, cache, lens, keep_x=keep)
 
     rng = np.random.default_rng(7)
     q = np.zeros((B, cfg.n_heads, cfg.d_head))
@@ -51,6 +54,7 @@ def run_decode_case(cfg, lens, t_max, sample=None, check_cache=True, repeat_bitw
     max_len = int(max(lens)) if len(lens) else 0
     out = decode(w, cache, qt, lens_t, max_len)
     torch.cuda.synchronize()
+    assert_finite(out, "decode out")
     got = _to_np(out)
     if repeat_bitwise:
         out2 = decode(w, cache, qt, lens_t, max_len)
@@ -58,28 +62,39 @@ def run_decode_case(cfg, lens, t_max, sample=None, check_cache=True, repeat_bitw
         assert torch.equal(out, out2), "decode is not bitwise deterministic"
 
     results = []
+    err2 = ref2 = 0.0
     for b in sample:
         L = int(lens[b])
         if L == 0:
             assert np.all(got[b] == 0.0), "empty sequence must give a zero output row"
             continue
-        c, kr = oracle_cache(cfg, layer, xs[b])
+        x = xs[b] if b in xs else synth.context_x(cfg, b, L)
+        c, kr = oracle_cache(cfg, layer, x)
+        del x
         if cfg.cache_fmt == "int4_g32":
             codes = oracle.unpack_nibbles(cache.ckv[b, :L].cpu().numpy())
             scales = cache.ckv_scale[b, :L].cpu().numpy()
-            check_int4_cache(c, codes, scales)
+            check_int4_cache(c, codes, scales, f"int4 b={b}")
             oc, osc = oracle.quantize_int4_g32(c.astype(np.float32))
             c_used = oracle.dequant_int4(oc, osc)  # attention over the oracle's own dequantised cache
         else:
             c_used = c
             if check_cache:
-                assert_close(_to_np(cache.ckv[b, :L]), c, cfg.dtype, f"c_kv b={b}")
+                check_rows(cfg, cache.ckv[b, :L], c, f"c_kv b={b}")
         if check_cache and cfg.r_pairs > 0:
-            assert_close(_to_np(cache.krope[b, :L]).reshape(L, cfg.n_heads, -1), kr, cfg.dtype, f"k_rope b={b}")
+            check_rows(cfg, cache.krope[b, :L], kr, f"k_rope b={b}")
         ref = oracle.decode_ref(q[b], c_used, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head, cfg.theta)
         r, a = assert_close(got[b], ref, cfg.dtype, f"decode out b={b} L={L}")
+        err2 += float(np.sum((got[b] - ref) ** 2))
+        ref2 += float(np.sum(ref ** 2))
         results.append((b, L, r, a))
         log(f"  b={b} L={L} rel-L2={r:.2e} max-abs={a:.2e}")
+    if len(sample) == B and results:
+        # the contract over the whole output tensor (empty sequences' zero rows included above)
+        r_all = float(np.sqrt(err2 / ref2)) if ref2 > 0 else 0.0
+        a_all = max(a for _, _, _, a in results)
+        assert r_all <= (1e-5 if cfg.dtype == "f32" else 5e-3), f"whole-tensor rel-L2 {r_all:.3e}"
+        log(f"  whole output [{B}, {cfg.n_heads}, {cfg.d_head}]: rel-L2 {r_all:.2e}, max-abs {a_all:.2e}")
     return results
 
 
@@ -207,13 +222,13 @@ def test_quantize_int4_bit_exact():
     np.testing.assert_array_equal(codes_g.cpu().numpy(), oracle.pack_nibbles(codes_o))
 
 
-# ------------------------------------------------------------------ full-size sampled cases
+# ------------------------------------------------------------------ full-size cases (every sequence)
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_full_llama_bf16_decode_b32_l4096():
     cfg = CONFIGS[1]
-    run_decode_case(cfg, synth.seq_lens(cfg), cfg.context, sample=[0, 31], check_cache=True)
+    run_decode_case(cfg, synth.seq_lens(cfg), cfg.context)
 
 
 @pytest.mark.slow
@@ -221,14 +236,14 @@ def test_full_llama_bf16_decode_b32_l4096():
 def test_full_llama_longctx_decode():
     cfg = CONFIGS[3]
     lens = synth.seq_lens(cfg)
-    run_decode_case(cfg, lens, int(lens.max()), sample=[int(np.argmin(lens)), int(np.argmax(lens))])
+    run_decode_case(cfg, lens, int(lens.max()))
 
 
 @pytest.mark.slow
-@pytest.mark.timeout(900)
+@pytest.mark.timeout(1200)
 def test_full_llama_int4_decode_b64_l8192():
     cfg = CONFIGS[4]
-    run_decode_case(cfg, synth.seq_lens(cfg), cfg.context, sample=[0, 63], repeat_bitwise=False)
+    run_decode_case(cfg, synth.seq_lens(cfg), cfg.context, repeat_bitwise=False)
 
 
 @pytest.mark.parametrize("variant,use_ws", [("bf16", False), ("bf16", True), ("int4", False), ("int4", True),
@@ -267,11 +282,12 @@ def test_step_append_batched_positions(variant, use_ws):
     torch.cuda.synchronize()
     for b, L in enumerate(lens):
         c, kr = oracle_cache(cfg, layer, xs[b])
-        assert_close(_to_np(cache.krope[b, :L]).reshape(L, cfg.n_heads, -1), kr, cfg.dtype, f"k_rope b={b}")
+        check_rows(cfg, cache.krope[b, :L], kr, f"k_rope b={b}")
         if variant == "int4":
-            check_int4_cache(c, oracle.unpack_nibbles(cache.ckv[b, :L].cpu().numpy()), cache.ckv_scale[b, :L].cpu().numpy())
+            check_int4_cache(c, oracle.unpack_nibbles(cache.ckv[b, :L].cpu().numpy()), cache.ckv_scale[b, :L].cpu().numpy(),
+                             f"int4 b={b}")
         else:
-            assert_close(_to_np(cache.ckv[b, :L]), c, cfg.dtype, f"c_kv b={b}")
+            check_rows(cfg, cache.ckv[b, :L], c, f"c_kv b={b}")
         # rows past the sequence were never written
         if L < t_max and variant != "int4":
             assert torch.isnan(cache.ckv[b, L:].float()).all()

@@ -13,7 +13,7 @@ import oracle
 import synth
 from synth import CONFIGS, scaled
 
-from parity_lib import (assert_close, check_int4_cache, converted_layer, decode_query, log, oracle_cache, shape_of,
+from parity_lib import (assert_close, check_int4_cache, check_rows, converted_layer, decode_query, log, oracle_cache, shape_of,
                         torch_dtype)
 
 pytestmark = pytest.mark.gpu
@@ -102,13 +102,13 @@ def test_paged_append_and_decode(case):
     for b, L in enumerate(lens):
         c, kr = oracle_cache(cfg, layer, xs[b])
         ckv, sc, krg = _pool_rows(paged, b, L)
-        assert_close(krg.reshape(L, cfg.n_heads, -1), kr, cfg.dtype, f"pool k_rope b={b}")
+        check_rows(cfg, krg.reshape(L, cfg.n_heads, -1), kr, f"pool k_rope b={b}")
         if cfg.cache_fmt == "int4_g32":
-            check_int4_cache(c, oracle.unpack_nibbles(ckv), sc)
+            check_int4_cache(c, oracle.unpack_nibbles(ckv), sc, f"pool int4 b={b}")
             oc, osc = oracle.quantize_int4_g32(c.astype(np.float32))
             c = oracle.dequant_int4(oc, osc)
         else:
-            assert_close(ckv, c, cfg.dtype, f"pool c_kv b={b}")
+            check_rows(cfg, ckv, c, f"pool c_kv b={b}")
         ref = oracle.decode_ref(q[b], c, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head, cfg.theta)
         rr, a = assert_close(got[b], ref, cfg.dtype, f"decode b={b} L={L}")
         log(f"  b={b} L={L} rel-L2={rr:.2e} max-abs={a:.2e}")

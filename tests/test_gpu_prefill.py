@@ -2,8 +2,9 @@
 
 Small cases compare every query row; lengths that are not multiples of the 64-key / 256-query tiles
 exercise the ragged tails, and a one-token prompt reduces to the first value row.  The full-size case
-(4 sequences x 4096 tokens, Llama-2-7B shapes) compares sampled query rows, including both ends of the
-causal range and tile boundaries."""
+(4 sequences x 4096 tokens, Llama-2-7B shapes) compares every query row of the first and last sequences and
+sampled rows (both ends of the causal range, tile boundaries) of the others.  The appended cache rows are
+compared element by element in every case."""
 
 import numpy as np
 import pytest
@@ -13,16 +14,19 @@ import oracle
 import synth
 from synth import CONFIGS, scaled
 
-from parity_lib import assert_close, converted_layer, log, shape_of, torch_dtype
+from parity_lib import assert_close, assert_finite, check_rows, converted_layer, log, shape_of, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill_case(cfg, S, B, rows=None, sample_b=None, variant=("2-norm", "joint"), layer=None):
+def run_prefill_case(cfg, S, B, rows=None, full_b=None, variant=("2-norm", "joint"), layer=None):
+    """Append + prefill of B seeded prompts of S tokens.  Sequences in full_b (all when None) are compared on
+    every query row; the others on `rows`.  The appended cache rows of every sequence are compared too."""
     from mla_latent_kv_cache_amd import LatentCache, append, pack_weights, prefill
 
     log(f"[prefill] family={cfg.family} r={cfg.r_pairs} d_kv={cfg.d_kv} B={B} S={S} "
-        f"rows={'all' if rows is None else rows} conversion={variant if layer is None else 'given'}")
+        f"every row of {'all' if full_b is None else full_b}, else rows {rows} "
+        f"conversion={variant if layer is None else 'given'}")
     if layer is None:
         layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype, *variant)
     shape = shape_of(cfg)
@@ -40,15 +44,18 @@ def run_prefill_case(cfg, S, B, rows=None, sample_b=None, variant=("2-norm", "jo
     out2 = prefill(w, cache, q)
     torch.cuda.synchronize()
     assert torch.equal(out, out2), "prefill is not bitwise deterministic"
+    assert_finite(out, "prefill out")
     got = out.float().cpu().numpy().astype(np.float64)
-    for b in (range(B) if sample_b is None else sample_b):
+    for b in range(B):
         c, kr = oracle.append_ref(xs[b], layer["w_dkv"], layer["w_krope"], layer["pair_idx"], np.arange(S),
                                   cfg.d_head, cfg.theta)
-        rr = np.arange(S) if rows is None else np.asarray(rows)
+        check_rows(cfg, cache.ckv[b, :S], c, f"c_kv b={b}")
+        check_rows(cfg, cache.krope[b, :S], kr, f"k_rope b={b}")
+        rr = np.arange(S) if (full_b is None or b in full_b or rows is None) else np.asarray(rows)
         ref = oracle.prefill_ref(qs[b], c, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head,
                                  cfg.theta, rows=rr)
         r, a = assert_close(got[b][rr], ref, cfg.dtype, f"prefill b={b}")
-        log(f"  b={b} rel-L2={r:.2e} max-abs={a:.2e}")
+        log(f"  b={b} {len(rr)} rows: rel-L2={r:.2e} max-abs={a:.2e}")
 
 
 def test_prefill_mid_ragged():
@@ -99,4 +106,4 @@ def test_prefill_gqa_source_layer():
 def test_prefill_full_llama_b4_s4096():
     cfg = CONFIGS[2]
     rows = [0, 1, 2, 63, 64, 127, 128, 129, 1000, 2047, 2048, 4031, 4032, 4094, 4095]
-    run_prefill_case(cfg, S=cfg.context, B=cfg.batch, rows=rows, sample_b=[0, 3])
+    run_prefill_case(cfg, S=cfg.context, B=cfg.batch, rows=rows, full_b=[0, 3])
