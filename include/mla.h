@@ -17,10 +17,12 @@
  * Conventions for every entry point
  *   - All pointers to tensors are DEVICE pointers to caller-owned memory unless marked [host].
  *     The library never allocates, frees or synchronises device memory; scratch space comes from
- *     the caller's workspace, sized by the matching *_workspace_bytes call.
+ *     the caller's workspace, sized by the matching *_workspace_bytes call (mla_decode_step_static
+ *     alone uses a static buffer the library holds per GPU instead, see there).
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream).  The calls keep no
- *     mutable global state and may be made from several host threads; calls that share output
- *     buffers or a workspace must be ordered by the caller (same stream or events).
+ *     mutable global state (apart from that static buffer) and may be made from several host
+ *     threads; calls that share output buffers or a workspace must be ordered by the caller (same
+ *     stream or events).
  *   - Return value: MLA_OK (0) or a negative mla_status.  Every argument check runs on the host
  *     before anything is enqueued, so a call that returns an error has written nothing.
  *     MLA_ERR_HIP reports a failed launch (hipGetLastError after enqueueing); work enqueued
@@ -199,6 +201,23 @@ int mla_decode_step(const mla_config *cfg, const mla_weights *w, mla_cache *cach
                     const int32_t *start_pos, int32_t t_new, int32_t max_start_pos, const void *q,
                     const int32_t *seq_lens, int32_t max_seq_len, void *out, void *workspace, size_t ws_bytes,
                     hipStream_t stream);
+
+/* ---------------------------------------------------------------- allocation-free decode step
+ * For callers that cannot allocate device memory (code under HIP graph capture, serving loops or harnesses that
+ * forbid allocation): mla_decode_step with no workspace argument.  The workspace comes from a static device
+ * buffer of MLA_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on until the process ends (the
+ * buffer of the current device, hipGetDevice; the stream and every pointer must belong to that device).  The
+ * call allocates and frees nothing; its first call on a device looks the buffer's address up once.
+ * Every call on one GPU shares that buffer: calls that overlap on one GPU (other streams, other host threads)
+ * race and must be ordered by the caller.  Nothing in the buffer needs clearing between calls: every byte a
+ * call reads is written earlier in the same call.
+ * Returns MLA_ERR_WORKSPACE when mla_decode_step_workspace_bytes(cfg, batch, t_new, max_seq_len) exceeds
+ * MLA_STATIC_SCRATCH_BYTES (for example a Llama-2-7B-shaped layer at 64 sequences x 8192 positions needs
+ * 45.3 MiB), before touching the device; every other argument and error as for mla_decode_step.      */
+#define MLA_STATIC_SCRATCH_BYTES (64u << 20)
+int mla_decode_step_static(const mla_config *cfg, const mla_weights *w, mla_cache *cache, const void *x,
+                           const int32_t *start_pos, int32_t t_new, int32_t max_start_pos, const void *q,
+                           const int32_t *seq_lens, int32_t max_seq_len, void *out, hipStream_t stream);
 
 /* ---------------------------------------------------------------- multi-query decode
  * q_len query tokens per sequence at once (e.g. tokens proposed for speculative decoding), each attending

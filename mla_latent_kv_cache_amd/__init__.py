@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     decode_multi,
     decode_phase,
     decode_step,
+    decode_step_static,
     decode_step_workspace_bytes,
     decode_workspace_bytes,
     pack_weights,
@@ -24,5 +25,6 @@ from .api import (  # noqa: F401
     quantize_int2,
     quantize_int4,
     rope_tables,
+    STATIC_SCRATCH_BYTES,
 )
 from .convert import convert_layer  # noqa: F401

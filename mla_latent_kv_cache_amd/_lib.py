@@ -23,6 +23,7 @@ EXPORTED = [
     "mla_decode_multi",
     "mla_decode_step_workspace_bytes",
     "mla_decode_step",
+    "mla_decode_step_static",
     "mla_prefill_workspace_bytes",
     "mla_prefill",
     "mla_quantize_int4",
@@ -102,6 +103,8 @@ def load():
     lib.mla_decode_step_workspace_bytes.restype = sz
     lib.mla_decode_step.argtypes = [C, W, K, P, P, i32, i32, P, P, i32, P, P, sz, P]
     lib.mla_decode_step.restype = ctypes.c_int
+    lib.mla_decode_step_static.argtypes = [C, W, K, P, P, i32, i32, P, P, i32, P, P]
+    lib.mla_decode_step_static.restype = ctypes.c_int
     lib.mla_prefill_workspace_bytes.argtypes = [C, i32, i32]
     lib.mla_prefill_workspace_bytes.restype = sz
     lib.mla_prefill.argtypes = [C, W, K, P, i32, P, P, sz, P]

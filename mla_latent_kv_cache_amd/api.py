@@ -400,6 +400,23 @@ def decode_step(w: LayerWeights, cache: LatentCache, x_new: torch.Tensor, start_
     return out
 
 
+STATIC_SCRATCH_BYTES = 64 << 20  # MLA_STATIC_SCRATCH_BYTES
+
+
+def decode_step_static(w: LayerWeights, cache: LatentCache, x_new: torch.Tensor, start_pos: torch.Tensor,
+                       max_start_pos: int, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                       out: torch.Tensor, stream=None) -> torch.Tensor:
+    """mla_decode_step_static: the decode step with the library's static per-GPU workspace (no workspace
+    argument, no allocation in the call; `out` must be given)."""
+    _check_step_args(w, cache, x_new, start_pos, q, seq_lens, out)
+    lib = _lib.load()
+    cfg, cw, cc = w.shape.c(), w.c(), cache.c()
+    _check("mla_decode_step_static", lib.mla_decode_step_static(
+        ctypes.byref(cfg), ctypes.byref(cw), ctypes.byref(cc), _ptr(x_new), _ptr(start_pos), x_new.shape[1],
+        int(max_start_pos), _ptr(q), _ptr(seq_lens), int(max_seq_len), _ptr(out), _stream(stream)))
+    return out
+
+
 def prefill_workspace_bytes(shape: LayerShape, batch: int, seq_len: int) -> int:
     cfg = shape.c()
     return _lib.load().mla_prefill_workspace_bytes(ctypes.byref(cfg), batch, seq_len)

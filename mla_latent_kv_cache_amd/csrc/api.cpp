@@ -4,6 +4,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+#include <mutex>
+
 #include "kernels.h"
 
 using mla::Shape;
@@ -236,10 +239,68 @@ size_t mla_decode_step_workspace_bytes(const mla_config* cfg, int32_t batch, int
   return align256(mla::append_workspace_bytes(s, batch * t_new)) + mla::plan_decode(s, batch, max_seq_len).total;
 }
 
+static int decode_step_impl(const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
+                            const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, const void* q,
+                            const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace,
+                            size_t ws_bytes, hipStream_t stream, bool static_ws);
+
 int mla_decode_step(const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
                     const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, const void* q,
                     const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace, size_t ws_bytes,
                     hipStream_t stream) {
+  return decode_step_impl(cfg, w, cache, x, start_pos, t_new, max_start_pos, q, seq_lens, max_seq_len, out, workspace,
+                          ws_bytes, stream, false);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free decode step
+// The workspace of mla_decode_step_static lives in this file-scope device array: each GPU the library runs on
+// holds one copy until the process ends.  Host code never uses the array's name as an address (on the host it
+// names a stand-in, not device memory): its device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[MLA_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's scratch array (nullptr with MLA_ERR_HIP if it cannot be found).
+int current_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return MLA_ERR_HIP;
+  *ptr = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int mla_decode_step_static(const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
+                           const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, const void* q,
+                           const int32_t* seq_lens, int32_t max_seq_len, void* out, hipStream_t stream) {
+  // the size check first, so that an oversized request is rejected before the device is touched
+  if (check_config(cfg) == MLA_OK && cache && cache->batch >= 0 && t_new >= 0 && max_seq_len >= 0 &&
+      mla_decode_step_workspace_bytes(cfg, cache->batch, t_new, max_seq_len) > (size_t)MLA_STATIC_SCRATCH_BYTES)
+    return MLA_ERR_WORKSPACE;
+  return decode_step_impl(cfg, w, cache, x, start_pos, t_new, max_start_pos, q, seq_lens, max_seq_len, out, nullptr,
+                          MLA_STATIC_SCRATCH_BYTES, stream, true);
+}
+
+}  // extern "C"
+
+static int decode_step_impl(const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
+                            const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, const void* q,
+                            const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace,
+                            size_t ws_bytes, hipStream_t stream, bool static_ws) {
   // validation of both halves, as the separate calls do it
   MLA_TRY(check_config(cfg));
   MLA_TRY(check_weights(cfg, w, true, true));
@@ -263,7 +324,9 @@ int mla_decode_step(const mla_config* cfg, const mla_weights* w, mla_cache* cach
   if (!mla::decode_fits(s, plan)) return MLA_ERR_UNSUPPORTED;
   if (mla::decode_uses_mfma(s) && (size_t)cache->t_max * s.d_kv * 2 >= ((size_t)1 << 31)) return MLA_ERR_UNSUPPORTED;
   const size_t app_bytes = align256(mla::append_workspace_bytes(s, cache->batch * t_new));
-  if (!workspace || ws_bytes < app_bytes + plan.total) return MLA_ERR_WORKSPACE;
+  if (ws_bytes < app_bytes + plan.total) return MLA_ERR_WORKSPACE;
+  if (static_ws) MLA_TRY(current_scratch(&workspace));  // the last step before enqueueing: a lookup, no allocation
+  if (!workspace) return MLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
   char* wsa = (char*)workspace;
   char* wsd = wsa + app_bytes;
@@ -279,6 +342,8 @@ int mla_decode_step(const mla_config* cfg, const mla_weights* w, mla_cache* cach
   if (t_new > 0) MLA_TRY(from_hip(mla::launch_append(aa, stream)));
   return from_hip(mla::launch_decode(da, stream, 7));
 }
+
+extern "C" {
 
 size_t mla_prefill_workspace_bytes(const mla_config* cfg, int32_t batch, int32_t seq_len) {
   if (check_config(cfg) != MLA_OK || batch < 0 || seq_len < 0) return 0;

@@ -271,3 +271,16 @@ def test_decode_multi_checks(lib):
     assert call(nbytes=n1 - 1) == WORKSPACE
     assert call(c=cfg(cache_fmt=2), nbytes=1 << 40) == UNSUPPORTED
     assert call(k=cache(batch=0), q=None, lens=None, out=None) == OK
+
+
+def test_static_step_rejects_oversized_request_on_the_host(lib):
+    """mla_decode_step_static refuses a step whose workspace exceeds its static buffer before touching the
+    device (here there is none): 256 sequences x 4096 positions of the Llama-2-7B-shaped layer."""
+    c, w, k = cfg(), weights(), cache(batch=256)
+    assert lib.mla_decode_step_workspace_bytes(ctypes.byref(c), 256, 1, 4096) > (64 << 20)
+    rc = lib.mla_decode_step_static(ctypes.byref(c), ctypes.byref(w), ctypes.byref(k), FAKE, FAKE, 1, 4095, FAKE,
+                                    FAKE, 4096, FAKE, None)
+    assert rc == WORKSPACE
+    # invalid arguments are reported as for mla_decode_step, before the size
+    assert lib.mla_decode_step_static(ctypes.byref(cfg(d_head=7)), ctypes.byref(w), ctypes.byref(k), FAKE, FAKE, 1,
+                                      4095, FAKE, FAKE, 4096, FAKE, None) == INVALID
