@@ -202,6 +202,18 @@ int mla_decode_step(const mla_config *cfg, const mla_weights *w, mla_cache *cach
                     const int32_t *seq_lens, int32_t max_seq_len, void *out, void *workspace, size_t ws_bytes,
                     hipStream_t stream);
 
+/* The three phases of mla_decode_step one at a time (for callers that time them or interleave other work):
+ *   phase 1  the append's first launch (split-K partial sums of the new rows, or the whole append when the
+ *            step does not split it) and the query preparation
+ *   phase 2  the attention (the append's reduction runs inside this launch when the step fuses it)
+ *   phase 3  the merge of the splits and the W_uv,h up-projection into `out`
+ * Same arguments as mla_decode_step; phases run in order 1, 2, 3 on the same stream and workspace; running
+ * 1, 2, 3 once gives the results of mla_decode_step.  phase outside 1..3 returns MLA_ERR_INVALID_ARG.  */
+int mla_decode_step_phase(int phase, const mla_config *cfg, const mla_weights *w, mla_cache *cache, const void *x,
+                          const int32_t *start_pos, int32_t t_new, int32_t max_start_pos, const void *q,
+                          const int32_t *seq_lens, int32_t max_seq_len, void *out, void *workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
 /* ---------------------------------------------------------------- allocation-free decode step
  * For callers that cannot allocate device memory (code under HIP graph capture, serving loops or harnesses that
  * forbid allocation): mla_decode_step with no workspace argument.  The workspace comes from a static device
@@ -234,8 +246,10 @@ int mla_decode_multi(const mla_config *cfg, const mla_weights *w, const mla_cach
 
 /* ---------------------------------------------------------------- prefill
  * Causal attention of seq_len query tokens per sequence, at positions 0..seq_len-1, over the
- * cache rows 0..seq_len-1 (append them first).  Unabsorbed form: K_nope and V of every head are
- * rebuilt from c_kv (c_kv . W_uk,h and c_kv . W_uv,h), the kept RoPE keys are read from the cache.
+ * cache rows 0..seq_len-1 (append them first).  Unabsorbed form of the key-designs section: K_nope and
+ * V of every head are recovered from the latent (c_kv . W_uk,h and c_kv . W_uv,h) and the retained RoPE
+ * keys, which cannot be merged into the matrices, are read from the cache; for a whole prompt this
+ * rebuilds each token's keys and values once instead of folding W_uk,h into every query.
  *   q    [batch, seq_len, n_h, d_h] raw queries;   out [batch, seq_len, n_h, d_h]
  * BF16 dense caches only (MLA_ERR_UNSUPPORTED otherwise).
  * Workspace: mla_prefill_workspace_bytes(cfg, batch, seq_len) bytes.                           */
@@ -243,14 +257,28 @@ size_t mla_prefill_workspace_bytes(const mla_config *cfg, int32_t batch, int32_t
 int mla_prefill(const mla_config *cfg, const mla_weights *w, const mla_cache *cache, const void *q,
                 int32_t seq_len, void *out, void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------- RoPE tables
+ * The rotation tables of the partial RoPE (key-designs section: each retained 2-D subspace [2p, 2p+1] of a
+ * head turns with its own frequency, theta^(-2p/d_head) per position): for positions t in [0, rope_len)
+ * and subspaces p in [0, d_head/2), cos_out[t][p] = cos(t * theta^(-2p/d_head)) and sin_out likewise,
+ * computed in fp64 on the host and rounded to fp32 -- the rope_cos / rope_sin of mla_weights.
+ *   cos_out, sin_out  [host] caller-owned [rope_len, d_head/2] fp32 buffers (may be NULL when rope_len == 0)
+ * Returns MLA_ERR_INVALID_ARG for rope_len < 0, an odd or non-positive d_head, theta not finite and > 0,
+ * or a NULL buffer.  Synchronous host code; touches no device.                                      */
+int mla_rope_tables(int32_t rope_len, int32_t d_head, double theta, float *cos_out, float *sin_out);
+
 /* ---------------------------------------------------------------- int4 codec
- * The latent quantiser of the INT4_G32 cache on its own, for bit-exact checks of the codes.
+ * The latent quantiser of the INT4_G32 cache on its own, for bit-exact checks of the codes (the key-designs
+ * section's remark that the latent composes with 4-bit KV-cache quantisation; the group-32 absmax format
+ * with fp16 scales is this library's, the pages fix none).
  *   in [n_groups*32] fp32 -> codes [n_groups*16] uint8 (packed as above), scales [n_groups] fp16 bits. */
 int mla_quantize_int4(const float *in, int64_t n_groups, uint8_t *codes, uint16_t *scales, hipStream_t stream);
 
 /* ---------------------------------------------------------------- 2-bit codec
  * The latent quantiser of the INT2_G32_WIN cache on its own (values already on the bf16 grid in the
- * cache; any fp32 values here), for bit-exact checks of the codes.
+ * cache; any fp32 values here), for bit-exact checks of the codes (the key-designs section's remark that the
+ * latent composes with 2-bit KV-cache quantisation; the affine group-32 format with fp16 scale and offset is
+ * this library's, the pages fix none).
  *   in [n_groups*32] fp32 -> codes [n_groups*8] uint8 (packed as above), meta [n_groups*2] fp16 bits
  *   (s, z per group).                                                                           */
 int mla_quantize_int2(const float *in, int64_t n_groups, uint8_t *codes, uint16_t *meta, hipStream_t stream);

@@ -6,7 +6,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmla_latent.so")
+# MLA_LATENT_LIB names another build of the same library (the host-sanitized one of the CPU test suite)
+LIB_PATH = os.environ.get("MLA_LATENT_LIB") or os.path.join(PKG, "libmla_latent.so")
 
 MLA_OK = 0
 MLA_F32, MLA_BF16 = 0, 1
@@ -24,10 +25,12 @@ EXPORTED = [
     "mla_decode_step_workspace_bytes",
     "mla_decode_step",
     "mla_decode_step_static",
+    "mla_decode_step_phase",
     "mla_prefill_workspace_bytes",
     "mla_prefill",
     "mla_quantize_int4",
     "mla_quantize_int2",
+    "mla_rope_tables",
     "mla_status_string",
 ]
 
@@ -105,6 +108,10 @@ def load():
     lib.mla_decode_step.restype = ctypes.c_int
     lib.mla_decode_step_static.argtypes = [C, W, K, P, P, i32, i32, P, P, i32, P, P]
     lib.mla_decode_step_static.restype = ctypes.c_int
+    lib.mla_decode_step_phase.argtypes = [ctypes.c_int, C, W, K, P, P, i32, i32, P, P, i32, P, P, sz, P]
+    lib.mla_decode_step_phase.restype = ctypes.c_int
+    lib.mla_rope_tables.argtypes = [i32, i32, ctypes.c_double, P, P]
+    lib.mla_rope_tables.restype = ctypes.c_int
     lib.mla_prefill_workspace_bytes.argtypes = [C, i32, i32]
     lib.mla_prefill_workspace_bytes.restype = sz
     lib.mla_prefill.argtypes = [C, W, K, P, i32, P, P, sz, P]

@@ -98,11 +98,13 @@ def _expect_ws(ws, name: str, need: int, device) -> None:
 
 
 def rope_tables(rope_len: int, d_head: int, theta: float = 1e4):
-    """cos / sin tables [rope_len, d_head/2] (fp32) of the angle pos * theta^(-2p/d_head), built in fp64."""
-    pos = np.arange(rope_len, dtype=np.float64)[:, None]
-    freq = theta ** (-2.0 * np.arange(d_head // 2, dtype=np.float64) / d_head)
-    ang = pos * freq[None, :]
-    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    """cos / sin tables [rope_len, d_head/2] (fp32) of the angle pos * theta^(-2p/d_head): mla_rope_tables."""
+    cos = np.empty((rope_len, d_head // 2), dtype=np.float32)
+    sin = np.empty_like(cos)
+    _check("mla_rope_tables", _lib.load().mla_rope_tables(int(rope_len), int(d_head), float(theta),
+                                                          cos.ctypes.data if cos.size else None,
+                                                          sin.ctypes.data if sin.size else None))
+    return cos, sin
 
 
 @dataclass
@@ -513,3 +515,8 @@ class BoundDecode:
 
     def phase(self, p: int, stream=None):
         _check("mla_decode_phase", self.lib.mla_decode_phase(p, *self.args_decode, _stream(stream)))
+
+    def step_phase(self, p: int, stream=None):
+        """mla_decode_step_phase: one of the step's three launches (1 append + q-prep, 2 attention with the
+        append's reduction, 3 combine)."""
+        _check("mla_decode_step_phase", self.lib.mla_decode_step_phase(p, *self.args_step, _stream(stream)))

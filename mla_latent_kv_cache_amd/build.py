@@ -20,6 +20,9 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla_latent.so")
 
 SOURCES = ["api.cpp", "append.hip", "decode.hip", "prefill.hip"]
+# the streaming-read ceiling kernel that bench.py measures HBM with, in a library of its own
+BW_SOURCE = "bandwidth.hip"
+BW_LIB = os.path.join(PKG, "libmla_bandwidth.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -36,9 +39,18 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the same sources (device code is built as
+# usual, only the host code is instrumented): the C ABI's argument validation runs under the sanitizers in the
+# CPU test suite, with the sanitizer runtime preloaded.
+SAN_BUILD = os.path.join(BUILD, "host_sanitized")
+SAN_LIB = os.path.join(SAN_BUILD, "libmla_latent_hostsan.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def _compile(src: str, out_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,19 +63,46 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [BW_SOURCE]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], BW_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {BW_LIB}")
     return LIB
+
+
+def build_host_sanitized(verbose: bool = True) -> str:
+    """The library with its host code built under ASan + UBSan (SAN_LIB); load it only in a process whose
+    sanitizer runtime is preloaded (sanitizer_runtime())."""
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda src: _compile(src, SAN_BUILD, SAN_FLAGS), SOURCES))
+    _link(objs, SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """The compiler's shared ASan runtime (it also carries the UBSan handlers), to LD_PRELOAD."""
+    r = subprocess.run([os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin", "clang"),
+                        "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the ASan runtime of the ROCm compiler was not found")
+    return path
 
 
 if __name__ == "__main__":

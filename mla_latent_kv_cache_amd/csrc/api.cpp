@@ -242,7 +242,7 @@ size_t mla_decode_step_workspace_bytes(const mla_config* cfg, int32_t batch, int
 static int decode_step_impl(const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
                             const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, const void* q,
                             const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace,
-                            size_t ws_bytes, hipStream_t stream, bool static_ws);
+                            size_t ws_bytes, hipStream_t stream, bool static_ws, int phase_mask = 7);
 
 int mla_decode_step(const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
                     const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, const void* q,
@@ -250,6 +250,15 @@ int mla_decode_step(const mla_config* cfg, const mla_weights* w, mla_cache* cach
                     hipStream_t stream) {
   return decode_step_impl(cfg, w, cache, x, start_pos, t_new, max_start_pos, q, seq_lens, max_seq_len, out, workspace,
                           ws_bytes, stream, false);
+}
+
+int mla_decode_step_phase(int phase, const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
+                          const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, const void* q,
+                          const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (phase < 1 || phase > 3) return MLA_ERR_INVALID_ARG;
+  return decode_step_impl(cfg, w, cache, x, start_pos, t_new, max_start_pos, q, seq_lens, max_seq_len, out, workspace,
+                          ws_bytes, stream, false, 1 << (phase - 1));
 }
 
 }  // extern "C"
@@ -300,7 +309,7 @@ int mla_decode_step_static(const mla_config* cfg, const mla_weights* w, mla_cach
 static int decode_step_impl(const mla_config* cfg, const mla_weights* w, mla_cache* cache, const void* x,
                             const int32_t* start_pos, int32_t t_new, int32_t max_start_pos, const void* q,
                             const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace,
-                            size_t ws_bytes, hipStream_t stream, bool static_ws) {
+                            size_t ws_bytes, hipStream_t stream, bool static_ws, int phase_mask) {
   // validation of both halves, as the separate calls do it
   MLA_TRY(check_config(cfg));
   MLA_TRY(check_weights(cfg, w, true, true));
@@ -338,9 +347,10 @@ static int decode_step_impl(const mla_config* cfg, const mla_weights* w, mla_cac
                      seq_lens, out, wsd, plan};
   set_window(aa, cfg, cache);
   set_window(da, cfg, cache);
-  if (t_new > 0 && mla::decode_step_fusable(aa, da)) return from_hip(mla::launch_decode_step(aa, da, stream));
-  if (t_new > 0) MLA_TRY(from_hip(mla::launch_append(aa, stream)));
-  return from_hip(mla::launch_decode(da, stream, 7));
+  if (t_new > 0 && mla::decode_step_fusable(aa, da))
+    return from_hip(mla::launch_decode_step(aa, da, stream, phase_mask));
+  if (t_new > 0 && (phase_mask & 1)) MLA_TRY(from_hip(mla::launch_append(aa, stream)));
+  return from_hip(mla::launch_decode(da, stream, phase_mask));
 }
 
 extern "C" {
@@ -369,6 +379,24 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const mla_cache* ca
                      cache->batch, cache->t_max, seq_len, out, (char*)workspace, plan};
   set_pages(a, cache);
   return from_hip(mla::launch_prefill(a, stream));
+}
+
+int mla_rope_tables(int32_t rope_len, int32_t d_head, double theta, float* cos_out, float* sin_out) {
+  if (rope_len < 0 || d_head <= 0 || d_head % 2 != 0 || !(theta > 0.0) || !std::isfinite(theta))
+    return MLA_ERR_INVALID_ARG;
+  if (rope_len == 0) return MLA_OK;
+  if (!cos_out || !sin_out) return MLA_ERR_INVALID_ARG;
+  const int half = d_head / 2;
+  for (int p = 0; p < half; ++p) {
+    // subspace p turns at theta^(-2p/d_head) per position; angles and their cosines in fp64
+    const double freq = std::pow(theta, -2.0 * p / d_head);
+    for (int32_t t = 0; t < rope_len; ++t) {
+      const double ang = (double)t * freq;
+      cos_out[(size_t)t * half + p] = (float)std::cos(ang);
+      sin_out[(size_t)t * half + p] = (float)std::sin(ang);
+    }
+  }
+  return MLA_OK;
 }
 
 int mla_quantize_int4(const float* in, int64_t n_groups, uint8_t* codes, uint16_t* scales, hipStream_t stream) {

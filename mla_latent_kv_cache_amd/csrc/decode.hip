@@ -2023,20 +2023,22 @@ bool decode_step_fusable(const AppendArgs& aa, const DecodeArgs& da) {
          da.s.d_kv % 128 == 0;
 }
 
-hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, hipStream_t st) {
+hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, hipStream_t st, int phase_mask) {
   const int M = aa.batch * aa.t_new;
   const int ks = append_ksplit(aa.s, M);
   const int nx = (aa.s.d_kv + aa.s.n_rope_cols() + 31) / 32;
   const int n_qp = da.s.n_heads * (da.s.d_kv / 128) * ((da.batch + 31) / 32);
-  hipLaunchKernelGGL(decode_step_prologue, dim3(nx * ks + n_qp), dim3(256), 0, st, aa, ks, da);
+  if (phase_mask & 1) hipLaunchKernelGGL(decode_step_prologue, dim3(nx * ks + n_qp), dim3(256), 0, st, aa, ks, da);
   // the split-K reduction runs inside the attention launch when its kernel takes it
   if (aa.t_new <= FUSE_MAXR && attn_takes_append(da.s) && !aa.pm.bt) {
     FuseArgs f{aa, ks};
-    return launch_decode(da, st, 2 | 4, &f);
+    return launch_decode(da, st, phase_mask & 6, &f);
   }
-  hipError_t e = launch_append_reduce(aa, ks, st);
-  if (e != hipSuccess) return e;
-  return launch_decode(da, st, 2 | 4);
+  if (phase_mask & 2) {
+    hipError_t e = launch_append_reduce(aa, ks, st);
+    if (e != hipSuccess) return e;
+  }
+  return launch_decode(da, st, phase_mask & 6);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask, const FuseArgs* fuse) {

@@ -284,3 +284,40 @@ def test_static_step_rejects_oversized_request_on_the_host(lib):
     # invalid arguments are reported as for mla_decode_step, before the size
     assert lib.mla_decode_step_static(ctypes.byref(cfg(d_head=7)), ctypes.byref(w), ctypes.byref(k), FAKE, FAKE, 1,
                                       4095, FAKE, FAKE, 4096, FAKE, None) == INVALID
+
+
+def test_rope_tables_through_the_abi(lib):
+    """mla_rope_tables fills host buffers with cos / sin of pos * theta^(-2p/d_head) rounded to fp32: within
+    half an fp32 step of the fp64 values (a value in [-1, 1] rounds by at most 2^-25), exactly cos 0 = 1 and
+    sin 0 = 0 at position 0 and subspace 0 turning by one radian per position."""
+    import numpy as np
+
+    L, dh, theta = 300, 64, 1e4
+    cos = np.full((L, dh // 2), np.nan, dtype=np.float32)
+    sin = np.full_like(cos, np.nan)
+    assert lib.mla_rope_tables(L, dh, theta, cos.ctypes.data, sin.ctypes.data) == OK
+    ang = np.arange(L)[:, None] * theta ** (-2.0 * np.arange(dh // 2) / dh)
+    assert np.max(np.abs(cos - np.cos(ang))) <= 2.0 ** -25 * (1 + 1e-9)
+    assert np.max(np.abs(sin - np.sin(ang))) <= 2.0 ** -25 * (1 + 1e-9)
+    assert np.all(cos[0] == 1.0) and np.all(sin[0] == 0.0)
+    assert np.all(cos[:, 0] == np.cos(np.arange(L)).astype(np.float32))
+    # the binding's tables are the library's
+    from mla_latent_kv_cache_amd import rope_tables
+
+    c2, s2 = rope_tables(L, dh, theta)
+    assert np.array_equal(c2, cos) and np.array_equal(s2, sin)
+    for args in ((-1, dh, theta), (L, 7, theta), (L, 0, theta), (L, dh, 0.0), (L, dh, float("inf"))):
+        assert lib.mla_rope_tables(*args, cos.ctypes.data, sin.ctypes.data) == INVALID
+    assert lib.mla_rope_tables(L, dh, theta, None, sin.ctypes.data) == INVALID
+    assert lib.mla_rope_tables(0, dh, theta, None, None) == OK
+
+
+def test_decode_step_phase_rejects_bad_phase(lib):
+    c, w, k = cfg(), weights(), cache()
+    ws = lib.mla_decode_step_workspace_bytes(ctypes.byref(c), 32, 1, 4096)
+    for phase in (0, 4, -1):
+        assert lib.mla_decode_step_phase(phase, ctypes.byref(c), ctypes.byref(w), ctypes.byref(k), FAKE, FAKE, 1, 4095,
+                                         FAKE, FAKE, 4096, FAKE, FAKE, ws, None) == INVALID
+    # argument errors as for mla_decode_step
+    assert lib.mla_decode_step_phase(1, ctypes.byref(c), ctypes.byref(w), ctypes.byref(k), FAKE, FAKE, 1, 4095,
+                                     FAKE, FAKE, 4096, FAKE, FAKE, ws - 16, None) == WORKSPACE

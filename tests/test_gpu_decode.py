@@ -498,3 +498,48 @@ def test_decode_step_fused_rows(variant):
     # the new rows were written (not NaN) for every sequence, including rows past the decode length
     for b, c in enumerate(ctx):
         assert not torch.isnan(caches[0].krope[b, c:c + t_new].float()).any(), f"new RoPE rows of b={b} missing"
+
+
+@pytest.mark.parametrize("variant", ["bf16", "int4", "f32"])
+def test_decode_step_phases_match_the_step(variant):
+    """mla_decode_step_phase 1, 2, 3 in order equals mla_decode_step bit for bit (outputs and cache rows), for
+    the fused step (bf16, int4) and the unfused one (f32)."""
+    from mla_latent_kv_cache_amd import BoundDecode, LatentCache, append, pack_weights
+
+    if variant == "f32":
+        cfg = scaled(CONFIGS[0], batch=3)
+    elif variant == "int4":
+        cfg = scaled(CONFIGS[4], family="mid", batch=3)
+    else:
+        cfg = scaled(CONFIGS[1], family="mid", batch=3)
+    lens, t_max = [150, 3, 64], 160
+    log(f"[decode-step-phases] {variant} lens={lens}")
+    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    w = pack_weights(shape_of(cfg), layer, rope_len=t_max, theta=cfg.theta)
+    caches = [LatentCache.allocate(shape_of(cfg), len(lens), t_max, fill=float("nan")) for _ in range(2)]
+    xs = [synth.context_x(cfg, b, L) for b, L in enumerate(lens)]
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for cache in caches:
+        for b, L in enumerate(lens):
+            xt = torch.from_numpy(xs[b][: L - 1].astype(np.float32)).cuda().to(torch_dtype(cfg)).reshape(1, L - 1, -1)
+            append(w, cache.view(b, b + 1), xt, zero, 0)
+    x_new = torch.from_numpy(np.stack([x[-1] for x in xs])[:, None, :].astype(np.float32)).cuda().to(torch_dtype(cfg))
+    start = torch.tensor([L - 1 for L in lens], dtype=torch.int32, device="cuda")
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    q = np.stack([decode_query(cfg, layer, x[-1]) for x in xs])
+    qt = torch.from_numpy(q.astype(np.float32)).cuda().to(torch_dtype(cfg))
+    outs = [torch.full_like(qt, float("nan")) for _ in range(2)]
+    bd = [BoundDecode(w, caches[i], x_new.contiguous(), start, max(lens) - 1, qt, lens_t, max(lens), outs[i])
+          for i in range(2)]
+    bd[0].step()
+    for p in (1, 2, 3):
+        bd[1].step_phase(p)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]), "the step's phases differ from the step"
+    for name in ("ckv", "krope"):
+        a, b_ = getattr(caches[0], name), getattr(caches[1], name)
+        assert torch.equal(a.contiguous().view(torch.uint8), b_.contiguous().view(torch.uint8)), name
+    if cfg.cache_fmt == "dense":
+        c, kr = oracle_cache(cfg, layer, xs[0])
+        ref = oracle.decode_ref(q[0], c, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head, cfg.theta)
+        assert_close(_to_np(outs[1])[0], ref, cfg.dtype, "phases b=0")
