@@ -22,14 +22,14 @@ rate of an in-tree streaming-read kernel over a 2 GiB buffer (libmla_bandwidth.s
 The cpu_baseline object times the oracle (plain fp64 numpy; the library never uses it) on the host's cores:
 its conversion of the layer, then the cache fill + unabsorbed decode of whole sequences of the same workload
 (a bounded sample), each timed apart.  Secondary workloads (long-context variable-length decode, int4-latent
-decode, 2-bit-latent decode with a 128-row bf16 window, the headline decode on a paged cache of 64-token pages
-in random order, a 4-query multi-query decode, causal prefill) are reported in `secondary`.
+decode, 2-bit- and int4-latent decode with a 128-row bf16 window, the headline decode on a paged cache of
+64-token pages in random order, a 4-query multi-query decode, causal prefill) are reported in `secondary`.
 
 `roofline.traffic` is the HBM traffic of one launch of that kernel from FETCH_SIZE / WRITE_SIZE counter
 runs (profiles/pmc_traffic.json, scaled by the counters of a plain copy of known size, see
 --copy-calibration); it is null when those counters were taken on different decode sources.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only bw,c1,c3,c4,c5,c6,c7,c2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only bw,c1,c3,c4,c5,c8,c6,c7,c2] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -61,8 +61,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="bw,c1,c3,c4,c5,c6,c7,c2")
+    ap.add_argument("--only", default="bw,c1,c3,c4,c5,c8,c6,c7,c2")
     ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--replays", type=int, default=50, help="graph replays the median step time is taken over (>= 50 "
+                                                             "for a reported figure; fewer for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -289,6 +291,9 @@ def median_replay_ms(graphs, replays, warmup):
     return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
 
 
+REPLAYS = 50
+
+
 def time_decode(wl, steps, warmup, check=True):
     """Step time: the median over >= 50 replays of a graph of STEPS_PER_GRAPH consecutive steps, per step;
     the median of single-step graph replays (one step in isolation, the graph launch included); the mean of
@@ -298,8 +303,8 @@ def time_decode(wl, steps, warmup, check=True):
     bound = wl["bound"]
     n = len(bound)
     single, multi = capture_steps(bound, check)
-    step_ms = median_replay_ms([multi], max(50, steps), warmup) / STEPS_PER_GRAPH
-    lat_ms = median_replay_ms(single, max(50, steps), warmup)
+    step_ms = median_replay_ms([multi], max(REPLAYS, steps), warmup) / STEPS_PER_GRAPH
+    lat_ms = median_replay_ms(single, max(REPLAYS, steps), warmup)
     del single, multi
     for i in range(warmup):
         bound[i % n].step()
@@ -427,7 +432,7 @@ def prefill_result(cfg, conv, steps, warmup):
     torch.cuda.synchronize()
     if not torch.equal(out, ref):
         raise RuntimeError("a graph replay of the prefill differs from the eager call")
-    ms = median_replay_ms([graph], max(20, steps), warmup)
+    ms = median_replay_ms([graph], max(min(20, REPLAYS), steps), warmup)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(steps):
@@ -530,6 +535,8 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     only = set(args.only.split(","))
+    global REPLAYS
+    REPLAYS = args.replays
     C = synth.CONFIGS
     if args.copy_calibration:
         copy_calibration()
@@ -583,6 +590,18 @@ def main():
         del wl5
         torch.cuda.empty_cache()
 
+    if "c8" in only:
+        # the int4 workload's shape with a bf16 window of the last 128 rows (older rows int4 codes of their bf16
+        # values), as the README page's quantised-cache evaluation keeps its most recent tokens unquantised
+        cfg8 = synth.scaled(C[4], name="llama_int4w_decode", cache_fmt="int4_g32_win")
+        wl8 = make_decode_workload(cfg8, conv_main, synth.seq_lens(cfg8), args.copies, seed=1008)
+        r8 = decode_result("llama_int4w_decode", cfg8, wl8, args.steps, args.warmup, check=False)
+        r8.update(hbm_frac=r8["kernel_gbs"] / HBM_PEAK_GBS, window=wl8["caches"][0].window,
+                  kernel="decode_attn_mfma<128, 8, 3>")
+        secondary["llama_int4w_decode"] = r8
+        del wl8
+        torch.cuda.empty_cache()
+
     if "c2" in only:
         secondary["llama_bf16_prefill"] = prefill_result(C[2], conv_main, max(2, args.steps // 5), max(1, args.warmup // 5))
         torch.cuda.empty_cache()
@@ -621,7 +640,7 @@ def main():
                                "mla_decode_step (append of the new token + decode)",
                    "batch": 32, "context": 4096, "d_kv": 512, "r_pairs": 4, "cache_bytes_per_step": main_res["bytes"],
                    "parallelism": "single GPU",
-                   "timing": f"median over {max(50, args.steps)} replays of a HIP graph of {STEPS_PER_GRAPH} "
+                   "timing": f"median over {max(REPLAYS, args.steps)} replays of a HIP graph of {STEPS_PER_GRAPH} "
                              f"consecutive steps (3 cache copies in rotation), per step"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -62,13 +62,15 @@ typedef enum {
   MLA_CACHE_DENSE = 0,       /* c_kv stored in the config dtype                                */
   MLA_CACHE_INT4_G32 = 1,    /* c_kv as int4 codes, groups of 32 latent dims, fp16 absmax scale;
                                 k_rope stays in the config dtype (BF16 only)                    */
-  MLA_CACHE_INT2_G32_WIN = 2 /* c_kv of the last `window` positions of each sequence as bf16 rows
+  MLA_CACHE_INT2_G32_WIN = 2,/* c_kv of the last `window` positions of each sequence as bf16 rows
                                 in a ring, older positions as affine 2-bit codes (groups of 32
                                 latent dims, fp16 scale and offset); k_rope bf16 (BF16 only)    */
+  MLA_CACHE_INT4_G32_WIN = 3 /* the same window of bf16 rows, older positions as the INT4_G32 codes
+                                of their bf16 values (BF16 only)                                */
 } mla_cache_fmt;
 
-/* Layer shape.  d_head even; 0 <= r_pairs <= d_head/2; d_kv >= 1 (multiple of 32 for the INT4_G32
- * and INT2_G32_WIN formats). */
+/* Layer shape.  d_head even; 0 <= r_pairs <= d_head/2; d_kv >= 1 (multiple of 32 for the quantised
+ * formats). */
 typedef struct {
   int32_t d_model;   /* model width d                                            */
   int32_t n_heads;   /* attention heads n_h                                      */
@@ -106,10 +108,13 @@ typedef struct {
  *             ckv_window [batch, window, d_kv] bf16 ring: slot pos % window holds position pos while
  *                                             pos >= L - window (L = the sequence's length)
  *             window >= 0 (0: every row is codes); ckv_window may be NULL when window == 0
+ *   INT4_G32_WIN: ckv and ckv_scale as INT4_G32 (row pos holds position pos once it has left the window),
+ *             ckv_window and window as INT2_G32_WIN
  *   all:      krope [batch, t_max, n_h, 2r]   config dtype, pair (j, c) of head h at index h*2r + 2j + c
- * ckv_window and window are read for INT2_G32_WIN only.
+ * ckv_window and window are read for the windowed formats (INT2_G32_WIN, INT4_G32_WIN) only.
  *
- * Paged caches (block_table != NULL; DENSE and INT4_G32): ckv, ckv_scale and krope hold a pool of
+ * Paged caches (block_table != NULL; DENSE and INT4_G32, not the windowed formats): ckv, ckv_scale and krope
+ * hold a pool of
  * n_pages pages of page_size rows each (the row layouts above, n_pages * page_size rows in place of
  * batch * t_max), and position pos of sequence b is pool row
  *     block_table[b * pages_per_seq + pos / page_size] * page_size + pos % page_size.
@@ -141,12 +146,13 @@ typedef struct {
  * Per token:  c_kv = x . W_dkv (fp32 accumulate, then rounded to the dtype, or quantised:
  *             s = fp16(absmax/7), code = clamp(rint(c/s), -7, 7), IEEE fp32 divisions);
  *             k_rope[h, j] = rotate((x . W_krope)[h, j, 0:2], pos * theta^(-2p/d_h)).
- * INT2_G32_WIN: each append must extend its sequences (start_pos[b] = the current length, all earlier
+ * Windowed formats: each append must extend its sequences (start_pos[b] = the current length, all earlier
  *             positions written by earlier appends).  A row c_kv is rounded to bf16; rows that end up
  *             among the last `window` positions go to the ring, every other row (a new one, or one
- *             pushed out of the ring) is quantised from its bf16 value per group of 32:
+ *             pushed out of the ring) is quantised from its bf16 value per group of 32 -- INT2_G32_WIN:
  *             z = fp16(min), s = fp16(max(max - z, 0) / 3), code = clamp(rint((c - z) / s), 0, 3)
- *             (fp32 arithmetic, IEEE division; s == 0 gives codes 0; infinite fp16 values saturate).
+ *             (fp32 arithmetic, IEEE division; s == 0 gives codes 0; infinite fp16 values saturate);
+ *             INT4_G32_WIN: the int4 codec above on the bf16 values.
  * t_new == 0 or batch == 0 is a no-op returning MLA_OK.                                        */
 int mla_cache_append(const mla_config *cfg, const mla_weights *w, mla_cache *cache, const void *x,
                      const int32_t *start_pos, int32_t t_new, int32_t max_start_pos, hipStream_t stream);
@@ -166,7 +172,7 @@ int mla_cache_append_ws(const mla_config *cfg, const mla_weights *w, mla_cache *
  * key-designs section: W_uk,h folded into the query, W_uv,h applied after the weighted latent sum).
  *   q          [batch, n_h, d_h] raw query (x . W_q, before RoPE, original head-dim order)
  *   seq_lens   [batch] int32 (device): L_b cached tokens, the query sits at position L_b - 1
- *              (append it first); L_b == 0 gives a zero output row.  INT2_G32_WIN: L_b must be the
+ *              (append it first); L_b == 0 gives a zero output row.  Windowed formats: L_b must be the
  *              sequence's appended length (the ring holds its last `window` positions)
  *   max_seq_len  host bound on seq_lens[], 0 <= max_seq_len <= t_max and <= rope_len
  *   out        [batch, n_h, d_h] per-head attention outputs (before the output projection)
@@ -237,7 +243,7 @@ int mla_decode_step_static(const mla_config *cfg, const mla_weights *w, mla_cach
  * L_b - q_len + i and attends to positions 0 .. L_b - q_len + i; a query at a negative position gives a
  * zero output row.  Same computation per query as mla_decode (q_len == 1 is mla_decode).
  *   q    [batch, q_len, n_h, d_h] raw queries;   out [batch, q_len, n_h, d_h]
- * DENSE and INT4_G32 caches, contiguous or paged (INT2_G32_WIN with q_len > 1: MLA_ERR_UNSUPPORTED).
+ * DENSE and INT4_G32 caches, contiguous or paged (windowed formats with q_len > 1: MLA_ERR_UNSUPPORTED).
  * Workspace: mla_decode_multi_workspace_bytes(cfg, batch, q_len, max_seq_len) bytes.               */
 size_t mla_decode_multi_workspace_bytes(const mla_config *cfg, int32_t batch, int32_t q_len, int32_t max_seq_len);
 int mla_decode_multi(const mla_config *cfg, const mla_weights *w, const mla_cache *cache, const void *q, int32_t q_len,
@@ -251,7 +257,11 @@ int mla_decode_multi(const mla_config *cfg, const mla_weights *w, const mla_cach
  * keys, which cannot be merged into the matrices, are read from the cache; for a whole prompt this
  * rebuilds each token's keys and values once instead of folding W_uk,h into every query.
  *   q    [batch, seq_len, n_h, d_h] raw queries;   out [batch, seq_len, n_h, d_h]
- * BF16 dense caches only (MLA_ERR_UNSUPPORTED otherwise).
+ * BF16 layers with d_head 128 and d_kv a multiple of 64 (MLA_ERR_UNSUPPORTED otherwise), any cache format:
+ * a quantised latent (INT4_G32, contiguous or paged; INT2_G32_WIN) is first dequantised into the workspace
+ * exactly as decode reads it (int4: code * scale; 2-bit: z + code * s, the window's rows from the ring; then
+ * rounded to bf16).  Windowed formats: every sequence's appended length must be seq_len (the ring then holds
+ * positions seq_len - window .. seq_len - 1).
  * Workspace: mla_prefill_workspace_bytes(cfg, batch, seq_len) bytes.                           */
 size_t mla_prefill_workspace_bytes(const mla_config *cfg, int32_t batch, int32_t seq_len);
 int mla_prefill(const mla_config *cfg, const mla_weights *w, const mla_cache *cache, const void *q,

@@ -11,7 +11,7 @@ LIB_PATH = os.environ.get("MLA_LATENT_LIB") or os.path.join(PKG, "libmla_latent.
 
 MLA_OK = 0
 MLA_F32, MLA_BF16 = 0, 1
-MLA_CACHE_DENSE, MLA_CACHE_INT4_G32, MLA_CACHE_INT2_G32_WIN = 0, 1, 2
+MLA_CACHE_DENSE, MLA_CACHE_INT4_G32, MLA_CACHE_INT2_G32_WIN, MLA_CACHE_INT4_G32_WIN = 0, 1, 2, 3
 
 EXPORTED = [
     "mla_cache_append",

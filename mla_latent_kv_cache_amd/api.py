@@ -15,10 +15,12 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import (MLA_BF16, MLA_CACHE_DENSE, MLA_CACHE_INT2_G32_WIN, MLA_CACHE_INT4_G32, MLA_F32, MlaCache, MlaConfig,
-                   MlaWeights)
+from ._lib import (MLA_BF16, MLA_CACHE_DENSE, MLA_CACHE_INT2_G32_WIN, MLA_CACHE_INT4_G32, MLA_CACHE_INT4_G32_WIN,
+                   MLA_F32, MlaCache, MlaConfig, MlaWeights)
 
-_FMT = {"dense": MLA_CACHE_DENSE, "int4_g32": MLA_CACHE_INT4_G32, "int2_g32_win": MLA_CACHE_INT2_G32_WIN}
+_FMT = {"dense": MLA_CACHE_DENSE, "int4_g32": MLA_CACHE_INT4_G32, "int2_g32_win": MLA_CACHE_INT2_G32_WIN,
+        "int4_g32_win": MLA_CACHE_INT4_G32_WIN}
+WINDOWED = ("int2_g32_win", "int4_g32_win")
 
 
 class MlaError(RuntimeError):
@@ -43,7 +45,7 @@ class LayerShape:
     r_pairs: int
     d_kv: int
     dtype: str = "bf16"  # "bf16" or "f32"
-    cache_fmt: str = "dense"  # "dense", "int4_g32" or "int2_g32_win"
+    cache_fmt: str = "dense"  # "dense", "int4_g32", "int2_g32_win" or "int4_g32_win"
 
     @property
     def torch_dtype(self):
@@ -154,9 +156,10 @@ def pack_weights(shape: LayerShape, conv: dict, rope_len: int, theta: float = 1e
 
 @dataclass
 class LatentCache:
-    """Latent cache for `batch` sequences of up to t_max tokens (layouts of mla_cache).  For the
-    "int2_g32_win" format, ckv holds 2-bit codes, ckv_scale (s, z) pairs per group of 32, and ckv_window
-    the bf16 ring of each sequence's last `window` rows."""
+    """Latent cache for `batch` sequences of up to t_max tokens (layouts of mla_cache).  For the windowed formats
+    ckv_window is the bf16 ring of each sequence's last `window` rows, and ckv / ckv_scale hold the older rows'
+    codes: 2-bit codes and (s, z) pairs per group of 32 ("int2_g32_win"), or int4 codes and fp16 scales
+    ("int4_g32_win")."""
 
     shape: LayerShape
     ckv: torch.Tensor
@@ -175,12 +178,14 @@ class LatentCache:
     @staticmethod
     def allocate(shape: LayerShape, batch: int, t_max: int, device="cuda", fill: Optional[float] = None,
                  window: int = 128):
-        """`window` (int2_g32_win only) is the number of recent rows kept in bf16 per sequence."""
+        """`window` (windowed formats only) is the number of recent rows kept in bf16 per sequence."""
         nr = shape.n_heads * 2 * shape.r_pairs
         ring = None
-        if shape.cache_fmt == "int4_g32":
+        if shape.cache_fmt in ("int4_g32", "int4_g32_win"):
             ckv = torch.zeros((batch, t_max, shape.d_kv // 2), dtype=torch.uint8, device=device)
             scale = torch.zeros((batch, t_max, shape.d_kv // 32), dtype=torch.float16, device=device)
+            if shape.cache_fmt == "int4_g32_win":
+                ring = torch.empty((batch, max(window, 1), shape.d_kv), dtype=torch.bfloat16, device=device)
         elif shape.cache_fmt == "int2_g32_win":
             ckv = torch.zeros((batch, t_max, shape.d_kv // 4), dtype=torch.uint8, device=device)
             scale = torch.zeros((batch, t_max, shape.d_kv // 32, 2), dtype=torch.float16, device=device)
@@ -196,14 +201,14 @@ class LatentCache:
                 ring.fill_(fill)
             krope.fill_(fill)
         return LatentCache(shape, ckv, scale, krope, batch, t_max, ring,
-                           window if shape.cache_fmt == "int2_g32_win" else 0)
+                           window if shape.cache_fmt in WINDOWED else 0)
 
     @staticmethod
     def allocate_paged(shape: LayerShape, block_table: torch.Tensor, page_size: int, n_pages: int, device="cuda",
                        fill: Optional[float] = None):
         """A paged cache: pools of n_pages pages of page_size rows and the page table block_table [batch,
         pages_per_seq] (int32, device); each sequence holds up to pages_per_seq * page_size tokens."""
-        if shape.cache_fmt == "int2_g32_win":
+        if shape.cache_fmt in WINDOWED:
             raise ValueError("paged caches hold dense or int4 latents")
         batch, pps = block_table.shape
         nr = shape.n_heads * 2 * shape.r_pairs
@@ -239,7 +244,7 @@ class LatentCache:
                         self.n_pages)
 
     def nbytes_per_token(self) -> int:
-        """Bytes per cached position (the ring of an int2_g32_win cache is a fixed extra per sequence)."""
+        """Bytes per cached position (the ring of a windowed cache is a fixed extra per sequence)."""
         n = self.ckv[0, 0].numel() * self.ckv.element_size() + self.krope[0, 0].numel() * self.krope.element_size()
         if self.ckv_scale is not None:
             n += self.ckv_scale[0, 0].numel() * 2

@@ -15,13 +15,19 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Formats whose last `window` rows per sequence are bf16 rows in a ring.
+bool windowed(const mla_config* c) {
+  return c->cache_fmt == MLA_CACHE_INT2_G32_WIN || c->cache_fmt == MLA_CACHE_INT4_G32_WIN;
+}
+
 // Shape-only checks shared by every entry point.
 int check_config(const mla_config* c) {
   if (!c) return MLA_ERR_INVALID_ARG;
   if (c->d_model <= 0 || c->n_heads <= 0 || c->d_head <= 0 || c->d_kv <= 0) return MLA_ERR_INVALID_ARG;
   if (c->d_head % 2 != 0 || c->r_pairs < 0 || 2 * c->r_pairs > c->d_head) return MLA_ERR_INVALID_ARG;
   if (c->dtype != MLA_F32 && c->dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
-  if (c->cache_fmt != MLA_CACHE_DENSE && c->cache_fmt != MLA_CACHE_INT4_G32 && c->cache_fmt != MLA_CACHE_INT2_G32_WIN)
+  if (c->cache_fmt != MLA_CACHE_DENSE && c->cache_fmt != MLA_CACHE_INT4_G32 && c->cache_fmt != MLA_CACHE_INT2_G32_WIN &&
+      c->cache_fmt != MLA_CACHE_INT4_G32_WIN)
     return MLA_ERR_INVALID_ARG;
   if (c->d_head > 256) return MLA_ERR_UNSUPPORTED;
   if (c->cache_fmt != MLA_CACHE_DENSE && (c->dtype != MLA_BF16 || c->d_kv % 32 != 0)) return MLA_ERR_UNSUPPORTED;
@@ -66,7 +72,7 @@ int check_cache(const mla_config* c, const mla_cache* k) {
   MLA_TRY(check_ptr(k->ckv, true));
   MLA_TRY(check_ptr(k->krope, c->r_pairs > 0));
   MLA_TRY(check_ptr(k->ckv_scale, c->cache_fmt != MLA_CACHE_DENSE));
-  if (c->cache_fmt == MLA_CACHE_INT2_G32_WIN) {
+  if (windowed(c)) {
     if (k->window < 0) return MLA_ERR_INVALID_ARG;
     MLA_TRY(check_ptr(k->ckv_window, k->window > 0));
   }
@@ -76,7 +82,7 @@ int check_cache(const mla_config* c, const mla_cache* k) {
       return MLA_ERR_INVALID_ARG;
     if ((long long)k->pages_per_seq * k->page_size != k->t_max) return MLA_ERR_INVALID_ARG;
     if ((long long)k->n_pages * k->page_size > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
-    if (c->cache_fmt == MLA_CACHE_INT2_G32_WIN) return MLA_ERR_UNSUPPORTED;
+    if (windowed(c)) return MLA_ERR_UNSUPPORTED;
   } else if ((long long)k->batch * k->t_max > 0x7fffffffLL) {
     return MLA_ERR_UNSUPPORTED;  // cache rows are indexed with 32-bit integers
   }
@@ -102,7 +108,7 @@ void set_pages(Args& a, const mla_cache* k) {
 template <typename Args>
 void set_window(Args& a, const mla_config* c, const mla_cache* k) {
   set_pages(a, k);
-  if (c->cache_fmt != MLA_CACHE_INT2_G32_WIN) return;
+  if (!windowed(c)) return;
   a.ckv_win = k->ckv_window;
   a.win = k->window;
 }
@@ -182,7 +188,7 @@ static int decode_impl(int phase_mask, const mla_config* cfg, const mla_weights*
   MLA_TRY(check_weights(cfg, w, false, true));
   MLA_TRY(check_cache(cfg, cache));
   if (max_seq_len < 0 || q_len < 1) return MLA_ERR_INVALID_ARG;
-  if (q_len > 1 && cfg->cache_fmt == MLA_CACHE_INT2_G32_WIN) return MLA_ERR_UNSUPPORTED;
+  if (q_len > 1 && windowed(cfg)) return MLA_ERR_UNSUPPORTED;
   if (cache->batch == 0) return MLA_OK;
   MLA_TRY(check_ptr(q, true));
   MLA_TRY(check_ptr(seq_lens, true));
@@ -377,7 +383,8 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const mla_cache* ca
   if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
   mla::PrefillArgs a{s, q, w->w_uk, w->w_uv, w->pair_idx, w->rope_cos, w->rope_sin, cache->ckv, cache->krope,
                      cache->batch, cache->t_max, seq_len, out, (char*)workspace, plan};
-  set_pages(a, cache);
+  set_window(a, cfg, cache);
+  a.ckv_scale = cache->ckv_scale;
   return from_hip(mla::launch_prefill(a, stream));
 }
 

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void append_generic(AppendArgs a) {
   if (a.s.fmt == 0) {
     T* ckv = (T*)a.ckv + row * D;
     for (int n = threadIdx.x; n < D; n += blockDim.x) ckv[n] = from_f32<T>(outs[n]);
-  } else if (a.s.fmt == 2) {
+  } else if (a.s.fmt >= 2) {
     for (int g = threadIdx.x; g < D / 32; g += blockDim.x) store_group_win2(a, m / a.t_new, pos, g, outs + 32 * g, 1);
   } else {
     uint8_t* codes = (uint8_t*)a.ckv + row * (D / 2);
@@ -153,8 +153,8 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
 
   // ---- epilogue
   const int r = a.s.r_pairs, R2 = a.s.r2(), half = a.s.d_head / 2;
-  if (a.s.fmt == 2 && n0 < D) {
-    // 2-bit latent: the tile's latent columns go to LDS (token rows 0-63 in sA, 64-127 in sB, which the
+  if (a.s.fmt >= 2 && n0 < D) {
+    // windowed latent (2-bit or int4 codes): the tile's latent columns go to LDS (token rows 0-63 in sA, 64-127 in sB, which the
     // main loop no longer reads), then one thread per (token, group of 32 columns) codes or windows it
     constexpr int SP = TN + 1;
     float* stg0 = (float*)&sA[0][0];
@@ -193,8 +193,8 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
             const int ml = wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
             if (m0 + ml < M) ((bf16*)a.ckv)[(size_t)rows[ml] * D + n] = (bf16)acc[i][j][e];
           }
-        } else if (a.s.fmt == 2) {
-          // staged through LDS below
+        } else if (a.s.fmt >= 2) {
+          // staged through LDS above
         } else {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
@@ -258,7 +258,7 @@ __device__ __forceinline__ void append_gemm_block(const AppendArgs& a, const f32
         const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         if (m0 + ml < M) ((bf16*)a.ckv)[(size_t)rows[ml] * D + n] = (bf16)v[e];
       }
-    } else if (a.s.fmt == 2) {
+    } else if (a.s.fmt >= 2) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);

@@ -391,6 +391,9 @@ __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
   // element k of the latent at position pos (from the window when `win`)
   auto lat = [&](int pos, bool win, int k) {
     if constexpr (FMT == 2) return latent2(a, b, pos, win, k);
+    else if constexpr (FMT == 3)  // int4 codes with a window of bf16 rows
+      return win ? (float)((const bf16*)a.ckv_win)[((size_t)cseq(a, b) * a.win + pos % a.win) * a.s.d_kv + k]
+                 : latent<T, 1>(a, (size_t)seq_row(a, b, pos), k);
     else return latent<T, FMT>(a, (size_t)seq_row(a, b, pos), k);
   };
   for (int h = 0; h < NH; ++h) {
@@ -532,6 +535,10 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   __shared__ int fbuf[4];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5, h = lane & 31;
+  // the code layout (0 dense, 1 int4, 2 2-bit) and whether the format keeps a window of bf16 rows (fmt 2: 2-bit
+  // codes, fmt 3: int4 codes)
+  constexpr int CODEC = FMT == 3 ? 1 : FMT;
+  constexpr bool HAS_WIN = FMT >= 2;
   static_assert(sizeof(cbuf) >= fuse_scratch_bytes(D, 32 * R2), "fused append scratch");
   if (blockIdx.x >= a.plan.max_items) {
     fused_orphans(a, f, (float*)cbuf);
@@ -540,7 +547,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   WorkItem wi;
   if (!locate_item(a, blockIdx.x, wi)) return;
   const int b = wi.b;
-  // the tile loop runs over [wi.t0, wi.t1) and then (2-bit format) over the window [wi.w0, wi.w1), whose rows
+  // the tile loop runs over [wi.t0, wi.t1) and then (windowed formats) over the window [wi.w0, wi.w1), whose rows
   // come from the ring (the WIN instances of load_tile / step); t1 is the end of the current run
   int t1 = wi.t1;
   if (fused_rows(f, b, wi.t0, wi.t1, (float*)cbuf)) MLA_WAIT_VMCNT(0);
@@ -576,24 +583,24 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
 
   // ---- register prefetch, two tiles deep: this wave's latent slice and its share of the RoPE keys
   // 16-byte chunks per row of the wave's slice: 8 bf16, 32 int4 or 64 2-bit latents each
-  constexpr int CPR = (FMT == 0) ? DW / 8 : (FMT == 1 ? DW / 32 : DW / 64);
+  constexpr int CPR = (CODEC == 0) ? DW / 8 : (CODEC == 1 ? DW / 32 : DW / 64);
   constexpr int CCH = 32 * CPR / 64;                  // chunks per lane
   typedef bf16 kv_t __attribute__((ext_vector_type(R2)));
   // per chunk: one fp16 scale (int4) or two (s, z) pairs of fp16 (2-bit: two groups of 32)
-  using meta_t = std::conditional_t<FMT == 2, uint2, uint16_t>;
+  using meta_t = std::conditional_t<CODEC == 2, uint2, uint16_t>;
   u32x4 creg[2][CCH];
   meta_t sreg[2][CCH];
   kv_t kreg[2][4];
 
   // full tiles: a wave-uniform tile base plus per-lane offsets that do not change per tile
-  constexpr int RBY = FMT == 0 ? D * 2 : (FMT == 1 ? D / 2 : D / 4);  // latent bytes per cache row
-  constexpr int MBY = FMT == 2 ? 4 : 2;                                // metadata bytes per group
+  constexpr int RBY = CODEC == 0 ? D * 2 : (CODEC == 1 ? D / 2 : D / 4);  // latent bytes per cache row
+  constexpr int MBY = CODEC == 2 ? 4 : 2;                                  // metadata bytes per group
   uint32_t coff[CCH], soff[CCH];
 #pragma unroll
   for (int it = 0; it < CCH; ++it) {
     const int c = it * 64 + lane, row = c / CPR, q = c - row * CPR;
-    coff[it] = row * RBY + (FMT == 0 ? 2 * (w * DW + 8 * q) : (FMT == 1 ? (w * DW + 32 * q) / 2 : (w * DW + 64 * q) / 4));
-    soff[it] = MBY * (row * (D / 32) + (w * DW) / 32 + (FMT == 2 ? 2 * q : q));
+    coff[it] = row * RBY + (CODEC == 0 ? 2 * (w * DW + 8 * q) : (CODEC == 1 ? (w * DW + 32 * q) / 2 : (w * DW + 64 * q) / 4));
+    soff[it] = MBY * (row * (D / 32) + (w * DW) / 32 + (CODEC == 2 ? 2 * q : q));
   }
   const uint32_t koff = ((xt0 * 32 + xh) * R2) * 2;  // RoPE keys of the lane's 4 tokens, head xh
   // window items (2-bit format) stage their bf16 rows straight from the ring in stage_window and
@@ -612,7 +619,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
 #pragma unroll
         for (int it = 0; it < CCH; ++it) {
           creg[B][it] = *(const u32x4*)(cb + coff[it]);
-          if constexpr (FMT != 0) sreg[B][it] = *(const meta_t*)(sb + soff[it]);
+          if constexpr (CODEC != 0) sreg[B][it] = *(const meta_t*)(sb + soff[it]);
         }
       }
 #pragma unroll
@@ -627,7 +634,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
         const char* cb = (const char*)a.ckv + (row0 + tok - tt + tb) * RBY;
         const char* sb = (const char*)a.ckv_scale + (row0 + tok - tt + tb) * (D / 32) * MBY;
         creg[B][it] = *(const u32x4*)(cb + coff[it] - row * RBY);
-        if constexpr (FMT != 0) sreg[B][it] = *(const meta_t*)(sb + soff[it] - MBY * row * (D / 32));
+        if constexpr (CODEC != 0) sreg[B][it] = *(const meta_t*)(sb + soff[it] - MBY * row * (D / 32));
       }
     }
 #pragma unroll
@@ -641,9 +648,9 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
 #pragma unroll
     for (int it = 0; it < CCH; ++it) {
       int c = it * 64 + lane, row = c / CPR, q = c - row * CPR;
-      if constexpr (FMT == 0) {
+      if constexpr (CODEC == 0) {
         *(u32x4*)&cw[row * CP + 8 * q] = creg[B][it];
-      } else if constexpr (FMT == 2) {
+      } else if constexpr (CODEC == 2) {
         const uint32_t wd[4] = {creg[B][it].x, creg[B][it].y, creg[B][it].z, creg[B][it].w};
         const uint32_t mg[2] = {sreg[B][it].x, sreg[B][it].y};
 #pragma unroll
@@ -805,7 +812,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
     }
   };
   if (wi.t0 < wi.t1) run(std::false_type{}, wi.t0, wi.t1);
-  if constexpr (FMT == 2) {
+  if constexpr (HAS_WIN) {
     if (wi.w0 < wi.w1) run(std::true_type{}, wi.w0, wi.w1);
   }
 
@@ -1930,8 +1937,10 @@ void launch_generic_attn(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_attn_generic<T, 0>), grid, dim3(256), shmem, st, a);
   else if (a.s.fmt == 1)
     hipLaunchKernelGGL((decode_attn_generic<T, 1>), grid, dim3(256), shmem, st, a);
-  else
+  else if (a.s.fmt == 2)
     hipLaunchKernelGGL((decode_attn_generic<T, 2>), grid, dim3(256), shmem, st, a);
+  else
+    hipLaunchKernelGGL((decode_attn_generic<T, 3>), grid, dim3(256), shmem, st, a);
 }
 
 template <int DW, int R2>
@@ -1946,8 +1955,10 @@ void launch_mfma_attn(const DecodeArgs& a, const FuseArgs& f, hipStream_t st) {
       hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 1, true>), attn_grid(a, f), dim3(256), 0, st, a, f);
     else
       hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 1, false>), attn_grid(a, f), dim3(256), 0, st, a, f);
-  else
+  else if (a.s.fmt == 2)
     hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 2, false>), attn_grid(a, f), dim3(256), 0, st, a, f);  // never paged
+  else
+    hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 3, false>), attn_grid(a, f), dim3(256), 0, st, a, f);  // never paged
 }
 
 }  // namespace

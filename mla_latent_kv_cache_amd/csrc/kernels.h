@@ -11,7 +11,7 @@ namespace mla {
 struct Shape {
   int d_model, n_heads, d_head, r_pairs, d_kv;
   int dtype;  // 0 f32, 1 bf16
-  int fmt;    // 0 dense, 1 int4 g32, 2 int2 g32 with a bf16 window of recent rows
+  int fmt;    // 0 dense, 1 int4 g32, 2 int2 g32 with a bf16 window of recent rows, 3 int4 g32 with that window
   __host__ __device__ int r2() const { return 2 * r_pairs; }
   __host__ __device__ int d_nope() const { return d_head - 2 * r_pairs; }
   __host__ __device__ int n_rope_cols() const { return n_heads * 2 * r_pairs; }
@@ -85,10 +85,11 @@ struct DecodeArgs {
 };
 
 // Prefill workspace: K [b, h, s_pad, 128] and V^T [b, h, 128, s_pad] bf16, s_pad = seq_len rounded up
-// to the 64-key tile.
+// to the 64-key tile; for a quantised latent (fmt 1, 2) also the dequantised latent rows [b, seq_len, d_kv]
+// bf16 that the reconstruction reads.
 struct PrefillPlan {
   int s_pad;
-  size_t off_k, off_vt, total;
+  size_t off_k, off_vt, off_lat, total;
 };
 PrefillPlan plan_prefill(const Shape& s, int batch, int seq_len);
 
@@ -103,6 +104,10 @@ struct PrefillArgs {
   char* ws;
   PrefillPlan plan;
   PageMap pm{};
+  const void* ckv_scale = nullptr;  // fmt 1: fp16 scales; fmt 2: fp16 (s, z) pairs
+  const void* ckv_win = nullptr;    // fmt 2: ring of the last `win` rows per sequence [batch, win, d_kv] bf16
+  int win = 0;
+  int lat_staged = 0;  // set by the launcher: latent rows come from the workspace's dequantised copy
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);  // uses a.ws when set and useful

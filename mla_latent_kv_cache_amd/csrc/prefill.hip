@@ -52,11 +52,45 @@ __device__ __forceinline__ int xcd_tile(int bid, int total) {
   return (total & 7) == 0 ? (bid & 7) * (total >> 3) + (bid >> 3) : bid;
 }
 
+// Latent rows 0 .. S-1 of every sequence of a quantised cache, dequantised as the decode kernels do (int4:
+// fp32(code) * fp32(scale); 2-bit: fp32(z + code * s) in one rounding; for the windowed formats the last
+// `win` positions from the bf16 ring, slot t % win) and rounded to bf16 into the workspace [batch, S, d_kv]: the latent operand of the
+// reconstruction GEMMs.  One lane per 8 latent values (16 output bytes).
+__global__ __launch_bounds__(256) void prefill_stage_latent(PrefillArgs a) {
+  const int D = a.s.d_kv, S = a.seq_len, per_row = D / 8;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)a.batch * S * per_row) return;
+  const int c8 = (int)(idx % per_row);
+  const size_t bt = idx / per_row;
+  const int b = (int)(bt / S), t = (int)(bt - (size_t)b * S);
+  bf16x8 v;
+  if (a.s.fmt >= 2 && t >= S - min(S, a.win)) {
+    v = *(const bf16x8*)((const bf16*)a.ckv_win + ((size_t)b * a.win + t % a.win) * D + 8 * c8);
+  } else {
+    const size_t row = (size_t)cache_row_of(a.pm, a.t_max, b, t);
+    const _Float16* meta = (const _Float16*)a.ckv_scale;
+    if (a.s.fmt == 1 || a.s.fmt == 3) {
+      const uint32_t w = *(const uint32_t*)((const uint8_t*)a.ckv + row * (D / 2) + 4 * c8);
+      const float sc = (float)meta[row * (D / 32) + c8 / 4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (bf16)((float)((int)(w << (28 - 4 * i)) >> 28) * sc);
+    } else {
+      const uint32_t w = *(const uint16_t*)((const uint8_t*)a.ckv + row * (D / 4) + 2 * c8);
+      const size_t g = (row * (D / 32) + c8 / 4) * 2;
+      const float sc = (float)meta[g], z = (float)meta[g + 1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (bf16)__builtin_fmaf((float)((w >> (2 * i)) & 3u), sc, z);
+    }
+  }
+  *(bf16x8*)((bf16*)(a.ws + a.plan.off_lat) + ((size_t)b * S + t) * D + 8 * c8) = v;
+}
+
 __global__ __launch_bounds__(256, 2) void rec_k_gemm(PrefillArgs a, int M) {
   __shared__ __attribute__((aligned(1024))) char lds[RecK::LDS_BYTES];
   __shared__ int dim_of[128];
   __shared__ int kept[64];
   __shared__ int crow[256], orow[256];  // cache row and output row of every token of the tile (-1: none)
+  __shared__ int lrow[256];             // latent row of every token (the cache row, or the staged copy's)
   const int K = a.s.d_kv, S = a.seq_len, SP = a.plan.s_pad, dn = a.s.d_nope(), NH = a.s.n_heads;
   const int r = a.s.r_pairs, R2 = a.s.r2();
   const int bid = xcd_tile(blockIdx.x, gridDim.x);
@@ -68,14 +102,15 @@ __global__ __launch_bounds__(256, 2) void rec_k_gemm(PrefillArgs a, int M) {
     const int b = m / S, t = m - b * S;
     crow[tid] = m < M ? cache_row_of(a.pm, a.t_max, b, t) : -1;
     orow[tid] = m < M ? (b * NH + hh) * SP + t : -1;
+    lrow[tid] = m < M ? (a.lat_staged ? m : crow[tid]) : -1;  // staged rows: [b * S + t]
   }
   build_nope_idx(a.pair_idx, hh, r, 64, kept, dim_of);
   if (tid < R2) dim_of[dn + tid] = 2 * load_pair(a.pair_idx, hh * r + (tid >> 1), 64) + (tid & 1);
   __syncthreads();
-  const bf16* ckv = (const bf16*)a.ckv;
-  const int last = crow[min(M - 1 - m0, 255)];
+  const bf16* ckv = (const bf16*)(a.lat_staged ? (const void*)(a.ws + a.plan.off_lat) : a.ckv);
+  const int last = lrow[min(M - 1 - m0, 255)];
   auto a_row = [&](int i) {
-    const int c = crow[i];
+    const int c = lrow[i];
     return ckv + (size_t)(c >= 0 ? c : last) * K;
   };
   auto b_row = [&](int i) -> const bf16* {  // rows past d_nope load valid rows (their results are unused)
@@ -139,14 +174,14 @@ __global__ __launch_bounds__(256, 2) void rec_vt_gemm(PrefillArgs a, int N) {
   const int tid = threadIdx.x;
   {
     const int n = min(n0 + tid, N - 1), b = n / SP, t = n - b * SP;
-    crow[tid] = cache_row_of(a.pm, a.t_max, b, min(t, S - 1));
+    crow[tid] = a.lat_staged ? b * S + min(t, S - 1) : cache_row_of(a.pm, a.t_max, b, min(t, S - 1));
     if (tid < 32) {
       const int nc = n0 + 8 * tid, bc = nc / SP, tc = nc - bc * SP;
       orow[tid] = nc < N ? ((size_t)(bc * NH + hh) * 128) * SP + tc : ~(size_t)0;
     }
   }
   __syncthreads();
-  const bf16* ckv = (const bf16*)a.ckv;
+  const bf16* ckv = (const bf16*)(a.lat_staged ? (const void*)(a.ws + a.plan.off_lat) : a.ckv);
   auto a_row = [&](int i) { return (const bf16*)a.w_uv + ((size_t)hh * 128 + i) * K; };
   auto b_row = [&](int i) { return ckv + (size_t)crow[i] * K; };
   f32x16 acc[RecV::FM][RecV::FN];
@@ -475,7 +510,7 @@ __global__ __launch_bounds__(512, 1) void prefill_attn(PrefillArgs a) {
 }  // namespace
 
 bool prefill_supported(const Shape& s) {
-  return s.dtype == 1 && s.fmt == 0 && s.d_head == 128 && s.d_kv % 64 == 0;
+  return s.dtype == 1 && s.fmt >= 0 && s.fmt <= 3 && s.d_head == 128 && s.d_kv % 64 == 0;
 }
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -488,12 +523,20 @@ PrefillPlan plan_prefill(const Shape& s, int batch, int seq_len) {
   off = align256(off + (size_t)batch * s.n_heads * p.s_pad * 128 * 2);
   p.off_vt = off;
   off = align256(off + (size_t)batch * s.n_heads * 128 * p.s_pad * 2);
+  p.off_lat = off;
+  if (s.fmt != 0) off = align256(off + (size_t)batch * seq_len * s.d_kv * 2);
   p.total = off;
   return p;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+hipError_t launch_prefill(const PrefillArgs& a0, hipStream_t st) {
+  PrefillArgs a = a0;
   const int S = a.seq_len, B = a.batch, NH = a.s.n_heads, SP = a.plan.s_pad;
+  if (a.s.fmt != 0) {  // quantised latent: dequantised copy first
+    const size_t lanes = (size_t)B * S * (a.s.d_kv / 8);
+    hipLaunchKernelGGL(prefill_stage_latent, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st, a);
+    a.lat_staged = 1;
+  }
   hipLaunchKernelGGL(rec_k_gemm, dim3(((B * S + 255) / 256) * NH), dim3(256), 0, st, a, B * S);
   hipLaunchKernelGGL(rec_vt_gemm, dim3(NH * ((B * SP + 255) / 256)), dim3(256), 0, st, a, B * SP);
   const int nqt = (S + FQ - 1) / FQ;

@@ -43,7 +43,7 @@ __device__ __forceinline__ void store_group(const AppendArgs& a, size_t row, int
   }
   ((__half*)a.ckv_scale)[row * (D / 32) + g] = s;
 }
-// ---- 2-bit latent with a window of recent bf16 rows (fmt 2)
+// ---- latents with a window of recent bf16 rows (fmt 2: 2-bit codes, fmt 3: int4 codes)
 // Group of 32 latent values of one token (already rounded to bf16): z = fp16(min), s = fp16(max(max - z,
 // 0) / 3), both saturating at the largest finite fp16; code = clamp(rint((x - z) / s), 0, 3) with an fp32
 // subtraction and an IEEE fp32 division (s == 0: code 0).  Row `row` of the code store holds 8 bytes per
@@ -79,6 +79,14 @@ __device__ __forceinline__ void store_group2(const AppendArgs& a, size_t row, in
   const int D = a.s.d_kv;
   code_group2(v, (uint8_t*)a.ckv + row * (D / 4) + 8 * g, (uint32_t*)a.ckv_scale + row * (D / 32) + g);
 }
+// A row group leaving (or never entering) the window of a windowed format, from its bf16 values v[0..31]:
+// the 2-bit codec (fmt 2) or the int4 codec (fmt 3).
+__device__ __forceinline__ void store_group_coded(const AppendArgs& a, size_t row, int g, const float* v) {
+  if (a.s.fmt == 3)
+    store_group(a, row, g, v, 1);
+  else
+    store_group2(a, row, g, v);
+}
 // Position that ring slot `slot` holds before an append that starts at position sp: the one in
 // [sp - W, sp) congruent to slot modulo W (negative: the slot has not been used yet).
 __device__ __forceinline__ int ring_occupant(int sp, int W, int slot) {
@@ -101,7 +109,7 @@ __device__ __forceinline__ void store_group_win2(const AppendArgs& a, int b, int
   float v[32];
   for (int c = 0; c < 32; ++c) v[c] = (float)(bf16)vals[c * stride];
   if (pos < sp + a.t_new - W) {
-    store_group2(a, (size_t)cache_row_of(a.pm, a.t_max, b, pos), g, v);
+    store_group_coded(a, (size_t)cache_row_of(a.pm, a.t_max, b, pos), g, v);
     return;
   }
   const int slot = pos % W;
@@ -110,7 +118,7 @@ __device__ __forceinline__ void store_group_win2(const AppendArgs& a, int b, int
   if (p_old >= 0) {
     float o[32];
     for (int c = 0; c < 32; ++c) o[c] = (float)ring[c];
-    store_group2(a, (size_t)cache_row_of(a.pm, a.t_max, b, p_old), g, o);
+    store_group_coded(a, (size_t)cache_row_of(a.pm, a.t_max, b, p_old), g, o);
   }
   for (int c = 0; c < 32; ++c) ring[c] = (bf16)v[c];
 }
@@ -134,6 +142,21 @@ __device__ __forceinline__ void store_lane_win2(const AppendArgs& a, bool ok, in
       evict = p_old >= 0;
       if (evict) x = (float)ring[c];
     }
+  }
+  if (a.s.fmt == 3) {  // int4 codes of the bf16 values: group absmax, scale, nibbles packed by lane pairs
+    float am = fabsf(x);
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) am = fmaxf(am, shfl_xor(am, m));
+    const __half s4 = int4_scale(am);
+    const int code = int4_code(x, __half2float(s4));
+    const int partner = __shfl_xor(code, 1, 64);
+    if (direct || evict) {
+      const size_t row = (size_t)cache_row_of(a.pm, a.t_max, b, direct ? pos : p_old);
+      if ((c & 1) == 0) ((uint8_t*)a.ckv)[row * (D / 2) + 16 * g + (c >> 1)] = (uint8_t)((code & 15) | ((partner & 15) << 4));
+      if (c == 0) ((__half*)a.ckv_scale)[row * (D / 32) + g] = s4;
+    }
+    if (ok && !direct) ring[c] = (bf16)vb;
+    return;
   }
   float lo = x, hi = x;
 #pragma unroll

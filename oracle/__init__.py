@@ -48,7 +48,15 @@ from .attention import (  # noqa: F401
     reconstruct_head,
     rope_rotate,
 )
-from .int4 import dequant_int4, int4_codes, int4_scale, pack_nibbles, quantize_int4_g32, unpack_nibbles  # noqa: F401
+from .int4 import (  # noqa: F401
+    dequant_int4,
+    int4_codes,
+    int4_scale,
+    pack_nibbles,
+    quantize_int4_g32,
+    unpack_nibbles,
+    windowed_latent_int4,
+)
 from . import int2  # noqa: F401
 from .paged import gather_pages, multi_query_decode_ref  # noqa: F401
 from .cache_bytes import cache_bytes_per_token, mha_bytes_per_token, reduction_pct  # noqa: F401

@@ -80,3 +80,20 @@ def dequant_int4(codes, scales):
     shp = c.shape
     g = c.reshape(-1, GROUP) * s.reshape(-1, 1)
     return g.reshape(shp).astype(np.float64)
+
+
+def windowed_latent_int4(rows_bf16, W):
+    """The latent rows that attention reads for one sequence of an int4 cache that keeps a window of recent bf16
+    rows (the README page's quantised-cache evaluation keeps the most recent tokens unquantised): rows older
+    than the last min(L, W) are replaced by the int4 codec of their bf16 values, the window's rows stay.
+
+    rows_bf16: [L, d_kv] values already on the bf16 grid.  Returns (rows [L, d_kv] fp64, codes
+    [L - min(L, W), d_kv], scales [L - min(L, W), d_kv/32])."""
+    x = np.asarray(rows_bf16, dtype=np.float32)
+    L = x.shape[0]
+    nq = L - min(L, W)
+    codes, scales = quantize_int4_g32(x[:nq])
+    out = x.astype(np.float64)
+    if nq > 0:
+        out[:nq] = dequant_int4(codes, scales)
+    return out, codes, scales

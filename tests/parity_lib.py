@@ -166,35 +166,43 @@ def check_bf16_values(got, ref, what=""):
     return n
 
 
-def check_int4_cache(c, codes, scales, what="int4"):
+def check_int4_cache(c, codes, scales, what="int4", via_bf16=False):
     """GPU int4 codes [L, d_kv] (int8, unpacked) and fp16 scales [L, d_kv/32] against the oracle's fp64 latent c
-    [L, d_kv].  The GPU quantises its own fp32 latent, which lies within acc_eps of c, so per group of 32:
-    the GPU scale must lie between the codec's scales of the smallest and the largest absmax that latent can
-    have, and each code, under the GPU's scale, between the codec's codes at c - acc_eps and c + acc_eps.
-    Every dequantised value stays within half a step (plus acc_eps) of the oracle's latent."""
+    [L, d_kv].  The GPU quantises its own fp32 latent, which lies within acc_eps of c -- or, with via_bf16 (the
+    windowed int4 format, which codes rows from their bf16 values), the bf16 rounding of that latent, which
+    lies between bf16(c - acc_eps) and bf16(c + acc_eps).  So per group of 32: the GPU scale must lie between
+    the codec's scales of the smallest and the largest absmax those inputs can have, and each code, under the
+    GPU's scale, between the codec's codes at the lowest and the highest input.  Every dequantised value stays
+    within half a step of some allowed input."""
     c = np.asarray(c, dtype=np.float64)
     L, D = c.shape
     g = c.reshape(L, D // 32, 32)
     e = acc_eps(g)
+    lo, hi = g - e, g + e
+    if via_bf16:
+        lo, hi = synth.round_to_device(lo, "bf16"), synth.round_to_device(hi, "bf16")
     s_gpu = np.asarray(scales, dtype=np.float16).reshape(L, D // 32)
     k_gpu = np.asarray(codes, dtype=np.int8).reshape(L, D // 32, 32)
     assert np.all(np.isfinite(s_gpu.astype(np.float32))), f"{what}: non-finite scales"
-    s_lo = oracle.int4_scale(np.max(np.maximum(np.abs(g) - e, 0.0), axis=-1).astype(np.float32))
-    s_hi = oracle.int4_scale(np.max(np.abs(g) + e, axis=-1).astype(np.float32))
+    min_abs = np.where(lo > 0, lo, np.where(hi < 0, -hi, 0.0))
+    max_abs = np.maximum(np.abs(lo), np.abs(hi))
+    s_lo = oracle.int4_scale(np.max(min_abs, axis=-1).astype(np.float32))
+    s_hi = oracle.int4_scale(np.max(max_abs, axis=-1).astype(np.float32))
     sg = s_gpu.astype(np.float32)
     bad_s = (sg < s_lo.astype(np.float32)) | (sg > s_hi.astype(np.float32))
     assert not bad_s.any(), (f"{what}: {np.count_nonzero(bad_s)} group scales are no scale of a latent within the "
                              f"accumulation bound, first at {_first(bad_s)}: got {sg[bad_s][:3]}, "
                              f"range [{s_lo[bad_s][:3]}, {s_hi[bad_s][:3]}]")
-    k_lo = oracle.int4_codes((g - e).astype(np.float32), s_gpu)
-    k_hi = oracle.int4_codes((g + e).astype(np.float32), s_gpu)
+    k_lo = oracle.int4_codes(lo.astype(np.float32), s_gpu)
+    k_hi = oracle.int4_codes(hi.astype(np.float32), s_gpu)
     bad_k = (k_gpu < k_lo) | (k_gpu > k_hi)
     assert not bad_k.any(), (f"{what}: {np.count_nonzero(bad_k)} codes are no code of a latent within the "
                              f"accumulation bound under the group's scale, first at {_first(bad_k)}")
     deq = k_gpu.astype(np.float64) * sg.astype(np.float64)[..., None]
-    bound = 0.5 * sg.astype(np.float64)[..., None] + e
+    bound = 0.5 * sg.astype(np.float64)[..., None] + np.maximum(g - lo, hi - g)
     assert np.all(np.abs(deq - g) <= bound), f"{what}: a dequantised value is more than half a step from the latent"
-    oc, osc = oracle.quantize_int4_g32(c.astype(np.float32))
+    ref_in = synth.round_to_device(c, "bf16") if via_bf16 else c
+    oc, osc = oracle.quantize_int4_g32(ref_in.astype(np.float32))
     n_s = int(np.count_nonzero(s_gpu.view(np.uint16) != osc.reshape(L, D // 32).view(np.uint16)))
     n_k = int(np.count_nonzero(k_gpu != oc.reshape(k_gpu.shape)))
     log(f"  {what}: scales exact up to {n_s} of {s_gpu.size} groups and codes up to {n_k} of {k_gpu.size} at "

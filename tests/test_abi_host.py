@@ -90,7 +90,9 @@ def test_workspace_sizes(lib):
         (dict(cache_fmt=1, d_kv=48), UNSUPPORTED),
         (dict(cache_fmt=2, dtype=0), UNSUPPORTED),
         (dict(cache_fmt=2, d_kv=48), UNSUPPORTED),
-        (dict(cache_fmt=3), INVALID),
+        (dict(cache_fmt=3, dtype=0), UNSUPPORTED),
+        (dict(cache_fmt=3, d_kv=48), UNSUPPORTED),
+        (dict(cache_fmt=4), INVALID),
     ],
 )
 def test_decode_rejects_bad_config(lib, kw, expected):
@@ -204,9 +206,16 @@ def test_prefill_checks(lib):
         return lib.mla_prefill(ctypes.byref(c), ctypes.byref(w), ctypes.byref(k), q, s, out, ws, nbytes, None)
 
     assert call(c=cfg(dtype=0)) == UNSUPPORTED
-    assert call(c=cfg(cache_fmt=1)) == UNSUPPORTED
-    assert call(c=cfg(cache_fmt=2)) == UNSUPPORTED
+    assert call(c=cfg(d_head=64)) == UNSUPPORTED
     assert call(s=-1) == INVALID
+    # quantised latents are accepted; their workspace also holds the dequantised latent rows [batch, S, d_kv]
+    dense = lib.mla_prefill_workspace_bytes(ctypes.byref(c), 4, 4096)
+    for fmt in (1, 2):
+        cq = cfg(cache_fmt=fmt)
+        need = lib.mla_prefill_workspace_bytes(ctypes.byref(cq), 4, 4096)
+        assert need == dense + 4 * 4096 * 512 * 2
+        assert call(c=cq, k=cache(batch=4), nbytes=need - 1) == WORKSPACE
+    assert call(c=cfg(cache_fmt=1), k=cache(batch=4, ckv_scale=None), nbytes=1 << 40) == INVALID
 
 
 def test_quantize_checks(lib):

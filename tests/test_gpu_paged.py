@@ -114,13 +114,15 @@ def test_paged_append_and_decode(case):
         log(f"  b={b} L={L} rel-L2={rr:.2e} max-abs={a:.2e}")
 
 
-def test_paged_prefill():
+@pytest.mark.parametrize("fmt", ["dense", "int4_g32"])
+def test_paged_prefill(fmt):
+    """Prefill over a paged cache (the int4 latent dequantised through the page table first)."""
     from mla_latent_kv_cache_amd import LatentCache, append, pack_weights, prefill
 
-    cfg = scaled(CONFIGS[2], family="mid")
+    cfg = scaled(CONFIGS[2], family="mid", cache_fmt=fmt)
     B, S, P = 2, 300, 64
     pps = (S + P - 1) // P
-    log(f"[paged-prefill] B={B} S={S} page={P}")
+    log(f"[paged-prefill] {fmt} B={B} S={S} page={P}")
     layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
     shape = shape_of(cfg)
     w = pack_weights(shape, layer, rope_len=pps * P, theta=cfg.theta)
@@ -137,6 +139,8 @@ def test_paged_prefill():
     for b in range(B):
         c, kr = oracle.append_ref(xs[b], layer["w_dkv"], layer["w_krope"], layer["pair_idx"], np.arange(S), cfg.d_head,
                                   cfg.theta)
+        if fmt == "int4_g32":
+            c = oracle.dequant_int4(*oracle.quantize_int4_g32(c.astype(np.float32)))
         ref = oracle.prefill_ref(qs[b], c, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head, cfg.theta)
         rr, a = assert_close(got[b], ref, cfg.dtype, f"paged prefill b={b}")
         log(f"  b={b} rel-L2={rr:.2e} max-abs={a:.2e}")

@@ -107,3 +107,47 @@ def test_prefill_full_llama_b4_s4096():
     cfg = CONFIGS[2]
     rows = [0, 1, 2, 63, 64, 127, 128, 129, 1000, 2047, 2048, 4031, 4032, 4094, 4095]
     run_prefill_case(cfg, S=cfg.context, B=cfg.batch, rows=rows, full_b=[0, 3])
+
+
+@pytest.mark.parametrize("fmt,window", [("int4_g32", 0), ("int2_g32_win", 128), ("int2_g32_win", 0),
+                                        ("int2_g32_win", 512), ("int4_g32_win", 128)])
+def test_prefill_quantised_latent(fmt, window):
+    """Prefill over a quantised latent cache (the key-designs section's 4- and 2-bit compatibility): the latent
+    rows are dequantised exactly as decode reads them, so the reference is the oracle's unabsorbed attention over
+    its own dequantised latent (int4 codec of the fp32 latent; 2-bit codec of the bf16 rows outside the last
+    `window` positions).  Window 512 exceeds the prompt (every row in the ring); window 0 codes every row."""
+    from mla_latent_kv_cache_amd import LatentCache, append, pack_weights, prefill
+    from oracle import int2
+
+    cfg = scaled(CONFIGS[2], family="mid", cache_fmt=fmt)
+    B, S = 2, 300
+    log(f"[prefill-quantised] {fmt} window={window} B={B} S={S}")
+    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    shape = shape_of(cfg)
+    w = pack_weights(shape, layer, rope_len=S, theta=cfg.theta)
+    cache = LatentCache.allocate(shape, B, S, fill=float("nan"), window=window)
+    xs = [synth.context_x(cfg, b, S) for b in range(B)]
+    x = torch.from_numpy(np.stack(xs).astype(np.float32)).cuda().to(torch_dtype(cfg))
+    append(w, cache, x, torch.zeros(B, dtype=torch.int32, device="cuda"), 0)
+    qs = [synth.query_rows(xb, layer["w_q"], cfg.dtype).reshape(S, cfg.n_heads, cfg.d_head) for xb in xs]
+    q = torch.from_numpy(np.stack(qs).astype(np.float32)).cuda().to(torch_dtype(cfg))
+    out = prefill(w, cache, q)
+    out2 = prefill(w, cache, q)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "prefill is not bitwise deterministic"
+    assert_finite(out, "prefill out")
+    got = out.float().cpu().numpy().astype(np.float64)
+    for b in range(B):
+        c, kr = oracle.append_ref(xs[b], layer["w_dkv"], layer["w_krope"], layer["pair_idx"], np.arange(S),
+                                  cfg.d_head, cfg.theta)
+        if fmt == "int4_g32":
+            oc, osc = oracle.quantize_int4_g32(c.astype(np.float32))
+            c_used = oracle.dequant_int4(oc, osc)
+        elif fmt == "int4_g32_win":
+            c_used, _, _ = oracle.windowed_latent_int4(synth.round_to_device(c, "bf16"), window)
+        else:
+            c_used, _, _ = int2.windowed_latent(synth.round_to_device(c, "bf16"), window)
+        ref = oracle.prefill_ref(qs[b], c_used, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head,
+                                 cfg.theta)
+        r, a = assert_close(got[b], ref, cfg.dtype, f"prefill b={b}")
+        log(f"  b={b} rel-L2={r:.2e} max-abs={a:.2e}")

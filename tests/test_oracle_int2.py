@@ -128,3 +128,24 @@ def test_int2_cache_bytes():
     assert oracle.reduction_pct(b, mha) == pytest.approx(100 * (1 - 704 / 16384))
     # the window adds W * d_kv * 2 bytes per sequence: 128 KiB at W = 128, d_kv = 512
     assert 128 * 512 * 2 == 131072
+
+
+@pytest.mark.parametrize("appends,W", [([300], 128), ([129, 200, 3], 64), ([5, 5, 5], 0), ([50], 128)])
+def test_int4_window_matches_ring_simulation(appends, W):
+    """The int4 cache with a window: the rows a ring of W slots still holds after the appends stay bf16, every
+    row that left it (or never entered it) is the int4 codec of its own bf16 values, row by row; W = 0 is the
+    plain int4 codec of the bf16 rows."""
+    slots, quantised, L = _ring_by_simulation(appends, W)
+    rng = np.random.default_rng(L + W + 1)
+    rows = np.round(rng.standard_normal((L, 64)) * 256) / 256
+    eff, codes, scales = oracle.windowed_latent_int4(rows, W)
+    nq = L - int2.window_len(L, W)
+    assert set(range(nq)) == quantised
+    assert codes.shape == (nq, 64) and scales.shape == (nq, 2)
+    np.testing.assert_array_equal(eff[nq:], rows[nq:])
+    for p in sorted(quantised):
+        c1, s1 = oracle.quantize_int4_g32(rows[p].astype(np.float32))
+        np.testing.assert_array_equal(eff[p], oracle.dequant_int4(c1, s1))
+    if W == 0:
+        c_all, s_all = oracle.quantize_int4_g32(rows.astype(np.float32))
+        np.testing.assert_array_equal(eff, oracle.dequant_int4(c_all, s_all))

@@ -113,3 +113,19 @@ def test_int2_rule_accepts_a_bf16_tie():
         b[0, j] = v
         codes, meta = int2.quantize_int2_g32(b.astype(np.float32))
         check_int2_codes(c, codes, meta, "tie")
+
+
+def test_int4_rule_through_bf16():
+    """The windowed int4 format codes rows from their bf16 values: the rule then bounds the inputs by the bf16
+    roundings of the accumulation window, and a code planted one off still fails."""
+    c, c32 = _latents()
+    b = synth.round_to_device(c32, "bf16").astype(np.float32)
+    codes, scales = oracle.quantize_int4_g32(b)
+    check_int4_cache(c, codes, scales, "bf16 rows", via_bf16=True)
+    q = b.reshape(-1, 32) / scales.reshape(-1).astype(np.float32)[:, None]
+    far = np.abs(np.abs(q - np.floor(q)) - 0.5) > 0.1
+    k = codes.copy().reshape(-1, 32)
+    g, j = np.argwhere(far & (np.abs(k) < 7))[0]
+    k[g, j] -= 1
+    with pytest.raises(AssertionError):
+        check_int4_cache(c, k.reshape(codes.shape), scales, "planted", via_bf16=True)
