@@ -31,8 +31,7 @@ constexpr int MAX_DH = 256;
 __device__ __forceinline__ int cseq(const DecodeArgs& a, int b) { return a.qn > 1 ? b / a.qn : b; }
 // Keys visible to query sequence b: its cache sequence's length (clamped to the host bound), less the
 // newer queries of the same sequence.
-__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
-  int L = a.seq_lens[cseq(a, b)];
+__device__ __forceinline__ int clamp_len_of(const DecodeArgs& a, int b, int L) {  // L: seq_lens[cseq(b)]
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   if (a.qn > 1) {
     L -= a.qn - 1 - b % a.qn;
@@ -40,6 +39,7 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
   }
   return L;
 }
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) { return clamp_len_of(a, b, a.seq_lens[cseq(a, b)]); }
 // Cache row of position pos of query sequence b (contiguous or through the page table).
 __device__ __forceinline__ int seq_row(const DecodeArgs& a, int b, int pos) {
   return cache_row_of(a.pm, a.t_max, cseq(a, b), pos);
@@ -241,47 +241,92 @@ __global__ __launch_bounds__(512) void decode_qprep(DecodeArgs a) {
   }
 }
 
-// 1b. query preparation on MFMA (bf16, d_h - 2r <= 128, latent width a multiple of 128).
-// Workgroup (head h, 128 latent columns, 32 sequences); wave w owns 32 of the columns.
-//   q~[b][k] = sum_i q_nope[b][i] W_uk,h[i][k]:  A = gathered NoPE query rows (LDS, rows b),
-//   B = W_uk tile (LDS, rows i, k contiguous) through the transpose read; K = NoPE dims padded to 128.
+// 1b. query preparation on MFMA (bf16, d_h <= 128 and a multiple of 8, latent width a multiple of 128,
+// 16-byte aligned query rows).  Workgroup (head h, 128 latent columns, 32 sequences); wave w owns 32 of
+// the columns.  q~[b][k] = sum_i q_nope[b][i] W_uk,h[i][k] runs over the head's own dims d (K = 128):
+// A = the query rows as they are (LDS, rows b, zero past d_h), B = W_uk row i stored at LDS row
+// nope_idx[i] (the i-th non-retained dim), every other row zero.  So nothing waits for the retained
+// pairs before the query loads: the workgroup issues all of its global loads at its start.
 __device__ __forceinline__ void qprep_mfma_tile(const DecodeArgs& a, int bx, int by, int bz) {
   constexpr int WP = 128 + 8;  // LDS pitch of both tiles (elements)
   __shared__ __attribute__((aligned(16))) bf16 wt[128 * WP];
   __shared__ __attribute__((aligned(16))) bf16 qa[32 * WP];
-  __shared__ int nope_idx[MAX_DH];
-  __shared__ int kept[MAX_DH / 2];
+  __shared__ int dest[128];  // LDS row of W_uk row i (rows i >= d_nope are zero)
   const int h = bx, kb = by * 128, b0 = bz * 32;
   const int D = a.s.d_kv, dh = a.s.d_head, r = a.s.r_pairs, dn = a.s.d_nope(), half = dh / 2, NH = a.s.n_heads;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5;
-  // W_uk rows i < dn, columns kb .. kb+127: 16 chunks of 16 bytes per row, issued first
-  const bf16* wuk = (const bf16*)a.w_uk + (size_t)h * dn * D + kb;
+  // global loads, in the order their values are needed: the retained pairs (wave 0), the rotation's
+  // pairs and lengths (by == 0), the W_uk tile (rows i < d_nope, columns kb .. kb+127), the query rows.
+  // Raw values first, clamped once every load is in flight (a use inside the loads' branches would wait
+  // for each load in turn).
+  const bool rot = by == 0 && tid < 32 * r;
+  const int rbb = rot ? tid / r : 0, rj = rot ? tid - rbb * r : 0, rb = b0 + rbb;
+  const bool rok = rot && rb < a.batch;
+  int pk_raw = 0, rp_raw = 0, rL_raw = 0;
+  if (tid < r) pk_raw = a.pair_idx[h * r + tid];
+  if (rok) {
+    rp_raw = a.pair_idx[h * r + rj];
+    rL_raw = a.seq_lens[cseq(a, rb)];
+  }
+  // (the tile loads read a clamped in-bounds address and are zeroed afterwards: a load under a branch
+  // would be waited for inside it)
+  const bf16* q = (const bf16*)a.q;
+  const bf16* wuk = dn > 0 ? (const bf16*)a.w_uk + (size_t)h * dn * D + kb : q;
   u32x4 wreg[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int c = u * 256 + tid, row = c >> 4, ch = c & 15;
-    wreg[u] = row < dn ? *(const u32x4*)(wuk + (size_t)row * D + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+    wreg[u] = *(const u32x4*)(dn > 0 ? wuk + (size_t)min(row, dn - 1) * D + ch * 8 : q);
   }
-  build_nope_idx(a.pair_idx, h, r, half, kept, nope_idx);
-  __syncthreads();
-  const bf16* q = (const bf16*)a.q;
-  bf16 g[16];
+  u32x4 qreg[2];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {  // q_nope of 32 rows x 128 padded dims: 16 per thread
-    const int c = u * 256 + tid, bb = c >> 7, i = c & 127, b = b0 + bb;
-    g[u] = (i < dn && b < a.batch) ? q[((size_t)b * NH + h) * dh + nope_idx[i]] : (bf16)0.f;
+  for (int u = 0; u < 2; ++u) {  // 32 rows x 16 chunks of 8 dims
+    const int c = u * 256 + tid, bb = c >> 4, ch = c & 15, b = min(b0 + bb, a.batch - 1);
+    qreg[u] = *(const u32x4*)(q + ((size_t)b * NH + h) * dh + 8 * min(ch, dh / 8 - 1));
   }
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (((u * 256 + tid) >> 4) >= dn) wreg[u] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = u * 256 + tid;
+    if (8 * (c & 15) >= dh || b0 + (c >> 4) >= a.batch) qreg[u] = u32x4{0u, 0u, 0u, 0u};
+  }
+  const int pk = tid < r ? (pk_raw < 0 ? 0 : (pk_raw >= half ? half - 1 : pk_raw)) : -1;
+  const int rp = rp_raw < 0 ? 0 : (rp_raw >= half ? half - 1 : rp_raw);
+  const int rL = rok ? clamp_len_of(a, rb, rL_raw) : 0;
+  if (w == 0) {
+    // kept pairs as a 64-bit mask (lane j < r holds pair j), then lane l places dims 2l, 2l+1: the
+    // non-retained pairs below d_h first, in ascending order, then the rest
+    uint64_t km = 0;
+    for (int j = 0; j < r; ++j) km |= 1ull << __builtin_amdgcn_readlane(pk, j);
+    const bool nope = 2 * lane < dh && !((km >> lane) & 1ull);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(nope);
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const int pos = nope ? 2 * __builtin_popcountll(m & below)
+                         : 2 * __builtin_popcountll(m) + 2 * __builtin_popcountll(~m & below);
+    dest[pos] = 2 * lane;
+    dest[pos + 1] = 2 * lane + 1;
+  }
+  // the rotation's RoPE factors (their addresses need the pair and the length)
+  float rc = 0.f, rs = 0.f;
+  if (rok) {
+    const int pos = rL > 0 ? rL - 1 : 0;
+    rc = a.rope_cos[(size_t)pos * half + rp];
+    rs = a.rope_sin[(size_t)pos * half + rp];
+  }
+  lds_barrier();
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int c = u * 256 + tid, row = c >> 4, ch = c & 15;
-    *(u32x4*)&wt[row * WP + ch * 8] = wreg[u];
+    *(u32x4*)&wt[dest[row] * WP + ch * 8] = wreg[u];
   }
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int c = u * 256 + tid, bb = c >> 7, i = c & 127;
-    qa[bb * WP + i] = g[u];
+  for (int u = 0; u < 2; ++u) {
+    const int c = u * 256 + tid, bb = c >> 4, ch = c & 15;
+    *(u32x4*)&qa[bb * WP + ch * 8] = qreg[u];
   }
-  __syncthreads();
+  lds_barrier();
   f32x16 acc = f32x16{};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -300,18 +345,24 @@ __device__ __forceinline__ void qprep_mfma_tile(const DecodeArgs& a, int bx, int
     const int b = b0 + 8 * (e >> 2) + 4 * hb + (e & 3);
     if (b < a.batch) qt[((size_t)b * NH + h) * D + k] = (bf16)(acc[e] * scale);
   }
-  if (by != 0) return;
-  float* qr = (float*)(a.ws + a.plan.off_qr);
-  for (int idx = tid; idx < 32 * r; idx += blockDim.x) {
-    const int bb = idx / r, j = idx - bb * r, b = b0 + bb;
-    if (b >= a.batch) continue;
-    const int L = clamp_len(a, b);
-    const int pos = L > 0 ? L - 1 : 0;
-    const int p = load_pair(a.pair_idx, h * r + j, half);
-    const float x0 = (float)q[((size_t)b * NH + h) * dh + 2 * p], x1 = (float)q[((size_t)b * NH + h) * dh + 2 * p + 1];
-    const float c = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
-    qr[((size_t)b * NH + h) * 2 * r + 2 * j] = (x0 * c - x1 * sn) * scale;
-    qr[((size_t)b * NH + h) * 2 * r + 2 * j + 1] = (x0 * sn + x1 * c) * scale;
+  if (rok) {  // the retained pairs of the query, rotated to the sequence's last position
+    float* qr = (float*)(a.ws + a.plan.off_qr);
+    const float x0 = (float)qa[rbb * WP + 2 * rp], x1 = (float)qa[rbb * WP + 2 * rp + 1];
+    qr[((size_t)rb * NH + h) * 2 * r + 2 * rj] = (x0 * rc - x1 * rs) * scale;
+    qr[((size_t)rb * NH + h) * 2 * r + 2 * rj + 1] = (x0 * rs + x1 * rc) * scale;
+  }
+  if (by == 0) {  // more than 256 (sequence, pair) entries: the rest in turn
+    float* qr = (float*)(a.ws + a.plan.off_qr);
+    for (int idx = tid + 256; idx < 32 * r; idx += 256) {
+      const int bb = idx / r, j = idx - bb * r, b = b0 + bb;
+      if (b >= a.batch) continue;
+      const int L = clamp_len(a, b), pos = L > 0 ? L - 1 : 0;
+      const int p = load_pair(a.pair_idx, h * r + j, half);
+      const float x0 = (float)qa[bb * WP + 2 * p], x1 = (float)qa[bb * WP + 2 * p + 1];
+      const float c = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
+      qr[((size_t)b * NH + h) * 2 * r + 2 * j] = (x0 * c - x1 * sn) * scale;
+      qr[((size_t)b * NH + h) * 2 * r + 2 * j + 1] = (x0 * sn + x1 * c) * scale;
+    }
   }
 }
 
@@ -1630,27 +1681,29 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   for (int s0 = 0; s0 < S; s0 += 8) {
     float ms[8], ls[8], v[8][KPL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool ok = s0 + u < S;
-      ms[u] = ok ? ml[(size_t)(s0 + u) * NH * MLS] : -INFINITY;
-      ls[u] = ok ? ml[(size_t)(s0 + u) * NH * MLS + 1] : 0.f;
+    for (int u = 0; u < 8; ++u) {  // unconditional loads (see merge_splits), masked slots re-read the last
+      const int su = min(s0 + u, S - 1);
+      ms[u] = s0 + u < S ? ml[(size_t)su * NH * MLS] : -INFINITY;
+      ls[u] = ml[(size_t)su * NH * MLS + 1];
 #pragma unroll
       for (int i = 0; i < KPL; ++i) {
         const int k = lane + 64 * i;
-        v[u][i] = (ok && k < D) ? po[(size_t)(s0 + u) * NH * D + k] : 0.f;
+        v[u][i] = k < D ? po[(size_t)su * NH * D + k] : 0.f;
       }
     }
     float gm = M;
 #pragma unroll
     for (int u = 0; u < 8; ++u) gm = fmaxf(gm, ms[u]);
-    if (gm == -INFINITY) continue;  // nothing seen yet (empty splits only)
-    const float c = exp2f(M - gm);  // rescale of what was merged so far (0 when M = -inf)
+    // no branch here (the group's loads would be sunk past it): with nothing seen yet (gm = -inf) the
+    // reference 0 gives every weight and the rescale exp2(-inf) = 0, leaving den and acc at zero
+    const float ref = gm == -INFINITY ? 0.f : gm;
+    const float c = exp2f(M - ref);  // rescale of what was merged so far (0 when M = -inf)
     den *= c;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) acc[i] *= c;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float wv = ms[u] == -INFINITY ? 0.f : exp2f(ms[u] - gm);
+      const float wv = exp2f(ms[u] - ref);  // 0 for an empty or masked split (ms = -inf)
       den = fmaf(wv, ls[u], den);
 #pragma unroll
       for (int i = 0; i < KPL; ++i) acc[i] = fmaf(wv, v[u][i], acc[i]);
@@ -1784,28 +1837,34 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs& a, int first, int
   for (int s0 = G * g0; s0 < S; s0 += G * gstep) {
     float ms[G], ls[G], as[G];
     pv_t v[G];
+    // every load of the group is issued unconditionally, so that they are all in flight together: a slot
+    // past the sequence's last split re-reads that split and is masked out through its maximum below
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      const bool ok = s0 + u < S;
-      const float* e = ml + (size_t)(s0 + u) * NH * MLS;
-      ms[u] = ok ? e[0] : -INFINITY;
-      ls[u] = ok ? e[1] : 0.f;
-      as[u] = F16 && ok ? e[2] : 1.f;
-      const size_t at = row0 + (size_t)(s0 + u) * NH * D;
-      v[u] = ok ? *(const pv_t*)((const typename std::conditional<F16, _Float16, float>::type*)(a.ws + a.plan.off_o) + at)
-                : pv_t{};
+      const int su = min(s0 + u, S - 1);
+      const float* e = ml + (size_t)su * NH * MLS;
+      ms[u] = e[0];
+      ls[u] = e[1];
+      as[u] = F16 ? e[2] : 1.f;
+      const size_t at = row0 + (size_t)su * NH * D;
+      v[u] = *(const pv_t*)((const typename std::conditional<F16, _Float16, float>::type*)(a.ws + a.plan.off_o) + at);
     }
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      if (s0 + u >= S) ms[u] = -INFINITY;
     float gm = M;
 #pragma unroll
     for (int u = 0; u < G; ++u) gm = fmaxf(gm, ms[u]);
-    if (gm == -INFINITY) continue;  // nothing seen yet (empty splits only)
-    const float c = exp2f(M - gm);  // rescale of what was merged so far (0 when M = -inf)
+    // no branch here (the group's loads would be sunk past it): with nothing seen yet (gm = -inf) the
+    // reference 0 gives every weight and the rescale exp2(-inf) = 0, leaving den and acc at zero
+    const float ref = gm == -INFINITY ? 0.f : gm;
+    const float c = exp2f(M - ref);  // rescale of what was merged so far (0 when M = -inf)
     den *= c;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) acc[i] *= c;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      const float wv = ms[u] == -INFINITY ? 0.f : exp2f(ms[u] - gm);
+      const float wv = exp2f(ms[u] - ref);  // 0 for an empty or masked split (ms = -inf)
       den = fmaf(wv, ls[u], den);
       const float wa = wv * as[u];
 #pragma unroll
@@ -2028,10 +2087,15 @@ DecodePlan plan_decode(const Shape& s, int batch, int max_seq_len) {
   return p;
 }
 
+// Shape and alignment conditions of the MFMA query preparation (the fused step's prologue runs it).
+static bool qprep_uses_mfma(const DecodeArgs& a) {
+  return a.s.dtype == 1 && a.s.d_head <= 128 && a.s.d_head % 8 == 0 && a.s.d_kv % 128 == 0 &&
+         ((uintptr_t)a.q & 15) == 0;
+}
+
 bool decode_step_fusable(const AppendArgs& aa, const DecodeArgs& da) {
   const int M = aa.batch * aa.t_new;
-  return aa.ws != nullptr && append_ksplit(aa.s, M) > 0 && da.s.dtype == 1 && da.s.d_nope() <= 128 &&
-         da.s.d_kv % 128 == 0;
+  return aa.ws != nullptr && append_ksplit(aa.s, M) > 0 && qprep_uses_mfma(da);
 }
 
 hipError_t launch_decode_step(const AppendArgs& aa, const DecodeArgs& da, hipStream_t st, int phase_mask) {
@@ -2059,7 +2123,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, int phase_mask, co
   const int nh = a.s.n_heads;
   if (phase_mask & 1) {
     dim3 gq(nh, (a.s.d_kv + 63) / 64, (a.batch + QB - 1) / QB);
-    if (a.s.dtype == 1 && a.s.d_nope() <= 128 && a.s.d_kv % 128 == 0)
+    if (qprep_uses_mfma(a))
       hipLaunchKernelGGL(decode_qprep_mfma, dim3(nh, a.s.d_kv / 128, (a.batch + 31) / 32), dim3(256), 0, st, a);
     else if (a.s.dtype == 0)
       hipLaunchKernelGGL(decode_qprep<float>, gq, dim3(64 * QW), 0, st, a);
