@@ -231,6 +231,8 @@ __device__ __forceinline__ void append_epilogue(const AppendArgs& a, const float
 // thread of the workgroup.  The stores are not waited for: the caller waits for vmcnt 0 before any load
 // that reads the rows.
 constexpr int FUSE_MAXR = 8;
+// Threads of the attention workgroups that run the reduction (a constant: blockDim is read from memory).
+constexpr int FUSE_NT = 256;
 constexpr int FUSE_HALF_MAX = 64;  // RoPE pairs per head whose tables are staged (d_head <= 128)
 constexpr int fuse_scratch_bytes(int D, int NR) {
   return FUSE_MAXR * (D + NR + 4) * 4 + 2 * FUSE_MAXR * 4 + 2 * FUSE_MAXR * FUSE_HALF_MAX * 4;
@@ -253,54 +255,71 @@ __device__ __forceinline__ bool append_rows_fused(const AppendArgs& a, int KS, i
     rows[threadIdx.x] = b * a.t_max + p_lo + threadIdx.x;
     poss[threadIdx.x] = p_lo + threadIdx.x;
   }
-  // loads that do not depend on the partial sums, issued first: the pair index of each RoPE pair this
-  // thread writes, and the rows' cos / sin tables (up to 4 rows: more take the per-pair loads below)
+  // Every load below reads an in-bounds address whether or not its value is used, and no load sits
+  // under a branch or next to a use of its value (either would make the compiler wait for it before the
+  // next load goes out); the partial sums go out first, then the pair indices of the RoPE pairs this
+  // thread writes and the rows' cos / sin entries (up to 4 rows: more take the per-pair loads below),
+  // then the caller's own loads (between()).  Without RoPE columns (no pair table or RoPE tables to
+  // read) those side loads read the first word of the partial sums instead.
   constexpr int RPT = 2;  // RoPE pairs per thread: 4 rows x 128 pairs over 256 threads
   constexpr int CPT = 1;  // table entries per thread: 4 rows x FUSE_HALF_MAX over 256 threads
-  const bool staged = half <= FUSE_HALF_MAX && R * (NR / 2) <= RPT * (int)blockDim.x &&
-                      R * half <= CPT * (int)blockDim.x;
-  int pidx[RPT];
+  const bool staged = NR > 0 && half <= FUSE_HALF_MAX && R * (NR / 2) <= RPT * FUSE_NT &&
+                      R * half <= CPT * FUSE_NT;
+  const float* part = (const float*)a.ws;
+  int praw[RPT];
   float cv[CPT], sv[CPT];
-  if (staged) {
+  auto side_loads = [&]() {
+    const int32_t* pi_src = NR > 0 ? a.pair_idx : (const int32_t*)part;
+    const float* cos_src = NR > 0 ? a.rope_cos : part;
+    const float* sin_src = NR > 0 ? a.rope_sin : part;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int idx = threadIdx.x + i * blockDim.x;
-      const int rel = 2 * (idx % (NR / 2)), hh = rel / R2, jj = (rel - hh * R2) >> 1;
-      pidx[i] = idx < R * (NR / 2) ? load_pair(a.pair_idx, hh * r + jj, half) : 0;
+      const int idx = threadIdx.x + i * FUSE_NT;
+      const int rel = NR > 0 ? 2 * (idx % (NR / 2)) : 0, hh = NR > 0 ? rel / R2 : 0, jj = (rel - hh * R2) >> 1;
+      praw[i] = pi_src[hh * r + jj];
     }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int idx = threadIdx.x + i * blockDim.x, m = idx / half;
-      const size_t at = (size_t)(p_lo + m) * half + (idx - m * half);
-      cv[i] = idx < R * half ? a.rope_cos[at] : 0.f;
-      sv[i] = idx < R * half ? a.rope_sin[at] : 0.f;
+      const int idx = min((int)threadIdx.x + i * FUSE_NT, R * half - 1), m = idx / half;
+      const size_t at = NR > 0 ? (size_t)(p_lo + m) * half + (idx - m * half) : 0;
+      cv[i] = cos_src[at];
+      sv[i] = sin_src[at];
     }
-  }
-  // partial sums: rounds of 4 blockDim columns, 16 bytes per thread and slice when rows hold whole 16-byte
-  // chunks; the first round's loads are in flight when between() issues the caller's own loads
-  const float* part = (const float*)a.ws;
+  };
+  // partial sums: rounds of 4 FUSE_NT columns, 16 bytes per thread and slice when rows hold whole 16-byte
+  // chunks
   if (N % 4 == 0) {
-    for (int base = 0; base < R * N; base += 4 * (int)blockDim.x) {
+    const size_t slice = (size_t)M * N / 4;  // one model-width slice of partial sums, in float4
+    auto round = [&](int base, bool first) {
       const int f0 = base + 4 * (int)threadIdx.x, m = f0 / N, n = f0 - m * N;
       const bool ok = f0 < R * N;
       const f32x4* src = (const f32x4*)(part + (size_t)(m0 + (ok ? m : 0)) * N + (ok ? n : 0));
-      const size_t slice = (size_t)M * N / 4;  // one model-width slice of partial sums, in float4
       f32x4 v[KS_MAX];
 #pragma unroll
-      for (int ks = 0; ks < KS_MAX; ++ks) v[ks] = (ks < KS && ok) ? src[ks * slice] : f32x4{0.f, 0.f, 0.f, 0.f};
-      if (base == 0) between();
+      for (int ks = 0; ks < KS_MAX; ++ks) v[ks] = src[min(ks, KS - 1) * slice];  // slices past KS unused
+      if (first) {
+        side_loads();
+        between();
+      }
       f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS_MAX; ++ks) sum += v[ks];
+      for (int ks = 0; ks < KS_MAX; ++ks)
+        if (ks < KS) sum += v[ks];
       if (ok) *(f32x4*)&lds[m * ld + n] = sum;
-    }
+    };
+    // the first round outside any loop: a loop around the caller's loads, whose values it does not use,
+    // makes the compiler wait for every earlier load before entering it
+    round(0, true);
+    if (R * N > 4 * FUSE_NT)
+      for (int base = 4 * FUSE_NT; base < R * N; base += 4 * FUSE_NT) round(base, false);
   } else {
+    side_loads();
     between();
-    for (int base = 0; base < R * N; base += 4 * (int)blockDim.x) {
+    for (int base = 0; base < R * N; base += 4 * FUSE_NT) {
       float v[4][KS_MAX];
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const int idx = base + it * blockDim.x + threadIdx.x;
+        const int idx = base + it * FUSE_NT + threadIdx.x;
         const int m = idx / N, n = idx - m * N;
 #pragma unroll
         for (int ks = 0; ks < KS_MAX; ++ks)
@@ -308,7 +327,7 @@ __device__ __forceinline__ bool append_rows_fused(const AppendArgs& a, int KS, i
       }
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const int idx = base + it * blockDim.x + threadIdx.x;
+        const int idx = base + it * FUSE_NT + threadIdx.x;
         float sum = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS_MAX; ++ks) sum += v[it][ks];
@@ -316,10 +335,13 @@ __device__ __forceinline__ bool append_rows_fused(const AppendArgs& a, int KS, i
       }
     }
   }
+  int pidx[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) pidx[i] = staged ? (praw[i] < 0 ? 0 : (praw[i] >= half ? half - 1 : praw[i])) : 0;
   if (staged) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int idx = threadIdx.x + i * blockDim.x;
+      const int idx = threadIdx.x + i * FUSE_NT;
       if (idx < R * half) {
         cst[idx] = cv[i];
         sst[idx] = sv[i];
@@ -332,12 +354,12 @@ __device__ __forceinline__ bool append_rows_fused(const AppendArgs& a, int KS, i
     if (spc != sp) return false;  // the same value in every thread: nothing was written to memory
   }
   if (a.s.fmt == 0) {
-    for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < R * D; idx += FUSE_NT) {
       const int m = idx / D, n = idx - m * D;
       store_latent(a, (size_t)rows[m], n, lds[m * ld + n]);
     }
   } else {
-    for (int idx = threadIdx.x; idx < R * (D / 32); idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < R * (D / 32); idx += FUSE_NT) {
       const int m = idx / (D / 32), g = idx - m * (D / 32);
       store_group(a, (size_t)rows[m], g, lds + m * ld + 32 * g, 1);
     }
@@ -345,7 +367,7 @@ __device__ __forceinline__ bool append_rows_fused(const AppendArgs& a, int KS, i
   if (staged) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int idx = threadIdx.x + i * blockDim.x;
+      const int idx = threadIdx.x + i * FUSE_NT;
       if (idx < R * (NR / 2)) {
         const int m = idx / (NR / 2), rel = 2 * (idx - m * (NR / 2));
         const float x0 = lds[m * ld + D + rel], x1 = lds[m * ld + D + rel + 1];
@@ -356,7 +378,7 @@ __device__ __forceinline__ bool append_rows_fused(const AppendArgs& a, int KS, i
       }
     }
   } else {
-    for (int idx = threadIdx.x; idx < R * (NR / 2); idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < R * (NR / 2); idx += FUSE_NT) {
       const int m = idx / (NR / 2), rel = 2 * (idx - m * (NR / 2));
       store_rope_pair(a, (size_t)rows[m], poss[m], rel, lds[m * ld + D + rel], lds[m * ld + D + rel + 1]);
     }
@@ -401,7 +423,7 @@ __device__ __forceinline__ void append_splitk_tile(const AppendArgs& a, int KS, 
     for (int e = 0; e < 16; ++e) red[w][mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][lane & 31] = acc[mb][e];
   __syncthreads();
   float* part = (float*)a.ws + (size_t)ks * M * N;
-  for (int idx = threadIdx.x; idx < M * 32; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < M * 32; idx += 256) {  // 256 threads (4 waves) per workgroup
     const int m = idx >> 5, c = idx & 31;
     if (n0 + c < N) part[(size_t)m * N + n0 + c] = red[0][m][c] + red[1][m][c] + red[2][m][c] + red[3][m][c];
   }
