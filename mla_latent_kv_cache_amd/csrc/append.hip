@@ -430,7 +430,8 @@ __global__ __launch_bounds__(512, 1) void append_small_bf16(AppendArgs a) {
 // output element per thread, all KS loads in one round) and runs the epilogue.
 
 __global__ __launch_bounds__(256) void append_splitk_bf16(AppendArgs a, int KS) {
-  append_splitk_tile(a, KS, blockIdx.x, blockIdx.y);
+  __shared__ SplitKLds sm;
+  append_splitk_tile(a, KS, blockIdx.x, blockIdx.y, sm);
 }
 
 __global__ __launch_bounds__(1024) void append_reduce(AppendArgs a, int KS) {

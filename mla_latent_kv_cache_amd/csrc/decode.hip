@@ -247,11 +247,17 @@ __global__ __launch_bounds__(512) void decode_qprep(DecodeArgs a) {
 // A = the query rows as they are (LDS, rows b, zero past d_h), B = W_uk row i stored at LDS row
 // nope_idx[i] (the i-th non-retained dim), every other row zero.  So nothing waits for the retained
 // pairs before the query loads: the workgroup issues all of its global loads at its start.
-__device__ __forceinline__ void qprep_mfma_tile(const DecodeArgs& a, int bx, int by, int bz) {
-  constexpr int WP = 128 + 8;  // LDS pitch of both tiles (elements)
-  __shared__ __attribute__((aligned(16))) bf16 wt[128 * WP];
-  __shared__ __attribute__((aligned(16))) bf16 qa[32 * WP];
-  __shared__ int dest[128];  // LDS row of W_uk row i (rows i >= d_nope are zero)
+constexpr int QP_WP = 128 + 8;  // LDS pitch of both q-prep tiles (elements)
+struct QprepLds {
+  __attribute__((aligned(16))) bf16 wt[128 * QP_WP];
+  __attribute__((aligned(16))) bf16 qa[32 * QP_WP];
+  int dest[128];  // LDS row of W_uk row i (rows i >= d_nope are zero)
+};
+__device__ __forceinline__ void qprep_mfma_tile(const DecodeArgs& a, int bx, int by, int bz, QprepLds& sm) {
+  constexpr int WP = QP_WP;
+  bf16* wt = sm.wt;
+  bf16* qa = sm.qa;
+  int* dest = sm.dest;
   const int h = bx, kb = by * 128, b0 = bz * 32;
   const int D = a.s.d_kv, dh = a.s.d_head, r = a.s.r_pairs, dn = a.s.d_nope(), half = dh / 2, NH = a.s.n_heads;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hb = lane >> 5;
@@ -367,7 +373,8 @@ __device__ __forceinline__ void qprep_mfma_tile(const DecodeArgs& a, int bx, int
 }
 
 __global__ __launch_bounds__(256) void decode_qprep_mfma(DecodeArgs a) {
-  qprep_mfma_tile(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  __shared__ QprepLds sm;
+  qprep_mfma_tile(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
 // Decode-step prologue: the new tokens' split-K append (phase 1) and the query preparation depend on
@@ -375,12 +382,17 @@ __global__ __launch_bounds__(256) void decode_qprep_mfma(DecodeArgs a) {
 // query-preparation tiles.
 __global__ __launch_bounds__(256) void decode_step_prologue(AppendArgs aa, int ks, DecodeArgs da) {
   const int nx = (aa.s.d_kv + aa.s.n_rope_cols() + 31) / 32, n_app = nx * ks;
+  // one LDS block for either role (a workgroup runs one of them), so that more workgroups fit on a CU
+  __shared__ union {
+    SplitKLds app;
+    QprepLds qp;
+  } sm;
   const int bid = blockIdx.x;
   if (bid < n_app) {
-    append_splitk_tile(aa, ks, bid % nx, bid / nx);
+    append_splitk_tile(aa, ks, bid % nx, bid / nx, sm.app);
   } else {
     const int j = bid - n_app, nh = da.s.n_heads, ny = da.s.d_kv / 128;
-    qprep_mfma_tile(da, j % nh, (j / nh) % ny, j / (nh * ny));
+    qprep_mfma_tile(da, j % nh, (j / nh) % ny, j / (nh * ny), sm.qp);
   }
 }
 

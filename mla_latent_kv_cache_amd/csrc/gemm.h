@@ -116,19 +116,22 @@ __device__ __forceinline__ void gemm_tile(char* lds, int K, ARow a_row, BRow b_r
   wait_stage(0);
   lds_barrier();
   if (C::NSTG - 1 < KT) issue(C::NSTG - 1);
+  // (the last stage is peeled off: a branch around the barrier part would join the two paths before
+  // mma(f1), and the compiler's wait for f1 there would then also wait for the next stage's reads)
   Frag f0, f1;
   load(f0, 0, 0);
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = 0; kt + 1 < KT; ++kt) {
     load(f1, kt, 1);
     mma(f0);
-    if (kt + 1 < KT) {
-      wait_stage(kt + 1);
-      lds_barrier();
-      if (kt + C::NSTG < KT) issue(kt + C::NSTG);
-      load(f0, kt + 1, 0);
-    }
+    wait_stage(kt + 1);
+    lds_barrier();
+    if (kt + C::NSTG < KT) issue(kt + C::NSTG);
+    load(f0, kt + 1, 0);
     mma(f1);
   }
+  load(f1, KT - 1, 1);
+  mma(f0);
+  mma(f1);
 }
 
 }  // namespace mla

@@ -390,8 +390,13 @@ __device__ __forceinline__ bool append_rows_fused(const AppendArgs& a, int KS, i
 // Split-K append, phase 1, workgroup (bx: 32 output columns, by: one of KS slices of the model width):
 // 4 waves split the slice, MFMA 32x32x16 over up to two 32-token blocks, and the workgroup's partial
 // sums (fp32, [KS][M][N]) go to the workspace.  The reduction and epilogue run in append_reduce.
-__device__ __forceinline__ void append_splitk_tile(const AppendArgs& a, int KS, int bx, int by) {
-  __shared__ float red[4][SM_MAXM][32];
+// LDS of one split-K append tile (the caller provides it, so that a launch that also runs other tiles can
+// overlay their LDS).
+struct SplitKLds {
+  float red[4][SM_MAXM][32];
+};
+__device__ __forceinline__ void append_splitk_tile(const AppendArgs& a, int KS, int bx, int by, SplitKLds& sm) {
+  auto& red = sm.red;
   const int K = a.s.d_model, D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR;
   const int M = a.batch * a.t_new, MB = (M + 31) / 32;
   const int n0 = bx * 32, ks = by;
