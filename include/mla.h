@@ -79,17 +79,22 @@ typedef struct {
   int32_t d_kv;      /* latent width (rank of the joint SVD), shared by all heads */
   int32_t dtype;     /* mla_dtype                                                 */
   int32_t cache_fmt; /* mla_cache_fmt                                             */
+  int32_t rope_heads;/* RoPE key heads n_rh: 0 (= n_heads, keys per query head) or a divisor of
+                        n_heads; query head h then uses RoPE key head h / (n_heads / n_rh), the
+                        layout of a layer converted from a grouped-query source (one key head per
+                        KV head, shared by its query heads)                                   */
 } mla_config;
 
-/* Converted weights (read-only, device).  nope(h) = the d_h - 2r dims of head h whose subspace is
- * not kept, ascending; rope(h) = dims 2p, 2p+1 for p = pair_idx[h][j], j = 0..r-1.              */
+/* Converted weights (read-only, device).  n_rh = rope_heads (n_h when 0), g(h) = h / (n_h / n_rh) the
+ * RoPE key head of query head h.  nope(h) = the d_h - 2r dims of head h whose subspace is not kept,
+ * ascending; rope(h) = dims 2p, 2p+1 for p = pair_idx[g(h)][j], j = 0..r-1.                      */
 typedef struct {
   const void *w_dkv;        /* [d_kv, d_model]           W_dkv^T (down-projection, U_trunc)      */
-  const void *w_krope;      /* [n_h*2r, d_model]         rows (h, j, c) = column 2p+c of head h
-                                                          of W_k, p = pair_idx[h][j]               */
+  const void *w_krope;      /* [n_rh*2r, d_model]        rows (g, j, c) = column 2p+c of key head g
+                                                          of W_k, p = pair_idx[g][j]               */
   const void *w_uk;         /* [n_h, d_h-2r, d_kv]       W_uk,h^T: row i rebuilds K dim nope(h)[i] */
   const void *w_uv;         /* [n_h, d_h, d_kv]          W_uv,h^T: row e rebuilds V dim e          */
-  const int32_t *pair_idx;  /* [n_h, r] int32, ascending per head, each in [0, d_h/2)           */
+  const int32_t *pair_idx;  /* [n_rh, r] int32, ascending per key head, each in [0, d_h/2)      */
   const float *rope_cos;    /* [rope_len, d_h/2] fp32: cos(pos * theta^(-2p/d_h))               */
   const float *rope_sin;    /* [rope_len, d_h/2] fp32: sin(...)                                 */
   int32_t rope_len;         /* rows of the RoPE tables (positions 0..rope_len-1)                */
@@ -110,7 +115,7 @@ typedef struct {
  *             window >= 0 (0: every row is codes); ckv_window may be NULL when window == 0
  *   INT4_G32_WIN: ckv and ckv_scale as INT4_G32 (row pos holds position pos once it has left the window),
  *             ckv_window and window as INT2_G32_WIN
- *   all:      krope [batch, t_max, n_h, 2r]   config dtype, pair (j, c) of head h at index h*2r + 2j + c
+ *   all:      krope [batch, t_max, n_rh, 2r]  config dtype, pair (j, c) of key head g at index g*2r + 2j + c
  * ckv_window and window are read for the windowed formats (INT2_G32_WIN, INT4_G32_WIN) only.
  *
  * Paged caches (block_table != NULL; DENSE and INT4_G32, not the windowed formats): ckv, ckv_scale and krope

@@ -36,7 +36,8 @@ EXPORTED = [
 
 
 class MlaConfig(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("d_model", "n_heads", "d_head", "r_pairs", "d_kv", "dtype", "cache_fmt")]
+    _fields_ = [(n, ctypes.c_int32)
+                for n in ("d_model", "n_heads", "d_head", "r_pairs", "d_kv", "dtype", "cache_fmt", "rope_heads")]
 
 
 class MlaWeights(ctypes.Structure):

@@ -46,10 +46,17 @@ class LayerShape:
     d_kv: int
     dtype: str = "bf16"  # "bf16" or "f32"
     cache_fmt: str = "dense"  # "dense", "int4_g32", "int2_g32_win" or "int4_g32_win"
+    # RoPE key heads: 0 (= n_heads, keys per query head) or a divisor of n_heads -- query head h uses key
+    # head h // (n_heads // rope_heads), the layout of a layer converted from a grouped-query source
+    rope_heads: int = 0
 
     @property
     def torch_dtype(self):
         return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    @property
+    def n_rope_heads(self) -> int:
+        return self.rope_heads or self.n_heads
 
     def c(self) -> MlaConfig:
         return MlaConfig(
@@ -60,6 +67,7 @@ class LayerShape:
             self.d_kv,
             MLA_BF16 if self.dtype == "bf16" else MLA_F32,
             _FMT[self.cache_fmt],
+            self.rope_heads,
         )
 
 
@@ -136,19 +144,38 @@ class LayerWeights:
 
 
 def pack_weights(shape: LayerShape, conv: dict, rope_len: int, theta: float = 1e4, device="cuda") -> LayerWeights:
-    """Move converted weights (math layouts: w_dkv [d, d_kv], w_krope [d, n_h*2r], w_uk [n_h, d_kv, d_h-2r],
-    w_uv [n_h, d_kv, d_h], pair_idx [n_h, r]) to the device in the ABI layouts and dtype."""
+    """Move converted weights (math layouts: w_dkv [d, d_kv], w_krope [d, n_rh*2r], w_uk [n_h, d_kv, d_h-2r],
+    w_uv [n_h, d_kv, d_h], pair_idx [n_rh, r]; n_rh = shape.n_rope_heads) to the device in the ABI layouts and
+    dtype."""
     dt = shape.torch_dtype
 
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(device=device, dtype=dt).contiguous()
 
     n_h, dn, dh, D, d = shape.n_heads, shape.d_head - 2 * shape.r_pairs, shape.d_head, shape.d_kv, shape.d_model
+    w_krope_m = np.asarray(conv["w_krope"]).reshape(d, -1)
+    pair_idx = np.asarray(conv["pair_idx"])
+    nrh = shape.n_rope_heads
+    if nrh != n_h and pair_idx.shape[0] == n_h:
+        # a layer expanded per query head (the GQA conversion): one RoPE key head per group of n_h / nrh heads,
+        # which must all carry the same kept pairs and key columns
+        hpg = n_h // nrh
+        wk3 = w_krope_m.reshape(d, n_h, -1)
+        for g in range(nrh):
+            heads = range(g * hpg, (g + 1) * hpg)
+            if any(not np.array_equal(pair_idx[h], pair_idx[g * hpg]) or not np.array_equal(wk3[:, h], wk3[:, g * hpg])
+                   for h in heads):
+                raise ValueError(f"query heads of RoPE key head {g} differ in their kept pairs or key columns")
+        pair_idx = pair_idx[::hpg]
+        w_krope_m = wk3[:, ::hpg, :].reshape(d, -1)
+    if pair_idx.shape != (nrh, shape.r_pairs) or w_krope_m.shape != (d, nrh * 2 * shape.r_pairs):
+        raise ValueError(f"pair_idx {pair_idx.shape} / w_krope {w_krope_m.shape} do not hold {nrh} RoPE key heads "
+                         f"of {shape.r_pairs} pairs")
     w_dkv = dev(np.asarray(conv["w_dkv"]).T)
-    w_krope = dev(np.asarray(conv["w_krope"]).reshape(d, -1).T)
+    w_krope = dev(w_krope_m.T)
     w_uk = dev(np.asarray(conv["w_uk"]).reshape(n_h, D, dn).transpose(0, 2, 1))
     w_uv = dev(np.asarray(conv["w_uv"]).reshape(n_h, D, dh).transpose(0, 2, 1))
-    pidx = torch.from_numpy(np.ascontiguousarray(conv["pair_idx"], dtype=np.int32)).to(device)
+    pidx = torch.from_numpy(np.ascontiguousarray(pair_idx, dtype=np.int32)).to(device)
     cos, sin = rope_tables(rope_len, dh, theta)
     return LayerWeights(shape, w_dkv, w_krope, w_uk, w_uv, pidx, torch.from_numpy(cos).to(device),
                         torch.from_numpy(sin).to(device))
@@ -179,7 +206,7 @@ class LatentCache:
     def allocate(shape: LayerShape, batch: int, t_max: int, device="cuda", fill: Optional[float] = None,
                  window: int = 128):
         """`window` (windowed formats only) is the number of recent rows kept in bf16 per sequence."""
-        nr = shape.n_heads * 2 * shape.r_pairs
+        nr = shape.n_rope_heads * 2 * shape.r_pairs
         ring = None
         if shape.cache_fmt in ("int4_g32", "int4_g32_win"):
             ckv = torch.zeros((batch, t_max, shape.d_kv // 2), dtype=torch.uint8, device=device)
@@ -211,7 +238,7 @@ class LatentCache:
         if shape.cache_fmt in WINDOWED:
             raise ValueError("paged caches hold dense or int4 latents")
         batch, pps = block_table.shape
-        nr = shape.n_heads * 2 * shape.r_pairs
+        nr = shape.n_rope_heads * 2 * shape.r_pairs
         if shape.cache_fmt == "int4_g32":
             ckv = torch.zeros((n_pages, page_size, shape.d_kv // 2), dtype=torch.uint8, device=device)
             scale = torch.zeros((n_pages, page_size, shape.d_kv // 32), dtype=torch.float16, device=device)
@@ -261,8 +288,11 @@ def _weight_specs(w: LayerWeights, cache: LatentCache):
         raise ValueError(f"weights are for {w.shape}, the cache for {cache.shape}")
     dev, s = cache.ckv.device, w.shape
     rope = (w.rope_cos.shape[0], s.d_head // 2)
-    return ([(getattr(w, n), n, s.torch_dtype, None, dev) for n in ("w_dkv", "w_krope", "w_uk", "w_uv")] +
-            [(w.pair_idx, "pair_idx", torch.int32, (s.n_heads, s.r_pairs), dev),
+    dn, nrh = s.d_head - 2 * s.r_pairs, s.n_rope_heads
+    shapes = {"w_dkv": (s.d_kv, s.d_model), "w_krope": (nrh * 2 * s.r_pairs, s.d_model),
+              "w_uk": (s.n_heads, dn, s.d_kv), "w_uv": (s.n_heads, s.d_head, s.d_kv)}
+    return ([(getattr(w, n), n, s.torch_dtype, shp, dev) for n, shp in shapes.items()] +
+            [(w.pair_idx, "pair_idx", torch.int32, (nrh, s.r_pairs), dev),
              (w.rope_cos, "rope_cos", torch.float32, rope, dev), (w.rope_sin, "rope_sin", torch.float32, rope, dev)])
 
 

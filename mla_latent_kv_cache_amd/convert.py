@@ -117,7 +117,8 @@ def _factor(w_k, w_v, pair_idx, n_kv, d_head, d_kv, svd):
     return out
 
 
-def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv, strategy="2-norm", svd="joint", n_kv_heads=None):
+def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv, strategy="2-norm", svd="joint", n_kv_heads=None,
+                  compact_rope=False):
     """Returns the converted layer in math layouts:
     pair_idx [n_h, r], w_dkv [d, d_kv], w_krope [d, n_h*2r], w_uk [n_h, d_kv, d_h-2r], w_uv [n_h, d_kv, d_h],
     and the singular values: sigma (all of [W_k,nope | W_v]) for the joint SVD, sigma_k / sigma_v (of W_k,nope
@@ -131,7 +132,9 @@ def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv, strategy="2-no
     n_kv_heads < n_heads converts a grouped-query layer (w_k, w_v [d, n_kv*d_h]; query head h reads KV head
     h // (n_heads / n_kv)): subspaces are kept per KV head by the group's mean score, the low-rank step runs
     over the n_kv heads' columns, and the result is expanded per query head (each head takes its group's
-    kept subspaces, RoPE key columns and up-projections; the per-group factors are under `group_*`)."""
+    kept subspaces, RoPE key columns and up-projections; the per-group factors are under `group_*`).  With
+    compact_rope the RoPE part stays per KV head instead: pair_idx [n_kv, r] and w_krope [d, n_kv*2r], the
+    layout of a cache that stores each group's RoPE keys once (LayerShape.rope_heads = n_kv)."""
     n_kv = n_heads if n_kv_heads is None else int(n_kv_heads)
     if n_kv <= 0 or n_heads % n_kv:
         raise ValueError("n_kv_heads must divide n_heads")
@@ -148,4 +151,6 @@ def convert_layer(w_q, w_k, w_v, x_cal, n_heads, d_head, r, d_kv, strategy="2-no
                w_krope=f["w_krope"].reshape(d, n_kv, 2 * r)[:, grp, :].reshape(d, n_heads * 2 * r),
                w_uk=np.ascontiguousarray(f["w_uk"][grp]), w_uv=np.ascontiguousarray(f["w_uv"][grp]),
                group_w_uk=f["w_uk"], group_w_uv=f["w_uv"], group_w_krope=f["w_krope"])
+    if compact_rope:
+        out.update(pair_idx=pair_idx, w_krope=f["w_krope"])
     return out

@@ -29,13 +29,15 @@ int check_config(const mla_config* c) {
   if (c->cache_fmt != MLA_CACHE_DENSE && c->cache_fmt != MLA_CACHE_INT4_G32 && c->cache_fmt != MLA_CACHE_INT2_G32_WIN &&
       c->cache_fmt != MLA_CACHE_INT4_G32_WIN)
     return MLA_ERR_INVALID_ARG;
+  if (c->rope_heads < 0 || (c->rope_heads > 0 && c->n_heads % c->rope_heads != 0)) return MLA_ERR_INVALID_ARG;
   if (c->d_head > 256) return MLA_ERR_UNSUPPORTED;
   if (c->cache_fmt != MLA_CACHE_DENSE && (c->dtype != MLA_BF16 || c->d_kv % 32 != 0)) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 
 Shape shape_of(const mla_config* c) {
-  return Shape{c->d_model, c->n_heads, c->d_head, c->r_pairs, c->d_kv, c->dtype, c->cache_fmt};
+  return Shape{c->d_model, c->n_heads, c->d_head, c->r_pairs, c->d_kv, c->dtype, c->cache_fmt,
+               c->rope_heads > 0 ? c->rope_heads : c->n_heads};
 }
 
 // A pointer that must be present (non-null, 16-byte aligned) when `needed`.

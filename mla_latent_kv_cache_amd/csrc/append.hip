@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void append_generic(AppendArgs a) {
   }
   const int r = a.s.r_pairs, R2 = a.s.r2(), half = a.s.d_head / 2;
   T* kr = (T*)a.krope + row * NR;
-  for (int q = threadIdx.x; q < a.s.n_heads * r; q += blockDim.x) {
+  for (int q = threadIdx.x; q < a.s.rope_heads * r; q += blockDim.x) {  // h: RoPE key head
     int h = q / r, j = q - h * r;
     int p = load_pair(a.pair_idx, h * r + j, half);
     float c = a.rope_cos[(size_t)pos * half + p], s = a.rope_sin[(size_t)pos * half + p];

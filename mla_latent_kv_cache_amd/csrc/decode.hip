@@ -181,7 +181,7 @@ __global__ __launch_bounds__(512) void decode_qprep(DecodeArgs a) {
   for (int u = 0; u < QMAXI; ++u) {
     if (u < per) wv[u] = to_f32(wuk[(size_t)min(i0 + u, dn - 1) * D]);
   }
-  build_nope_idx(a.pair_idx, h, r, half, kept, nope_idx);
+  build_nope_idx(a.pair_idx, a.s.rope_head(h), r, half, kept, nope_idx);
   __syncthreads();
   const T* q = (const T*)a.q;
   {  // gather the NoPE query dims of the QB rows in one round (QB * d_nope <= 4 * blockDim)
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(512) void decode_qprep(DecodeArgs a) {
     if (b >= a.batch) continue;
     int L = clamp_len(a, b);
     int pos = L > 0 ? L - 1 : 0;
-    int p = load_pair(a.pair_idx, h * r + j, half);
+    int p = load_pair(a.pair_idx, a.s.rope_head(h) * r + j, half);
     float x0 = to_f32(q[((size_t)b * NH + h) * dh + 2 * p]), x1 = to_f32(q[((size_t)b * NH + h) * dh + 2 * p + 1]);
     float c = a.rope_cos[(size_t)pos * half + p], s = a.rope_sin[(size_t)pos * half + p];
     qr[((size_t)b * NH + h) * 2 * r + 2 * j] = (x0 * c - x1 * s) * scale;
@@ -269,9 +269,10 @@ __device__ __forceinline__ void qprep_mfma_tile(const DecodeArgs& a, int bx, int
   const int rbb = rot ? tid / r : 0, rj = rot ? tid - rbb * r : 0, rb = b0 + rbb;
   const bool rok = rot && rb < a.batch;
   int pk_raw = 0, rp_raw = 0, rL_raw = 0;
-  if (tid < r) pk_raw = a.pair_idx[h * r + tid];
+  const int g = a.s.rope_head(h);  // the head's row of the pair table
+  if (tid < r) pk_raw = a.pair_idx[g * r + tid];
   if (rok) {
-    rp_raw = a.pair_idx[h * r + rj];
+    rp_raw = a.pair_idx[g * r + rj];
     rL_raw = a.seq_lens[cseq(a, rb)];
   }
   // (the tile loads read a clamped in-bounds address and are zeroed afterwards: a load under a branch
@@ -363,7 +364,7 @@ __device__ __forceinline__ void qprep_mfma_tile(const DecodeArgs& a, int bx, int
       const int bb = idx / r, j = idx - bb * r, b = b0 + bb;
       if (b >= a.batch) continue;
       const int L = clamp_len(a, b), pos = L > 0 ? L - 1 : 0;
-      const int p = load_pair(a.pair_idx, h * r + j, half);
+      const int p = load_pair(a.pair_idx, g * r + j, half);
       const float x0 = (float)qa[bb * WP + 2 * p], x1 = (float)qa[bb * WP + 2 * p + 1];
       const float c = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
       qr[((size_t)b * NH + h) * 2 * r + 2 * j] = (x0 * c - x1 * sn) * scale;
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
         for (int t = threadIdx.x; t < n; t += blockDim.x) {
           float s = 0.f;
           for (int k = 0; k < D; ++k) s = fmaf(qs[k], lat(r0 + t, win, k), s);
-          const T* kr = (const T*)a.krope + ((size_t)seq_row(a, b, r0 + t) * NH + h) * R2;
+          const T* kr = (const T*)a.krope + ((size_t)seq_row(a, b, r0 + t) * a.s.rope_heads + a.s.rope_head(h)) * R2;
           for (int j = 0; j < R2; ++j) s = fmaf(qrs[j], to_f32(kr[j]), s);
           sc[t] = s;
           mloc = fmaxf(mloc, s);
@@ -643,6 +644,8 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   const size_t rowb = (size_t)cseq(a, b) * a.t_max;
   const bf16* krb = (const bf16*)a.krope;
   bf16* cw = cbuf[w];
+  // RoPE key rows: NRH key heads of R2 dims (NRH = 32, or fewer when query heads share keys)
+  const int NRH = a.s.rope_heads, KRW = NRH * R2;
 
   // ---- register prefetch, two tiles deep: this wave's latent slice and its share of the RoPE keys
   // 16-byte chunks per row of the wave's slice: 8 bf16, 32 int4 or 64 2-bit latents each
@@ -665,7 +668,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
     coff[it] = row * RBY + (CODEC == 0 ? 2 * (w * DW + 8 * q) : (CODEC == 1 ? (w * DW + 32 * q) / 2 : (w * DW + 64 * q) / 4));
     soff[it] = MBY * (row * (D / 32) + (w * DW) / 32 + (CODEC == 2 ? 2 * q : q));
   }
-  const uint32_t koff = ((xt0 * 32 + xh) * R2) * 2;  // RoPE keys of the lane's 4 tokens, head xh
+  const uint32_t koff = ((xt0 * NRH + a.s.rope_head(xh)) * R2) * 2;  // RoPE keys of the lane's 4 tokens, head xh
   // window items (2-bit format) stage their bf16 rows straight from the ring in stage_window and
   // prefetch only the RoPE keys here
   auto load_tile = [&](auto bsel, auto winsel, int tt) {
@@ -677,7 +680,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
     if (tt + 32 <= t1) {
       const char* cb = (const char*)a.ckv + (row0 + tb) * RBY;
       const char* sb = (const char*)a.ckv_scale + (row0 + tb) * (D / 32) * MBY;
-      const char* kb = (const char*)(krb + row0 * 32 * R2) + (size_t)tb * 32 * R2 * 2 + koff;
+      const char* kb = (const char*)(krb + row0 * KRW) + (size_t)tb * KRW * 2 + koff;
       if constexpr (!WIN) {
 #pragma unroll
         for (int it = 0; it < CCH; ++it) {
@@ -686,7 +689,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kreg[B][i] = *(const kv_t*)(kb + i * 32 * R2 * 2);
+      for (int i = 0; i < 4; ++i) kreg[B][i] = *(const kv_t*)(kb + i * KRW * 2);
       return;
     }
     if constexpr (!WIN) {
@@ -703,7 +706,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int tok = min(tt + xt0 + i, t1 - 1);
-      kreg[B][i] = *(const kv_t*)(krb + row0 * 32 * R2 + ((size_t)(tok - tt + tb) * 32 + xh) * R2);
+      kreg[B][i] = *(const kv_t*)(krb + row0 * KRW + ((size_t)(tok - tt + tb) * NRH + a.s.rope_head(xh)) * R2);
     }
   };
   auto stage_tile = [&](auto bsel) {
@@ -926,12 +929,19 @@ __device__ __forceinline__ char* own_at(char* kss, int w, int L) {
 // factors) through the part of the RoPE slot that only it reads, its own heads' keys, once it has read
 // them; the next RoPE load into that slot therefore waits for the following tile's first barrier.  Per
 // lane and tile: 4 partial-score reads, 4 exponentials, two probability reads, two barriers.
-template <int DW, int R2, int NSLOT, bool PG>
+// CR (compact RoPE rows): the cache holds 8 RoPE key heads per row, query heads 4g .. 4g+3 sharing key
+// head g (a layer converted from a grouped-query source); each wave loads its 8 rows of them (1 KB) into
+// the end of its part of the RoPE slot and spreads them to the per-head layout before the tile's first
+// barrier, so that everything after reads the per-head layout as usual.
+template <int DW, int R2, int NSLOT, bool PG, bool CR = false>
 __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs f) {
+  static_assert(!CR || R2 == 8, "compact RoPE rows hold 8 key heads of 8 dims");
   constexpr int NS = DW / 16, NB = DW / 32, D = 4 * DW;
   constexpr int CSL = 32 * DW * 2;       // bytes of one wave's latent slice of a tile
-  constexpr int KSL = 8 * 32 * R2 * 2;   // bytes of one wave's RoPE rows of a tile
-  constexpr int NC = CSL / 1024, NK = KSL / 1024;
+  constexpr int KSL = 8 * 32 * R2 * 2;   // bytes of one wave's RoPE rows of a tile (per-head layout)
+  constexpr int RRB = (CR ? 8 : 32) * R2 * 2;  // RoPE bytes per cache row
+  constexpr int KDST = CR ? KSL - 1024 : 0;    // where a wave's RoPE rows land in its part of the slot
+  constexpr int NC = CSL / 1024, NK = 8 * RRB / 1024;
   constexpr int RB = DW * 2;             // bytes per slice row
   constexpr float kRescale = 8.f;        // log2 headroom before the running max must be raised
   __shared__ __attribute__((aligned(1024))) char cs0[4 * CSL], cs1[4 * CSL], cs2[NSLOT > 2 ? 4 * CSL : 16];
@@ -957,8 +967,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
   const size_t rowb = (size_t)cseq(a, b) * a.t_max;
   // contiguous cache: the sequence's bases, a tile at a fixed offset from them
   const char* cbase = (const char*)a.ckv + (rowb * D + wu * DW) * 2;
-  const char* kseq = (const char*)a.krope + rowb * 32 * R2 * 2;
-  const char* kbase = kseq + 8 * wu * 32 * R2 * 2;
+  const char* kseq = (const char*)a.krope + rowb * RRB;
+  const char* kbase = kseq + 8 * wu * RRB;
   uint32_t coff[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
@@ -988,7 +998,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
       const int pi = __builtin_amdgcn_readfirstlane(tt / a.pm.page - pg0);
       const size_t prow = (size_t)__builtin_amdgcn_readlane(pid, pi) * a.pm.page + tt % a.pm.page;
       cb0 = (const char*)a.ckv + (prow * D + wu * DW) * 2;
-      kt = (const char*)a.krope + prow * (32 * R2 * 2);
+      kt = (const char*)a.krope + prow * RRB;
       tb = 0;
     } else {
       cb0 = cbase;
@@ -1011,15 +1021,15 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
     // the wave's RoPE rows 8w .. 8w+7 of the tile are one contiguous block
     if (!(PARTS & 2)) {
     } else if (tt + 8 * wu + 8 <= t1) {
-      const char* kb = (PG ? kt + 8 * wu * 32 * R2 * 2 : kbase) + (size_t)tb * (32 * R2 * 2);
+      const char* kb = (PG ? kt + 8 * wu * RRB : kbase) + (size_t)tb * RRB;
 #pragma unroll
-      for (int j = 0; j < NK; ++j) dma16(kb, (uint32_t)(1024 * j + 16 * lane), k_lds[SL] + 1024 * j);
+      for (int j = 0; j < NK; ++j) dma16(kb, (uint32_t)(1024 * j + 16 * lane), k_lds[SL] + KDST + 1024 * j);
     } else {
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
-        const int off = 1024 * j + 16 * lane, tk = off / (64 * R2), within = off % (64 * R2);
+        const int off = 1024 * j + 16 * lane, tk = off / RRB, within = off % RRB;
         const int tok = min(tt + 8 * wu + tk, t1 - 1) - tt + tb;  // row relative to the base, >= 0
-        dma16(kt, (uint32_t)(tok * (64 * R2) + within), k_lds[SL] + 1024 * j);
+        dma16(kt, (uint32_t)(tok * RRB + within), k_lds[SL] + KDST + 1024 * j);
       }
     }
   };
@@ -1101,6 +1111,14 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
       }
     } else {
       MLA_WAIT_VMCNT(0);
+    }
+    if constexpr (CR) {
+      // lane l holds key head l % 8 of row l / 8 (16 bytes); it writes them for query heads 4g .. 4g+3
+      char* kr = kss + wu * KSL;
+      const bf16x8 kv8 = *(const bf16x8*)(kr + KDST + 16 * lane);
+      const int row = lane >> 3, g = lane & 7;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(bf16x8*)(kr + row * (32 * R2 * 2) + (4 * g + i) * (R2 * 2)) = kv8;
     }
     __builtin_amdgcn_wave_barrier();
     if (ahead < t1) issue_slot(std::integral_constant<int, NX>{}, ahead, PC{});
@@ -2016,7 +2034,14 @@ void launch_generic_attn(const DecodeArgs& a, hipStream_t st) {
 
 template <int DW, int R2>
 void launch_mfma_attn(const DecodeArgs& a, const FuseArgs& f, hipStream_t st) {
-  if (a.s.fmt == 0)
+  if (a.s.fmt == 0 && a.s.compact_rope()) {
+    if constexpr (R2 == 8) {  // 8 key heads (decode_uses_mfma admits no other compact shape here)
+      if (a.pm.bt)
+        hipLaunchKernelGGL((decode_attn_dma<DW, R2, 3, true, true>), attn_grid(a, f), dim3(256), 0, st, a, f);
+      else
+        hipLaunchKernelGGL((decode_attn_dma<DW, R2, 3, false, true>), attn_grid(a, f), dim3(256), 0, st, a, f);
+    }
+  } else if (a.s.fmt == 0)
     if (a.pm.bt)
       hipLaunchKernelGGL((decode_attn_dma<DW, R2, 3, true>), attn_grid(a, f), dim3(256), 0, st, a, f);
     else
@@ -2037,7 +2062,8 @@ void launch_mfma_attn(const DecodeArgs& a, const FuseArgs& f, hipStream_t st) {
 // Latent width 256 (bf16 or int4).  At width 512 the register-staged kernel is as fast for int4 (its
 // dequantisation runs on two workgroups per CU) and the DMA ring kernel faster for bf16.
 bool decode_uses_wave(const Shape& s) {
-  return s.dtype == 1 && s.fmt <= 1 && s.n_heads == 32 && (s.r_pairs == 2 || s.r_pairs == 4) && s.d_kv == 256;
+  return s.dtype == 1 && s.fmt <= 1 && s.n_heads == 32 && (s.r_pairs == 2 || s.r_pairs == 4) && s.d_kv == 256 &&
+         !s.compact_rope();
 }
 
 // Specialised attention kernels that run the second phase of a split-K append (see FuseArgs).
@@ -2047,9 +2073,12 @@ static bool attn_takes_append(const Shape& s) {
 
 // (at latent width 256 the dense and int4 formats take the per-wave kernel; the 2-bit format runs the
 // register-staged kernel at width 512 only)
+// Shared RoPE keys: the int4 / 2-bit kernel indexes them per key head (any divisor of the heads); the
+// dense DMA kernel has a compact instance for 8 key heads of 4 pairs.
 bool decode_uses_mfma(const Shape& s) {
   return s.dtype == 1 && s.n_heads == 32 && (s.d_kv == 512 || (s.d_kv == 256 && s.fmt <= 1)) &&
-         (s.r_pairs == 2 || s.r_pairs == 4);
+         (s.r_pairs == 2 || s.r_pairs == 4) &&
+         (!s.compact_rope() || (s.d_kv == 512 && (s.fmt != 0 || (s.rope_heads == 8 && s.r_pairs == 4))));
 }
 
 bool decode_uses_combine(const Shape& s) {

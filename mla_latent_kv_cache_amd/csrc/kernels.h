@@ -12,9 +12,13 @@ struct Shape {
   int d_model, n_heads, d_head, r_pairs, d_kv;
   int dtype;  // 0 f32, 1 bf16
   int fmt;    // 0 dense, 1 int4 g32, 2 int2 g32 with a bf16 window of recent rows, 3 int4 g32 with that window
+  int rope_heads;  // RoPE key heads (n_heads, or a divisor: consecutive query heads share one)
   __host__ __device__ int r2() const { return 2 * r_pairs; }
   __host__ __device__ int d_nope() const { return d_head - 2 * r_pairs; }
-  __host__ __device__ int n_rope_cols() const { return n_heads * 2 * r_pairs; }
+  __host__ __device__ int n_rope_cols() const { return rope_heads * 2 * r_pairs; }
+  // RoPE key head (row of the pair table and of W_krope, slot of a cache row's keys) of query head h
+  __host__ __device__ int rope_head(int h) const { return h / (n_heads / rope_heads); }
+  __host__ __device__ bool compact_rope() const { return rope_heads != n_heads; }
 };
 
 // Where the rows of a cache sequence live: contiguous (b * t_max + pos) when bt is null, else through a

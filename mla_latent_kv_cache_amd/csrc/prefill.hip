@@ -104,8 +104,9 @@ __global__ __launch_bounds__(256, 2) void rec_k_gemm(PrefillArgs a, int M) {
     orow[tid] = m < M ? (b * NH + hh) * SP + t : -1;
     lrow[tid] = m < M ? (a.lat_staged ? m : crow[tid]) : -1;  // staged rows: [b * S + t]
   }
-  build_nope_idx(a.pair_idx, hh, r, 64, kept, dim_of);
-  if (tid < R2) dim_of[dn + tid] = 2 * load_pair(a.pair_idx, hh * r + (tid >> 1), 64) + (tid & 1);
+  const int gh = a.s.rope_head(hh), NRH = a.s.rope_heads;  // the head's RoPE key head
+  build_nope_idx(a.pair_idx, gh, r, 64, kept, dim_of);
+  if (tid < R2) dim_of[dn + tid] = 2 * load_pair(a.pair_idx, gh * r + (tid >> 1), 64) + (tid & 1);
   __syncthreads();
   const bf16* ckv = (const bf16*)(a.lat_staged ? (const void*)(a.ws + a.plan.off_lat) : a.ckv);
   const int last = lrow[min(M - 1 - m0, 255)];
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void rec_k_gemm(PrefillArgs a, int M) {
   const bf16* kr = (const bf16*)a.krope;
   if (R2 <= 16) {
     const int c = crow[tid];
-    const uint32_t* src = (const uint32_t*)(kr + ((size_t)(c >= 0 ? c : 0) * NH + hh) * R2);
+    const uint32_t* src = (const uint32_t*)(kr + ((size_t)(c >= 0 ? c : 0) * NRH + gh) * R2);
     uint32_t kv[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) kv[q] = (c >= 0 && 2 * q < R2) ? src[q] : 0u;
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(256, 2) void rec_k_gemm(PrefillArgs a, int M) {
   } else {
     for (int idx = tid; idx < 256 * R2; idx += 256) {
       const int row = idx / R2, q = idx - row * R2, c = crow[row];
-      const bf16 v = c >= 0 ? kr[((size_t)c * NH + hh) * R2 + q] : (bf16)0.f;
+      const bf16 v = c >= 0 ? kr[((size_t)c * NRH + gh) * R2 + q] : (bf16)0.f;
       *(bf16*)(lds + stage_off(row, dim_of[dn + q], 256)) = v;
     }
   }
@@ -266,7 +267,7 @@ __device__ __forceinline__ void attend_query_tile(const PrefillArgs& a, char* ri
   int pp[RP];
 #pragma unroll
   for (int j = 0; j < RP; ++j)
-    if (j < r) pp[j] = load_pair(a.pair_idx, h * r + j, 64);
+    if (j < r) pp[j] = load_pair(a.pair_idx, a.s.rope_head(h) * r + j, 64);
   MLA_WAIT_VMCNT(0);
   const uint32_t ring_lds = lds_addr_of(ring);
   auto issue = [&](int kt) {
@@ -321,7 +322,7 @@ __device__ __forceinline__ void attend_query_tile(const PrefillArgs& a, char* ri
     for (int j = 0; j < RP; ++j)
       if (j < r) rotate(pp[j], pc[j], ps[j]);
     for (int j = RP; j < r; ++j) {
-      const int p = load_pair(a.pair_idx, h * r + j, 64);
+      const int p = load_pair(a.pair_idx, a.s.rope_head(h) * r + j, 64);
       rotate(p, a.rope_cos[(size_t)pos * 64 + p], a.rope_sin[(size_t)pos * 64 + p]);
     }
     const float scale = kLog2e / sqrtf(128.f);

@@ -72,10 +72,25 @@ def gqa_converted_layer(family: str, r: int, d_kv: int, dtype: str):
     return out
 
 
-def shape_of(cfg):
+def shape_of(cfg, rope_heads=0):
     from mla_latent_kv_cache_amd import LayerShape
 
-    return LayerShape(cfg.d_model, cfg.n_heads, cfg.d_head, cfg.r_pairs, cfg.d_kv, cfg.dtype, cfg.cache_fmt)
+    return LayerShape(cfg.d_model, cfg.n_heads, cfg.d_head, cfg.r_pairs, cfg.d_kv, cfg.dtype, cfg.cache_fmt,
+                      rope_heads=rope_heads)
+
+
+def rope_key_rows(kr, n_heads, rope_heads=0):
+    """The oracle's RoPE keys [L, n_heads * 2r] (one key per query head) in the cache layout of `rope_heads` key
+    heads: key head g is query head g * (n_heads / rope_heads), whose group all hold the same key."""
+    kr = np.asarray(kr)
+    if not rope_heads or rope_heads == n_heads:
+        return kr
+    L = kr.shape[0]
+    k3 = kr.reshape(L, n_heads, -1)
+    hpg = n_heads // rope_heads
+    for g in range(rope_heads):  # the shared key is one key: every head of the group computes the same one
+        assert np.array_equal(k3[:, g * hpg:(g + 1) * hpg], np.repeat(k3[:, g * hpg:g * hpg + 1], hpg, axis=1))
+    return k3[:, ::hpg].reshape(L, -1)
 
 
 def torch_dtype(cfg):

@@ -64,6 +64,13 @@ def decode_call(lib, c=None, w=None, k=None, q=FAKE, lens=FAKE, max_len=4096, ou
     return lib.mla_decode(ctypes.byref(c), ctypes.byref(w), ctypes.byref(k), q, lens, max_len, out, ws, ws_bytes, None)
 
 
+def test_shared_rope_heads_accepted(lib):
+    # 0 (one key head per query head) and every divisor of n_heads pass validation: the call then fails
+    # only on the deliberately short workspace
+    for nrh in (0, 1, 2, 8, 16, 32):
+        assert decode_call(lib, c=cfg(rope_heads=nrh), ws_bytes=16) == WORKSPACE, nrh
+
+
 def test_workspace_sizes(lib):
     c = cfg()
     n = lib.mla_decode_workspace_bytes(ctypes.byref(c), 32, 4096)
@@ -93,6 +100,9 @@ def test_workspace_sizes(lib):
         (dict(cache_fmt=3, dtype=0), UNSUPPORTED),
         (dict(cache_fmt=3, d_kv=48), UNSUPPORTED),
         (dict(cache_fmt=4), INVALID),
+        (dict(rope_heads=-1), INVALID),
+        (dict(rope_heads=5), INVALID),  # not a divisor of the 32 query heads
+        (dict(rope_heads=64), INVALID),
     ],
 )
 def test_decode_rejects_bad_config(lib, kw, expected):

@@ -13,7 +13,8 @@ import synth
 from synth import CONFIGS, scaled
 
 from parity_lib import (assert_close, assert_finite, check_int4_cache, check_rows, converted_layer, decode_query,
-                        fill_cache_per_sequence, log, max_abs, oracle_cache, rel_l2, shape_of, torch_dtype)
+                        fill_cache_per_sequence, log, max_abs, oracle_cache, rel_l2, rope_key_rows, shape_of,
+                        torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,15 +24,16 @@ def _to_np(t):
 
 
 def run_decode_case(cfg, lens, t_max, sample=None, check_cache=True, repeat_bitwise=True, variant=("2-norm", "joint"),
-                    layer=None):
+                    layer=None, rope_heads=0):
     from mla_latent_kv_cache_amd import LatentCache, decode, pack_weights
 
     log(f"[decode] {cfg.name} family={cfg.family} d_kv={cfg.d_kv} r={cfg.r_pairs} fmt={cfg.cache_fmt} "
-        f"B={len(lens)} lens={list(lens)[:8]} t_max={t_max} conversion={variant if layer is None else 'given'}")
+        f"B={len(lens)} lens={list(lens)[:8]} t_max={t_max} conversion={variant if layer is None else 'given'} "
+        f"rope_heads={rope_heads or cfg.n_heads}")
     B = len(lens)
     if layer is None:
         layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype, *variant)
-    shape = shape_of(cfg)
+    shape = shape_of(cfg, rope_heads)
     w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
     cache = LatentCache.allocate(shape, B, t_max, fill=float("nan"))
     if cache.ckv_scale is not None:
@@ -82,7 +84,7 @@ def run_decode_case(cfg, lens, t_max, sample=None, check_cache=True, repeat_bitw
             if check_cache:
                 check_rows(cfg, cache.ckv[b, :L], c, f"c_kv b={b}")
         if check_cache and cfg.r_pairs > 0:
-            check_rows(cfg, cache.krope[b, :L], kr, f"k_rope b={b}")
+            check_rows(cfg, cache.krope[b, :L], rope_key_rows(kr, cfg.n_heads, rope_heads), f"k_rope b={b}")
         ref = oracle.decode_ref(q[b], c_used, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head, cfg.theta)
         r, a = assert_close(got[b], ref, cfg.dtype, f"decode out b={b} L={L}")
         err2 += float(np.sum((got[b] - ref) ** 2))

@@ -13,8 +13,8 @@ import oracle
 import synth
 from synth import CONFIGS, scaled
 
-from parity_lib import (assert_close, check_int4_cache, check_rows, converted_layer, decode_query, log, oracle_cache, shape_of,
-                        torch_dtype)
+from parity_lib import (assert_close, check_int4_cache, check_rows, converted_layer, decode_query, log, oracle_cache,
+                        rope_key_rows, shape_of, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -73,19 +73,23 @@ CASES = {
 def test_paged_append_and_decode(case):
     """Pool rows through the page table against the oracle's cache; decode equal to a contiguous cache bit for bit
     and to the oracle within tolerance."""
+    run_paged_case(*CASES[case], seed=list(CASES).index(case) + 1, name=case)
+
+
+def run_paged_case(base, family, d_kv, r, prompts, seed, name="", layer=None, rope_heads=0):
     from mla_latent_kv_cache_amd import LatentCache, decode, pack_weights
 
-    base, family, d_kv, r, prompts = CASES[case]
     cfg = scaled(base, family=family, d_kv=d_kv, r_pairs=r, batch=len(prompts), context=0, ctx_range=None)
     steps, P = 2, 64
     lens = [p + steps for p in prompts]
     pps = (max(lens) + P - 1) // P
     t_max = pps * P
-    log(f"[paged] {case} prompts={prompts} page={P} pages/seq={pps}")
-    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
-    shape = shape_of(cfg)
+    log(f"[paged] {name} prompts={prompts} page={P} pages/seq={pps} rope_heads={rope_heads or cfg.n_heads}")
+    if layer is None:
+        layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    shape = shape_of(cfg, rope_heads)
     w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
-    table, n_pages = _table(len(prompts), pps, 7, seed=list(CASES).index(case) + 1)
+    table, n_pages = _table(len(prompts), pps, 7, seed=seed)
     paged = LatentCache.allocate_paged(shape, table, P, n_pages, fill=float("nan"))
     contig = LatentCache.allocate(shape, len(prompts), t_max, fill=float("nan"))
     xs = [synth.context_x(cfg, b, L) for b, L in enumerate(lens)]
@@ -102,7 +106,8 @@ def test_paged_append_and_decode(case):
     for b, L in enumerate(lens):
         c, kr = oracle_cache(cfg, layer, xs[b])
         ckv, sc, krg = _pool_rows(paged, b, L)
-        check_rows(cfg, krg.reshape(L, cfg.n_heads, -1), kr, f"pool k_rope b={b}")
+        check_rows(cfg, krg.reshape(L, shape.n_rope_heads, -1), rope_key_rows(kr, cfg.n_heads, rope_heads).reshape(
+            L, shape.n_rope_heads, -1), f"pool k_rope b={b}")
         if cfg.cache_fmt == "int4_g32":
             check_int4_cache(c, oracle.unpack_nibbles(ckv), sc, f"pool int4 b={b}")
             oc, osc = oracle.quantize_int4_g32(c.astype(np.float32))

@@ -14,22 +14,23 @@ import oracle
 import synth
 from synth import CONFIGS, scaled
 
-from parity_lib import assert_close, assert_finite, check_rows, converted_layer, log, shape_of, torch_dtype
+from parity_lib import (assert_close, assert_finite, check_rows, converted_layer, log, rope_key_rows, shape_of,
+                        torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill_case(cfg, S, B, rows=None, full_b=None, variant=("2-norm", "joint"), layer=None):
+def run_prefill_case(cfg, S, B, rows=None, full_b=None, variant=("2-norm", "joint"), layer=None, rope_heads=0):
     """Append + prefill of B seeded prompts of S tokens.  Sequences in full_b (all when None) are compared on
     every query row; the others on `rows`.  The appended cache rows of every sequence are compared too."""
     from mla_latent_kv_cache_amd import LatentCache, append, pack_weights, prefill
 
     log(f"[prefill] family={cfg.family} r={cfg.r_pairs} d_kv={cfg.d_kv} B={B} S={S} "
         f"every row of {'all' if full_b is None else full_b}, else rows {rows} "
-        f"conversion={variant if layer is None else 'given'}")
+        f"conversion={variant if layer is None else 'given'} rope_heads={rope_heads or cfg.n_heads}")
     if layer is None:
         layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype, *variant)
-    shape = shape_of(cfg)
+    shape = shape_of(cfg, rope_heads)
     t_max = S + 3
     w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
     cache = LatentCache.allocate(shape, B, t_max, fill=float("nan"))
@@ -50,7 +51,7 @@ def run_prefill_case(cfg, S, B, rows=None, full_b=None, variant=("2-norm", "join
         c, kr = oracle.append_ref(xs[b], layer["w_dkv"], layer["w_krope"], layer["pair_idx"], np.arange(S),
                                   cfg.d_head, cfg.theta)
         check_rows(cfg, cache.ckv[b, :S], c, f"c_kv b={b}")
-        check_rows(cfg, cache.krope[b, :S], kr, f"k_rope b={b}")
+        check_rows(cfg, cache.krope[b, :S], rope_key_rows(kr, cfg.n_heads, rope_heads), f"k_rope b={b}")
         rr = np.arange(S) if (full_b is None or b in full_b or rows is None) else np.asarray(rows)
         ref = oracle.prefill_ref(qs[b], c, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head,
                                  cfg.theta, rows=rr)

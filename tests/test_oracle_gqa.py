@@ -166,3 +166,32 @@ def test_gqa_reference_and_rows_at_full_rank():
     row = ablation.gqa_rows(wq, wk, wv, xc, x, n_h, n_kv, d_h, 1, d)[0]
     assert row["kv_fit_err"] < 1e-12
     assert row["end_to_end_err"] == pytest.approx(row["partial_rope_err"], rel=1e-8, abs=1e-12)
+
+
+def test_compact_rope_conversion_and_packing():
+    """The converter's compact output keeps the RoPE part per KV head (the oracle's group pairs and key columns),
+    and pack_weights forms the same compact device weights from the per-query-head expansion; a layer whose
+    query heads of one key head differ is refused."""
+    from mla_latent_kv_cache_amd import LayerShape, pack_weights
+
+    wq, wk, wv, xc = synth.gqa_layer_weights("gqa_mid")
+    ref = oracle.convert_gqa_layer(wq, wk, wv, xc, 32, 8, 128, 4, 256)
+    comp = convert_layer(wq, wk, wv, xc, 32, 128, 4, 256, n_kv_heads=8, compact_rope=True)
+    np.testing.assert_array_equal(comp["pair_idx"], ref["group_pair_idx"])
+    assert comp["w_krope"].shape == (1024, 8 * 8)
+    np.testing.assert_array_equal(comp["w_krope"].reshape(1024, 8, 8), ref["w_krope"].reshape(1024, 32, 8)[:, ::4])
+    shape = LayerShape(1024, 32, 128, 4, 256, "f32", rope_heads=8)
+    a = pack_weights(shape, comp, rope_len=16, device="cpu")
+    b = pack_weights(shape, ref, rope_len=16, device="cpu")
+    assert tuple(a.pair_idx.shape) == (8, 4) and tuple(a.w_krope.shape) == (64, 1024)
+    assert torch.equal(a.pair_idx, b.pair_idx) and torch.equal(a.w_krope, b.w_krope)
+    # 16 key heads (pairs of query heads) from the same expansion
+    b16 = pack_weights(LayerShape(1024, 32, 128, 4, 256, "f32", rope_heads=16), ref, rope_len=16, device="cpu")
+    assert torch.equal(b16.pair_idx[::2], a.pair_idx)
+    bad = dict(ref)
+    bad["pair_idx"] = ref["pair_idx"].copy()
+    bad["pair_idx"][1] = (bad["pair_idx"][1] + 1) % 64
+    with pytest.raises(ValueError):
+        pack_weights(shape, bad, rope_len=16, device="cpu")
+    with pytest.raises(ValueError):  # per-key-head tables of the wrong count
+        pack_weights(LayerShape(1024, 32, 128, 4, 256, "f32", rope_heads=4), comp, rope_len=16, device="cpu")
