@@ -219,16 +219,24 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
         const int h = rel / (R2 > 0 ? R2 : 1);
         const int jj = (rel - h * R2) >> 1, comp = rel & 1;
         const bool colok = rel < NR;
-        const int p = colok ? load_pair(a.pair_idx, h * r + jj, half) : 0;
+        const int p = load_pair(a.pair_idx, colok ? h * r + jj : 0, half);
+        // the 16 rows' table entries in one round of loads (clamped in-bounds indices, no branch)
+        float cst[16], snt[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int ml = wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const size_t t = (size_t)(m0 + ml < M ? poss[ml] : 0) * half + p;
+          cst[e] = a.rope_cos[t];
+          snt[e] = a.rope_sin[t];
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           float v = acc[i][j][e];
           float partner = shfl_xor(v, 1);
           const int ml = wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
           if (m0 + ml < M && colok) {
-            const int pos = poss[ml];
             const size_t row = (size_t)rows[ml];
-            float cs = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
+            const float cs = cst[e], sn = snt[e];
             float x0 = comp ? partner : v, x1 = comp ? v : partner;
             float o = comp ? (x0 * sn + x1 * cs) : (x0 * cs - x1 * sn);
             ((bf16*)a.krope)[row * NR + rel] = (bf16)o;
@@ -288,14 +296,23 @@ __device__ __forceinline__ void append_gemm_block(const AppendArgs& a, const f32
     const int h = rel / (R2 > 0 ? R2 : 1);
     const int jj = (rel - h * R2) >> 1, comp = rel & 1;
     const bool colok = rel < NR;
-    const int p = colok ? load_pair(a.pair_idx, h * r + jj, half) : 0;
+    const int p = load_pair(a.pair_idx, colok ? h * r + jj : 0, half);
+    // the 16 rows' table entries in one round of loads (clamped in-bounds indices, no branch: a load
+    // under the store's condition would be waited for before the next one is issued)
+    float cst[16], snt[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const size_t t = (size_t)(m0 + ml < M ? poss[ml] : 0) * half + p;
+      cst[e] = a.rope_cos[t];
+      snt[e] = a.rope_sin[t];
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float partner = shfl_xor(v[e], 1);
       const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
       if (m0 + ml < M && colok) {
-        const int pos = poss[ml];
-        const float cs = a.rope_cos[(size_t)pos * half + p], sn = a.rope_sin[(size_t)pos * half + p];
+        const float cs = cst[e], sn = snt[e];
         const float x0 = comp ? partner : v[e], x1 = comp ? v[e] : partner;
         const float o = comp ? (x0 * sn + x1 * cs) : (x0 * cs - x1 * sn);
         ((bf16*)a.krope)[(size_t)rows[ml] * NR + rel] = (bf16)o;
