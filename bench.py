@@ -23,13 +23,14 @@ The cpu_baseline object times the oracle (plain fp64 numpy; the library never us
 its conversion of the layer, then the cache fill + unabsorbed decode of whole sequences of the same workload
 (a bounded sample), each timed apart.  Secondary workloads (long-context variable-length decode, int4-latent
 decode, 2-bit- and int4-latent decode with a 128-row bf16 window, the headline decode on a paged cache of
-64-token pages in random order, a 4-query multi-query decode, causal prefill) are reported in `secondary`.
+64-token pages in random order, a 4-query multi-query decode, a grouped-query source whose RoPE keys are
+stored once per KV head, causal prefill) are reported in `secondary`.
 
 `roofline.traffic` is the HBM traffic of one launch of that kernel from FETCH_SIZE / WRITE_SIZE counter
 runs (profiles/pmc_traffic.json, scaled by the counters of a plain copy of known size, see
 --copy-calibration); it is null when those counters were taken on different decode sources.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only bw,c1,c3,c4,c5,c8,c6,c7,c2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only bw,c1,c3,c4,c5,c8,c6,c7,c9,c2] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -48,7 +49,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode latent-cache GB/s (% of HBM peak); prefill MFMA TFLOP/s"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure (no sparsity)
-DOMINANT_KERNEL = "decode_attn_dma<128, 8, 3, false>"
+DOMINANT_KERNEL = "decode_attn_dma<128, 8, 3, false, false>"
 FUSED_KEY = DOMINANT_KERNEL + " in mla_decode_step"  # the same kernel launched with the append's reduction
 
 
@@ -61,7 +62,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="bw,c1,c3,c4,c5,c8,c6,c7,c2")
+    ap.add_argument("--only", default="bw,c1,c3,c4,c5,c8,c6,c7,c9,c2")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--replays", type=int, default=50, help="graph replays the median step time is taken over (>= 50 "
                                                              "for a reported figure; fewer for profiler runs)")
@@ -177,15 +178,31 @@ def converted(family, r, d_kv):
     return conv
 
 
-def make_decode_workload(cfg, conv, lens, copies, seed, page_size=0):
+def converted_gqa(family, r, d_kv):
+    """The library converter on a seeded grouped-query layer (synth.GQA_FAMILIES), RoPE part kept per KV head."""
+    import synth
+    from mla_latent_kv_cache_amd import convert_layer
+
+    d, n_h, n_kv, d_h, _ = synth.GQA_FAMILIES[family]
+    wq, wk, wv, xc = synth.gqa_layer_weights(family)
+    t = time.time()
+    conv = convert_layer(wq, wk, wv, xc, n_h, d_h, r, d_kv, n_kv_heads=n_kv, compact_rope=True)
+    log(f"[bench] converted {family} (GQA, {n_kv} KV heads) r={r} d_kv={d_kv} in {time.time() - t:.1f}s")
+    conv["w_q"] = wq
+    return conv
+
+
+def make_decode_workload(cfg, conv, lens, copies, seed, page_size=0, rope_heads=0):
     """Weights, `copies` filled caches (through mla_cache_append), the step's new-token activations, queries
     and one BoundDecode per copy.  Activations are seeded N(0,1) generated on the device.  page_size > 0:
-    paged caches whose pages are a random permutation of the pool."""
+    paged caches whose pages are a random permutation of the pool; rope_heads > 0: RoPE keys stored per key
+    head (LayerShape.rope_heads)."""
     import torch
 
     from mla_latent_kv_cache_amd import BoundDecode, LatentCache, LayerShape, append, pack_weights
 
-    shape = LayerShape(cfg.d_model, cfg.n_heads, cfg.d_head, cfg.r_pairs, cfg.d_kv, cfg.dtype, cfg.cache_fmt)
+    shape = LayerShape(cfg.d_model, cfg.n_heads, cfg.d_head, cfg.r_pairs, cfg.d_kv, cfg.dtype, cfg.cache_fmt,
+                       rope_heads=rope_heads)
     B = len(lens)
     t_max = int(max(lens))
     w = pack_weights(shape, conv, rope_len=t_max, theta=cfg.theta)
@@ -555,7 +572,7 @@ def main():
         wl6 = make_decode_workload(cfg1, conv_main, synth.seq_lens(cfg1), args.copies, seed=1006, page_size=64)
         r6 = decode_result("llama_bf16_decode_paged64", cfg1, wl6, args.steps, args.warmup)
         r6.update(hbm_frac=r6["kernel_gbs"] / HBM_PEAK_GBS, page_size=64,
-                  kernel="decode_attn_dma<128, 8, 3, true>")
+                  kernel="decode_attn_dma<128, 8, 3, true, false>")
         secondary["llama_bf16_decode_paged64"] = r6
         del wl6
         torch.cuda.empty_cache()
@@ -566,7 +583,9 @@ def main():
         lens3 = synth.seq_lens(cfg3)
         wl3 = make_decode_workload(cfg3, conv3, lens3, args.copies, seed=1003)
         r3 = decode_result("llama_bf16_longctx_decode", cfg3, wl3, args.steps, args.warmup)
-        r3.update(lens=[int(v) for v in lens3], hbm_frac=r3["kernel_gbs"] / HBM_PEAK_GBS)
+        k3 = "decode_attn_wave<256, 4, 0, 3, false>"
+        r3.update(lens=[int(v) for v in lens3], hbm_frac=r3["kernel_gbs"] / HBM_PEAK_GBS, kernel=k3,
+                  traffic=measured_traffic(k3 + " in mla_decode_step"), traffic_alone=measured_traffic(k3))
         secondary["llama_bf16_longctx_decode"] = r3
         del wl3, conv3
         torch.cuda.empty_cache()
@@ -574,7 +593,9 @@ def main():
         cfg4 = C[4]
         wl4 = make_decode_workload(cfg4, conv_main, synth.seq_lens(cfg4), args.copies, seed=1004)
         r4 = decode_result("llama_int4_decode", cfg4, wl4, args.steps, args.warmup)
-        r4.update(hbm_frac=r4["kernel_gbs"] / HBM_PEAK_GBS)
+        k4 = "decode_attn_mfma<128, 8, 1, false>"
+        r4.update(hbm_frac=r4["kernel_gbs"] / HBM_PEAK_GBS, kernel=k4,
+                  traffic=measured_traffic(k4 + " in mla_decode_step"), traffic_alone=measured_traffic(k4))
         secondary["llama_int4_decode"] = r4
         del wl4
         torch.cuda.empty_cache()
@@ -600,6 +621,21 @@ def main():
                   kernel="decode_attn_mfma<128, 8, 3>")
         secondary["llama_int4w_decode"] = r8
         del wl8
+        torch.cuda.empty_cache()
+
+    if "c9" in only:
+        # a grouped-query source (Llama-3-8B-shaped attention: 32 query heads, 8 KV heads) converted at r 4,
+        # d_kv 512, its RoPE keys stored once per KV head: 1152 cache bytes per token instead of 1536; the
+        # batch and context of the main workload
+        cfg9 = synth.scaled(C[1], name="llama3_gqa_compact_decode")
+        conv9 = converted_gqa("llama3", 4, 512)
+        wl9 = make_decode_workload(cfg9, conv9, synth.seq_lens(cfg9), args.copies, seed=1009, rope_heads=8)
+        r9 = decode_result("llama3_gqa_compact_decode", cfg9, wl9, args.steps, args.warmup)
+        k9 = "decode_attn_dma<128, 8, 3, false, true>"
+        r9.update(hbm_frac=r9["kernel_gbs"] / HBM_PEAK_GBS, rope_heads=8, bytes_per_token=wl9["bytes_per_row"],
+                  kernel=k9, traffic=measured_traffic(k9 + " in mla_decode_step"), traffic_alone=measured_traffic(k9))
+        secondary["llama3_gqa_compact_decode"] = r9
+        del wl9, conv9
         torch.cuda.empty_cache()
 
     if "c2" in only:

@@ -82,7 +82,8 @@ typedef struct {
   int32_t rope_heads;/* RoPE key heads n_rh: 0 (= n_heads, keys per query head) or a divisor of
                         n_heads; query head h then uses RoPE key head h / (n_heads / n_rh), the
                         layout of a layer converted from a grouped-query source (one key head per
-                        KV head, shared by its query heads)                                   */
+                        KV head, shared by its query heads; Paper-Notes page, 关键发现: GQA models
+                        migrate as MHA ones do).  Else MLA_ERR_INVALID_ARG                     */
 } mla_config;
 
 /* Converted weights (read-only, device).  n_rh = rope_heads (n_h when 0), g(h) = h / (n_h / n_rh) the
