@@ -24,13 +24,14 @@ its conversion of the layer, then the cache fill + unabsorbed decode of whole se
 (a bounded sample), each timed apart.  Secondary workloads (long-context variable-length decode, int4-latent
 decode, 2-bit- and int4-latent decode with a 128-row bf16 window, the headline decode on a paged cache of
 64-token pages in random order, a 4-query multi-query decode, a grouped-query source whose RoPE keys are
-stored once per KV head, causal prefill) are reported in `secondary`.
+stored once per KV head, the headline layer at the shape of the pages' LongBench runs (batch 16 x 2048
+tokens), causal prefill) are reported in `secondary`.
 
 `roofline.traffic` is the HBM traffic of one launch of that kernel from FETCH_SIZE / WRITE_SIZE counter
 runs (profiles/pmc_traffic.json, scaled by the counters of a plain copy of known size, see
 --copy-calibration); it is null when those counters were taken on different decode sources.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only bw,c1,c3,c4,c5,c8,c6,c7,c9,c2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only bw,c1,c3,c4,c5,c8,c6,c7,c9,c10,c2] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -62,7 +63,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="bw,c1,c3,c4,c5,c8,c6,c7,c9,c2")
+    ap.add_argument("--only", default="bw,c1,c3,c4,c5,c8,c6,c7,c9,c10,c2")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--replays", type=int, default=50, help="graph replays the median step time is taken over (>= 50 "
                                                              "for a reported figure; fewer for profiler runs)")
@@ -119,9 +120,10 @@ def copy_calibration():
 
 
 def stream_read_ceiling(reps=10, nbytes=2 << 30):
-    """The best rate of the in-tree streaming-read kernel (libmla_bandwidth.so: 16-byte loads, grid-stride,
-    nothing written) over launch shapes, reading a 2 GiB buffer (far past the 256 MB last-level cache):
-    the practical ceiling of a kernel that reads HBM once, reported beside the vendor peak."""
+    """The best rate of the in-tree streaming-read kernels (libmla_bandwidth.so: 16-byte loads, grid-stride, or
+    1 KB direct-to-LDS requests with the non-temporal hint; nothing written) over launch shapes, reading a 2 GiB
+    buffer (far past the 256 MB last-level cache): the practical ceiling of a kernel that reads HBM once,
+    reported beside the vendor peak."""
     import ctypes
 
     import torch
@@ -132,13 +134,21 @@ def stream_read_ceiling(reps=10, nbytes=2 << 30):
     lib.mla_bw_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_void_p]
     lib.mla_bw_stream_read.restype = ctypes.c_int
+    lib.mla_bw_stream_dma.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p]
+    lib.mla_bw_stream_dma.restype = ctypes.c_int
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_()
-    shapes = [(256 * k, u, nt) for k in (4, 8, 16, 32) for u in (2, 4, 8) for nt in (0, 1)]
+    shapes = [(256 * k, u, nt) for k in (1, 4, 8, 16, 32) for u in (2, 4, 8) for nt in (0, 1)]
+    # LDS DMA with the non-temporal hint (the decode kernels' load path): one workgroup of 4 waves per CU
+    shapes += [(256, f, "dma") for f in (4, 8, 16)]
     sink = torch.zeros(max(b for b, _, _ in shapes), dtype=torch.int32, device="cuda")
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def launch(b, u, nt):
-        rc = lib.mla_bw_stream_read(src.data_ptr(), nbytes // 16, sink.data_ptr(), b, u, nt, stream)
+        if nt == "dma":
+            rc = lib.mla_bw_stream_dma(src.data_ptr(), nbytes // 1024, sink.data_ptr(), b, u, stream)
+        else:
+            rc = lib.mla_bw_stream_read(src.data_ptr(), nbytes // 16, sink.data_ptr(), b, u, nt, stream)
         if rc != 0:
             raise RuntimeError(f"mla_bw_stream_read failed ({rc})")
 
@@ -154,13 +164,14 @@ def stream_read_ceiling(reps=10, nbytes=2 << 30):
         torch.cuda.synchronize()
         gbs = nbytes * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
         if gbs > best[0]:
-            best = (gbs, dict(workgroups=b, loads_in_flight=u, nontemporal=bool(nt)))
+            best = (gbs, dict(workgroups=b, loads_in_flight=u, nontemporal=True, lds_dma=True) if nt == "dma" else
+                    dict(workgroups=b, loads_in_flight=u, nontemporal=bool(nt), lds_dma=False))
     del src, sink
     torch.cuda.empty_cache()
     log(f"[bench] streaming-read ceiling: {best[0]:.0f} GB/s ({100 * best[0] / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f}) "
         f"at {best[1]}")
     return {"gbs": round(best[0], 1), "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4), "bytes": nbytes,
-            "launch": best[1], "kernel": "stream_read (libmla_bandwidth.so)"}
+            "launch": best[1], "kernel": "stream_dma (libmla_bandwidth.so)" if best[1].get("lds_dma") else "stream_read (libmla_bandwidth.so)"}
 
 
 # ---------------------------------------------------------------- workloads
@@ -621,6 +632,17 @@ def main():
                   kernel="decode_attn_mfma<128, 8, 3>")
         secondary["llama_int4w_decode"] = r8
         del wl8
+        torch.cuda.empty_cache()
+
+    if "c10" in only:
+        # the shape of the pages' LongBench evaluation (batch 16, 2048 tokens per sequence) on the main
+        # workload's layer: seeded synthetic inputs stand in for the benchmark's items
+        cfg10 = synth.scaled(C[1], name="longbench_shape_decode", batch=16, context=2048)
+        wl10 = make_decode_workload(cfg10, conv_main, synth.seq_lens(cfg10), args.copies, seed=1010)
+        r10 = decode_result("longbench_shape_decode", cfg10, wl10, args.steps, args.warmup)
+        r10.update(hbm_frac=r10["kernel_gbs"] / HBM_PEAK_GBS, batch=16, context=2048)
+        secondary["longbench_shape_decode"] = r10
+        del wl10
         torch.cuda.empty_cache()
 
     if "c9" in only:

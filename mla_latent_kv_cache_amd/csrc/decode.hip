@@ -647,7 +647,8 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   // RoPE key rows: NRH key heads of R2 dims (NRH = 32, or fewer when query heads share keys)
   const int NRH = a.s.rope_heads, KRW = NRH * R2;
 
-  // ---- register prefetch, two tiles deep: this wave's latent slice and its share of the RoPE keys
+  // ---- register prefetch, two tiles deep: this wave's latent slice and its share of the RoPE keys (loads
+  // with the non-temporal hint: each cache row is read once per query)
   // 16-byte chunks per row of the wave's slice: 8 bf16, 32 int4 or 64 2-bit latents each
   constexpr int CPR = (CODEC == 0) ? DW / 8 : (CODEC == 1 ? DW / 32 : DW / 64);
   constexpr int CCH = 32 * CPR / 64;                  // chunks per lane
@@ -684,12 +685,12 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
       if constexpr (!WIN) {
 #pragma unroll
         for (int it = 0; it < CCH; ++it) {
-          creg[B][it] = *(const u32x4*)(cb + coff[it]);
+          creg[B][it] = __builtin_nontemporal_load((const u32x4*)(cb + coff[it]));
           if constexpr (CODEC != 0) sreg[B][it] = *(const meta_t*)(sb + soff[it]);
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kreg[B][i] = *(const kv_t*)(kb + i * KRW * 2);
+      for (int i = 0; i < 4; ++i) kreg[B][i] = __builtin_nontemporal_load((const kv_t*)(kb + i * KRW * 2));
       return;
     }
     if constexpr (!WIN) {
@@ -699,14 +700,14 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
         const int tok = min(tt + row, t1 - 1);  // rows past the sequence repeat its last row (masked below)
         const char* cb = (const char*)a.ckv + (row0 + tok - tt + tb) * RBY;
         const char* sb = (const char*)a.ckv_scale + (row0 + tok - tt + tb) * (D / 32) * MBY;
-        creg[B][it] = *(const u32x4*)(cb + coff[it] - row * RBY);
+        creg[B][it] = __builtin_nontemporal_load((const u32x4*)(cb + coff[it] - row * RBY));
         if constexpr (CODEC != 0) sreg[B][it] = *(const meta_t*)(sb + soff[it] - MBY * row * (D / 32));
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int tok = min(tt + xt0 + i, t1 - 1);
-      kreg[B][i] = *(const kv_t*)(krb + row0 * KRW + ((size_t)(tok - tt + tb) * NRH + a.s.rope_head(xh)) * R2);
+      kreg[B][i] = __builtin_nontemporal_load((const kv_t*)(krb + row0 * KRW + ((size_t)(tok - tt + tb) * NRH + a.s.rope_head(xh)) * R2));
     }
   };
   auto stage_tile = [&](auto bsel) {
@@ -1009,13 +1010,13 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
     } else if (tt + 32 <= t1) {
       const char* cb = cb0 + (size_t)tb * (D * 2);
 #pragma unroll
-      for (int j = 0; j < NC; ++j) dma16(cb, coff[j], c_lds[SL] + 1024 * j);
+      for (int j = 0; j < NC; ++j) dma16_nt(cb, coff[j], c_lds[SL] + 1024 * j);
     } else {  // last, partial tile: rows past the sequence repeat its last row (masked later)
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int off = 1024 * j + 16 * lane, row = off / RB;
         const int tok = min(tt + row, t1 - 1) - tt + tb;
-        dma16(cb0, (uint32_t)(tok * (D * 2) + 16 * swz<DW>(row, (off % RB) / 16)), c_lds[SL] + 1024 * j);
+        dma16_nt(cb0, (uint32_t)(tok * (D * 2) + 16 * swz<DW>(row, (off % RB) / 16)), c_lds[SL] + 1024 * j);
       }
     }
     // the wave's RoPE rows 8w .. 8w+7 of the tile are one contiguous block
@@ -1023,13 +1024,13 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
     } else if (tt + 8 * wu + 8 <= t1) {
       const char* kb = (PG ? kt + 8 * wu * RRB : kbase) + (size_t)tb * RRB;
 #pragma unroll
-      for (int j = 0; j < NK; ++j) dma16(kb, (uint32_t)(1024 * j + 16 * lane), k_lds[SL] + KDST + 1024 * j);
+      for (int j = 0; j < NK; ++j) dma16_nt(kb, (uint32_t)(1024 * j + 16 * lane), k_lds[SL] + KDST + 1024 * j);
     } else {
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
         const int off = 1024 * j + 16 * lane, tk = off / RRB, within = off % RRB;
         const int tok = min(tt + 8 * wu + tk, t1 - 1) - tt + tb;  // row relative to the base, >= 0
-        dma16(kt, (uint32_t)(tok * RRB + within), k_lds[SL] + KDST + 1024 * j);
+        dma16_nt(kt, (uint32_t)(tok * RRB + within), k_lds[SL] + KDST + 1024 * j);
       }
     }
   };
@@ -1339,7 +1340,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a, FuseArg
     for (int i = 0; i < W::NL; ++i) {
       const int off = 1024 * i + 16 * lane, row = off / W::RB, pos = (off % W::RB) / 16;
       const int tok = min(tt + row, last);
-      dma16(lat, (uint32_t)((tok - tt) * W::RB + 16 * (pos ^ (row & SWM))), base + 1024 * i);
+      dma16_nt(lat, (uint32_t)((tok - tt) * W::RB + 16 * (pos ^ (row & SWM))), base + 1024 * i);
     }
 #pragma unroll
     for (int i = 0; i < W::NSC; ++i) {
@@ -1352,7 +1353,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a, FuseArg
     for (int i = 0; i < W::NK; ++i) {
       const int off = 1024 * i + 16 * lane, row = off / W::KRB, within = off % W::KRB;
       const int tok = min(tt + row, last);
-      dma16(kro, (uint32_t)((tok - tt) * W::KRB + within), base + W::LB + W::SB + 1024 * i);
+      dma16_nt(kro, (uint32_t)((tok - tt) * W::KRB + within), base + W::LB + W::SB + 1024 * i);
     }
   };
   constexpr int PF = NSLOT - 1;  // tiles in flight ahead of the one being computed
