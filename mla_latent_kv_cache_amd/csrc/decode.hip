@@ -522,7 +522,7 @@ __global__ __launch_bounds__(256) void decode_attn_generic(DecodeArgs a) {
 // statistics: (m, l, A) per head.
 template <int DW>
 __device__ __forceinline__ void store_partial(const DecodeArgs& a, const f32x16 (&oacc)[DW / 32], float* red,
-                                              float m_run, float l_run, bool write_ml = true) {
+                                              char* stage, float m_run, float l_run, bool write_ml = true) {
   constexpr int NB = DW / 32, D = 4 * DW;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hb = lane >> 5, h = lane & 31;
   float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * MLS;
@@ -540,16 +540,28 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, const f32x16 
     A = fmaxf(fmaxf(red[h], red[32 + h]), fmaxf(red[64 + h], red[96 + h]));
     const float inv = A > 0.f ? 1.f / A : 0.f;
     _Float16* po = (_Float16*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * 32 * D;
+    // through the wave's own staging area ([32 heads][DW] fp16, 16-byte chunks XOR-swizzled by row), so that
+    // the rows leave as 16-byte stores, DW * 2 contiguous bytes per head, instead of 8-byte pieces 2 * D
+    // bytes apart
+    constexpr int CH = DW / 8;  // 16-byte chunks per row
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int k = w * DW + blk * 32 + 8 * e4 + 4 * hb;
+        const int kl = blk * 32 + 8 * e4 + 4 * hb;
         f16x4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = (_Float16)(oacc[blk][4 * e4 + i] * inv);
-        *(f16x4*)&po[(size_t)h * D + k] = v;
+        *(f16x4*)(stage + h * (DW * 2) + 16 * ((kl >> 3) ^ (h & (CH - 1))) + 2 * (kl & 7)) = v;
       }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 32 * CH / 64; ++i) {
+      const int c = i * 64 + lane, row = c / CH, ch = c % CH;
+      const u32x4 v = *(const u32x4*)(stage + row * (DW * 2) + 16 * (ch ^ (row & (CH - 1))));
+      *(u32x4*)&po[(size_t)row * D + w * DW + 8 * ch] = v;
+    }
   } else {
     float* po = (float*)(a.ws + a.plan.off_o) + (size_t)blockIdx.x * 32 * D;
 #pragma unroll
@@ -887,7 +899,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   l_run += shfl_xor(l_run, 8);
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
-  store_partial<DW>(a, oacc, (float*)sbuf, m_run, l_run, false);
+  store_partial<DW>(a, oacc, (float*)sbuf, (char*)cbuf[w], m_run, l_run, false);  // cbuf[w]: this wave's own
   if (lane < 8) {
     float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * MLS;
     pml[MLS * xh] = m_run;
@@ -1219,7 +1231,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
   l_run += shfl_xor(l_run, 8);
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
-  store_partial<DW>(a, oacc, (float*)sbuf, m_run, l_run, false);
+  // (the wave's latent slice of slot 0 is its own and free: its last DMA has landed, its last PV is done)
+  store_partial<DW>(a, oacc, (float*)sbuf, cs0 + wu * CSL, m_run, l_run, false);
   if (lane < 8) {
     float* pml = (float*)(a.ws + a.plan.off_ml) + (size_t)blockIdx.x * 32 * MLS;
     pml[MLS * xh] = m_run;
@@ -1609,7 +1622,11 @@ __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a, FuseArg
   __syncthreads();
   // O in rounds of 128 columns: every wave stores its raw accumulators (straight from the accumulation
   // registers), then wave w forms columns [32 w, 32 w + 32) as the weighted sum over the four waves
-  float* ob = (float*)(lds + 2048);  // [4 waves][32 heads][128 columns]
+  // [4 waves][32 heads][128 columns], rows padded to OBP floats: the 32 heads a store instruction writes
+  // then fall on different banks (a 128-float pitch put them all on the same ones)
+  constexpr int OBP = 132;
+  static_assert(2048 + 4 * 32 * OBP * 4 <= W::LDS_BYTES, "merge buffer");
+  float* ob = (float*)(lds + 2048);
   const int h = lane & 31, hb = lane >> 5;
   // lane's heads: 8 it + lane / 8 (it = 0..3), 4 columns 32 w + 4 (lane % 8) of every 128-column round
   f32x4 vr[D / 128][4];
@@ -1621,7 +1638,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a, FuseArg
       for (int e4 = 0; e4 < 4; ++e4) {
         const f32x16& o = oacc[4 * r + gg];
         const int col = 32 * gg + 8 * e4 + 4 * hb;
-        *(f32x4*)&ob[(w * 32 + h) * 128 + col] = f32x4{o[4 * e4], o[4 * e4 + 1], o[4 * e4 + 2], o[4 * e4 + 3]};
+        *(f32x4*)&ob[(w * 32 + h) * OBP + col] = f32x4{o[4 * e4], o[4 * e4 + 1], o[4 * e4 + 2], o[4 * e4 + 3]};
       }
     __syncthreads();
 #pragma unroll
@@ -1629,7 +1646,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a, FuseArg
       const int hh = 8 * it + (lane >> 3), col = 32 * w + 4 * (lane & 7);
       f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) v += wt[ww * 32 + hh] * *(const f32x4*)&ob[(ww * 32 + hh) * 128 + col];
+      for (int ww = 0; ww < 4; ++ww) v += wt[ww * 32 + hh] * *(const f32x4*)&ob[(ww * 32 + hh) * OBP + col];
       vr[r][it] = v;
     }
     __syncthreads();
