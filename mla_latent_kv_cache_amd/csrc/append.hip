@@ -247,15 +247,19 @@ __global__ __launch_bounds__(256, 2) void append_mfma_bf16(AppendArgs a) {
   }
 }
 
-using AppCfg = GemmCfg<256, 192, 4>;
+// 256 x 192 tiles in eight waves of 64 x 96 (two per SIMD, so that one wave's MFMAs run while the other
+// waits at the stage barrier or for its LDS operands): 133 us against 150 us with four waves of 128 x 96
+// (one per SIMD) for the 16384 x 768 x 4096 down-projection of a 4 x 4096-token prompt (same-box A/B,
+// identical cache rows).
+using AppCfg8 = GemmCfg<256, 192, 4, 4, 2>;
 
 // Epilogue of accumulator block (I, J): 32 output columns (one per lane, mod 32) x 32 tokens.
-template <int I, int J>
+template <class C, int I, int J>
 __device__ __forceinline__ void append_gemm_block(const AppendArgs& a, const f32x16& v, const int* rows,
                                                   const int* poss, int m0, int n0, int M) {
   const int D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
-  const int c0 = n0 + wn * AppCfg::WN + J * 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN, wn = w % C::WGN;
+  const int c0 = n0 + wn * C::WN + J * 32;
   const int n = c0 + (lane & 31);
   if (c0 >= N) return;  // uniform across the wave
   const int r = a.s.r_pairs, R2 = a.s.r2(), half = a.s.d_head / 2;
@@ -263,13 +267,13 @@ __device__ __forceinline__ void append_gemm_block(const AppendArgs& a, const f32
     if (a.s.fmt == 0) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int ml = wm * C::WM + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         if (m0 + ml < M) ((bf16*)a.ckv)[(size_t)rows[ml] * D + n] = (bf16)v[e];
       }
     } else if (a.s.fmt >= 2) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int ml = wm * C::WM + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         const bool ok = m0 + ml < M;
         store_lane_win2(a, ok, (m0 + ml) / a.t_new, ok ? poss[ml] : 0, n >> 5, v[e]);
       }
@@ -282,7 +286,7 @@ __device__ __forceinline__ void append_gemm_block(const AppendArgs& a, const f32
         const __half s = int4_scale(am);
         const int code = int4_code(v[e], __half2float(s));
         const int partner = __shfl_xor(code, 1, 64);
-        const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int ml = wm * C::WM + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         if (m0 + ml < M) {
           const size_t row = (size_t)rows[ml];
           if ((lane & 1) == 0)
@@ -302,7 +306,7 @@ __device__ __forceinline__ void append_gemm_block(const AppendArgs& a, const f32
     float cst[16], snt[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const int ml = wm * C::WM + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
       const size_t t = (size_t)(m0 + ml < M ? poss[ml] : 0) * half + p;
       cst[e] = a.rope_cos[t];
       snt[e] = a.rope_sin[t];
@@ -310,7 +314,7 @@ __device__ __forceinline__ void append_gemm_block(const AppendArgs& a, const f32
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float partner = shfl_xor(v[e], 1);
-      const int ml = wm * 128 + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const int ml = wm * C::WM + I * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
       if (m0 + ml < M && colok) {
         const float cs = cst[e], sn = snt[e];
         const float x0 = comp ? partner : v[e], x1 = comp ? v[e] : partner;
@@ -321,23 +325,24 @@ __device__ __forceinline__ void append_gemm_block(const AppendArgs& a, const f32
   }
 }
 // All blocks, unrolled at compile time (the accumulators stay in registers).
-template <int I, int J>
-__device__ __forceinline__ void append_gemm_blocks(const AppendArgs& a, f32x16 (&acc)[AppCfg::FM][AppCfg::FN],
+template <class C, int I, int J>
+__device__ __forceinline__ void append_gemm_blocks(const AppendArgs& a, f32x16 (&acc)[C::FM][C::FN],
                                                    const int* rows, const int* poss, int m0, int n0, int M) {
-  append_gemm_block<I, J>(a, acc[I][J], rows, poss, m0, n0, M);
-  if constexpr (J + 1 < AppCfg::FN) {
-    append_gemm_blocks<I, J + 1>(a, acc, rows, poss, m0, n0, M);
-  } else if constexpr (I + 1 < AppCfg::FM) {
-    append_gemm_blocks<I + 1, 0>(a, acc, rows, poss, m0, n0, M);
+  append_gemm_block<C, I, J>(a, acc[I][J], rows, poss, m0, n0, M);
+  if constexpr (J + 1 < C::FN) {
+    append_gemm_blocks<C, I, J + 1>(a, acc, rows, poss, m0, n0, M);
+  } else if constexpr (I + 1 < C::FM) {
+    append_gemm_blocks<C, I + 1, 0>(a, acc, rows, poss, m0, n0, M);
   }
 }
 
 // ------------------------------------------------------------------ MFMA path for long prompts (bf16)
 // Tiles of 256 tokens x 192 output columns through the shared GEMM main loop (gemm.h, four stages,
-// one workgroup per CU, a K loop over the whole model width); the tokens' cache rows and positions
-// are resolved once per tile.  Same epilogue as the 128 x 128 path.
-__global__ __launch_bounds__(256, 1) void append_gemm_bf16(AppendArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[AppCfg::LDS_BYTES];
+// one workgroup of eight waves per CU, a K loop over the whole model width); the tokens' cache rows and
+// positions are resolved once per tile.  Same epilogue as the 128 x 128 path.
+template <class C>
+__global__ __launch_bounds__(C::THREADS, 1) void append_gemm_bf16(AppendArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
   __shared__ int rows[256], poss[256];
   const int K = a.s.d_model, D = a.s.d_kv, NR = a.s.n_rope_cols(), N = D + NR;
   const int M = a.batch * a.t_new;
@@ -347,7 +352,7 @@ __global__ __launch_bounds__(256, 1) void append_gemm_bf16(AppendArgs a) {
   if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
   const int m0 = (bid / n_tiles) * 256, n0 = (bid % n_tiles) * 192;  // consecutive tiles share tokens
   const int tid = threadIdx.x;
-  if (m0 + tid < M) {
+  if (tid < 256 && m0 + tid < M) {
     int pos;
     rows[tid] = cache_row(a, m0 + tid, &pos);
     poss[tid] = pos;
@@ -359,9 +364,9 @@ __global__ __launch_bounds__(256, 1) void append_gemm_bf16(AppendArgs a) {
     const int n = min(n0 + i, N - 1);
     return n < D ? (const bf16*)a.w_dkv + (size_t)n * K : (const bf16*)a.w_krope + (size_t)(n - D) * K;
   };
-  f32x16 acc[AppCfg::FM][AppCfg::FN];
-  gemm_tile<256, 192, 4>(lds, K, a_row, b_row, acc);
-  append_gemm_blocks<0, 0>(a, acc, rows, poss, m0, n0, M);
+  f32x16 acc[C::FM][C::FN];
+  gemm_tile_cfg<C>(lds, K, a_row, b_row, acc);
+  append_gemm_blocks<C, 0, 0>(a, acc, rows, poss, m0, n0, M);
 }
 
 // ------------------------------------------------------------------ MFMA path for few tokens (decode steps)
@@ -553,7 +558,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   } else if (append_uses_mfma(a.s) && a.s.d_model % 32 == 0 && ((M + 255) / 256) * ((N + 191) / 192) >= 192) {
     // long prompts: enough 256 x 192 tiles to fill most CUs
     const int grid = ((M + 255) / 256) * ((N + 191) / 192);
-    hipLaunchKernelGGL(append_gemm_bf16, dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(append_gemm_bf16<AppCfg8>, dim3(grid), dim3(AppCfg8::THREADS), 0, st, a);
   } else if (append_uses_mfma(a.s)) {
     int grid = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
     hipLaunchKernelGGL(append_mfma_bf16, dim3(grid), dim3(256), 0, st, a);

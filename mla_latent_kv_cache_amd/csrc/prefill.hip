@@ -52,6 +52,24 @@ __device__ __forceinline__ int xcd_tile(int bid, int total) {
   return (total & 7) == 0 ? (bid & 7) * (total >> 3) + (bid >> 3) : bid;
 }
 
+// (head, token tile) of reconstruction workgroup k.  When the head count is a multiple of 8, XCD x (which
+// hardware dispatch gives workgroups k = x mod 8) takes heads x, x + 8, ... of every token tile, token tile
+// by token tile: its heads' weight rows (n_h / 8 x 128 KB) stay in its L2 for the whole launch, and each
+// latent tile is read once per XCD by the n_h / 8 workgroups that run it at the same time.  (With every head
+// on every XCD, the 4 MB of all heads' weights did not fit beside the latent tiles in one L2 and were
+// fetched again for every token tile.)
+__device__ __forceinline__ void rec_tile(int bid, int total, int NH, int& hh, int& tile) {
+  if ((NH & 7) == 0 && (total & 7) == 0) {
+    const int x = bid & 7, j = bid >> 3, hpx = NH >> 3;
+    tile = j / hpx;
+    hh = x + 8 * (j - tile * hpx);
+  } else {
+    const int t = xcd_tile(bid, total);
+    hh = t % NH;
+    tile = t / NH;
+  }
+}
+
 // Latent rows 0 .. S-1 of every sequence of a quantised cache, dequantised as the decode kernels do (int4:
 // fp32(code) * fp32(scale); 2-bit: fp32(z + code * s) in one rounding; for the windowed formats the last
 // `win` positions from the bf16 ring, slot t % win) and rounded to bf16 into the workspace [batch, S, d_kv]: the latent operand of the
@@ -85,7 +103,7 @@ __global__ __launch_bounds__(256) void prefill_stage_latent(PrefillArgs a) {
   *(bf16x8*)((bf16*)(a.ws + a.plan.off_lat) + ((size_t)b * S + t) * D + 8 * c8) = v;
 }
 
-__global__ __launch_bounds__(256, 2) void rec_k_gemm(PrefillArgs a, int M) {
+__global__ __launch_bounds__(RecK::THREADS, 2) void rec_k_gemm(PrefillArgs a, int M) {
   __shared__ __attribute__((aligned(1024))) char lds[RecK::LDS_BYTES];
   __shared__ int dim_of[128];
   __shared__ int kept[64];
@@ -93,11 +111,12 @@ __global__ __launch_bounds__(256, 2) void rec_k_gemm(PrefillArgs a, int M) {
   __shared__ int lrow[256];             // latent row of every token (the cache row, or the staged copy's)
   const int K = a.s.d_kv, S = a.seq_len, SP = a.plan.s_pad, dn = a.s.d_nope(), NH = a.s.n_heads;
   const int r = a.s.r_pairs, R2 = a.s.r2();
-  const int bid = xcd_tile(blockIdx.x, gridDim.x);
-  const int hh = bid % NH, m0 = (bid / NH) * 256;  // consecutive tiles share the token rows
+  int hh, tile;
+  rec_tile(blockIdx.x, gridDim.x, NH, hh, tile);
+  const int m0 = tile * 256;
   const int tid = threadIdx.x;
   if (tid < 128) dim_of[tid] = 0;  // duplicate pairs leave entries unset: keep them in range
-  {
+  if (tid < 256) {
     const int m = m0 + tid;
     const int b = m / S, t = m - b * S;
     crow[tid] = m < M ? cache_row_of(a.pm, a.t_max, b, t) : -1;
@@ -119,20 +138,20 @@ __global__ __launch_bounds__(256, 2) void rec_k_gemm(PrefillArgs a, int M) {
     return (const bf16*)a.w_uk + ((size_t)hh * dn + min(i, dn - 1)) * K;
   };
   f32x16 acc[RecK::FM][RecK::FN];
-  gemm_tile<256, 128, 3>(lds, K, a_row, b_row, acc);
+  gemm_tile_cfg<RecK>(lds, K, a_row, b_row, acc);
   __syncthreads();  // the ring is idle; its LDS becomes the staging tile [256 tokens][128 dims]
 
-  const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = tid & 63, w = tid >> 6, wm = w / RecK::WGN, wn = w % RecK::WGN;
 #pragma unroll
   for (int j = 0; j < RecK::FN; ++j) {
-    const int col = wn * 64 + 32 * j + (lane & 31);
+    const int col = wn * RecK::WN + 32 * j + (lane & 31);
     if (col < dn) {
       const int d = dim_of[col];
 #pragma unroll
       for (int i = 0; i < RecK::FM; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = wm * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int row = wm * RecK::WM + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
           *(bf16*)(lds + stage_off(row, d, 256)) = (bf16)acc[i][j][e];
         }
     }
@@ -140,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void rec_k_gemm(PrefillArgs a, int M) {
   // retained dims: the cache's rotated k_rope of (token, head).  Up to 16 of them per row: each thread
   // owns one row and issues all its (4-byte) loads before the first use; more take a slower loop.
   const bf16* kr = (const bf16*)a.krope;
-  if (R2 <= 16) {
+  if (R2 <= 16 && tid < 256) {
     const int c = crow[tid];
     const uint32_t* src = (const uint32_t*)(kr + ((size_t)(c >= 0 ? c : 0) * NRH + gh) * R2);
     uint32_t kv[8];
@@ -149,8 +168,8 @@ __global__ __launch_bounds__(256, 2) void rec_k_gemm(PrefillArgs a, int M) {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       if (2 * q < R2) *(uint32_t*)(lds + stage_off(tid, dim_of[dn + 2 * q], 256)) = kv[q];
-  } else {
-    for (int idx = tid; idx < 256 * R2; idx += 256) {
+  } else if (R2 > 16) {
+    for (int idx = tid; idx < 256 * R2; idx += RecK::THREADS) {
       const int row = idx / R2, q = idx - row * R2, c = crow[row];
       const bf16 v = c >= 0 ? kr[((size_t)c * NRH + gh) * R2 + q] : (bf16)0.f;
       *(bf16*)(lds + stage_off(row, dim_of[dn + q], 256)) = v;
@@ -158,22 +177,24 @@ __global__ __launch_bounds__(256, 2) void rec_k_gemm(PrefillArgs a, int M) {
   }
   __syncthreads();
   bf16* outk = (bf16*)(a.ws + a.plan.off_k);
+  constexpr int KROWS = RecK::THREADS / 16;  // rows stored per round
 #pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int row = it * 16 + (tid >> 4), ch = tid & 15, o = orow[row];
+  for (int it = 0; it < 256 / KROWS; ++it) {
+    const int row = it * KROWS + (tid >> 4), ch = tid & 15, o = orow[row];
     if (o >= 0) *(u32x4*)(outk + (size_t)o * 128 + ch * 8) = *(const u32x4*)(lds + row * 256 + 16 * (ch ^ (row & 7)));
   }
 }
 
-__global__ __launch_bounds__(256, 2) void rec_vt_gemm(PrefillArgs a, int N) {
+__global__ __launch_bounds__(RecV::THREADS, 2) void rec_vt_gemm(PrefillArgs a, int N) {
   __shared__ __attribute__((aligned(1024))) char lds[RecV::LDS_BYTES];
   __shared__ int crow[256];  // cache row of every token column of the tile (clamped to valid rows)
   __shared__ size_t orow[32];  // output offset of every 8-position chunk (-1: none)
   const int K = a.s.d_kv, S = a.seq_len, SP = a.plan.s_pad, NH = a.s.n_heads;
-  const int bid = xcd_tile(blockIdx.x, gridDim.x);
-  const int hh = bid % NH, n0 = (bid / NH) * 256;  // consecutive tiles share the token tile
+  int hh, tile;
+  rec_tile(blockIdx.x, gridDim.x, NH, hh, tile);
+  const int n0 = tile * 256;
   const int tid = threadIdx.x;
-  {
+  if (tid < 256) {
     const int n = min(n0 + tid, N - 1), b = n / SP, t = n - b * SP;
     crow[tid] = a.lat_staged ? b * S + min(t, S - 1) : cache_row_of(a.pm, a.t_max, b, min(t, S - 1));
     if (tid < 32) {
@@ -186,28 +207,29 @@ __global__ __launch_bounds__(256, 2) void rec_vt_gemm(PrefillArgs a, int N) {
   auto a_row = [&](int i) { return (const bf16*)a.w_uv + ((size_t)hh * 128 + i) * K; };
   auto b_row = [&](int i) { return ckv + (size_t)crow[i] * K; };
   f32x16 acc[RecV::FM][RecV::FN];
-  gemm_tile<128, 256, 3>(lds, K, a_row, b_row, acc);
+  gemm_tile_cfg<RecV>(lds, K, a_row, b_row, acc);
   __syncthreads();  // staging tile [128 dims][256 positions]
 
-  const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = tid & 63, w = tid >> 6, wm = w / RecV::WGN, wn = w % RecV::WGN;
 #pragma unroll
   for (int j = 0; j < RecV::FN; ++j) {
-    const int col = wn * 128 + 32 * j + (lane & 31), n = n0 + col, t = n % SP;
+    const int col = wn * RecV::WN + 32 * j + (lane & 31), n = n0 + col, t = n % SP;
     const bool live = n < N && t < S;
     const int p = vt_pos(col);
 #pragma unroll
     for (int i = 0; i < RecV::FM; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = wm * 64 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int row = wm * RecV::WM + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         *(bf16*)(lds + stage_off(row, p, 512)) = live ? (bf16)acc[i][j][e] : (bf16)0.f;
       }
   }
   __syncthreads();
   bf16* outv = (bf16*)(a.ws + a.plan.off_vt);
+  constexpr int VROWS = RecV::THREADS / 32;  // rows stored per round
 #pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int row = it * 8 + (tid >> 5), ch = tid & 31;
+  for (int it = 0; it < 128 / VROWS; ++it) {
+    const int row = it * VROWS + (tid >> 5), ch = tid & 31;
     const size_t o = orow[ch];  // eight positions never straddle two sequences (s_pad is a multiple of 64)
     if (o != ~(size_t)0) *(u32x4*)(outv + o + (size_t)row * SP) = *(const u32x4*)(lds + row * 512 + 16 * (ch ^ (row & 7)));
   }
@@ -538,8 +560,8 @@ hipError_t launch_prefill(const PrefillArgs& a0, hipStream_t st) {
     hipLaunchKernelGGL(prefill_stage_latent, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st, a);
     a.lat_staged = 1;
   }
-  hipLaunchKernelGGL(rec_k_gemm, dim3(((B * S + 255) / 256) * NH), dim3(256), 0, st, a, B * S);
-  hipLaunchKernelGGL(rec_vt_gemm, dim3(NH * ((B * SP + 255) / 256)), dim3(256), 0, st, a, B * SP);
+  hipLaunchKernelGGL(rec_k_gemm, dim3(((B * S + 255) / 256) * NH), dim3(RecK::THREADS), 0, st, a, B * S);
+  hipLaunchKernelGGL(rec_vt_gemm, dim3(NH * ((B * SP + 255) / 256)), dim3(RecV::THREADS), 0, st, a, B * SP);
   const int nqt = (S + FQ - 1) / FQ;
   hipLaunchKernelGGL(prefill_attn, dim3(B * NH * ((nqt + 1) / 2)), dim3(512), 0, st, a);
   return hipGetLastError();
