@@ -119,15 +119,15 @@ typedef struct {
  *   all:      krope [batch, t_max, n_rh, 2r]  config dtype, pair (j, c) of key head g at index g*2r + 2j + c
  * ckv_window and window are read for the windowed formats (INT2_G32_WIN, INT4_G32_WIN) only.
  *
- * Paged caches (block_table != NULL; DENSE and INT4_G32, not the windowed formats): ckv, ckv_scale and krope
- * hold a pool of
+ * Paged caches (block_table != NULL; every format): ckv, ckv_scale and krope hold a pool of
  * n_pages pages of page_size rows each (the row layouts above, n_pages * page_size rows in place of
  * batch * t_max), and position pos of sequence b is pool row
  *     block_table[b * pages_per_seq + pos / page_size] * page_size + pos % page_size.
  * page_size is a multiple of 64; t_max must equal pages_per_seq * page_size; n_pages * page_size <= 2^31 - 1.
  * block_table [batch, pages_per_seq] int32 (device, 4-byte aligned); entries are clamped to
  * [0, n_pages), so a bad entry cannot make a kernel leave the pool.  Sequences may share pages (the
- * multi-query decode below reads one sequence's pages from several queries).                    */
+ * multi-query decode below reads one sequence's pages from several queries).  The windowed formats page
+ * their codes, scales and RoPE keys; their ring ckv_window stays [batch, window, d_kv], one per sequence. */
 typedef struct {
   void *ckv;
   void *ckv_scale;
@@ -264,7 +264,7 @@ int mla_decode_multi(const mla_config *cfg, const mla_weights *w, const mla_cach
  * rebuilds each token's keys and values once instead of folding W_uk,h into every query.
  *   q    [batch, seq_len, n_h, d_h] raw queries;   out [batch, seq_len, n_h, d_h]
  * BF16 layers with d_head 128 and d_kv a multiple of 64 (MLA_ERR_UNSUPPORTED otherwise), any cache format:
- * a quantised latent (INT4_G32, contiguous or paged; INT2_G32_WIN) is first dequantised into the workspace
+ * a quantised latent (INT4_G32, INT2_G32_WIN, INT4_G32_WIN; contiguous or paged) is first dequantised into the workspace
  * exactly as decode reads it (int4: code * scale; 2-bit: z + code * s, the window's rows from the ring; then
  * rounded to bf16).  Windowed formats: every sequence's appended length must be seq_len (the ring then holds
  * positions seq_len - window .. seq_len - 1).

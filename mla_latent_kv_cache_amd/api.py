@@ -232,25 +232,34 @@ class LatentCache:
 
     @staticmethod
     def allocate_paged(shape: LayerShape, block_table: torch.Tensor, page_size: int, n_pages: int, device="cuda",
-                       fill: Optional[float] = None):
+                       fill: Optional[float] = None, window: int = 128):
         """A paged cache: pools of n_pages pages of page_size rows and the page table block_table [batch,
-        pages_per_seq] (int32, device); each sequence holds up to pages_per_seq * page_size tokens."""
-        if shape.cache_fmt in WINDOWED:
-            raise ValueError("paged caches hold dense or int4 latents")
+        pages_per_seq] (int32, device); each sequence holds up to pages_per_seq * page_size tokens.  The windowed
+        formats page their codes, scales and RoPE keys; the bf16 ring of each sequence's last `window` rows
+        stays one block per sequence."""
         batch, pps = block_table.shape
         nr = shape.n_rope_heads * 2 * shape.r_pairs
-        if shape.cache_fmt == "int4_g32":
+        ring = None
+        if shape.cache_fmt in ("int4_g32", "int4_g32_win"):
             ckv = torch.zeros((n_pages, page_size, shape.d_kv // 2), dtype=torch.uint8, device=device)
             scale = torch.zeros((n_pages, page_size, shape.d_kv // 32), dtype=torch.float16, device=device)
+        elif shape.cache_fmt == "int2_g32_win":
+            ckv = torch.zeros((n_pages, page_size, shape.d_kv // 4), dtype=torch.uint8, device=device)
+            scale = torch.zeros((n_pages, page_size, shape.d_kv // 32, 2), dtype=torch.float16, device=device)
         else:
             ckv = torch.empty((n_pages, page_size, shape.d_kv), dtype=shape.torch_dtype, device=device)
             scale = None
+        if shape.cache_fmt in WINDOWED:
+            ring = torch.empty((batch, max(window, 1), shape.d_kv), dtype=torch.bfloat16, device=device)
         krope = torch.empty((n_pages, page_size, max(nr, 1)), dtype=shape.torch_dtype, device=device)
         if fill is not None:
             if scale is None:
                 ckv.fill_(fill)
+            if ring is not None:
+                ring.fill_(fill)
             krope.fill_(fill)
-        return LatentCache(shape, ckv, scale, krope, batch, pps * page_size, None, 0,
+        return LatentCache(shape, ckv, scale, krope, batch, pps * page_size, ring,
+                           window if shape.cache_fmt in WINDOWED else 0,
                            block_table.to(device=device, dtype=torch.int32).contiguous(), page_size, n_pages)
 
     def view(self, b0: int, b1: int) -> "LatentCache":
@@ -258,7 +267,8 @@ class LatentCache:
         takes those sequences' page-table rows)."""
         sl = slice(b0, b1)
         if self.block_table is not None:
-            return LatentCache(self.shape, self.ckv, self.ckv_scale, self.krope, b1 - b0, self.t_max, None, 0,
+            return LatentCache(self.shape, self.ckv, self.ckv_scale, self.krope, b1 - b0, self.t_max,
+                               None if self.ckv_window is None else self.ckv_window[sl], self.window,
                                self.block_table[sl], self.page_size, self.n_pages)
         return LatentCache(self.shape, self.ckv[sl], None if self.ckv_scale is None else self.ckv_scale[sl],
                            self.krope[sl], b1 - b0, self.t_max, None if self.ckv_window is None else self.ckv_window[sl],

@@ -84,7 +84,6 @@ int check_cache(const mla_config* c, const mla_cache* k) {
       return MLA_ERR_INVALID_ARG;
     if ((long long)k->pages_per_seq * k->page_size != k->t_max) return MLA_ERR_INVALID_ARG;
     if ((long long)k->n_pages * k->page_size > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
-    if (windowed(c)) return MLA_ERR_UNSUPPORTED;
   } else if ((long long)k->batch * k->t_max > 0x7fffffffLL) {
     return MLA_ERR_UNSUPPORTED;  // cache rows are indexed with 32-bit integers
   }

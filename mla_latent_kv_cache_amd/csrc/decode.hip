@@ -687,6 +687,17 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   auto load_tile = [&](auto bsel, auto winsel, int tt) {
     constexpr int B = decltype(bsel)::value;
     constexpr bool WIN = decltype(winsel)::value;
+    if constexpr (PG && WIN) {
+      // window rows start at L - window, so a tile of them may cross a page boundary: each lane looks up the
+      // rows of its 4 tokens (only their RoPE keys are loaded here; the latents come from the ring)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = min(tt + xt0 + i, t1 - 1);
+        kreg[B][i] = __builtin_nontemporal_load(
+            (const kv_t*)(krb + ((size_t)seq_row(a, b, tok) * NRH + a.s.rope_head(xh)) * R2));
+      }
+      return;
+    }
     // row0: the tile's first row (paged) or the sequence's (contiguous); tb: the tile's offset from it
     const size_t row0 = PG ? (size_t)__builtin_amdgcn_readfirstlane(seq_row(a, b, tt)) : rowb;
     const int tb = PG ? 0 : tt;
@@ -2070,9 +2081,14 @@ void launch_mfma_attn(const DecodeArgs& a, const FuseArgs& f, hipStream_t st) {
     else
       hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 1, false>), attn_grid(a, f), dim3(256), 0, st, a, f);
   else if (a.s.fmt == 2)
-    hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 2, false>), attn_grid(a, f), dim3(256), 0, st, a, f);  // never paged
+    if (a.pm.bt)
+      hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 2, true>), attn_grid(a, f), dim3(256), 0, st, a, f);
+    else
+      hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 2, false>), attn_grid(a, f), dim3(256), 0, st, a, f);
+  else if (a.pm.bt)
+    hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 3, true>), attn_grid(a, f), dim3(256), 0, st, a, f);
   else
-    hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 3, false>), attn_grid(a, f), dim3(256), 0, st, a, f);  // never paged
+    hipLaunchKernelGGL((decode_attn_mfma<DW, R2, 3, false>), attn_grid(a, f), dim3(256), 0, st, a, f);
 }
 
 }  // namespace

@@ -256,7 +256,7 @@ def test_status_strings(lib):
 
 def test_paged_cache_checks(lib):
     """A paged cache: page size a multiple of 64, t_max = pages_per_seq * page_size, a 4-byte aligned table,
-    a pool of at most 2^31 - 1 rows, dense or int4 latents."""
+    a pool of at most 2^31 - 1 rows, any latent format."""
     def paged(**kw):
         base = dict(block_table=FAKE, page_size=64, pages_per_seq=64, n_pages=2048, t_max=4096)
         base.update(kw)
@@ -270,7 +270,10 @@ def test_paged_cache_checks(lib):
     assert decode_call(lib, k=paged(block_table=FAKE + 2), ws_bytes=big) == ALIGN
     assert decode_call(lib, k=paged(block_table=FAKE + 4), ws_bytes=big, q=None) == INVALID  # 4-byte aligned is fine
     assert decode_call(lib, k=paged(n_pages=1 << 26), ws_bytes=big) == UNSUPPORTED
-    assert decode_call(lib, c=cfg(cache_fmt=2), k=paged(), ws_bytes=big) == UNSUPPORTED
+    # the windowed formats page their codes too: such a cache passes the cache checks and the call stops at the
+    # missing query pointer
+    assert decode_call(lib, c=cfg(cache_fmt=2), k=paged(), ws_bytes=big, q=None) == INVALID
+    assert decode_call(lib, c=cfg(cache_fmt=3), k=paged(), ws_bytes=big, q=None) == INVALID
     # a contiguous cache with more than 2^31 - 1 rows
     assert decode_call(lib, k=cache(batch=1 << 17, t_max=1 << 15), max_len=1, ws_bytes=big) == UNSUPPORTED
 

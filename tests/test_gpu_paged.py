@@ -119,10 +119,12 @@ def run_paged_case(base, family, d_kv, r, prompts, seed, name="", layer=None, ro
         log(f"  b={b} L={L} rel-L2={rr:.2e} max-abs={a:.2e}")
 
 
-@pytest.mark.parametrize("fmt", ["dense", "int4_g32"])
+@pytest.mark.parametrize("fmt", ["dense", "int4_g32", "int4_g32_win", "int2_g32_win"])
 def test_paged_prefill(fmt):
-    """Prefill over a paged cache (the int4 latent dequantised through the page table first)."""
+    """Prefill over a paged cache (quantised latents dequantised through the page table first; the windowed
+    formats take their last 128 rows from the per-sequence ring)."""
     from mla_latent_kv_cache_amd import LatentCache, append, pack_weights, prefill
+    from oracle import int2
 
     cfg = scaled(CONFIGS[2], family="mid", cache_fmt=fmt)
     B, S, P = 2, 300, 64
@@ -146,6 +148,10 @@ def test_paged_prefill(fmt):
                                   cfg.theta)
         if fmt == "int4_g32":
             c = oracle.dequant_int4(*oracle.quantize_int4_g32(c.astype(np.float32)))
+        elif fmt == "int4_g32_win":
+            c = oracle.windowed_latent_int4(synth.round_to_device(c, "bf16"), 128)[0]
+        elif fmt == "int2_g32_win":
+            c = int2.windowed_latent(synth.round_to_device(c, "bf16"), 128)[0]
         ref = oracle.prefill_ref(qs[b], c, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head, cfg.theta)
         rr, a = assert_close(got[b], ref, cfg.dtype, f"paged prefill b={b}")
         log(f"  b={b} rel-L2={rr:.2e} max-abs={a:.2e}")
@@ -238,3 +244,59 @@ def test_paged_decode_step_matches_separate_calls():
         c, kr = oracle_cache(cfg, layer, xs[b])
         ref = oracle.decode_ref(q[b], c, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head, cfg.theta)
         assert_close(got[b], ref, cfg.dtype, f"paged decode_step b={b}")
+
+
+def _pool_gather(pool, table_row, L, P):
+    """Rows 0..L-1 of one sequence from a pool tensor [n_pages, P, ...] through its page-table row."""
+    pos = np.arange(L)
+    rows = torch.from_numpy(table_row[pos // P] * P + pos % P).to(pool.device)
+    return pool.reshape(-1, *pool.shape[2:])[rows]
+
+
+@pytest.mark.parametrize("fmt,W", [("int2_g32_win", 128), ("int4_g32_win", 128), ("int4_g32_win", 64)])
+def test_paged_windowed_append_and_decode(fmt, W):
+    """The windowed formats on a paged cache (codes, scales and RoPE keys in the pool, the bf16 ring per sequence):
+    pool rows equal to a contiguous cache filled the same way, decode equal to it bit for bit (window rows start at
+    L - W, so their tiles cross page boundaries) and to the oracle over its windowed latent within tolerance."""
+    from mla_latent_kv_cache_amd import LatentCache, decode, pack_weights
+    from oracle import int2
+
+    prompts = [700, 1, 129, 0, 200]
+    cfg = scaled(CONFIGS[4], family="mid", cache_fmt=fmt, batch=len(prompts), context=0, ctx_range=None)
+    steps, P = 3, 64
+    lens = [p + steps for p in prompts]
+    pps = (max(lens) + P - 1) // P
+    t_max = pps * P
+    log(f"[paged-win] {fmt} W={W} prompts={prompts} page={P} pages/seq={pps}")
+    layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
+    shape = shape_of(cfg)
+    w = pack_weights(shape, layer, rope_len=t_max, theta=cfg.theta)
+    table, n_pages = _table(len(prompts), pps, 5, seed=31 + W)
+    paged = LatentCache.allocate_paged(shape, table, P, n_pages, fill=float("nan"), window=W)
+    contig = LatentCache.allocate(shape, len(prompts), t_max, fill=float("nan"), window=W)
+    xs = [synth.context_x(cfg, b, L) for b, L in enumerate(lens)]
+    for cache in (paged, contig):
+        _fill(cfg, layer, w, cache, prompts, steps, xs)
+    q = np.stack([decode_query(cfg, layer, x[-1]) for x in xs])
+    qt = torch.from_numpy(q.astype(np.float32)).cuda().to(torch_dtype(cfg))
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out_p = decode(w, paged, qt, lens_t, max(lens))
+    out_c = decode(w, contig, qt, lens_t, max(lens))
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out_c), "paged decode differs from the contiguous one"
+    # bit patterns (slots no append reached still hold the NaN fill in both)
+    assert torch.equal(paged.ckv_window.view(torch.int16), contig.ckv_window.view(torch.int16)), "rings differ"
+    tab = table.cpu().numpy()
+    got = _np(out_p)
+    for b, L in enumerate(lens):
+        nq = L - min(L, W)
+        for name, pool, flat in (("codes", paged.ckv, contig.ckv), ("scales", paged.ckv_scale, contig.ckv_scale)):
+            assert torch.equal(_pool_gather(pool, tab[b], L, P)[:nq], flat[b, :nq]), f"pool {name} b={b}"
+        kr_p = _pool_gather(paged.krope, tab[b], L, P)
+        assert torch.equal(kr_p, contig.krope[b, :L]), f"pool k_rope b={b}"
+        c, kr = oracle_cache(cfg, layer, xs[b])
+        c_bf = synth.round_to_device(c, "bf16")
+        eff = (int2.windowed_latent(c_bf, W) if fmt == "int2_g32_win" else oracle.windowed_latent_int4(c_bf, W))[0]
+        ref = oracle.decode_ref(q[b], eff, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head, cfg.theta)
+        rr, a = assert_close(got[b], ref, cfg.dtype, f"decode b={b} L={L}")
+        log(f"  b={b} L={L} rel-L2={rr:.2e} max-abs={a:.2e}")
