@@ -249,7 +249,9 @@ int mla_decode_step_static(const mla_config *cfg, const mla_weights *w, mla_cach
  * L_b - q_len + i and attends to positions 0 .. L_b - q_len + i; a query at a negative position gives a
  * zero output row.  Same computation per query as mla_decode (q_len == 1 is mla_decode).
  *   q    [batch, q_len, n_h, d_h] raw queries;   out [batch, q_len, n_h, d_h]
- * DENSE and INT4_G32 caches, contiguous or paged (windowed formats with q_len > 1: MLA_ERR_UNSUPPORTED).
+ * Every cache format, contiguous or paged.  Windowed formats: seq_lens are the appended lengths, so the ring
+ * holds positions L_b - window .. L_b - 1 of every query's cache sequence; a query sees the coded rows before
+ * that range and the ring rows up to its own position.
  * Workspace: mla_decode_multi_workspace_bytes(cfg, batch, q_len, max_seq_len) bytes.               */
 size_t mla_decode_multi_workspace_bytes(const mla_config *cfg, int32_t batch, int32_t q_len, int32_t max_seq_len);
 int mla_decode_multi(const mla_config *cfg, const mla_weights *w, const mla_cache *cache, const void *q, int32_t q_len,

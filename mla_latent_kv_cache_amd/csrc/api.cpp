@@ -189,7 +189,6 @@ static int decode_impl(int phase_mask, const mla_config* cfg, const mla_weights*
   MLA_TRY(check_weights(cfg, w, false, true));
   MLA_TRY(check_cache(cfg, cache));
   if (max_seq_len < 0 || q_len < 1) return MLA_ERR_INVALID_ARG;
-  if (q_len > 1 && windowed(cfg)) return MLA_ERR_UNSUPPORTED;
   if (cache->batch == 0) return MLA_OK;
   MLA_TRY(check_ptr(q, true));
   MLA_TRY(check_ptr(seq_lens, true));

@@ -59,11 +59,19 @@ __device__ __forceinline__ int wave_iscan(int v) {  // inclusive prefix sum over
   }
   return v;
 }
-// Items of a sequence of L tokens.  With a window of bf16 rows (fmt 2, a.win > 0) only the coded positions
-// [0, L - min(L, win)) are cut into chunks, and the sequence's last item also takes the window; a sequence
-// with no coded rows has one item, its window.
-__device__ __forceinline__ int item_count(const DecodeArgs& a, int L, int chunk) {
-  const int lq = L - min(L, a.win), nq = (lq + chunk - 1) / chunk;
+// Coded positions visible to query sequence b with L = clamp_len(b) visible keys.  With a window of bf16 rows
+// (windowed formats, a.win > 0) the cache sequence's own last min(Lc, win) positions are ring rows, where Lc is
+// its appended length (L plus the newer queries of the same sequence); the query sees [0, min(L, Lc - win)) as
+// codes and the rest of its keys from the ring.  Without a window every key is coded.
+__device__ __forceinline__ int coded_len(const DecodeArgs& a, int b, int L) {
+  if (a.win <= 0 || L <= 0) return L;
+  const int Lc = L + (a.qn > 1 ? a.qn - 1 - b % a.qn : 0);
+  return min(L, Lc - min(Lc, a.win));
+}
+// Items of query sequence b (L visible keys): its coded positions are cut into chunks, and the last item also
+// takes the window rows; a sequence with no coded rows has one item, its window.
+__device__ __forceinline__ int item_count(const DecodeArgs& a, int b, int L, int chunk) {
+  const int lq = coded_len(a, b, L), nq = (lq + chunk - 1) / chunk;
   return (nq == 0 && L > 0) ? 1 : nq;
 }
 // Lengths of sequences lane, lane + 64, ... : the first block's is returned in L0 (the callers reuse it,
@@ -95,14 +103,14 @@ __device__ bool locate_item(const DecodeArgs& a, int item, WorkItem& wi) {
   for (int c0 = 0; c0 < a.batch; c0 += 64) {
     const int i = c0 + lane;
     const int L = c0 == 0 ? L0 : (i < a.batch ? clamp_len(a, i) : 0);
-    const int cnt = item_count(a, L, chunk);
+    const int cnt = item_count(a, i, L, chunk);
     const int incl = wave_iscan(cnt);
     const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
     if (item < base + total) {
       const unsigned long long hit = __builtin_amdgcn_ballot_w64(base + incl > item);
       const int ln = (int)__builtin_ctzll(hit);
       const int first = base + __shfl(incl - cnt, ln, 64);
-      const int Lb = __shfl(L, ln, 64), lq = Lb - min(Lb, a.win), nq = (lq + chunk - 1) / chunk;
+      const int Lb = __shfl(L, ln, 64), lq = coded_len(a, c0 + ln, Lb), nq = (lq + chunk - 1) / chunk;
       const int j = item - first;
       const bool last = j + 1 >= nq;
       // the values are wave-uniform; readfirstlane lets the compiler keep them (and the addresses
@@ -123,9 +131,9 @@ __device__ bool locate_item(const DecodeArgs& a, int item, WorkItem& wi) {
 __device__ void sequence_items(const DecodeArgs& a, int b, int& first, int& count) {
   const int chunk = work_chunk(a), lane = threadIdx.x & 63;
   int before = 0;
-  for (int i = lane; i < b; i += 64) before += item_count(a, clamp_len(a, i), chunk);
+  for (int i = lane; i < b; i += 64) before += item_count(a, i, clamp_len(a, i), chunk);
   first = __builtin_amdgcn_readfirstlane(wave_isum(before));
-  count = item_count(a, clamp_len(a, b), chunk);
+  count = item_count(a, b, clamp_len(a, b), chunk);
 }
 
 // Rows of a fused split-K append (FuseArgs) at positions [t0, t1) of sequence b, written by the calling
@@ -782,7 +790,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   // (in two halves of four 16-byte chunks per lane, to stay within the registers the prefetch leaves)
   auto stage_window = [&](int tt) {
     constexpr int WCPR = DW / 8, WCH = 32 * WCPR / 64, HALF = WCH / 2;  // chunks per row slice, per lane
-    const bf16* ring = (const bf16*)a.ckv_win + (size_t)b * a.win * D + w * DW;
+    const bf16* ring = (const bf16*)a.ckv_win + (size_t)cseq(a, b) * a.win * D + w * DW;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       u32x4 tmp[HALF];
@@ -1966,14 +1974,14 @@ __global__ __launch_bounds__(64 * CB_NW) void decode_combine(DecodeArgs a, int s
   while (wps < CB_NW && nseq * wps * 2 <= CB_NW) wps *= 2;
   int L0;  // length of sequence `lane` (one read serves the chunk, the item offsets and the counts)
   const int chunk = work_chunk(a, L0);
-  const int cnt0 = item_count(a, L0, chunk);
+  const int cnt0 = item_count(a, lane, L0, chunk);
   bool loaded = false;
   for (int j = w / wps; j < nseq; j += CB_NW / wps) {
     const int b = b0 + j, q = w % wps;
     int before = lane < b ? cnt0 : 0;
-    for (int i = lane + 64; i < b; i += 64) before += item_count(a, clamp_len(a, i), chunk);
+    for (int i = lane + 64; i < b; i += 64) before += item_count(a, i, clamp_len(a, i), chunk);
     const int first = __builtin_amdgcn_readfirstlane(wave_isum(before));
-    const int S = b < 64 ? __builtin_amdgcn_readfirstlane(__shfl(cnt0, b, 64)) : item_count(a, clamp_len(a, b), chunk);
+    const int S = b < 64 ? __builtin_amdgcn_readfirstlane(__shfl(cnt0, b, 64)) : item_count(a, b, clamp_len(a, b), chunk);
     float M, den, acc[KPL];
     if (!loaded) {  // after the sequence lengths: waiting for them does not wait for these
       load_wuv();

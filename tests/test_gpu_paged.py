@@ -157,28 +157,35 @@ def test_paged_prefill(fmt):
         log(f"  b={b} rel-L2={rr:.2e} max-abs={a:.2e}")
 
 
-@pytest.mark.parametrize("fmt,paged,q_len", [("dense", False, 4), ("dense", True, 3), ("int4_g32", True, 2),
-                                            ("dense", False, 1)])
-def test_multi_query_decode(fmt, paged, q_len):
+@pytest.mark.parametrize("fmt,paged,q_len,W,fam", [("dense", False, 4, 0, "mid"), ("dense", True, 3, 0, "mid"),
+                                                  ("int4_g32", True, 2, 0, "mid"), ("dense", False, 1, 0, "mid"),
+                                                  ("int4_g32_win", False, 4, 128, "mid"),
+                                                  ("int2_g32_win", True, 3, 64, "mid"),
+                                                  ("int4_g32_win", True, 2, 64, "mid"),
+                                                  ("int2_g32_win", False, 3, 64, "odd")])
+def test_multi_query_decode(fmt, paged, q_len, W, fam):
     """q_len new tokens of each sequence decoded at once, each causally (sequence lengths below, at and above
-    q_len); equal to the oracle's multi-query decode, and for q_len = 1 to mla_decode bit for bit."""
+    q_len); equal to the oracle's multi-query decode, and for q_len = 1 to mla_decode bit for bit.  With a
+    window of W bf16 rows (windowed formats) the ring holds the last W appended positions of every sequence, so
+    the queries see the same coded rows and ring rows up to their own positions."""
     from mla_latent_kv_cache_amd import LatentCache, decode, decode_multi, pack_weights
+    from oracle import int2
 
-    base = CONFIGS[4] if fmt == "int4_g32" else CONFIGS[1]
+    base = CONFIGS[4] if fmt != "dense" else CONFIGS[1]
     prompts = [500, 2, 70, 0]
-    cfg = scaled(base, family="mid", batch=len(prompts), context=0)
+    cfg = scaled(base, family=fam, batch=len(prompts), context=0, cache_fmt=fmt)
     steps, P = 3, 64
     lens = [p + steps for p in prompts]
     pps = (max(lens) + P - 1) // P
-    log(f"[multi-query] fmt={fmt} paged={paged} q_len={q_len} lens={lens}")
+    log(f"[multi-query] fmt={fmt} paged={paged} q_len={q_len} W={W} family={fam} lens={lens}")
     layer = converted_layer(cfg.family, cfg.r_pairs, cfg.d_kv, cfg.dtype)
     shape = shape_of(cfg)
     w = pack_weights(shape, layer, rope_len=pps * P, theta=cfg.theta)
     if paged:
         table, n_pages = _table(len(prompts), pps, 5, seed=q_len)
-        cache = LatentCache.allocate_paged(shape, table, P, n_pages, fill=float("nan"))
+        cache = LatentCache.allocate_paged(shape, table, P, n_pages, fill=float("nan"), window=W)
     else:
-        cache = LatentCache.allocate(shape, len(prompts), pps * P, fill=float("nan"))
+        cache = LatentCache.allocate(shape, len(prompts), pps * P, fill=float("nan"), window=W)
     xs = [synth.context_x(cfg, b, L) for b, L in enumerate(lens)]
     _fill(cfg, layer, w, cache, prompts, steps, xs)
     # query i of sequence b: the token at position L_b - q_len + i (zeros where that position is negative)
@@ -202,6 +209,10 @@ def test_multi_query_decode(fmt, paged, q_len):
         if fmt == "int4_g32":
             oc, osc = oracle.quantize_int4_g32(c.astype(np.float32))
             c = oracle.dequant_int4(oc, osc)
+        elif fmt == "int4_g32_win":
+            c = oracle.windowed_latent_int4(synth.round_to_device(c, "bf16"), W)[0]
+        elif fmt == "int2_g32_win":
+            c = int2.windowed_latent(synth.round_to_device(c, "bf16"), W)[0]
         ref = oracle.multi_query_decode_ref(q[b], c, kr, layer["w_uk"], layer["w_uv"], layer["pair_idx"], cfg.d_head,
                                             cfg.theta)
         for i in range(q_len):
