@@ -69,9 +69,12 @@ __device__ __forceinline__ int coded_len(const DecodeArgs& a, int b, int L) {
   return min(L, Lc - min(Lc, a.win));
 }
 // Items of query sequence b (L visible keys): its coded positions are cut into chunks, and the last item also
-// takes the window rows; a sequence with no coded rows has one item, its window.
+// takes the window rows; a sequence with no coded rows has one item, its window.  WIN = false: a kernel of a
+// format without a window (a.win is 0 there, so both forms count the same items; the constant one keeps the
+// window arithmetic out of the kernels that never need it).
+template <bool WIN = true>
 __device__ __forceinline__ int item_count(const DecodeArgs& a, int b, int L, int chunk) {
-  const int lq = coded_len(a, b, L), nq = (lq + chunk - 1) / chunk;
+  const int lq = WIN ? coded_len(a, b, L) : L, nq = (lq + chunk - 1) / chunk;
   return (nq == 0 && L > 0) ? 1 : nq;
 }
 // Lengths of sequences lane, lane + 64, ... : the first block's is returned in L0 (the callers reuse it,
@@ -95,7 +98,8 @@ struct WorkItem {
   int w0, w1;     // window rows [w0, w1) of the sequence's last item (fmt 2), else empty
   int L;          // the sequence's (clamped) length
 };
-// Item `item` of the split; false when the batch has fewer items.
+// Item `item` of the split; false when the batch has fewer items (WIN as for item_count).
+template <bool WIN = true>
 __device__ bool locate_item(const DecodeArgs& a, int item, WorkItem& wi) {
   int L0;
   const int chunk = work_chunk(a, L0), lane = threadIdx.x & 63;
@@ -103,14 +107,14 @@ __device__ bool locate_item(const DecodeArgs& a, int item, WorkItem& wi) {
   for (int c0 = 0; c0 < a.batch; c0 += 64) {
     const int i = c0 + lane;
     const int L = c0 == 0 ? L0 : (i < a.batch ? clamp_len(a, i) : 0);
-    const int cnt = item_count(a, i, L, chunk);
+    const int cnt = item_count<WIN>(a, i, L, chunk);
     const int incl = wave_iscan(cnt);
     const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
     if (item < base + total) {
       const unsigned long long hit = __builtin_amdgcn_ballot_w64(base + incl > item);
       const int ln = (int)__builtin_ctzll(hit);
       const int first = base + __shfl(incl - cnt, ln, 64);
-      const int Lb = __shfl(L, ln, 64), lq = coded_len(a, c0 + ln, Lb), nq = (lq + chunk - 1) / chunk;
+      const int Lb = __shfl(L, ln, 64), lq = WIN ? coded_len(a, c0 + ln, Lb) : Lb, nq = (lq + chunk - 1) / chunk;
       const int j = item - first;
       const bool last = j + 1 >= nq;
       // the values are wave-uniform; readfirstlane lets the compiler keep them (and the addresses
@@ -629,7 +633,7 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
     return;
   }
   WorkItem wi;
-  if (!locate_item(a, blockIdx.x, wi)) return;
+  if (!locate_item<HAS_WIN>(a, blockIdx.x, wi)) return;
   const int b = wi.b;
   // the tile loop runs over [wi.t0, wi.t1) and then (windowed formats) over the window [wi.w0, wi.w1), whose rows
   // come from the ring (the WIN instances of load_tile / step); t1 is the end of the current run
@@ -695,16 +699,20 @@ __global__ __launch_bounds__(256, (DW == 128 && FMT == 0) ? 1 : 2) void decode_a
   auto load_tile = [&](auto bsel, auto winsel, int tt) {
     constexpr int B = decltype(bsel)::value;
     constexpr bool WIN = decltype(winsel)::value;
-    if constexpr (PG && WIN) {
-      // window rows start at L - window, so a tile of them may cross a page boundary: each lane looks up the
-      // rows of its 4 tokens (only their RoPE keys are loaded here; the latents come from the ring)
+    // window tiles of a paged cache: the window starts at L - window, so a tile of its rows may cross a page
+    // boundary; each lane looks up the rows of its 4 tokens (only their RoPE keys are loaded for a window
+    // tile, the latents come from the ring).  (Gated first on the kernel's own constants, so that formats
+    // without a window do not see this code at all.)
+    if constexpr (PG && HAS_WIN) {
+      if constexpr (WIN) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = min(tt + xt0 + i, t1 - 1);
-        kreg[B][i] = __builtin_nontemporal_load(
-            (const kv_t*)(krb + ((size_t)seq_row(a, b, tok) * NRH + a.s.rope_head(xh)) * R2));
+        for (int i = 0; i < 4; ++i) {
+          const int tok = min(tt + xt0 + i, t1 - 1);
+          kreg[B][i] = __builtin_nontemporal_load(
+              (const kv_t*)(krb + ((size_t)seq_row(a, b, tok) * NRH + a.s.rope_head(xh)) * R2));
+        }
+        return;
       }
-      return;
     }
     // row0: the tile's first row (paged) or the sequence's (contiguous); tb: the tile's offset from it
     const size_t row0 = PG ? (size_t)__builtin_amdgcn_readfirstlane(seq_row(a, b, tt)) : rowb;
@@ -988,7 +996,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_dma(DecodeArgs a, FuseArgs
     return;
   }
   WorkItem wi;
-  if (!locate_item(a, blockIdx.x, wi)) return;
+  if (!locate_item<false>(a, blockIdx.x, wi)) return;
   const int b = wi.b, t0 = wi.t0, t1 = wi.t1;
 
   // DMA addresses: a wave-uniform tile base (SGPRs) plus per-lane offsets that do not change per tile
@@ -1337,7 +1345,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_wave(DecodeArgs a, FuseArg
     return;
   }
   WorkItem wi;
-  if (!locate_item(a, blockIdx.x, wi)) return;
+  if (!locate_item<false>(a, blockIdx.x, wi)) return;
   const int b = wi.b;
   if (fused_rows(f, b, wi.t0, wi.t1, (float*)lds)) MLA_WAIT_VMCNT(0);
   // the wave's quarter of the item, in whole tiles
