@@ -124,9 +124,11 @@ __global__ __launch_bounds__(RecK::THREADS, 2) void rec_k_gemm(PrefillArgs a, in
     lrow[tid] = m < M ? (a.lat_staged ? m : crow[tid]) : -1;  // staged rows: [b * S + t]
   }
   const int gh = a.s.rope_head(hh), NRH = a.s.rope_heads;  // the head's RoPE key head
-  build_nope_idx(a.pair_idx, gh, r, 64, kept, dim_of);
-  if (tid < R2) dim_of[dn + tid] = 2 * load_pair(a.pair_idx, gh * r + (tid >> 1), 64) + (tid & 1);
   __syncthreads();
+  // the head's retained pairs (for the head-dim table) are loaded now and used after the GEMM: their round
+  // trip runs under its first stages instead of before them (a __syncthreads would wait for them)
+  const int kp = tid < r ? load_pair(a.pair_idx, gh * r + tid, 64) : 0;
+  const int rp = tid < R2 ? load_pair(a.pair_idx, gh * r + (tid >> 1), 64) : 0;
   const bf16* ckv = (const bf16*)(a.lat_staged ? (const void*)(a.ws + a.plan.off_lat) : a.ckv);
   const int last = lrow[min(M - 1 - m0, 255)];
   auto a_row = [&](int i) {
@@ -137,9 +139,37 @@ __global__ __launch_bounds__(RecK::THREADS, 2) void rec_k_gemm(PrefillArgs a, in
     if (dn == 0) return ckv;
     return (const bf16*)a.w_uk + ((size_t)hh * dn + min(i, dn - 1)) * K;
   };
+  // retained dims of the keys: the cache's rotated k_rope of (token, head).  Up to 16 of them per row: each
+  // thread owns one row and loads them (4 bytes each) before the GEMM; they are written after it.
+  const bf16* kr = (const bf16*)a.krope;
+  uint32_t kv[8];
+  const int kc = tid < 256 ? crow[tid] : -1;
+  {
+    const uint32_t* src = (const uint32_t*)(kr + ((size_t)(kc >= 0 ? kc : 0) * NRH + gh) * R2);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) kv[q] = (kc >= 0 && R2 <= 16 && 2 * q < R2) ? src[q] : 0u;
+  }
   f32x16 acc[RecK::FM][RecK::FN];
   gemm_tile_cfg<RecK>(lds, K, a_row, b_row, acc);
   __syncthreads();  // the ring is idle; its LDS becomes the staging tile [256 tokens][128 dims]
+  // the head-dim table (ascending non-retained dims, then the retained pairs' dims), from the loads above
+  for (int i = tid; i < 64; i += RecK::THREADS) kept[i] = 0;
+  __syncthreads();
+  if (tid < r) kept[kp] = 1;
+  __syncthreads();
+  if (tid < 64) {
+    const int l = tid;
+    const bool k0 = kept[l] != 0;
+    const uint64_t m0 = __builtin_amdgcn_ballot_w64(k0);
+    const uint64_t below = l ? (~0ull >> (64 - l)) : 0ull;
+    if (!k0) {
+      const int pos = l - __builtin_popcountll(m0 & below);
+      dim_of[2 * pos] = 2 * l;
+      dim_of[2 * pos + 1] = 2 * l + 1;
+    }
+  }
+  if (tid < R2) dim_of[dn + tid] = 2 * rp + (tid & 1);
+  __syncthreads();
 
   const int lane = tid & 63, w = tid >> 6, wm = w / RecK::WGN, wn = w % RecK::WGN;
 #pragma unroll
@@ -156,15 +186,8 @@ __global__ __launch_bounds__(RecK::THREADS, 2) void rec_k_gemm(PrefillArgs a, in
         }
     }
   }
-  // retained dims: the cache's rotated k_rope of (token, head).  Up to 16 of them per row: each thread
-  // owns one row and issues all its (4-byte) loads before the first use; more take a slower loop.
-  const bf16* kr = (const bf16*)a.krope;
+  // retained dims from the registers loaded before the GEMM; more than 16 take a slower loop
   if (R2 <= 16 && tid < 256) {
-    const int c = crow[tid];
-    const uint32_t* src = (const uint32_t*)(kr + ((size_t)(c >= 0 ? c : 0) * NRH + gh) * R2);
-    uint32_t kv[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) kv[q] = (c >= 0 && 2 * q < R2) ? src[q] : 0u;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       if (2 * q < R2) *(uint32_t*)(lds + stage_off(tid, dim_of[dn + 2 * q], 256)) = kv[q];
